@@ -1,0 +1,66 @@
+"""Loops of the single-head oracle functions over [B, H, T, d] arrays.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Heads are independent in every form on the source page, so a batch is just
+a loop over (b, h); nothing is fused or reordered.  Layouts: q, k [B,H,T,d_k],
+v [B,H,T,d_v], alpha/beta [B,H,T], S [B,H,d_v,d_k], z [B,H,d_k].
+An optional ``heads`` list of (b, h) pairs restricts the work to a sample.
+"""
+
+import numpy as np
+
+from .linear_attention import phi, la_parallel, la_recurrent, la_chunked
+from .gated_delta import gdn_recurrent, gdn_chunked
+
+
+def _heads(B, H, heads):
+    return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+
+
+def lin_attn(q, k, v, form="chunked", chunk=64, S0=None, z0=None, heads=None):
+    """Returns (o, S, z) over the batch (only the listed heads are filled)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    S = np.zeros((B, H, dv, dk))
+    z = np.zeros((B, H, dk))
+    for b, h in _heads(B, H, heads):
+        s0 = None if S0 is None else S0[b, h]
+        z_0 = None if z0 is None else z0[b, h]
+        if form == "parallel":
+            if (s0 is not None and np.any(s0)) or (z_0 is not None and np.any(z_0)):
+                raise ValueError("the parallel form has no carried state")
+            o[b, h] = la_parallel(q[b, h], k[b, h], v[b, h])
+            S[b, h], z[b, h] = _final_la_state(k[b, h], v[b, h])
+        elif form == "recurrent":
+            o[b, h], S[b, h], z[b, h] = la_recurrent(q[b, h], k[b, h], v[b, h], s0, z_0)
+        elif form == "chunked":
+            o[b, h], S[b, h], z[b, h] = la_chunked(q[b, h], k[b, h], v[b, h], chunk, s0, z_0)
+        else:
+            raise ValueError(form)
+    return o, S, z
+
+
+def _final_la_state(k, v):
+    """S_T = sum_j v_j phi(k_j)^T and z_T = sum_j phi(k_j): the sums S_i, z_i
+    of the kernel-trick equation at i = T ("The kernel trick" section)."""
+    fk = phi(k)
+    return v.T @ fk, fk.sum(axis=0)
+
+
+def gdn(q, k, v, alpha, beta, form="chunked", chunk=64, S0=None, heads=None):
+    """Returns (o, S) over the batch (only the listed heads are filled)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    S = np.zeros((B, H, dv, dk))
+    for b, h in _heads(B, H, heads):
+        s0 = None if S0 is None else S0[b, h]
+        if form == "recurrent":
+            o[b, h], S[b, h] = gdn_recurrent(q[b, h], k[b, h], v[b, h], alpha[b, h], beta[b, h], s0)
+        elif form == "chunked":
+            o[b, h], S[b, h] = gdn_chunked(q[b, h], k[b, h], v[b, h], alpha[b, h], beta[b, h], chunk, s0)
+        else:
+            raise ValueError(form)
+    return o, S

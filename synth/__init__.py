@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module only draws and rounds numbers; it holds none of the method's
+arithmetic, and it imports neither the oracle nor the HIP library, so both
+sides can consume the very same values.
+
+Recipe (one generator per head, so any sample of heads can be regenerated
+without drawing the rest):
+
+* ``np.random.default_rng([seed, stream, b, h])`` with streams
+  q=0, k=1, v=2, alpha=3, beta=4, S0=5, z0=6; draws are float32 standard
+  normals (``Generator.standard_normal(dtype=float32)``).
+* q, k, v ~ N(0, 1), optionally scaled (1/sqrt(d) for the bf16 linear-attention
+  workload) or L2-normalised per token (the gated-delta workloads), then
+  rounded to the I/O dtype.  bf16 rounding is round-to-nearest-even, and the
+  returned float32 arrays hold exactly the bf16 values the GPU sees.
+* alpha = sigmoid(N(3, 1)), beta = sigmoid(N(0, 1)), kept in float32.
+* decode: the carried state S0 ~ N(0, 0.02^2) float32 per head; the per-step
+  token inputs come from a pool of ``pool`` draws (step s uses pool entry
+  s mod pool), generated with ``default_rng([seed, stream, 1000 + entry])``.
+"""
+
+import numpy as np
+
+STREAM_Q, STREAM_K, STREAM_V, STREAM_ALPHA, STREAM_BETA, STREAM_S0, STREAM_Z0 = range(7)
+
+# The five named workloads.  ``seed`` is the per-workload base seed.
+WORKLOADS = {
+    "la_fp32_small": dict(seed=1001, kind="la", B=1, H=2, T=256, dk=16, dv=16, dtype="f32",
+                          chunk=32, scale=1.0),
+    "la_bf16_4x16x4096": dict(seed=1002, kind="la", B=4, H=16, T=4096, dk=128, dv=128,
+                              dtype="bf16", chunk=64, scale=1.0 / np.sqrt(128.0)),
+    "gdn_bf16_2x16x8192": dict(seed=1003, kind="gdn", B=2, H=16, T=8192, dk=128, dv=128,
+                               dtype="bf16", chunk=64),
+    "gdn_decode_256x32": dict(seed=1004, kind="decode", N=256, H=32, dk=128, dv=128,
+                              dtype="bf16", steps=1000, state_std=0.02),
+    "gdn_bf16_1x16x262144": dict(seed=1005, kind="gdn", B=1, H=16, T=262144, dk=128, dv=128,
+                                 dtype="bf16", chunk=64),
+}
+
+
+def round_bf16(x):
+    """Round to the nearest bfloat16 (ties to even); returns float32 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+def round_io(x, dtype):
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def _rng(seed, stream, *idx):
+    return np.random.default_rng([int(seed), int(stream), *[int(i) for i in idx]])
+
+
+def _normal(seed, stream, idx, shape):
+    return _rng(seed, stream, *idx).standard_normal(size=shape, dtype=np.float32)
+
+
+def _unit_rows(x):
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x / n).astype(np.float32)
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def la_head(seed, b, h, T, dk, dv, dtype, scale=1.0):
+    """q, k, v for one head of a linear-attention workload (float32 arrays)."""
+    q = _normal(seed, STREAM_Q, (b, h), (T, dk)) * np.float32(scale)
+    k = _normal(seed, STREAM_K, (b, h), (T, dk)) * np.float32(scale)
+    v = _normal(seed, STREAM_V, (b, h), (T, dv)) * np.float32(scale)
+    return round_io(q, dtype), round_io(k, dtype), round_io(v, dtype)
+
+
+def gdn_head(seed, b, h, T, dk, dv, dtype, alpha_mean=3.0, beta_mean=0.0):
+    """q, k (unit rows), v, alpha, beta for one head of a gated-delta workload."""
+    q = round_io(_unit_rows(_normal(seed, STREAM_Q, (b, h), (T, dk))), dtype)
+    k = round_io(_unit_rows(_normal(seed, STREAM_K, (b, h), (T, dk))), dtype)
+    v = round_io(_normal(seed, STREAM_V, (b, h), (T, dv)), dtype)
+    alpha = _sigmoid(_normal(seed, STREAM_ALPHA, (b, h), (T,)) + np.float32(alpha_mean))
+    beta = _sigmoid(_normal(seed, STREAM_BETA, (b, h), (T,)) + np.float32(beta_mean))
+    return q, k, v, alpha, beta
+
+
+def state_head(seed, b, h, dk, dv, std, stream=STREAM_S0):
+    """A carried fp32 state S0 for one head, N(0, std^2)."""
+    return (_normal(seed, stream, (b, h), (dv, dk)) * np.float32(std)).astype(np.float32)
+
+
+def norm_head(seed, b, h, dk, scale=1.0):
+    """A carried normaliser z0 for one head (positive, like a sum of phi(k))."""
+    return (np.abs(_normal(seed, STREAM_Z0, (b, h), (dk,))) * np.float32(scale) + 1).astype(np.float32)
+
+
+def la_batch(seed, B, H, T, dk, dv, dtype, scale=1.0):
+    q = np.empty((B, H, T, dk), np.float32)
+    k = np.empty((B, H, T, dk), np.float32)
+    v = np.empty((B, H, T, dv), np.float32)
+    for b in range(B):
+        for h in range(H):
+            q[b, h], k[b, h], v[b, h] = la_head(seed, b, h, T, dk, dv, dtype, scale)
+    return q, k, v
+
+
+def gdn_batch(seed, B, H, T, dk, dv, dtype, **kw):
+    q = np.empty((B, H, T, dk), np.float32)
+    k = np.empty((B, H, T, dk), np.float32)
+    v = np.empty((B, H, T, dv), np.float32)
+    a = np.empty((B, H, T), np.float32)
+    be = np.empty((B, H, T), np.float32)
+    for b in range(B):
+        for h in range(H):
+            q[b, h], k[b, h], v[b, h], a[b, h], be[b, h] = gdn_head(seed, b, h, T, dk, dv, dtype, **kw)
+    return q, k, v, a, be
+
+
+def state_batch(seed, B, H, dk, dv, std, stream=STREAM_S0):
+    S = np.empty((B, H, dv, dk), np.float32)
+    for b in range(B):
+        for h in range(H):
+            S[b, h] = state_head(seed, b, h, dk, dv, std, stream)
+    return S
+
+
+def decode_state_fast(seed, N, H, dk, dv, std):
+    """The whole decode state [N,H,dv,dk] from one generator (large sizes);
+    the same values as ``decode_state_heads`` would not be produced, so the
+    decode recipe uses this function on both sides."""
+    rng = _rng(seed, STREAM_S0)
+    return (rng.standard_normal(size=(N, H, dv, dk), dtype=np.float32) * np.float32(std))
+
+
+def decode_token_inputs(seed, N, H, dk, dv, dtype, entry):
+    """One pool entry of per-step decode inputs: q, k (unit), v [N,H,d], alpha, beta [N,H]."""
+    q = round_io(_unit_rows(_normal(seed, STREAM_Q, (1000 + entry,), (N, H, dk))), dtype)
+    k = round_io(_unit_rows(_normal(seed, STREAM_K, (1000 + entry,), (N, H, dk))), dtype)
+    v = round_io(_normal(seed, STREAM_V, (1000 + entry,), (N, H, dv)), dtype)
+    alpha = _sigmoid(_normal(seed, STREAM_ALPHA, (1000 + entry,), (N, H)) + np.float32(3.0))
+    beta = _sigmoid(_normal(seed, STREAM_BETA, (1000 + entry,), (N, H)))
+    return q, k, v, alpha, beta
+
+
+def la_decode_token_inputs(seed, N, H, dk, dv, dtype, entry, scale=1.0):
+    """One pool entry of per-step inputs for the normalised linear-attention decode."""
+    q = round_io(_normal(seed, STREAM_Q, (2000 + entry,), (N, H, dk)) * np.float32(scale), dtype)
+    k = round_io(_normal(seed, STREAM_K, (2000 + entry,), (N, H, dk)) * np.float32(scale), dtype)
+    v = round_io(_normal(seed, STREAM_V, (2000 + entry,), (N, H, dv)) * np.float32(scale), dtype)
+    return q, k, v

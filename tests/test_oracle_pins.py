@@ -1,0 +1,365 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Every check here runs on the CPU.  Sources of truth:
+
+* values printed on the source page ("Linear attention and hybrids",
+  ai.flicky.cc lesson 5.5.03), stored under tests/golden/ with their citation;
+* closed forms and invariants of the equations (beta = 0, unit keys with
+  beta = 1, orthonormal keys, identical keys, constant values);
+* brute force: the gated delta rule unrolled into explicit products of
+  transition matrices, evaluated exactly in rational arithmetic.
+
+The last part plants plausible mistakes (a dropped term, a wrong sign, a
+transposed operand, an off-by-one mask) into copies of the oracle source and
+checks that at least one pin rejects each of them.
+"""
+
+import json
+import os
+import types
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gated_delta as gd_mod
+from oracle import linear_attention as la_mod
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rand_gdn(rng, T, dk, dv, alpha_mean=3.0, unit=True):
+    Q = rng.normal(size=(T, dk))
+    K = rng.normal(size=(T, dk))
+    if unit:
+        Q /= np.linalg.norm(Q, axis=1, keepdims=True)
+        K /= np.linalg.norm(K, axis=1, keepdims=True)
+    V = rng.normal(size=(T, dv))
+    a = 1 / (1 + np.exp(-rng.normal(alpha_mean, 1, T)))
+    b = 1 / (1 + np.exp(-rng.normal(0, 1, T)))
+    return Q, K, V, a, b
+
+
+# --------------------------------------------------------------------------
+# Pin functions.  Each takes a namespace holding the oracle functions, so the
+# same checks can be run against planted mutants below.  Each raises
+# AssertionError on failure.
+# --------------------------------------------------------------------------
+
+def pin_phi(ns):
+    g = golden("phi_worked_example.json")
+    fq, fk = ns.phi(np.array(g["q"])), ns.phi(np.array(g["k"]))
+    d = g["decimals"]
+    assert np.allclose(np.round(fq, d), g["phi_q"]) and np.allclose(np.round(fk, d), g["phi_k"])
+    assert round(float(fq @ fk), d) == g["linear_similarity"]
+    assert round(float(np.exp(np.dot(g["q"], g["k"]))), d) == g["softmax_similarity"]
+    # closed form: phi(-1) = 1/e, phi(0) = 1, phi(x) = x + 1 for x > 0
+    g2 = golden("phi_selfcheck.json")
+    px = ns.phi(np.array(g2["x"]))
+    assert np.allclose(np.round(px, g2["decimals"]), g2["phi_x"])
+    assert abs(px[0] - np.exp(-1.0)) < 1e-15 and px[1] == 1.0 and px[2] == 3.0
+    assert np.all(ns.phi(np.linspace(-30, 30, 101)) > 0)
+
+
+def pin_three_forms(ns):
+    """The page's self-check: rng(0), Q, K, V of shape (6, 4), C = 4 (last block
+    of 2 tokens); all forms agree and the state is (d_v, d_k) = (4, 4)."""
+    rng = np.random.default_rng(0)
+    Q, K, V = rng.normal(size=(3, 6, 4))
+    p = ns.la_parallel(Q, K, V)
+    r, S, z = ns.la_recurrent(Q, K, V)
+    c, S2, z2 = ns.la_chunked(Q, K, V, 4)
+    assert np.allclose(p, r) and np.allclose(p, c)
+    assert S.shape == (4, 4) and z.shape == (4,)
+    assert np.abs(p - r).max() < 1e-12 and np.abs(p - c).max() < 1e-12
+    assert np.abs(S - S2).max() < 1e-12 and np.abs(z - z2).max() < 1e-12
+
+
+def pin_la_closed_forms(ns):
+    rng = np.random.default_rng(7)
+    T, d = 9, 5
+    # identical keys: every weight in a row is equal, so o_t is the running mean of v
+    q = rng.normal(size=(T, d))
+    k = np.tile(rng.normal(size=(1, d)), (T, 1))
+    v = rng.normal(size=(T, 3))
+    mean = np.cumsum(v, axis=0) / np.arange(1, T + 1)[:, None]
+    for o in (ns.la_parallel(q, k, v), ns.la_recurrent(q, k, v)[0], ns.la_chunked(q, k, v, 4)[0]):
+        assert np.abs(o - mean).max() < 1e-12
+    # a single token reads back its own value
+    for o in (ns.la_parallel(q[:1], q[:1], v[:1]), ns.la_recurrent(q[:1], k[:1], v[:1])[0]):
+        assert np.abs(o - v[:1]).max() < 1e-15
+    # constant values: the normalised output is that constant at every step
+    k2 = rng.normal(size=(T, d))
+    vc = np.full((T, 2), 2.5)
+    for o in (ns.la_parallel(q, k2, vc), ns.la_recurrent(q, k2, vc)[0], ns.la_chunked(q, k2, vc, 4)[0]):
+        assert np.abs(o - 2.5).max() < 1e-12
+    # final state is the plain sum over all tokens
+    _, S, z = ns.la_recurrent(q, k2, v)
+    assert np.abs(S - v.T @ ns.phi(k2)).max() < 1e-12
+    assert np.abs(z - ns.phi(k2).sum(0)).max() < 1e-12
+
+
+def pin_la_chunk_invariance(ns):
+    rng = np.random.default_rng(11)
+    T, dk, dv = 37, 6, 5
+    Q, K, V = rng.normal(size=(T, dk)), rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    S0 = rng.normal(size=(dv, dk)) ** 2
+    z0 = np.abs(rng.normal(size=dk)) + 1
+    o_r, S_r, z_r = ns.la_recurrent(Q, K, V, S0, z0)
+    for C in (1, 7, 32, 64, T):
+        o_c, S_c, z_c = ns.la_chunked(Q, K, V, C, S0, z0)
+        assert np.abs(o_c - o_r).max() < 1e-12
+        assert np.abs(S_c - S_r).max() < 1e-12 and np.abs(z_c - z_r).max() < 1e-12
+    assert np.abs(ns.la_parallel(Q, K, V) - ns.la_chunked(Q, K, V, 8)[0]).max() < 1e-12
+    # split-resume: two calls with the carried state equal one call
+    o1, S1, z1 = ns.la_recurrent(Q[:20], K[:20], V[:20], S0, z0)
+    o2, S2, z2 = ns.la_chunked(Q[20:], K[20:], V[20:], 8, S1, z1)
+    assert np.abs(np.vstack([o1, o2]) - o_r).max() < 1e-12 and np.abs(S2 - S_r).max() < 1e-12
+
+
+def pin_decay(ns):
+    g = golden("decay_forms.json")
+    rng = np.random.default_rng(0)
+    Q, K, V = rng.normal(size=(3, g["T"], g["d"]))
+    o_rec, _ = ns.decayed_recurrent(Q, K, V, g["gamma"])
+    o_par, D = ns.decayed_parallel(Q, K, V, g["gamma"])
+    assert np.abs(o_rec - o_par).max() < 10 * g["printed_max_discrepancy"]
+    assert np.array_equal(D.round(2), np.array(g["D_rounded_2dp"]))
+
+
+def pin_delta_example(ns):
+    g = golden("delta_rule_example.json")
+    k = np.array([g["key"], g["key"]])
+    v = np.array(g["values_written"])
+    ones = np.ones(2)
+    o_delta, _ = ns.gdn_recurrent(k, k, v, ones, ones * g["beta"])
+    o_delta_c, _ = ns.gdn_chunked(k, k, v, ones, ones * g["beta"], 2)
+    o_lin, _ = ns.decayed_recurrent(k, k, v, 1.0)
+    assert np.allclose(o_delta[-1], g["read_delta_rule"], atol=1e-15)
+    assert np.allclose(o_delta_c[-1], g["read_delta_rule"], atol=1e-15)
+    assert np.allclose(o_lin[-1], g["read_plain_linear"], atol=1e-15)
+
+
+def pin_memory_capacity(ns):
+    g = golden("memory_capacity.json")
+    d = 32
+    rng = np.random.default_rng(0)
+
+    def cos_rows(x, y):
+        return np.sum(x * y, axis=1) / np.linalg.norm(x, axis=1) / np.linalg.norm(y, axis=1)
+
+    for n, soft_p, lin_p, delta_p, last_p in g["rows"]:
+        K = rng.normal(size=(n, d))
+        K = K / np.linalg.norm(K, axis=1, keepdims=True)
+        V = rng.normal(size=(n, d))
+        logits = 20.0 * K @ K.T
+        w = np.exp(logits - logits.max(axis=1, keepdims=True))
+        soft = (w / w.sum(axis=1, keepdims=True)) @ V
+        _, S_lin = ns.decayed_recurrent(K, K, V, 1.0)
+        _, S_delta = ns.gdn_recurrent(K, K, V, np.ones(n), np.ones(n))
+        c_delta = cos_rows(K @ S_delta.T, V)
+        got = [cos_rows(soft, V).mean(), cos_rows(K @ S_lin.T, V).mean(), c_delta.mean(),
+               c_delta[-4:].mean()]
+        want = [soft_p, lin_p, delta_p, last_p]
+        assert [round(float(x), g["decimals"]) for x in got] == want, (n, got, want)
+
+
+def pin_gdn_unit_key_recall(ns):
+    """beta = 1 and |k| = 1: right after the write, S_t k_t = v_t for any alpha."""
+    rng = np.random.default_rng(3)
+    T, d = 23, 6
+    _, K, V, a, _ = rand_gdn(rng, T, d, 4)
+    S0 = rng.normal(size=(4, d))
+    for o in (ns.gdn_recurrent(K, K, V, a, np.ones(T), S0)[0],
+              ns.gdn_chunked(K, K, V, a, np.ones(T), 8, S0)[0]):
+        assert np.abs(o - V).max() < 1e-13
+
+
+def pin_gdn_beta_zero(ns):
+    """beta = 0: nothing is written, S_t = (prod alpha) S0 and o_t = that times q_t."""
+    rng = np.random.default_rng(4)
+    T, d = 17, 5
+    Q, K, V, a, _ = rand_gdn(rng, T, d, 3, unit=False)
+    S0 = rng.normal(size=(3, d))
+    gam = np.cumprod(a)
+    want = gam[:, None] * (Q @ S0.T)
+    for o, S in (ns.gdn_recurrent(Q, K, V, a, np.zeros(T), S0),
+                 ns.gdn_chunked(Q, K, V, a, np.zeros(T), 4, S0)):
+        assert np.abs(o - want).max() < 1e-13
+        assert np.abs(S - gam[-1] * S0).max() < 1e-13
+    o, S = ns.gdn_recurrent(Q, K, V, np.ones(T), np.zeros(T), S0)
+    assert np.abs(S - S0).max() == 0
+
+
+def pin_gdn_orthonormal_recall(ns):
+    """d orthonormal keys, alpha = beta = 1: every stored value is read back exactly."""
+    rng = np.random.default_rng(5)
+    d = 8
+    Kq, _ = np.linalg.qr(rng.normal(size=(d, d)))
+    K = Kq.T
+    V = rng.normal(size=(d, d))
+    for _, S in (ns.gdn_recurrent(K, K, V, np.ones(d), np.ones(d)),
+                 ns.gdn_chunked(K, K, V, np.ones(d), np.ones(d), 3)):
+        assert np.abs(K @ S.T - V).max() < 1e-12
+
+
+def pin_gdn_bruteforce_exact(ns):
+    """States and outputs against the unrolled product form in exact rationals."""
+    rng = np.random.default_rng(6)
+    T, dk, dv = 5, 3, 2
+
+    def rat(x, den=16):
+        return Fraction(int(round(x * den)), den)
+
+    K = [[rat(x) for x in row] for row in rng.normal(size=(T, dk))]
+    Qr = [[rat(x) for x in row] for row in rng.normal(size=(T, dk))]
+    V = [[rat(x) for x in row] for row in rng.normal(size=(T, dv))]
+    al = [Fraction(int(x), 32) for x in rng.integers(20, 32, T)]
+    be = [Fraction(int(x), 32) for x in rng.integers(1, 32, T)]
+    S0 = [[rat(x) for x in row] for row in rng.normal(size=(dv, dk))]
+    exact = gd_mod.gdn_bruteforce_states(K, V, al, be, S0)
+    f = lambda m: np.array([[float(x) for x in r] for r in m])
+    Kf, Qf, Vf, S0f = f(K), f(Qr), f(V), f(S0)
+    af, bf = np.array([float(x) for x in al]), np.array([float(x) for x in be])
+    o_exact = np.array([[float(sum(exact[t][i][p] * Qr[t][p] for p in range(dk))) for i in range(dv)]
+                        for t in range(T)])
+    for C in (None, 1, 2, T):
+        if C is None:
+            o, S = ns.gdn_recurrent(Qf, Kf, Vf, af, bf, S0f)
+        else:
+            o, S = ns.gdn_chunked(Qf, Kf, Vf, af, bf, C, S0f)
+        assert np.abs(o - o_exact).max() < 1e-13, C
+        assert np.abs(S - f(exact[-1])).max() < 1e-13, C
+    # every intermediate state of the recurrence, via its one-token steps
+    S = S0f
+    for t in range(T):
+        o_t, S = ns.gdn_decode_step(Qf[t], Kf[t], Vf[t], af[t], bf[t], S)
+        assert np.abs(S - f(exact[t])).max() < 1e-13
+        assert np.abs(o_t - o_exact[t]).max() < 1e-13
+
+
+def pin_gdn_chunk_invariance(ns):
+    rng = np.random.default_rng(12)
+    T, dk, dv = 70, 8, 6
+    Q, K, V, a, b = rand_gdn(rng, T, dk, dv, alpha_mean=1.0)
+    S0 = rng.normal(size=(dv, dk))
+    o_r, S_r = ns.gdn_recurrent(Q, K, V, a, b, S0)
+    for C in (1, 7, 32, 64, T):
+        o_c, S_c = ns.gdn_chunked(Q, K, V, a, b, C, S0)
+        assert np.abs(o_c - o_r).max() < 1e-12, C
+        assert np.abs(S_c - S_r).max() < 1e-12, C
+    o_p, S_p = ns.gdn_parallel(Q, K, V, a, b)
+    o_r0, S_r0 = ns.gdn_recurrent(Q, K, V, a, b)
+    assert np.abs(o_p - o_r0).max() < 1e-12 and np.abs(S_p - S_r0).max() < 1e-12
+    # split-resume with the carried state
+    o1, S1 = ns.gdn_chunked(Q[:29], K[:29], V[:29], a[:29], b[:29], 8, S0)
+    o2, S2 = ns.gdn_chunked(Q[29:], K[29:], V[29:], a[29:], b[29:], 16, S1)
+    assert np.abs(np.vstack([o1, o2]) - o_r).max() < 1e-12 and np.abs(S2 - S_r).max() < 1e-12
+
+
+GDN_PINS = [pin_delta_example, pin_memory_capacity, pin_gdn_unit_key_recall, pin_gdn_beta_zero,
+            pin_gdn_orthonormal_recall, pin_gdn_bruteforce_exact, pin_gdn_chunk_invariance]
+LA_PINS = [pin_phi, pin_three_forms, pin_la_closed_forms, pin_la_chunk_invariance, pin_decay]
+
+
+@pytest.mark.parametrize("pin", LA_PINS + GDN_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(oracle)
+
+
+def test_sizes_closed_forms():
+    """Sizes the page states, from their closed forms; the decode bench prices
+    its state traffic with the same per-head figure."""
+    g = golden("sizes.json")
+    d = 128
+    assert d * d == g["state_numbers_per_head_d128"]
+    n = 10 ** 6
+    ratio = (n * n * d) / (n * d * d)
+    assert abs(ratio - g["op_ratio_n1e6_d128_approx"]) / g["op_ratio_n1e6_d128_approx"] < 0.03
+    kv_1m = 48 * 2 * 2 * 256 * 2 * n / 2 ** 30   # layers x (K,V) x heads x dim x bf16 x tokens
+    assert round(kv_1m) == g["kv_cache_48_layers_1M_tokens_GiB_approx"]
+    per_token_12 = 12 * 1024 * 2
+    assert per_token_12 * 262144 / 2 ** 30 == g["kv_cache_12_layers_262K_GiB"]
+    assert 4 * per_token_12 * 262144 / 2 ** 30 == g["kv_cache_48_layers_262K_GiB"]
+    assert 36 * 32 * 128 * 128 * 4 / 2 ** 20 == g["gdn_states_36_layers_32_heads_MiB"]
+
+
+# --------------------------------------------------------------------------
+# Planted mistakes: each mutant of the oracle source must fail some pin.
+# --------------------------------------------------------------------------
+
+def _mutant(module, old, new):
+    src = open(module.__file__).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    ns = {"__name__": module.__name__ + "_mutant"}
+    exec(compile(src.replace(old, new), module.__file__ + "<mutant>", "exec"), ns)
+    return ns
+
+
+def _namespace(la_ns=None, gd_ns=None):
+    la_src = la_ns or vars(la_mod)
+    gd_src = gd_ns or vars(gd_mod)
+    names = ["phi", "la_parallel", "la_recurrent", "la_chunked", "la_decode_step",
+             "decayed_recurrent", "decayed_parallel"]
+    gnames = ["gdn_recurrent", "gdn_chunked", "gdn_parallel", "gdn_decode_step"]
+    return types.SimpleNamespace(**{n: la_src[n] for n in names}, **{n: gd_src[n] for n in gnames})
+
+
+LA_MUTATIONS = [
+    ("np.where(x > 0, x + 1.0,", "np.where(x > 0, x,"),
+    ("np.exp(np.minimum(x, 0.0))", "np.exp(-np.minimum(x, 0.0))"),
+    ("A = np.tril(phi(Q) @ phi(K).T)", "A = np.triu(phi(Q) @ phi(K).T)"),
+    ("        z = z + fk\n", "        z = z + fq\n"),
+    ("A_in = np.tril(fq @ fk.T)", "A_in = np.tril(fq @ fk.T, k=-1)"),
+    ("num = A_in @ V[a:b] + fq @ S.T", "num = A_in @ V[a:b] + fq @ S"),
+    ("den = A_in.sum(axis=1) + fq @ z", "den = A_in.sum(axis=0) + fq @ z"),
+    ("S = S + V[a:b].T @ fk", "S = S + fk.T @ V[a:b]"),
+    ("np.maximum(i - j, 0)", "np.maximum(j - i, 0)"),
+    ("S = gamma * S + np.outer(V[t], K[t])", "S = gamma * S + np.outer(K[t], V[t])"),
+]
+
+GD_MUTATIONS = [
+    ("S = alpha[t] * S @ (I - beta[t]", "S = S @ (I - beta[t]"),
+    ("(I - beta[t] * np.outer(k, k))", "(I + beta[t] * np.outer(k, k))"),
+    ("beta[t] * np.outer(V[t], k)", "beta[t] * np.outer(k, V[t])"),
+    ("L = np.tril(bc[:, None] * Gamma * (Kc @ Kc.T), k=-1)",
+     "L = np.tril(bc[:, None] * Gamma * (Kc @ Kc.T), k=0)"),
+    ("L = np.tril(bc[:, None] * Gamma", "L = np.tril(Gamma"),
+    ("W = Tm @ ((bc * np.exp(g))[:, None] * Kc)", "W = Tm @ (bc[:, None] * Kc)"),
+    ("A = np.tril((Qc @ Kc.T) * Gamma)", "A = np.tril((Qc @ Kc.T) * Gamma, k=-1)"),
+    ("U = Ut - W @ S.T", "U = Ut + W @ S.T"),
+    ("S = np.exp(g[-1]) * S + U.T", "S = S + U.T"),
+    ("np.exp(g[-1] - g)[:, None] * Kc)", "np.exp(g - g[-1])[:, None] * Kc)"),
+    ("Gamma = np.exp(g[:, None] - g[None, :])", "Gamma = np.exp(g[None, :] - g[:, None])"),
+    ("O[a:b] = np.exp(g)[:, None] * (Qc @ S.T) + A @ U", "O[a:b] = (Qc @ S.T) + A @ U"),
+]
+
+
+def _fails_some_pin(ns, pins):
+    for pin in pins:
+        try:
+            with np.errstate(all="ignore"):
+                pin(ns)
+        except (AssertionError, ValueError, FloatingPointError, np.linalg.LinAlgError):
+            return True
+    return False
+
+
+def test_genuine_oracle_passes_all_pins_via_namespace():
+    assert not _fails_some_pin(_namespace(), LA_PINS + GDN_PINS)
+
+
+@pytest.mark.parametrize("old,new", LA_MUTATIONS, ids=[m[1][:40] for m in LA_MUTATIONS])
+def test_planted_la_mistake_is_caught(old, new):
+    assert _fails_some_pin(_namespace(la_ns=_mutant(la_mod, old, new)), LA_PINS + GDN_PINS)
+
+
+@pytest.mark.parametrize("old,new", GD_MUTATIONS, ids=[m[1][:40] for m in GD_MUTATIONS])
+def test_planted_gdn_mistake_is_caught(old, new):
+    assert _fails_some_pin(_namespace(gd_ns=_mutant(gd_mod, old, new)), GDN_PINS)
