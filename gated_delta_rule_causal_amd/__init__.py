@@ -1,0 +1,229 @@
+"""Python binding of liblinattn.so (causal linear attention and the gated
+delta rule on MI355X / gfx950).
+
+Argument marshalling only: tensors are allocated by PyTorch (device memory
+and streams are all torch is used for) and passed to the C ABI as raw device
+pointers together with the current HIP stream.  Every step of the computation
+runs in the HIP kernels of liblinattn.so; there is no fallback of any kind.
+If the library has not been built, importing the binding functions raises.
+
+Layouts (row-major, contiguous): q, k [B,H,T,dk]; v, o [B,H,T,dv];
+alpha, beta [B,H,T] float32; S [B,H,dv,dk] float32; z [B,H,dk] float32.
+q, k, v are float32 or bfloat16 (all three the same).
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "lin_attn_prefill",
+    "gdn_prefill",
+    "lin_attn_decode_step",
+    "la_workspace_bytes",
+    "la_status_str",
+    "la_abi_version",
+    "library_path",
+    "LinAttnError",
+    "FORMS",
+    "KINDS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_F32, LA_BF16 = 0, 1
+FORMS = {"chunked": 0, "recurrent": 1, "parallel": 2}
+KINDS = {"normalized": 0, "gated_delta": 1}
+FNS = {"lin_attn_prefill": 0, "gdn_prefill": 1, "decode_step": 2}
+
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {la_status_str(status)} (status {status})")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -m gated_delta_rule_causal_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.lin_attn_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, Z, P]
+    lib.lin_attn_prefill.restype = I
+    lib.gdn_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, Z, P]
+    lib.gdn_prefill.restype = I
+    lib.lin_attn_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+    lib.lin_attn_decode_step.restype = I
+    lib.la_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
+    lib.la_workspace_bytes.restype = Z
+    lib.la_status_str.argtypes = [I]
+    lib.la_status_str.restype = ctypes.c_char_p
+    lib.la_abi_version.argtypes = []
+    lib.la_abi_version.restype = I
+    _lib = lib
+    return lib
+
+
+def la_status_str(status):
+    return _load().la_status_str(int(status)).decode()
+
+
+def la_abi_version():
+    return int(_load().la_abi_version())
+
+
+def la_workspace_bytes(fn, dtype, B, H, T, dk, dv, form="chunked", chunk=64):
+    fn_i = FNS[fn] if isinstance(fn, str) else int(fn)
+    form_i = FORMS[form] if isinstance(form, str) else int(form)
+    dt = _dtype_code(dtype) if not isinstance(dtype, int) else dtype
+    n = _load().la_workspace_bytes(fn_i, dt, B, H, T, dk, dv, form_i, chunk)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("la_workspace_bytes: invalid or unsupported arguments")
+    return int(n)
+
+
+# ---------------------------------------------------------------- helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.float32 or dt == "f32":
+        return LA_F32
+    if dt == torch.bfloat16 or dt == "bf16":
+        return LA_BF16
+    raise TypeError(f"unsupported activation dtype {dt}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _workspace(fn, dt, B, H, T, dk, dv, form, chunk, workspace, device):
+    torch = _torch()
+    need = la_workspace_bytes(fn, dt, B, H, T, dk, dv, form, chunk)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# ------------------------------------------------------------ entry points
+def lin_attn_prefill(q, k, v, S0=None, z0=None, form="chunked", chunk=64, out=None,
+                     S_out=None, z_out=None, want_state=True, workspace=None, stream=None):
+    """Normalised causal linear attention; returns (o, S_out, z_out).
+
+    ``S_out``/``z_out`` may be passed explicitly (``S_out is S0`` updates in
+    place); otherwise they are allocated when ``want_state``.
+    """
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    _check(z0, "z0", torch.float32, (B, H, dk))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (B, H, T, dv))
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if want_state and z_out is None:
+        z_out = torch.empty((B, H, dk), dtype=torch.float32, device=q.device)
+    _check(S_out, "S_out", torch.float32, (B, H, dv, dk))
+    _check(z_out, "z_out", torch.float32, (B, H, dk))
+    ws, ws_bytes = _workspace("lin_attn_prefill", dt, B, H, T, dk, dv, form, chunk, workspace, q.device)
+    st = _load().lin_attn_prefill(dt, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0),
+                                  _ptr(out), _ptr(S_out), _ptr(z_out), FORMS[form], chunk, _ptr(ws),
+                                  ws_bytes, _stream_ptr(stream, q.device))
+    if st != 0:
+        raise LinAttnError(st, "lin_attn_prefill")
+    return out, S_out, z_out
+
+
+def gdn_prefill(q, k, v, alpha, beta, S0=None, form="chunked", chunk=64, out=None, S_out=None,
+                want_state=True, workspace=None, stream=None):
+    """Gated delta rule over T tokens; returns (o, S_out)."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(alpha, "alpha", torch.float32, (B, H, T))
+    _check(beta, "beta", torch.float32, (B, H, T))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (B, H, T, dv))
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(S_out, "S_out", torch.float32, (B, H, dv, dk))
+    ws, ws_bytes = _workspace("gdn_prefill", dt, B, H, T, dk, dv, form, chunk, workspace, q.device)
+    st = _load().gdn_prefill(dt, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                             _ptr(S0), _ptr(out), _ptr(S_out), FORMS[form], chunk, _ptr(ws), ws_bytes,
+                             _stream_ptr(stream, q.device))
+    if st != 0:
+        raise LinAttnError(st, "gdn_prefill")
+    return out, S_out
+
+
+def lin_attn_decode_step(kind, q, k, v, S, z=None, alpha=None, beta=None, out=None, stream=None):
+    """One decode step for [N,H] heads, updating S (and z) in place; returns o."""
+    torch = _torch()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    kind_i = KINDS[kind] if isinstance(kind, str) else int(kind)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (N, H, dk))
+    _check(v, "v", q.dtype, (N, H, dv))
+    _check(S, "S", torch.float32, (N, H, dv, dk))
+    _check(z, "z", torch.float32, (N, H, dk))
+    _check(alpha, "alpha", torch.float32, (N, H))
+    _check(beta, "beta", torch.float32, (N, H))
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (N, H, dv))
+    st = _load().lin_attn_decode_step(kind_i, dt, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                      _ptr(beta), _ptr(S), _ptr(z), _ptr(out),
+                                      _stream_ptr(stream, q.device))
+    if st != 0:
+        raise LinAttnError(st, "lin_attn_decode_step")
+    return out

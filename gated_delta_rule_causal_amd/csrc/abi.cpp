@@ -1,0 +1,265 @@
+// C ABI of liblinattn.so: host-side validation and dispatch to the gfx950
+// kernels.  The public contract (argument meaning, layouts, ownership, error
+// behaviour) is documented in include/linattn.h.
+#include "linattn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kParallelMaxT = 8192;
+
+bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Sizes: all element counts are computed in 64 bits; the bound keeps every
+// per-tensor byte count far below 2^63 and every head index within a grid
+// dimension.
+bool sizes_ok(long long B, long long H, long long T) {
+    if (B < 0 || H < 0 || T < 0) return false;
+    if (B * H > 0x7fffffffLL) return false;
+    if (T > (1LL << 30)) return false;
+    return B * H * T <= (1LL << 40);
+}
+
+size_t io_size(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+la_status from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+// Copy S0 -> S_out (zero-fill when S0 is NULL) for empty sequences.
+__global__ void state_copy_kernel(const float* src, float* dst, size_t n) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+la_status copy_state(const float* src, float* dst, size_t n, hipStream_t s) {
+    if (dst == nullptr || n == 0 || src == dst) return LA_OK;
+    const unsigned blocks = static_cast<unsigned>((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(state_copy_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n);
+    return from_hip(hipGetLastError());
+}
+
+size_t la_prefill_ws(int dtype, int B, int H, int T, int dk, int dv, int form, int chunk) {
+    if (form == LA_FORM_CHUNKED && la::la_mfma_supported(dtype, dk, dv, chunk))
+        return la::la_mfma_workspace_bytes(B, H, T, dk, dv, chunk);
+    return 0;
+}
+
+size_t gdn_prefill_ws(int dtype, int B, int H, int T, int dk, int dv, int form, int chunk) {
+    if (form == LA_FORM_CHUNKED && la::gdn_mfma_supported(dtype, dk, dv, chunk))
+        return la::gdn_mfma_workspace_bytes(B, H, T, dk, dv, chunk);
+    return 0;
+}
+
+// Which kernel family a chunked call uses; -1 when none fits.
+int la_chunked_path(int dtype, int dk, int dv, int chunk) {
+    if (la::la_mfma_supported(dtype, dk, dv, chunk)) return 1;
+    if (la::la_chunked_generic_lds_bytes(dk, dv, chunk) <= kMaxLds) return 0;
+    return -1;
+}
+int gdn_chunked_path(int dtype, int dk, int dv, int chunk) {
+    if (la::gdn_mfma_supported(dtype, dk, dv, chunk)) return 1;
+    if (la::gdn_chunked_generic_lds_bytes(dk, dv, chunk) <= kMaxLds) return 0;
+    return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+const char* la_status_str(la_status s) {
+    switch (s) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_NULL: return "LA_ERR_NULL: a required pointer is NULL";
+        case LA_ERR_SHAPE: return "LA_ERR_SHAPE: a size is negative, unsupported or too large";
+        case LA_ERR_DTYPE: return "LA_ERR_DTYPE: dtype must be LA_F32 or LA_BF16";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: valid arguments, combination not implemented";
+        case LA_ERR_ALIGN: return "LA_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
+        case LA_ERR_HIP: return "LA_ERR_HIP: the HIP runtime reported an error";
+        case LA_ERR_ARG: return "LA_ERR_ARG: bad enum value or overlapping buffers";
+        default: return "unknown la_status";
+    }
+}
+
+size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv, int form, int chunk) {
+    const size_t bad = static_cast<size_t>(-1);
+    if (dtype != LA_F32 && dtype != LA_BF16) return bad;
+    if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return bad;
+    if (fn == LA_FN_DECODE_STEP) return 0;  // form and chunk do not apply
+    if (form == LA_FORM_CHUNKED && !valid_chunk(chunk)) return bad;
+    switch (fn) {
+        case LA_FN_LIN_ATTN_PREFILL:
+            if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT && form != LA_FORM_PARALLEL) return bad;
+            if (form == LA_FORM_CHUNKED && la_chunked_path(dtype, dk, dv, chunk) < 0) return bad;
+            return la_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
+        case LA_FN_GDN_PREFILL:
+            if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
+            if (form == LA_FORM_CHUNKED && gdn_chunked_path(dtype, dk, dv, chunk) < 0) return bad;
+            return gdn_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
+        default:
+            return bad;
+    }
+}
+
+la_status lin_attn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q,
+                           const void* k, const void* v, const float* S0, const float* z0, void* o,
+                           float* S_out, float* z_out, int form, int chunk, void* workspace,
+                           size_t ws_bytes, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT && form != LA_FORM_PARALLEL) return LA_ERR_ARG;
+    if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (form == LA_FORM_CHUNKED && !valid_chunk(chunk)) return LA_ERR_SHAPE;
+    if (form == LA_FORM_PARALLEL && T > kParallelMaxT) return LA_ERR_SHAPE;
+    const size_t heads = static_cast<size_t>(B) * H;
+    if (heads == 0) return LA_OK;
+    const size_t es = io_size(dtype);
+    const size_t nqk = heads * T * dk * es, nv = heads * T * dv * es;
+    const size_t nS = heads * dv * dk * sizeof(float), nz = heads * dk * sizeof(float);
+    if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr)) return LA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(S0),
+                          static_cast<const void*>(z0), static_cast<const void*>(S_out),
+                          static_cast<const void*>(z_out), static_cast<const void*>(workspace)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    if (form == LA_FORM_PARALLEL && (S0 != nullptr || z0 != nullptr)) return LA_ERR_ARG;
+    // outputs must not overlap inputs, except the documented in-place states
+    const Span in[] = {{q, nqk}, {k, nqk}, {v, nv}, {S0, nS}, {z0, nz}};
+    const Span outs[] = {{o, T > 0 ? nv : 0}, {S_out, nS}, {z_out, nz}};
+    for (const Span& a : outs)
+        for (const Span& b : in) {
+            if ((a.p == S_out && b.p == S0 && S_out == S0) || (a.p == z_out && b.p == z0 && z_out == z0)) continue;
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        }
+    if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return LA_ERR_ARG;
+    int path = 0;
+    if (form == LA_FORM_CHUNKED) {
+        path = la_chunked_path(dtype, dk, dv, chunk);
+        if (path < 0) return LA_ERR_UNSUPPORTED;
+    }
+    const size_t need = la_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        la_status st = copy_state(S0, S_out, heads * dv * dk, s);
+        if (st != LA_OK) return st;
+        return copy_state(z0, z_out, heads * dk, s);
+    }
+    const int nh = static_cast<int>(heads);
+    switch (form) {
+        case LA_FORM_PARALLEL:
+            return from_hip(la::launch_la_parallel(dtype, nh, T, dk, dv, q, k, v, o, S_out, z_out, s));
+        case LA_FORM_RECURRENT:
+            return from_hip(la::launch_recurrent(la::kNormalized, dtype, nh, T, dk, dv, q, k, v, nullptr,
+                                                 nullptr, S0, S_out, z0, z_out, o, s));
+        default:
+            if (path == 1)
+                return from_hip(la::launch_la_mfma(B, H, T, q, k, v, S0, z0, o, S_out, z_out, workspace, s));
+            return from_hip(la::launch_la_chunked_generic(dtype, nh, T, dk, dv, chunk, q, k, v, S0, z0, o,
+                                                          S_out, z_out, s));
+    }
+}
+
+la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, const float* S0, void* o,
+                      float* S_out, int form, int chunk, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return LA_ERR_ARG;
+    if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (form == LA_FORM_CHUNKED && !valid_chunk(chunk)) return LA_ERR_SHAPE;
+    const size_t heads = static_cast<size_t>(B) * H;
+    if (heads == 0) return LA_OK;
+    const size_t es = io_size(dtype);
+    const size_t nqk = heads * T * dk * es, nv = heads * T * dv * es, ng = heads * T * sizeof(float);
+    const size_t nS = heads * dv * dk * sizeof(float);
+    if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr || alpha == nullptr ||
+                  beta == nullptr))
+        return LA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(alpha),
+                          static_cast<const void*>(beta), static_cast<const void*>(S0),
+                          static_cast<const void*>(S_out), static_cast<const void*>(workspace)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {{q, nqk}, {k, nqk}, {v, nv}, {alpha, ng}, {beta, ng}, {S0, nS}};
+    const Span outs[] = {{o, T > 0 ? nv : 0}, {S_out, nS}};
+    for (const Span& a : outs)
+        for (const Span& b : in) {
+            if (a.p == S_out && b.p == S0 && S_out == S0) continue;
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        }
+    if (overlaps(outs[0], outs[1])) return LA_ERR_ARG;
+    int path = 0;
+    if (form == LA_FORM_CHUNKED) {
+        path = gdn_chunked_path(dtype, dk, dv, chunk);
+        if (path < 0) return LA_ERR_UNSUPPORTED;
+    }
+    const size_t need = gdn_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
+    if (need > 0 && overlaps({workspace, need}, outs[0])) return LA_ERR_ARG;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) return copy_state(S0, S_out, heads * dv * dk, s);
+    const int nh = static_cast<int>(heads);
+    if (form == LA_FORM_RECURRENT)
+        return from_hip(la::launch_recurrent(la::kGatedDelta, dtype, nh, T, dk, dv, q, k, v, alpha, beta,
+                                             S0, S_out, nullptr, nullptr, o, s));
+    if (path == 1)
+        return from_hip(la::launch_gdn_mfma(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, s));
+    return from_hip(la::launch_gdn_chunked_generic(dtype, nh, T, dk, dv, chunk, q, k, v, alpha, beta, S0,
+                                                   o, S_out, s));
+}
+
+la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv, const void* q,
+                               const void* k, const void* v, const float* alpha, const float* beta,
+                               float* S, float* z, void* o, void* stream) {
+    if (kind != LA_KIND_NORMALIZED && kind != LA_KIND_GATED_DELTA) return LA_ERR_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (!sizes_ok(N, H, 1) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    const size_t heads = static_cast<size_t>(N) * H;
+    if (heads == 0) return LA_OK;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || S == nullptr) return LA_ERR_NULL;
+    if (kind == LA_KIND_GATED_DELTA) {
+        if (alpha == nullptr || beta == nullptr) return LA_ERR_NULL;
+        if (z != nullptr) return LA_ERR_ARG;
+    } else {
+        if (z == nullptr) return LA_ERR_NULL;
+        if (alpha != nullptr || beta != nullptr) return LA_ERR_ARG;
+    }
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(alpha),
+                          static_cast<const void*>(beta), static_cast<const void*>(S),
+                          static_cast<const void*>(z)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const size_t es = io_size(dtype);
+    const Span outs[] = {{o, heads * dv * es}, {S, heads * dv * dk * sizeof(float)}, {z, heads * dk * sizeof(float)}};
+    const Span in[] = {{q, heads * dk * es}, {k, heads * dk * es}, {v, heads * dv * es},
+                       {alpha, heads * sizeof(float)}, {beta, heads * sizeof(float)}};
+    for (const Span& a : outs)
+        for (const Span& b : in)
+            if (overlaps(a, b)) return LA_ERR_ARG;
+    if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return LA_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int k_kind = kind == LA_KIND_GATED_DELTA ? la::kGatedDelta : la::kNormalized;
+    return from_hip(la::launch_recurrent(k_kind, dtype, static_cast<int>(heads), 1, dk, dv, q, k, v, alpha,
+                                         beta, S, S, z, z, o, s));
+}
+
+}  // extern "C"

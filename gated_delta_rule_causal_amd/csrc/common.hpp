@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 conversion, vector
+// loads, wave-level reductions, and thin wrappers over the CDNA4 matrix-core
+// (MFMA) builtins with the operand/accumulator lane layouts written down.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 / I/O
+__device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round-to-nearest-even float -> bf16 (gfx950 has a native convert; clang
+// lowers the __bf16 cast to it).
+__device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }
+__device__ __forceinline__ u16 f32_to_bf16_bits(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(u16, h);
+}
+
+// Activation element type tags.
+struct IoF32 {
+    using T = float;
+    static __device__ __forceinline__ float load(const T* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(T* p, size_t i, float x) { p[i] = x; }
+    // 4 consecutive elements (p + i must be 16-byte aligned for fp32)
+    static __device__ __forceinline__ void load4(const T* p, size_t i, float* out) {
+        float4 v = *reinterpret_cast<const float4*>(p + i);
+        out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    }
+};
+struct IoBF16 {
+    using T = u16;
+    static __device__ __forceinline__ float load(const T* p, size_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(T* p, size_t i, float x) { p[i] = f32_to_bf16_bits(x); }
+    // 4 consecutive elements (p + i must be 8-byte aligned)
+    static __device__ __forceinline__ void load4(const T* p, size_t i, float* out) {
+        uint2 v = *reinterpret_cast<const uint2*>(p + i);
+        out[0] = __uint_as_float(v.x << 16);
+        out[1] = __uint_as_float(v.x & 0xffff0000u);
+        out[2] = __uint_as_float(v.y << 16);
+        out[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+};
+
+// ------------------------------------------------------------ feature map
+// elu(x) + 1: x + 1 for x > 0, exp(x) otherwise; always positive.
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// --------------------------------------------------------- wave reductions
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
+// every lane of the group receives the group sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// ------------------------------------------------------------------ MFMA
+// v_mfma_f32_16x16x32_bf16: D(16x16) += A(16x32) * B(32x16), fp32 accumulate.
+// Lane l (0..63), with r = l % 16 and g = l / 16 (0..3):
+//   A operand: 8 bf16 = A[row r][k = 8g .. 8g+7]
+//   B operand: 8 bf16 = B[k = 8g .. 8g+7][col r]
+//   C/D      : 4 fp32 = D[row 4g + i][col r], i = 0..3
+// Any permutation of the K index applied identically to A and B leaves the
+// product unchanged; the kernels use that to feed an accumulator tile back in
+// as the B operand of the next product without moving data between lanes.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(float x0, float x1, float x2, float x3, float x4, float x5,
+                                        float x6, float x7) {
+    bf16x8 r;
+    r[0] = f32_to_bf16(x0); r[1] = f32_to_bf16(x1); r[2] = f32_to_bf16(x2); r[3] = f32_to_bf16(x3);
+    r[4] = f32_to_bf16(x4); r[5] = f32_to_bf16(x5); r[6] = f32_to_bf16(x6); r[7] = f32_to_bf16(x7);
+    return r;
+}
+// Two accumulator tiles (4 values each) as one K=32 B/A operand in the
+// permuted-K order: slots 0..3 from tile `lo`, slots 4..7 from tile `hi`.
+__device__ __forceinline__ bf16x8 pack_acc_pair(f32x4 lo, f32x4 hi) {
+    return pack8(lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace la

@@ -1,0 +1,60 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernel
+// translation units.  Not part of the public ABI.  Every launcher enqueues on
+// `stream`, checks nothing (abi.cpp validated the arguments) and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace la {
+
+enum Kind { kNormalized = 0, kGatedDelta = 1 };
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+// ---- token-by-token recurrence, one block per head (recurrent.hip) --------
+// heads = B*H (or N*H for a decode step); T >= 1.  q,k [heads,T,dk];
+// v,o [heads,T,dv]; alpha,beta [heads,T] (gated delta only); S0/S_out
+// [heads,dv,dk] (may alias); z0/z_out [heads,dk] (normalized only, may alias).
+hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int dv,
+                            const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta,
+                            const float* S0, float* S_out, const float* z0, float* z_out,
+                            void* o, hipStream_t stream);
+
+// ---- normalised linear attention, masked parallel form (la_parallel.hip) -
+hipError_t launch_la_parallel(int dtype, int heads, int T, int dk, int dv,
+                              const void* q, const void* k, const void* v, void* o,
+                              float* S_out, float* z_out, hipStream_t stream);
+
+// ---- chunked forms with fp32 arithmetic on the vector ALUs (chunked_generic.hip)
+// One block per head; state and the current chunk live in LDS.
+size_t la_chunked_generic_lds_bytes(int dk, int dv, int chunk);
+hipError_t launch_la_chunked_generic(int dtype, int heads, int T, int dk, int dv, int chunk,
+                                     const void* q, const void* k, const void* v,
+                                     const float* S0, const float* z0, void* o,
+                                     float* S_out, float* z_out, hipStream_t stream);
+size_t gdn_chunked_generic_lds_bytes(int dk, int dv, int chunk);
+hipError_t launch_gdn_chunked_generic(int dtype, int heads, int T, int dk, int dv, int chunk,
+                                      const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const float* S0, void* o, float* S_out, hipStream_t stream);
+
+// ---- bf16 matrix-core paths (dk = dv = 128, chunk = 64) -------------------
+// Gated delta: per-chunk state-independent pass (gdn_prep.hip) then the
+// sequential inter-chunk scan (gdn_scan.hip).  Workspace layout is private
+// to those two files; gdn_mfma_workspace_bytes sizes it.
+bool gdn_mfma_supported(int dtype, int dk, int dv, int chunk);
+size_t gdn_mfma_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+hipError_t launch_gdn_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* S0,
+                           void* o, float* S_out, void* workspace, hipStream_t stream);
+
+// Normalised linear attention, chunked, bf16 in/out (la_mfma.hip).
+bool la_mfma_supported(int dtype, int dk, int dv, int chunk);
+size_t la_mfma_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
+                          const float* S0, const float* z0, void* o, float* S_out, float* z_out,
+                          void* workspace, hipStream_t stream);
+
+}  // namespace la

@@ -1,0 +1,241 @@
+// Token-by-token recurrence with the state held in registers.
+//
+// One kernel template serves both kinds of recurrence on the page "Linear
+// attention and hybrids":
+//   * kGatedDelta - section "Delta rule and Gated DeltaNet", Gated DeltaNet
+//     equation: S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+//     o_t = S_t q_t.  Expanded per state row s_i (value channel i):
+//       u = s_i.k,  p = s_i.q,  c = beta (v_i - alpha u),
+//       s_i <- alpha s_i + c k,   o_i = alpha p + c (k.q)
+//     so each row is read once and written once per token.
+//   * kNormalized - section "Three forms of one computation", recurrent form:
+//       s_i <- s_i + v_i phi(k),  z <- z + phi(k),  o_i = s_i.phi(q) / z.phi(q)
+// With T = 1 it is the decode step (the state streams from HBM and back,
+// in place); with T > 1 it is the recurrent prefill form.
+//
+// Rows of S evolve independently (each new row depends only on the same old
+// row and the token), so a block owns one head and splits its rows over
+// lane groups: LPR = dk/8 lanes per row, 8 fp32 state elements per lane held
+// as two float4 (columns [4l, 4l+4) and [dk/2 + 4l, dk/2 + 4l + 4) for lane l
+// of the group, so one load instruction covers 256 contiguous bytes of a row).
+// Dot products reduce over the LPR lanes with xor-shuffles.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace la {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int DK>
+struct RowSlice {
+    static constexpr int LPR = DK / 8;
+    static constexpr int RG = kThreads / LPR;  // row groups per block
+};
+
+template <class IO>
+__device__ __forceinline__ void load_slice(const typename IO::T* p, size_t base, int c0, int c1,
+                                           float* out) {
+    IO::load4(p, base + c0, out);
+    IO::load4(p, base + c1, out + 4);
+}
+
+template <int KIND, class IO, int DK, int R>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(
+    int T, int DV, const typename IO::T* __restrict__ q, const typename IO::T* __restrict__ k,
+    const typename IO::T* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const float* S0, float* S_out, const float* z0, float* z_out,
+    typename IO::T* __restrict__ o) {
+    constexpr int LPR = RowSlice<DK>::LPR;
+    constexpr int RG = RowSlice<DK>::RG;
+    const int head = blockIdx.x;
+    const int li = threadIdx.x % LPR;
+    const int rg = threadIdx.x / LPR;
+    const int c0 = 4 * li;
+    const int c1 = DK / 2 + 4 * li;
+    const size_t sbase = static_cast<size_t>(head) * DV * DK;
+
+    // ---- carried state: R rows per lane group, 8 columns per lane
+    float s[R][8];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int r = rg + RG * j;
+        if (S0 != nullptr && r < DV) {
+            const float4 a = *reinterpret_cast<const float4*>(S0 + sbase + static_cast<size_t>(r) * DK + c0);
+            const float4 b = *reinterpret_cast<const float4*>(S0 + sbase + static_cast<size_t>(r) * DK + c1);
+            s[j][0] = a.x; s[j][1] = a.y; s[j][2] = a.z; s[j][3] = a.w;
+            s[j][4] = b.x; s[j][5] = b.y; s[j][6] = b.z; s[j][7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
+        }
+    }
+    float z[8];
+    if constexpr (KIND == kNormalized) {
+        const size_t zb = static_cast<size_t>(head) * DK;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = 0.f;
+        if (z0 != nullptr) {
+            const float4 a = *reinterpret_cast<const float4*>(z0 + zb + c0);
+            const float4 b = *reinterpret_cast<const float4*>(z0 + zb + c1);
+            z[0] = a.x; z[1] = a.y; z[2] = a.z; z[3] = a.w;
+            z[4] = b.x; z[5] = b.y; z[6] = b.z; z[7] = b.w;
+        }
+    }
+
+    // ---- token inputs, prefetched one token ahead
+    float kn[8], qn[8], vn[R], an = 1.f, bn = 0.f;
+    auto fetch = [&](int t) {
+        const size_t tk = (static_cast<size_t>(head) * T + t) * DK;
+        const size_t tv = (static_cast<size_t>(head) * T + t) * DV;
+        load_slice<IO>(k, tk, c0, c1, kn);
+        load_slice<IO>(q, tk, c0, c1, qn);
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int r = rg + RG * j;
+            vn[j] = r < DV ? IO::load(v, tv + r) : 0.f;
+        }
+        if constexpr (KIND == kGatedDelta) {
+            an = alpha[static_cast<size_t>(head) * T + t];
+            bn = beta[static_cast<size_t>(head) * T + t];
+        }
+    };
+    fetch(0);
+
+    for (int t = 0; t < T; ++t) {
+        float kc[8], qc[8], vc[R];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kc[e] = kn[e]; qc[e] = qn[e]; }
+#pragma unroll
+        for (int j = 0; j < R; ++j) vc[j] = vn[j];
+        const float a = an, b = bn;
+        if (t + 1 < T) fetch(t + 1);
+        const size_t to = (static_cast<size_t>(head) * T + t) * DV;
+
+        if constexpr (KIND == kGatedDelta) {
+            float kq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kq = fmaf(kc[e], qc[e], kq);
+            kq = group_sum<LPR>(kq);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float u = 0.f, p = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    u = fmaf(s[j][e], kc[e], u);
+                    p = fmaf(s[j][e], qc[e], p);
+                }
+                u = group_sum<LPR>(u);
+                p = group_sum<LPR>(p);
+                const float c = b * (vc[j] - a * u);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[j][e] = fmaf(a, s[j][e], c * kc[e]);
+                const int r = rg + RG * j;
+                if (li == 0 && r < DV) IO::store(o, to + r, fmaf(a, p, c * kq));
+            }
+        } else {
+            float fk[8], fq[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { fk[e] = phi(kc[e]); fq[e] = phi(qc[e]); }
+            float den = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                z[e] += fk[e];
+                den = fmaf(z[e], fq[e], den);
+            }
+            den = group_sum<LPR>(den);
+            const float rden = 1.f / den;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float num = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    s[j][e] = fmaf(vc[j], fk[e], s[j][e]);
+                    num = fmaf(s[j][e], fq[e], num);
+                }
+                num = group_sum<LPR>(num);
+                const int r = rg + RG * j;
+                if (li == 0 && r < DV) IO::store(o, to + r, num * rden);
+            }
+        }
+    }
+
+    // ---- write back the state (same lanes that read it: in-place safe)
+    if (S_out != nullptr) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int r = rg + RG * j;
+            if (r < DV) {
+                float* row = S_out + sbase + static_cast<size_t>(r) * DK;
+                *reinterpret_cast<float4*>(row + c0) = make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+                *reinterpret_cast<float4*>(row + c1) = make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
+            }
+        }
+    }
+    if constexpr (KIND == kNormalized) {
+        if (z_out != nullptr) {
+            __syncthreads();  // every lane group has read z0 before it is overwritten
+            if (rg == 0) {
+                float* zp = z_out + static_cast<size_t>(head) * DK;
+                *reinterpret_cast<float4*>(zp + c0) = make_float4(z[0], z[1], z[2], z[3]);
+                *reinterpret_cast<float4*>(zp + c1) = make_float4(z[4], z[5], z[6], z[7]);
+            }
+        }
+    }
+}
+
+template <int KIND, class IO, int DK>
+hipError_t launch_dk(int heads, int T, int dv, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const float* S0, float* S_out,
+                     const float* z0, float* z_out, void* o, hipStream_t stream) {
+    using E = typename IO::T;
+    constexpr int RG = RowSlice<DK>::RG;
+    const int R = (dv + RG - 1) / RG;
+    dim3 grid(heads), block(kThreads);
+    auto args = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, T, dv, static_cast<const E*>(q),
+                           static_cast<const E*>(k), static_cast<const E*>(v), alpha, beta, S0,
+                           S_out, z0, z_out, static_cast<E*>(o));
+        return hipGetLastError();
+    };
+    switch (R) {
+        case 1: return args(recurrent_kernel<KIND, IO, DK, 1>);
+        case 2: return args(recurrent_kernel<KIND, IO, DK, 2>);
+        case 4: return args(recurrent_kernel<KIND, IO, DK, 4>);
+        case 8: return args(recurrent_kernel<KIND, IO, DK, 8>);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int KIND, class IO>
+hipError_t launch_io(int heads, int T, int dk, int dv, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const float* S0, float* S_out,
+                     const float* z0, float* z_out, void* o, hipStream_t stream) {
+    switch (dk) {
+        case 16: return launch_dk<KIND, IO, 16>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
+        case 32: return launch_dk<KIND, IO, 32>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
+        case 64: return launch_dk<KIND, IO, 64>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
+        case 128: return launch_dk<KIND, IO, 128>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int dv, const void* q,
+                            const void* k, const void* v, const float* alpha, const float* beta,
+                            const float* S0, float* S_out, const float* z0, float* z_out, void* o,
+                            hipStream_t stream) {
+    if (heads <= 0 || T <= 0) return hipSuccess;
+    if (kind == kGatedDelta) {
+        return dtype == kBF16
+                   ? launch_io<kGatedDelta, IoBF16>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream)
+                   : launch_io<kGatedDelta, IoF32>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream);
+    }
+    return dtype == kBF16
+               ? launch_io<kNormalized, IoBF16>(heads, T, dk, dv, q, k, v, nullptr, nullptr, S0, S_out, z0, z_out, o, stream)
+               : launch_io<kNormalized, IoF32>(heads, T, dk, dv, q, k, v, nullptr, nullptr, S0, S_out, z0, z_out, o, stream);
+}
+
+}  // namespace la

@@ -1,0 +1,156 @@
+/*
+ * linattn.h - C ABI of liblinattn.so: causal linear attention and the gated
+ * delta rule on AMD Instinct MI355X (gfx950).
+ *
+ * Operations are defined on the page "Linear attention and hybrids"
+ * (ai.flicky.cc, stage 5, module 5.5, lesson 03); each entry point below names
+ * the section and equation it computes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or keeps device memory, and keeps no
+ *    mutable global state; calls on different streams are independent.
+ *  - Tensors are dense row-major (C order) with the shapes given, and every
+ *    pointer must be 16-byte aligned.
+ *  - Activations (q, k, v, o) are float32 (LA_F32) or bfloat16 (LA_BF16), as
+ *    chosen by `dtype`.  Gates (alpha, beta), states (S, z) and all
+ *    accumulation are float32 whatever `dtype` is.
+ *  - Layouts: q, k [B,H,T,dk]; v, o [B,H,T,dv]; alpha, beta [B,H,T];
+ *    S [B,H,dv,dk] (row i of S belongs to value channel i); z [B,H,dk].
+ *  - No 1/sqrt(d) scale is applied anywhere (the equations have none).
+ *  - Arguments are validated on the host before anything is enqueued.  On an
+ *    error nothing is launched and no output is written.  Work is enqueued
+ *    asynchronously on `stream` (a hipStream_t passed as void*; NULL is the
+ *    null stream); there is no host synchronisation.  A launch failure
+ *    returns LA_ERR_HIP; faults inside kernels surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  - Results are deterministic: two identical calls give bitwise-equal
+ *    outputs (no atomics in any reduction).
+ *  - Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64, 128};
+ *    B, H, N >= 0 and T >= 0 (a zero-sized call copies the carried state to
+ *    the output state and returns LA_OK).  Combinations that are valid but
+ *    not implemented return LA_ERR_UNSUPPORTED.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef int la_status;
+
+enum {
+    LA_OK = 0,
+    LA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    LA_ERR_SHAPE = 2,       /* a size is negative, out of range or too large      */
+    LA_ERR_DTYPE = 3,       /* dtype is not LA_F32 / LA_BF16                      */
+    LA_ERR_UNSUPPORTED = 4, /* valid arguments, combination not implemented       */
+    LA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                   */
+    LA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required         */
+    LA_ERR_HIP = 7,         /* the HIP runtime reported an error                  */
+    LA_ERR_ARG = 8          /* bad enum value (form, kind, fn) or overlap         */
+};
+
+enum { LA_F32 = 0, LA_BF16 = 1 };
+enum { LA_FORM_CHUNKED = 0, LA_FORM_RECURRENT = 1, LA_FORM_PARALLEL = 2 };
+enum { LA_KIND_NORMALIZED = 0, LA_KIND_GATED_DELTA = 1 };
+enum { LA_FN_LIN_ATTN_PREFILL = 0, LA_FN_GDN_PREFILL = 1, LA_FN_DECODE_STEP = 2 };
+
+/*
+ * lin_attn_prefill - normalised causal linear attention over T tokens.
+ *
+ * Computes, per head and token t (section "The kernel trick: removing
+ * softmax", the rewritten o_i equation; section "Three forms of one
+ * computation", recurrent form):
+ *     phi(x) = x + 1 for x > 0, exp(x) otherwise (elu + 1)
+ *     S_t = S_{t-1} + v_t phi(k_t)^T,  z_t = z_{t-1} + phi(k_t)
+ *     o_t = S_t phi(q_t) / (z_t . phi(q_t))        (token t included)
+ * with S_0 = S0 and z_0 = z0 (zeros when NULL).  `form` picks how it is
+ * evaluated (same section: masked parallel form, recurrent form, or the
+ * chunked form with block size `chunk`, the last block possibly shorter):
+ *   LA_FORM_PARALLEL  - masked T x T form; S0 and z0 must be NULL; T <= 8192.
+ *   LA_FORM_RECURRENT - token by token, state in registers.
+ *   LA_FORM_CHUNKED   - block-parallel form; `chunk` is the block size.
+ * Outputs: o [B,H,T,dv]; S_out [B,H,dv,dk] and z_out [B,H,dk] receive the
+ * final state when not NULL.  S_out may be the same pointer as S0 and z_out
+ * the same as z0 (in-place update); any other overlap is an error.
+ * workspace/ws_bytes: device scratch of at least
+ * la_workspace_bytes(LA_FN_LIN_ATTN_PREFILL, ...) bytes (may be NULL when that
+ * is 0); its contents on entry and exit are unspecified.
+ */
+la_status lin_attn_prefill(int dtype, int B, int H, int T, int dk, int dv,
+                           const void* q, const void* k, const void* v,
+                           const float* S0, const float* z0,
+                           void* o, float* S_out, float* z_out,
+                           int form, int chunk,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gdn_prefill - the gated delta rule (Gated DeltaNet) over T tokens.
+ *
+ * Computes, per head and token t (section "Delta rule and Gated DeltaNet",
+ * Gated DeltaNet equation; no feature map and no denominator, as the page
+ * writes k for phi(k) and drops the normaliser from the decay section on):
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ * with S_0 = S0 (zeros when NULL).  alpha, beta [B,H,T] are gate VALUES
+ * (alpha in (0,1], beta in [0,1]), float32.
+ *   LA_FORM_RECURRENT - token by token, state in registers.
+ *   LA_FORM_CHUNKED   - chunkwise form with chunk length `chunk`: per chunk
+ *     a state-independent pass (chunk-local cumulative log-gates, K K^T, the
+ *     unit lower-triangular solve of the WY/UT representation, Q K^T) and a
+ *     sequential scan that carries S between chunks in float32.
+ * Outputs: o [B,H,T,dv]; S_out [B,H,dv,dk] (final state) when not NULL; it
+ * may be the same pointer as S0.  workspace: at least
+ * la_workspace_bytes(LA_FN_GDN_PREFILL, ...) bytes.
+ */
+la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta,
+                      const float* S0, void* o, float* S_out,
+                      int form, int chunk,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * lin_attn_decode_step - one generation step for N sequences x H heads,
+ * updating the carried state IN PLACE.
+ *   LA_KIND_GATED_DELTA (section "Delta rule and Gated DeltaNet"):
+ *       S <- alpha S (I - beta k k^T) + beta v k^T,   o = S q
+ *     alpha, beta [N,H] float32 are required; z must be NULL.
+ *   LA_KIND_NORMALIZED (section "Three forms of one computation", recurrent
+ *   form, applied to one token):
+ *       S <- S + v phi(k)^T,  z <- z + phi(k),  o = S phi(q) / (z . phi(q))
+ *     z [N,H,dk] float32 is required; alpha and beta must be NULL.
+ * q, k [N,H,dk]; v, o [N,H,dv]; S [N,H,dv,dk] float32, read once and written
+ * once.  Each head's state is read and rewritten by one pass over HBM.
+ */
+la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv,
+                               const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta,
+                               float* S, float* z, void* o, void* stream);
+
+/*
+ * la_workspace_bytes - device workspace needed by one call of `fn` with the
+ * given arguments (0 when none is needed).  Returns (size_t)-1 when the
+ * arguments are invalid or the combination is not supported.
+ */
+size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv,
+                          int form, int chunk);
+
+/* la_status_str - a static, human-readable name for a status code. */
+const char* la_status_str(la_status s);
+
+/* la_abi_version - LA_ABI_VERSION of the built library. */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

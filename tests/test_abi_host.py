@@ -1,0 +1,160 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU.
+
+No call here reaches a kernel launch: every call either fails validation or
+has an empty batch, both of which return before any HIP call.  Pointers are
+fake device addresses that are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_causal_amd as gd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN, \
+    LA_ERR_WORKSPACE, LA_ERR_HIP, LA_ERR_ARG = range(9)
+F32, BF16 = 0, 1
+CHUNKED, RECURRENT, PARALLEL = 0, 1, 2
+NORMALIZED, GATED = 0, 1
+
+BASE = 0x7F0000000000  # fake, 16-byte aligned, never dereferenced
+GiB = 1 << 30
+
+
+def P(i):
+    """A distinct fake device pointer, 1 GiB apart so buffers never overlap."""
+    return ctypes.c_void_p(BASE + i * GiB)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gd.library_path()):
+        pytest.skip("liblinattn.so not built")
+    return gd._load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == sorted(["lin_attn_prefill", "gdn_prefill", "lin_attn_decode_step",
+                            "la_workspace_bytes", "la_status_str", "la_abi_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(gd.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert gd.la_abi_version() == 1
+    for s in range(9):
+        assert gd.la_status_str(s).startswith(
+            ["LA_OK", "LA_ERR_NULL", "LA_ERR_SHAPE", "LA_ERR_DTYPE", "LA_ERR_UNSUPPORTED",
+             "LA_ERR_ALIGN", "LA_ERR_WORKSPACE", "LA_ERR_HIP", "LA_ERR_ARG"][s])
+    assert "unknown" in gd.la_status_str(99)
+
+
+def prefill(lib, dtype=F32, B=1, H=2, T=8, dk=16, dv=16, q=1, k=2, v=3, S0=None, z0=None, o=4,
+            S_out=None, z_out=None, form=CHUNKED, chunk=16, ws=None, ws_bytes=0):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    return lib.lin_attn_prefill(dtype, B, H, T, dk, dv, f(q), f(k), f(v), f(S0), f(z0), f(o), f(S_out),
+                                f(z_out), form, chunk, f(ws), ws_bytes, None)
+
+
+def gdn(lib, dtype=F32, B=1, H=2, T=8, dk=16, dv=16, q=1, k=2, v=3, a=5, b=6, S0=None, o=4, S_out=None,
+        form=CHUNKED, chunk=16, ws=None, ws_bytes=0):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    return lib.gdn_prefill(dtype, B, H, T, dk, dv, f(q), f(k), f(v), f(a), f(b), f(S0), f(o), f(S_out),
+                           form, chunk, f(ws), ws_bytes, None)
+
+
+def decode(lib, kind=GATED, dtype=BF16, N=2, H=2, dk=16, dv=16, q=1, k=2, v=3, a=5, b=6, S=7, z=None, o=4):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    return lib.lin_attn_decode_step(kind, dtype, N, H, dk, dv, f(q), f(k), f(v), f(a), f(b), f(S), f(z),
+                                    f(o), None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, dtype=7) == LA_ERR_DTYPE
+    assert prefill(lib, form=9) == LA_ERR_ARG
+    assert prefill(lib, dk=48) == LA_ERR_SHAPE
+    assert prefill(lib, dv=256) == LA_ERR_SHAPE
+    assert prefill(lib, chunk=24) == LA_ERR_SHAPE
+    assert prefill(lib, B=-1) == LA_ERR_SHAPE
+    assert prefill(lib, T=-3) == LA_ERR_SHAPE
+    assert prefill(lib, q=None) == LA_ERR_NULL
+    assert prefill(lib, o=None) == LA_ERR_NULL
+    assert prefill(lib, v=ctypes.c_void_p(BASE + 3 * GiB + 8)) == LA_ERR_ALIGN
+    assert prefill(lib, S_out=ctypes.c_void_p(BASE + 9 * GiB + 4)) == LA_ERR_ALIGN
+    assert prefill(lib, form=PARALLEL, S0=8) == LA_ERR_ARG
+    assert prefill(lib, form=PARALLEL, T=8193) == LA_ERR_SHAPE
+    # output overlapping an input
+    assert prefill(lib, o=1) == LA_ERR_ARG
+    assert prefill(lib, o=ctypes.c_void_p(BASE + 3 * GiB + 256)) == LA_ERR_ARG
+    # S_out partially overlapping S0 is an error; S_out == S0 is the in-place update
+    assert prefill(lib, S0=8, S_out=ctypes.c_void_p(BASE + 8 * GiB + 16)) == LA_ERR_ARG
+    # too large: B*H beyond a grid dimension
+    assert prefill(lib, B=1 << 20, H=1 << 12) == LA_ERR_SHAPE
+    # empty batch: nothing to do, nothing launched
+    assert prefill(lib, B=0) == LA_OK
+    assert prefill(lib, H=0, q=None, k=None, v=None, o=None) == LA_OK
+
+
+def test_gdn_validation(lib):
+    assert gdn(lib, dtype=2) == LA_ERR_DTYPE
+    assert gdn(lib, form=PARALLEL) == LA_ERR_ARG
+    assert gdn(lib, dk=8) == LA_ERR_SHAPE
+    assert gdn(lib, chunk=0) == LA_ERR_SHAPE
+    assert gdn(lib, a=None) == LA_ERR_NULL
+    assert gdn(lib, b=None) == LA_ERR_NULL
+    assert gdn(lib, a=ctypes.c_void_p(BASE + 5 * GiB + 4)) == LA_ERR_ALIGN
+    assert gdn(lib, o=5) == LA_ERR_ARG  # o on top of alpha
+    assert gdn(lib, S0=8, S_out=ctypes.c_void_p(BASE + 8 * GiB + 64)) == LA_ERR_ARG
+    assert gdn(lib, B=0) == LA_OK
+
+
+def test_decode_validation(lib):
+    assert decode(lib, kind=3) == LA_ERR_ARG
+    assert decode(lib, dtype=9) == LA_ERR_DTYPE
+    assert decode(lib, dk=100) == LA_ERR_SHAPE
+    assert decode(lib, S=None) == LA_ERR_NULL
+    assert decode(lib, a=None) == LA_ERR_NULL             # gated delta needs gates
+    assert decode(lib, z=8) == LA_ERR_ARG                 # ... and takes no z
+    assert decode(lib, kind=NORMALIZED) == LA_ERR_NULL    # normalized needs z
+    assert decode(lib, kind=NORMALIZED, z=8) == LA_ERR_ARG  # ... and takes no gates
+    assert decode(lib, o=7) == LA_ERR_ARG                 # o on top of S
+    assert decode(lib, q=ctypes.c_void_p(BASE + GiB + 2)) == LA_ERR_ALIGN
+    assert decode(lib, N=0) == LA_OK
+
+
+def test_workspace_query(lib):
+    big = ctypes.c_size_t(-1).value
+    assert lib.la_workspace_bytes(9, F32, 1, 1, 8, 16, 16, CHUNKED, 16) == big
+    assert lib.la_workspace_bytes(0, 5, 1, 1, 8, 16, 16, CHUNKED, 16) == big
+    assert lib.la_workspace_bytes(1, F32, 1, 1, 8, 16, 16, PARALLEL, 16) == big
+    assert lib.la_workspace_bytes(0, F32, 1, 1, 8, 16, 16, CHUNKED, 17) == big
+    assert lib.la_workspace_bytes(2, BF16, 4, 4, 1, 128, 128, 0, 0) == 0
+    assert lib.la_workspace_bytes(0, F32, 1, 2, 256, 16, 16, RECURRENT, 0) == 0
+    assert lib.la_workspace_bytes(1, F32, 1, 2, 256, 16, 16, RECURRENT, 0) == 0
+    # fp32 chunked at dk = dv = 128 with chunk 128 does not fit any kernel
+    assert lib.la_workspace_bytes(1, F32, 1, 1, 256, 128, 128, CHUNKED, 128) == big
+    assert gdn(lib, dk=128, dv=128, chunk=128) == LA_ERR_UNSUPPORTED
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gd, "_lib", None)
+    monkeypatch.setattr(gd, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="build the HIP library"):
+        gd.la_abi_version()

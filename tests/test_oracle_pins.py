@@ -363,3 +363,24 @@ def test_planted_la_mistake_is_caught(old, new):
 @pytest.mark.parametrize("old,new", GD_MUTATIONS, ids=[m[1][:40] for m in GD_MUTATIONS])
 def test_planted_gdn_mistake_is_caught(old, new):
     assert _fails_some_pin(_namespace(gd_ns=_mutant(gd_mod, old, new)), GDN_PINS)
+
+
+def test_batched_steps_equal_single_head_steps():
+    """The head-batched steps used for large decode checks equal the pinned
+    single-head steps, head by head."""
+    from oracle import batched
+    rng = np.random.default_rng(21)
+    n, dk, dv = 5, 6, 4
+    q, k = rng.normal(size=(n, dk)), rng.normal(size=(n, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.normal(size=(n, dv))
+    a, b = rng.uniform(0.5, 1, n), rng.uniform(0, 1, n)
+    S, z = rng.normal(size=(n, dv, dk)), np.abs(rng.normal(size=(n, dk))) + 1
+    o, S1 = batched.gdn_step_heads(q, k, v, a, b, S)
+    o2, S2, z2 = batched.la_step_heads(q, k, v, S, z)
+    for i in range(n):
+        oi, Si = oracle.gdn_decode_step(q[i], k[i], v[i], a[i], b[i], S[i])
+        assert np.abs(oi - o[i]).max() < 1e-13 and np.abs(Si - S1[i]).max() < 1e-13
+        oi, Si, zi = oracle.la_decode_step(q[i], k[i], v[i], S[i], z[i])
+        assert np.abs(oi - o2[i]).max() < 1e-13 and np.abs(Si - S2[i]).max() < 1e-13
+        assert np.abs(zi - z2[i]).max() < 1e-13
