@@ -1,0 +1,225 @@
+"""Benchmark of the gated-delta prefill and decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+One timed step is one chunked gated-delta prefill (state-independent pass +
+sequential scan) over the 2 x 16 x 8192 workload (B=2, H=16, T=8192,
+d_k = d_v = 128, bf16 activations, fp32 state, chunk 64), inputs resident in
+HBM.  `value` is prefill tokens/s (B*T tokens per step).  In the same run the
+decode workload (256 sequences x 32 heads, d = 128, fp32 state, 1000 steps)
+is timed and reported as state HBM GB/s, plus the fp64 CPU oracle on a
+bounded sample of the prefill workload.  Prints one JSON line.
+
+Per-kernel durations come from HIP events recorded on the stream the kernels
+are launched on (torch's current stream, which the binding passes to the C
+ABI).  Input sets rotate over three copies so the 256 MB last-level cache
+cannot serve one step's inputs from the previous step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 flop/clk, dense
+PREFILL = "gdn_bf16_2x16x8192"
+DECODE = "gdn_decode_256x32"
+
+# Algorithmic work per head-token of the chunked gated-delta path, chunk C,
+# d = d_k = d_v: bytes = q, k, v, o in bf16 + alpha, beta in fp32; flops as
+# the chunk form computes them with triangular halves counted once:
+# 5 C d + C^2 / 3 + 6 d^2.
+def path_bytes_per_head_token(d):
+    return 4 * d * 2 + 8
+
+
+def path_flops_per_head_token(d, C):
+    return 5 * C * d + C * C / 3 + 6 * d * d
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
+              "multi-GPU mode: each GPU would run its own share of heads independently.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_causal_amd as gd
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    gd._load()
+
+    # ------------------------------------------------------------ prefill
+    w = synth.WORKLOADS[PREFILL]
+    B, H, T, d, C = w["B"], w["H"], w["T"], w["dk"], w["chunk"]
+    q, k, v, a, b = synth.gdn_batch(w["seed"], B, H, T, d, d, "bf16")
+    sets = []
+    for _ in range(3):
+        sets.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v)) +
+                    tuple(torch.from_numpy(x).to(dev) for x in (a, b)))
+    del q, k, v, a, b
+    ws = gd.gdn_workspace(sets[0][0], sets[0][2], C)
+    out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        tq, tk, tv, ta, tb = sets[i % 3]
+        if ev is not None:
+            ev[0].record()
+        gd.gdn_prefill_prep(tq, tk, tv, ta, tb, ws, chunk=C)
+        if ev is not None:
+            ev[1].record()
+        gd.gdn_prefill_scan(tq, ws, None, out=out, S_out=S_out, chunk=C)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = B * T * args.steps / elapsed
+    head_tokens = B * H * T
+    nchunks = B * H * ((T + C - 1) // C)
+    ws_bytes = ws.numel()
+    per_chunk_ws = ws_bytes / nchunks
+    # per-kernel compulsory bytes of this two-kernel design (inputs read once, outputs written once)
+    prep_bytes = head_tokens * (3 * d * 2 + 8) + ws_bytes
+    scan_bytes = ws_bytes + head_tokens * (d * 2) * 2 + B * H * d * d * 4
+    kern = {"gdn_prep_kernel": (prep_ms, prep_bytes), "gdn_scan_kernel": (scan_ms, scan_bytes)}
+    dom = max(kern, key=lambda n: kern[n][0])
+    dom_ms, dom_bytes = kern[dom]
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+    path_gbps = head_tokens * path_bytes_per_head_token(d) / ((prep_ms + scan_ms) * 1e-3) / 1e9
+    path_tflops = head_tokens * path_flops_per_head_token(d, C) / ((prep_ms + scan_ms) * 1e-3) / 1e12
+
+    # ------------------------------------------------------------- decode
+    wd = synth.WORKLOADS[DECODE]
+    N, Hd, dd, steps = wd["N"], wd["H"], wd["dk"], args.decode_steps
+    S = torch.from_numpy(synth.decode_state_fast(wd["seed"], N, Hd, dd, dd, wd["state_std"])).to(dev)
+    pool = []
+    for e in range(8):
+        tq, tk, tv, ta, tb = synth.decode_token_inputs(wd["seed"], N, Hd, dd, dd, "bf16", e)
+        pool.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (tq, tk, tv)) +
+                    tuple(torch.from_numpy(x).to(dev) for x in (ta, tb)))
+    o_dec = torch.empty((N, Hd, dd), dtype=torch.bfloat16, device=dev)
+    for i in range(5):
+        tq, tk, tv, ta, tb = pool[i % 8]
+        gd.lin_attn_decode_step("gated_delta", tq, tk, tv, S, alpha=ta, beta=tb, out=o_dec)
+    torch.cuda.synchronize()
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    dev_ev[0].record()
+    for i in range(steps):
+        tq, tk, tv, ta, tb = pool[i % 8]
+        gd.lin_attn_decode_step("gated_delta", tq, tk, tv, S, alpha=ta, beta=tb, out=o_dec)
+        dev_ev[i + 1].record()
+    torch.cuda.synchronize()
+    dec_elapsed = time.perf_counter() - t0
+    dec_ms = float(np.mean([dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(steps)]))
+    state_bytes = 2 * N * Hd * dd * dd * 4
+    io_bytes = N * Hd * (3 * dd * 2 + dd * 2 + 8)
+    dec_state_gbps = state_bytes / (dec_ms * 1e-3) / 1e9
+    dec_total_gbps = (state_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
+
+    # ----------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    rec = {
+        "metric": "prefill tokens/s (gated delta, H=16,d=128) + decode state HBM GB/s at 1 GPU",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k unit rows, v~N(0,1), alpha=sigmoid(N(3,1)), beta=sigmoid(N(0,1)))",
+        "config": {"workload": "gated delta prefill B=2 H=16 T=8192 d_k=d_v=128 chunk=64, bf16 I/O, fp32 state",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "chunk": C,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms},
+        "kernels_ms": {"gdn_prep_kernel": prep_ms, "gdn_scan_kernel": scan_ms},
+        "path_roofline": {"bytes_per_head_token": path_bytes_per_head_token(d),
+                          "flops_per_head_token": path_flops_per_head_token(d, C),
+                          "achieved_GBps": path_gbps, "hbm_frac": path_gbps / HBM_PEAK_GBPS,
+                          "achieved_TFLOPs": path_tflops, "mfma_frac": path_tflops / BF16_PEAK_TFLOPS,
+                          "workspace_bytes_per_chunk": per_chunk_ws},
+        "decode": {"workload": "gated delta decode 256 seq x 32 heads, d=128, fp32 state, bf16 token I/O",
+                   "steps": steps, "ms_per_step": dec_ms, "steps_per_s": 1e3 / dec_ms,
+                   "wall_steps_per_s": steps / dec_elapsed,
+                   "state_GBps": dec_state_gbps, "total_GBps": dec_total_gbps,
+                   "roofline": {"kernel": "recurrent_kernel (decode)", "bound": "hbm",
+                                "achieved": dec_total_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                "frac": dec_total_gbps / HBM_PEAK_GBPS, "traffic": None,
+                                "bytes_per_launch": state_bytes + io_bytes, "avg_launch_ms": dec_ms}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle (chunked form), single-threaded BLAS, on the first heads
+    of the prefill workload until `seconds` have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    B, H, T, d, C = w["B"], w["H"], w["T"], w["dk"], w["chunk"]
+    done = 0
+    spent = 0.0
+    with threadpool_limits(limits=1):
+        for bb in range(B):
+            for hh in range(H):
+                if spent > seconds:
+                    break
+                q, k, v, a, b = synth.gdn_head(w["seed"], bb, hh, T, d, d, "bf16")
+                ts = time.perf_counter()
+                oracle.gdn_chunked(q, k, v, a, b, C)
+                spent += time.perf_counter() - ts
+                done += 1
+    elapsed = spent
+    # one token of the workload carries H heads
+    return {"value": done * T / H / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {B * H} heads of the prefill workload ({done * T} head-tokens), "
+                      f"fp64 chunked form, {elapsed:.1f} s of oracle time",
+            "seconds": elapsed}
+
+
+if __name__ == "__main__":
+    main()

@@ -41,14 +41,19 @@ hipError_t launch_gdn_chunked_generic(int dtype, int heads, int T, int dk, int d
                                       const float* S0, void* o, float* S_out, hipStream_t stream);
 
 // ---- bf16 matrix-core paths (dk = dv = 128, chunk = 64) -------------------
-// Gated delta: per-chunk state-independent pass (gdn_prep.hip) then the
-// sequential inter-chunk scan (gdn_scan.hip).  Workspace layout is private
-// to those two files; gdn_mfma_workspace_bytes sizes it.
+// Gated delta (gdn_mfma.hip): per-chunk state-independent pass, then the
+// sequential inter-chunk scan.  The workspace layout is private to that
+// file; gdn_mfma_workspace_bytes sizes it.
 bool gdn_mfma_supported(int dtype, int dk, int dv, int chunk);
 size_t gdn_mfma_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 hipError_t launch_gdn_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* S0,
                            void* o, float* S_out, void* workspace, hipStream_t stream);
+hipError_t launch_gdn_mfma_prep(int B, int H, int T, const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, void* workspace,
+                                hipStream_t stream);
+hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const float* S0, void* o,
+                                float* S_out, const void* workspace, hipStream_t stream);
 
 // Normalised linear attention, chunked, bf16 in/out (la_mfma.hip).
 bool la_mfma_supported(int dtype, int dk, int dv, int chunk);

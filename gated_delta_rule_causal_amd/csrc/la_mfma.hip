@@ -1,10 +1,266 @@
-// placeholder until the matrix-core linear-attention path lands
+// Normalised causal linear attention, chunked form, on the CDNA4 matrix
+// cores: bf16 activations, fp32 state and normaliser, d_k = d_v = 128,
+// chunk C = 64.
+//
+// Source: page "Linear attention and hybrids", section "Three forms of one
+// computation", chunk equation and block flowchart (plus the same
+// normalisation as the recurrent form): per block b,
+//     A   = tril(phi(Q_b) phi(K_b)^T)                 (diagonal included)
+//     num = A V_b + phi(Q_b) S^T,   den = rowsum(A) + phi(Q_b) z
+//     O_b = num / den,   then  S += V_b^T phi(K_b),  z += colsum phi(K_b)
+//
+// One workgroup (4 waves) per head walks the blocks in order.  Each wave
+// owns 32 value channels of the state, P = S_rows^T (d_k x 32, fp32) in
+// accumulator registers; the state update is a plain accumulation
+// P += phi(K_b)^T V_b on MFMA and, as in the gated-delta scan, accumulator
+// tiles feed the next product as B operands through a permuted contraction
+// index.  Per block the tiles phi(Q), phi(K) (row-major), phi(K)^T and V^T
+// are staged in LDS with phi applied on the way in; the next block's raw
+// q/k/v are prefetched into registers while the current block computes.
+// z lives in LDS and is only written back by this workgroup, so an in-place
+// update of z is race-free.
+#include "common.hpp"
 #include "kernels.hpp"
+
 namespace la {
-bool la_mfma_supported(int, int, int, int) { return false; }
-size_t la_mfma_workspace_bytes(int, int, int, int, int, int) { return 0; }
-hipError_t launch_la_mfma(int, int, int, const void*, const void*, const void*, const float*,
-                          const float*, void*, float*, float*, void*, hipStream_t) {
-    return hipErrorInvalidValue;
+
+namespace {
+
+constexpr int C = 64;
+constexpr int D = 128;
+constexpr int LDR = D + 8;   // row-major [C][LDR] bf16 tiles (272-B rows)
+constexpr int LDT = C + 8;   // transposed [D][LDT] bf16 tiles (144-B rows)
+constexpr int kThreads = 256;
+constexpr int kItems = C * D / 8 / kThreads;  // 16-byte loads per thread per tile
+
+__device__ __forceinline__ int perm_row(int t, int rr) {
+    return 32 * (t >> 1) + 8 * (rr >> 2) + 4 * (t & 1) + (rr & 3);
 }
+
+__device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
+    int T, int NC, const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const float* S0, const float* z0, u16* __restrict__ o, float* S_out, float* z_out) {
+    __shared__ __attribute__((aligned(16))) u16 fQ[C][LDR];
+    __shared__ __attribute__((aligned(16))) u16 fK[C][LDR];
+    __shared__ __attribute__((aligned(16))) u16 fKt[D][LDT];
+    __shared__ __attribute__((aligned(16))) u16 Vt[D][LDT];
+    __shared__ __attribute__((aligned(16))) u16 As[C][LDT];
+    __shared__ float zs[D], dens[C], rsum[C];
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int r = lane & 15;
+    const int g = lane >> 4;
+
+    // ---- state: wave w owns value channels 32w + 16nb + r (nb = 0, 1)
+    f32x4 P[2][8];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int vc = 32 * w + 16 * nb + r;
+        const float* srow = S0 ? S0 + (static_cast<size_t>(bh) * D + vc) * D : nullptr;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int d0 = 32 * s + 8 * g;
+            if (srow) {
+                const float4 a = *reinterpret_cast<const float4*>(srow + d0);
+                const float4 b = *reinterpret_cast<const float4*>(srow + d0 + 4);
+                P[nb][2 * s] = f32x4{a.x, a.y, a.z, a.w};
+                P[nb][2 * s + 1] = f32x4{b.x, b.y, b.z, b.w};
+            } else {
+                P[nb][2 * s] = zero4();
+                P[nb][2 * s + 1] = zero4();
+            }
+        }
+    }
+    if (tid < D) zs[tid] = z0 ? z0[static_cast<size_t>(bh) * D + tid] : 0.f;
+
+    // ---- raw chunk prefetch: item e = tid + kThreads * it -> row = e % C, c8 = 8 (e / C)
+    uint4 rq[kItems], rk[kItems], rv[kItems];
+    const size_t head = static_cast<size_t>(bh) * T * D;
+    auto fetch = [&](int n) {
+        const int t0 = n * C;
+        const int len = min(C, T - t0);
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int e = tid + kThreads * it;
+            const int row = e % C, c8 = 8 * (e / C);
+            rq[it] = rk[it] = rv[it] = make_uint4(0, 0, 0, 0);
+            if (row < len) {
+                const size_t gi = head + static_cast<size_t>(t0 + row) * D + c8;
+                rq[it] = *reinterpret_cast<const uint4*>(q + gi);
+                rk[it] = *reinterpret_cast<const uint4*>(k + gi);
+                rv[it] = *reinterpret_cast<const uint4*>(v + gi);
+            }
+        }
+    };
+    fetch(0);
+
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * C;
+        const int len = min(C, T - t0);
+        __syncthreads();  // the previous block's LDS tiles are no longer read
+        // ---- stage phi(Q), phi(K), phi(K)^T, V^T (padded rows stay zero: phi is
+        //      applied only to real tokens, so they add nothing to A, S or z)
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int e = tid + kThreads * it;
+            const int row = e % C, c8 = 8 * (e / C);
+            const bool real = row < len;
+            const uint32_t wq[4] = {rq[it].x, rq[it].y, rq[it].z, rq[it].w};
+            const uint32_t wk[4] = {rk[it].x, rk[it].y, rk[it].z, rk[it].w};
+            const uint32_t wv[4] = {rv[it].x, rv[it].y, rv[it].z, rv[it].w};
+            float xq[8], xk[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t bq = (j & 1) ? (wq[j >> 1] & 0xffff0000u) : (wq[j >> 1] << 16);
+                const uint32_t bk = (j & 1) ? (wk[j >> 1] & 0xffff0000u) : (wk[j >> 1] << 16);
+                xq[j] = real ? phi(__uint_as_float(bq)) : 0.f;
+                xk[j] = real ? phi(__uint_as_float(bk)) : 0.f;
+            }
+            const bf16x8 pq = pack8(xq[0], xq[1], xq[2], xq[3], xq[4], xq[5], xq[6], xq[7]);
+            const bf16x8 pk = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
+            *reinterpret_cast<bf16x8*>(&fQ[row][c8]) = pq;
+            *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                fKt[c8 + j][row] = __builtin_bit_cast(u16, pk[j]);
+                Vt[c8 + j][row] = static_cast<u16>((j & 1) ? (wv[j >> 1] >> 16) : (wv[j >> 1] & 0xffffu));
+            }
+        }
+        if (n + 1 < NC) fetch(n + 1);
+        __syncthreads();
+
+        // ---- A = tril(phi(Q) phi(K)^T), row tile w, and its row sums (fp32)
+        {
+            float rs[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < 4; ++ct) {
+                if (ct <= w) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc = mfma16x16x32(lds8(&fQ[16 * w + r][32 * s + 8 * g]),
+                                           lds8(&fK[16 * ct + r][32 * s + 8 * g]), acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * w + 4 * g + i, col = 16 * ct + r;
+                        const float a = col <= row ? acc[i] : 0.f;
+                        As[row][col] = f32_to_bf16_bits(a);
+                        rs[i] += a;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) As[16 * w + 4 * g + i][16 * ct + r] = 0;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float t = group_sum<16>(rs[i]);
+                if (r == 0) rsum[16 * w + 4 * g + i] = t;
+            }
+        }
+        __syncthreads();
+        // ---- den = rowsum(A) + phi(Q) z   (z of the previous blocks)
+        {
+            const int row = tid >> 2, qd = (tid & 3) * 32;
+            float acc = 0.f;
+#pragma unroll
+            for (int d = 0; d < 32; ++d) acc = fmaf(bf16_bits_to_f32(fQ[row][qd + d]), zs[qd + d], acc);
+            acc = group_sum<4>(acc);
+            if ((tid & 3) == 0) dens[row] = acc + rsum[row];
+        }
+        __syncthreads();
+        // ---- z += colsum phi(K)  (read again only after the next loop-top barrier)
+        if (tid < D) {
+            float acc = zs[tid];
+            for (int c = 0; c < C; ++c) acc += bf16_bits_to_f32(fK[c][tid]);
+            zs[tid] = acc;
+        }
+
+        // ---- this wave's 32 value channels: outputs, then the state update
+        bf16x8 Pb[2][4], Vb[2][2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Pb[nb][s] = pack_acc_pair(P[nb][2 * s], P[nb][2 * s + 1]);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) Vb[nb][s2] = lds8(&Vt[32 * w + 16 * nb + r][32 * s2 + 8 * g]);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 a = lds8(&fQ[16 * m + r][32 * s + 8 * g]);
+                acc[0] = mfma16x16x32(a, Pb[0][s], acc[0]);
+                acc[1] = mfma16x16x32(a, Pb[1][s], acc[1]);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 <= (m >> 1); ++s2) {
+                const bf16x8 a = lds8(&As[16 * m + r][32 * s2 + 8 * g]);
+                acc[0] = mfma16x16x32(a, Vb[0][s2], acc[0]);
+                acc[1] = mfma16x16x32(a, Vb[1][s2], acc[1]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * m + 4 * g + i;
+                if (row < len) {
+                    const float rden = 1.f / dens[row];
+                    const size_t oi = head + static_cast<size_t>(t0 + row) * D + 32 * w + r;
+                    o[oi] = f32_to_bf16_bits(acc[0][i] * rden);
+                    o[oi + 16] = f32_to_bf16_bits(acc[1][i] * rden);
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 a = lds8(&fKt[perm_row(t, r)][32 * s2 + 8 * g]);
+                P[0][t] = mfma16x16x32(a, Vb[0][s2], P[0][t]);
+                P[1][t] = mfma16x16x32(a, Vb[1][s2], P[1][t]);
+            }
+        }
+    }
+
+    if (S_out) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            float* srow = S_out + (static_cast<size_t>(bh) * D + 32 * w + 16 * nb + r) * D;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int d0 = 32 * s + 8 * g;
+                *reinterpret_cast<float4*>(srow + d0) =
+                    make_float4(P[nb][2 * s][0], P[nb][2 * s][1], P[nb][2 * s][2], P[nb][2 * s][3]);
+                *reinterpret_cast<float4*>(srow + d0 + 4) =
+                    make_float4(P[nb][2 * s + 1][0], P[nb][2 * s + 1][1], P[nb][2 * s + 1][2], P[nb][2 * s + 1][3]);
+            }
+        }
+    }
+    __syncthreads();
+    if (z_out && tid < D) z_out[static_cast<size_t>(bh) * D + tid] = zs[tid];
+}
+
+}  // namespace
+
+bool la_mfma_supported(int dtype, int dk, int dv, int chunk) {
+    return dtype == kBF16 && dk == D && dv == D && chunk == C;
+}
+
+size_t la_mfma_workspace_bytes(int, int, int, int, int, int) { return 0; }
+
+hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* S0,
+                          const float* z0, void* o, float* S_out, float* z_out, void*, hipStream_t stream) {
+    const int BH = B * H;
+    if (BH <= 0 || T <= 0) return hipSuccess;
+    const int NC = (T + C - 1) / C;
+    hipLaunchKernelGGL(la_chunked_mfma_kernel, dim3(BH), dim3(kThreads), 0, stream, T, NC,
+                       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), S0, z0,
+                       static_cast<u16*>(o), S_out, z_out);
+    return hipGetLastError();
+}
+
 }  // namespace la

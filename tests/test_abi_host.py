@@ -47,8 +47,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == sorted(["lin_attn_prefill", "gdn_prefill", "lin_attn_decode_step",
-                            "la_workspace_bytes", "la_status_str", "la_abi_version"])
+    assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
+                            "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -158,3 +158,34 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gd, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="build the HIP library"):
         gd.la_abi_version()
+
+
+def test_split_gdn_validation(lib):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+
+    def prep(dtype=BF16, B=1, H=2, T=100, dk=128, dv=128, q=1, k=2, v=3, a=5, b=6, chunk=64, ws=9,
+             ws_bytes=1 << 40):
+        return lib.gdn_prefill_prep(dtype, B, H, T, dk, dv, f(q), f(k), f(v), f(a), f(b), chunk, f(ws), ws_bytes,
+                                    None)
+
+    def scan(dtype=BF16, B=1, H=2, T=100, dk=128, dv=128, q=1, S0=None, o=4, S_out=None, chunk=64, ws=9,
+             ws_bytes=1 << 40):
+        return lib.gdn_prefill_scan(dtype, B, H, T, dk, dv, f(q), f(S0), f(o), f(S_out), chunk, f(ws), ws_bytes,
+                                    None)
+
+    assert prep(dtype=F32) == LA_ERR_UNSUPPORTED
+    assert prep(dk=64, dv=64) == LA_ERR_UNSUPPORTED
+    assert prep(chunk=32) == LA_ERR_UNSUPPORTED
+    assert prep(chunk=33) == LA_ERR_SHAPE
+    assert prep(ws=None) == LA_ERR_WORKSPACE
+    assert prep(ws_bytes=1000) == LA_ERR_WORKSPACE
+    assert prep(a=None) == LA_ERR_NULL
+    assert prep(ws=2) == LA_ERR_ARG          # workspace on top of k
+    assert prep(B=0) == LA_OK
+    assert scan(o=None) == LA_ERR_NULL
+    assert scan(o=9) == LA_ERR_ARG           # output on top of the workspace
+    assert scan(o=1) == LA_ERR_ARG           # output on top of q
+    assert scan(S0=7, S_out=ctypes.c_void_p(BASE + 7 * GiB + 32)) == LA_ERR_ARG
+    assert scan(ws=ctypes.c_void_p(BASE + 9 * GiB + 8)) == LA_ERR_ALIGN
+    n = lib.la_workspace_bytes(1, BF16, 1, 2, 100, 128, 128, CHUNKED, 64)
+    assert n > 0 and scan(ws_bytes=n - 1) == LA_ERR_WORKSPACE
