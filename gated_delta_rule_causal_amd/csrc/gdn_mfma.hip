@@ -189,8 +189,11 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(
             *reinterpret_cast<uint4*>(wsc + kOffA + (static_cast<size_t>(row) * C + c8) * 2) =
                 *reinterpret_cast<const uint4*>(&As[row][c8]);
         }
-        if (t3 < C) reinterpret_cast<float*>(wsc + kOffEg)[t3] = egs[t3];
-        if (t3 == C) reinterpret_cast<float*>(wsc + kOffEg)[C] = egs[C - 1];
+        // e^g, e^{g_c}, and 16 zero bytes at byte 272 (the source of padded q rows in the scan)
+        float* egw = reinterpret_cast<float*>(wsc + kOffEg);
+        if (t3 < C) egw[t3] = egs[t3];
+        if (t3 == C) egw[C] = egs[C - 1];
+        if (t3 > C && t3 <= C + 3 + 4) egw[t3] = 0.f;
     }
     __syncthreads();
 
@@ -252,146 +255,234 @@ __device__ __forceinline__ int perm_row(int t, int rr) {
     return 32 * (t >> 1) + 8 * (rr >> 2) + 4 * (t & 1) + (rr & 3);
 }
 
-__global__ __launch_bounds__(64) void gdn_scan_kernel(int BH, int T, int NC, const u16* __restrict__ q,
-                                                      const unsigned char* __restrict__ ws,
-                                                      const float* S0, float* S_out,
-                                                      u16* __restrict__ o) {
+// One workgroup per (head, 16-wide value tile), four waves with fixed roles:
+//   wave 0    - the scan: state in accumulator registers, operands from LDS;
+//   waves 1,2 - copy the next chunk's operands global -> LDS with the direct
+//               LDS-load instruction (no registers), double-buffered, each
+//               1-KiB fragment laid out exactly as the MFMA lanes read it;
+//   wave 3    - touches the workspace kPrefetchAhead chunks ahead so that
+//               the copies are served from L2.
+// Every role runs its own loop with the same number of barriers.
+constexpr int kScanThreads = 256;
+constexpr int kFragW = 0;     // W        (m, s)    16 fragments
+constexpr int kFragQ = 16;    // Q        (m, s)    16
+constexpr int kFragA = 32;    // A        lower (m, s2) blocks: 6
+constexpr int kFragKt = 38;   // K~^T     (t, s2)   16
+constexpr int kFragU = 54;    // Ut^T rows of this value tile (s2): 2
+constexpr int kNumFrag = 56;
+constexpr int kEgBytes = 272;                       // e^g (64), e^{g_c}, pad: 17 lanes x 16 B
+constexpr int kBufBytes = kNumFrag * 1024 + kEgBytes;
+constexpr int kZeroOff = 272;                       // 16 zero bytes inside each chunk's e^g area
+constexpr int kPrefetchAhead = 6;
+constexpr int kWsLines = static_cast<int>((kChunkBytes + 127) / 128);
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_dst, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vm0() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unconstrained
+}
+
+__device__ __forceinline__ int afrag_m(int idx) { return idx < 2 ? idx : 2 + ((idx - 2) >> 1); }
+__device__ __forceinline__ int afrag_s(int idx) { return idx < 2 ? 0 : ((idx - 2) & 1); }
+
+__global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(int BH, int T, int NC, const u16* __restrict__ q,
+                                                                const unsigned char* __restrict__ ws,
+                                                                const float* S0, float* S_out,
+                                                                u16* __restrict__ o) {
+    __shared__ __attribute__((aligned(16))) unsigned char sbuf[2][kBufBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char scratch[256];
+
     // blockIdx -> (head, value tile) such that the 8 tiles of a head share an XCD
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
     const int j = blk >> 3;
     const int tile = j & 7;
     const int bh = (j >> 3) * 8 + xcd;
-    if (bh >= BH) return;
-    const int lane = threadIdx.x;
+    if (bh >= BH) return;  // uniform over the workgroup
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int g = lane >> 4;
-    const int vcol = 16 * tile + r;  // this lane's value channel
-
-    // ---- state slice P[d][vcol] = S[vcol][d], d = perm_row(t, 4g + i)
-    f32x4 P[8];
-    {
-        const float* srow = S0 ? S0 + (static_cast<size_t>(bh) * D + vcol) * D : nullptr;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int d0 = 32 * s + 8 * g;
-            if (srow) {
-                const float4 a = *reinterpret_cast<const float4*>(srow + d0);
-                const float4 b = *reinterpret_cast<const float4*>(srow + d0 + 4);
-                P[2 * s] = f32x4{a.x, a.y, a.z, a.w};
-                P[2 * s + 1] = f32x4{b.x, b.y, b.z, b.w};
-            } else {
-                P[2 * s] = zero4();
-                P[2 * s + 1] = zero4();
-            }
-        }
-    }
-
     const size_t qhead = static_cast<size_t>(bh) * T * D;
-    for (int n = 0; n < NC; ++n) {
-        const unsigned char* wsc = ws + (static_cast<size_t>(bh) * NC + n) * kChunkBytes;
-        const u16* W = reinterpret_cast<const u16*>(wsc + kOffW);
-        const u16* Kt = reinterpret_cast<const u16*>(wsc + kOffKt);
-        const u16* Ut = reinterpret_cast<const u16*>(wsc + kOffUt);
-        const u16* A = reinterpret_cast<const u16*>(wsc + kOffA);
-        const float* eg = reinterpret_cast<const float*>(wsc + kOffEg);
-        const int t0 = n * C;
-        const int len = min(C, T - t0);
+    const unsigned char* wsh = ws + static_cast<size_t>(bh) * NC * kChunkBytes;
 
-        // state as B operand (bf16), K = d_k in four slices of 32
-        bf16x8 Pb[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Pb[s] = pack_acc_pair(P[2 * s], P[2 * s + 1]);
-
-        // X = W P  (rows of W permuted so that X lands in the U layout)
-        f32x4 X[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            X[m] = zero4();
-            const u16* wrow = W + static_cast<size_t>(perm_row(m, r)) * D + 8 * g;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                X[m] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(wrow + 32 * s), Pb[s], X[m]);
-        }
-        // U = Ut - X ; Ut^T row vcol holds 8 consecutive chunk rows per lane group
-        f32x4 U[4];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(Ut + static_cast<size_t>(vcol) * C + 32 * s2 + 8 * g);
-            const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = wds[i >> 1];
-                const uint32_t hi = wds[2 + (i >> 1)];
-                const float u_lo = (i & 1) ? __uint_as_float(lo & 0xffff0000u) : __uint_as_float(lo << 16);
-                const float u_hi = (i & 1) ? __uint_as_float(hi & 0xffff0000u) : __uint_as_float(hi << 16);
-                U[2 * s2][i] = u_lo - X[2 * s2][i];
-                U[2 * s2 + 1][i] = u_hi - X[2 * s2 + 1][i];
-            }
-        }
-        bf16x8 Ub[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) Ub[s2] = pack_acc_pair(U[2 * s2], U[2 * s2 + 1]);
-
-        // O = e^g (Q P) + A U
-        // (rows past the sequence end read as zero; the MFMAs themselves run
-        // unconditionally on the whole wave)
-        f32x4 O[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            O[m] = zero4();
-            const int row = perm_row(m, r);
-            const u16* qrow = q + qhead + static_cast<size_t>(t0 + row) * D + 8 * g;
+    if (w == 0) {
+        // ------------------------------------------------------------ scan
+        const int vcol = 16 * tile + r;
+        f32x4 P[8];
+        {
+            const float* srow = S0 ? S0 + (static_cast<size_t>(bh) * D + vcol) * D : nullptr;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                uint4 raw = make_uint4(0, 0, 0, 0);
-                if (row < len) raw = *reinterpret_cast<const uint4*>(qrow + 32 * s);
-                O[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, raw), Pb[s], O[m]);
+                const int d0 = 32 * s + 8 * g;
+                if (srow) {
+                    const float4 a = *reinterpret_cast<const float4*>(srow + d0);
+                    const float4 b = *reinterpret_cast<const float4*>(srow + d0 + 4);
+                    P[2 * s] = f32x4{a.x, a.y, a.z, a.w};
+                    P[2 * s + 1] = f32x4{b.x, b.y, b.z, b.w};
+                } else {
+                    P[2 * s] = zero4();
+                    P[2 * s + 1] = zero4();
+                }
             }
         }
+        __syncthreads();
+        for (int n = 0; n < NC; ++n) {
+            const unsigned char* B = sbuf[n & 1];
+            auto frag = [&](int f) { return *reinterpret_cast<const bf16x8*>(B + f * 1024 + lane * 16); };
+            const float* eg = reinterpret_cast<const float*>(B + kNumFrag * 1024);
+            const int t0 = n * C;
+            const int len = min(C, T - t0);
+
+            bf16x8 Pb[4];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const float4 e_lo = *reinterpret_cast<const float4*>(eg + 32 * s2 + 8 * g);
-            const float4 e_hi = *reinterpret_cast<const float4*>(eg + 32 * s2 + 8 * g + 4);
-            O[2 * s2] *= f32x4{e_lo.x, e_lo.y, e_lo.z, e_lo.w};
-            O[2 * s2 + 1] *= f32x4{e_hi.x, e_hi.y, e_hi.z, e_hi.w};
-        }
+            for (int s = 0; s < 4; ++s) Pb[s] = pack_acc_pair(P[2 * s], P[2 * s + 1]);
+            // X = W P
+            f32x4 X[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const u16* arow = A + static_cast<size_t>(perm_row(m, r)) * C + 8 * g;
+            for (int m = 0; m < 4; ++m) {
+                X[m] = zero4();
 #pragma unroll
-            for (int s2 = 0; s2 <= (m >> 1); ++s2)
-                O[m] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(arow + 32 * s2), Ub[s2], O[m]);
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = perm_row(m, 4 * g + i);
-                if (row < len) o[qhead + static_cast<size_t>(t0 + row) * D + vcol] = f32_to_bf16_bits(O[m][i]);
+                for (int s = 0; s < 4; ++s) X[m] = mfma16x16x32(frag(kFragW + 4 * m + s), Pb[s], X[m]);
             }
-
-        // P <- e^{g_c} P + K~^T U
-        const float egc = eg[C];
+            // U = Ut - X
+            f32x4 U[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            P[t] *= egc;
-            const u16* krow = Kt + static_cast<size_t>(perm_row(t, r)) * C + 8 * g;
+            for (int s2 = 0; s2 < 2; ++s2) {
+                // decode the 8 bf16 with integer ops (element extraction from
+                // __bf16 vectors is avoided throughout)
+                const uint4 raw = *reinterpret_cast<const uint4*>(B + (kFragU + s2) * 1024 + lane * 16);
+                const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                P[t] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(krow + 32 * s2), Ub[s2], P[t]);
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = wds[i >> 1], hi = wds[2 + (i >> 1)];
+                    const float u_lo = __uint_as_float((i & 1) ? (lo & 0xffff0000u) : (lo << 16));
+                    const float u_hi = __uint_as_float((i & 1) ? (hi & 0xffff0000u) : (hi << 16));
+                    U[2 * s2][i] = u_lo - X[2 * s2][i];
+                    U[2 * s2 + 1][i] = u_hi - X[2 * s2 + 1][i];
+                }
+            }
+            bf16x8 Ub[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) Ub[s2] = pack_acc_pair(U[2 * s2], U[2 * s2 + 1]);
+            // O = e^g (Q P) + A U  (padded Q rows were copied as zeros)
+            f32x4 O[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                O[m] = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) O[m] = mfma16x16x32(frag(kFragQ + 4 * m + s), Pb[s], O[m]);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    O[2 * s2][i] *= eg[32 * s2 + 8 * g + i];
+                    O[2 * s2 + 1][i] *= eg[32 * s2 + 8 * g + 4 + i];
+                }
+            }
+#pragma unroll
+            for (int idx = 0; idx < 6; ++idx) {
+                const int m = afrag_m(idx), s2 = afrag_s(idx);
+                O[m] = mfma16x16x32(frag(kFragA + idx), Ub[s2], O[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = perm_row(m, 4 * g + i);
+                    if (row < len) o[qhead + static_cast<size_t>(t0 + row) * D + vcol] = f32_to_bf16_bits(O[m][i]);
+                }
+            // P <- e^{g_c} P + K~^T U
+            const float egc = eg[C];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                P[t] *= egc;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) P[t] = mfma16x16x32(frag(kFragKt + 2 * t + s2), Ub[s2], P[t]);
+            }
+            __syncthreads();
         }
-    }
-
-    if (S_out) {
-        float* srow = S_out + (static_cast<size_t>(bh) * D + vcol) * D;
+        if (S_out) {
+            float* srow = S_out + (static_cast<size_t>(bh) * D + vcol) * D;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int d0 = 32 * s + 8 * g;
-            *reinterpret_cast<float4*>(srow + d0) = make_float4(P[2 * s][0], P[2 * s][1], P[2 * s][2], P[2 * s][3]);
-            *reinterpret_cast<float4*>(srow + d0 + 4) =
-                make_float4(P[2 * s + 1][0], P[2 * s + 1][1], P[2 * s + 1][2], P[2 * s + 1][3]);
+            for (int s = 0; s < 4; ++s) {
+                const int d0 = 32 * s + 8 * g;
+                *reinterpret_cast<float4*>(srow + d0) =
+                    make_float4(P[2 * s][0], P[2 * s][1], P[2 * s][2], P[2 * s][3]);
+                *reinterpret_cast<float4*>(srow + d0 + 4) =
+                    make_float4(P[2 * s + 1][0], P[2 * s + 1][1], P[2 * s + 1][2], P[2 * s + 1][3]);
+            }
         }
+    } else if (w <= 2) {
+        // --------------------------------------------------- operand copies
+        const int half = w - 1;
+        auto issue = [&](int n) {
+            unsigned char* B = sbuf[n & 1];
+            const unsigned char* wsc = wsh + static_cast<size_t>(n) * kChunkBytes;
+            const int t0 = n * C;
+            const int len = min(C, T - t0);
+            for (int f = half; f < kNumFrag; f += 2) {
+                const void* src;
+                if (f < kFragQ) {
+                    const int m = (f - kFragW) >> 2, s = (f - kFragW) & 3;
+                    src = wsc + kOffW + (static_cast<size_t>(perm_row(m, r)) * D + 32 * s + 8 * g) * 2;
+                } else if (f < kFragA) {
+                    const int m = (f - kFragQ) >> 2, s = (f - kFragQ) & 3;
+                    const int row = perm_row(m, r);
+                    src = row < len ? static_cast<const void*>(q + qhead + static_cast<size_t>(t0 + row) * D + 32 * s + 8 * g)
+                                    : static_cast<const void*>(wsc + kOffEg + kZeroOff);
+                } else if (f < kFragKt) {
+                    const int idx = f - kFragA;
+                    src = wsc + kOffA + (static_cast<size_t>(perm_row(afrag_m(idx), r)) * C + 32 * afrag_s(idx) + 8 * g) * 2;
+                } else if (f < kFragU) {
+                    const int idx = f - kFragKt;
+                    src = wsc + kOffKt + (static_cast<size_t>(perm_row(idx >> 1, r)) * C + 32 * (idx & 1) + 8 * g) * 2;
+                } else {
+                    const int s2 = f - kFragU;
+                    src = wsc + kOffUt + (static_cast<size_t>(16 * tile + r) * C + 32 * s2 + 8 * g) * 2;
+                }
+                dma16(src, B + f * 1024);
+            }
+            if (half == 0 && lane < kEgBytes / 16) dma16(wsc + kOffEg + lane * 16, B + kNumFrag * 1024);
+        };
+        issue(0);
+        wait_vm0();
+        __syncthreads();
+        for (int n = 0; n < NC; ++n) {
+            if (n + 1 < NC) issue(n + 1);
+            wait_vm0();
+            __syncthreads();
+        }
+    } else {
+        // -------------------------------------------------- L2 prefetcher
+        auto touch = [&](int n) {
+            const unsigned char* wsc = wsh + static_cast<size_t>(n) * kChunkBytes;
+            for (int l = lane; l < kWsLines; l += 64) dma4(wsc + static_cast<size_t>(l) * 128, scratch);
+            const int t0 = n * C;
+            const int len = min(C, T - t0);
+            if (lane < len) {
+                const u16* qrow = q + qhead + static_cast<size_t>(t0 + lane) * D;
+                dma4(qrow, scratch);
+                dma4(qrow + 64, scratch);
+            }
+        };
+        // This wave shares nothing through LDS (its copies land in a scratch
+        // area nobody reads), so it joins the barriers without the release
+        // fence of __syncthreads, which would wait for its loads to land.
+        for (int n = 1; n <= kPrefetchAhead && n < NC; ++n) touch(n);
+        __builtin_amdgcn_s_barrier();
+        for (int n = 0; n < NC; ++n) {
+            if (n + kPrefetchAhead + 1 < NC) touch(n + kPrefetchAhead + 1);
+            __builtin_amdgcn_s_barrier();
+        }
+        wait_vm0();
     }
 }
 
@@ -423,7 +514,7 @@ hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const float*
     if (BH <= 0 || T <= 0) return hipSuccess;
     const int NC = (T + C - 1) / C;
     const unsigned scan_blocks = static_cast<unsigned>((BH * 8 + 63) / 64 * 64);
-    hipLaunchKernelGGL(gdn_scan_kernel, dim3(scan_blocks), dim3(64), 0, stream, BH, T, NC,
+    hipLaunchKernelGGL(gdn_scan_kernel, dim3(scan_blocks), dim3(kScanThreads), 0, stream, BH, T, NC,
                        static_cast<const u16*>(q), static_cast<const unsigned char*>(workspace), S0, S_out,
                        static_cast<u16*>(o));
     return hipGetLastError();

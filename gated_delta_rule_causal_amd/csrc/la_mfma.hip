@@ -127,7 +127,9 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                fKt[c8 + j][row] = __builtin_bit_cast(u16, pk[j]);
+                // bits from the fp32 value, not from an element of the packed
+                // __bf16 vector (extracting those for a bit cast miscompiles)
+                fKt[c8 + j][row] = f32_to_bf16_bits(xk[j]);
                 Vt[c8 + j][row] = static_cast<u16>((j & 1) ? (wv[j >> 1] >> 16) : (wv[j >> 1] & 0xffffu));
             }
         }
