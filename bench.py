@@ -87,7 +87,7 @@ def main():
         gd.gdn_prefill_prep(tq, tk, tv, ta, tb, ws, chunk=C)
         if ev is not None:
             ev[1].record()
-        gd.gdn_prefill_scan(tq, ws, None, out=out, S_out=S_out, chunk=C)
+        gd.gdn_prefill_scan(tq, tk, tv, ta, tb, ws, None, out=out, S_out=S_out, chunk=C)
         if ev is not None:
             ev[2].record()
 
@@ -106,13 +106,19 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = B * T * args.steps / elapsed
     head_tokens = B * H * T
-    nchunks = B * H * ((T + C - 1) // C)
-    ws_bytes = ws.numel()
-    per_chunk_ws = ws_bytes / nchunks
-    # per-kernel compulsory bytes of this two-kernel design (inputs read once, outputs written once)
-    prep_bytes = head_tokens * (3 * d * 2 + 8) + ws_bytes
-    scan_bytes = ws_bytes + head_tokens * (d * 2) * 2 + B * H * d * d * 4
-    kern = {"gdn_prep_kernel": (prep_ms, prep_bytes), "gdn_scan_kernel": (scan_ms, scan_bytes)}
+    # segments per head, from the workspace size (3 fp32 d x d matrices per head-segment)
+    mat = d * d * 4
+    G = max(1, ws.numel() // (B * H * 3 * mat)) if ws.numel() > 16 else 1
+    # compulsory bytes of each call in this design (inputs read once, outputs written once):
+    #   prep  = segment maps: k, v, alpha, beta of the first G-1 segments; (M, N) per head-segment
+    #   scan  = combine (maps + entering states) + outputs: q, k, v, alpha, beta, o, entering
+    #           states, final state
+    frac = (G - 1) / G
+    prep_bytes = head_tokens * frac * (2 * d * 2 + 8) + B * H * (G - 1) * 2 * mat
+    scan_bytes = (head_tokens * (3 * d * 2 + 8 + d * 2) + B * H * (G - 1) * 2 * mat + B * H * G * 2 * mat +
+                  B * H * mat)
+    kern = {"gdn_prefill_prep (gdn_map_kernel)": (prep_ms, prep_bytes),
+            "gdn_prefill_scan (gdn_combine_kernel + gdn_out_kernel)": (scan_ms, scan_bytes)}
     dom = max(kern, key=lambda n: kern[n][0])
     dom_ms, dom_bytes = kern[dom]
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -172,12 +178,11 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None,
                      "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms},
-        "kernels_ms": {"gdn_prep_kernel": prep_ms, "gdn_scan_kernel": scan_ms},
+        "kernels_ms": {"gdn_prefill_prep": prep_ms, "gdn_prefill_scan": scan_ms, "segments_per_head": G},
         "path_roofline": {"bytes_per_head_token": path_bytes_per_head_token(d),
                           "flops_per_head_token": path_flops_per_head_token(d, C),
                           "achieved_GBps": path_gbps, "hbm_frac": path_gbps / HBM_PEAK_GBPS,
-                          "achieved_TFLOPs": path_tflops, "mfma_frac": path_tflops / BF16_PEAK_TFLOPS,
-                          "workspace_bytes_per_chunk": per_chunk_ws},
+                          "achieved_TFLOPs": path_tflops, "mfma_frac": path_tflops / BF16_PEAK_TFLOPS},
         "decode": {"workload": "gated delta decode 256 seq x 32 heads, d=128, fp32 state, bf16 token I/O",
                    "steps": steps, "ms_per_step": dec_ms, "steps_per_s": 1e3 / dec_ms,
                    "wall_steps_per_s": steps / dec_elapsed,

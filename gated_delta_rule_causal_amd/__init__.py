@@ -68,7 +68,7 @@ def _load():
     lib.gdn_prefill.restype = I
     lib.gdn_prefill_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P, Z, P]
     lib.gdn_prefill_prep.restype = I
-    lib.gdn_prefill_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, I, P, Z, P]
+    lib.gdn_prefill_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, Z, P]
     lib.gdn_prefill_scan.restype = I
     lib.lin_attn_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
     lib.lin_attn_decode_step.restype = I
@@ -216,11 +216,11 @@ def gdn_workspace(q, v, chunk=64):
     torch = _torch()
     B, H, T, dk = q.shape
     n = la_workspace_bytes("gdn_prefill", _dtype_code(q.dtype), B, H, T, dk, v.shape[-1], "chunked", chunk)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
 
 
 def gdn_prefill_prep(q, k, v, alpha, beta, workspace, chunk=64, stream=None):
-    """State-independent half of the chunked gated-delta path; fills workspace."""
+    """State-independent half of the chunked gated-delta path (segment maps)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
@@ -233,14 +233,14 @@ def gdn_prefill_prep(q, k, v, alpha, beta, workspace, chunk=64, stream=None):
         raise LinAttnError(st, "gdn_prefill_prep")
 
 
-def gdn_prefill_scan(q, workspace, S0=None, out=None, S_out=None, dv=None, chunk=64, stream=None):
-    """Sequential half of the chunked gated-delta path; returns (o, S_out)."""
+def gdn_prefill_scan(q, k, v, alpha, beta, workspace, S0=None, out=None, S_out=None, chunk=64, stream=None):
+    """Entering states of the segments, then outputs and final state; returns (o, S_out)."""
     torch = _torch()
     B, H, T, dk = q.shape
-    dv = dk if dv is None else dv
+    dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    _check(q, "q")
-    _check(workspace, "workspace")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta"), (workspace, "workspace")):
+        _check(t, n)
     _check(S0, "S0", torch.float32, (B, H, dv, dk))
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
@@ -248,9 +248,9 @@ def gdn_prefill_scan(q, workspace, S0=None, out=None, S_out=None, dv=None, chunk
         S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
     _check(out, "out", q.dtype, (B, H, T, dv))
     _check(S_out, "S_out", torch.float32, (B, H, dv, dk))
-    st = _load().gdn_prefill_scan(dt, B, H, T, dk, dv, _ptr(q), _ptr(S0), _ptr(out), _ptr(S_out), chunk,
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _stream_ptr(stream, q.device))
+    st = _load().gdn_prefill_scan(dt, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(S0), _ptr(out), _ptr(S_out), chunk, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream_ptr(stream, q.device))
     if st != 0:
         raise LinAttnError(st, "gdn_prefill_scan")
     return out, S_out

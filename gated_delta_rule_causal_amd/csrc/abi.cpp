@@ -214,7 +214,11 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
     }
     const size_t need = gdn_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
     if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
-    if (need > 0 && overlaps({workspace, need}, outs[0])) return LA_ERR_ARG;
+    if (need > 0 && (overlaps({workspace, need}, outs[0]) || overlaps({workspace, need}, outs[1]) ||
+                     overlaps({workspace, need}, Span{S0, nS})))
+        return LA_ERR_ARG;
+    for (const Span& b : in)
+        if (need > 0 && overlaps({workspace, need}, b)) return LA_ERR_ARG;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) return copy_state(S0, S_out, heads * dv * dk, s);
@@ -231,16 +235,24 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
 namespace {
 
 // Shared checks of the two halves of the chunked matrix-core gated-delta path.
-la_status gdn_split_common(int dtype, int B, int H, int T, int dk, int dv, int chunk, const void* ws,
-                           size_t ws_bytes, size_t* heads_out) {
+la_status gdn_split_common(int dtype, int B, int H, int T, int dk, int dv, int chunk, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta, const void* ws, size_t ws_bytes,
+                           size_t* heads_out) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
     if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv) || !valid_chunk(chunk)) return LA_ERR_SHAPE;
     if (!la::gdn_mfma_supported(dtype, dk, dv, chunk)) return LA_ERR_UNSUPPORTED;
     *heads_out = static_cast<size_t>(B) * H;
     if (*heads_out == 0 || T == 0) return LA_OK;
+    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr) return LA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta)})
+        if (!aligned16(p)) return LA_ERR_ALIGN;
     const size_t need = la::gdn_mfma_workspace_bytes(B, H, T, dk, dv, chunk);
-    if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
-    if (!aligned16(ws)) return LA_ERR_ALIGN;
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
+    if (ws != nullptr && !aligned16(ws)) return LA_ERR_ALIGN;
+    const size_t nqk = *heads_out * T * dk * 2, nv = *heads_out * T * dv * 2, ng = *heads_out * T * sizeof(float);
+    const Span w{ws, need};
+    for (const Span& b : {Span{q, nqk}, Span{k, nqk}, Span{v, nv}, Span{alpha, ng}, Span{beta, ng}})
+        if (overlaps(w, b)) return LA_ERR_ARG;
     return LA_OK;
 }
 
@@ -250,40 +262,41 @@ la_status gdn_prefill_prep(int dtype, int B, int H, int T, int dk, int dv, const
                            const void* v, const float* alpha, const float* beta, int chunk, void* workspace,
                            size_t ws_bytes, void* stream) {
     size_t heads = 0;
-    la_status st = gdn_split_common(dtype, B, H, T, dk, dv, chunk, workspace, ws_bytes, &heads);
+    const la_status st =
+        gdn_split_common(dtype, B, H, T, dk, dv, chunk, q, k, v, alpha, beta, workspace, ws_bytes, &heads);
     if (st != LA_OK || heads == 0 || T == 0) return st;
-    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr) return LA_ERR_NULL;
-    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta)})
-        if (!aligned16(p)) return LA_ERR_ALIGN;
-    const size_t nqk = heads * T * dk * 2, nv = heads * T * dv * 2, ng = heads * T * sizeof(float);
-    const Span ws{workspace, la::gdn_mfma_workspace_bytes(B, H, T, dk, dv, chunk)};
-    for (const Span& b : {Span{q, nqk}, Span{k, nqk}, Span{v, nv}, Span{alpha, ng}, Span{beta, ng}})
-        if (overlaps(ws, b)) return LA_ERR_ARG;
     return from_hip(la::launch_gdn_mfma_prep(B, H, T, q, k, v, alpha, beta, workspace,
                                              static_cast<hipStream_t>(stream)));
 }
 
-la_status gdn_prefill_scan(int dtype, int B, int H, int T, int dk, int dv, const void* q, const float* S0,
-                           void* o, float* S_out, int chunk, const void* workspace, size_t ws_bytes,
-                           void* stream) {
+la_status gdn_prefill_scan(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta, const float* S0, void* o,
+                           float* S_out, int chunk, void* workspace, size_t ws_bytes, void* stream) {
     size_t heads = 0;
-    la_status st = gdn_split_common(dtype, B, H, T, dk, dv, chunk, workspace, ws_bytes, &heads);
+    const la_status st =
+        gdn_split_common(dtype, B, H, T, dk, dv, chunk, q, k, v, alpha, beta, workspace, ws_bytes, &heads);
     if (st != LA_OK || heads == 0) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (T == 0) return copy_state(S0, S_out, heads * dv * dk, s);
-    if (q == nullptr || o == nullptr) return LA_ERR_NULL;
-    for (const void* p : {q, static_cast<const void*>(o), static_cast<const void*>(S0),
-                          static_cast<const void*>(S_out)})
+    if (T == 0) {
+        if (S0 != nullptr && !aligned16(S0)) return LA_ERR_ALIGN;
+        if (S_out != nullptr && !aligned16(S_out)) return LA_ERR_ALIGN;
+        return copy_state(S0, S_out, heads * dv * dk, s);
+    }
+    if (o == nullptr) return LA_ERR_NULL;
+    for (const void* p : {static_cast<const void*>(o), static_cast<const void*>(S0), static_cast<const void*>(S_out)})
         if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
-    const size_t nqk = heads * T * dk * 2, nv = heads * T * dv * 2, nS = heads * dv * dk * sizeof(float);
+    const size_t nqk = heads * T * dk * 2, nv = heads * T * dv * 2, ng = heads * T * sizeof(float);
+    const size_t nS = heads * dv * dk * sizeof(float);
     const Span ws{workspace, la::gdn_mfma_workspace_bytes(B, H, T, dk, dv, chunk)};
     const Span outs[] = {{o, nv}, {S_out, nS}};
     for (const Span& a : outs) {
-        for (const Span& b : {Span{q, nqk}, ws}) if (overlaps(a, b)) return LA_ERR_ARG;
+        for (const Span& b : {Span{q, nqk}, Span{k, nqk}, Span{v, nv}, Span{alpha, ng}, Span{beta, ng}, ws})
+            if (overlaps(a, b)) return LA_ERR_ARG;
         if (!(a.p == S_out && S_out == S0) && overlaps(a, Span{S0, nS})) return LA_ERR_ARG;
     }
     if (overlaps(outs[0], outs[1])) return LA_ERR_ARG;
-    return from_hip(la::launch_gdn_mfma_scan(B, H, T, q, S0, o, S_out, workspace, s));
+    if (overlaps(ws, Span{S0, nS})) return LA_ERR_ARG;
+    return from_hip(la::launch_gdn_mfma_scan(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, s));
 }
 
 la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv, const void* q,

@@ -41,9 +41,10 @@ hipError_t launch_gdn_chunked_generic(int dtype, int heads, int T, int dk, int d
                                       const float* S0, void* o, float* S_out, hipStream_t stream);
 
 // ---- bf16 matrix-core paths (dk = dv = 128, chunk = 64) -------------------
-// Gated delta (gdn_mfma.hip): per-chunk state-independent pass, then the
-// sequential inter-chunk scan.  The workspace layout is private to that
-// file; gdn_mfma_workspace_bytes sizes it.
+// Gated delta (gdn_mfma.hip): the sequence of each head is cut into
+// segments; prep = the affine map of every segment but the last, scan = the
+// entering state of every segment and then outputs.  The workspace holds the
+// per-(head, segment) state and map; gdn_mfma_workspace_bytes sizes it.
 bool gdn_mfma_supported(int dtype, int dk, int dv, int chunk);
 size_t gdn_mfma_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 hipError_t launch_gdn_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
@@ -52,8 +53,9 @@ hipError_t launch_gdn_mfma(int B, int H, int T, const void* q, const void* k, co
 hipError_t launch_gdn_mfma_prep(int B, int H, int T, const void* q, const void* k, const void* v,
                                 const float* alpha, const float* beta, void* workspace,
                                 hipStream_t stream);
-hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const float* S0, void* o,
-                                float* S_out, const void* workspace, hipStream_t stream);
+hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* S0, void* o,
+                                float* S_out, void* workspace, hipStream_t stream);
 
 // Normalised linear attention, chunked, bf16 in/out (la_mfma.hip).
 bool la_mfma_supported(int dtype, int dk, int dv, int chunk);

@@ -121,25 +121,30 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv,
  * gdn_prefill_prep / gdn_prefill_scan - the two halves of gdn_prefill with
  * LA_FORM_CHUNKED on the matrix-core path (dtype LA_BF16, dk = dv = 128,
  * chunk = 64; other shapes return LA_ERR_UNSUPPORTED).  Same equation and
- * section as gdn_prefill.
- *   prep: everything that does not depend on the carried state, for every
- *     chunk of every head in parallel (chunk-local cumulative log-gates,
- *     K K^T, Q K^T, the unit lower-triangular solve); writes `workspace`.
- *   scan: walks the chunks of each head in order with the float32 state and
- *     writes o and S_out; reads q and the workspace written by prep with the
- *     same B, H, T.
+ * section as gdn_prefill.  The library cuts each head's sequence into
+ * segments of whole chunks (so that the chip is filled even with few heads);
+ * over a segment the recurrence is an affine map of the entering state.
+ *   prep: state-independent; for every segment but the last of every head,
+ *     the segment's map (from k, v, alpha, beta), all segments in parallel;
+ *     writes `workspace`.
+ *   scan: composes the maps with S0 into each segment's entering state, then
+ *     computes o and S_out for all segments in parallel; reads q, k, v,
+ *     alpha, beta and the workspace written by prep for the same B, H, T.
  * gdn_prefill(..., LA_FORM_CHUNKED, 64, ...) is exactly prep followed by scan
  * on one stream.  Callers that split them must order scan after prep (e.g.
  * with an event) and must not reuse the workspace before scan has finished.
- * The workspace layout is private to the library.
+ * The workspace layout is private to the library; when a single segment
+ * covers the sequence the workspace size is 0 and prep does nothing.
  */
 la_status gdn_prefill_prep(int dtype, int B, int H, int T, int dk, int dv,
                            const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, int chunk,
                            void* workspace, size_t ws_bytes, void* stream);
 la_status gdn_prefill_scan(int dtype, int B, int H, int T, int dk, int dv,
-                           const void* q, const float* S0, void* o, float* S_out,
-                           int chunk, const void* workspace, size_t ws_bytes,
+                           const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           const float* S0, void* o, float* S_out,
+                           int chunk, void* workspace, size_t ws_bytes,
                            void* stream);
 
 /*

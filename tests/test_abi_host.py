@@ -168,10 +168,10 @@ def test_split_gdn_validation(lib):
         return lib.gdn_prefill_prep(dtype, B, H, T, dk, dv, f(q), f(k), f(v), f(a), f(b), chunk, f(ws), ws_bytes,
                                     None)
 
-    def scan(dtype=BF16, B=1, H=2, T=100, dk=128, dv=128, q=1, S0=None, o=4, S_out=None, chunk=64, ws=9,
-             ws_bytes=1 << 40):
-        return lib.gdn_prefill_scan(dtype, B, H, T, dk, dv, f(q), f(S0), f(o), f(S_out), chunk, f(ws), ws_bytes,
-                                    None)
+    def scan(dtype=BF16, B=1, H=2, T=100, dk=128, dv=128, q=1, k=2, v=3, a=5, b=6, S0=None, o=4, S_out=None,
+             chunk=64, ws=9, ws_bytes=1 << 40):
+        return lib.gdn_prefill_scan(dtype, B, H, T, dk, dv, f(q), f(k), f(v), f(a), f(b), f(S0), f(o), f(S_out),
+                                    chunk, f(ws), ws_bytes, None)
 
     assert prep(dtype=F32) == LA_ERR_UNSUPPORTED
     assert prep(dk=64, dv=64) == LA_ERR_UNSUPPORTED
@@ -187,5 +187,8 @@ def test_split_gdn_validation(lib):
     assert scan(o=1) == LA_ERR_ARG           # output on top of q
     assert scan(S0=7, S_out=ctypes.c_void_p(BASE + 7 * GiB + 32)) == LA_ERR_ARG
     assert scan(ws=ctypes.c_void_p(BASE + 9 * GiB + 8)) == LA_ERR_ALIGN
-    n = lib.la_workspace_bytes(1, BF16, 1, 2, 100, 128, 128, CHUNKED, 64)
-    assert n > 0 and scan(ws_bytes=n - 1) == LA_ERR_WORKSPACE
+    assert scan(a=None) == LA_ERR_NULL
+    n = lib.la_workspace_bytes(1, BF16, 1, 2, 1000, 128, 128, CHUNKED, 64)
+    assert n > 0 and scan(T=1000, ws_bytes=n - 1) == LA_ERR_WORKSPACE
+    # one segment per head needs no workspace (many heads, short sequence)
+    assert lib.la_workspace_bytes(1, BF16, 64, 8, 64, 128, 128, CHUNKED, 64) == 0

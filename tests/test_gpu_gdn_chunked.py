@@ -33,9 +33,12 @@ def run_gpu(gd, q, k, v, a, b, S0=None, inplace=False, chunk=C):
     return to_host(o), to_host(S)
 
 
+# (the library cuts each head into up to 256 / (B*H) segments of whole chunks:
+#  these cases cover one chunk per segment, several chunks per segment with a
+#  short last segment (4x16x600: 10 chunks -> 3,3,3,1), and a single segment)
 @pytest.mark.parametrize("B,H,T,amean,with_state", [
     (1, 2, 300, 3.0, True), (2, 1, 64, 3.0, False), (1, 3, 65, 3.0, True), (1, 1, 1, 3.0, True),
-    (1, 2, 2000, 6.0, True), (2, 2, 777, 0.0, True)])
+    (1, 2, 2000, 6.0, True), (2, 2, 777, 0.0, True), (4, 16, 600, 3.0, True), (16, 16, 130, 3.0, False)])
 def test_gdn_mfma_small(gd, B, H, T, amean, with_state):
     q, k, v, a, b = synth.gdn_batch(31, B, H, T, D, D, "bf16", alpha_mean=amean)
     S0 = synth.state_batch(32, B, H, D, D, 0.05) if with_state else None
