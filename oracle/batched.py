@@ -64,3 +64,32 @@ def gdn(q, k, v, alpha, beta, form="chunked", chunk=64, S0=None, heads=None):
         else:
             raise ValueError(form)
     return o, S
+
+
+def gdn_step_heads(q, k, v, alpha, beta, S):
+    """One Gated DeltaNet step for many independent heads at once.
+
+    q, k [n, dk]; v [n, dv]; alpha, beta [n]; S [n, dv, dk].  The equation of
+    section "Delta rule and Gated DeltaNet" applied to every head; np.matmul
+    broadcasts over the head axis.  Returns (o [n, dv], S_new).
+    """
+    q, k, v, alpha, beta, S = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, beta, S))
+    dk = k.shape[-1]
+    P = np.eye(dk)[None] - beta[:, None, None] * (k[:, :, None] * k[:, None, :])
+    S_new = alpha[:, None, None] * (S @ P) + beta[:, None, None] * (v[:, :, None] * k[:, None, :])
+    return (S_new @ q[:, :, None])[..., 0], S_new
+
+
+def la_step_heads(q, k, v, S, z):
+    """One normalised linear-attention step for many independent heads.
+
+    q, k [n, dk]; v [n, dv]; S [n, dv, dk]; z [n, dk].  The recurrent form of
+    section "Three forms of one computation" applied to every head.
+    Returns (o [n, dv], S_new, z_new).
+    """
+    q, k, v, S, z = (np.asarray(a, dtype=np.float64) for a in (q, k, v, S, z))
+    fk, fq = phi(k), phi(q)
+    S_new = S + v[:, :, None] * fk[:, None, :]
+    z_new = z + fk
+    o = (S_new @ fq[:, :, None])[..., 0] / np.sum(z_new * fq, axis=1)[:, None]
+    return o, S_new, z_new
