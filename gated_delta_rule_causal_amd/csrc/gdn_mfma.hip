@@ -50,8 +50,7 @@ constexpr int C = 64;        // chunk length
 constexpr int D = 128;       // d_k = d_v
 constexpr int LDQ = D + 8;   // bf16 row stride of 128-wide LDS tiles (272 B)
 constexpr int LDA = C + 8;   // bf16 row stride of 64-wide LDS tiles (144 B)
-constexpr int kThreads = 256;
-constexpr int kItems = C * D / 8 / kThreads;  // 16-byte pieces per thread per 64 x 128 tile
+constexpr int kThreads = 512;                 // 8 waves per workgroup
 constexpr int kTargetBlocks = 256;            // workgroups that fill the chip (one per CU)
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -93,34 +92,39 @@ __device__ __forceinline__ void unpack8(uint4 raw, float* x) {
 
 // ------------------------------------------------------------------ LDS
 struct ChunkTiles {
-    u16 Qs[C][LDQ];     // q rows of the chunk (output kernel only)
-    u16 Ks[C][LDQ];     // k rows
-    u16 Vs[C][LDQ];     // v rows
-    u16 Ws[C][LDQ];     // W rows
-    u16 Kt[D][LDA];     // K~^T: [d][c]
-    u16 Ut[D][LDA];     // Ut^T: [value channel][c]
-    u16 Lb[C][LDA];     // -L (bf16), blocks below the diagonal
-    u16 As[C][LDA];     // decay-masked Q K^T (output kernel only)
-    u16 Ts[4][16][24];  // inverses of the diagonal 16x16 blocks of I + L
+    u16 Qs[C][LDQ];      // q rows (output kernel only)
+    u16 Ks[C][LDQ];      // k rows; dead after K K^T, then reused for the rows of W
+    u16 KtR[D][LDA];     // k transposed: [d][c]
+    u16 Vt[D][LDA];      // v transposed: [value channel][c]
+    u16 Kt[D][LDA];      // K~^T = (diag(e^{g_c - g}) K)^T: [d][c]
+    u16 Ut[D][LDA];      // Ut^T: [value channel][c]
+    u16 Lb[C][LDA];      // -L (bf16)
+    u16 Tm[C][LDA];      // (I + L)^{-1}, lower triangular
+    u16 As[C][LDA];      // decay-masked Q K^T (output kernel only)
     float Ld[4][16][17];  // diagonal blocks of L, fp32
-    float gs[C], bs[C], egs[C];
+    float gs[C], bs[C], egs[C], sws[C], eks[C];  // g, beta, e^g, beta e^g, e^{g_c - g}
 };
 
-// Raw chunk inputs held in registers between chunks.
+// Raw chunk inputs held in registers between chunks.  Item e -> chunk row
+// e % 64, 8 columns starting at 8 (e / 64): rows run fastest across lanes,
+// which makes the transposed LDS stores of k and v conflict-free.
+// NTHR threads (tid 0 .. NTHR-1) share the work; NI 16-byte pieces each.
+template <int NTHR>
 struct RawChunk {
-    uint4 q[kItems], k[kItems], v[kItems];
+    static constexpr int NI = C * D / 8 / NTHR;
+    uint4 q[NI], k[NI], v[NI];
     float a, b;
 };
 
-template <bool WITH_Q>
-__device__ __forceinline__ void fetch_chunk(RawChunk& rc, const u16* __restrict__ q, const u16* __restrict__ k,
+template <bool WITH_Q, int NTHR>
+__device__ __forceinline__ void fetch_chunk(RawChunk<NTHR>& rc, const u16* __restrict__ q, const u16* __restrict__ k,
                                             const u16* __restrict__ v, const float* __restrict__ alpha,
                                             const float* __restrict__ beta, size_t head_tok, int t0, int len,
                                             int tid) {
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-        const int e = tid + kThreads * it;
-        const int row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
+        const int e = tid + NTHR * it;
+        const int row = e & (C - 1), c8 = (e / C) * 8;
         rc.q[it] = rc.k[it] = rc.v[it] = make_uint4(0, 0, 0, 0);
         if (row < len) {
             const size_t gi = (head_tok + t0 + row) * D + c8;
@@ -136,15 +140,23 @@ __device__ __forceinline__ void fetch_chunk(RawChunk& rc, const u16* __restrict_
     }
 }
 
-template <bool WITH_Q>
-__device__ __forceinline__ void stage_chunk(ChunkTiles& sm, const RawChunk& rc, int tid) {
+__device__ __forceinline__ u16 word_half(uint32_t wd, int hi) { return static_cast<u16>(hi ? (wd >> 16) : (wd & 0xffffu)); }
+
+template <bool WITH_Q, int NTHR>
+__device__ __forceinline__ void stage_chunk(ChunkTiles& sm, const RawChunk<NTHR>& rc, int tid) {
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-        const int e = tid + kThreads * it;
-        const int row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
+        const int e = tid + NTHR * it;
+        const int row = e & (C - 1), c8 = (e / C) * 8;
         if (WITH_Q) *reinterpret_cast<uint4*>(&sm.Qs[row][c8]) = rc.q[it];
         *reinterpret_cast<uint4*>(&sm.Ks[row][c8]) = rc.k[it];
-        *reinterpret_cast<uint4*>(&sm.Vs[row][c8]) = rc.v[it];
+        const uint32_t wk[4] = {rc.k[it].x, rc.k[it].y, rc.k[it].z, rc.k[it].w};
+        const uint32_t wv[4] = {rc.v[it].x, rc.v[it].y, rc.v[it].z, rc.v[it].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            sm.KtR[c8 + j][row] = word_half(wk[j >> 1], j & 1);
+            sm.Vt[c8 + j][row] = word_half(wv[j >> 1], j & 1);
+        }
     }
     if (tid < C) {
         float x = __logf(rc.a);
@@ -153,109 +165,179 @@ __device__ __forceinline__ void stage_chunk(ChunkTiles& sm, const RawChunk& rc, 
             const float y = __shfl_up(x, off, 64);
             if (tid >= off) x += y;
         }
+        const float gl = __shfl(x, C - 1, 64);
+        const float eg = __expf(x);
         sm.gs[tid] = x;
         sm.bs[tid] = rc.b;
-        sm.egs[tid] = __expf(x);
+        sm.egs[tid] = eg;
+        sm.sws[tid] = rc.b * eg;
+        sm.eks[tid] = __expf(gl - x);
     }
 }
 
-// The state-independent tiles of the staged chunk (W, Ut^T, K~^T and, with
-// WITH_Q, A), all in LDS.  Called by all four waves; ends on a barrier.
+// B operand (K = 16) of a diagonal block of Tm: lane (r, g) holds T[4g+i][r].
+__device__ __forceinline__ short4v tdiag_b(const ChunkTiles& sm, int blk, int r, int g) {
+    short4v x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = static_cast<short>(sm.Tm[16 * blk + 4 * g + i][16 * blk + r]);
+    return x;
+}
+
+// The state-independent tiles of the staged chunk (rows of W, Ut^T, K~^T
+// and, with WITH_Q, A), all in LDS.  Called by all eight waves; starts and
+// ends on a barrier.
 template <bool WITH_Q>
 __device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid) {
-    const int w = tid >> 6;
+    // The wave index must be a scalar: the matrix-core instructions below sit
+    // in branches on it, and a branch the compiler takes as divergent runs
+    // both sides under EXEC masks, where an MFMA would still write its
+    // destination registers.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int r = lane & 15;
     const int g = lane >> 4;
+    u16(*Ws)[LDQ] = sm.Ks;
     __syncthreads();
 
-    // K K^T (and Q K^T) for row tile w; L and A in their final forms
-    for (int ct = 0; ct < 4; ++ct) {
-        if (ct <= w) {
-            f32x4 acck = zero4(), accq = zero4();
+    // waves 0-3: K K^T for row tile w -> L (-L in bf16, diagonal blocks in fp32)
+    // waves 4-7: Q K^T for row tile w-4 -> A (decay-masked, causal)
+    if (w < 4 || WITH_Q) {
+        const int rt = w & 3;
+        const bool kk = w < 4;
+        for (int ct = 0; ct < 4; ++ct) {
+            if (ct <= rt) {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 bk = lds_bf16x8(&sm.Ks[16 * ct + r][32 * s + 8 * g]);
-                acck = mfma16x16x32(lds_bf16x8(&sm.Ks[16 * w + r][32 * s + 8 * g]), bk, acck);
-                if (WITH_Q) accq = mfma16x16x32(lds_bf16x8(&sm.Qs[16 * w + r][32 * s + 8 * g]), bk, accq);
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8 bk = lds_bf16x8(&sm.Ks[16 * ct + r][32 * s + 8 * g]);
+                    const bf16x8 a = kk ? lds_bf16x8(&sm.Ks[16 * rt + r][32 * s + 8 * g])
+                                        : lds_bf16x8(&sm.Qs[16 * rt + r][32 * s + 8 * g]);
+                    acc = mfma16x16x32(a, bk, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
+                    const float dec = __expf(fminf(sm.gs[row] - sm.gs[col], 0.f));
+                    if (kk) {
+                        const float lval = col < row ? sm.bs[row] * dec * acc[i] : 0.f;
+                        sm.Lb[row][col] = f32_to_bf16_bits(-lval);
+                        if (ct == rt) sm.Ld[rt][4 * g + i][r] = lval;
+                    } else {
+                        sm.As[row][col] = f32_to_bf16_bits(col <= row ? dec * acc[i] : 0.f);
+                    }
+                }
+            } else if (!kk) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.As[16 * rt + 4 * g + i][16 * ct + r] = 0;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i, col = 16 * ct + r;
-                const float dec = __expf(fminf(sm.gs[row] - sm.gs[col], 0.f));
-                const float lval = col < row ? sm.bs[row] * dec * acck[i] : 0.f;
-                sm.Lb[row][col] = f32_to_bf16_bits(-lval);
-                if (ct == w) sm.Ld[w][4 * g + i][r] = lval;
-                if (WITH_Q) sm.As[row][col] = f32_to_bf16_bits(col <= row ? dec * accq[i] : 0.f);
-            }
-        } else if (WITH_Q) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.As[16 * w + 4 * g + i][16 * ct + r] = 0;
         }
     }
     __syncthreads();
 
-    // wave 0: inverses of the diagonal blocks of I + L (one column per lane, fp32)
-    // waves 1-3: K~^T[d][c] = e^{g_c - g_row} K[c][d]
     if (w == 0) {
-        const int b = lane >> 4, c = lane & 15;
-        float x[16];
+        // (I + L)^{-1}: diagonal 16x16 blocks by forward substitution, one
+        // column per lane, fp32 ...
+        {
+            const int b = lane >> 4, c = lane & 15;
+            float x[16];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float val = rr == c ? 1.f : 0.f;
+            for (int rr = 0; rr < 16; ++rr) {
+                float val = rr == c ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < rr; ++j) val = fmaf(-sm.Ld[b][rr][j], x[j], val);
-            x[rr] = val;
-            sm.Ts[b][rr][c] = f32_to_bf16_bits(val);
+                for (int j = 0; j < rr; ++j) val = fmaf(-sm.Ld[b][rr][j], x[j], val);
+                x[rr] = val;
+                sm.Tm[16 * b + rr][16 * b + c] = f32_to_bf16_bits(val);
+            }
+            // blocks above the diagonal that the 32-wide operand slices touch
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sm.Tm[4 * g + i][16 + r] = 0;
+                sm.Tm[32 + 4 * g + i][48 + r] = 0;
+            }
         }
+        // ... then the blocks below it by diagonal distance:
+        //     T_ij = T_ii * sum_{j<=k<i} (-L_ik) T_kj
+        const short4v t00 = tdiag_b(sm, 0, r, g), t11 = tdiag_b(sm, 1, r, g), t22 = tdiag_b(sm, 2, r, g);
+        auto nl = [&](int i, int j) { return lds_short4(&sm.Lb[16 * i + r][16 * j + 4 * g]); };
+        auto ta = [&](int i) { return lds_short4(&sm.Tm[16 * i + r][16 * i + 4 * g]); };
+        const short4v t10 = to_bf16x4(mfma16x16x16(ta(1), to_bf16x4(mfma16x16x16(nl(1, 0), t00, zero4())), zero4()));
+        const short4v t21 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(mfma16x16x16(nl(2, 1), t11, zero4())), zero4()));
+        const short4v t32 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(mfma16x16x16(nl(3, 2), t22, zero4())), zero4()));
+        f32x4 y = mfma16x16x16(nl(2, 1), t10, mfma16x16x16(nl(2, 0), t00, zero4()));
+        const short4v t20 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(y), zero4()));
+        y = mfma16x16x16(nl(3, 2), t21, mfma16x16x16(nl(3, 1), t11, zero4()));
+        const short4v t31 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
+        y = mfma16x16x16(nl(3, 2), t20, mfma16x16x16(nl(3, 1), t10, mfma16x16x16(nl(3, 0), t00, zero4())));
+        const short4v t30 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
+        auto put = [&](int i, int j, short4v t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.Tm[16 * i + 4 * g + e][16 * j + r] = static_cast<u16>(t[e]);
+        };
+        put(1, 0, t10);
+        put(2, 1, t21);
+        put(3, 2, t32);
+        put(2, 0, t20);
+        put(3, 1, t31);
+        put(3, 0, t30);
     } else {
-        const float gl = sm.gs[C - 1];
+        // waves 1-7: K~^T = e^{g_c - g} K^T, 16 bytes at a time
         for (int e = tid - 64; e < D * (C / 8); e += kThreads - 64) {
             const int d = e >> 3, c0 = (e & 7) * 8;
             float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = bf16_bits_to_f32(sm.Ks[c0 + j][d]) * __expf(gl - sm.gs[c0 + j]);
-            *reinterpret_cast<bf16x8*>(&sm.Kt[d][c0]) = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+            unpack8(*reinterpret_cast<const uint4*>(&sm.KtR[d][c0]), x);
+            *reinterpret_cast<bf16x8*>(&sm.Kt[d][c0]) =
+                pack8(x[0] * sm.eks[c0], x[1] * sm.eks[c0 + 1], x[2] * sm.eks[c0 + 2], x[3] * sm.eks[c0 + 3],
+                      x[4] * sm.eks[c0 + 4], x[5] * sm.eks[c0 + 5], x[6] * sm.eks[c0 + 6], x[7] * sm.eks[c0 + 7]);
         }
     }
     __syncthreads();
 
-    // blocked forward substitution: X_rb = T_rb,rb (RHS_rb - sum_{kb<rb} L_rb,kb X_kb);
-    // waves 0,1 solve the two 64-column halves of W, waves 2,3 those of Ut
+    // W = (I + L)^{-1} diag(beta e^g) K and Ut = (I + L)^{-1} diag(beta) V as
+    // plain products; the row scalings fold into the (I + L)^{-1} operand.
+    // waves 0-3: W^T = K^T (Tm diag(beta e^g))^T for d rows 32w..32w+31, so each
+    //            lane ends up holding 4 consecutive d of one W row (8-byte stores);
+    // waves 4-7: Ut = (Tm diag(beta)) V for value channels 32(w-4)..+31.
     {
-        const bool isW = w < 2;
-        const int cb = (w & 1) * 64;
-        short4v Xb[4][4];
+        const bool isW = w < 4;
+        const int w4 = w & 3;
+        f32x4 acc[2][4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            f32x4 acc[4];
+        for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * rb + 4 * g + i;
-                const float sc = isW ? sm.bs[row] * sm.egs[row] : sm.bs[row];
+            for (int ct = 0; ct < 4; ++ct) acc[a2][ct] = zero4();
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    acc[nt][i] = sc * bf16_bits_to_f32(isW ? sm.Ks[row][cb + 16 * nt + r] : sm.Vs[row][cb + 16 * nt + r]);
-            }
+        for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
-            for (int kb = 0; kb < rb; ++kb) {
-                const short4v a = lds_short4(&sm.Lb[16 * rb + r][16 * kb + 4 * g]);
+            for (int s = 0; s < 2; ++s) {
+                if (s == 1 && ct < 2) continue;  // (I + L)^{-1} is lower triangular
+                float t[8];
+                unpack8(*reinterpret_cast<const uint4*>(&sm.Tm[16 * ct + r][32 * s + 8 * g]), t);
+                const float* sc = isW ? sm.sws : sm.bs;
+                const bf16x8 tf = pack8(t[0] * sc[32 * s + 8 * g], t[1] * sc[32 * s + 8 * g + 1],
+                                        t[2] * sc[32 * s + 8 * g + 2], t[3] * sc[32 * s + 8 * g + 3],
+                                        t[4] * sc[32 * s + 8 * g + 4], t[5] * sc[32 * s + 8 * g + 5],
+                                        t[6] * sc[32 * s + 8 * g + 6], t[7] * sc[32 * s + 8 * g + 7]);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) acc[nt] = mfma16x16x16(a, Xb[kb][nt], acc[nt]);
-            }
-            const short4v tb = lds_short4(&sm.Ts[rb][r][4 * g]);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                Xb[rb][nt] = to_bf16x4(mfma16x16x16(tb, to_bf16x4(acc[nt]), zero4()));
-                if (isW) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sm.Ws[16 * rb + 4 * g + i][cb + 16 * nt + r] = static_cast<u16>(Xb[rb][nt][i]);
-                } else {
-                    *reinterpret_cast<short4v*>(&sm.Ut[cb + 16 * nt + r][16 * rb + 4 * g]) = Xb[rb][nt];
+                for (int a2 = 0; a2 < 2; ++a2) {
+                    const int rowx = 32 * w4 + 16 * a2 + r;  // d (W) or value channel (Ut)
+                    const bf16x8 xf = isW ? lds_bf16x8(&sm.KtR[rowx][32 * s + 8 * g])
+                                          : lds_bf16x8(&sm.Vt[rowx][32 * s + 8 * g]);
+                    // W^T tile (d x c):  A = K^T rows, B = scaled Tm rows
+                    // Ut tile (c x v):   A = scaled Tm rows, B = V^T rows
+                    acc[a2][ct] = isW ? mfma16x16x32(xf, tf, acc[a2][ct]) : mfma16x16x32(tf, xf, acc[a2][ct]);
                 }
             }
         }
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const short4v h = to_bf16x4(acc[a2][ct]);
+                if (isW)  // lane holds W^T[d = 32w+16a2+4g+i][c = 16ct+r]
+                    *reinterpret_cast<short4v*>(&Ws[16 * ct + r][32 * w4 + 16 * a2 + 4 * g]) = h;
+                else      // lane holds Ut[c = 16ct+4g+i][v = 32(w-4)+16a2+r]
+                    *reinterpret_cast<short4v*>(&sm.Ut[32 * w4 + 16 * a2 + r][16 * ct + 4 * g]) = h;
+            }
     }
     __syncthreads();
 }
@@ -269,6 +351,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][
                                            int lane, u16* __restrict__ o, size_t o_row0, int len) {
     const int r = lane & 15;
     const int g = lane >> 4;
+    const u16(*Ws)[LDQ] = sm.Ks;
     // X = W P, U = Ut - X (or -X), one half of the chunk rows at a time.  W rows
     // are taken in the permuted order so X lands in U's layout; the bf16 copy
     // of the state (the B operand) is packed on the fly to save registers.
@@ -280,8 +363,8 @@ __device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][
         for (int nt = 0; nt < NT; ++nt) Xa[nt] = Xb[nt] = zero4();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const bf16x8 a0 = lds_bf16x8(&sm.Ws[perm_row(2 * s2, r)][32 * s + 8 * g]);
-            const bf16x8 a1 = lds_bf16x8(&sm.Ws[perm_row(2 * s2 + 1, r)][32 * s + 8 * g]);
+            const bf16x8 a0 = lds_bf16x8(&Ws[perm_row(2 * s2, r)][32 * s + 8 * g]);
+            const bf16x8 a1 = lds_bf16x8(&Ws[perm_row(2 * s2 + 1, r)][32 * s + 8 * g]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const bf16x8 pb = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
@@ -412,9 +495,21 @@ __device__ __forceinline__ void store_state(const f32x4 (&P)[NT][8], float* rows
     }
 }
 
-// ---- workspace: per (head, segment) three 128 x 128 fp32 matrices in the
-// state's row layout: the entering state P_s, and the segment map N_s, M_s
-// (M_s stored as rows j of M^T: Mst[j][d] = M[d][j]).
+// The same slice written as plain row-major M[d][j] (j = column of P).
+template <int NT>
+__device__ __forceinline__ void store_state_rowmajor(const f32x4 (&P)[NT][8], float* M, int col0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) M[static_cast<size_t>(perm_row(t, 4 * g + i)) * D + col0 + 16 * nt + r] = P[nt][t][i];
+}
+
+// ---- workspace: per (head, segment) three 128 x 128 fp32 matrices: the
+// entering state P_s and N_s in the state's row layout ([value channel][d]),
+// and M_s row-major ([d][j]).
 constexpr size_t kMat = static_cast<size_t>(D) * D;
 __device__ __forceinline__ size_t ws_P(int bh, int G, int s) { return (static_cast<size_t>(bh) * G + s) * 3 * kMat; }
 __device__ __forceinline__ size_t ws_N(int bh, int G, int s) { return ws_P(bh, G, s) + kMat; }
@@ -429,24 +524,25 @@ __global__ __launch_bounds__(kThreads) void gdn_map_kernel(int BH, int T, int NC
     const int bh = blockIdx.x / (G - 1);
     const int seg = blockIdx.x - bh * (G - 1);
     if (bh >= BH) return;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int n0 = seg * SEGC, n1 = min(NC, n0 + SEGC);
     const size_t head_tok = static_cast<size_t>(bh) * T;
-    // waves 0,1: N columns (value channels 64w..64w+63), start 0;
-    // waves 2,3: M columns j = 64(w-2)..+63, start = identity
-    const bool npart = w < 2;
-    const int col0 = 64 * (w & 1);
-    f32x4 P[4][8];
+    // waves 0-3: N columns (value channels 32w..32w+31), start 0;
+    // waves 4-7: M columns j = 32(w-4)..+31, start = identity
+    const bool npart = w < 4;
+    const int col0 = 32 * (w & 3);
+    f32x4 P[2][8];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 P[nt][t][i] = (!npart && perm_row(t, 4 * g + i) == col0 + 16 * nt + r) ? 1.f : 0.f;
 
-    RawChunk rc;
+    RawChunk<kThreads> rc;
     fetch_chunk<false>(rc, nullptr, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), tid);
     for (int n = n0; n < n1; ++n) {
         __syncthreads();
@@ -454,66 +550,89 @@ __global__ __launch_bounds__(kThreads) void gdn_map_kernel(int BH, int T, int NC
         if (n + 1 < n1)
             fetch_chunk<false>(rc, nullptr, k, v, alpha, beta, head_tok, (n + 1) * C, min(C, T - (n + 1) * C), tid);
         chunk_tiles<false>(sm, tid);
-        scan_chunk<4, false>(sm, P, col0, npart, lane, nullptr, 0, 0);
+        scan_chunk<2, false>(sm, P, col0, npart, lane, nullptr, 0, 0);
     }
-    store_state<4>(P, ws + (npart ? ws_N(bh, G, seg) : ws_M(bh, G, seg)), col0, lane);
+    if (npart)
+        store_state<2>(P, ws + ws_N(bh, G, seg), col0, lane);
+    else
+        store_state_rowmajor<2>(P, ws + ws_M(bh, G, seg), col0, lane);
 }
 
 // ============================================================ combine
-// One workgroup per (head, 16 state rows): P_0 = S0, P_{s+1} = M_s P_s + N_s
-// in fp32; writes every P_s to the workspace.  Thread (row, 8 d's).
-__global__ __launch_bounds__(kThreads) void gdn_combine_kernel(int BH, int G, const float* S0, float* __restrict__ ws) {
-    __shared__ __attribute__((aligned(16))) float Ms[D][D];
-    __shared__ float Ps[16][D + 4];
+// One workgroup (4 waves) per (head, 16 value channels): P_0 = S0,
+// P_{s+1} = M_s P_s + N_s, writing every P_s.  The products run on MFMA with
+// both operands split into bf16 high and low parts (hi*hi + hi*lo + lo*hi),
+// which keeps about 16 significant bits.  Wave w owns d rows 32w..32w+31.
+constexpr int kCombineThreads = 256;
+
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+    float h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        h[j] = bf16_bits_to_f32(f32_to_bf16_bits(x[j]));
+        l[j] = x[j] - h[j];
+    }
+    hi = pack8(h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]);
+    lo = pack8(l[0], l[1], l[2], l[3], l[4], l[5], l[6], l[7]);
+}
+
+__global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, int G, const float* S0,
+                                                                      float* __restrict__ ws) {
+    __shared__ __attribute__((aligned(16))) float Ps[16][D + 4];  // P_s: [value channel][j]
     const int bh = blockIdx.x >> 3;
     const int tile = blockIdx.x & 7;
     if (bh >= BH) return;
-    const int tid = threadIdx.x;
-    const int rl = tid >> 4;           // local state row (value channel 16 tile + rl)
-    const int d0 = (tid & 15) * 8;     // 8 consecutive d
-    const int row = 16 * tile + rl;
-    float p[8];
-    {
-        const float* src = S0 ? S0 + (static_cast<size_t>(bh) * D + row) * D + d0 : nullptr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = src ? src[e] : 0.f;
-    }
-    float* dst = ws + ws_P(bh, G, 0) + static_cast<size_t>(row) * D + d0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        dst[e] = p[e];
-        Ps[rl][d0 + e] = p[e];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    // P_0 = S0 (zeros when absent) for value channels 16 tile .. +15
+    for (int e = tid; e < 16 * D / 4; e += kCombineThreads) {
+        const int rl = e / (D / 4), d4 = (e % (D / 4)) * 4;
+        const size_t off = static_cast<size_t>(16 * tile + rl) * D + d4;
+        const float4 x = S0 ? *reinterpret_cast<const float4*>(S0 + static_cast<size_t>(bh) * kMat + off)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(&Ps[rl][d4]) = x;
+        *reinterpret_cast<float4*>(ws + ws_P(bh, G, 0) + off) = x;
     }
     for (int s = 0; s + 1 < G; ++s) {
-        const float* Mg = ws + ws_M(bh, G, s);
-        for (int e4 = tid; e4 < D * D / 4; e4 += kThreads)
-            reinterpret_cast<float4*>(&Ms[0][0])[e4] = reinterpret_cast<const float4*>(Mg)[e4];
         __syncthreads();
-        const float* Ng = ws + ws_N(bh, G, s) + static_cast<size_t>(row) * D + d0;
-        float acc[8];
+        const float* M = ws + ws_M(bh, G, s);
+        f32x4 acc[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = Ng[e];
-        for (int j = 0; j < D; ++j) {
-            const float pj = Ps[rl][j];
-            const float4 m0 = *reinterpret_cast<const float4*>(&Ms[j][d0]);
-            const float4 m1 = *reinterpret_cast<const float4*>(&Ms[j][d0 + 4]);
-            acc[0] = fmaf(m0.x, pj, acc[0]);
-            acc[1] = fmaf(m0.y, pj, acc[1]);
-            acc[2] = fmaf(m0.z, pj, acc[2]);
-            acc[3] = fmaf(m0.w, pj, acc[3]);
-            acc[4] = fmaf(m1.x, pj, acc[4]);
-            acc[5] = fmaf(m1.y, pj, acc[5]);
-            acc[6] = fmaf(m1.z, pj, acc[6]);
-            acc[7] = fmaf(m1.w, pj, acc[7]);
+        for (int mt = 0; mt < 2; ++mt) {
+            // N_s[d][v] is stored as [v][d]: lane (r, g) wants rows d = 32w+16mt+4g..+3 of column v = r
+            const float4 n4 = *reinterpret_cast<const float4*>(ws + ws_N(bh, G, s) +
+                                                              static_cast<size_t>(16 * tile + r) * D + 32 * w +
+                                                              16 * mt + 4 * g);
+            acc[mt] = f32x4{n4.x, n4.y, n4.z, n4.w};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 ph, pl;
+            split8(&Ps[r][32 * ks + 8 * g], ph, pl);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const float* mrow = M + static_cast<size_t>(32 * w + 16 * mt + r) * D + 32 * ks + 8 * g;
+                float mv[8];
+                const float4 m0 = *reinterpret_cast<const float4*>(mrow);
+                const float4 m1 = *reinterpret_cast<const float4*>(mrow + 4);
+                mv[0] = m0.x; mv[1] = m0.y; mv[2] = m0.z; mv[3] = m0.w;
+                mv[4] = m1.x; mv[5] = m1.y; mv[6] = m1.z; mv[7] = m1.w;
+                bf16x8 mh, ml;
+                split8(mv, mh, ml);
+                acc[mt] = mfma16x16x32(mh, ph, acc[mt]);
+                acc[mt] = mfma16x16x32(mh, pl, acc[mt]);
+                acc[mt] = mfma16x16x32(ml, ph, acc[mt]);
+            }
         }
         __syncthreads();
-        float* out = ws + ws_P(bh, G, s + 1) + static_cast<size_t>(row) * D + d0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            out[e] = acc[e];
-            Ps[rl][d0 + e] = acc[e];
+        for (int mt = 0; mt < 2; ++mt) {
+            // lane holds P_{s+1}[d = 32w+16mt+4g+i][v = r]
+            const int d0 = 32 * w + 16 * mt + 4 * g;
+            const float4 x = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+            *reinterpret_cast<float4*>(&Ps[r][d0]) = x;
+            *reinterpret_cast<float4*>(ws + ws_P(bh, G, s + 1) + static_cast<size_t>(16 * tile + r) * D + d0) = x;
         }
-        __syncthreads();
     }
 }
 
@@ -528,27 +647,40 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
     const int bh = blockIdx.x / G;
     const int seg = blockIdx.x - bh * G;
     if (bh >= BH) return;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branch below is scalar
     const int n0 = seg * SEGC, n1 = min(NC, n0 + SEGC);
     const size_t head_tok = static_cast<size_t>(bh) * T;
-    const int col0 = 32 * w;  // this wave's value channels: col0 .. col0 + 31
-    f32x4 P[2][8];
-    // entering state: S0 itself when the sequence is one segment, else the
-    // combined state (segment 0 included, so S_out may alias S0)
-    load_state<2>(P, G == 1 ? (S0 ? S0 + static_cast<size_t>(bh) * kMat : nullptr) : ws + ws_P(bh, G, seg), col0,
-                  lane);
-
-    RawChunk rc;
-    fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), tid);
-    for (int n = n0; n < n1; ++n) {
-        const int t0 = n * C;
-        __syncthreads();
-        stage_chunk<true>(sm, rc, tid);
-        if (n + 1 < n1) fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, t0 + C, min(C, T - t0 - C), tid);
-        chunk_tiles<true>(sm, tid);
-        scan_chunk<2, true>(sm, P, col0, true, lane, o, head_tok + t0, min(C, T - t0));
+    // Waves 0-3 carry the state (32 value channels each); waves 4-7 stage the
+    // chunks and hold the next chunk's raw inputs.  All eight build the chunk
+    // tiles.  The two loops meet at the same barriers (five per chunk), and
+    // neither set of waves keeps the other's registers live.
+    if (w < 4) {
+        const int col0 = 32 * w;
+        f32x4 P[2][8];
+        // entering state: S0 itself when the sequence is one segment, else the
+        // combined state (segment 0 included, so S_out may alias S0)
+        load_state<2>(P, G == 1 ? (S0 ? S0 + static_cast<size_t>(bh) * kMat : nullptr) : ws + ws_P(bh, G, seg),
+                      col0, lane);
+        for (int n = n0; n < n1; ++n) {
+            const int t0 = n * C;
+            __syncthreads();
+            chunk_tiles<true>(sm, tid);
+            scan_chunk<2, true>(sm, P, col0, true, lane, o, head_tok + t0, min(C, T - t0));
+        }
+        if (seg == G - 1 && S_out) store_state<2>(P, S_out + static_cast<size_t>(bh) * kMat, col0, lane);
+    } else {
+        const int ptid = tid - kThreads / 2;
+        RawChunk<kThreads / 2> rc;
+        fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), ptid);
+        for (int n = n0; n < n1; ++n) {
+            const int t0 = n * C;
+            __syncthreads();
+            stage_chunk<true>(sm, rc, ptid);
+            if (n + 1 < n1) fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, t0 + C, min(C, T - t0 - C), ptid);
+            chunk_tiles<true>(sm, tid);
+        }
     }
-    if (seg == G - 1 && S_out) store_state<2>(P, S_out + static_cast<size_t>(bh) * kMat, col0, lane);
 }
 
 struct Plan {
@@ -601,7 +733,7 @@ hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const void* 
     const Plan p = make_plan(BH, T);
     float* ws = static_cast<float*>(workspace);
     if (p.G > 1) {
-        hipLaunchKernelGGL(gdn_combine_kernel, dim3(static_cast<unsigned>(BH) * 8), dim3(kThreads), 0, stream, BH,
+        hipLaunchKernelGGL(gdn_combine_kernel, dim3(static_cast<unsigned>(BH) * 8), dim3(kCombineThreads), 0, stream, BH,
                            p.G, S0, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

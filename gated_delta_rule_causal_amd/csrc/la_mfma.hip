@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: MFMAs sit in branches on it
     const int lane = tid & 63;
     const int r = lane & 15;
     const int g = lane >> 4;
