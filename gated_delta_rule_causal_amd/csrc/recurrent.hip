@@ -14,11 +14,17 @@
 // in place); with T > 1 it is the recurrent prefill form.
 //
 // Rows of S evolve independently (each new row depends only on the same old
-// row and the token), so a block owns one head and splits its rows over
-// lane groups: LPR = dk/8 lanes per row, 8 fp32 state elements per lane held
-// as two float4 (columns [4l, 4l+4) and [dk/2 + 4l, dk/2 + 4l + 4) for lane l
-// of the group, so one load instruction covers 256 contiguous bytes of a row).
-// Dot products reduce over the LPR lanes with xor-shuffles.
+// row and the token), so a block owns SPLIT-th of one head's rows and splits
+// them over lane groups: LPR = dk/8 lanes per row, 8 fp32 state elements per
+// lane held as two float4 (columns [4l, 4l+4) and [dk/2 + 4l, dk/2 + 4l + 4)
+// for lane l of the group, so one load instruction covers 256 contiguous
+// bytes of a row).  Dot products reduce over the LPR lanes with xor-shuffles.
+// The gated-delta kind cuts each head's rows in two blocks (twice the blocks,
+// half the registers); the normalised kind keeps one block per head because
+// every row needs the shared normaliser z, which is updated in place.
+// The state is touched exactly once per call, so its loads and stores carry
+// the nontemporal hint: the decode step streams the whole state through HBM
+// and nothing it moves is reused by the next kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,6 +40,25 @@ struct RowSlice {
     static constexpr int RG = kThreads / LPR;  // row groups per block
 };
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_state8(const float* row, int c0, int c1, float* s) {
+    const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(row + c0));
+    const f32x4v b = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(row + c1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        s[e] = a[e];
+        s[4 + e] = b[e];
+    }
+}
+
+__device__ __forceinline__ void store_state8(float* row, int c0, int c1, const float* s) {
+    const f32x4v a = {s[0], s[1], s[2], s[3]};
+    const f32x4v b = {s[4], s[5], s[6], s[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4v*>(row + c0));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4v*>(row + c1));
+}
+
 template <class IO>
 __device__ __forceinline__ void load_slice(const typename IO::T* p, size_t base, int c0, int c1,
                                            float* out) {
@@ -41,7 +66,7 @@ __device__ __forceinline__ void load_slice(const typename IO::T* p, size_t base,
     IO::load4(p, base + c1, out + 4);
 }
 
-template <int KIND, class IO, int DK, int R>
+template <int KIND, class IO, int DK, int R, int SPLIT, bool ONE>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     int T, int DV, const typename IO::T* __restrict__ q, const typename IO::T* __restrict__ k,
     const typename IO::T* __restrict__ v, const float* __restrict__ alpha,
@@ -49,9 +74,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     typename IO::T* __restrict__ o) {
     constexpr int LPR = RowSlice<DK>::LPR;
     constexpr int RG = RowSlice<DK>::RG;
-    const int head = blockIdx.x;
+    static_assert(KIND == kGatedDelta || SPLIT == 1, "z is shared by all rows of a head");
+    const int head = blockIdx.x / SPLIT;
     const int li = threadIdx.x % LPR;
-    const int rg = threadIdx.x / LPR;
+    const int rg = threadIdx.x / LPR + (blockIdx.x % SPLIT) * RG * R;  // first row of this lane group
     const int c0 = 4 * li;
     const int c1 = DK / 2 + 4 * li;
     const size_t sbase = static_cast<size_t>(head) * DV * DK;
@@ -62,10 +88,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     for (int j = 0; j < R; ++j) {
         const int r = rg + RG * j;
         if (S0 != nullptr && r < DV) {
-            const float4 a = *reinterpret_cast<const float4*>(S0 + sbase + static_cast<size_t>(r) * DK + c0);
-            const float4 b = *reinterpret_cast<const float4*>(S0 + sbase + static_cast<size_t>(r) * DK + c1);
-            s[j][0] = a.x; s[j][1] = a.y; s[j][2] = a.z; s[j][3] = a.w;
-            s[j][4] = b.x; s[j][5] = b.y; s[j][6] = b.z; s[j][7] = b.w;
+            load_state8(S0 + sbase + static_cast<size_t>(r) * DK, c0, c1, s[j]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
@@ -103,14 +126,15 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     };
     fetch(0);
 
-    for (int t = 0; t < T; ++t) {
+    const int steps = ONE ? 1 : T;  // ONE: the decode step (T = 1), no prefetch path
+    for (int t = 0; t < steps; ++t) {
         float kc[8], qc[8], vc[R];
 #pragma unroll
         for (int e = 0; e < 8; ++e) { kc[e] = kn[e]; qc[e] = qn[e]; }
 #pragma unroll
         for (int j = 0; j < R; ++j) vc[j] = vn[j];
         const float a = an, b = bn;
-        if (t + 1 < T) fetch(t + 1);
+        if (!ONE && t + 1 < T) fetch(t + 1);
         const size_t to = (static_cast<size_t>(head) * T + t) * DV;
 
         if constexpr (KIND == kGatedDelta) {
@@ -166,11 +190,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int r = rg + RG * j;
-            if (r < DV) {
-                float* row = S_out + sbase + static_cast<size_t>(r) * DK;
-                *reinterpret_cast<float4*>(row + c0) = make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
-                *reinterpret_cast<float4*>(row + c1) = make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
-            }
+            if (r < DV) store_state8(S_out + sbase + static_cast<size_t>(r) * DK, c0, c1, s[j]);
         }
     }
     if constexpr (KIND == kNormalized) {
@@ -185,27 +205,49 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     }
 }
 
-template <int KIND, class IO, int DK>
-hipError_t launch_dk(int heads, int T, int dv, const void* q, const void* k, const void* v,
+template <int KIND, class IO, int DK, bool ONE>
+hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, const void* v,
                      const float* alpha, const float* beta, const float* S0, float* S_out,
                      const float* z0, float* z_out, void* o, hipStream_t stream) {
     using E = typename IO::T;
     constexpr int RG = RowSlice<DK>::RG;
-    const int R = (dv + RG - 1) / RG;
-    dim3 grid(heads), block(kThreads);
+    // gated delta: two blocks per head when each still gets a whole row group
+    const int split = (KIND == kGatedDelta && dv >= 2 * RG) ? 2 : 1;
+    const int R = (dv / split + RG - 1) / RG;
+    dim3 grid(static_cast<unsigned>(heads) * split), block(kThreads);
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, T, dv, static_cast<const E*>(q),
                            static_cast<const E*>(k), static_cast<const E*>(v), alpha, beta, S0,
                            S_out, z0, z_out, static_cast<E*>(o));
         return hipGetLastError();
     };
+    if (split == 2) {
+        if constexpr (KIND == kGatedDelta) {
+            switch (R) {
+                case 1: return args(recurrent_kernel<KIND, IO, DK, 1, 2, ONE>);
+                case 2: return args(recurrent_kernel<KIND, IO, DK, 2, 2, ONE>);
+                case 4: return args(recurrent_kernel<KIND, IO, DK, 4, 2, ONE>);
+                default: return hipErrorInvalidValue;
+            }
+        }
+        return hipErrorInvalidValue;
+    }
     switch (R) {
-        case 1: return args(recurrent_kernel<KIND, IO, DK, 1>);
-        case 2: return args(recurrent_kernel<KIND, IO, DK, 2>);
-        case 4: return args(recurrent_kernel<KIND, IO, DK, 4>);
-        case 8: return args(recurrent_kernel<KIND, IO, DK, 8>);
+        case 1: return args(recurrent_kernel<KIND, IO, DK, 1, 1, ONE>);
+        case 2: return args(recurrent_kernel<KIND, IO, DK, 2, 1, ONE>);
+        case 4: return args(recurrent_kernel<KIND, IO, DK, 4, 1, ONE>);
+        case 8: return args(recurrent_kernel<KIND, IO, DK, 8, 1, ONE>);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int KIND, class IO, int DK>
+hipError_t launch_dk(int heads, int T, int dv, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const float* S0, float* S_out,
+                     const float* z0, float* z_out, void* o, hipStream_t stream) {
+    if (T == 1)
+        return launch_rows<KIND, IO, DK, true>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
+    return launch_rows<KIND, IO, DK, false>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
 }
 
 template <int KIND, class IO>
