@@ -91,23 +91,56 @@ __device__ __forceinline__ void unpack8(uint4 raw, float* x) {
 }
 
 // ------------------------------------------------------------------ LDS
-struct ChunkTiles {
-    u16 Qs[C][LDQ];      // q rows (output kernel only)
-    u16 Ks[C][LDQ];      // k rows; dead after K K^T, then reused for the rows of W
-    u16 KtR[D][LDA];     // k transposed: [d][c]
-    u16 Vt[D][LDA];      // v transposed: [value channel][c]
-    u16 Kt[D][LDA];      // K~^T = (diag(e^{g_c - g}) K)^T: [d][c]
-    u16 Ut[D][LDA];      // Ut^T: [value channel][c]
-    u16 Lb[C][LDA];      // -L (bf16)
-    u16 Tm[C][LDA];      // (I + L)^{-1}, lower triangular
-    u16 As[C][LDA];      // decay-masked Q K^T (output kernel only)
-    float Ld[4][16][17];  // diagonal blocks of L, fp32
-    float gs[C], bs[C], egs[C], sws[C], eks[C];  // g, beta, e^g, beta e^g, e^{g_c - g}
+// Gate vectors of one chunk.
+struct Gates {
+    float g[C], b[C], eg[C], sw[C], ek[C];  // g, beta, e^g, beta e^g, e^{g_c - g}
 };
 
+// Every 64 x 128 tile is row-major (row = token of the chunk).  Products
+// that contract over the token index read their operands with the
+// transposing LDS load, so no transposed copy is ever stored.  The gates come
+// in two copies selected by chunk parity: the scan of chunk n still reads
+// its copy while the next chunk's is written.
+struct ChunkTiles {
+    u16 Qs[C][LDQ];       // q (output kernel only)
+    u16 Ks[C][LDQ];       // k
+    u16 Kx[C][LDQ];       // K~ = diag(e^{g_c - g}) K (state update)
+    u16 Vs[C][LDQ];       // v
+    u16 Ws[C][LDQ];       // W
+    u16 Ut[D][LDA];       // Ut^T: [value channel][c]
+    u16 Lb[C][LDA];       // -L (bf16)
+    u16 Tm[C][LDA];       // (I + L)^{-1}, lower triangular
+    u16 As[C][LDA];       // decay-masked Q K^T (output kernel only)
+    float Ld[4][16][17];  // diagonal blocks of L, fp32
+    Gates gt[2];
+};
+
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v* lds_short4_ptr;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// i reads 4 consecutive 16-bit values E[i][0..3] at its own address, and lane
+// j = 4a + b receives E[a][b], E[a+4][b], E[a+8][b], E[a+12][b].
+__device__ __forceinline__ short4v ds_read_tr(const u16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(p));
+}
+
+// MFMA operand (8 values along the contraction index k) from a tile stored
+// k-major, X[k][n]: lane (r = 4a + b, g) receives X[k0 + 8g + j][col(a) + b],
+// j = 0..7, where col(a) (a multiple of 4) is the first of the four columns
+// that lanes 4a..4a+3 of every group take.
+template <class ColFn>
+__device__ __forceinline__ bf16x8 tr_operand(const u16 (*X)[LDQ], int k0, ColFn col, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int c = col(i & 3);
+    const short4v lo = ds_read_tr(&X[k0 + 8 * g + (i >> 2)][c]);
+    const short4v hi = ds_read_tr(&X[k0 + 8 * g + 4 + (i >> 2)][c]);
+    return __builtin_bit_cast(bf16x8, short8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+}
+
 // Raw chunk inputs held in registers between chunks.  Item e -> chunk row
-// e % 64, 8 columns starting at 8 (e / 64): rows run fastest across lanes,
-// which makes the transposed LDS stores of k and v conflict-free.
+// e / 16, 8 columns starting at 8 (e % 16): sixteen lanes cover one 256-byte
+// row, so the global loads are contiguous and the LDS stores conflict-free.
 // NTHR threads (tid 0 .. NTHR-1) share the work; NI 16-byte pieces each.
 template <int NTHR>
 struct RawChunk {
@@ -124,7 +157,7 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<NTHR>& rc, const u16* __res
 #pragma unroll
     for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
         const int e = tid + NTHR * it;
-        const int row = e & (C - 1), c8 = (e / C) * 8;
+        const int row = e >> 4, c8 = (e & 15) * 8;
         rc.q[it] = rc.k[it] = rc.v[it] = make_uint4(0, 0, 0, 0);
         if (row < len) {
             const size_t gi = (head_tok + t0 + row) * D + c8;
@@ -140,23 +173,24 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<NTHR>& rc, const u16* __res
     }
 }
 
-__device__ __forceinline__ u16 word_half(uint32_t wd, int hi) { return static_cast<u16>(hi ? (wd >> 16) : (wd & 0xffffu)); }
-
-template <bool WITH_Q, int NTHR>
-__device__ __forceinline__ void stage_chunk(ChunkTiles& sm, const RawChunk<NTHR>& rc, int tid) {
+template <int NTHR>
+__device__ __forceinline__ void stage_q(ChunkTiles& sm, const RawChunk<NTHR>& rc, int tid) {
 #pragma unroll
     for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
         const int e = tid + NTHR * it;
-        const int row = e & (C - 1), c8 = (e / C) * 8;
-        if (WITH_Q) *reinterpret_cast<uint4*>(&sm.Qs[row][c8]) = rc.q[it];
-        *reinterpret_cast<uint4*>(&sm.Ks[row][c8]) = rc.k[it];
-        const uint32_t wk[4] = {rc.k[it].x, rc.k[it].y, rc.k[it].z, rc.k[it].w};
-        const uint32_t wv[4] = {rc.v[it].x, rc.v[it].y, rc.v[it].z, rc.v[it].w};
+        *reinterpret_cast<uint4*>(&sm.Qs[e >> 4][(e & 15) * 8]) = rc.q[it];
+    }
+}
+
+// k, v and the gate vectors of copy `buf` (g by a wave-wide inclusive scan of
+// log alpha).
+template <int NTHR>
+__device__ __forceinline__ void stage_kv(ChunkTiles& sm, const RawChunk<NTHR>& rc, int tid, int buf) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            sm.KtR[c8 + j][row] = word_half(wk[j >> 1], j & 1);
-            sm.Vt[c8 + j][row] = word_half(wv[j >> 1], j & 1);
-        }
+    for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
+        const int e = tid + NTHR * it;
+        *reinterpret_cast<uint4*>(&sm.Ks[e >> 4][(e & 15) * 8]) = rc.k[it];
+        *reinterpret_cast<uint4*>(&sm.Vs[e >> 4][(e & 15) * 8]) = rc.v[it];
     }
     if (tid < C) {
         float x = __logf(rc.a);
@@ -167,11 +201,12 @@ __device__ __forceinline__ void stage_chunk(ChunkTiles& sm, const RawChunk<NTHR>
         }
         const float gl = __shfl(x, C - 1, 64);
         const float eg = __expf(x);
-        sm.gs[tid] = x;
-        sm.bs[tid] = rc.b;
-        sm.egs[tid] = eg;
-        sm.sws[tid] = rc.b * eg;
-        sm.eks[tid] = __expf(gl - x);
+        Gates& gt = sm.gt[buf];
+        gt.g[tid] = x;
+        gt.b[tid] = rc.b;
+        gt.eg[tid] = eg;
+        gt.sw[tid] = rc.b * eg;
+        gt.ek[tid] = __expf(gl - x);
     }
 }
 
@@ -183,11 +218,20 @@ __device__ __forceinline__ short4v tdiag_b(const ChunkTiles& sm, int blk, int r,
     return x;
 }
 
-// The state-independent tiles of the staged chunk (rows of W, Ut^T, K~^T
-// and, with WITH_Q, A), all in LDS.  Called by all eight waves; starts and
-// ends on a barrier.
+// 16x16 tile (rt, ct) of X Y^T for two row-major 64 x 128 LDS operands.
+__device__ __forceinline__ f32x4 rows_dot(const u16 (*X)[LDQ], const u16 (*Y)[LDQ], int rt, int ct, int r, int g) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = mfma16x16x32(lds_bf16x8(&X[16 * rt + r][32 * s + 8 * g]), lds_bf16x8(&Y[16 * ct + r][32 * s + 8 * g]), acc);
+    return acc;
+}
+
+// The state-independent tiles of the staged chunk (W, Ut^T, K~ and, with
+// WITH_Q, A), all in LDS.  Called by all eight waves; starts and ends on a
+// barrier.  buf selects the chunk's copy of the gates.
 template <bool WITH_Q>
-__device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid) {
+__device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid, int buf) {
     // The wave index must be a scalar: the matrix-core instructions below sit
     // in branches on it, and a branch the compiler takes as divergent runs
     // both sides under EXEC masks, where an MFMA would still write its
@@ -196,40 +240,22 @@ __device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid) {
     const int lane = tid & 63;
     const int r = lane & 15;
     const int g = lane >> 4;
-    u16(*Ws)[LDQ] = sm.Ks;
+    const Gates& gt = sm.gt[buf];
     __syncthreads();
 
-    // waves 0-3: K K^T for row tile w -> L (-L in bf16, diagonal blocks in fp32)
-    // waves 4-7: Q K^T for row tile w-4 -> A (decay-masked, causal)
-    if (w < 4 || WITH_Q) {
-        const int rt = w & 3;
-        const bool kk = w < 4;
-        for (int ct = 0; ct < 4; ++ct) {
-            if (ct <= rt) {
-                f32x4 acc = zero4();
+    // K K^T -> L: the ten lower 16x16 tiles over the eight waves (-L in bf16,
+    // the diagonal blocks also in fp32)
+    for (int t = w; t < 10; t += 8) {
+        const int rt = (t >= 1) + (t >= 3) + (t >= 6);
+        const int ct = t - rt * (rt + 1) / 2;
+        const f32x4 acc = rows_dot(sm.Ks, sm.Ks, rt, ct, r, g);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x8 bk = lds_bf16x8(&sm.Ks[16 * ct + r][32 * s + 8 * g]);
-                    const bf16x8 a = kk ? lds_bf16x8(&sm.Ks[16 * rt + r][32 * s + 8 * g])
-                                        : lds_bf16x8(&sm.Qs[16 * rt + r][32 * s + 8 * g]);
-                    acc = mfma16x16x32(a, bk, acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
-                    const float dec = __expf(fminf(sm.gs[row] - sm.gs[col], 0.f));
-                    if (kk) {
-                        const float lval = col < row ? sm.bs[row] * dec * acc[i] : 0.f;
-                        sm.Lb[row][col] = f32_to_bf16_bits(-lval);
-                        if (ct == rt) sm.Ld[rt][4 * g + i][r] = lval;
-                    } else {
-                        sm.As[row][col] = f32_to_bf16_bits(col <= row ? dec * acc[i] : 0.f);
-                    }
-                }
-            } else if (!kk) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.As[16 * rt + 4 * g + i][16 * ct + r] = 0;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
+            const float dec = __expf(fminf(gt.g[row] - gt.g[col], 0.f));
+            const float lval = col < row ? gt.b[row] * dec * acc[i] : 0.f;
+            sm.Lb[row][col] = f32_to_bf16_bits(-lval);
+            if (ct == rt) sm.Ld[rt][4 * g + i][r] = lval;
         }
     }
     __syncthreads();
@@ -280,20 +306,39 @@ __device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid) {
         put(3, 1, t31);
         put(3, 0, t30);
     } else {
-        // waves 1-7: K~^T = e^{g_c - g} K^T, 16 bytes at a time
-        for (int e = tid - 64; e < D * (C / 8); e += kThreads - 64) {
-            const int d = e >> 3, c0 = (e & 7) * 8;
+        // waves 1-7 meanwhile: K~ = diag(e^{g_c - g}) K ...
+        for (int e = tid - 64; e < C * (D / 8); e += kThreads - 64) {
+            const int row = e >> 4, c0 = (e & 15) * 8;
             float x[8];
-            unpack8(*reinterpret_cast<const uint4*>(&sm.KtR[d][c0]), x);
-            *reinterpret_cast<bf16x8*>(&sm.Kt[d][c0]) =
-                pack8(x[0] * sm.eks[c0], x[1] * sm.eks[c0 + 1], x[2] * sm.eks[c0 + 2], x[3] * sm.eks[c0 + 3],
-                      x[4] * sm.eks[c0 + 4], x[5] * sm.eks[c0 + 5], x[6] * sm.eks[c0 + 6], x[7] * sm.eks[c0 + 7]);
+            unpack8(*reinterpret_cast<const uint4*>(&sm.Ks[row][c0]), x);
+            const float f = gt.ek[row];
+            *reinterpret_cast<bf16x8*>(&sm.Kx[row][c0]) =
+                pack8(x[0] * f, x[1] * f, x[2] * f, x[3] * f, x[4] * f, x[5] * f, x[6] * f, x[7] * f);
+        }
+        // ... and A = (Q K^T) * Gamma, causal (diagonal included)
+        if (WITH_Q) {
+            for (int t = w - 1; t < 16; t += 7) {
+                const int rt = t >> 2, ct = t & 3;
+                if (ct <= rt) {
+                    const f32x4 acc = rows_dot(sm.Qs, sm.Ks, rt, ct, r, g);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
+                        const float dec = __expf(fminf(gt.g[row] - gt.g[col], 0.f));
+                        sm.As[row][col] = f32_to_bf16_bits(col <= row ? dec * acc[i] : 0.f);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sm.As[16 * rt + 4 * g + i][16 * ct + r] = 0;
+                }
+            }
         }
     }
     __syncthreads();
 
     // W = (I + L)^{-1} diag(beta e^g) K and Ut = (I + L)^{-1} diag(beta) V as
-    // plain products; the row scalings fold into the (I + L)^{-1} operand.
+    // plain products; the row scalings fold into the (I + L)^{-1} operand and
+    // K, V are read transposed.
     // waves 0-3: W^T = K^T (Tm diag(beta e^g))^T for d rows 32w..32w+31, so each
     //            lane ends up holding 4 consecutive d of one W row (8-byte stores);
     // waves 4-7: Ut = (Tm diag(beta)) V for value channels 32(w-4)..+31.
@@ -306,25 +351,28 @@ __device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) acc[a2][ct] = zero4();
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 xf[2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int a2 = 0; a2 < 2; ++a2) {
+                const int n0 = 32 * w4 + 16 * a2;  // d (W) or value channel (Ut)
+                xf[a2] = tr_operand(isW ? sm.Ks : sm.Vs, 32 * s, [&](int aa) { return n0 + 4 * aa; }, lane);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
                 if (s == 1 && ct < 2) continue;  // (I + L)^{-1} is lower triangular
                 float t[8];
                 unpack8(*reinterpret_cast<const uint4*>(&sm.Tm[16 * ct + r][32 * s + 8 * g]), t);
-                const float* sc = isW ? sm.sws : sm.bs;
+                const float* sc = isW ? gt.sw : gt.b;
                 const bf16x8 tf = pack8(t[0] * sc[32 * s + 8 * g], t[1] * sc[32 * s + 8 * g + 1],
                                         t[2] * sc[32 * s + 8 * g + 2], t[3] * sc[32 * s + 8 * g + 3],
                                         t[4] * sc[32 * s + 8 * g + 4], t[5] * sc[32 * s + 8 * g + 5],
                                         t[6] * sc[32 * s + 8 * g + 6], t[7] * sc[32 * s + 8 * g + 7]);
 #pragma unroll
                 for (int a2 = 0; a2 < 2; ++a2) {
-                    const int rowx = 32 * w4 + 16 * a2 + r;  // d (W) or value channel (Ut)
-                    const bf16x8 xf = isW ? lds_bf16x8(&sm.KtR[rowx][32 * s + 8 * g])
-                                          : lds_bf16x8(&sm.Vt[rowx][32 * s + 8 * g]);
-                    // W^T tile (d x c):  A = K^T rows, B = scaled Tm rows
-                    // Ut tile (c x v):   A = scaled Tm rows, B = V^T rows
-                    acc[a2][ct] = isW ? mfma16x16x32(xf, tf, acc[a2][ct]) : mfma16x16x32(tf, xf, acc[a2][ct]);
+                    // W^T tile (d x c):  A = K^T, B = scaled Tm rows
+                    // Ut tile (c x v):   A = scaled Tm rows, B = V
+                    acc[a2][ct] = isW ? mfma16x16x32(xf[a2], tf, acc[a2][ct]) : mfma16x16x32(tf, xf[a2], acc[a2][ct]);
                 }
             }
         }
@@ -334,7 +382,7 @@ __device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid) {
             for (int ct = 0; ct < 4; ++ct) {
                 const short4v h = to_bf16x4(acc[a2][ct]);
                 if (isW)  // lane holds W^T[d = 32w+16a2+4g+i][c = 16ct+r]
-                    *reinterpret_cast<short4v*>(&Ws[16 * ct + r][32 * w4 + 16 * a2 + 4 * g]) = h;
+                    *reinterpret_cast<short4v*>(&sm.Ws[16 * ct + r][32 * w4 + 16 * a2 + 4 * g]) = h;
                 else      // lane holds Ut[c = 16ct+4g+i][v = 32(w-4)+16a2+r]
                     *reinterpret_cast<short4v*>(&sm.Ut[32 * w4 + 16 * a2 + r][16 * ct + 4 * g]) = h;
             }
@@ -348,10 +396,10 @@ __device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid) {
 // forms the outputs O = e^g (Q P) + A U and stores the rows that exist.
 template <int NT, bool WITH_O>
 __device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][8], int col0, bool use_ut,
-                                           int lane, u16* __restrict__ o, size_t o_row0, int len) {
+                                           int lane, u16* __restrict__ o, size_t o_row0, int len, int buf) {
     const int r = lane & 15;
     const int g = lane >> 4;
-    const u16(*Ws)[LDQ] = sm.Ks;
+    const Gates& gt = sm.gt[buf];
     // X = W P, U = Ut - X (or -X), one half of the chunk rows at a time.  W rows
     // are taken in the permuted order so X lands in U's layout; the bf16 copy
     // of the state (the B operand) is packed on the fly to save registers.
@@ -363,8 +411,8 @@ __device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][
         for (int nt = 0; nt < NT; ++nt) Xa[nt] = Xb[nt] = zero4();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const bf16x8 a0 = lds_bf16x8(&Ws[perm_row(2 * s2, r)][32 * s + 8 * g]);
-            const bf16x8 a1 = lds_bf16x8(&Ws[perm_row(2 * s2 + 1, r)][32 * s + 8 * g]);
+            const bf16x8 a0 = lds_bf16x8(&sm.Ws[perm_row(2 * s2, r)][32 * s + 8 * g]);
+            const bf16x8 a1 = lds_bf16x8(&sm.Ws[perm_row(2 * s2 + 1, r)][32 * s + 8 * g]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const bf16x8 pb = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
@@ -412,7 +460,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float elo = sm.egs[32 * s2 + 8 * g + i], ehi = sm.egs[32 * s2 + 8 * g + 4 + i];
+                const float elo = gt.eg[32 * s2 + 8 * g + i], ehi = gt.eg[32 * s2 + 8 * g + 4 + i];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     O[nt][2 * s2][i] *= elo;
@@ -440,15 +488,15 @@ __device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][
                 }
             }
     }
-    // P <- e^{g_c} P + K~^T U
-    const float egc = sm.egs[C - 1];
+    // P <- e^{g_c} P + K~^T U, K~^T read transposed in the permuted row order
+    const float egc = gt.eg[C - 1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) P[nt][t] *= egc;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 a = lds_bf16x8(&sm.Kt[perm_row(t, r)][32 * s2 + 8 * g]);
+            const bf16x8 a = tr_operand(sm.Kx, 32 * s2, [&](int aa) { return 32 * (t >> 1) + 8 * aa + 4 * (t & 1); }, lane);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) P[nt][t] = mfma16x16x32(a, Ub[nt][s2], P[nt][t]);
         }
@@ -546,11 +594,11 @@ __global__ __launch_bounds__(kThreads) void gdn_map_kernel(int BH, int T, int NC
     fetch_chunk<false>(rc, nullptr, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), tid);
     for (int n = n0; n < n1; ++n) {
         __syncthreads();
-        stage_chunk<false>(sm, rc, tid);
+        stage_kv(sm, rc, tid, n & 1);
         if (n + 1 < n1)
             fetch_chunk<false>(rc, nullptr, k, v, alpha, beta, head_tok, (n + 1) * C, min(C, T - (n + 1) * C), tid);
-        chunk_tiles<false>(sm, tid);
-        scan_chunk<2, false>(sm, P, col0, npart, lane, nullptr, 0, 0);
+        chunk_tiles<false>(sm, tid, n & 1);
+        scan_chunk<2, false>(sm, P, col0, npart, lane, nullptr, 0, 0, n & 1);
     }
     if (npart)
         store_state<2>(P, ws + ws_N(bh, G, seg), col0, lane);
@@ -665,20 +713,24 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
         for (int n = n0; n < n1; ++n) {
             const int t0 = n * C;
             __syncthreads();
-            chunk_tiles<true>(sm, tid);
-            scan_chunk<2, true>(sm, P, col0, true, lane, o, head_tok + t0, min(C, T - t0));
+            chunk_tiles<true>(sm, tid, n & 1);
+            scan_chunk<2, true>(sm, P, col0, true, lane, o, head_tok + t0, min(C, T - t0), n & 1);
         }
         if (seg == G - 1 && S_out) store_state<2>(P, S_out + static_cast<size_t>(bh) * kMat, col0, lane);
     } else {
         const int ptid = tid - kThreads / 2;
+        // k, v and the gates of chunk n+1 are written while the state
+        // carriers run the scan of chunk n (which reads neither).
         RawChunk<kThreads / 2> rc;
         fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), ptid);
+        stage_kv(sm, rc, ptid, n0 & 1);
         for (int n = n0; n < n1; ++n) {
             const int t0 = n * C;
             __syncthreads();
-            stage_chunk<true>(sm, rc, ptid);
+            stage_q(sm, rc, ptid);
             if (n + 1 < n1) fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, t0 + C, min(C, T - t0 - C), ptid);
-            chunk_tiles<true>(sm, tid);
+            chunk_tiles<true>(sm, tid, n & 1);
+            if (n + 1 < n1) stage_kv(sm, rc, ptid, (n + 1) & 1);
         }
     }
 }
