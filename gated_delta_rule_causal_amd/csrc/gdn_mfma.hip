@@ -39,6 +39,8 @@
 // back as the B operand of the next product by permuting the contraction
 // index (pack_acc_pair), so no state crosses lanes.  The next chunk's raw
 // q/k/v are loaded into registers while the current chunk computes.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -111,7 +113,6 @@ struct ChunkTiles {
     u16 Lb[C][LDA];       // -L (bf16)
     u16 Tm[C][LDA];       // (I + L)^{-1}, lower triangular
     u16 As[C][LDA];       // decay-masked Q K^T (output kernel only)
-    float Ld[4][16][17];  // diagonal blocks of L, fp32
     Gates gt[2];
 };
 
@@ -138,75 +139,121 @@ __device__ __forceinline__ bf16x8 tr_operand(const u16 (*X)[LDQ], int k0, ColFn 
     return __builtin_bit_cast(bf16x8, short8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
 }
 
-// Raw chunk inputs held in registers between chunks.  Item e -> chunk row
-// e / 16, 8 columns starting at 8 (e % 16): sixteen lanes cover one 256-byte
-// row, so the global loads are contiguous and the LDS stores conflict-free.
-// NTHR threads (tid 0 .. NTHR-1) share the work; NI 16-byte pieces each.
-template <int NTHR>
+// Raw chunk inputs held in registers between chunks.  Each 16-byte piece is
+// one of the sixteen in a 256-byte row, so the global loads are contiguous
+// and the LDS stores conflict-free.  NTHR threads (tid 0 .. NTHR-1) share the
+// work, NI pieces each.  Piece it of thread tid:
+//   WAVE_ROWS = false: rows interleaved over all threads, row = (tid + NTHR it) / 16;
+//   WAVE_ROWS = true:  wave u holds rows 16u .. 16u+15 (NTHR = 256, four waves),
+//                      so a wave can use its own rows right after writing them.
+// Every wave also holds the gates of all 64 tokens, one per lane.
+template <int NTHR, bool WAVE_ROWS = false>
 struct RawChunk {
     static constexpr int NI = C * D / 8 / NTHR;
+    static_assert(!WAVE_ROWS || NTHR == 256, "wave-owned rows need four waves");
     uint4 q[NI], k[NI], v[NI];
     float a, b;
+    static __device__ __forceinline__ int row(int tid, int it) {
+        return WAVE_ROWS ? 16 * (tid >> 6) + 4 * it + ((tid & 63) >> 4) : (tid + NTHR * it) >> 4;
+    }
+    static __device__ __forceinline__ int col(int tid) { return (tid & 15) * 8; }
 };
 
-template <bool WITH_Q, int NTHR>
-__device__ __forceinline__ void fetch_chunk(RawChunk<NTHR>& rc, const u16* __restrict__ q, const u16* __restrict__ k,
+// WITH_Q / WITH_KV select the tensors loaded (the gates come with k and v).
+template <bool WITH_Q, bool WITH_KV, int NTHR, bool WR>
+__device__ __forceinline__ void fetch_chunk(RawChunk<NTHR, WR>& rc, const u16* __restrict__ q, const u16* __restrict__ k,
                                             const u16* __restrict__ v, const float* __restrict__ alpha,
                                             const float* __restrict__ beta, size_t head_tok, int t0, int len,
                                             int tid) {
+    using RC = RawChunk<NTHR, WR>;
 #pragma unroll
-    for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
-        const int e = tid + NTHR * it;
-        const int row = e >> 4, c8 = (e & 15) * 8;
-        rc.q[it] = rc.k[it] = rc.v[it] = make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < RC::NI; ++it) {
+        const int row = RC::row(tid, it), c8 = RC::col(tid);
+        if (WITH_Q) rc.q[it] = make_uint4(0, 0, 0, 0);
+        if (WITH_KV) rc.k[it] = rc.v[it] = make_uint4(0, 0, 0, 0);
         if (row < len) {
             const size_t gi = (head_tok + t0 + row) * D + c8;
             if (WITH_Q) rc.q[it] = *reinterpret_cast<const uint4*>(q + gi);
-            rc.k[it] = *reinterpret_cast<const uint4*>(k + gi);
-            rc.v[it] = *reinterpret_cast<const uint4*>(v + gi);
+            if (WITH_KV) {
+                rc.k[it] = *reinterpret_cast<const uint4*>(k + gi);
+                rc.v[it] = *reinterpret_cast<const uint4*>(v + gi);
+            }
         }
     }
-    if (tid < C) {
+    if (WITH_KV) {
         // padded tokens: alpha = 1 (log 0), beta = 0, zero rows: they change nothing
-        rc.a = tid < len ? alpha[head_tok + t0 + tid] : 1.f;
-        rc.b = tid < len ? beta[head_tok + t0 + tid] : 0.f;
+        const int t = tid & 63;
+        rc.a = t < len ? alpha[head_tok + t0 + t] : 1.f;
+        rc.b = t < len ? beta[head_tok + t0 + t] : 0.f;
     }
 }
 
-template <int NTHR>
-__device__ __forceinline__ void stage_q(ChunkTiles& sm, const RawChunk<NTHR>& rc, int tid) {
+template <int NTHR, bool WR>
+__device__ __forceinline__ void stage_q(ChunkTiles& sm, const RawChunk<NTHR, WR>& rc, int tid) {
+    using RC = RawChunk<NTHR, WR>;
 #pragma unroll
-    for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
-        const int e = tid + NTHR * it;
-        *reinterpret_cast<uint4*>(&sm.Qs[e >> 4][(e & 15) * 8]) = rc.q[it];
-    }
+    for (int it = 0; it < RC::NI; ++it) *reinterpret_cast<uint4*>(&sm.Qs[RC::row(tid, it)][RC::col(tid)]) = rc.q[it];
 }
 
-// k, v and the gate vectors of copy `buf` (g by a wave-wide inclusive scan of
-// log alpha).
-template <int NTHR>
-__device__ __forceinline__ void stage_kv(ChunkTiles& sm, const RawChunk<NTHR>& rc, int tid, int buf) {
+// Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
+// for this wave's global loads to land (its fence covers global memory); no
+// kernel here communicates through global memory inside a launch, so loads
+// issued ahead of time stay in flight across these barriers.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data (a wave executes LDS operations in order; this keeps the compiler from
+// moving them across).
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
+// Gates of the chunk, one token per lane: g = inclusive scan of log alpha
+// over the wave.
+struct GateRegs {
+    float g, b, eg, ek;
+};
+
+// x + (x of the lane selected by the DPP control, 0 where there is none or
+// the row is masked off).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xf, true));
+}
+
+__device__ __forceinline__ GateRegs chunk_gates(float a, float b) {
+    // inclusive scan without LDS: shifts by 1, 2, 4, 8 inside each 16-lane
+    // row, then lane 15 added into rows 1 and 3 and lane 31 into rows 2 and 3
+    float x = __logf(a);
+    x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);   // row_bcast:15
+    x = dpp_add<0x143, 0xc>(x);   // row_bcast:31
+    const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
+    return GateRegs{x, b, __expf(x), __expf(gl - x)};
+}
+
+// k, v and the gate vectors of copy `buf` (the first wave writes the gates).
+template <int NTHR, bool WR>
+__device__ __forceinline__ void stage_kv(ChunkTiles& sm, const RawChunk<NTHR, WR>& rc, const GateRegs& gr, int tid,
+                                         int buf) {
+    using RC = RawChunk<NTHR, WR>;
 #pragma unroll
-    for (int it = 0; it < RawChunk<NTHR>::NI; ++it) {
-        const int e = tid + NTHR * it;
-        *reinterpret_cast<uint4*>(&sm.Ks[e >> 4][(e & 15) * 8]) = rc.k[it];
-        *reinterpret_cast<uint4*>(&sm.Vs[e >> 4][(e & 15) * 8]) = rc.v[it];
+    for (int it = 0; it < RC::NI; ++it) {
+        *reinterpret_cast<uint4*>(&sm.Ks[RC::row(tid, it)][RC::col(tid)]) = rc.k[it];
+        *reinterpret_cast<uint4*>(&sm.Vs[RC::row(tid, it)][RC::col(tid)]) = rc.v[it];
     }
     if (tid < C) {
-        float x = __logf(rc.a);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (tid >= off) x += y;
-        }
-        const float gl = __shfl(x, C - 1, 64);
-        const float eg = __expf(x);
         Gates& gt = sm.gt[buf];
-        gt.g[tid] = x;
-        gt.b[tid] = rc.b;
-        gt.eg[tid] = eg;
-        gt.sw[tid] = rc.b * eg;
-        gt.ek[tid] = __expf(gl - x);
+        gt.g[tid] = gr.g;
+        gt.b[tid] = gr.b;
+        gt.eg[tid] = gr.eg;
+        gt.sw[tid] = gr.b * gr.eg;
+        gt.ek[tid] = gr.ek;
     }
 }
 
@@ -218,6 +265,54 @@ __device__ __forceinline__ short4v tdiag_b(const ChunkTiles& sm, int blk, int r,
     return x;
 }
 
+// fp32 value as a bf16 pair (high part, rounded remainder).
+struct Split4 {
+    short4v h, l;
+};
+
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+    Split4 s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const u16 hb = f32_to_bf16_bits(x[e]);
+        s.h[e] = static_cast<short>(hb);
+        s.l[e] = static_cast<short>(f32_to_bf16_bits(x[e] - bf16_bits_to_f32(hb)));
+    }
+    return s;
+}
+
+// c + a b for 16x16 fp32 matrices given as bf16 pairs (hi*hi + hi*lo + lo*hi:
+// about 16 significant bits).  a in operand layout, b in accumulator layout.
+__device__ __forceinline__ f32x4 mm3(const Split4& a, const Split4& b, f32x4 c) {
+    c = mfma16x16x16(a.l, b.h, c);
+    c = mfma16x16x16(a.h, b.l, c);
+    return mfma16x16x16(a.h, b.h, c);
+}
+
+// (I - N)^{-1} for a strictly lower triangular 16x16 N = -L given in the
+// accumulator layout together with its transpose Nt (the operand layout of N
+// is the accumulator layout of N^T).  N is nilpotent (N^16 = 0), so
+//     (I - N)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8),
+// built by three squarings, each folded into the running product; the
+// factors are powers of one matrix and commute.  The first (largest)
+// correction is formed from split bf16 pairs, the higher powers in bf16.
+__device__ __forceinline__ f32x4 unit_lower_inverse(f32x4 N, f32x4 Nt, int r, int g) {
+    f32x4 R = N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * g + i == r) R[i] += 1.f;
+    const Split4 P = split4(N), Pt = split4(Nt);
+    const f32x4 P2 = mm3(Pt, P, zero4());    // N N
+    const f32x4 P2t = mm3(P, Pt, zero4());   // (N N)^T = N^T N^T
+    R = mm3(split4(P2t), split4(R), R);      // R (I + N^2)
+    const short4v q2 = to_bf16x4(P2), q2t = to_bf16x4(P2t);
+    const f32x4 P4 = mfma16x16x16(q2t, q2, zero4());
+    const f32x4 P4t = mfma16x16x16(q2, q2t, zero4());
+    R = mfma16x16x16(to_bf16x4(P4t), to_bf16x4(R), R);   // R (I + N^4)
+    const f32x4 P8t = mfma16x16x16(to_bf16x4(P4), to_bf16x4(P4t), zero4());
+    return mfma16x16x16(to_bf16x4(P8t), to_bf16x4(R), R);   // R (I + N^8)
+}
+
 // 16x16 tile (rt, ct) of X Y^T for two row-major 64 x 128 LDS operands.
 __device__ __forceinline__ f32x4 rows_dot(const u16 (*X)[LDQ], const u16 (*Y)[LDQ], int rt, int ct, int r, int g) {
     f32x4 acc = zero4();
@@ -227,183 +322,198 @@ __device__ __forceinline__ f32x4 rows_dot(const u16 (*X)[LDQ], const u16 (*Y)[LD
     return acc;
 }
 
-// The state-independent tiles of the staged chunk (W, Ut^T, K~ and, with
-// WITH_Q, A), all in LDS.  Called by all eight waves; starts and ends on a
-// barrier.  buf selects the chunk's copy of the gates.
-template <bool WITH_Q>
-__device__ __forceinline__ void chunk_tiles(ChunkTiles& sm, int tid, int buf) {
-    // The wave index must be a scalar: the matrix-core instructions below sit
-    // in branches on it, and a branch the compiler takes as divergent runs
-    // both sides under EXEC masks, where an MFMA would still write its
-    // destination registers.
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const Gates& gt = sm.gt[buf];
-    __syncthreads();
+// Two such tiles formed together (interleaved products for latency hiding).
+__device__ __forceinline__ void rows_dot2(const u16 (*X)[LDQ], const u16 (*Y)[LDQ], int rta, int cta, int rtb, int ctb,
+                                          int r, int g, f32x4& acc_a, f32x4& acc_b) {
+    acc_a = acc_b = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        acc_a = mfma16x16x32(lds_bf16x8(&X[16 * rta + r][32 * s + 8 * g]), lds_bf16x8(&Y[16 * cta + r][32 * s + 8 * g]), acc_a);
+        acc_b = mfma16x16x32(lds_bf16x8(&X[16 * rtb + r][32 * s + 8 * g]), lds_bf16x8(&Y[16 * ctb + r][32 * s + 8 * g]), acc_b);
+    }
+}
 
-    // K K^T -> L: the ten lower 16x16 tiles over the eight waves (-L in bf16,
-    // the diagonal blocks also in fp32)
-    for (int t = w; t < 10; t += 8) {
-        const int rt = (t >= 1) + (t >= 3) + (t >= 6);
-        const int ct = t - rt * (rt + 1) / 2;
-        const f32x4 acc = rows_dot(sm.Ks, sm.Ks, rt, ct, r, g);
+// 16x16 block coordinates.  Blocks below the diagonal, 0..5:
+// (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); blocks on or below it, 0..9, in row order.
+__device__ __forceinline__ int below_row(int t) { return 1 + (t >= 1) + (t >= 3); }
+__device__ __forceinline__ int below_col(int t) { const int rt = below_row(t); return t - rt * (rt - 1) / 2; }
+__device__ __forceinline__ int lower_row(int t) { return (t >= 1) + (t >= 3) + (t >= 6); }
+__device__ __forceinline__ int lower_col(int t) { const int rt = lower_row(t); return t - rt * (rt + 1) / 2; }
+
+// ---- step 1: L = beta Gamma (K K^T) below the diagonal, and the inverses of
+// the diagonal 16x16 blocks of I + L.
+//
+// Diagonal block b: K K^T is symmetric there, so one accumulator tile yields
+// both L_bb and its transpose; the inverse is formed in registers and stored
+// in bf16 into Tm.
+// Gates come from the wave's registers (one token per lane).
+__device__ __forceinline__ void step1_diag(ChunkTiles& sm, const GateRegs& grg, int b, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const f32x4 acc = rows_dot(sm.Ks, sm.Ks, b, b, r, g);
+    const int kap = 16 * b + r;
+    const float gk = __shfl(grg.g, kap, 64), bk = __shfl(grg.b, kap, 64);
+    f32x4 N, Nt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rho = 16 * b + 4 * g + i;
+        const float gr = __shfl(grg.g, rho, 64), br = __shfl(grg.b, rho, 64);
+        N[i] = r < 4 * g + i ? -br * __expf(fminf(gr - gk, 0.f)) * acc[i] : 0.f;
+        Nt[i] = 4 * g + i < r ? -bk * __expf(fminf(gk - gr, 0.f)) * acc[i] : 0.f;
+    }
+    const f32x4 Tb = unit_lower_inverse(N, Nt, r, g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.Tm[16 * b + 4 * g + i][16 * b + r] = f32_to_bf16_bits(Tb[i]);
+}
+
+// Below-diagonal blocks ta and tb (numbering above): -L in bf16 into Lb.  With
+// two = false, tb is formed and dropped, which keeps the code free of
+// branches around the matrix-core instructions.
+__device__ __forceinline__ void step1_below(ChunkTiles& sm, const Gates& gt, int ta, int tb, bool two, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    f32x4 acc[2];
+    rows_dot2(sm.Ks, sm.Ks, below_row(ta), below_col(ta), below_row(tb), below_col(tb), r, g, acc[0], acc[1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (j == 1 && !two) break;
+        const int t = j ? tb : ta;
+        const int rt = below_row(t), ct = below_col(t);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
-            const float dec = __expf(fminf(gt.g[row] - gt.g[col], 0.f));
-            const float lval = col < row ? gt.b[row] * dec * acc[i] : 0.f;
-            sm.Lb[row][col] = f32_to_bf16_bits(-lval);
-            if (ct == rt) sm.Ld[rt][4 * g + i][r] = lval;
+            sm.Lb[row][col] = f32_to_bf16_bits(-gt.b[row] * __expf(fminf(gt.g[row] - gt.g[col], 0.f)) * acc[j][i]);
         }
     }
-    __syncthreads();
-
-    if (w == 0) {
-        // (I + L)^{-1}: diagonal 16x16 blocks by forward substitution, one
-        // column per lane, fp32 ...
-        {
-            const int b = lane >> 4, c = lane & 15;
-            float x[16];
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float val = rr == c ? 1.f : 0.f;
-#pragma unroll
-                for (int j = 0; j < rr; ++j) val = fmaf(-sm.Ld[b][rr][j], x[j], val);
-                x[rr] = val;
-                sm.Tm[16 * b + rr][16 * b + c] = f32_to_bf16_bits(val);
-            }
-            // blocks above the diagonal that the 32-wide operand slices touch
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm.Tm[4 * g + i][16 + r] = 0;
-                sm.Tm[32 + 4 * g + i][48 + r] = 0;
-            }
-        }
-        // ... then the blocks below it by diagonal distance:
-        //     T_ij = T_ii * sum_{j<=k<i} (-L_ik) T_kj
-        const short4v t00 = tdiag_b(sm, 0, r, g), t11 = tdiag_b(sm, 1, r, g), t22 = tdiag_b(sm, 2, r, g);
-        auto nl = [&](int i, int j) { return lds_short4(&sm.Lb[16 * i + r][16 * j + 4 * g]); };
-        auto ta = [&](int i) { return lds_short4(&sm.Tm[16 * i + r][16 * i + 4 * g]); };
-        const short4v t10 = to_bf16x4(mfma16x16x16(ta(1), to_bf16x4(mfma16x16x16(nl(1, 0), t00, zero4())), zero4()));
-        const short4v t21 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(mfma16x16x16(nl(2, 1), t11, zero4())), zero4()));
-        const short4v t32 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(mfma16x16x16(nl(3, 2), t22, zero4())), zero4()));
-        f32x4 y = mfma16x16x16(nl(2, 1), t10, mfma16x16x16(nl(2, 0), t00, zero4()));
-        const short4v t20 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(y), zero4()));
-        y = mfma16x16x16(nl(3, 2), t21, mfma16x16x16(nl(3, 1), t11, zero4()));
-        const short4v t31 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
-        y = mfma16x16x16(nl(3, 2), t20, mfma16x16x16(nl(3, 1), t10, mfma16x16x16(nl(3, 0), t00, zero4())));
-        const short4v t30 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
-        auto put = [&](int i, int j, short4v t) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Tm[16 * i + 4 * g + e][16 * j + r] = static_cast<u16>(t[e]);
-        };
-        put(1, 0, t10);
-        put(2, 1, t21);
-        put(3, 2, t32);
-        put(2, 0, t20);
-        put(3, 1, t31);
-        put(3, 0, t30);
-    } else {
-        // waves 1-7 meanwhile: K~ = diag(e^{g_c - g}) K ...
-        for (int e = tid - 64; e < C * (D / 8); e += kThreads - 64) {
-            const int row = e >> 4, c0 = (e & 15) * 8;
-            float x[8];
-            unpack8(*reinterpret_cast<const uint4*>(&sm.Ks[row][c0]), x);
-            const float f = gt.ek[row];
-            *reinterpret_cast<bf16x8*>(&sm.Kx[row][c0]) =
-                pack8(x[0] * f, x[1] * f, x[2] * f, x[3] * f, x[4] * f, x[5] * f, x[6] * f, x[7] * f);
-        }
-        // ... and A = (Q K^T) * Gamma, causal (diagonal included)
-        if (WITH_Q) {
-            for (int t = w - 1; t < 16; t += 7) {
-                const int rt = t >> 2, ct = t & 3;
-                if (ct <= rt) {
-                    const f32x4 acc = rows_dot(sm.Qs, sm.Ks, rt, ct, r, g);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
-                        const float dec = __expf(fminf(gt.g[row] - gt.g[col], 0.f));
-                        sm.As[row][col] = f32_to_bf16_bits(col <= row ? dec * acc[i] : 0.f);
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.As[16 * rt + 4 * g + i][16 * ct + r] = 0;
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // W = (I + L)^{-1} diag(beta e^g) K and Ut = (I + L)^{-1} diag(beta) V as
-    // plain products; the row scalings fold into the (I + L)^{-1} operand and
-    // K, V are read transposed.
-    // waves 0-3: W^T = K^T (Tm diag(beta e^g))^T for d rows 32w..32w+31, so each
-    //            lane ends up holding 4 consecutive d of one W row (8-byte stores);
-    // waves 4-7: Ut = (Tm diag(beta)) V for value channels 32(w-4)..+31.
-    {
-        const bool isW = w < 4;
-        const int w4 = w & 3;
-        f32x4 acc[2][4];
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) acc[a2][ct] = zero4();
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            bf16x8 xf[2];
-#pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2) {
-                const int n0 = 32 * w4 + 16 * a2;  // d (W) or value channel (Ut)
-                xf[a2] = tr_operand(isW ? sm.Ks : sm.Vs, 32 * s, [&](int aa) { return n0 + 4 * aa; }, lane);
-            }
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                if (s == 1 && ct < 2) continue;  // (I + L)^{-1} is lower triangular
-                float t[8];
-                unpack8(*reinterpret_cast<const uint4*>(&sm.Tm[16 * ct + r][32 * s + 8 * g]), t);
-                const float* sc = isW ? gt.sw : gt.b;
-                const bf16x8 tf = pack8(t[0] * sc[32 * s + 8 * g], t[1] * sc[32 * s + 8 * g + 1],
-                                        t[2] * sc[32 * s + 8 * g + 2], t[3] * sc[32 * s + 8 * g + 3],
-                                        t[4] * sc[32 * s + 8 * g + 4], t[5] * sc[32 * s + 8 * g + 5],
-                                        t[6] * sc[32 * s + 8 * g + 6], t[7] * sc[32 * s + 8 * g + 7]);
-#pragma unroll
-                for (int a2 = 0; a2 < 2; ++a2) {
-                    // W^T tile (d x c):  A = K^T, B = scaled Tm rows
-                    // Ut tile (c x v):   A = scaled Tm rows, B = V
-                    acc[a2][ct] = isW ? mfma16x16x32(xf[a2], tf, acc[a2][ct]) : mfma16x16x32(tf, xf[a2], acc[a2][ct]);
-                }
-            }
-        }
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                const short4v h = to_bf16x4(acc[a2][ct]);
-                if (isW)  // lane holds W^T[d = 32w+16a2+4g+i][c = 16ct+r]
-                    *reinterpret_cast<short4v*>(&sm.Ws[16 * ct + r][32 * w4 + 16 * a2 + 4 * g]) = h;
-                else      // lane holds Ut[c = 16ct+4g+i][v = 32(w-4)+16a2+r]
-                    *reinterpret_cast<short4v*>(&sm.Ut[32 * w4 + 16 * a2 + r][16 * ct + 4 * g]) = h;
-            }
-    }
-    __syncthreads();
 }
 
-// One chunk of the scan for NT 16-wide state tiles owned by this wave
-// (columns col0 + 16 nt + r of P).  use_ut: the columns belong to the value
-// channels (U = Ut - X); otherwise to the map part (U = -X).  WITH_O also
-// forms the outputs O = e^g (Q P) + A U and stores the rows that exist.
-template <int NT, bool WITH_O>
-__device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][8], int col0, bool use_ut,
-                                           int lane, u16* __restrict__ o, size_t o_row0, int len, int buf) {
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const Gates& gt = sm.gt[buf];
-    // X = W P, U = Ut - X (or -X), one half of the chunk rows at a time.  W rows
-    // are taken in the permuted order so X lands in U's layout; the bf16 copy
-    // of the state (the B operand) is packed on the fly to save registers.
-    bf16x8 Ub[NT][2];
+// ---- step 2 (one wave): (I + L)^{-1} below the diagonal, by diagonal distance,
+//     T_ij = T_ii * sum_{j<=k<i} (-L_ik) T_kj.
+__device__ __forceinline__ void step2_inverse_below(ChunkTiles& sm, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const short4v t00 = tdiag_b(sm, 0, r, g), t11 = tdiag_b(sm, 1, r, g), t22 = tdiag_b(sm, 2, r, g);
+    auto nl = [&](int i, int j) { return lds_short4(&sm.Lb[16 * i + r][16 * j + 4 * g]); };
+    auto ta = [&](int i) { return lds_short4(&sm.Tm[16 * i + r][16 * i + 4 * g]); };
+    const short4v t10 = to_bf16x4(mfma16x16x16(ta(1), to_bf16x4(mfma16x16x16(nl(1, 0), t00, zero4())), zero4()));
+    const short4v t21 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(mfma16x16x16(nl(2, 1), t11, zero4())), zero4()));
+    const short4v t32 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(mfma16x16x16(nl(3, 2), t22, zero4())), zero4()));
+    f32x4 y = mfma16x16x16(nl(2, 1), t10, mfma16x16x16(nl(2, 0), t00, zero4()));
+    const short4v t20 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(y), zero4()));
+    y = mfma16x16x16(nl(3, 2), t21, mfma16x16x16(nl(3, 1), t11, zero4()));
+    const short4v t31 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
+    y = mfma16x16x16(nl(3, 2), t20, mfma16x16x16(nl(3, 1), t10, mfma16x16x16(nl(3, 0), t00, zero4())));
+    const short4v t30 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
+    auto put = [&](int i, int j, short4v t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Tm[16 * i + 4 * g + e][16 * j + r] = static_cast<u16>(t[e]);
+    };
+    put(1, 0, t10);
+    put(2, 1, t21);
+    put(3, 2, t32);
+    put(2, 0, t20);
+    put(3, 1, t31);
+    put(3, 0, t30);
+}
+
+// K~ = diag(e^{g_c - g}) K, rows of 16-byte pieces shared by threads t = 0..nthr-1.
+__device__ __forceinline__ void step2_ktilde(ChunkTiles& sm, const Gates& gt, int t, int nthr) {
+    for (int e = t; e < C * (D / 8); e += nthr) {
+        const int row = e >> 4, c0 = (e & 15) * 8;
+        float x[8];
+        unpack8(*reinterpret_cast<const uint4*>(&sm.Ks[row][c0]), x);
+        const float f = gt.ek[row];
+        *reinterpret_cast<bf16x8*>(&sm.Kx[row][c0]) =
+            pack8(x[0] * f, x[1] * f, x[2] * f, x[3] * f, x[4] * f, x[5] * f, x[6] * f, x[7] * f);
+    }
+}
+
+// A = (Q K^T) * Gamma on and below the diagonal: blocks ta and tb of the
+// 0..9 numbering (tb formed and dropped when two = false).
+__device__ __forceinline__ void step2_qk(ChunkTiles& sm, const Gates& gt, int ta, int tb, bool two, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    f32x4 acc[2];
+    rows_dot2(sm.Qs, sm.Ks, lower_row(ta), lower_col(ta), lower_row(tb), lower_col(tb), r, g, acc[0], acc[1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (j == 1 && !two) break;
+        const int t = j ? tb : ta;
+        const int rt = lower_row(t), ct = lower_col(t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
+            sm.As[row][col] = f32_to_bf16_bits(col <= row ? __expf(fminf(gt.g[row] - gt.g[col], 0.f)) * acc[j][i] : 0.f);
+        }
+    }
+}
+
+// Zero block z (the transpose of below-diagonal block z) of a 64 x 64 tile.
+__device__ __forceinline__ void zero_above(u16 (*X)[LDA], int z, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[16 * below_col(z) + 4 * g + i][16 * below_row(z) + r] = 0;
+}
+
+// ---- step 4: W = (I + L)^{-1} diag(beta e^g) K and Ut = (I + L)^{-1} diag(beta) V
+// as plain products; the row scalings fold into the (I + L)^{-1} operand and
+// K, V are read transposed.
+// waves 0-3: W^T = K^T (Tm diag(beta e^g))^T for d rows 32w..32w+31, so each
+//            lane ends up holding 4 consecutive d of one W row (8-byte stores);
+// waves 4-7: Ut = (Tm diag(beta)) V for value channels 32(w-4)..+31.
+__device__ __forceinline__ void step4_w_ut(ChunkTiles& sm, const Gates& gt, int w, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const bool isW = w < 4;
+    const int w4 = w & 3;
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[a2][ct] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        bf16x8 xf[2];
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+            const int n0 = 32 * w4 + 16 * a2;  // d (W) or value channel (Ut)
+            xf[a2] = tr_operand(isW ? sm.Ks : sm.Vs, 32 * s, [&](int aa) { return n0 + 4 * aa; }, lane);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            if (s == 1 && ct < 2) continue;  // (I + L)^{-1} is lower triangular
+            float t[8];
+            unpack8(*reinterpret_cast<const uint4*>(&sm.Tm[16 * ct + r][32 * s + 8 * g]), t);
+            const float* sc = isW ? gt.sw : gt.b;
+            const bf16x8 tf = pack8(t[0] * sc[32 * s + 8 * g], t[1] * sc[32 * s + 8 * g + 1],
+                                    t[2] * sc[32 * s + 8 * g + 2], t[3] * sc[32 * s + 8 * g + 3],
+                                    t[4] * sc[32 * s + 8 * g + 4], t[5] * sc[32 * s + 8 * g + 5],
+                                    t[6] * sc[32 * s + 8 * g + 6], t[7] * sc[32 * s + 8 * g + 7]);
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) {
+                // W^T tile (d x c):  A = K^T, B = scaled Tm rows
+                // Ut tile (c x v):   A = scaled Tm rows, B = V
+                acc[a2][ct] = isW ? mfma16x16x32(xf[a2], tf, acc[a2][ct]) : mfma16x16x32(tf, xf[a2], acc[a2][ct]);
+            }
+        }
+    }
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const short4v h = to_bf16x4(acc[a2][ct]);
+            if (isW)  // lane holds W^T[d = 32w+16a2+4g+i][c = 16ct+r]
+                *reinterpret_cast<short4v*>(&sm.Ws[16 * ct + r][32 * w4 + 16 * a2 + 4 * g]) = h;
+            else      // lane holds Ut[c = 16ct+4g+i][v = 32(w-4)+16a2+r]
+                *reinterpret_cast<short4v*>(&sm.Ut[32 * w4 + 16 * a2 + r][16 * ct + 4 * g]) = h;
+        }
+}
+
+// ---- scan of one chunk for the NT 16-wide state tiles a wave owns (columns
+// col0 + 16 nt + r of P).
+//
+// U = Ut - W P (use_ut) or -W P (the map part), in the B-operand layout.  W
+// rows are taken in the permuted order so X = W P lands in U's layout; the
+// bf16 copy of the state is packed on the fly to save registers.
+template <int NT>
+__device__ __forceinline__ void scan_u(const ChunkTiles& sm, const f32x4 (&P)[NT][8], int col0, bool use_ut, int lane,
+                                       bf16x8 (&Ub)[NT][2]) {
+    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
         f32x4 Xa[NT], Xb[NT];
@@ -438,57 +548,73 @@ __device__ __forceinline__ void scan_chunk(const ChunkTiles& sm, f32x4 (&P)[NT][
             Ub[nt][s2] = pack_acc_pair(lo, hi);
         }
     }
-    if (WITH_O) {
-        f32x4 O[NT][4];
+}
+
+// O = Q P (the inter-chunk part of the outputs, before the e^g row scaling).
+template <int NT>
+__device__ __forceinline__ void scan_qp(const ChunkTiles& sm, const f32x4 (&P)[NT][8], int lane, f32x4 (&O)[NT][4]) {
+    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) O[nt][m] = zero4();
+        for (int m = 0; m < 4; ++m) O[nt][m] = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8 pb[NT];
+    for (int s = 0; s < 4; ++s) {
+        bf16x8 pb[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) pb[nt] = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
+        for (int nt = 0; nt < NT; ++nt) pb[nt] = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const bf16x8 a = lds_bf16x8(&sm.Qs[perm_row(m, r)][32 * s + 8 * g]);
+        for (int m = 0; m < 4; ++m) {
+            const bf16x8 a = lds_bf16x8(&sm.Qs[perm_row(m, r)][32 * s + 8 * g]);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, pb[nt], O[nt][m]);
+            for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, pb[nt], O[nt][m]);
+        }
+    }
+}
+
+// O <- diag(e^g) O + A U, stored for the rows that exist.
+template <int NT>
+__device__ __forceinline__ void scan_out(const ChunkTiles& sm, const Gates& gt, f32x4 (&O)[NT][4],
+                                         const bf16x8 (&Ub)[NT][2], int col0, int lane, u16* __restrict__ o,
+                                         size_t o_row0, int len) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float elo = gt.eg[32 * s2 + 8 * g + i], ehi = gt.eg[32 * s2 + 8 * g + 4 + i];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                O[nt][2 * s2][i] *= elo;
+                O[nt][2 * s2 + 1][i] *= ehi;
             }
         }
+    // row tile m (chunk rows 32(m/2)..+31) needs column slices s2 <= m/2
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float elo = gt.eg[32 * s2 + 8 * g + i], ehi = gt.eg[32 * s2 + 8 * g + 4 + i];
+        for (int s2 = 0; s2 <= (m >> 1); ++s2) {
+            const bf16x8 a = lds_bf16x8(&sm.As[perm_row(m, r)][32 * s2 + 8 * g]);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    O[nt][2 * s2][i] *= elo;
-                    O[nt][2 * s2 + 1][i] *= ehi;
-                }
+            for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, Ub[nt][s2], O[nt][m]);
+        }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = perm_row(m, 4 * g + i);
+            if (row < len) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    o[(o_row0 + row) * D + col0 + 16 * nt + r] = f32_to_bf16_bits(O[nt][m][i]);
             }
-        // A U over the causal blocks: row tile m (chunk rows 32(m/2)..+31) needs column slices s2 <= m/2
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int s2 = 0; s2 <= (m >> 1); ++s2) {
-                const bf16x8 a = lds_bf16x8(&sm.As[perm_row(m, r)][32 * s2 + 8 * g]);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, Ub[nt][s2], O[nt][m]);
-            }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = perm_row(m, 4 * g + i);
-                if (row < len) {
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        o[(o_row0 + row) * D + col0 + 16 * nt + r] = f32_to_bf16_bits(O[nt][m][i]);
-                }
-            }
-    }
-    // P <- e^{g_c} P + K~^T U, K~^T read transposed in the permuted row order
+        }
+}
+
+// P <- e^{g_c} P + K~^T U, K~^T read transposed in the permuted row order.
+template <int NT>
+__device__ __forceinline__ void scan_update(const ChunkTiles& sm, const Gates& gt, f32x4 (&P)[NT][8],
+                                            const bf16x8 (&Ub)[NT][2], int lane) {
     const float egc = gt.eg[C - 1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -590,15 +716,36 @@ __global__ __launch_bounds__(kThreads) void gdn_map_kernel(int BH, int T, int NC
             for (int i = 0; i < 4; ++i)
                 P[nt][t][i] = (!npart && perm_row(t, 4 * g + i) == col0 + 16 * nt + r) ? 1.f : 0.f;
 
+    // The blocks (0,1) and (2,3) above the diagonal of Tm and A are read by
+    // 32-wide operand slices and must be zero; nothing else writes them.
+    if (w >= 4) zero_above(w < 6 ? sm.Tm : sm.As, (w & 1) ? 5 : 0, lane);
     RawChunk<kThreads> rc;
-    fetch_chunk<false>(rc, nullptr, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), tid);
+    fetch_chunk<false, true>(rc, nullptr, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), tid);
     for (int n = n0; n < n1; ++n) {
-        __syncthreads();
-        stage_kv(sm, rc, tid, n & 1);
+        const Gates& gt = sm.gt[n & 1];
+        const GateRegs grg = chunk_gates(rc.a, rc.b);
+        lds_barrier();
+        stage_kv(sm, rc, grg, tid, n & 1);
         if (n + 1 < n1)
-            fetch_chunk<false>(rc, nullptr, k, v, alpha, beta, head_tok, (n + 1) * C, min(C, T - (n + 1) * C), tid);
-        chunk_tiles<false>(sm, tid, n & 1);
-        scan_chunk<2, false>(sm, P, col0, npart, lane, nullptr, 0, 0, n & 1);
+            fetch_chunk<false, true>(rc, nullptr, k, v, alpha, beta, head_tok, (n + 1) * C, min(C, T - (n + 1) * C), tid);
+        lds_barrier();
+        if (w < 4) {
+            step1_diag(sm, grg, w, lane);
+        } else {
+            const int u = w - 4;
+            step1_below(sm, gt, u, u < 2 ? u + 4 : u, u < 2, lane);
+        }
+        lds_barrier();
+        if (w == 0)
+            step2_inverse_below(sm, lane);
+        else
+            step2_ktilde(sm, gt, tid - 64, kThreads - 64);
+        lds_barrier();
+        step4_w_ut(sm, gt, w, lane);
+        lds_barrier();
+        bf16x8 Ub[2][2];
+        scan_u<2>(sm, P, col0, npart, lane, Ub);
+        scan_update<2>(sm, gt, P, Ub, lane);
     }
     if (npart)
         store_state<2>(P, ws + ws_N(bh, G, seg), col0, lane);
@@ -642,7 +789,7 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, in
         *reinterpret_cast<float4*>(ws + ws_P(bh, G, 0) + off) = x;
     }
     for (int s = 0; s + 1 < G; ++s) {
-        __syncthreads();
+        lds_barrier();
         const float* M = ws + ws_M(bh, G, s);
         f32x4 acc[2];
 #pragma unroll
@@ -672,7 +819,7 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, in
                 acc[mt] = mfma16x16x32(ml, ph, acc[mt]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             // lane holds P_{s+1}[d = 32w+16mt+4g+i][v = r]
@@ -700,9 +847,16 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
     const int n0 = seg * SEGC, n1 = min(NC, n0 + SEGC);
     const size_t head_tok = static_cast<size_t>(bh) * T;
     // Waves 0-3 carry the state (32 value channels each); waves 4-7 stage the
-    // chunks and hold the next chunk's raw inputs.  All eight build the chunk
-    // tiles.  The two loops meet at the same barriers (five per chunk), and
-    // neither set of waves keeps the other's registers live.
+    // chunks and hold the raw inputs of the next one.  Per chunk n, after
+    // barrier A: step 2 (all), B3, step 4 (all), B4, the first half of the scan
+    // (Q P and U, state carriers) while the stagers write k, v and the gates of
+    // chunk n+1, B5, then the second half (outputs, state update) while the
+    // stagers write q and run step 1 of chunk n+1 (L and the diagonal inverse
+    // blocks, whose LDS tiles the scan no longer reads).  Both roles meet the
+    // same barriers; neither keeps the other's registers live.
+    // The blocks (0,1) and (2,3) above the diagonal of Tm and A are read by
+    // 32-wide operand slices and must be zero; nothing else writes them.
+    if (w >= 4) zero_above(w < 6 ? sm.Tm : sm.As, (w & 1) ? 5 : 0, lane);
     if (w < 4) {
         const int col0 = 32 * w;
         f32x4 P[2][8];
@@ -710,27 +864,73 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
         // combined state (segment 0 included, so S_out may alias S0)
         load_state<2>(P, G == 1 ? (S0 ? S0 + static_cast<size_t>(bh) * kMat : nullptr) : ws + ws_P(bh, G, seg),
                       col0, lane);
+        lds_barrier();  // chunk n0 staged
+        lds_barrier();  // step 1 of chunk n0 done
         for (int n = n0; n < n1; ++n) {
             const int t0 = n * C;
-            __syncthreads();
-            chunk_tiles<true>(sm, tid, n & 1);
-            scan_chunk<2, true>(sm, P, col0, true, lane, o, head_tok + t0, min(C, T - t0), n & 1);
+            const Gates& gt = sm.gt[n & 1];
+            lds_barrier();  // A
+            if (w == 0)
+                step2_inverse_below(sm, lane);
+            else
+                step2_qk(sm, gt, w - 1, w + 2, true, lane);
+            lds_barrier();  // B3
+            step4_w_ut(sm, gt, w, lane);
+            lds_barrier();  // B4
+            f32x4 O[2][4];
+            bf16x8 Ub[2][2];
+            scan_qp<2>(sm, P, lane, O);
+            scan_u<2>(sm, P, col0, true, lane, Ub);
+            lds_barrier();  // B5
+            scan_out<2>(sm, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0));
+            scan_update<2>(sm, gt, P, Ub, lane);
         }
         if (seg == G - 1 && S_out) store_state<2>(P, S_out + static_cast<size_t>(bh) * kMat, col0, lane);
     } else {
         const int ptid = tid - kThreads / 2;
-        // k, v and the gates of chunk n+1 are written while the state
-        // carriers run the scan of chunk n (which reads neither).
-        RawChunk<kThreads / 2> rc;
-        fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), ptid);
-        stage_kv(sm, rc, ptid, n0 & 1);
+        const int u = w - 4;
+        // Wave u owns rows 16u..16u+15 of every staged tile, so right after
+        // writing its k rows it can form diagonal block u of step 1.  Loads of
+        // k and v for chunk n+2 are issued once those of n+1 are staged, loads
+        // of q once its q is staged.
+        RawChunk<kThreads / 2, true> rc;
+        auto fetch = [&](int n, auto with_q, auto with_kv) {
+            fetch_chunk<decltype(with_q)::value, decltype(with_kv)::value>(rc, q, k, v, alpha, beta, head_tok, n * C,
+                                                                           min(C, T - n * C), ptid);
+        };
+        using yes = std::true_type;
+        using no = std::false_type;
+        auto step1 = [&](int n, const GateRegs& grg) {
+            step1_diag(sm, grg, u, lane);
+            step1_below(sm, sm.gt[n & 1], u, u < 2 ? u + 4 : u, u < 2, lane);
+        };
+        fetch(n0, yes{}, yes{});
+        GateRegs grg = chunk_gates(rc.a, rc.b);
+        stage_kv(sm, rc, grg, ptid, n0 & 1);
+        stage_q(sm, rc, ptid);
+        lds_barrier();  // chunk n0 staged
+        step1(n0, grg);
+        if (n0 + 1 < n1) fetch(n0 + 1, yes{}, yes{});
+        lds_barrier();  // step 1 of chunk n0 done
         for (int n = n0; n < n1; ++n) {
-            const int t0 = n * C;
-            __syncthreads();
-            stage_q(sm, rc, ptid);
-            if (n + 1 < n1) fetch_chunk<true>(rc, q, k, v, alpha, beta, head_tok, t0 + C, min(C, T - t0 - C), ptid);
-            chunk_tiles<true>(sm, tid, n & 1);
-            if (n + 1 < n1) stage_kv(sm, rc, ptid, (n + 1) & 1);
+            const Gates& gt = sm.gt[n & 1];
+            lds_barrier();  // A
+            step2_ktilde(sm, gt, ptid, kThreads / 2);
+            step2_qk(sm, gt, w + 2, w + 2, false, lane);
+            lds_barrier();  // B3
+            step4_w_ut(sm, gt, w, lane);
+            lds_barrier();  // B4
+            if (n + 1 < n1) {
+                grg = chunk_gates(rc.a, rc.b);
+                stage_kv(sm, rc, grg, ptid, (n + 1) & 1);
+                if (n + 2 < n1) fetch(n + 2, no{}, yes{});
+            }
+            lds_barrier();  // B5
+            if (n + 1 < n1) {
+                stage_q(sm, rc, ptid);
+                if (n + 2 < n1) fetch(n + 2, yes{}, no{});
+                step1(n + 1, grg);
+            }
         }
     }
 }
