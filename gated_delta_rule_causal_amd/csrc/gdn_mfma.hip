@@ -773,7 +773,7 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
 
 __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, int G, const float* S0,
                                                                       float* __restrict__ ws) {
-    __shared__ __attribute__((aligned(16))) float Ps[16][D + 4];  // P_s: [value channel][j]
+    __shared__ __attribute__((aligned(16))) float Ps[2][16][D + 4];  // P_s by parity: [value channel][j]
     const int bh = blockIdx.x >> 3;
     const int tile = blockIdx.x & 7;
     if (bh >= BH) return;
@@ -785,49 +785,71 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, in
         const size_t off = static_cast<size_t>(16 * tile + rl) * D + d4;
         const float4 x = S0 ? *reinterpret_cast<const float4*>(S0 + static_cast<size_t>(bh) * kMat + off)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(&Ps[rl][d4]) = x;
+        *reinterpret_cast<float4*>(&Ps[0][rl][d4]) = x;
         *reinterpret_cast<float4*>(ws + ws_P(bh, G, 0) + off) = x;
     }
-    for (int s = 0; s + 1 < G; ++s) {
-        lds_barrier();
-        const float* M = ws + ws_M(bh, G, s);
-        f32x4 acc[2];
+    // The maps (M_s, N_s) do not depend on the states: those of step s+1 are
+    // loaded while step s runs, and M is split into bf16 pairs ahead of use.
+    // Lane (r, g) of wave w uses rows d = 32w + 16mt + r of M (8 columns per
+    // k-step) and rows d = 32w + 16mt + 4g .. +3 of column v = r of N.
+    float4 mraw[2][4][2], nraw[2];
+    auto load_maps = [&](int st) {
+        const float* M = ws + ws_M(bh, G, st);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            // N_s[d][v] is stored as [v][d]: lane (r, g) wants rows d = 32w+16mt+4g..+3 of column v = r
-            const float4 n4 = *reinterpret_cast<const float4*>(ws + ws_N(bh, G, s) +
-                                                              static_cast<size_t>(16 * tile + r) * D + 32 * w +
-                                                              16 * mt + 4 * g);
-            acc[mt] = f32x4{n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const float* mrow = M + static_cast<size_t>(32 * w + 16 * mt + r) * D + 32 * ks + 8 * g;
+                mraw[mt][ks][0] = *reinterpret_cast<const float4*>(mrow);
+                mraw[mt][ks][1] = *reinterpret_cast<const float4*>(mrow + 4);
+            }
+            nraw[mt] = *reinterpret_cast<const float4*>(ws + ws_N(bh, G, st) + static_cast<size_t>(16 * tile + r) * D +
+                                                        32 * w + 16 * mt + 4 * g);
         }
+    };
+    bf16x8 mh[2][4], ml[2][4];
+    f32x4 nv[2];
+    auto split_maps = [&]() {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const float mv[8] = {mraw[mt][ks][0].x, mraw[mt][ks][0].y, mraw[mt][ks][0].z, mraw[mt][ks][0].w,
+                                     mraw[mt][ks][1].x, mraw[mt][ks][1].y, mraw[mt][ks][1].z, mraw[mt][ks][1].w};
+                split8(mv, mh[mt][ks], ml[mt][ks]);
+            }
+            nv[mt] = f32x4{nraw[mt].x, nraw[mt].y, nraw[mt].z, nraw[mt].w};
+        }
+    };
+    if (G > 1) {
+        load_maps(0);
+        split_maps();
+    }
+    for (int s = 0; s + 1 < G; ++s) {
+        if (s + 2 < G) load_maps(s + 1);
+        lds_barrier();
+        const int cur = s & 1;
+        f32x4 acc[2] = {nv[0], nv[1]};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             bf16x8 ph, pl;
-            split8(&Ps[r][32 * ks + 8 * g], ph, pl);
+            split8(&Ps[cur][r][32 * ks + 8 * g], ph, pl);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const float* mrow = M + static_cast<size_t>(32 * w + 16 * mt + r) * D + 32 * ks + 8 * g;
-                float mv[8];
-                const float4 m0 = *reinterpret_cast<const float4*>(mrow);
-                const float4 m1 = *reinterpret_cast<const float4*>(mrow + 4);
-                mv[0] = m0.x; mv[1] = m0.y; mv[2] = m0.z; mv[3] = m0.w;
-                mv[4] = m1.x; mv[5] = m1.y; mv[6] = m1.z; mv[7] = m1.w;
-                bf16x8 mh, ml;
-                split8(mv, mh, ml);
-                acc[mt] = mfma16x16x32(mh, ph, acc[mt]);
-                acc[mt] = mfma16x16x32(mh, pl, acc[mt]);
-                acc[mt] = mfma16x16x32(ml, ph, acc[mt]);
+                acc[mt] = mfma16x16x32(mh[mt][ks], ph, acc[mt]);
+                acc[mt] = mfma16x16x32(mh[mt][ks], pl, acc[mt]);
+                acc[mt] = mfma16x16x32(ml[mt][ks], ph, acc[mt]);
             }
         }
-        lds_barrier();
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             // lane holds P_{s+1}[d = 32w+16mt+4g+i][v = r]
             const int d0 = 32 * w + 16 * mt + 4 * g;
             const float4 x = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-            *reinterpret_cast<float4*>(&Ps[r][d0]) = x;
+            *reinterpret_cast<float4*>(&Ps[cur ^ 1][r][d0]) = x;
             *reinterpret_cast<float4*>(ws + ws_P(bh, G, s + 1) + static_cast<size_t>(16 * tile + r) * D + d0) = x;
         }
+        if (s + 2 < G) split_maps();
     }
 }
 
