@@ -51,6 +51,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
@@ -124,6 +126,16 @@ def main():
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
     path_gbps = head_tokens * path_bytes_per_head_token(d) / ((prep_ms + scan_ms) * 1e-3) / 1e9
     path_tflops = head_tokens * path_flops_per_head_token(d, C) / ((prep_ms + scan_ms) * 1e-3) / 1e12
+
+    if args.copy_probe:
+        # a plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
+        # WRITE_SIZE give the factor that turns those counters into bytes
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------- decode
     wd = synth.WORKLOADS[DECODE]

@@ -774,8 +774,12 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
 __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, int G, const float* S0,
                                                                       float* __restrict__ ws) {
     __shared__ __attribute__((aligned(16))) float Ps[2][16][D + 4];  // P_s by parity: [value channel][j]
-    const int bh = blockIdx.x >> 3;
-    const int tile = blockIdx.x & 7;
+    // Workgroups are dealt to the 8 XCDs round-robin (each XCD has its own
+    // L2): the 8 column tiles of one head take block indices 8 apart, so all
+    // of them land on one XCD and share that head's maps in its L2.
+    const int i = blockIdx.x;
+    const int bh = (i >> 6) * 8 + (i & 7);
+    const int tile = (i >> 3) & 7;
     if (bh >= BH) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -1007,7 +1011,8 @@ hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const void* 
     const Plan p = make_plan(BH, T);
     float* ws = static_cast<float*>(workspace);
     if (p.G > 1) {
-        hipLaunchKernelGGL(gdn_combine_kernel, dim3(static_cast<unsigned>(BH) * 8), dim3(kCombineThreads), 0, stream, BH,
+        hipLaunchKernelGGL(gdn_combine_kernel, dim3(static_cast<unsigned>((BH + 7) / 8) * 64), dim3(kCombineThreads), 0,
+                           stream, BH,
                            p.G, S0, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
