@@ -346,17 +346,16 @@ __device__ __forceinline__ int lower_col(int t) { const int rt = lower_row(t); r
 // Diagonal block b: K K^T is symmetric there, so one accumulator tile yields
 // both L_bb and its transpose; the inverse is formed in registers and stored
 // in bf16 into Tm.
-// Gates come from the wave's registers (one token per lane).
-__device__ __forceinline__ void step1_diag(ChunkTiles& sm, const GateRegs& grg, int b, int lane) {
+__device__ __forceinline__ void step1_diag(ChunkTiles& sm, const Gates& gt, int b, int lane) {
     const int r = lane & 15, g = lane >> 4;
     const f32x4 acc = rows_dot(sm.Ks, sm.Ks, b, b, r, g);
     const int kap = 16 * b + r;
-    const float gk = __shfl(grg.g, kap, 64), bk = __shfl(grg.b, kap, 64);
+    const float gk = gt.g[kap], bk = gt.b[kap];
     f32x4 N, Nt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rho = 16 * b + 4 * g + i;
-        const float gr = __shfl(grg.g, rho, 64), br = __shfl(grg.b, rho, 64);
+        const float gr = gt.g[rho], br = gt.b[rho];
         N[i] = r < 4 * g + i ? -br * __expf(fminf(gr - gk, 0.f)) * acc[i] : 0.f;
         Nt[i] = 4 * g + i < r ? -bk * __expf(fminf(gk - gr, 0.f)) * acc[i] : 0.f;
     }
@@ -719,33 +718,46 @@ __global__ __launch_bounds__(kThreads) void gdn_map_kernel(int BH, int T, int NC
     // The blocks (0,1) and (2,3) above the diagonal of Tm and A are read by
     // 32-wide operand slices and must be zero; nothing else writes them.
     if (w >= 4) zero_above(w < 6 ? sm.Tm : sm.As, (w & 1) ? 5 : 0, lane);
+    // Per chunk n: barrier A, step 2, B3, step 4, B4, then k, v and the gates of
+    // chunk n+1 are staged (their LDS tiles are no longer read), B5, and the
+    // scan of chunk n runs together with step 1 of chunk n+1 (the scan reads
+    // neither L nor the inverse blocks).
     RawChunk<kThreads> rc;
-    fetch_chunk<false, true>(rc, nullptr, k, v, alpha, beta, head_tok, n0 * C, min(C, T - n0 * C), tid);
-    for (int n = n0; n < n1; ++n) {
-        const Gates& gt = sm.gt[n & 1];
-        const GateRegs grg = chunk_gates(rc.a, rc.b);
-        lds_barrier();
-        stage_kv(sm, rc, grg, tid, n & 1);
-        if (n + 1 < n1)
-            fetch_chunk<false, true>(rc, nullptr, k, v, alpha, beta, head_tok, (n + 1) * C, min(C, T - (n + 1) * C), tid);
-        lds_barrier();
+    auto fetch = [&](int n) {
+        fetch_chunk<false, true>(rc, nullptr, k, v, alpha, beta, head_tok, n * C, min(C, T - n * C), tid);
+    };
+    auto step1 = [&](int n) {
         if (w < 4) {
-            step1_diag(sm, grg, w, lane);
+            step1_diag(sm, sm.gt[n & 1], w, lane);
         } else {
             const int u = w - 4;
-            step1_below(sm, gt, u, u < 2 ? u + 4 : u, u < 2, lane);
+            step1_below(sm, sm.gt[n & 1], u, u < 2 ? u + 4 : u, u < 2, lane);
         }
-        lds_barrier();
+    };
+    fetch(n0);
+    stage_kv(sm, rc, chunk_gates(rc.a, rc.b), tid, n0 & 1);
+    if (n0 + 1 < n1) fetch(n0 + 1);
+    lds_barrier();
+    step1(n0);
+    for (int n = n0; n < n1; ++n) {
+        const Gates& gt = sm.gt[n & 1];
+        lds_barrier();  // A
         if (w == 0)
             step2_inverse_below(sm, lane);
         else
             step2_ktilde(sm, gt, tid - 64, kThreads - 64);
-        lds_barrier();
+        lds_barrier();  // B3
         step4_w_ut(sm, gt, w, lane);
-        lds_barrier();
+        lds_barrier();  // B4
+        if (n + 1 < n1) {
+            stage_kv(sm, rc, chunk_gates(rc.a, rc.b), tid, (n + 1) & 1);
+            if (n + 2 < n1) fetch(n + 2);
+        }
+        lds_barrier();  // B5
         bf16x8 Ub[2][2];
         scan_u<2>(sm, P, col0, npart, lane, Ub);
         scan_update<2>(sm, gt, P, Ub, lane);
+        if (n + 1 < n1) step1(n + 1);
     }
     if (npart)
         store_state<2>(P, ws + ws_N(bh, G, seg), col0, lane);
@@ -926,16 +938,15 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
         };
         using yes = std::true_type;
         using no = std::false_type;
-        auto step1 = [&](int n, const GateRegs& grg) {
-            step1_diag(sm, grg, u, lane);
+        auto step1 = [&](int n) {
+            step1_diag(sm, sm.gt[n & 1], u, lane);
             step1_below(sm, sm.gt[n & 1], u, u < 2 ? u + 4 : u, u < 2, lane);
         };
         fetch(n0, yes{}, yes{});
-        GateRegs grg = chunk_gates(rc.a, rc.b);
-        stage_kv(sm, rc, grg, ptid, n0 & 1);
+        stage_kv(sm, rc, chunk_gates(rc.a, rc.b), ptid, n0 & 1);
         stage_q(sm, rc, ptid);
         lds_barrier();  // chunk n0 staged
-        step1(n0, grg);
+        step1(n0);
         if (n0 + 1 < n1) fetch(n0 + 1, yes{}, yes{});
         lds_barrier();  // step 1 of chunk n0 done
         for (int n = n0; n < n1; ++n) {
@@ -947,15 +958,14 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
             step4_w_ut(sm, gt, w, lane);
             lds_barrier();  // B4
             if (n + 1 < n1) {
-                grg = chunk_gates(rc.a, rc.b);
-                stage_kv(sm, rc, grg, ptid, (n + 1) & 1);
+                stage_kv(sm, rc, chunk_gates(rc.a, rc.b), ptid, (n + 1) & 1);
                 if (n + 2 < n1) fetch(n + 2, no{}, yes{});
             }
             lds_barrier();  // B5
             if (n + 1 < n1) {
                 stage_q(sm, rc, ptid);
                 if (n + 2 < n1) fetch(n + 2, yes{}, no{});
-                step1(n + 1, grg);
+                step1(n + 1);
             }
         }
     }
