@@ -30,6 +30,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 PREFILL = "gdn_bf16_2x16x8192"
 DECODE = "gdn_decode_256x32"
+LA_PREFILL = "la_bf16_4x16x4096"
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
 # d = d_k = d_v: bytes = q, k, v, o in bf16 + alpha, beta in fp32; flops as
@@ -43,6 +44,30 @@ def path_flops_per_head_token(d, C):
     return 5 * C * d + C * C / 3 + 6 * d * d
 
 
+# HBM bytes per dispatch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# (scaled by the same counters on a plain copy of known size), stored per
+# kernel with the hash of the source file it was built from; numbers taken on
+# another version of that source are not used.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def measured_traffic(kernels):
+    """Summed HBM bytes per launch of `kernels`, or None when any of them has
+    no counters for its current source."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))["kernels"]
+        total = 0.0
+        for k in kernels:
+            src = os.path.join(ROOT, rec[k]["source"])
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec[k]["source_sha256"]:
+                return None
+            total += rec[k]["bytes_per_dispatch"]
+        return total
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -51,6 +76,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--la-steps", type=int, default=10, help="timed calls of the linear-attention prefill")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -115,15 +141,17 @@ def main():
     #   prep  = segment maps: k, v, alpha, beta of the first G-1 segments; (M, N) per head-segment
     #   scan  = combine (maps + entering states) + outputs: q, k, v, alpha, beta, o, entering
     #           states, final state
-    frac = (G - 1) / G
-    prep_bytes = head_tokens * frac * (2 * d * 2 + 8) + B * H * (G - 1) * 2 * mat
-    scan_bytes = (head_tokens * (3 * d * 2 + 8 + d * 2) + B * H * (G - 1) * 2 * mat + B * H * G * 2 * mat +
-                  B * H * mat)
-    kern = {"gdn_prefill_prep (gdn_map_kernel)": (prep_ms, prep_bytes),
-            "gdn_prefill_scan (gdn_combine_kernel + gdn_out_kernel)": (scan_ms, scan_bytes)}
+    # roofline of the dominant launch: algorithmic bytes = the path's minimal
+    # I/O per head-token (q, k, v, o in bf16, alpha, beta in fp32) times the
+    # head-tokens one launch processes (all of them, for either launch)
+    alg_bytes = head_tokens * path_bytes_per_head_token(d)
+    kern = {"gdn_prefill_prep (gdn_map_kernel)": (prep_ms, ["gdn_map_kernel"]),
+            "gdn_prefill_scan (gdn_combine_kernel + gdn_out_kernel)": (scan_ms,
+                                                                       ["gdn_combine_kernel", "gdn_out_kernel"])}
     dom = max(kern, key=lambda n: kern[n][0])
-    dom_ms, dom_bytes = kern[dom]
-    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dom_ms, dom_kernels = kern[dom]
+    dom_gbps = alg_bytes / (dom_ms * 1e-3) / 1e9
+    dom_traffic = measured_traffic(dom_kernels)
     path_gbps = head_tokens * path_bytes_per_head_token(d) / ((prep_ms + scan_ms) * 1e-3) / 1e9
     path_tflops = head_tokens * path_flops_per_head_token(d, C) / ((prep_ms + scan_ms) * 1e-3) / 1e12
 
@@ -136,6 +164,31 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    # ------------------------------------------- linear-attention prefill
+    wl = synth.WORKLOADS[LA_PREFILL]
+    Bl, Hl, Tl, dl, Cl = wl["B"], wl["H"], wl["T"], wl["dk"], wl["chunk"]
+    lq, lk, lv = synth.la_batch(wl["seed"], Bl, Hl, Tl, dl, dl, "bf16", wl["scale"])
+    la_sets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (lq, lk, lv)) for _ in range(3)]
+    del lq, lk, lv
+    la_out = torch.empty((Bl, Hl, Tl, dl), dtype=torch.bfloat16, device=dev)
+    la_S = torch.empty((Bl, Hl, dl, dl), dtype=torch.float32, device=dev)
+    la_z = torch.empty((Bl, Hl, dl), dtype=torch.float32, device=dev)
+    for i in range(2):
+        gd.lin_attn_prefill(*la_sets[i % 3], form="chunked", chunk=Cl, out=la_out, S_out=la_S, z_out=la_z)
+    torch.cuda.synchronize()
+    la_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    la_ev[0].record()
+    for i in range(args.la_steps):
+        gd.lin_attn_prefill(*la_sets[i % 3], form="chunked", chunk=Cl, out=la_out, S_out=la_S, z_out=la_z)
+        la_ev[i + 1].record()
+    torch.cuda.synchronize()
+    la_ms = float(np.mean([la_ev[i].elapsed_time(la_ev[i + 1]) for i in range(args.la_steps)]))
+    la_head_tokens = Bl * Hl * Tl
+    la_bytes = la_head_tokens * 4 * dl * 2           # q, k, v, o in bf16
+    la_flops = la_head_tokens * (2 * Cl * dl + 4 * dl * dl)
+    la_gbps = la_bytes / (la_ms * 1e-3) / 1e9
+    del la_sets
 
     # ------------------------------------------------------------- decode
     wd = synth.WORKLOADS[DECODE]
@@ -188,8 +241,8 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "chunk": C,
                    "parallelism": "single GPU"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms},
+                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": dom_traffic,
+                     "bytes_per_launch": alg_bytes, "avg_launch_ms": dom_ms},
         "kernels_ms": {"gdn_prefill_prep": prep_ms, "gdn_prefill_scan": scan_ms, "segments_per_head": G},
         "path_roofline": {"bytes_per_head_token": path_bytes_per_head_token(d),
                           "flops_per_head_token": path_flops_per_head_token(d, C),
@@ -201,8 +254,16 @@ def main():
                    "state_GBps": dec_state_gbps, "total_GBps": dec_total_gbps,
                    "roofline": {"kernel": "recurrent_kernel (decode)", "bound": "hbm",
                                 "achieved": dec_total_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                "frac": dec_total_gbps / HBM_PEAK_GBPS, "traffic": None,
+                                "frac": dec_total_gbps / HBM_PEAK_GBPS,
+                                "traffic": measured_traffic(["recurrent_kernel_gated_delta_decode"]),
                                 "bytes_per_launch": state_bytes + io_bytes, "avg_launch_ms": dec_ms}},
+        "la_prefill": {"workload": "normalised linear attention prefill B=4 H=16 T=4096 d=128 chunk=64, bf16 I/O, "
+                                   "fp32 state", "calls": args.la_steps, "ms_per_call": la_ms,
+                       "tokens_per_s": Bl * Tl / (la_ms * 1e-3),
+                       "roofline": {"kernel": "la_chunked_mfma_kernel", "bound": "hbm", "achieved": la_gbps,
+                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": la_gbps / HBM_PEAK_GBPS,
+                                    "bytes_per_launch": la_bytes, "avg_launch_ms": la_ms,
+                                    "achieved_TFLOPs": la_flops / (la_ms * 1e-3) / 1e12}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
