@@ -157,6 +157,13 @@ la_status lin_attn_prefill(int dtype, int B, int H, int T, int dk, int dv, const
     }
     const size_t need = la_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
     if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
+    if (need > 0) {
+        const Span w{workspace, need};
+        for (const Span& b : in)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+        for (const Span& b : outs)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) {

@@ -9,7 +9,15 @@
 //     num = A V_b + phi(Q_b) S^T,   den = rowsum(A) + phi(Q_b) z
 //     O_b = num / den,   then  S += V_b^T phi(K_b),  z += colsum phi(K_b)
 //
-// One workgroup (4 waves) per head walks the blocks in order.  Each wave
+// The sequence of every head is cut into G segments of whole blocks so that
+// B*H*G workgroups fill the chip (S and z are sums over tokens, so a segment's
+// contribution does not depend on what came before):
+//  * la_chunked_mfma_kernel<false> (segments 0..G-2): the segment's
+//    contributions dS = sum V_b^T phi(K_b), dz = sum colsum phi(K_b);
+//  * la_combine_kernel: entering states by prefix sums, S0 + dS_0 + ... ;
+//  * la_chunked_mfma_kernel<true> (every segment): outputs from the entering
+//    state, and the final state in the last segment.
+// One workgroup (4 waves) walks the blocks of its segment in order.  Each wave
 // owns 32 value channels of the state, P = S_rows^T (d_k x 32, fp32) in
 // accumulator registers; the state update is a plain accumulation
 // P += phi(K_b)^T V_b on MFMA and, as in the gated-delta scan, accumulator
@@ -32,6 +40,16 @@ constexpr int LDR = D + 8;   // row-major [C][LDR] bf16 tiles (272-B rows)
 constexpr int LDT = C + 8;   // transposed [D][LDT] bf16 tiles (144-B rows)
 constexpr int kThreads = 256;
 constexpr int kItems = C * D / 8 / kThreads;  // 16-byte loads per thread per tile
+constexpr int kTargetBlocks = 256;           // workgroups that fill the chip (one per CU)
+constexpr size_t kMat = static_cast<size_t>(D) * D;
+
+// Workspace record per (head, segment): entering state P (state layout
+// [d_v][d_k]) and normaliser zP, then the segment's contributions dS, dz.
+constexpr size_t kRec = 2 * kMat + 2 * D;
+__device__ __forceinline__ size_t ws_P(int bh, int G, int s) { return (static_cast<size_t>(bh) * G + s) * kRec; }
+__device__ __forceinline__ size_t ws_zP(int bh, int G, int s) { return ws_P(bh, G, s) + kMat; }
+__device__ __forceinline__ size_t ws_dS(int bh, int G, int s) { return ws_P(bh, G, s) + kMat + D; }
+__device__ __forceinline__ size_t ws_dz(int bh, int G, int s) { return ws_P(bh, G, s) + 2 * kMat + D; }
 
 __device__ __forceinline__ int perm_row(int t, int rr) {
     return 32 * (t >> 1) + 8 * (rr >> 2) + 4 * (t & 1) + (rr & 3);
@@ -39,9 +57,12 @@ __device__ __forceinline__ int perm_row(int t, int rr) {
 
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// OUT = false: segment contributions only (no q, no outputs), from a zero state.
+template <bool OUT>
 __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
-    int T, int NC, const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const float* S0, const float* z0, u16* __restrict__ o, float* S_out, float* z_out) {
+    int BH, int T, int NC, int G, int SEGC, const u16* __restrict__ q, const u16* __restrict__ k,
+    const u16* __restrict__ v, const float* S0, const float* z0, float* ws, u16* __restrict__ o, float* S_out,
+    float* z_out) {
     __shared__ __attribute__((aligned(16))) u16 fQ[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 fK[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 fKt[D][LDT];
@@ -49,7 +70,19 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
     __shared__ __attribute__((aligned(16))) u16 As[C][LDT];
     __shared__ float zs[D], dens[C], rsum[C];
 
-    const int bh = blockIdx.x;
+    const int nseg = OUT ? G : G - 1;
+    const int bh = blockIdx.x / nseg;
+    const int seg = blockIdx.x - bh * nseg;
+    if (bh >= BH) return;
+    const int n0 = seg * SEGC, n1 = min(NC, n0 + SEGC);
+    // entering state: S0 itself when the sequence is one segment, else the
+    // prefix sum from the workspace (segment 0 included, so S_out may alias S0)
+    const float* Sin = !OUT ? nullptr
+                       : G == 1 ? (S0 ? S0 + static_cast<size_t>(bh) * kMat : nullptr)
+                                : ws + ws_P(bh, G, seg);
+    const float* zin = !OUT ? nullptr
+                       : G == 1 ? (z0 ? z0 + static_cast<size_t>(bh) * D : nullptr)
+                                : ws + ws_zP(bh, G, seg);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: MFMAs sit in branches on it
     const int lane = tid & 63;
@@ -61,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int vc = 32 * w + 16 * nb + r;
-        const float* srow = S0 ? S0 + (static_cast<size_t>(bh) * D + vc) * D : nullptr;
+        const float* srow = Sin ? Sin + static_cast<size_t>(vc) * D : nullptr;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int d0 = 32 * s + 8 * g;
@@ -76,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             }
         }
     }
-    if (tid < D) zs[tid] = z0 ? z0[static_cast<size_t>(bh) * D + tid] : 0.f;
+    if (tid < D) zs[tid] = zin ? zin[tid] : 0.f;
 
     // ---- raw chunk prefetch: item e = tid + kThreads * it -> row = e % C, c8 = 8 (e / C)
     uint4 rq[kItems], rk[kItems], rv[kItems];
@@ -91,15 +124,15 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             rq[it] = rk[it] = rv[it] = make_uint4(0, 0, 0, 0);
             if (row < len) {
                 const size_t gi = head + static_cast<size_t>(t0 + row) * D + c8;
-                rq[it] = *reinterpret_cast<const uint4*>(q + gi);
+                if (OUT) rq[it] = *reinterpret_cast<const uint4*>(q + gi);
                 rk[it] = *reinterpret_cast<const uint4*>(k + gi);
                 rv[it] = *reinterpret_cast<const uint4*>(v + gi);
             }
         }
     };
-    fetch(0);
+    fetch(n0);
 
-    for (int n = 0; n < NC; ++n) {
+    for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
         const int len = min(C, T - t0);
         __syncthreads();  // the previous block's LDS tiles are no longer read
@@ -123,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             }
             const bf16x8 pq = pack8(xq[0], xq[1], xq[2], xq[3], xq[4], xq[5], xq[6], xq[7]);
             const bf16x8 pk = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
-            *reinterpret_cast<bf16x8*>(&fQ[row][c8]) = pq;
+            if (OUT) *reinterpret_cast<bf16x8*>(&fQ[row][c8]) = pq;
             *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -133,11 +166,11 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 Vt[c8 + j][row] = static_cast<u16>((j & 1) ? (wv[j >> 1] >> 16) : (wv[j >> 1] & 0xffffu));
             }
         }
-        if (n + 1 < NC) fetch(n + 1);
+        if (n + 1 < n1) fetch(n + 1);
         __syncthreads();
 
         // ---- A = tril(phi(Q) phi(K)^T), row tile w, and its row sums (fp32)
-        {
+        if constexpr (OUT) {
             float rs[4] = {0.f, 0.f, 0.f, 0.f};
             for (int ct = 0; ct < 4; ++ct) {
                 if (ct <= w) {
@@ -164,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 if (r == 0) rsum[16 * w + 4 * g + i] = t;
             }
         }
+        if constexpr (OUT) {
         __syncthreads();
         // ---- den = rowsum(A) + phi(Q) z   (z of the previous blocks)
         {
@@ -175,6 +209,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             if ((tid & 3) == 0) dens[row] = acc + rsum[row];
         }
         __syncthreads();
+        }
         // ---- z += colsum phi(K)  (read again only after the next loop-top barrier)
         if (tid < D) {
             float acc = zs[tid];
@@ -192,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             for (int s2 = 0; s2 < 2; ++s2) Vb[nb][s2] = lds8(&Vt[32 * w + 16 * nb + r][32 * s2 + 8 * g]);
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < (OUT ? 4 : 0); ++m) {
             f32x4 acc[2] = {zero4(), zero4()};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -228,10 +263,15 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
         }
     }
 
-    if (S_out) {
+    // OUT: final state of the last segment; otherwise the segment's contributions
+    float* Sdst = OUT ? (seg == G - 1 && S_out ? S_out + static_cast<size_t>(bh) * kMat : nullptr)
+                      : ws + ws_dS(bh, G, seg);
+    float* zdst = OUT ? (seg == G - 1 && z_out ? z_out + static_cast<size_t>(bh) * D : nullptr)
+                      : ws + ws_dz(bh, G, seg);
+    if (Sdst) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            float* srow = S_out + (static_cast<size_t>(bh) * D + 32 * w + 16 * nb + r) * D;
+            float* srow = Sdst + static_cast<size_t>(32 * w + 16 * nb + r) * D;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int d0 = 32 * s + 8 * g;
@@ -243,7 +283,49 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
         }
     }
     __syncthreads();
-    if (z_out && tid < D) z_out[static_cast<size_t>(bh) * D + tid] = zs[tid];
+    if (zdst && tid < D) zdst[tid] = zs[tid];
+}
+
+// Entering states of every segment: P_0 = S0 (or 0), P_{s+1} = P_s + dS_s, and
+// the same for z.  16 workgroups per head, 4 consecutive floats per thread.
+__global__ __launch_bounds__(kThreads) void la_combine_kernel(int BH, int G, const float* S0, const float* z0,
+                                                              float* ws) {
+    const int bh = blockIdx.x >> 4;
+    if (bh >= BH) return;
+    const int part = blockIdx.x & 15;
+    const size_t e = (static_cast<size_t>(part) * kThreads + threadIdx.x) * 4;   // < kMat
+    float4 run = S0 ? *reinterpret_cast<const float4*>(S0 + static_cast<size_t>(bh) * kMat + e)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < G; ++s) {
+        *reinterpret_cast<float4*>(ws + ws_P(bh, G, s) + e) = run;
+        if (s + 1 < G) {
+            const float4 d = *reinterpret_cast<const float4*>(ws + ws_dS(bh, G, s) + e);
+            run.x += d.x; run.y += d.y; run.z += d.z; run.w += d.w;
+        }
+    }
+    if (part == 0 && threadIdx.x < D) {
+        float zr = z0 ? z0[static_cast<size_t>(bh) * D + threadIdx.x] : 0.f;
+        for (int s = 0; s < G; ++s) {
+            ws[ws_zP(bh, G, s) + threadIdx.x] = zr;
+            if (s + 1 < G) zr += ws[ws_dz(bh, G, s) + threadIdx.x];
+        }
+    }
+}
+
+struct Plan {
+    int NC, G, SEGC;
+};
+
+// Segments per head so that B*H*G workgroups roughly fill the chip.
+Plan make_plan(int BH, int T) {
+    Plan p;
+    p.NC = (T + C - 1) / C;
+    int G = kTargetBlocks / (BH > 0 ? BH : 1);
+    if (G < 1) G = 1;
+    if (G > p.NC) G = p.NC;
+    p.SEGC = (p.NC + G - 1) / G;
+    p.G = (p.NC + p.SEGC - 1) / p.SEGC;  // every segment non-empty
+    return p;
 }
 
 }  // namespace
@@ -252,16 +334,32 @@ bool la_mfma_supported(int dtype, int dk, int dv, int chunk) {
     return dtype == kBF16 && dk == D && dv == D && chunk == C;
 }
 
-size_t la_mfma_workspace_bytes(int, int, int, int, int, int) { return 0; }
+size_t la_mfma_workspace_bytes(int B, int H, int T, int, int, int) {
+    const int BH = B * H;
+    if (BH <= 0 || T <= 0) return 0;
+    const Plan p = make_plan(BH, T);
+    return p.G == 1 ? 0 : static_cast<size_t>(BH) * p.G * kRec * sizeof(float);
+}
 
 hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* S0,
-                          const float* z0, void* o, float* S_out, float* z_out, void*, hipStream_t stream) {
+                          const float* z0, void* o, float* S_out, float* z_out, void* workspace, hipStream_t stream) {
     const int BH = B * H;
     if (BH <= 0 || T <= 0) return hipSuccess;
-    const int NC = (T + C - 1) / C;
-    hipLaunchKernelGGL(la_chunked_mfma_kernel, dim3(BH), dim3(kThreads), 0, stream, T, NC,
-                       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), S0, z0,
-                       static_cast<u16*>(o), S_out, z_out);
+    const Plan p = make_plan(BH, T);
+    float* ws = static_cast<float*>(workspace);
+    const u16 *q16 = static_cast<const u16*>(q), *k16 = static_cast<const u16*>(k), *v16 = static_cast<const u16*>(v);
+    if (p.G > 1) {
+        hipLaunchKernelGGL(la_chunked_mfma_kernel<false>, dim3(static_cast<unsigned>(BH) * (p.G - 1)), dim3(kThreads),
+                           0, stream, BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, S0, z0, ws, nullptr, nullptr, nullptr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(la_combine_kernel, dim3(static_cast<unsigned>(BH) * 16), dim3(kThreads), 0, stream, BH,
+                           p.G, S0, z0, ws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(la_chunked_mfma_kernel<true>, dim3(static_cast<unsigned>(BH) * p.G), dim3(kThreads), 0, stream,
+                       BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, S0, z0, ws, static_cast<u16*>(o), S_out, z_out);
     return hipGetLastError();
 }
 

@@ -82,7 +82,8 @@ enum { LA_FN_LIN_ATTN_PREFILL = 0, LA_FN_GDN_PREFILL = 1, LA_FN_DECODE_STEP = 2 
  * the same as z0 (in-place update); any other overlap is an error.
  * workspace/ws_bytes: device scratch of at least
  * la_workspace_bytes(LA_FN_LIN_ATTN_PREFILL, ...) bytes (may be NULL when that
- * is 0); its contents on entry and exit are unspecified.
+ * is 0); its contents on entry and exit are unspecified, and it must not
+ * overlap any tensor argument (LA_ERR_ARG).
  */
 la_status lin_attn_prefill(int dtype, int B, int H, int T, int dk, int dv,
                            const void* q, const void* k, const void* v,

@@ -192,3 +192,22 @@ def test_split_gdn_validation(lib):
     assert n > 0 and scan(T=1000, ws_bytes=n - 1) == LA_ERR_WORKSPACE
     # one segment per head needs no workspace (many heads, short sequence)
     assert lib.la_workspace_bytes(1, BF16, 64, 8, 64, 128, 128, CHUNKED, 64) == 0
+
+
+def test_segmented_linear_attention_workspace(lib):
+    """The bf16 chunked linear-attention path cuts long sequences into segments
+    and needs a workspace; it must not overlap any tensor."""
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+
+    def la(T=1000, ws=9, ws_bytes=1 << 40, q=1, o=4):
+        return lib.lin_attn_prefill(BF16, 1, 2, T, 128, 128, f(q), P(2), P(3), None, None, f(o), None, None,
+                                    CHUNKED, 64, f(ws), ws_bytes, None)
+
+    n = lib.la_workspace_bytes(0, BF16, 1, 2, 1000, 128, 128, CHUNKED, 64)
+    assert n > 0
+    assert la(ws=None) == LA_ERR_WORKSPACE
+    assert la(ws_bytes=n - 1) == LA_ERR_WORKSPACE
+    assert la(ws=1) == LA_ERR_ARG            # workspace on top of q
+    assert la(ws=4) == LA_ERR_ARG            # workspace on top of o
+    # one segment (short sequence, many heads): no workspace
+    assert lib.la_workspace_bytes(0, BF16, 64, 8, 64, 128, 128, CHUNKED, 64) == 0

@@ -25,8 +25,12 @@ def gd():
     return m
 
 
+# (the library cuts each head into up to 256 / (B*H) segments of whole chunks:
+#  one chunk per segment, several per segment with a short last one
+#  (4x16x600: 10 chunks -> 3,3,3,1), and a single segment (16x16x130))
 @pytest.mark.parametrize("B,H,T,with_state", [(1, 2, 300, True), (2, 1, 64, False), (1, 3, 65, True),
-                                              (1, 1, 1, False), (2, 2, 1000, True)])
+                                              (1, 1, 1, False), (2, 2, 1000, True), (4, 16, 600, True),
+                                              (16, 16, 130, True)])
 def test_la_mfma_small(gd, B, H, T, with_state):
     q, k, v = synth.la_batch(41, B, H, T, D, D, "bf16", scale=1 / np.sqrt(D))
     S0 = z0 = None
