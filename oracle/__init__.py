@@ -27,6 +27,9 @@ from .linear_attention import (
     la_decode_step,
     decayed_recurrent,
     decayed_parallel,
+    gated_recurrent,
+    gated_parallel,
+    gated_decode_step,
 )
 from .gated_delta import (
     gdn_recurrent,

@@ -10,7 +10,7 @@ An optional ``heads`` list of (b, h) pairs restricts the work to a sample.
 
 import numpy as np
 
-from .linear_attention import phi, la_parallel, la_recurrent, la_chunked
+from .linear_attention import phi, la_parallel, la_recurrent, la_chunked, gated_recurrent
 from .gated_delta import gdn_recurrent, gdn_chunked
 
 
@@ -93,3 +93,25 @@ def la_step_heads(q, k, v, S, z):
     z_new = z + fk
     o = (S_new @ fq[:, :, None])[..., 0] / np.sum(z_new * fq, axis=1)[:, None]
     return o, S_new, z_new
+
+
+def gla(q, k, v, alpha, S0=None, heads=None):
+    """Gated (scalar-gate) unnormalised linear attention over the batch with
+    the recurrent definition; returns (o, S) (only the listed heads filled)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    S = np.zeros((B, H, dv, dk))
+    for b, h in _heads(B, H, heads):
+        s0 = None if S0 is None else S0[b, h]
+        o[b, h], S[b, h] = gated_recurrent(q[b, h], k[b, h], v[b, h], alpha[b, h], s0)
+    return o, S
+
+
+def gla_step_heads(q, k, v, alpha, S):
+    """One gated linear-attention step for many independent heads at once:
+    S <- alpha S + v k^T, o = S q (section "Memory must forget: decay and
+    gates"), broadcast over the head axis.  Returns (o [n, dv], S_new)."""
+    q, k, v, alpha, S = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, S))
+    S_new = alpha[:, None, None] * S + v[:, :, None] * k[:, None, :]
+    return (S_new @ q[:, :, None])[..., 0], S_new

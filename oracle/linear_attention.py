@@ -137,3 +137,55 @@ def decayed_parallel(Q, K, V, gamma):
     j = np.arange(T)[None, :]
     D = np.where(j <= i, float(gamma) ** np.maximum(i - j, 0), 0.0)
     return ((Q @ K.T) * D) @ V, D
+
+
+
+def gated_recurrent(Q, K, V, alpha, S0=None):
+    """Unnormalised linear attention with a per-token scalar gate; returns (O, S).
+
+    [Linear attention and hybrids, section "Memory must forget: decay and
+    gates": the input-dependent gate alpha_t in place of the constant gamma of
+    the decay equation]: S_t = alpha_t S_{t-1} + v_t k_t^T, o_t = S_t q_t
+    (written first, then read, as in every recurrent form on the page).
+    alpha_t = gamma for all t is the decay equation itself.
+    """
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    alpha = np.asarray(alpha, dtype=np.float64)
+    T, dk = Q.shape
+    dv = V.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, dtype=np.float64)
+    O = np.zeros((T, dv))
+    for t in range(T):
+        S = alpha[t] * S + np.outer(V[t], K[t])
+        O[t] = S @ Q[t]
+    return O, S
+
+
+def gated_parallel(Q, K, V, alpha, S0=None):
+    """Masked parallel form of :func:`gated_recurrent`; returns (O, D).
+
+    [Same section: with the gate, D_ij = alpha_{j+1} alpha_{j+2} ... alpha_i for
+    j <= i (an empty product, 1, on the diagonal) and 0 above it]:
+    O = ((Q K^T) * D) V, plus the entering state seen through all gates so
+    far: row i adds (alpha_1 ... alpha_i) S0 q_i.  The products are formed
+    directly, not through logarithms.
+    """
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    alpha = np.asarray(alpha, dtype=np.float64)
+    T = Q.shape[0]
+    D = np.zeros((T, T))
+    for i in range(T):
+        for j in range(i + 1):
+            D[i, j] = np.prod(alpha[j + 1:i + 1])
+    O = ((Q @ K.T) * D) @ V
+    if S0 is not None:
+        carry = np.array([np.prod(alpha[:i + 1]) for i in range(T)])
+        O = O + carry[:, None] * (Q @ np.asarray(S0, dtype=np.float64).T)
+    return O, D
+
+
+def gated_decode_step(q, k, v, alpha, S):
+    """One generation step of :func:`gated_recurrent`; returns (o, S_new)."""
+    O, S1 = gated_recurrent(np.asarray(q)[None, :], np.asarray(k)[None, :], np.asarray(v)[None, :],
+                            np.array([alpha]), S)
+    return O[0], S1

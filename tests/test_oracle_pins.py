@@ -133,6 +133,50 @@ def pin_decay(ns):
     assert np.array_equal(D.round(2), np.array(g["D_rounded_2dp"]))
 
 
+def pin_gated_reduces_to_decay(ns):
+    """A constant gate is the decay equation: same outputs as the decayed
+    recurrence on the page's example inputs, and the gated mask D equals the
+    page's printed gamma^(i-j) mask."""
+    g = golden("decay_forms.json")
+    rng = np.random.default_rng(0)
+    Q, K, V = rng.normal(size=(3, g["T"], g["d"]))
+    alpha = np.full(g["T"], g["gamma"])
+    o_g, S_g = ns.gated_recurrent(Q, K, V, alpha)
+    o_d, S_d = ns.decayed_recurrent(Q, K, V, g["gamma"])
+    assert np.abs(o_g - o_d).max() < 1e-13 and np.abs(S_g - S_d).max() < 1e-13
+    _, D = ns.gated_parallel(Q, K, V, alpha)
+    assert np.array_equal(D.round(2), np.array(g["D_rounded_2dp"]))
+    # alpha = 1: the plain outer-product memory
+    o_1, _ = ns.gated_recurrent(Q, K, V, np.ones(g["T"]))
+    assert np.abs(o_1 - np.tril(Q @ K.T) @ V).max() < 1e-12
+
+
+def pin_gated_forms_and_exact(ns):
+    """Recurrent and masked parallel forms (the gate products formed directly)
+    agree with a carried state; both match the recurrence evaluated exactly in
+    rational arithmetic; split-resume equals one call; the decode step is the
+    recurrence for one token."""
+    rng = np.random.default_rng(11)
+    T, dk, dv = 23, 5, 3
+    Q, K, V = rng.normal(size=(T, dk)), rng.normal(size=(T, dk)), rng.normal(size=(T, dv))
+    a = 1 / (1 + np.exp(-rng.normal(1.0, 1.0, T)))
+    S0 = rng.normal(size=(dv, dk))
+    o_r, S_r = ns.gated_recurrent(Q, K, V, a, S0)
+    o_p, _ = ns.gated_parallel(Q, K, V, a, S0)
+    assert np.abs(o_r - o_p).max() < 1e-12
+    F = lambda x: Fraction(float(x))
+    S = [[F(S0[i, j]) for j in range(dk)] for i in range(dv)]
+    for t in range(8):
+        S = [[F(a[t]) * S[i][j] + F(V[t, i]) * F(K[t, j]) for j in range(dk)] for i in range(dv)]
+        o_t = [sum(S[i][j] * F(Q[t, j]) for j in range(dk)) for i in range(dv)]
+        assert max(abs(float(o_t[i]) - o_r[t, i]) for i in range(dv)) < 1e-12
+    o1, S1 = ns.gated_recurrent(Q[:9], K[:9], V[:9], a[:9], S0)
+    o2, S2 = ns.gated_recurrent(Q[9:], K[9:], V[9:], a[9:], S1)
+    assert np.abs(np.vstack([o1, o2]) - o_r).max() < 1e-12 and np.abs(S2 - S_r).max() < 1e-12
+    o_s, S_s = ns.gated_decode_step(Q[0], K[0], V[0], a[0], S0)
+    assert np.abs(o_s - o_r[0]).max() < 1e-13
+
+
 def pin_delta_example(ns):
     g = golden("delta_rule_example.json")
     k = np.array([g["key"], g["key"]])
@@ -265,7 +309,8 @@ def pin_gdn_chunk_invariance(ns):
 
 GDN_PINS = [pin_delta_example, pin_memory_capacity, pin_gdn_unit_key_recall, pin_gdn_beta_zero,
             pin_gdn_orthonormal_recall, pin_gdn_bruteforce_exact, pin_gdn_chunk_invariance]
-LA_PINS = [pin_phi, pin_three_forms, pin_la_closed_forms, pin_la_chunk_invariance, pin_decay]
+LA_PINS = [pin_phi, pin_three_forms, pin_la_closed_forms, pin_la_chunk_invariance, pin_decay,
+           pin_gated_reduces_to_decay, pin_gated_forms_and_exact]
 
 
 @pytest.mark.parametrize("pin", LA_PINS + GDN_PINS, ids=lambda f: f.__name__)
@@ -306,7 +351,7 @@ def _namespace(la_ns=None, gd_ns=None):
     la_src = la_ns or vars(la_mod)
     gd_src = gd_ns or vars(gd_mod)
     names = ["phi", "la_parallel", "la_recurrent", "la_chunked", "la_decode_step",
-             "decayed_recurrent", "decayed_parallel"]
+             "decayed_recurrent", "decayed_parallel", "gated_recurrent", "gated_parallel", "gated_decode_step"]
     gnames = ["gdn_recurrent", "gdn_chunked", "gdn_parallel", "gdn_decode_step"]
     return types.SimpleNamespace(**{n: la_src[n] for n in names}, **{n: gd_src[n] for n in gnames})
 
@@ -322,6 +367,13 @@ LA_MUTATIONS = [
     ("S = S + V[a:b].T @ fk", "S = S + fk.T @ V[a:b]"),
     ("np.maximum(i - j, 0)", "np.maximum(j - i, 0)"),
     ("S = gamma * S + np.outer(V[t], K[t])", "S = gamma * S + np.outer(K[t], V[t])"),
+    ("S = alpha[t] * S + np.outer(V[t], K[t])", "S = S + np.outer(V[t], K[t])"),
+    ("S = alpha[t] * S + np.outer(V[t], K[t])", "S = alpha[t] * S + np.outer(V[t], Q[t])"),
+    ("D[i, j] = np.prod(alpha[j + 1:i + 1])", "D[i, j] = np.prod(alpha[j:i + 1])"),
+    ("carry = np.array([np.prod(alpha[:i + 1]) for i in range(T)])",
+     "carry = np.array([np.prod(alpha[:i]) for i in range(T)])"),
+    ("O = O + carry[:, None] * (Q @ np.asarray(S0, dtype=np.float64).T)",
+     "O = O + carry[:, None] * (Q @ np.asarray(S0, dtype=np.float64))"),
 ]
 
 GD_MUTATIONS = [
@@ -378,9 +430,12 @@ def test_batched_steps_equal_single_head_steps():
     S, z = rng.normal(size=(n, dv, dk)), np.abs(rng.normal(size=(n, dk))) + 1
     o, S1 = batched.gdn_step_heads(q, k, v, a, b, S)
     o2, S2, z2 = batched.la_step_heads(q, k, v, S, z)
+    o3, S3 = batched.gla_step_heads(q, k, v, a, S)
     for i in range(n):
         oi, Si = oracle.gdn_decode_step(q[i], k[i], v[i], a[i], b[i], S[i])
         assert np.abs(oi - o[i]).max() < 1e-13 and np.abs(Si - S1[i]).max() < 1e-13
         oi, Si, zi = oracle.la_decode_step(q[i], k[i], v[i], S[i], z[i])
         assert np.abs(oi - o2[i]).max() < 1e-13 and np.abs(Si - S2[i]).max() < 1e-13
         assert np.abs(zi - z2[i]).max() < 1e-13
+        oi, Si = oracle.gated_decode_step(q[i], k[i], v[i], a[i], S[i])
+        assert np.abs(oi - o3[i]).max() < 1e-13 and np.abs(Si - S3[i]).max() < 1e-13
