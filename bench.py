@@ -31,6 +31,7 @@ BF16_PEAK_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 PREFILL = "gdn_bf16_2x16x8192"
 DECODE = "gdn_decode_256x32"
 LA_PREFILL = "la_bf16_4x16x4096"
+GLA_PREFILL = "gla_bf16_2x16x8192"
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
 # d = d_k = d_v: bytes = q, k, v, o in bf16 + alpha, beta in fp32; flops as
@@ -190,6 +191,28 @@ def main():
     la_gbps = la_bytes / (la_ms * 1e-3) / 1e9
     del la_sets
 
+    # --------------------------------- scalar-gated linear-attention prefill
+    wg = synth.WORKLOADS[GLA_PREFILL]
+    gq, gk, gv, ga, _ = synth.gdn_batch(wg["seed"], wg["B"], wg["H"], wg["T"], wg["dk"], wg["dv"], "bf16")
+    gla_sets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (gq, gk, gv)) +
+                (torch.from_numpy(ga).to(dev),) for _ in range(3)]
+    del gq, gk, gv, ga
+    gla_out = torch.empty((wg["B"], wg["H"], wg["T"], wg["dv"]), dtype=torch.bfloat16, device=dev)
+    gla_S = torch.empty((wg["B"], wg["H"], wg["dv"], wg["dk"]), dtype=torch.float32, device=dev)
+    for i in range(2):
+        gd.gla_prefill(*gla_sets[i % 3], form="chunked", chunk=wg["chunk"], out=gla_out, S_out=gla_S)
+    torch.cuda.synchronize()
+    g_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    g_ev[0].record()
+    for i in range(args.la_steps):
+        gd.gla_prefill(*gla_sets[i % 3], form="chunked", chunk=wg["chunk"], out=gla_out, S_out=gla_S)
+        g_ev[i + 1].record()
+    torch.cuda.synchronize()
+    gla_ms = float(np.mean([g_ev[i].elapsed_time(g_ev[i + 1]) for i in range(args.la_steps)]))
+    gla_bytes = wg["B"] * wg["H"] * wg["T"] * (4 * wg["dk"] * 2 + 4)   # q, k, v, o bf16 + alpha fp32
+    gla_gbps = gla_bytes / (gla_ms * 1e-3) / 1e9
+    del gla_sets
+
     # ------------------------------------------------------------- decode
     wd = synth.WORKLOADS[DECODE]
     N, Hd, dd, steps = wd["N"], wd["H"], wd["dk"], args.decode_steps
@@ -264,6 +287,13 @@ def main():
                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": la_gbps / HBM_PEAK_GBPS,
                                     "bytes_per_launch": la_bytes, "avg_launch_ms": la_ms,
                                     "achieved_TFLOPs": la_flops / (la_ms * 1e-3) / 1e12}},
+        "gla_prefill": {"workload": "scalar-gated linear attention prefill B=2 H=16 T=8192 d=128 chunk=64, bf16 "
+                                    "I/O, fp32 state", "calls": args.la_steps, "ms_per_call": gla_ms,
+                        "tokens_per_s": wg["B"] * wg["T"] / (gla_ms * 1e-3),
+                        "roofline": {"kernel": "la_chunked_mfma_kernel (gated)", "bound": "hbm",
+                                     "achieved": gla_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": gla_gbps / HBM_PEAK_GBPS, "bytes_per_launch": gla_bytes,
+                                     "avg_launch_ms": gla_ms}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

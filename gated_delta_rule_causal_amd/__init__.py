@@ -18,6 +18,7 @@ import os
 __all__ = [
     "lin_attn_prefill",
     "gdn_prefill",
+    "gla_prefill",
     "gdn_prefill_prep",
     "gdn_prefill_scan",
     "lin_attn_decode_step",
@@ -36,8 +37,8 @@ _LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 LA_F32, LA_BF16 = 0, 1
 FORMS = {"chunked": 0, "recurrent": 1, "parallel": 2}
-KINDS = {"normalized": 0, "gated_delta": 1}
-FNS = {"lin_attn_prefill": 0, "gdn_prefill": 1, "decode_step": 2}
+KINDS = {"normalized": 0, "gated_delta": 1, "gated": 2}
+FNS = {"lin_attn_prefill": 0, "gdn_prefill": 1, "decode_step": 2, "gla_prefill": 3}
 
 _lib = None
 
@@ -66,6 +67,8 @@ def _load():
     lib.lin_attn_prefill.restype = I
     lib.gdn_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, Z, P]
     lib.gdn_prefill.restype = I
+    lib.gla_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, P, Z, P]
+    lib.gla_prefill.restype = I
     lib.gdn_prefill_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P, Z, P]
     lib.gdn_prefill_prep.restype = I
     lib.gdn_prefill_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, Z, P]
@@ -208,6 +211,32 @@ def gdn_prefill(q, k, v, alpha, beta, S0=None, form="chunked", chunk=64, out=Non
                              _stream_ptr(stream, q.device))
     if st != 0:
         raise LinAttnError(st, "gdn_prefill")
+    return out, S_out
+
+
+def gla_prefill(q, k, v, alpha, S0=None, form="chunked", chunk=64, out=None, S_out=None, want_state=True,
+                workspace=None, stream=None):
+    """Scalar-gated unnormalised linear attention over T tokens; returns (o, S_out)."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(alpha, "alpha", torch.float32, (B, H, T))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (B, H, T, dv))
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(S_out, "S_out", torch.float32, (B, H, dv, dk))
+    ws, ws_bytes = _workspace("gla_prefill", dt, B, H, T, dk, dv, form, chunk, workspace, q.device)
+    st = _load().gla_prefill(dt, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S0), _ptr(out),
+                             _ptr(S_out), FORMS[form], chunk, _ptr(ws), ws_bytes, _stream_ptr(stream, q.device))
+    if st != 0:
+        raise LinAttnError(st, "gla_prefill")
     return out, S_out
 
 

@@ -116,6 +116,10 @@ size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv
             if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
             if (form == LA_FORM_CHUNKED && gdn_chunked_path(dtype, dk, dv, chunk) < 0) return bad;
             return gdn_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
+        case LA_FN_GLA_PREFILL:
+            if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
+            if (form == LA_FORM_CHUNKED && !la::la_mfma_supported(dtype, dk, dv, chunk)) return bad;
+            return form == LA_FORM_CHUNKED ? la::la_mfma_workspace_bytes(B, H, T, dk, dv, chunk) : 0;
         default:
             return bad;
     }
@@ -239,6 +243,51 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
                                                    o, S_out, s));
 }
 
+la_status gla_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* S0, void* o, float* S_out, int form,
+                      int chunk, void* workspace, size_t ws_bytes, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return LA_ERR_ARG;
+    if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (form == LA_FORM_CHUNKED && !valid_chunk(chunk)) return LA_ERR_SHAPE;
+    const size_t heads = static_cast<size_t>(B) * H;
+    if (heads == 0) return LA_OK;
+    const size_t es = io_size(dtype);
+    const size_t nqk = heads * T * dk * es, nv = heads * T * dv * es, ng = heads * T * sizeof(float);
+    const size_t nS = heads * dv * dk * sizeof(float);
+    if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr || alpha == nullptr))
+        return LA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(alpha),
+                          static_cast<const void*>(S0), static_cast<const void*>(S_out),
+                          static_cast<const void*>(workspace)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {{q, nqk}, {k, nqk}, {v, nv}, {alpha, ng}, {S0, nS}};
+    const Span outs[] = {{o, T > 0 ? nv : 0}, {S_out, nS}};
+    for (const Span& a : outs)
+        for (const Span& b : in) {
+            if (a.p == S_out && b.p == S0 && S_out == S0) continue;
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        }
+    if (overlaps(outs[0], outs[1])) return LA_ERR_ARG;
+    if (form == LA_FORM_CHUNKED && !la::la_mfma_supported(dtype, dk, dv, chunk)) return LA_ERR_UNSUPPORTED;
+    const size_t need = form == LA_FORM_CHUNKED ? la::la_mfma_workspace_bytes(B, H, T, dk, dv, chunk) : 0;
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
+    if (need > 0) {
+        const Span w{workspace, need};
+        for (const Span& b : in)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+        for (const Span& b : outs)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) return copy_state(S0, S_out, heads * dv * dk, s);
+    if (form == LA_FORM_RECURRENT)
+        return from_hip(la::launch_recurrent(la::kGated, dtype, static_cast<int>(heads), T, dk, dv, q, k, v, alpha,
+                                             nullptr, S0, S_out, nullptr, nullptr, o, s));
+    return from_hip(la::launch_gla_mfma(B, H, T, q, k, v, alpha, S0, o, S_out, workspace, s));
+}
+
 namespace {
 
 // Shared checks of the two halves of the chunked matrix-core gated-delta path.
@@ -309,7 +358,7 @@ la_status gdn_prefill_scan(int dtype, int B, int H, int T, int dk, int dv, const
 la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv, const void* q,
                                const void* k, const void* v, const float* alpha, const float* beta,
                                float* S, float* z, void* o, void* stream) {
-    if (kind != LA_KIND_NORMALIZED && kind != LA_KIND_GATED_DELTA) return LA_ERR_ARG;
+    if (kind != LA_KIND_NORMALIZED && kind != LA_KIND_GATED_DELTA && kind != LA_KIND_GATED) return LA_ERR_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
     if (!sizes_ok(N, H, 1) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
     const size_t heads = static_cast<size_t>(N) * H;
@@ -318,6 +367,9 @@ la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv
     if (kind == LA_KIND_GATED_DELTA) {
         if (alpha == nullptr || beta == nullptr) return LA_ERR_NULL;
         if (z != nullptr) return LA_ERR_ARG;
+    } else if (kind == LA_KIND_GATED) {
+        if (alpha == nullptr) return LA_ERR_NULL;
+        if (beta != nullptr || z != nullptr) return LA_ERR_ARG;
     } else {
         if (z == nullptr) return LA_ERR_NULL;
         if (alpha != nullptr || beta != nullptr) return LA_ERR_ARG;
@@ -335,7 +387,7 @@ la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv
             if (overlaps(a, b)) return LA_ERR_ARG;
     if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return LA_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int k_kind = kind == LA_KIND_GATED_DELTA ? la::kGatedDelta : la::kNormalized;
+    const int k_kind = kind == LA_KIND_GATED_DELTA ? la::kGatedDelta : kind == LA_KIND_GATED ? la::kGated : la::kNormalized;
     return from_hip(la::launch_recurrent(k_kind, dtype, static_cast<int>(heads), 1, dk, dv, q, k, v, alpha,
                                          beta, S, S, z, z, o, s));
 }

@@ -9,12 +9,13 @@
 
 namespace la {
 
-enum Kind { kNormalized = 0, kGatedDelta = 1 };
+enum Kind { kNormalized = 0, kGatedDelta = 1, kGated = 2 };
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
 // ---- token-by-token recurrence, one block per head (recurrent.hip) --------
 // heads = B*H (or N*H for a decode step); T >= 1.  q,k [heads,T,dk];
-// v,o [heads,T,dv]; alpha,beta [heads,T] (gated delta only); S0/S_out
+// v,o [heads,T,dv]; alpha [heads,T] (gated kinds), beta [heads,T] (gated
+// delta only); S0/S_out
 // [heads,dv,dk] (may alias); z0/z_out [heads,dk] (normalized only, may alias).
 hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int dv,
                             const void* q, const void* k, const void* v,
@@ -63,5 +64,9 @@ size_t la_mfma_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
                           const float* S0, const float* z0, void* o, float* S_out, float* z_out,
                           void* workspace, hipStream_t stream);
+// Scalar-gated (unnormalised) linear attention, same kernels and workspace
+// as the normalised path (la_mfma_supported / la_mfma_workspace_bytes).
+hipError_t launch_gla_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
+                           const float* S0, void* o, float* S_out, void* workspace, hipStream_t stream);
 
 }  // namespace la

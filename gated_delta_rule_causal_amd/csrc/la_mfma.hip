@@ -27,6 +27,16 @@
 // q/k/v are prefetched into registers while the current block computes.
 // z lives in LDS and is only written back by this workgroup, so an in-place
 // update of z is race-free.
+//
+// GATED selects the scalar-gated, unnormalised variant of the same page
+// (section "Memory must forget: decay and gates": the decay equation with an
+// input-dependent gate alpha_t): S_t = alpha_t S_{t-1} + v_t k_t^T,
+// o_t = S_t q_t, no feature map and no normaliser.  With g the chunk-local
+// cumsum of log alpha (a DPP scan per wave), a chunk is
+//     A = tril(Q K^T) * Gamma,  Gamma_ij = e^{g_i - g_j}
+//     O = diag(e^g) Q S^T + A V,   S <- e^{g_c} S + V^T diag(e^{g_c - g}) K
+// and a segment's contribution is (decay m = e^{sum of log alpha}, dS), with
+// entering states P_{s+1} = m_s P_s + dS_s.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -57,18 +67,37 @@ __device__ __forceinline__ int perm_row(int t, int rr) {
 
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// x + (x of the lane the DPP control selects, 0 where there is none).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xf, true));
+}
+
+// Inclusive prefix sum over the 64 lanes without LDS: shifts inside 16-lane
+// rows, then lane 15 into rows 1 and 3 and lane 31 into rows 2 and 3.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x = dpp_add<0x111, 0xf>(x);
+    x = dpp_add<0x112, 0xf>(x);
+    x = dpp_add<0x114, 0xf>(x);
+    x = dpp_add<0x118, 0xf>(x);
+    x = dpp_add<0x142, 0xa>(x);
+    return dpp_add<0x143, 0xc>(x);
+}
+
 // OUT = false: segment contributions only (no q, no outputs), from a zero state.
-template <bool OUT>
+// GATED: the scalar-gated variant (alpha used, z0/z_out unused).
+template <bool GATED, bool OUT>
 __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
     int BH, int T, int NC, int G, int SEGC, const u16* __restrict__ q, const u16* __restrict__ k,
-    const u16* __restrict__ v, const float* S0, const float* z0, float* ws, u16* __restrict__ o, float* S_out,
-    float* z_out) {
+    const u16* __restrict__ v, const float* __restrict__ alpha, const float* S0, const float* z0, float* ws,
+    u16* __restrict__ o, float* S_out, float* z_out) {
     __shared__ __attribute__((aligned(16))) u16 fQ[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 fK[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 fKt[D][LDT];
     __shared__ __attribute__((aligned(16))) u16 Vt[D][LDT];
     __shared__ __attribute__((aligned(16))) u16 As[C][LDT];
     __shared__ float zs[D], dens[C], rsum[C];
+    __shared__ float gs[C], egs[C];   // GATED: chunk-local g and e^g
 
     const int nseg = OUT ? G : G - 1;
     const int bh = blockIdx.x / nseg;
@@ -80,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
     const float* Sin = !OUT ? nullptr
                        : G == 1 ? (S0 ? S0 + static_cast<size_t>(bh) * kMat : nullptr)
                                 : ws + ws_P(bh, G, seg);
-    const float* zin = !OUT ? nullptr
+    const float* zin = (!OUT || GATED) ? nullptr
                        : G == 1 ? (z0 ? z0 + static_cast<size_t>(bh) * D : nullptr)
                                 : ws + ws_zP(bh, G, seg);
     const int tid = threadIdx.x;
@@ -113,6 +142,8 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
 
     // ---- raw chunk prefetch: item e = tid + kThreads * it -> row = e % C, c8 = 8 (e / C)
     uint4 rq[kItems], rk[kItems], rv[kItems];
+    float ra = 1.f;   // GATED: alpha of token `lane` of the chunk (1 past the end)
+    float decay = 1.f;  // GATED: product of the gates seen so far in this segment
     const size_t head = static_cast<size_t>(bh) * T * D;
     auto fetch = [&](int n) {
         const int t0 = n * C;
@@ -129,6 +160,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 rv[it] = *reinterpret_cast<const uint4*>(v + gi);
             }
         }
+        if (GATED) ra = lane < len ? alpha[static_cast<size_t>(bh) * T + t0 + lane] : 1.f;
     };
     fetch(n0);
 
@@ -136,8 +168,22 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
         const int t0 = n * C;
         const int len = min(C, T - t0);
         __syncthreads();  // the previous block's LDS tiles are no longer read
+        // GATED: g for token `lane` (every item of this thread has row = lane),
+        // e^{g_c - g} scales K^T for the state update
+        float ek = 1.f, egc = 1.f;
+        if constexpr (GATED) {
+            const float gx = wave_prefix_sum(__logf(ra));
+            const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gx), C - 1));
+            ek = __expf(gl - gx);
+            egc = __expf(gl);
+            if (w == 0) {
+                gs[lane] = gx;
+                egs[lane] = __expf(gx);
+            }
+        }
         // ---- stage phi(Q), phi(K), phi(K)^T, V^T (padded rows stay zero: phi is
-        //      applied only to real tokens, so they add nothing to A, S or z)
+        //      applied only to real tokens, so they add nothing to A, S or z);
+        //      GATED: Q, K, (e^{g_c - g} K)^T, V^T
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int e = tid + kThreads * it;
@@ -151,8 +197,13 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             for (int j = 0; j < 8; ++j) {
                 const uint32_t bq = (j & 1) ? (wq[j >> 1] & 0xffff0000u) : (wq[j >> 1] << 16);
                 const uint32_t bk = (j & 1) ? (wk[j >> 1] & 0xffff0000u) : (wk[j >> 1] << 16);
-                xq[j] = real ? phi(__uint_as_float(bq)) : 0.f;
-                xk[j] = real ? phi(__uint_as_float(bk)) : 0.f;
+                if (GATED) {
+                    xq[j] = __uint_as_float(bq);
+                    xk[j] = __uint_as_float(bk);
+                } else {
+                    xq[j] = real ? phi(__uint_as_float(bq)) : 0.f;
+                    xk[j] = real ? phi(__uint_as_float(bk)) : 0.f;
+                }
             }
             const bf16x8 pq = pack8(xq[0], xq[1], xq[2], xq[3], xq[4], xq[5], xq[6], xq[7]);
             const bf16x8 pk = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
@@ -162,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             for (int j = 0; j < 8; ++j) {
                 // bits from the fp32 value, not from an element of the packed
                 // __bf16 vector (extracting those for a bit cast miscompiles)
-                fKt[c8 + j][row] = f32_to_bf16_bits(xk[j]);
+                fKt[c8 + j][row] = f32_to_bf16_bits(GATED ? xk[j] * ek : xk[j]);
                 Vt[c8 + j][row] = static_cast<u16>((j & 1) ? (wv[j >> 1] >> 16) : (wv[j >> 1] & 0xffffu));
             }
         }
@@ -182,7 +233,9 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int row = 16 * w + 4 * g + i, col = 16 * ct + r;
-                        const float a = col <= row ? acc[i] : 0.f;
+                        const float a = col > row ? 0.f
+                                        : GATED ? acc[i] * __expf(fminf(gs[row] - gs[col], 0.f))
+                                                : acc[i];
                         As[row][col] = f32_to_bf16_bits(a);
                         rs[i] += a;
                     }
@@ -191,13 +244,16 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                     for (int i = 0; i < 4; ++i) As[16 * w + 4 * g + i][16 * ct + r] = 0;
                 }
             }
+            if (!GATED) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float t = group_sum<16>(rs[i]);
-                if (r == 0) rsum[16 * w + 4 * g + i] = t;
+                for (int i = 0; i < 4; ++i) {
+                    const float t = group_sum<16>(rs[i]);
+                    if (r == 0) rsum[16 * w + 4 * g + i] = t;
+                }
             }
         }
-        if constexpr (OUT) {
+        if constexpr (OUT && GATED) __syncthreads();   // A complete
+        if constexpr (OUT && !GATED) {
         __syncthreads();
         // ---- den = rowsum(A) + phi(Q) z   (z of the previous blocks)
         {
@@ -211,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
         __syncthreads();
         }
         // ---- z += colsum phi(K)  (read again only after the next loop-top barrier)
-        if (tid < D) {
+        if (!GATED && tid < D) {
             float acc = zs[tid];
             for (int c = 0; c < C; ++c) acc += bf16_bits_to_f32(fK[c][tid]);
             zs[tid] = acc;
@@ -235,6 +291,14 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 acc[0] = mfma16x16x32(a, Pb[0][s], acc[0]);
                 acc[1] = mfma16x16x32(a, Pb[1][s], acc[1]);
             }
+            if (GATED) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float eg = egs[16 * m + 4 * g + i];
+                    acc[0][i] *= eg;
+                    acc[1][i] *= eg;
+                }
+            }
 #pragma unroll
             for (int s2 = 0; s2 <= (m >> 1); ++s2) {
                 const bf16x8 a = lds8(&As[16 * m + r][32 * s2 + 8 * g]);
@@ -245,11 +309,19 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * m + 4 * g + i;
                 if (row < len) {
-                    const float rden = 1.f / dens[row];
+                    const float rden = GATED ? 1.f : 1.f / dens[row];
                     const size_t oi = head + static_cast<size_t>(t0 + row) * D + 32 * w + r;
                     o[oi] = f32_to_bf16_bits(acc[0][i] * rden);
                     o[oi + 16] = f32_to_bf16_bits(acc[1][i] * rden);
                 }
+            }
+        }
+        if (GATED) {
+            decay *= egc;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                P[0][t] *= egc;
+                P[1][t] *= egc;
             }
         }
 #pragma unroll
@@ -283,11 +355,18 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
         }
     }
     __syncthreads();
-    if (zdst && tid < D) zdst[tid] = zs[tid];
+    if (GATED) {
+        // the segment's total decay in slot 0 of the dz record (z is unused)
+        if (!OUT && tid == 0) zdst[0] = decay;
+    } else if (zdst && tid < D) {
+        zdst[tid] = zs[tid];
+    }
 }
 
 // Entering states of every segment: P_0 = S0 (or 0), P_{s+1} = P_s + dS_s, and
-// the same for z.  16 workgroups per head, 4 consecutive floats per thread.
+// the same for z; GATED: P_{s+1} = m_s P_s + dS_s with the segment decay m_s.
+// 16 workgroups per head, 4 consecutive floats per thread.
+template <bool GATED>
 __global__ __launch_bounds__(kThreads) void la_combine_kernel(int BH, int G, const float* S0, const float* z0,
                                                               float* ws) {
     const int bh = blockIdx.x >> 4;
@@ -300,10 +379,12 @@ __global__ __launch_bounds__(kThreads) void la_combine_kernel(int BH, int G, con
         *reinterpret_cast<float4*>(ws + ws_P(bh, G, s) + e) = run;
         if (s + 1 < G) {
             const float4 d = *reinterpret_cast<const float4*>(ws + ws_dS(bh, G, s) + e);
-            run.x += d.x; run.y += d.y; run.z += d.z; run.w += d.w;
+            const float m = GATED ? ws[ws_dz(bh, G, s)] : 1.f;
+            run.x = fmaf(m, run.x, d.x); run.y = fmaf(m, run.y, d.y);
+            run.z = fmaf(m, run.z, d.z); run.w = fmaf(m, run.w, d.w);
         }
     }
-    if (part == 0 && threadIdx.x < D) {
+    if (!GATED && part == 0 && threadIdx.x < D) {
         float zr = z0 ? z0[static_cast<size_t>(bh) * D + threadIdx.x] : 0.f;
         for (int s = 0; s < G; ++s) {
             ws[ws_zP(bh, G, s) + threadIdx.x] = zr;
@@ -341,26 +422,44 @@ size_t la_mfma_workspace_bytes(int B, int H, int T, int, int, int) {
     return p.G == 1 ? 0 : static_cast<size_t>(BH) * p.G * kRec * sizeof(float);
 }
 
-hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* S0,
-                          const float* z0, void* o, float* S_out, float* z_out, void* workspace, hipStream_t stream) {
+namespace {
+
+template <bool GATED>
+hipError_t launch_segmented(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
+                            const float* S0, const float* z0, void* o, float* S_out, float* z_out, void* workspace,
+                            hipStream_t stream) {
     const int BH = B * H;
     if (BH <= 0 || T <= 0) return hipSuccess;
     const Plan p = make_plan(BH, T);
     float* ws = static_cast<float*>(workspace);
     const u16 *q16 = static_cast<const u16*>(q), *k16 = static_cast<const u16*>(k), *v16 = static_cast<const u16*>(v);
     if (p.G > 1) {
-        hipLaunchKernelGGL(la_chunked_mfma_kernel<false>, dim3(static_cast<unsigned>(BH) * (p.G - 1)), dim3(kThreads),
-                           0, stream, BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, S0, z0, ws, nullptr, nullptr, nullptr);
+        hipLaunchKernelGGL((la_chunked_mfma_kernel<GATED, false>), dim3(static_cast<unsigned>(BH) * (p.G - 1)),
+                           dim3(kThreads), 0, stream, BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, alpha, S0, z0, ws,
+                           nullptr, nullptr, nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(la_combine_kernel, dim3(static_cast<unsigned>(BH) * 16), dim3(kThreads), 0, stream, BH,
-                           p.G, S0, z0, ws);
+        hipLaunchKernelGGL(la_combine_kernel<GATED>, dim3(static_cast<unsigned>(BH) * 16), dim3(kThreads), 0, stream,
+                           BH, p.G, S0, z0, ws);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(la_chunked_mfma_kernel<true>, dim3(static_cast<unsigned>(BH) * p.G), dim3(kThreads), 0, stream,
-                       BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, S0, z0, ws, static_cast<u16*>(o), S_out, z_out);
+    hipLaunchKernelGGL((la_chunked_mfma_kernel<GATED, true>), dim3(static_cast<unsigned>(BH) * p.G), dim3(kThreads),
+                       0, stream, BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, alpha, S0, z0, ws, static_cast<u16*>(o),
+                       S_out, z_out);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* S0,
+                          const float* z0, void* o, float* S_out, float* z_out, void* workspace, hipStream_t stream) {
+    return launch_segmented<false>(B, H, T, q, k, v, nullptr, S0, z0, o, S_out, z_out, workspace, stream);
+}
+
+hipError_t launch_gla_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
+                           const float* S0, void* o, float* S_out, void* workspace, hipStream_t stream) {
+    return launch_segmented<true>(B, H, T, q, k, v, alpha, S0, nullptr, o, S_out, nullptr, workspace, stream);
 }
 
 }  // namespace la

@@ -8,6 +8,10 @@
 //       u = s_i.k,  p = s_i.q,  c = beta (v_i - alpha u),
 //       s_i <- alpha s_i + c k,   o_i = alpha p + c (k.q)
 //     so each row is read once and written once per token.
+//   * kGated - section "Memory must forget: decay and gates", the decay
+//     equation with the input-dependent gate alpha_t in place of gamma:
+//       S_t = alpha_t S_{t-1} + v_t k_t^T,  o_t = S_t q_t, per row
+//       p = s_i.q,  s_i <- alpha s_i + v_i k,  o_i = alpha p + v_i (k.q)
 //   * kNormalized - section "Three forms of one computation", recurrent form:
 //       s_i <- s_i + v_i phi(k),  z <- z + phi(k),  o_i = s_i.phi(q) / z.phi(q)
 // With T = 1 it is the decode step (the state streams from HBM and back,
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     typename IO::T* __restrict__ o) {
     constexpr int LPR = RowSlice<DK>::LPR;
     constexpr int RG = RowSlice<DK>::RG;
-    static_assert(KIND == kGatedDelta || SPLIT == 1, "z is shared by all rows of a head");
+    static_assert(KIND != kNormalized || SPLIT == 1, "z is shared by all rows of a head");
     const int head = blockIdx.x / SPLIT;
     const int li = threadIdx.x % LPR;
     const int rg = threadIdx.x / LPR + (blockIdx.x % SPLIT) * RG * R;  // first row of this lane group
@@ -119,10 +123,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
             const int r = rg + RG * j;
             vn[j] = r < DV ? IO::load(v, tv + r) : 0.f;
         }
-        if constexpr (KIND == kGatedDelta) {
-            an = alpha[static_cast<size_t>(head) * T + t];
-            bn = beta[static_cast<size_t>(head) * T + t];
-        }
+        if constexpr (KIND != kNormalized) an = alpha[static_cast<size_t>(head) * T + t];
+        if constexpr (KIND == kGatedDelta) bn = beta[static_cast<size_t>(head) * T + t];
     };
     fetch(0);
 
@@ -137,7 +139,24 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
         if (!ONE && t + 1 < T) fetch(t + 1);
         const size_t to = (static_cast<size_t>(head) * T + t) * DV;
 
-        if constexpr (KIND == kGatedDelta) {
+        if constexpr (KIND == kGated) {
+            (void)b;
+            float kq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kq = fmaf(kc[e], qc[e], kq);
+            kq = group_sum<LPR>(kq);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float p = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p = fmaf(s[j][e], qc[e], p);
+                p = group_sum<LPR>(p);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[j][e] = fmaf(a, s[j][e], vc[j] * kc[e]);
+                const int r = rg + RG * j;
+                if (li == 0 && r < DV) IO::store(o, to + r, fmaf(a, p, vc[j] * kq));
+            }
+        } else if constexpr (KIND == kGatedDelta) {
             float kq = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) kq = fmaf(kc[e], qc[e], kq);
@@ -212,7 +231,7 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
     using E = typename IO::T;
     constexpr int RG = RowSlice<DK>::RG;
     // gated delta: two blocks per head when each still gets a whole row group
-    const int split = (KIND == kGatedDelta && dv >= 2 * RG) ? 2 : 1;
+    const int split = (KIND != kNormalized && dv >= 2 * RG) ? 2 : 1;
     const int R = (dv / split + RG - 1) / RG;
     dim3 grid(static_cast<unsigned>(heads) * split), block(kThreads);
     auto args = [&](auto kern) {
@@ -222,7 +241,7 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
         return hipGetLastError();
     };
     if (split == 2) {
-        if constexpr (KIND == kGatedDelta) {
+        if constexpr (KIND != kNormalized) {
             switch (R) {
                 case 1: return args(recurrent_kernel<KIND, IO, DK, 1, 2, ONE>);
                 case 2: return args(recurrent_kernel<KIND, IO, DK, 2, 2, ONE>);
@@ -270,6 +289,11 @@ hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int d
                             const float* S0, float* S_out, const float* z0, float* z_out, void* o,
                             hipStream_t stream) {
     if (heads <= 0 || T <= 0) return hipSuccess;
+    if (kind == kGated) {
+        return dtype == kBF16
+                   ? launch_io<kGated, IoBF16>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr, nullptr, o, stream)
+                   : launch_io<kGated, IoF32>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr, nullptr, o, stream);
+    }
     if (kind == kGatedDelta) {
         return dtype == kBF16
                    ? launch_io<kGatedDelta, IoBF16>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream)

@@ -59,8 +59,8 @@ enum {
 
 enum { LA_F32 = 0, LA_BF16 = 1 };
 enum { LA_FORM_CHUNKED = 0, LA_FORM_RECURRENT = 1, LA_FORM_PARALLEL = 2 };
-enum { LA_KIND_NORMALIZED = 0, LA_KIND_GATED_DELTA = 1 };
-enum { LA_FN_LIN_ATTN_PREFILL = 0, LA_FN_GDN_PREFILL = 1, LA_FN_DECODE_STEP = 2 };
+enum { LA_KIND_NORMALIZED = 0, LA_KIND_GATED_DELTA = 1, LA_KIND_GATED = 2 };
+enum { LA_FN_LIN_ATTN_PREFILL = 0, LA_FN_GDN_PREFILL = 1, LA_FN_DECODE_STEP = 2, LA_FN_GLA_PREFILL = 3 };
 
 /*
  * lin_attn_prefill - normalised causal linear attention over T tokens.
@@ -91,6 +91,30 @@ la_status lin_attn_prefill(int dtype, int B, int H, int T, int dk, int dv,
                            void* o, float* S_out, float* z_out,
                            int form, int chunk,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gla_prefill - scalar-gated (unnormalised) linear attention over T tokens.
+ *
+ * Section "Memory must forget: decay and gates": the decay equation
+ * S_t = gamma S_{t-1} + v_t k_t^T with the constant gamma replaced by an
+ * input-dependent gate alpha_t, no feature map and no normaliser:
+ *     S_t = alpha_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t   (token t included)
+ * alpha [B,H,T] float32 holds gate values (a constant alpha is the decay
+ * equation itself).  S_0 = S0 (zeros when NULL).  form:
+ *   LA_FORM_RECURRENT - token by token, any supported dtype and sizes;
+ *   LA_FORM_CHUNKED   - block form, bf16 with dk = dv = 128 and chunk 64
+ *                       (other shapes: LA_ERR_UNSUPPORTED).
+ * Outputs o [B,H,T,dv] and, when not NULL, S_out [B,H,dv,dk] (may be the
+ * same pointer as S0).  workspace/ws_bytes: at least
+ * la_workspace_bytes(LA_FN_GLA_PREFILL, ...) bytes, not overlapping any
+ * tensor argument.
+ */
+la_status gla_prefill(int dtype, int B, int H, int T, int dk, int dv,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* S0,
+                      void* o, float* S_out,
+                      int form, int chunk,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * gdn_prefill - the gated delta rule (Gated DeltaNet) over T tokens.
@@ -154,6 +178,10 @@ la_status gdn_prefill_scan(int dtype, int B, int H, int T, int dk, int dv,
  *   LA_KIND_GATED_DELTA (section "Delta rule and Gated DeltaNet"):
  *       S <- alpha S (I - beta k k^T) + beta v k^T,   o = S q
  *     alpha, beta [N,H] float32 are required; z must be NULL.
+ *   LA_KIND_GATED (section "Memory must forget: decay and gates", the decay
+ *   equation with the input-dependent gate alpha_t):
+ *       S <- alpha S + v k^T,   o = S q
+ *     alpha [N,H] float32 is required; beta and z must be NULL.
  *   LA_KIND_NORMALIZED (section "Three forms of one computation", recurrent
  *   form, applied to one token):
  *       S <- S + v phi(k)^T,  z <- z + phi(k),  o = S phi(q) / (z . phi(q))

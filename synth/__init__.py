@@ -36,6 +36,10 @@ WORKLOADS = {
                               dtype="bf16", steps=1000, state_std=0.02),
     "gdn_bf16_1x16x262144": dict(seed=1005, kind="gdn", B=1, H=16, T=262144, dk=128, dv=128,
                                  dtype="bf16", chunk=64),
+    # scalar-gated linear attention (no delta term): the gated-delta inputs
+    # without beta, at the gated-delta prefill shape
+    "gla_bf16_2x16x8192": dict(seed=1006, kind="gla", B=2, H=16, T=8192, dk=128, dv=128,
+                               dtype="bf16", chunk=64),
 }
 
 

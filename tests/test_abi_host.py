@@ -47,7 +47,7 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
+    assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gla_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
                             "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
 
 
@@ -211,3 +211,31 @@ def test_segmented_linear_attention_workspace(lib):
     assert la(ws=4) == LA_ERR_ARG            # workspace on top of o
     # one segment (short sequence, many heads): no workspace
     assert lib.la_workspace_bytes(0, BF16, 64, 8, 64, 128, 128, CHUNKED, 64) == 0
+
+
+def test_gla_validation(lib):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    GLA = 3
+
+    def gla(dtype=BF16, T=1000, dk=128, dv=128, q=1, k=2, v=3, a=5, S0=None, o=4, S_out=None, form=CHUNKED,
+            chunk=64, ws=9, ws_bytes=1 << 40):
+        return lib.gla_prefill(dtype, 1, 2, T, dk, dv, f(q), f(k), f(v), f(a), f(S0), f(o), f(S_out), form, chunk,
+                               f(ws), ws_bytes, None)
+
+    assert gla(a=None) == LA_ERR_NULL
+    assert gla(form=PARALLEL) == LA_ERR_ARG
+    assert gla(dtype=F32) == LA_ERR_UNSUPPORTED            # chunked: bf16, d = 128, chunk 64 only
+    assert gla(ws=None) == LA_ERR_WORKSPACE
+    assert gla(ws=5) == LA_ERR_ARG                         # workspace on top of alpha
+    assert gla(o=5) == LA_ERR_ARG                          # output on top of alpha
+    assert gla(S0=7, S_out=ctypes.c_void_p(BASE + 7 * GiB + 32)) == LA_ERR_ARG
+    n = lib.la_workspace_bytes(GLA, BF16, 1, 2, 1000, 128, 128, CHUNKED, 64)
+    assert n > 0 and gla(ws_bytes=n - 1) == LA_ERR_WORKSPACE
+    assert lib.la_workspace_bytes(GLA, F32, 1, 2, 1000, 16, 16, RECURRENT, 0) == 0
+    assert lib.la_workspace_bytes(GLA, F32, 1, 2, 1000, 16, 16, CHUNKED, 16) == ctypes.c_size_t(-1).value
+    # decode: the gated kind needs alpha, no beta, no z
+    dec = lambda a=5, b=None, z=None: lib.lin_attn_decode_step(2, BF16, 4, 2, 128, 128, P(1), P(2), P(3), f(a), f(b),
+                                                               P(6), f(z), P(4), None)
+    assert dec(a=None) == LA_ERR_NULL
+    assert dec(b=8) == LA_ERR_ARG
+    assert dec(z=8) == LA_ERR_ARG
