@@ -67,6 +67,16 @@ __device__ __forceinline__ int perm_row(int t, int rr) {
 
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Workgroup barrier that orders LDS accesses only: __syncthreads also waits
+// for this wave's outstanding global loads, which would stall on the next
+// block's prefetch.  Nothing here communicates through global memory inside
+// a launch.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // x + (x of the lane the DPP control selects, 0 where there is none).
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ float dpp_add(float x) {
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
         const int len = min(C, T - t0);
-        __syncthreads();  // the previous block's LDS tiles are no longer read
+        lds_barrier();  // the previous block's LDS tiles are no longer read
         // GATED: g for token `lane` (every item of this thread has row = lane),
         // e^{g_c - g} scales K^T for the state update
         float ek = 1.f, egc = 1.f;
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             }
         }
         if (n + 1 < n1) fetch(n + 1);
-        __syncthreads();
+        lds_barrier();
 
         // ---- A = tril(phi(Q) phi(K)^T), row tile w, and its row sums (fp32)
         if constexpr (OUT) {
@@ -252,9 +262,9 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 }
             }
         }
-        if constexpr (OUT && GATED) __syncthreads();   // A complete
+        if constexpr (OUT && GATED) lds_barrier();   // A complete
         if constexpr (OUT && !GATED) {
-        __syncthreads();
+        lds_barrier();
         // ---- den = rowsum(A) + phi(Q) z   (z of the previous blocks)
         {
             const int row = tid >> 2, qd = (tid & 3) * 32;
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             acc = group_sum<4>(acc);
             if ((tid & 3) == 0) dens[row] = acc + rsum[row];
         }
-        __syncthreads();
+        lds_barrier();
         }
         // ---- z += colsum phi(K)  (read again only after the next loop-top barrier)
         if (!GATED && tid < D) {
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (GATED) {
         // the segment's total decay in slot 0 of the dz record (z is unused)
         if (!OUT && tid == 0) zdst[0] = decay;
