@@ -39,6 +39,7 @@ from .gated_delta import (
     gdn_bruteforce_states,
 )
 from . import batched
+from . import preops
 
 __all__ = [
     "phi",
@@ -54,4 +55,5 @@ __all__ = [
     "gdn_decode_step",
     "gdn_bruteforce_states",
     "batched",
+    "preops",
 ]

@@ -439,3 +439,80 @@ def test_batched_steps_equal_single_head_steps():
         assert np.abs(zi - z2[i]).max() < 1e-13
         oi, Si = oracle.gated_decode_step(q[i], k[i], v[i], a[i], S[i])
         assert np.abs(oi - o3[i]).max() < 1e-13 and np.abs(Si - S3[i]).max() < 1e-13
+
+
+# --------------------------------------------------------------------------
+# Pre-operations: causal depthwise convolution, L2 normalisation, sigmoid gates
+# --------------------------------------------------------------------------
+
+from oracle import preops as pre_mod
+
+
+def pin_preops(ns):
+    rng = np.random.default_rng(31)
+    T, C = 11, 7
+    x = rng.normal(size=(T, C))
+    w = rng.normal(size=(C, 4))
+    st = rng.normal(size=(3, C))
+    # taps: [0,0,0,1] is the identity, [1,0,0,0] a delay of three tokens
+    ident = np.tile([0.0, 0.0, 0.0, 1.0], (C, 1))
+    delay = np.tile([1.0, 0.0, 0.0, 0.0], (C, 1))
+    assert np.array_equal(ns.causal_conv(x, ident)[0], x)
+    y, _ = ns.causal_conv(x, delay, st)
+    assert np.array_equal(y[3:], x[:-3]) and np.array_equal(y[:3], st)
+    # against numpy's full convolution of each channel (zero history)
+    y, _ = ns.causal_conv(x, w)
+    for c in range(C):
+        assert np.abs(y[:, c] - np.convolve(x[:, c], w[c, ::-1])[:T]).max() < 1e-12
+    # a carried state equals the concatenated history; split-resume equals one call
+    y_full, s_full = ns.causal_conv(np.vstack([st, x]), w)
+    y_st, s_st = ns.causal_conv(x, w, st)
+    assert np.abs(y_full[3:] - y_st).max() < 1e-12 and np.abs(s_full - s_st).max() == 0
+    y1, s1 = ns.causal_conv(x[:4], w, st)
+    y2, s2 = ns.causal_conv(x[4:], w, s1)
+    assert np.abs(np.vstack([y1, y2]) - y_st).max() < 1e-12 and np.array_equal(s2, s_st)
+    # L2: unit rows in the same direction; zero rows stay zero
+    z = np.vstack([x, np.zeros(C)])
+    n = ns.l2_normalize(z)
+    assert np.abs(np.linalg.norm(n[:-1], axis=1) - 1).max() < 1e-14 and np.all(n[-1] == 0)
+    assert np.abs(n[:-1] * np.linalg.norm(x, axis=1, keepdims=True) - x).max() < 1e-12
+    # sigmoid: closed values and symmetry
+    p = np.array([0.1, 0.5, 0.9])
+    assert np.abs(ns.sigmoid(np.log(p / (1 - p))) - p).max() < 1e-15
+    assert np.abs(ns.sigmoid(-x) - (1 - ns.sigmoid(x))).max() < 1e-15
+    # layout of the fused call: q | k | v channel blocks, head-contiguous
+    H, dk, dv = 2, 3, 2
+    Ct = H * (2 * dk + dv)
+    xs = rng.normal(size=(T, Ct))
+    a, b = rng.normal(size=(T, H)), rng.normal(size=(T, H))
+    q, k, v, al, be, _ = ns.gdn_preprocess(xs, np.tile([0.0, 0.0, 0.0, 1.0], (Ct, 1)), a, b, H, dk, dv)
+    for h in range(H):
+        qh = xs[:, h * dk:(h + 1) * dk]
+        vh = xs[:, 2 * H * dk + h * dv:2 * H * dk + (h + 1) * dv]
+        kh = xs[:, H * dk + h * dk:H * dk + (h + 1) * dk]
+        assert np.abs(q[h] - qh / np.linalg.norm(qh, axis=1, keepdims=True)).max() < 1e-12
+        assert np.abs(k[h] - kh / np.linalg.norm(kh, axis=1, keepdims=True)).max() < 1e-12
+        assert np.array_equal(v[h], vh)
+        assert np.abs(al[h] - 1 / (1 + np.exp(-a[:, h]))).max() < 1e-15
+        assert np.abs(be[h] - 1 / (1 + np.exp(-b[:, h]))).max() < 1e-15
+
+
+PRE_MUTATIONS = [
+    ("y[t] += w[:, i] * xx[t + i]", "y[t] += w[:, 3 - i] * xx[t + i]"),
+    ("xx = np.concatenate([prev, x], axis=0)", "xx = np.concatenate([np.zeros_like(prev), x], axis=0)"),
+    ("return y, xx[-3:].copy()", "return y, xx[:3].copy()"),
+    ("n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))", "n = np.sum(x * x, axis=-1, keepdims=True)"),
+    ("return 1.0 / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(x))"),
+    ("k = y[:, H * dk:2 * H * dk].reshape(T, H, dk).transpose(1, 0, 2)",
+     "k = y[:, H * dk:2 * H * dk].reshape(T, dk, H).transpose(2, 0, 1)"),
+]
+
+
+def test_preops_pins():
+    pin_preops(pre_mod)
+
+
+@pytest.mark.parametrize("old,new", PRE_MUTATIONS, ids=[m[1][:40] for m in PRE_MUTATIONS])
+def test_planted_preops_mistake_is_caught(old, new):
+    ns = types.SimpleNamespace(**_mutant(pre_mod, old, new))
+    assert _fails_some_pin(ns, [pin_preops])
