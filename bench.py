@@ -32,6 +32,7 @@ PREFILL = "gdn_bf16_2x16x8192"
 DECODE = "gdn_decode_256x32"
 LA_PREFILL = "la_bf16_4x16x4096"
 GLA_PREFILL = "gla_bf16_2x16x8192"
+PREOPS = "preops_bf16_2x16x8192"
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
 # d = d_k = d_v: bytes = q, k, v, o in bf16 + alpha, beta in fp32; flops as
@@ -213,6 +214,34 @@ def main():
     gla_gbps = gla_bytes / (gla_ms * 1e-3) / 1e9
     del gla_sets
 
+    # --------------------------------------- pre-operations of the layer
+    wp = synth.WORKLOADS[PREOPS]
+    Bp, Tp, Hp, dkp, dvp = wp["B"], wp["T"], wp["H"], wp["dk"], wp["dv"]
+    px, pw, pa, pb = synth.preops_batch(wp["seed"], Bp, Tp, Hp, dkp, dvp, "bf16")
+    x0 = torch.from_numpy(px).to(dev).to(torch.bfloat16)
+    pre_sets = [(x0 if i == 0 else x0.clone(), torch.from_numpy(pw).to(dev), torch.from_numpy(pa).to(dev),
+                 torch.from_numpy(pb).to(dev)) for i in range(3)]
+    del px, pw, pa, pb, x0
+    pre_out = dict(q=torch.empty((Bp, Hp, Tp, dkp), dtype=torch.bfloat16, device=dev),
+                   k=torch.empty((Bp, Hp, Tp, dkp), dtype=torch.bfloat16, device=dev),
+                   v=torch.empty((Bp, Hp, Tp, dvp), dtype=torch.bfloat16, device=dev),
+                   alpha=torch.empty((Bp, Hp, Tp), dtype=torch.float32, device=dev),
+                   beta=torch.empty((Bp, Hp, Tp), dtype=torch.float32, device=dev))
+    for i in range(2):
+        gd.gdn_preprocess(*pre_sets[i % 3], Hp, dkp, dvp, want_state=False, **pre_out)
+    torch.cuda.synchronize()
+    p_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    p_ev[0].record()
+    for i in range(args.la_steps):
+        gd.gdn_preprocess(*pre_sets[i % 3], Hp, dkp, dvp, want_state=False, **pre_out)
+        p_ev[i + 1].record()
+    torch.cuda.synchronize()
+    pre_ms = float(np.mean([p_ev[i].elapsed_time(p_ev[i + 1]) for i in range(args.la_steps)]))
+    # x read + gate logits read, q, k, v written + alpha, beta written
+    pre_bytes = Bp * Hp * Tp * (2 * ((2 * dkp + dvp) * 2 + 8))
+    pre_gbps = pre_bytes / (pre_ms * 1e-3) / 1e9
+    del pre_sets, pre_out
+
     # ------------------------------------------------------------- decode
     wd = synth.WORKLOADS[DECODE]
     N, Hd, dd, steps = wd["N"], wd["H"], wd["dk"], args.decode_steps
@@ -294,6 +323,13 @@ def main():
                                      "achieved": gla_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                      "frac": gla_gbps / HBM_PEAK_GBPS, "bytes_per_launch": gla_bytes,
                                      "avg_launch_ms": gla_ms}},
+        "preprocess": {"workload": "Gated DeltaNet pre-operations (conv k=4, q/k L2 norm, sigmoid gates) B=2 "
+                                   "H=16 T=8192 d=128, bf16 I/O", "calls": args.la_steps, "ms_per_call": pre_ms,
+                       "tokens_per_s": Bp * Tp / (pre_ms * 1e-3),
+                       "roofline": {"kernel": "gdn_preprocess_kernel", "bound": "hbm", "achieved": pre_gbps,
+                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pre_gbps / HBM_PEAK_GBPS,
+                                    "traffic": measured_traffic(["gdn_preprocess_kernel"]),
+                                    "bytes_per_launch": pre_bytes, "avg_launch_ms": pre_ms}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

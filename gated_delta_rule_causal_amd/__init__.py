@@ -21,6 +21,7 @@ __all__ = [
     "gla_prefill",
     "gdn_prefill_prep",
     "gdn_prefill_scan",
+    "gdn_preprocess",
     "lin_attn_decode_step",
     "la_workspace_bytes",
     "la_status_str",
@@ -69,6 +70,8 @@ def _load():
     lib.gdn_prefill.restype = I
     lib.gla_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, P, Z, P]
     lib.gla_prefill.restype = I
+    lib.gdn_preprocess.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gdn_preprocess.restype = I
     lib.gdn_prefill_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P, Z, P]
     lib.gdn_prefill_prep.restype = I
     lib.gdn_prefill_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, Z, P]
@@ -238,6 +241,48 @@ def gla_prefill(q, k, v, alpha, S0=None, form="chunked", chunk=64, out=None, S_o
     if st != 0:
         raise LinAttnError(st, "gla_prefill")
     return out, S_out
+
+
+def gdn_preprocess(x, conv_w, a_logit, b_logit, H, dk, dv, conv_state=None, want_state=True, q=None, k=None, v=None,
+                   alpha=None, beta=None, conv_state_out=None, stream=None):
+    """Fused pre-operations of a Gated DeltaNet layer; returns
+    (q, k, v, alpha, beta, conv_state_out).
+
+    x [B,T,H*(2dk+dv)] (float32 or bfloat16, channels q | k | v); conv_w
+    [H*(2dk+dv), 4] float32; a_logit, b_logit [B,T,H] float32; conv_state
+    [B,3,H*(2dk+dv)] in x's dtype or None.  Outputs q, k [B,H,T,dk] (convolved,
+    L2-normalised), v [B,H,T,dv] (convolved), alpha, beta [B,H,T] float32
+    (sigmoids), and the next conv state when ``want_state``.
+    """
+    torch = _torch()
+    B, T, C = x.shape
+    if C != H * (2 * dk + dv):
+        raise ValueError(f"x has {C} channels, expected H*(2dk+dv) = {H * (2 * dk + dv)}")
+    dt = _dtype_code(x.dtype)
+    _check(x, "x", x.dtype)
+    _check(conv_w, "conv_w", torch.float32, (C, 4))
+    _check(a_logit, "a_logit", torch.float32, (B, T, H))
+    _check(b_logit, "b_logit", torch.float32, (B, T, H))
+    _check(conv_state, "conv_state", x.dtype, (B, 3, C))
+    dev = x.device
+    q = torch.empty((B, H, T, dk), dtype=x.dtype, device=dev) if q is None else q
+    k = torch.empty((B, H, T, dk), dtype=x.dtype, device=dev) if k is None else k
+    v = torch.empty((B, H, T, dv), dtype=x.dtype, device=dev) if v is None else v
+    alpha = torch.empty((B, H, T), dtype=torch.float32, device=dev) if alpha is None else alpha
+    beta = torch.empty((B, H, T), dtype=torch.float32, device=dev) if beta is None else beta
+    if want_state and conv_state_out is None:
+        conv_state_out = torch.empty((B, 3, C), dtype=x.dtype, device=dev)
+    for t, n, d, shp in ((q, "q", x.dtype, (B, H, T, dk)), (k, "k", x.dtype, (B, H, T, dk)),
+                         (v, "v", x.dtype, (B, H, T, dv)), (alpha, "alpha", torch.float32, (B, H, T)),
+                         (beta, "beta", torch.float32, (B, H, T)),
+                         (conv_state_out, "conv_state_out", x.dtype, (B, 3, C))):
+        _check(t, n, d, shp)
+    st = _load().gdn_preprocess(dt, B, T, H, dk, dv, _ptr(x), _ptr(conv_w), _ptr(a_logit), _ptr(b_logit),
+                                _ptr(conv_state), _ptr(conv_state_out), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                _ptr(beta), _stream_ptr(stream, dev))
+    if st != 0:
+        raise LinAttnError(st, "gdn_preprocess")
+    return q, k, v, alpha, beta, conv_state_out
 
 
 def gdn_workspace(q, v, chunk=64):

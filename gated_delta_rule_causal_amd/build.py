@@ -25,6 +25,7 @@ SOURCES = [
     "chunked_generic.hip",
     "gdn_mfma.hip",
     "la_mfma.hip",
+    "preops.hip",
 ]
 
 ARCH = "gfx950"

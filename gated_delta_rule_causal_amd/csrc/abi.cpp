@@ -288,6 +288,43 @@ la_status gla_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
     return from_hip(la::launch_gla_mfma(B, H, T, q, k, v, alpha, S0, o, S_out, workspace, s));
 }
 
+la_status gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const void* x, const float* conv_w,
+                         const float* a_logit, const float* b_logit, const void* conv_state, void* conv_state_out,
+                         void* q, void* k, void* v, float* alpha, float* beta, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (static_cast<long long>(H) * (2 * dk + dv) > 0x7fffffffLL) return LA_ERR_SHAPE;
+    // one workgroup per (sequence, head, 64-token tile): the grid must fit one dimension
+    if (static_cast<long long>(B) * H * ((T + 63) / 64 > 0 ? (T + 63) / 64 : 1) > 0x7fffffffLL) return LA_ERR_SHAPE;
+    if (B == 0 || H == 0) return LA_OK;
+    const size_t es = io_size(dtype);
+    const size_t C = static_cast<size_t>(H) * (2 * dk + dv);
+    const size_t rows = static_cast<size_t>(B) * T;
+    if (conv_w == nullptr) return LA_ERR_NULL;
+    if (T > 0 && (x == nullptr || a_logit == nullptr || b_logit == nullptr || q == nullptr || k == nullptr ||
+                  v == nullptr || alpha == nullptr || beta == nullptr))
+        return LA_ERR_NULL;
+    for (const void* p : {x, static_cast<const void*>(conv_w), static_cast<const void*>(a_logit),
+                          static_cast<const void*>(b_logit), conv_state, static_cast<const void*>(conv_state_out),
+                          static_cast<const void*>(q), static_cast<const void*>(k), static_cast<const void*>(v),
+                          static_cast<const void*>(alpha), static_cast<const void*>(beta)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const size_t nx = rows * C * es, nl = rows * H * sizeof(float), nst = static_cast<size_t>(B) * 3 * C * es;
+    const size_t nqk = rows * H * dk * es, nv = rows * H * dv * es;
+    const Span in[] = {{x, nx}, {conv_w, C * 4 * sizeof(float)}, {a_logit, nl}, {b_logit, nl}, {conv_state, nst}};
+    const Span outs[] = {{conv_state_out, nst}, {q, nqk}, {k, nqk}, {v, nv}, {alpha, nl}, {beta, nl}};
+    for (const Span& a : outs) {
+        for (const Span& b : in)
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        for (const Span& b : outs)
+            if (&a != &b && overlaps(a, b)) return LA_ERR_ARG;
+    }
+    if (T == 0 && conv_state_out == nullptr) return LA_OK;
+    return from_hip(la::launch_gdn_preprocess(dtype, B, T, H, dk, dv, x, conv_w, a_logit, b_logit, conv_state,
+                                              conv_state_out, q, k, v, alpha, beta,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Shared checks of the two halves of the chunked matrix-core gated-delta path.

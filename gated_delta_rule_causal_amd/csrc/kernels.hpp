@@ -69,4 +69,13 @@ hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, con
 hipError_t launch_gla_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
                            const float* S0, void* o, float* S_out, void* workspace, hipStream_t stream);
 
+// ---- fused pre-operations of a Gated DeltaNet layer (preops.hip) ---------
+// x [B,T,H*(2dk+dv)] token-major (q | k | v channel blocks), w [C,4] fp32,
+// a_logit/b_logit [B,T,H] fp32, conv state [B,3,C] (I/O dtype; NULL = zeros,
+// st_out NULL = not written, never the same memory as st_in); outputs q,k
+// [B,H,T,dk], v [B,H,T,dv], alpha/beta [B,H,T] fp32.  T may be 0.
+hipError_t launch_gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const void* x, const float* w,
+                                 const float* a_logit, const float* b_logit, const void* st_in, void* st_out,
+                                 void* q, void* k, void* v, float* alpha, float* beta, hipStream_t stream);
+
 }  // namespace la

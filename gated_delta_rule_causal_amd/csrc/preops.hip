@@ -1,0 +1,219 @@
+// Pre-operations in front of a Gated DeltaNet layer, fused into one pass:
+// kernel-4 causal depthwise convolution over time, per-head L2 normalisation
+// of q and k, sigmoid gates, and the change of layout from token-major
+// projections [B, T, channels] to the head-major rows [B, H, T, d] the
+// prefill kernels read.
+//
+// Source: page "Linear attention and hybrids", section "2025 hybrids:
+// Qwen3-Next and Kimi Linear" (a short causal depthwise convolution over time
+// with kernel 4 before q, k and v), section "Memory must forget: decay and
+// gates" (the gate is a sigmoid of the input).  Per channel c and token t:
+//     y_t[c] = sum_{i<4} w[c][i] x_{t-3+i}[c]
+// with the three tokens before the first taken from a carried state (zeros
+// without one); q and k are then divided by their per-head Euclidean norm;
+// alpha = sigma(a_logit), beta = sigma(b_logit).
+//
+// One workgroup per (sequence, head, 64-token tile), 256 threads.  A lane
+// owns 8 consecutive channels of a few consecutive tokens and keeps the input
+// rows of its sliding window in registers; the D/8 lanes of a q (or k) row
+// reduce its sum of squares with xor shuffles.  Input rows are read straight
+// from global memory with 16-byte loads (the three rows a tile shares with
+// the one before it come from the caches), every output row is written with
+// 16-byte stores, and the HBM traffic is one read of the projections and one
+// write of the head-major tensors.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace la {
+
+namespace {
+
+constexpr int kTile = 64;
+constexpr int kThreads = 256;
+
+// 8 consecutive elements at p (16-byte aligned for fp32, 16-byte for bf16).
+__device__ __forceinline__ void load8(const float* p, float* x) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const u16* p, float* x) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void store8(float* p, const float* x) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(u16* p, const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = static_cast<uint32_t>(f32_to_bf16_bits(x[2 * i])) |
+               (static_cast<uint32_t>(f32_to_bf16_bits(x[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Convolve one head's block of D channels (starting at channel cbase of the
+// projection) over the tile's tokens and write rows of dst [.., T, D].  Lane
+// layout: D/8 lanes per token row, each lane 8 channels; a lane handles TPL
+// consecutive tokens so that it reads TPL + 3 input rows for TPL outputs.
+// With NORM every output row is divided by its Euclidean norm (zero rows stay
+// zero).  Called by every thread of the block (the xor reductions need the
+// whole wave).
+template <int D, bool NORM, class E>
+__device__ __forceinline__ void conv_rows(const E* __restrict__ xb, const E* st, const float* __restrict__ w, int C,
+                                          int cbase, int t0, int len, E* __restrict__ dst, int tid) {
+    constexpr int L = D / 8;                    // lanes per token row
+    constexpr int TPL = L >= 4 ? L / 4 : 1;     // tokens per lane
+    constexpr int NL = kTile / TPL * L;         // lanes in use (a multiple of 64)
+    static_assert(NL <= kThreads && NL % kWave == 0, "lane layout");
+    if (tid >= NL) return;
+    const int m = tid % L, grp = tid / L;
+    const int c0 = cbase + 8 * m;
+    float wv[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float4 a = *reinterpret_cast<const float4*>(w + static_cast<size_t>(c0 + e) * 4);
+        wv[e][0] = a.x; wv[e][1] = a.y; wv[e][2] = a.z; wv[e][3] = a.w;
+    }
+    const int jb = grp * TPL;                   // first token of this lane, within the tile
+    float xr[TPL + 3][8];
+#pragma unroll
+    for (int r = 0; r < TPL + 3; ++r) {
+        const int ts = t0 + jb - 3 + r;         // absolute token index (negative: carried state)
+        if (jb + r - 3 < len) {
+            if (ts >= 0)
+                load8(xb + static_cast<size_t>(ts) * C + c0, xr[r]);
+            else if (st != nullptr)
+                load8(st + static_cast<size_t>(3 + ts) * C + c0, xr[r]);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xr[r][e] = 0.f;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[r][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < TPL; ++s) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float acc = wv[e][0] * xr[s][e];
+            acc = fmaf(wv[e][1], xr[s + 1][e], acc);
+            acc = fmaf(wv[e][2], xr[s + 2][e], acc);
+            y[e] = fmaf(wv[e][3], xr[s + 3][e], acc);
+        }
+        if constexpr (NORM) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+            ss = group_sum<L>(ss);
+            const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= inv;
+        }
+        const int j = jb + s;
+        if (j < len) store8(dst + static_cast<size_t>(t0 + j) * D + 8 * m, y);
+    }
+}
+
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
+    int T, int H, int tiles, const typename IO::T* __restrict__ x, const float* __restrict__ w,
+    const float* __restrict__ a_logit, const float* __restrict__ b_logit, const typename IO::T* st_in,
+    typename IO::T* st_out, typename IO::T* __restrict__ q, typename IO::T* __restrict__ k,
+    typename IO::T* __restrict__ v, float* __restrict__ alpha, float* __restrict__ beta) {
+    using E = typename IO::T;
+    const int C = H * (2 * DK + DV);
+    const int tile = blockIdx.x % tiles;
+    const int h = (blockIdx.x / tiles) % H;
+    const int b = blockIdx.x / (tiles * H);
+    const int t0 = tile * kTile;
+    const int len = max(0, min(kTile, T - t0));
+    const E* xb = x + static_cast<size_t>(b) * T * C;
+    const E* st = st_in ? st_in + static_cast<size_t>(b) * 3 * C : nullptr;
+    const size_t row0 = (static_cast<size_t>(b) * H + h) * T;   // row (b, h, t = 0) of the outputs
+    const int tid = threadIdx.x;
+
+    conv_rows<DK, true>(xb, st, w, C, h * DK, t0, len, q + row0 * DK, tid);
+    conv_rows<DK, true>(xb, st, w, C, H * DK + h * DK, t0, len, k + row0 * DK, tid);
+    conv_rows<DV, false>(xb, st, w, C, 2 * H * DK + h * DV, t0, len, v + row0 * DV, tid);
+
+    if (tid < len) {
+        const size_t li = (static_cast<size_t>(b) * T + t0 + tid) * H + h;
+        alpha[row0 + t0 + tid] = 1.f / (1.f + __expf(-a_logit[li]));
+        beta[row0 + t0 + tid] = 1.f / (1.f + __expf(-b_logit[li]));
+    }
+    // carried state: the last three tokens of [state; x], this head's channels
+    if (st_out != nullptr && tile == tiles - 1) {
+        constexpr int nch = 2 * DK + DV;
+        for (int e = tid; e < 3 * nch; e += kThreads) {
+            const int r = e / nch, cc = e % nch;
+            const int c = cc < DK       ? h * DK + cc
+                          : cc < 2 * DK ? H * DK + h * DK + (cc - DK)
+                                        : 2 * H * DK + h * DV + (cc - 2 * DK);
+            const int ts = T - 3 + r;
+            float val = 0.f;
+            if (ts >= 0)
+                val = IO::load(xb, static_cast<size_t>(ts) * C + c);
+            else if (st != nullptr)
+                val = IO::load(st, static_cast<size_t>(3 + ts) * C + c);
+            IO::store(st_out + static_cast<size_t>(b) * 3 * C, static_cast<size_t>(r) * C + c, val);
+        }
+    }
+}
+
+template <class IO, int DK>
+hipError_t launch_dv(int B, int T, int H, int dv, const void* x, const float* w, const float* al, const float* bl,
+                     const void* st_in, void* st_out, void* q, void* k, void* v, float* alpha, float* beta,
+                     hipStream_t stream) {
+    using E = typename IO::T;
+    const int tiles = T > 0 ? (T + kTile - 1) / kTile : 1;   // T == 0: one block per head writes the state
+    const dim3 grid(static_cast<unsigned>(B) * H * tiles), block(kThreads);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, T, H, tiles, static_cast<const E*>(x), w, al, bl,
+                           static_cast<const E*>(st_in), static_cast<E*>(st_out), static_cast<E*>(q),
+                           static_cast<E*>(k), static_cast<E*>(v), alpha, beta);
+        return hipGetLastError();
+    };
+    switch (dv) {
+        case 16: return go(gdn_preprocess_kernel<IO, DK, 16>);
+        case 32: return go(gdn_preprocess_kernel<IO, DK, 32>);
+        case 64: return go(gdn_preprocess_kernel<IO, DK, 64>);
+        case 128: return go(gdn_preprocess_kernel<IO, DK, 128>);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class IO>
+hipError_t launch_io(int B, int T, int H, int dk, int dv, const void* x, const float* w, const float* al,
+                     const float* bl, const void* st_in, void* st_out, void* q, void* k, void* v, float* alpha,
+                     float* beta, hipStream_t stream) {
+    switch (dk) {
+        case 16: return launch_dv<IO, 16>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
+        case 32: return launch_dv<IO, 32>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
+        case 64: return launch_dv<IO, 64>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
+        case 128: return launch_dv<IO, 128>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const void* x, const float* w,
+                                 const float* a_logit, const float* b_logit, const void* st_in, void* st_out,
+                                 void* q, void* k, void* v, float* alpha, float* beta, hipStream_t stream) {
+    if (B <= 0 || H <= 0) return hipSuccess;
+    return dtype == kBF16 ? launch_io<IoBF16>(B, T, H, dk, dv, x, w, a_logit, b_logit, st_in, st_out, q, k, v, alpha,
+                                              beta, stream)
+                          : launch_io<IoF32>(B, T, H, dk, dv, x, w, a_logit, b_logit, st_in, st_out, q, k, v, alpha,
+                                             beta, stream);
+}
+
+}  // namespace la

@@ -195,6 +195,44 @@ la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv
                                float* S, float* z, void* o, void* stream);
 
 /*
+ * gdn_preprocess - the cheap per-token operations in front of a Gated
+ * DeltaNet layer, fused into one pass that also turns the token-major
+ * projections into the head-major rows gdn_prefill reads.
+ *
+ * Page "Linear attention and hybrids": section "2025 hybrids: Qwen3-Next and
+ * Kimi Linear" (a causal depthwise convolution over time with kernel 4 in
+ * front of q, k and v), section "Delta rule and Gated DeltaNet" (unit-length
+ * keys), section "Memory must forget: decay and gates" (sigmoid gates).  Per
+ * sequence b, token t and channel c (C = H*(2dk+dv) channels):
+ *     y_t[c] = sum_{i=0..3} conv_w[c][i] x_{t-3+i}[c]     (no bias)
+ * where the three tokens before t = 0 are conv_state (zeros when NULL).  The
+ * channels are q (H*dk), then k (H*dk), then v (H*dv), each head's block
+ * contiguous.  Then, per head h:
+ *     q[b,h,t] = y_t[q block h] / |y_t[q block h]|   (a zero row stays zero)
+ *     k[b,h,t] = y_t[k block h] / |y_t[k block h]|
+ *     v[b,h,t] = y_t[v block h]
+ *     alpha[b,h,t] = sigmoid(a_logit[b,t,h]),  beta[b,h,t] = sigmoid(b_logit[b,t,h])
+ * Arguments (device pointers, 16-byte aligned, element type `dtype` unless
+ * stated):
+ *   x [B,T,C]; conv_w [C,4] float32 (tap 3 multiplies the current token);
+ *   a_logit, b_logit [B,T,H] float32; conv_state [B,3,C] or NULL (row 0 is
+ *   token t-3); conv_state_out [B,3,C] or NULL receives the last three tokens
+ *   of [conv_state; x], ready for the next call on the same sequences; it must
+ *   not overlap conv_state or any other argument (LA_ERR_ARG);
+ *   q, k [B,H,T,dk]; v [B,H,T,dv]; alpha, beta [B,H,T] float32.
+ * dk, dv in {16, 32, 64, 128}.  T = 0 only copies conv_state to
+ * conv_state_out.  Errors: LA_ERR_DTYPE, LA_ERR_SHAPE, LA_ERR_NULL,
+ * LA_ERR_ALIGN, LA_ERR_ARG (overlap), LA_ERR_HIP; nothing is launched on
+ * error.  Works asynchronously on `stream`; the caller owns every buffer.
+ */
+la_status gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv,
+                         const void* x, const float* conv_w,
+                         const float* a_logit, const float* b_logit,
+                         const void* conv_state, void* conv_state_out,
+                         void* q, void* k, void* v, float* alpha, float* beta,
+                         void* stream);
+
+/*
  * la_workspace_bytes - device workspace needed by one call of `fn` with the
  * given arguments (0 when none is needed).  Returns (size_t)-1 when the
  * arguments are invalid or the combination is not supported.

@@ -15,6 +15,11 @@ without drawing the rest):
   rounded to the I/O dtype.  bf16 rounding is round-to-nearest-even, and the
   returned float32 arrays hold exactly the bf16 values the GPU sees.
 * alpha = sigmoid(N(3, 1)), beta = sigmoid(N(0, 1)), kept in float32.
+* pre-operations: the token-major projections x [B, T, H*(2dk+dv)] ~ N(0, 1)
+  (one generator per sequence) rounded to the I/O dtype; depthwise conv
+  weights [C, 4] ~ N(0, 0.5^2) float32; gate logits a ~ N(3, 1) and
+  b ~ N(0, 1) float32 [B, T, H]; a carried conv state [B, 3, C] ~ N(0, 1)
+  rounded to the I/O dtype.
 * decode: the carried state S0 ~ N(0, 0.02^2) float32 per head; the per-step
   token inputs come from a pool of ``pool`` draws (step s uses pool entry
   s mod pool), generated with ``default_rng([seed, stream, 1000 + entry])``.
@@ -23,6 +28,7 @@ without drawing the rest):
 import numpy as np
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_ALPHA, STREAM_BETA, STREAM_S0, STREAM_Z0 = range(7)
+STREAM_X, STREAM_CONV_W, STREAM_LOGITS, STREAM_CONV_STATE = range(7, 11)
 
 # The five named workloads.  ``seed`` is the per-workload base seed.
 WORKLOADS = {
@@ -40,6 +46,10 @@ WORKLOADS = {
     # without beta, at the gated-delta prefill shape
     "gla_bf16_2x16x8192": dict(seed=1006, kind="gla", B=2, H=16, T=8192, dk=128, dv=128,
                                dtype="bf16", chunk=64),
+    # pre-operations of a Gated DeltaNet layer in front of the 2 x 16 x 8192
+    # prefill: x [2, 8192, 16 * (128 + 128 + 128)]
+    "preops_bf16_2x16x8192": dict(seed=1007, kind="preops", B=2, H=16, T=8192, dk=128, dv=128,
+                                  dtype="bf16"),
 }
 
 
@@ -158,3 +168,21 @@ def la_decode_token_inputs(seed, N, H, dk, dv, dtype, entry, scale=1.0):
     k = round_io(_normal(seed, STREAM_K, (2000 + entry,), (N, H, dk)) * np.float32(scale), dtype)
     v = round_io(_normal(seed, STREAM_V, (2000 + entry,), (N, H, dv)) * np.float32(scale), dtype)
     return q, k, v
+
+
+def preops_batch(seed, B, T, H, dk, dv, dtype, w_std=0.5):
+    """Inputs of the pre-operations: x [B,T,C] (rounded to dtype), conv
+    weights [C,4], gate logits a_logit, b_logit [B,T,H] (float32)."""
+    C = H * (2 * dk + dv)
+    x = np.empty((B, T, C), np.float32)
+    for b in range(B):
+        x[b] = round_io(_normal(seed, STREAM_X, (b,), (T, C)), dtype)
+    w = (_normal(seed, STREAM_CONV_W, (), (C, 4)) * np.float32(w_std)).astype(np.float32)
+    a = (_normal(seed, STREAM_LOGITS, (0,), (B, T, H)) + np.float32(3.0)).astype(np.float32)
+    bl = _normal(seed, STREAM_LOGITS, (1,), (B, T, H))
+    return x, w, a, bl
+
+
+def conv_state_batch(seed, B, H, dk, dv, dtype):
+    """A carried conv state [B, 3, H*(2dk+dv)] rounded to dtype."""
+    return round_io(_normal(seed, STREAM_CONV_STATE, (), (B, 3, H * (2 * dk + dv))), dtype)

@@ -48,7 +48,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gla_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
-                            "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
+                            "gdn_preprocess", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -239,3 +239,27 @@ def test_gla_validation(lib):
     assert dec(a=None) == LA_ERR_NULL
     assert dec(b=8) == LA_ERR_ARG
     assert dec(z=8) == LA_ERR_ARG
+
+
+def test_preprocess_validation(lib):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+
+    def pre(dtype=BF16, B=2, T=100, H=4, dk=128, dv=128, x=1, w=2, a=3, b=4, st=None, st_out=None, q=5, k=6, v=7,
+            al=8, be=9):
+        return lib.gdn_preprocess(dtype, B, T, H, dk, dv, f(x), f(w), f(a), f(b), f(st), f(st_out), f(q), f(k),
+                                  f(v), f(al), f(be), None)
+
+    assert pre(dtype=3) == LA_ERR_DTYPE
+    assert pre(dk=48) == LA_ERR_SHAPE
+    assert pre(dv=256) == LA_ERR_SHAPE
+    assert pre(T=-1) == LA_ERR_SHAPE
+    assert pre(x=None) == LA_ERR_NULL
+    assert pre(w=None) == LA_ERR_NULL
+    assert pre(be=None) == LA_ERR_NULL
+    assert pre(q=ctypes.c_void_p(BASE + 5 * GiB + 8)) == LA_ERR_ALIGN
+    assert pre(q=1) == LA_ERR_ARG                          # output on top of x
+    assert pre(k=5) == LA_ERR_ARG                          # two outputs on the same memory
+    assert pre(st=10, st_out=10) == LA_ERR_ARG             # the conv state is not updated in place
+    assert pre(al=4) == LA_ERR_ARG                         # alpha on top of b_logit
+    assert pre(B=0) == LA_OK                               # empty batch: nothing to do
+    assert pre(T=0, st=10) == LA_OK                        # no tokens and no state to write
