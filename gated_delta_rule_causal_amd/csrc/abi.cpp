@@ -294,8 +294,8 @@ la_status gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const v
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
     if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
     if (static_cast<long long>(H) * (2 * dk + dv) > 0x7fffffffLL) return LA_ERR_SHAPE;
-    // one workgroup per (sequence, head, 64-token tile): the grid must fit one dimension
-    if (static_cast<long long>(B) * H * ((T + 63) / 64 > 0 ? (T + 63) / 64 : 1) > 0x7fffffffLL) return LA_ERR_SHAPE;
+    // one workgroup per (sequence, head, 128-token tile): the grid must fit one dimension
+    if (static_cast<long long>(B) * H * ((T + 127) / 128 > 0 ? (T + 127) / 128 : 1) > 0x7fffffffLL) return LA_ERR_SHAPE;
     if (B == 0 || H == 0) return LA_OK;
     const size_t es = io_size(dtype);
     const size_t C = static_cast<size_t>(H) * (2 * dk + dv);

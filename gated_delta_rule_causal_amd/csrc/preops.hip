@@ -13,14 +13,20 @@
 // without one); q and k are then divided by their per-head Euclidean norm;
 // alpha = sigma(a_logit), beta = sigma(b_logit).
 //
-// One workgroup per (sequence, head, 64-token tile), 256 threads.  A lane
-// owns 8 consecutive channels of a few consecutive tokens and keeps the input
-// rows of its sliding window in registers; the D/8 lanes of a q (or k) row
-// reduce its sum of squares with xor shuffles.  Input rows are read straight
-// from global memory with 16-byte loads (the three rows a tile shares with
-// the one before it come from the caches), every output row is written with
-// 16-byte stores, and the HBM traffic is one read of the projections and one
-// write of the head-major tensors.
+// Work split: one workgroup per (sequence, head, tile of 128 tokens), 256
+// threads, which produce the tile's q, then k, then v rows.  For one part
+// (D channels) a lane owns 8 consecutive channels and TPL consecutive tokens
+// (D/8 lanes per token row): it loads its channels of the TPL + 3 rows its
+// outputs need (its tokens and the three before them: the previous tile, the
+// carried state, or zeros) with 16-byte loads, all issued before the first
+// is used, then convolves, normalises (the D/8 lanes of a q or k row are an
+// aligned lane group and reduce its sum of squares with xor shuffles) and
+// writes each output row piece with one 16-byte nontemporal store (nothing
+// here reads the outputs back).  The heads of one tile are neighbours in the
+// launch order, so the workgroups in flight read whole projection rows
+// between them.  HBM traffic: one read of the projections (the three history
+// rows of a tile come from the caches) and one write of the head-major
+// tensors.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,26 +34,46 @@ namespace la {
 
 namespace {
 
-constexpr int kTile = 64;
+constexpr int kTile = 128;
 constexpr int kThreads = 256;
 
-// 8 consecutive elements at p (16-byte aligned for fp32, 16-byte for bf16).
-__device__ __forceinline__ void load8(const float* p, float* x) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void load8(const u16* p, float* x) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// 8 consecutive elements of one input row, as loaded (16-byte aligned).
+template <class E>
+struct Raw;
+template <>
+struct Raw<u16> {
+    uint4 u;
+    __device__ __forceinline__ void load(const u16* p) { u = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void get(float* x) const {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
     }
+};
+template <>
+struct Raw<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ void get(float* x) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+
+__device__ __forceinline__ void nt_store16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const u32x4v v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4v*>(p));
 }
 __device__ __forceinline__ void store8(float* p, const float* x) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    nt_store16(p, __float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
+    nt_store16(p + 4, __float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7]));
 }
 __device__ __forceinline__ void store8(u16* p, const float* x) {
     uint32_t w[4];
@@ -55,25 +81,26 @@ __device__ __forceinline__ void store8(u16* p, const float* x) {
     for (int i = 0; i < 4; ++i)
         w[i] = static_cast<uint32_t>(f32_to_bf16_bits(x[2 * i])) |
                (static_cast<uint32_t>(f32_to_bf16_bits(x[2 * i + 1])) << 16);
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    nt_store16(p, w[0], w[1], w[2], w[3]);
 }
 
-// Convolve one head's block of D channels (starting at channel cbase of the
-// projection) over the tile's tokens and write rows of dst [.., T, D].  Lane
-// layout: D/8 lanes per token row, each lane 8 channels; a lane handles TPL
-// consecutive tokens so that it reads TPL + 3 input rows for TPL outputs.
-// With NORM every output row is divided by its Euclidean norm (zero rows stay
-// zero).  Called by every thread of the block (the xor reductions need the
-// whole wave).
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// One part of the tile: the head's D channels starting at channel cbase of
+// the projection, written to dst = the head's rows [T, D].  With NORM every
+// output row is divided by its Euclidean norm (a zero row stays zero).
+// Called by every thread of the workgroup with len > 0 (the xor reductions
+// need whole waves).
 template <int D, bool NORM, class E>
-__device__ __forceinline__ void conv_rows(const E* __restrict__ xb, const E* st, const float* __restrict__ w, int C,
-                                          int cbase, int t0, int len, E* __restrict__ dst, int tid) {
-    constexpr int L = D / 8;                    // lanes per token row
-    constexpr int TPL = L >= 4 ? L / 4 : 1;     // tokens per lane
-    constexpr int NL = kTile / TPL * L;         // lanes in use (a multiple of 64)
+__device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st, const float* __restrict__ w, int C,
+                                          int cbase, int t0, int len, int T, E* __restrict__ dst, int tid) {
+    constexpr int L = D / 8;                                          // lanes per token row
+    constexpr int TPL = kTile * L / kThreads >= 1 ? kTile * L / kThreads : 1;   // tokens per lane
+    constexpr int NL = kTile / TPL * L;                               // lanes in use
     static_assert(NL <= kThreads && NL % kWave == 0, "lane layout");
-    if (tid >= NL) return;
-    const int m = tid % L, grp = tid / L;
+    if (tid >= NL) return;                                            // whole waves
+    const int m = tid % L;
+    const int jb = (tid / L) * TPL;                                   // first token of this lane in the tile
     const int c0 = cbase + 8 * m;
     float wv[8][4];
 #pragma unroll
@@ -81,23 +108,30 @@ __device__ __forceinline__ void conv_rows(const E* __restrict__ xb, const E* st,
         const float4 a = *reinterpret_cast<const float4*>(w + static_cast<size_t>(c0 + e) * 4);
         wv[e][0] = a.x; wv[e][1] = a.y; wv[e][2] = a.z; wv[e][3] = a.w;
     }
-    const int jb = grp * TPL;                   // first token of this lane, within the tile
+    // Window rows r = 0 .. TPL + 2 hold token t0 + jb - 3 + r.  Every load is
+    // unconditional (a row the outputs do not need reads row t0, which
+    // exists), so that no load waits in a branch of its own.
+    Raw<E> raw[TPL + 3];
+#pragma unroll
+    for (int r = 0; r < TPL + 3; ++r) {
+        const int ts = t0 + jb - 3 + r;                               // >= -3
+        const bool in_tile = jb + r - 3 < len;                        // later rows feed no stored output
+        const bool from_state = in_tile && ts < 0 && st != nullptr;
+        const int row = in_tile && ts >= 0 ? ts : t0;
+        const E* src = from_state ? st + static_cast<size_t>(3 + ts) * C : xb + static_cast<size_t>(row) * C;
+        raw[r].load(src + c0);
+    }
+    // keep the scheduler from unpacking the first rows (and so waiting for
+    // them) before every load above has been issued
+    __builtin_amdgcn_sched_barrier(0);
     float xr[TPL + 3][8];
 #pragma unroll
     for (int r = 0; r < TPL + 3; ++r) {
-        const int ts = t0 + jb - 3 + r;         // absolute token index (negative: carried state)
-        if (jb + r - 3 < len) {
-            if (ts >= 0)
-                load8(xb + static_cast<size_t>(ts) * C + c0, xr[r]);
-            else if (st != nullptr)
-                load8(st + static_cast<size_t>(3 + ts) * C + c0, xr[r]);
-            else
+        raw[r].get(xr[r]);
+        // before the first token, without a carried state: zeros
+        const bool live = t0 + jb - 3 + r >= 0 || st != nullptr;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) xr[r][e] = 0.f;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xr[r][e] = 0.f;
-        }
+        for (int e = 0; e < 8; ++e) xr[r][e] = live ? xr[r][e] : 0.f;
     }
 #pragma unroll
     for (int s = 0; s < TPL; ++s) {
@@ -131,9 +165,9 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     typename IO::T* __restrict__ v, float* __restrict__ alpha, float* __restrict__ beta) {
     using E = typename IO::T;
     const int C = H * (2 * DK + DV);
-    const int tile = blockIdx.x % tiles;
-    const int h = (blockIdx.x / tiles) % H;
-    const int b = blockIdx.x / (tiles * H);
+    const int h = blockIdx.x % H;
+    const int tile = (blockIdx.x / H) % tiles;
+    const int b = blockIdx.x / (H * tiles);
     const int t0 = tile * kTile;
     const int len = max(0, min(kTile, T - t0));
     const E* xb = x + static_cast<size_t>(b) * T * C;
@@ -141,14 +175,15 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     const size_t row0 = (static_cast<size_t>(b) * H + h) * T;   // row (b, h, t = 0) of the outputs
     const int tid = threadIdx.x;
 
-    conv_rows<DK, true>(xb, st, w, C, h * DK, t0, len, q + row0 * DK, tid);
-    conv_rows<DK, true>(xb, st, w, C, H * DK + h * DK, t0, len, k + row0 * DK, tid);
-    conv_rows<DV, false>(xb, st, w, C, 2 * H * DK + h * DV, t0, len, v + row0 * DV, tid);
-
-    if (tid < len) {
-        const size_t li = (static_cast<size_t>(b) * T + t0 + tid) * H + h;
-        alpha[row0 + t0 + tid] = 1.f / (1.f + __expf(-a_logit[li]));
-        beta[row0 + t0 + tid] = 1.f / (1.f + __expf(-b_logit[li]));
+    if (len > 0) {   // (T == 0: only the state below)
+        conv_part<DK, true>(xb, st, w, C, h * DK, t0, len, T, q + row0 * DK, tid);
+        conv_part<DK, true>(xb, st, w, C, H * DK + h * DK, t0, len, T, k + row0 * DK, tid);
+        conv_part<DV, false>(xb, st, w, C, 2 * H * DK + h * DV, t0, len, T, v + row0 * DV, tid);
+        for (int j = tid; j < len; j += kThreads) {
+            const size_t li = (static_cast<size_t>(b) * T + t0 + j) * H + h;
+            alpha[row0 + t0 + j] = sigmoid(a_logit[li]);
+            beta[row0 + t0 + j] = sigmoid(b_logit[li]);
+        }
     }
     // carried state: the last three tokens of [state; x], this head's channels
     if (st_out != nullptr && tile == tiles - 1) {
@@ -174,8 +209,8 @@ hipError_t launch_dv(int B, int T, int H, int dv, const void* x, const float* w,
                      const void* st_in, void* st_out, void* q, void* k, void* v, float* alpha, float* beta,
                      hipStream_t stream) {
     using E = typename IO::T;
-    const int tiles = T > 0 ? (T + kTile - 1) / kTile : 1;   // T == 0: one block per head writes the state
-    const dim3 grid(static_cast<unsigned>(B) * H * tiles), block(kThreads);
+    const int tiles = T > 0 ? (T + kTile - 1) / kTile : 1;   // T == 0: one workgroup per head writes the state
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * H * tiles)), block(kThreads);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, T, H, tiles, static_cast<const E*>(x), w, al, bl,
                            static_cast<const E*>(st_in), static_cast<E*>(st_out), static_cast<E*>(q),
