@@ -38,6 +38,12 @@ from .gated_delta import (
     gdn_decode_step,
     gdn_bruteforce_states,
 )
+from .kda import (
+    kda_recurrent,
+    kda_chunked,
+    kda_decode_step,
+    kda_bruteforce_states,
+)
 from . import batched
 from . import preops
 
@@ -54,6 +60,10 @@ __all__ = [
     "gdn_parallel",
     "gdn_decode_step",
     "gdn_bruteforce_states",
+    "kda_recurrent",
+    "kda_chunked",
+    "kda_decode_step",
+    "kda_bruteforce_states",
     "batched",
     "preops",
 ]

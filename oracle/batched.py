@@ -12,6 +12,7 @@ import numpy as np
 
 from .linear_attention import phi, la_parallel, la_recurrent, la_chunked, gated_recurrent
 from .gated_delta import gdn_recurrent, gdn_chunked
+from .kda import kda_recurrent, kda_chunked
 
 
 def _heads(B, H, heads):
@@ -114,4 +115,33 @@ def gla_step_heads(q, k, v, alpha, S):
     gates"), broadcast over the head axis.  Returns (o [n, dv], S_new)."""
     q, k, v, alpha, S = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, S))
     S_new = alpha[:, None, None] * S + v[:, :, None] * k[:, None, :]
+    return (S_new @ q[:, :, None])[..., 0], S_new
+
+
+def kda(q, k, v, alpha, beta, S0=None, form="recurrent", chunk=64, heads=None):
+    """KDA over the batch (alpha [B,H,T,d_k] per channel); returns (o, S)
+    with only the listed heads filled."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    S = np.zeros((B, H, dv, dk))
+    for b, h in _heads(B, H, heads):
+        s0 = None if S0 is None else S0[b, h]
+        if form == "recurrent":
+            o[b, h], S[b, h] = kda_recurrent(q[b, h], k[b, h], v[b, h], alpha[b, h], beta[b, h], s0)
+        elif form == "chunked":
+            o[b, h], S[b, h] = kda_chunked(q[b, h], k[b, h], v[b, h], alpha[b, h], beta[b, h], chunk, s0)
+        else:
+            raise ValueError(form)
+    return o, S
+
+
+def kda_step_heads(q, k, v, alpha, beta, S):
+    """One KDA step for many independent heads at once (alpha [n, d_k]):
+    S <- S Diag(alpha) (I - beta k k^T) + beta v k^T, o = S q, broadcast over
+    the head axis.  Returns (o [n, dv], S_new)."""
+    q, k, v, alpha, beta, S = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, beta, S))
+    Sd = S * alpha[:, None, :]
+    Sk = (Sd @ k[:, :, None])[..., 0]                       # S Diag(alpha) k
+    S_new = Sd - beta[:, None, None] * Sk[:, :, None] * k[:, None, :] + beta[:, None, None] * v[:, :, None] * k[:, None, :]
     return (S_new @ q[:, :, None])[..., 0], S_new

@@ -516,3 +516,158 @@ def test_preops_pins():
 def test_planted_preops_mistake_is_caught(old, new):
     ns = types.SimpleNamespace(**_mutant(pre_mod, old, new))
     assert _fails_some_pin(ns, [pin_preops])
+
+
+# ------------------------------------------------------------------ KDA
+from oracle import kda as kda_mod
+
+
+def rand_kda(rng, T, dk, dv, spread=1.5):
+    Q = rng.normal(size=(T, dk))
+    K = rng.normal(size=(T, dk))
+    K /= np.linalg.norm(K, axis=1, keepdims=True)
+    V = rng.normal(size=(T, dv))
+    # per-channel decay: slow and fast channels side by side
+    a = 1.0 / (1.0 + np.exp(-(rng.normal(size=(T, dk)) * spread + np.linspace(-1.0, 5.0, dk))))
+    b = 1.0 / (1.0 + np.exp(-rng.normal(size=T)))
+    return Q, K, V, a, b
+
+
+def pin_kda_uniform_is_gdn(ns):
+    """Equal decay on every channel is the Gated DeltaNet equation (the
+    genuine, separately pinned oracle)."""
+    rng = np.random.default_rng(41)
+    T, dk, dv = 40, 6, 5
+    Q, K, V, a, b = rand_kda(rng, T, dk, dv)
+    a1 = np.repeat(a[:, :1], dk, axis=1)
+    S0 = rng.normal(size=(dv, dk))
+    o_ref, S_ref = oracle.gdn_recurrent(Q, K, V, a1[:, 0], b, S0)
+    for o, S in (ns.kda_recurrent(Q, K, V, a1, b, S0), ns.kda_chunked(Q, K, V, a1, b, 8, S0)):
+        assert np.abs(o - o_ref).max() < 1e-12 and np.abs(S - S_ref).max() < 1e-12
+
+
+def pin_kda_beta_zero(ns):
+    """beta = 0: pure per-channel forgetting of the key side,
+    S_t = S0 Diag(prod_{s<=t} alpha_s), o_t = S_t q_t."""
+    rng = np.random.default_rng(42)
+    T, d = 13, 4
+    Q, K, V, a, _ = rand_kda(rng, T, d, d)
+    b = np.zeros(T)
+    S0 = rng.normal(size=(d, d))
+    P = np.cumprod(a, axis=0)
+    o_ref = np.stack([(S0 * P[t][None, :]) @ Q[t] for t in range(T)])
+    S_ref = S0 * P[-1][None, :]
+    for o, S in (ns.kda_recurrent(Q, K, V, a, b, S0), ns.kda_chunked(Q, K, V, a, b, 4, S0)):
+        assert np.abs(o - o_ref).max() < 1e-12 and np.abs(S - S_ref).max() < 1e-12
+
+
+def pin_kda_unit_key_recall(ns):
+    """beta = 1 and a unit key: the decay comes before the correction, so a
+    read with the key just written returns exactly the value written,
+    whatever the decay."""
+    rng = np.random.default_rng(43)
+    T, dk, dv = 9, 5, 3
+    Q, K, V, a, _ = rand_kda(rng, T, dk, dv)
+    b = np.ones(T)
+    S = rng.normal(size=(dv, dk))
+    for t in range(T):
+        _, S = ns.kda_decode_step(Q[t], K[t], V[t], a[t], b[t], S)
+        assert np.abs(S @ K[t] - V[t]).max() < 1e-12
+    _, Sc = ns.kda_chunked(Q, K, V, a, b, 4, rng.normal(size=(dv, dk)))
+    assert np.abs(Sc @ K[-1] - V[-1]).max() < 1e-12
+
+
+def pin_kda_bruteforce_exact(ns):
+    """States and outputs against the unrolled product form in exact rationals."""
+    rng = np.random.default_rng(44)
+    T, dk, dv = 5, 3, 2
+
+    def rat(x, den=16):
+        return Fraction(int(round(x * den)), den)
+
+    K = [[rat(x) for x in row] for row in rng.normal(size=(T, dk))]
+    Qr = [[rat(x) for x in row] for row in rng.normal(size=(T, dk))]
+    V = [[rat(x) for x in row] for row in rng.normal(size=(T, dv))]
+    al = [[Fraction(int(x), 32) for x in row] for row in rng.integers(12, 33, (T, dk))]
+    be = [Fraction(int(x), 32) for x in rng.integers(1, 32, T)]
+    S0 = [[rat(x) for x in row] for row in rng.normal(size=(dv, dk))]
+    exact = ns.kda_bruteforce_states(K, V, al, be, S0)
+    f = lambda m: np.array([[float(x) for x in r] for r in m])
+    Kf, Qf, Vf, S0f, af = f(K), f(Qr), f(V), f(S0), f(al)
+    bf = np.array([float(x) for x in be])
+    o_exact = np.array([[float(sum(exact[t][i][p] * Qr[t][p] for p in range(dk))) for i in range(dv)]
+                        for t in range(T)])
+    for C in (None, 1, 2, T):
+        o, S = ns.kda_recurrent(Qf, Kf, Vf, af, bf, S0f) if C is None else \
+            ns.kda_chunked(Qf, Kf, Vf, af, bf, C, S0f)
+        assert np.abs(o - o_exact).max() < 1e-13, C
+        assert np.abs(S - f(exact[-1])).max() < 1e-13, C
+    S = S0f
+    for t in range(T):
+        o_t, S = ns.kda_decode_step(Qf[t], Kf[t], Vf[t], af[t], bf[t], S)
+        assert np.abs(S - f(exact[t])).max() < 1e-13 and np.abs(o_t - o_exact[t]).max() < 1e-13
+
+
+def pin_kda_chunk_invariance(ns):
+    rng = np.random.default_rng(45)
+    T, dk, dv = 70, 8, 6
+    Q, K, V, a, b = rand_kda(rng, T, dk, dv, spread=3.0)
+    S0 = rng.normal(size=(dv, dk))
+    o_r, S_r = ns.kda_recurrent(Q, K, V, a, b, S0)
+    for C in (1, 5, 16, 64, T):
+        o_c, S_c = ns.kda_chunked(Q, K, V, a, b, C, S0)
+        assert np.abs(o_c - o_r).max() < 1e-11 and np.abs(S_c - S_r).max() < 1e-11, C
+    o1, S1 = ns.kda_chunked(Q[:29], K[:29], V[:29], a[:29], b[:29], 8, S0)
+    o2, S2 = ns.kda_chunked(Q[29:], K[29:], V[29:], a[29:], b[29:], 16, S1)
+    assert np.abs(np.vstack([o1, o2]) - o_r).max() < 1e-11 and np.abs(S2 - S_r).max() < 1e-11
+
+
+KDA_PINS = [pin_kda_uniform_is_gdn, pin_kda_beta_zero, pin_kda_unit_key_recall, pin_kda_bruteforce_exact,
+            pin_kda_chunk_invariance]
+
+
+@pytest.mark.parametrize("pin", KDA_PINS, ids=lambda f: f.__name__)
+def test_kda_pin(pin):
+    pin(kda_mod)
+
+
+def test_kda_batched_step_matches_single_head():
+    rng = np.random.default_rng(46)
+    n, dk, dv = 5, 6, 4
+    q, k, v = rng.normal(size=(n, dk)), rng.normal(size=(n, dk)), rng.normal(size=(n, dv))
+    a, b, S = rng.uniform(0.2, 1.0, (n, dk)), rng.uniform(0, 1, n), rng.normal(size=(n, dv, dk))
+    o, S1 = oracle.batched.kda_step_heads(q, k, v, a, b, S)
+    for i in range(n):
+        o_i, S_i = oracle.kda_decode_step(q[i], k[i], v[i], a[i], b[i], S[i])
+        assert np.abs(o[i] - o_i).max() < 1e-12 and np.abs(S1[i] - S_i).max() < 1e-12
+
+
+KDA_MUTATIONS = [
+    # decay on the value side instead of the key side
+    ("S = (S * alpha[t][None, :]) @", "S = (S * alpha[t][:, None]) @"),
+    # decay after the delta correction
+    ("S = (S * alpha[t][None, :]) @ (I - beta[t] * np.outer(k, k)) + beta[t] * np.outer(V[t], k)",
+     "S = (S @ (I - beta[t] * np.outer(k, k))) * alpha[t][None, :] + beta[t] * np.outer(V[t], k)"),
+    # no decay at all
+    ("S = (S * alpha[t][None, :]) @", "S = (S * 1.0) @"),
+    # W without the decay factor
+    ("W = Tm @ (bc[:, None] * (Kc * np.exp(g)))", "W = Tm @ (bc[:, None] * Kc)"),
+    # entry state decayed by the first token's factor only
+    ("S = S * np.exp(g[-1])[None, :] +", "S = S * np.exp(g[0])[None, :] +"),
+    # intra-chunk products without their diagonal
+    ("lower = np.tril(np.ones((c, c)))", "lower = np.tril(np.ones((c, c)), k=-1)"),
+    # inter-chunk output without the decay of q
+    ("O[a:b] = (Qc * np.exp(g)) @ S.T + A @ U", "O[a:b] = Qc @ S.T + A @ U"),
+    # beta on the column side of L
+    ("L = bc[:, None] * np.tril(KK, k=-1)", "L = bc[None, :] * np.tril(KK, k=-1)"),
+    # end-state key factors decayed the wrong way
+    ("U.T @ (Kc * np.exp(g[-1][None, :] - g))", "U.T @ (Kc * np.exp(g - g[-1][None, :]))"),
+    # brute force with the diagonal on the other side of the transition
+    ("A = [[[alpha[s][i] *", "A = [[[alpha[s][j] *"),
+]
+
+
+@pytest.mark.parametrize("old,new", KDA_MUTATIONS, ids=[m[1][:40] for m in KDA_MUTATIONS])
+def test_planted_kda_mistake_is_caught(old, new):
+    ns = types.SimpleNamespace(**_mutant(kda_mod, old, new))
+    assert _fails_some_pin(ns, KDA_PINS)
