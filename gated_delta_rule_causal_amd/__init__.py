@@ -8,7 +8,8 @@ runs in the HIP kernels of liblinattn.so; there is no fallback of any kind.
 If the library has not been built, importing the binding functions raises.
 
 Layouts (row-major, contiguous): q, k [B,H,T,dk]; v, o [B,H,T,dv];
-alpha, beta [B,H,T] float32; S [B,H,dv,dk] float32; z [B,H,dk] float32.
+alpha, beta [B,H,T] float32 (KDA: alpha [B,H,T,dk]); S [B,H,dv,dk] float32;
+z [B,H,dk] float32.
 q, k, v are float32 or bfloat16 (all three the same).
 """
 
@@ -19,6 +20,7 @@ __all__ = [
     "lin_attn_prefill",
     "gdn_prefill",
     "gla_prefill",
+    "kda_prefill",
     "gdn_prefill_prep",
     "gdn_prefill_scan",
     "gdn_preprocess",
@@ -38,8 +40,8 @@ _LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 LA_F32, LA_BF16 = 0, 1
 FORMS = {"chunked": 0, "recurrent": 1, "parallel": 2}
-KINDS = {"normalized": 0, "gated_delta": 1, "gated": 2}
-FNS = {"lin_attn_prefill": 0, "gdn_prefill": 1, "decode_step": 2, "gla_prefill": 3}
+KINDS = {"normalized": 0, "gated_delta": 1, "gated": 2, "kda": 3}
+FNS = {"lin_attn_prefill": 0, "gdn_prefill": 1, "decode_step": 2, "gla_prefill": 3, "kda_prefill": 4}
 
 _lib = None
 
@@ -70,6 +72,8 @@ def _load():
     lib.gdn_prefill.restype = I
     lib.gla_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, P, Z, P]
     lib.gla_prefill.restype = I
+    lib.kda_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, Z, P]
+    lib.kda_prefill.restype = I
     lib.gdn_preprocess.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdn_preprocess.restype = I
     lib.gdn_prefill_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P, Z, P]
@@ -243,6 +247,33 @@ def gla_prefill(q, k, v, alpha, S0=None, form="chunked", chunk=64, out=None, S_o
     return out, S_out
 
 
+def kda_prefill(q, k, v, alpha, beta, S0=None, form="recurrent", chunk=64, out=None, S_out=None, want_state=True,
+                stream=None):
+    """Kimi Delta Attention (per-channel decay alpha [B,H,T,dk]) over T tokens;
+    returns (o, S_out)."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(alpha, "alpha", torch.float32, (B, H, T, dk))
+    _check(beta, "beta", torch.float32, (B, H, T))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (B, H, T, dv))
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(S_out, "S_out", torch.float32, (B, H, dv, dk))
+    st = _load().kda_prefill(dt, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                             _ptr(out), _ptr(S_out), FORMS[form], chunk, None, 0, _stream_ptr(stream, q.device))
+    if st != 0:
+        raise LinAttnError(st, "kda_prefill")
+    return out, S_out
+
+
 def gdn_preprocess(x, conv_w, a_logit, b_logit, H, dk, dv, conv_state=None, want_state=True, q=None, k=None, v=None,
                    alpha=None, beta=None, conv_state_out=None, stream=None):
     """Fused pre-operations of a Gated DeltaNet layer; returns
@@ -342,7 +373,7 @@ def lin_attn_decode_step(kind, q, k, v, S, z=None, alpha=None, beta=None, out=No
     _check(v, "v", q.dtype, (N, H, dv))
     _check(S, "S", torch.float32, (N, H, dv, dk))
     _check(z, "z", torch.float32, (N, H, dk))
-    _check(alpha, "alpha", torch.float32, (N, H))
+    _check(alpha, "alpha", torch.float32, (N, H, dk) if kind_i == KINDS["kda"] else (N, H))
     _check(beta, "beta", torch.float32, (N, H))
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)

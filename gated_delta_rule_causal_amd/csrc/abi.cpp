@@ -120,6 +120,9 @@ size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv
             if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
             if (form == LA_FORM_CHUNKED && !la::la_mfma_supported(dtype, dk, dv, chunk)) return bad;
             return form == LA_FORM_CHUNKED ? la::la_mfma_workspace_bytes(B, H, T, dk, dv, chunk) : 0;
+        case LA_FN_KDA_PREFILL:
+            if (form != LA_FORM_RECURRENT) return bad;
+            return 0;
         default:
             return bad;
     }
@@ -325,6 +328,43 @@ la_status gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const v
                                               static_cast<hipStream_t>(stream)));
 }
 
+la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const float* S0, void* o, float* S_out, int form,
+                      int chunk, void* workspace, size_t ws_bytes, void* stream) {
+    (void)chunk;
+    (void)workspace;
+    (void)ws_bytes;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return LA_ERR_ARG;
+    if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (form == LA_FORM_CHUNKED) return LA_ERR_UNSUPPORTED;
+    const size_t heads = static_cast<size_t>(B) * H;
+    if (heads == 0) return LA_OK;
+    const size_t es = io_size(dtype);
+    const size_t nqk = heads * T * dk * es, nv = heads * T * dv * es;
+    const size_t na = heads * T * dk * sizeof(float), nb = heads * T * sizeof(float);
+    const size_t nS = heads * dv * dk * sizeof(float);
+    if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr || alpha == nullptr ||
+                  beta == nullptr))
+        return LA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(alpha),
+                          static_cast<const void*>(beta), static_cast<const void*>(S0),
+                          static_cast<const void*>(S_out)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {{q, nqk}, {k, nqk}, {v, nv}, {alpha, na}, {beta, nb}, {S0, nS}};
+    const Span outs[] = {{o, T > 0 ? nv : 0}, {S_out, nS}};
+    for (const Span& a : outs)
+        for (const Span& b : in) {
+            if (a.p == S_out && b.p == S0 && S_out == S0) continue;
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        }
+    if (overlaps(outs[0], outs[1])) return LA_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) return copy_state(S0, S_out, heads * dv * dk, s);
+    return from_hip(la::launch_recurrent(la::kKda, dtype, static_cast<int>(heads), T, dk, dv, q, k, v, alpha, beta,
+                                         S0, S_out, nullptr, nullptr, o, s));
+}
+
 namespace {
 
 // Shared checks of the two halves of the chunked matrix-core gated-delta path.
@@ -395,13 +435,14 @@ la_status gdn_prefill_scan(int dtype, int B, int H, int T, int dk, int dv, const
 la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv, const void* q,
                                const void* k, const void* v, const float* alpha, const float* beta,
                                float* S, float* z, void* o, void* stream) {
-    if (kind != LA_KIND_NORMALIZED && kind != LA_KIND_GATED_DELTA && kind != LA_KIND_GATED) return LA_ERR_ARG;
+    if (kind != LA_KIND_NORMALIZED && kind != LA_KIND_GATED_DELTA && kind != LA_KIND_GATED && kind != LA_KIND_KDA)
+        return LA_ERR_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
     if (!sizes_ok(N, H, 1) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
     const size_t heads = static_cast<size_t>(N) * H;
     if (heads == 0) return LA_OK;
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || S == nullptr) return LA_ERR_NULL;
-    if (kind == LA_KIND_GATED_DELTA) {
+    if (kind == LA_KIND_GATED_DELTA || kind == LA_KIND_KDA) {
         if (alpha == nullptr || beta == nullptr) return LA_ERR_NULL;
         if (z != nullptr) return LA_ERR_ARG;
     } else if (kind == LA_KIND_GATED) {
@@ -418,13 +459,16 @@ la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv
     const size_t es = io_size(dtype);
     const Span outs[] = {{o, heads * dv * es}, {S, heads * dv * dk * sizeof(float)}, {z, heads * dk * sizeof(float)}};
     const Span in[] = {{q, heads * dk * es}, {k, heads * dk * es}, {v, heads * dv * es},
-                       {alpha, heads * sizeof(float)}, {beta, heads * sizeof(float)}};
+                       {alpha, heads * (kind == LA_KIND_KDA ? dk : 1) * sizeof(float)}, {beta, heads * sizeof(float)}};
     for (const Span& a : outs)
         for (const Span& b : in)
             if (overlaps(a, b)) return LA_ERR_ARG;
     if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return LA_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int k_kind = kind == LA_KIND_GATED_DELTA ? la::kGatedDelta : kind == LA_KIND_GATED ? la::kGated : la::kNormalized;
+    const int k_kind = kind == LA_KIND_GATED_DELTA ? la::kGatedDelta
+                       : kind == LA_KIND_GATED ? la::kGated
+                       : kind == LA_KIND_KDA   ? la::kKda
+                                               : la::kNormalized;
     return from_hip(la::launch_recurrent(k_kind, dtype, static_cast<int>(heads), 1, dk, dv, q, k, v, alpha,
                                          beta, S, S, z, z, o, s));
 }

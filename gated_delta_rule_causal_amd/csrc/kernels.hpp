@@ -9,13 +9,13 @@
 
 namespace la {
 
-enum Kind { kNormalized = 0, kGatedDelta = 1, kGated = 2 };
+enum Kind { kNormalized = 0, kGatedDelta = 1, kGated = 2, kKda = 3 };
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
 // ---- token-by-token recurrence, one block per head (recurrent.hip) --------
 // heads = B*H (or N*H for a decode step); T >= 1.  q,k [heads,T,dk];
-// v,o [heads,T,dv]; alpha [heads,T] (gated kinds), beta [heads,T] (gated
-// delta only); S0/S_out
+// v,o [heads,T,dv]; alpha [heads,T] (gated kinds; [heads,T,dk] per channel
+// for KDA), beta [heads,T] (gated delta and KDA); S0/S_out
 // [heads,dv,dk] (may alias); z0/z_out [heads,dk] (normalized only, may alias).
 hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int dv,
                             const void* q, const void* k, const void* v,

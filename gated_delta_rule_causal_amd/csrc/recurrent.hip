@@ -12,6 +12,11 @@
 //     equation with the input-dependent gate alpha_t in place of gamma:
 //       S_t = alpha_t S_{t-1} + v_t k_t^T,  o_t = S_t q_t, per row
 //       p = s_i.q,  s_i <- alpha s_i + v_i k,  o_i = alpha p + v_i (k.q)
+//   * kKda - same section, Kimi Delta Attention: the scalar gate becomes a
+//     per-channel decay Diag(alpha_t) on the key side of S,
+//     S_t = S_{t-1} Diag(alpha_t)(I - beta_t k_t k_t^T) + beta_t v_t k_t^T; per row
+//       d = s_i * alpha (elementwise),  u = d.k,  p = d.q,  c = beta (v_i - u),
+//       s_i <- d + c k,   o_i = p + c (k.q)
 //   * kNormalized - section "Three forms of one computation", recurrent form:
 //       s_i <- s_i + v_i phi(k),  z <- z + phi(k),  o_i = s_i.phi(q) / z.phi(q)
 // With T = 1 it is the decode step (the state streams from HBM and back,
@@ -112,27 +117,32 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     }
 
     // ---- token inputs, prefetched one token ahead
-    float kn[8], qn[8], vn[R], an = 1.f, bn = 0.f;
+    float kn[8], qn[8], vn[R], an = 1.f, bn = 0.f, avn[8];
     auto fetch = [&](int t) {
         const size_t tk = (static_cast<size_t>(head) * T + t) * DK;
         const size_t tv = (static_cast<size_t>(head) * T + t) * DV;
         load_slice<IO>(k, tk, c0, c1, kn);
         load_slice<IO>(q, tk, c0, c1, qn);
+        if constexpr (KIND == kKda) load_slice<IoF32>(alpha, tk, c0, c1, avn);
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int r = rg + RG * j;
             vn[j] = r < DV ? IO::load(v, tv + r) : 0.f;
         }
-        if constexpr (KIND != kNormalized) an = alpha[static_cast<size_t>(head) * T + t];
-        if constexpr (KIND == kGatedDelta) bn = beta[static_cast<size_t>(head) * T + t];
+        if constexpr (KIND == kGated || KIND == kGatedDelta) an = alpha[static_cast<size_t>(head) * T + t];
+        if constexpr (KIND == kGatedDelta || KIND == kKda) bn = beta[static_cast<size_t>(head) * T + t];
     };
     fetch(0);
 
     const int steps = ONE ? 1 : T;  // ONE: the decode step (T = 1), no prefetch path
     for (int t = 0; t < steps; ++t) {
-        float kc[8], qc[8], vc[R];
+        float kc[8], qc[8], vc[R], ac[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) { kc[e] = kn[e]; qc[e] = qn[e]; }
+        if constexpr (KIND == kKda) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ac[e] = avn[e];
+        }
 #pragma unroll
         for (int j = 0; j < R; ++j) vc[j] = vn[j];
         const float a = an, b = bn;
@@ -176,6 +186,29 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
                 for (int e = 0; e < 8; ++e) s[j][e] = fmaf(a, s[j][e], c * kc[e]);
                 const int r = rg + RG * j;
                 if (li == 0 && r < DV) IO::store(o, to + r, fmaf(a, p, c * kq));
+            }
+        } else if constexpr (KIND == kKda) {
+            (void)a;
+            float kq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kq = fmaf(kc[e], qc[e], kq);
+            kq = group_sum<LPR>(kq);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float u = 0.f, p = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    s[j][e] *= ac[e];
+                    u = fmaf(s[j][e], kc[e], u);
+                    p = fmaf(s[j][e], qc[e], p);
+                }
+                u = group_sum<LPR>(u);
+                p = group_sum<LPR>(p);
+                const float c = b * (vc[j] - u);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[j][e] = fmaf(c, kc[e], s[j][e]);
+                const int r = rg + RG * j;
+                if (li == 0 && r < DV) IO::store(o, to + r, fmaf(c, kq, p));
             }
         } else {
             float fk[8], fq[8];
@@ -293,6 +326,11 @@ hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int d
         return dtype == kBF16
                    ? launch_io<kGated, IoBF16>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr, nullptr, o, stream)
                    : launch_io<kGated, IoF32>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr, nullptr, o, stream);
+    }
+    if (kind == kKda) {
+        return dtype == kBF16
+                   ? launch_io<kKda, IoBF16>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream)
+                   : launch_io<kKda, IoF32>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream);
     }
     if (kind == kGatedDelta) {
         return dtype == kBF16

@@ -59,8 +59,14 @@ enum {
 
 enum { LA_F32 = 0, LA_BF16 = 1 };
 enum { LA_FORM_CHUNKED = 0, LA_FORM_RECURRENT = 1, LA_FORM_PARALLEL = 2 };
-enum { LA_KIND_NORMALIZED = 0, LA_KIND_GATED_DELTA = 1, LA_KIND_GATED = 2 };
-enum { LA_FN_LIN_ATTN_PREFILL = 0, LA_FN_GDN_PREFILL = 1, LA_FN_DECODE_STEP = 2, LA_FN_GLA_PREFILL = 3 };
+enum { LA_KIND_NORMALIZED = 0, LA_KIND_GATED_DELTA = 1, LA_KIND_GATED = 2, LA_KIND_KDA = 3 };
+enum {
+    LA_FN_LIN_ATTN_PREFILL = 0,
+    LA_FN_GDN_PREFILL = 1,
+    LA_FN_DECODE_STEP = 2,
+    LA_FN_GLA_PREFILL = 3,
+    LA_FN_KDA_PREFILL = 4
+};
 
 /*
  * lin_attn_prefill - normalised causal linear attention over T tokens.
@@ -182,6 +188,10 @@ la_status gdn_prefill_scan(int dtype, int B, int H, int T, int dk, int dv,
  *   equation with the input-dependent gate alpha_t):
  *       S <- alpha S + v k^T,   o = S q
  *     alpha [N,H] float32 is required; beta and z must be NULL.
+ *   LA_KIND_KDA (same section as the gated delta kind, Kimi Delta Attention):
+ *       S <- S Diag(alpha) (I - beta k k^T) + beta v k^T,   o = S q
+ *     alpha [N,H,dk] float32 (one decay per key channel) and beta [N,H]
+ *     float32 are required; z must be NULL.
  *   LA_KIND_NORMALIZED (section "Three forms of one computation", recurrent
  *   form, applied to one token):
  *       S <- S + v phi(k)^T,  z <- z + phi(k),  o = S phi(q) / (z . phi(q))
@@ -193,6 +203,32 @@ la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv
                                const void* q, const void* k, const void* v,
                                const float* alpha, const float* beta,
                                float* S, float* z, void* o, void* stream);
+
+/*
+ * kda_prefill - Kimi Delta Attention over T tokens: the gated delta rule with
+ * a per-channel decay.
+ *
+ * Section "Delta rule and Gated DeltaNet": KDA replaces the scalar gate of the
+ * Gated DeltaNet equation by a diagonal matrix Diag(alpha_t), one decay rate
+ * per memory channel.  The diagonal acts on the key side of S (d_v x d_k),
+ * where the scalar stands:
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t                                   (token t included)
+ * alpha [B,H,T,dk] float32 holds decay values per key channel (all equal: the
+ * Gated DeltaNet equation); beta [B,H,T] float32.  S_0 = S0 (zeros when NULL).
+ * form:
+ *   LA_FORM_RECURRENT - token by token, any supported dtype and sizes;
+ *   LA_FORM_CHUNKED   - LA_ERR_UNSUPPORTED (no block form of KDA here).
+ * Outputs o [B,H,T,dv] and, when not NULL, S_out [B,H,dv,dk] (may be the
+ * same pointer as S0; any other overlap is LA_ERR_ARG).  workspace/ws_bytes
+ * are unused (la_workspace_bytes(LA_FN_KDA_PREFILL, ...) is 0).
+ */
+la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const float* S0,
+                      void* o, float* S_out,
+                      int form, int chunk,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * gdn_preprocess - the cheap per-token operations in front of a Gated

@@ -20,6 +20,9 @@ without drawing the rest):
   weights [C, 4] ~ N(0, 0.5^2) float32; gate logits a ~ N(3, 1) and
   b ~ N(0, 1) float32 [B, T, H]; a carried conv state [B, 3, C] ~ N(0, 1)
   rounded to the I/O dtype.
+* KDA: q, k, v, beta as for the gated delta rule; the per-channel decay
+  alpha[t, c] = sigmoid(N(mu_c, 1)) with mu_c spread evenly over [1, 5] across
+  the d_k key channels (fast- and slow-forgetting channels side by side).
 * decode: the carried state S0 ~ N(0, 0.02^2) float32 per head; the per-step
   token inputs come from a pool of ``pool`` draws (step s uses pool entry
   s mod pool), generated with ``default_rng([seed, stream, 1000 + entry])``.
@@ -46,6 +49,11 @@ WORKLOADS = {
     # without beta, at the gated-delta prefill shape
     "gla_bf16_2x16x8192": dict(seed=1006, kind="gla", B=2, H=16, T=8192, dk=128, dv=128,
                                dtype="bf16", chunk=64),
+    # Kimi Delta Attention (per-channel decay) at the gated-delta prefill
+    # shape, and its decode at the decode shape
+    "kda_bf16_2x16x8192": dict(seed=1008, kind="kda", B=2, H=16, T=8192, dk=128, dv=128, dtype="bf16"),
+    "kda_decode_256x32": dict(seed=1009, kind="kda_decode", N=256, H=32, dk=128, dv=128, dtype="bf16",
+                              steps=1000, state_std=0.02),
     # pre-operations of a Gated DeltaNet layer in front of the 2 x 16 x 8192
     # prefill: x [2, 8192, 16 * (128 + 128 + 128)]
     "preops_bf16_2x16x8192": dict(seed=1007, kind="preops", B=2, H=16, T=8192, dk=128, dv=128,
@@ -186,3 +194,35 @@ def preops_batch(seed, B, T, H, dk, dv, dtype, w_std=0.5):
 def conv_state_batch(seed, B, H, dk, dv, dtype):
     """A carried conv state [B, 3, H*(2dk+dv)] rounded to dtype."""
     return round_io(_normal(seed, STREAM_CONV_STATE, (), (B, 3, H * (2 * dk + dv))), dtype)
+
+
+def _channel_decay(z, dk):
+    """sigmoid(z + mu_c), mu_c evenly spread over [1, 5] along the last axis."""
+    mu = np.linspace(1.0, 5.0, dk, dtype=np.float32)
+    return _sigmoid(z + mu)
+
+
+def kda_head(seed, b, h, T, dk, dv, dtype):
+    """q, k (unit rows), v, per-channel alpha [T, dk], beta [T] for one head."""
+    q, k, v, _, beta = gdn_head(seed, b, h, T, dk, dv, dtype)
+    alpha = _channel_decay(_normal(seed, STREAM_ALPHA, (b, h, 1), (T, dk)), dk)
+    return q, k, v, alpha, beta
+
+
+def kda_batch(seed, B, H, T, dk, dv, dtype):
+    q = np.empty((B, H, T, dk), np.float32)
+    k = np.empty((B, H, T, dk), np.float32)
+    v = np.empty((B, H, T, dv), np.float32)
+    a = np.empty((B, H, T, dk), np.float32)
+    be = np.empty((B, H, T), np.float32)
+    for b in range(B):
+        for h in range(H):
+            q[b, h], k[b, h], v[b, h], a[b, h], be[b, h] = kda_head(seed, b, h, T, dk, dv, dtype)
+    return q, k, v, a, be
+
+
+def kda_decode_token_inputs(seed, N, H, dk, dv, dtype, entry):
+    """One pool entry of KDA decode inputs: q, k (unit), v [N,H,d], alpha [N,H,dk], beta [N,H]."""
+    q, k, v, _, beta = decode_token_inputs(seed, N, H, dk, dv, dtype, entry)
+    alpha = _channel_decay(_normal(seed, STREAM_ALPHA, (3000 + entry,), (N, H, dk)), dk)
+    return q, k, v, alpha, beta

@@ -48,7 +48,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gla_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
-                            "gdn_preprocess", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
+                            "gdn_preprocess", "kda_prefill", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -126,7 +126,7 @@ def test_gdn_validation(lib):
 
 
 def test_decode_validation(lib):
-    assert decode(lib, kind=3) == LA_ERR_ARG
+    assert decode(lib, kind=9) == LA_ERR_ARG
     assert decode(lib, dtype=9) == LA_ERR_DTYPE
     assert decode(lib, dk=100) == LA_ERR_SHAPE
     assert decode(lib, S=None) == LA_ERR_NULL
@@ -263,3 +263,32 @@ def test_preprocess_validation(lib):
     assert pre(al=4) == LA_ERR_ARG                         # alpha on top of b_logit
     assert pre(B=0) == LA_OK                               # empty batch: nothing to do
     assert pre(T=0, st=10) == LA_OK                        # no tokens and no state to write
+
+
+def test_kda_validation(lib):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    KDA = 4
+
+    def kda(dtype=BF16, T=100, dk=128, dv=128, q=1, k=2, v=3, a=5, b=6, S0=None, o=4, S_out=None, form=RECURRENT):
+        return lib.kda_prefill(dtype, 1, 2, T, dk, dv, f(q), f(k), f(v), f(a), f(b), f(S0), f(o), f(S_out), form, 64,
+                               None, 0, None)
+
+    assert kda(a=None) == LA_ERR_NULL
+    assert kda(b=None) == LA_ERR_NULL
+    assert kda(form=PARALLEL) == LA_ERR_ARG
+    assert kda(form=CHUNKED) == LA_ERR_UNSUPPORTED
+    assert kda(dk=48) == LA_ERR_SHAPE
+    assert kda(o=5) == LA_ERR_ARG                          # output on top of alpha
+    assert kda(S0=7, S_out=ctypes.c_void_p(BASE + 7 * GiB + 32)) == LA_ERR_ARG
+    assert kda(q=ctypes.c_void_p(BASE + GiB + 4)) == LA_ERR_ALIGN
+    assert lib.la_workspace_bytes(KDA, BF16, 1, 2, 100, 128, 128, RECURRENT, 0) == 0
+    assert lib.la_workspace_bytes(KDA, BF16, 1, 2, 100, 128, 128, CHUNKED, 64) == ctypes.c_size_t(-1).value
+    # decode: KDA needs alpha (per channel) and beta, no z
+    dec = lambda a=5, b=6, z=None: lib.lin_attn_decode_step(3, BF16, 4, 2, 128, 128, P(1), P(2), P(3), f(a), f(b),
+                                                            P(7), f(z), P(4), None)
+    assert dec(a=None) == LA_ERR_NULL
+    assert dec(b=None) == LA_ERR_NULL
+    assert dec(z=8) == LA_ERR_ARG
+    # alpha spans N*H*dk floats: an output placed inside it is an overlap
+    assert lib.lin_attn_decode_step(3, BF16, 4, 2, 128, 128, P(1), P(2), P(3), P(5), P(6), P(7), None,
+                                    ctypes.c_void_p(BASE + 5 * GiB + 2048), None) == LA_ERR_ARG
