@@ -46,6 +46,7 @@ from .kda import (
 )
 from . import batched
 from . import preops
+from . import varlen
 
 __all__ = [
     "phi",
@@ -66,4 +67,5 @@ __all__ = [
     "kda_bruteforce_states",
     "batched",
     "preops",
+    "varlen",
 ]

@@ -671,3 +671,70 @@ KDA_MUTATIONS = [
 def test_planted_kda_mistake_is_caught(old, new):
     ns = types.SimpleNamespace(**_mutant(kda_mod, old, new))
     assert _fails_some_pin(ns, KDA_PINS)
+
+
+# ------------------------------------------------- packed batches, snapshots
+from oracle import varlen as vl_mod
+
+
+def pin_varlen(ns):
+    """Packed sequences are independent recurrences on their own slices (the
+    separately pinned gdn_recurrent); a snapshot is the final state of the
+    recurrence over that prefix, and resuming from it reproduces the rest of
+    the sequence."""
+    rng = np.random.default_rng(51)
+    H, dk, dv, iv = 2, 4, 3, 4
+    lens = [9, 0, 4, 13, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    Tt = int(cu[-1])
+    q, k = rng.normal(size=(H, Tt, dk)), rng.normal(size=(H, Tt, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(size=(H, Tt, dv))
+    a = 1 / (1 + np.exp(-rng.normal(2, 1, (H, Tt))))
+    b = 1 / (1 + np.exp(-rng.normal(size=(H, Tt))))
+    S0 = rng.normal(size=(len(lens), H, dv, dk))
+    o, S, snaps = ns.gdn_varlen(q, k, v, a, b, cu, S0, snap_interval=iv)
+    assert ns.snapshot_count(cu, iv) == sum(L // iv for L in lens) == snaps.shape[0]
+    j = 0
+    for n, L in enumerate(lens):
+        s, e = cu[n], cu[n + 1]
+        for h in range(H):
+            o_ref, S_ref = oracle.gdn_recurrent(q[h, s:e], k[h, s:e], v[h, s:e], a[h, s:e], b[h, s:e], S0[n, h])
+            assert np.abs(o[h, s:e] - o_ref).max(initial=0) < 1e-12
+            assert np.abs(S[n, h] - (S0[n, h] if L == 0 else S_ref)).max() < 1e-12
+        for p in range(iv, L + 1, iv):
+            for h in range(H):
+                _, S_p = oracle.gdn_recurrent(q[h, s:s + p], k[h, s:s + p], v[h, s:s + p], a[h, s:s + p],
+                                              b[h, s:s + p], S0[n, h])
+                assert np.abs(snaps[j, h] - S_p).max() < 1e-12
+                # prefix caching: the tail from the snapshot gives the same outputs
+                o_t, S_t = oracle.gdn_recurrent(q[h, s + p:e], k[h, s + p:e], v[h, s + p:e], a[h, s + p:e],
+                                                b[h, s + p:e], snaps[j, h])
+                assert np.abs(o_t - o[h, s + p:e]).max(initial=0) < 1e-12
+                assert np.abs(S_t - S[n, h]).max() < 1e-12
+            j += 1
+    # without an initial state every sequence starts from zero; without snapshots none are returned
+    o0, S0z, sn0 = ns.gdn_varlen(q, k, v, a, b, cu)
+    assert sn0.shape[0] == 0 and np.all(S0z[1] == 0)
+    o_ref, _ = oracle.gdn_recurrent(q[0, :9], k[0, :9], v[0, :9], a[0, :9], b[0, :9])
+    assert np.abs(o0[0, :9] - o_ref).max() < 1e-12
+
+
+def test_varlen_pin():
+    pin_varlen(vl_mod)
+
+
+VARLEN_MUTATIONS = [
+    ("cuts = [a + p for p in range(snap_interval, b - a + 1, snap_interval)]",
+     "cuts = [a + p for p in range(snap_interval, b - a, snap_interval)]"),
+    ("S = None if S0 is None else np.asarray(S0[n, h], dtype=np.float64)", "S = None"),
+    ("return sum((cu[n + 1] - cu[n]) // snap_interval for n in range(len(cu) - 1))",
+     "return (cu[-1] - cu[0]) // snap_interval"),
+    ("states.append(S.copy())", "states.append(np.zeros_like(S))"),
+]
+
+
+@pytest.mark.parametrize("old,new", VARLEN_MUTATIONS, ids=[m[1][:40] for m in VARLEN_MUTATIONS])
+def test_planted_varlen_mistake_is_caught(old, new):
+    ns = types.SimpleNamespace(**_mutant(vl_mod, old, new))
+    assert _fails_some_pin(ns, [pin_varlen])
