@@ -56,6 +56,9 @@ la_status copy_state(const float* src, float* dst, size_t n, hipStream_t s) {
     return from_hip(hipGetLastError());
 }
 
+// seg_base and snap_base of a packed batch, [N+1] ints each, rounded to 256 bytes
+size_t varlen_table_bytes(int N) { return N > 0 ? (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256 : 0; }
+
 size_t la_prefill_ws(int dtype, int B, int H, int T, int dk, int dv, int form, int chunk) {
     if (form == LA_FORM_CHUNKED && la::la_mfma_supported(dtype, dk, dv, chunk))
         return la::la_mfma_workspace_bytes(B, H, T, dk, dv, chunk);
@@ -123,6 +126,10 @@ size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv
         case LA_FN_KDA_PREFILL:
             if (form != LA_FORM_RECURRENT) return bad;
             return 0;
+        case LA_FN_GDN_VARLEN:   // B = number of sequences, T = total tokens
+            if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
+            if (form == LA_FORM_CHUNKED && !la::gdn_mfma_supported(dtype, dk, dv, chunk)) return bad;
+            return form == LA_FORM_CHUNKED ? la::gdn_mfma_varlen_workspace_bytes(B, H, T) : varlen_table_bytes(B);
         default:
             return bad;
     }
@@ -326,6 +333,74 @@ la_status gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const v
     return from_hip(la::launch_gdn_preprocess(dtype, B, T, H, dk, dv, x, conv_w, a_logit, b_logit, conv_state,
                                               conv_state_out, q, k, v, alpha, beta,
                                               static_cast<hipStream_t>(stream)));
+}
+
+la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int dv, const int* cu_seqlens,
+                             const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                             const float* S0, void* o, float* S_out, int snap_interval, int snap_count,
+                             float* S_snap, int form, int chunk, void* workspace, size_t ws_bytes, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return LA_ERR_ARG;
+    if (!sizes_ok(N, H, T_total) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (static_cast<long long>(T_total) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
+    if (snap_interval < 0 || snap_count < 0) return LA_ERR_SHAPE;
+    if (form == LA_FORM_CHUNKED) {
+        if (!valid_chunk(chunk)) return LA_ERR_SHAPE;
+        if (!la::gdn_mfma_supported(dtype, dk, dv, chunk)) return LA_ERR_UNSUPPORTED;
+        if (snap_interval % chunk != 0) return LA_ERR_SHAPE;
+    }
+    if (N == 0 || H == 0) return LA_OK;
+    if (cu_seqlens == nullptr) return LA_ERR_NULL;
+    if (T_total > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr || alpha == nullptr ||
+                        beta == nullptr))
+        return LA_ERR_NULL;
+    if (snap_interval > 0 && snap_count > 0 && S_snap == nullptr) return LA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return LA_ERR_ALIGN;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(alpha),
+                          static_cast<const void*>(beta), static_cast<const void*>(S0),
+                          static_cast<const void*>(S_out), static_cast<const void*>(S_snap),
+                          static_cast<const void*>(workspace)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const size_t es = io_size(dtype);
+    const size_t rows = static_cast<size_t>(H) * T_total;
+    const size_t nS = static_cast<size_t>(N) * H * dv * dk * sizeof(float);
+    const size_t nsnap = snap_interval > 0 ? static_cast<size_t>(snap_count) * H * dv * dk * sizeof(float) : 0;
+    const Span in[] = {{q, rows * dk * es}, {k, rows * dk * es}, {v, rows * dv * es}, {alpha, rows * sizeof(float)},
+                       {beta, rows * sizeof(float)}, {S0, nS}, {cu_seqlens, (static_cast<size_t>(N) + 1) * sizeof(int)}};
+    const Span outs[] = {{o, rows * dv * es}, {S_out, nS}, {S_snap, nsnap}};
+    for (const Span& a : outs)
+        for (const Span& b : in) {
+            if (a.p == S_out && b.p == S0 && S_out == S0) continue;
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        }
+    if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return LA_ERR_ARG;
+    const size_t need = form == LA_FORM_CHUNKED ? la::gdn_mfma_varlen_workspace_bytes(N, H, T_total)
+                                                : varlen_table_bytes(N);
+    if (workspace == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
+    {
+        const Span w{workspace, need};
+        for (const Span& b : in)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+        for (const Span& b : outs)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (form == LA_FORM_CHUNKED)
+        return from_hip(la::launch_gdn_mfma_varlen(N, H, T_total, cu_seqlens, q, k, v, alpha, beta, S0, o, S_out,
+                                                   S_snap ? snap_interval : 0, snap_count, S_snap, workspace, s));
+    int* tab = static_cast<int*>(workspace);
+    la::Packed pk;
+    pk.cu = cu_seqlens;
+    pk.snap_base = tab + (N + 1);
+    pk.H = H;
+    pk.Ttot = T_total;
+    pk.snap = S_snap ? snap_interval : 0;
+    pk.snap_cap = snap_count;
+    pk.S_snap = S_snap;
+    const hipError_t e = la::launch_varlen_table(N, T_total, 1, pk.snap, cu_seqlens, tab, s);
+    if (e != hipSuccess) return LA_ERR_HIP;
+    return from_hip(la::launch_recurrent(la::kGatedDelta, dtype, N * H, T_total, dk, dv, q, k, v, alpha, beta, S0,
+                                         S_out, nullptr, nullptr, o, s, pk));
 }
 
 la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k, const void* v,

@@ -684,24 +684,98 @@ __device__ __forceinline__ void store_state_rowmajor(const f32x4 (&P)[NT][8], fl
 // entering state P_s and N_s in the state's row layout ([value channel][d]),
 // and M_s row-major ([d][j]).
 constexpr size_t kMat = static_cast<size_t>(D) * D;
-__device__ __forceinline__ size_t ws_P(int bh, int G, int s) { return (static_cast<size_t>(bh) * G + s) * 3 * kMat; }
-__device__ __forceinline__ size_t ws_N(int bh, int G, int s) { return ws_P(bh, G, s) + kMat; }
-__device__ __forceinline__ size_t ws_M(int bh, int G, int s) { return ws_P(bh, G, s) + 2 * kMat; }
+__device__ __forceinline__ size_t ws_P(size_t slot) { return slot * 3 * kMat; }
+__device__ __forceinline__ size_t ws_N(size_t slot) { return ws_P(slot) + kMat; }
+__device__ __forceinline__ size_t ws_M(size_t slot) { return ws_P(slot) + 2 * kMat; }
+
+// ============================================================ work items
+// Every (sequence, head) runs as G segments of SEGC chunks; a map or output
+// workgroup takes one segment.  Two layouts:
+// * uniform (cu == nullptr): BH = B*H sequences of T tokens, rows [BH][T][d],
+//   gates [BH][T], states [BH][d][d], G segments each;
+// * packed: N sequences, sequence n = tokens cu[n] .. cu[n+1] of every head's
+//   rows [H][Ttot][d] (gates [H][Ttot]), states [N][H][d][d]; the segment
+//   count varies per sequence, seg_base[n] numbers the segments of all
+//   sequences in order (built on the device), and the workspace slots of head
+//   h start at h * Gcap (Gcap bounds the total segment count).  The state
+//   after every snap tokens of a sequence (snap a multiple of C, 0 for none)
+//   is written to S_snap[snap_base[n] + j][h] for the first snap_cap slots.
+struct Geo {
+    int BH, T, G, SEGC;
+    const int* cu;
+    const int* seg_base;
+    const int* snap_base;
+    int N, H, Ttot, Gcap;
+    int snap, snap_cap;
+    float* S_snap;
+};
+
+struct Item {
+    size_t head_tok;  // row of the sequence's first token (this head) in q/k/v/o and alpha/beta
+    int len;          // tokens of the sequence
+    int seg, G;       // this segment and the sequence's segment count
+    int n0, n1;       // chunks of the segment
+    size_t slot0;     // workspace slot of the sequence's segment 0
+    size_t state;     // index of the sequence's state in S0 / S_out
+    int snap0, h;     // first snapshot of the sequence, head
+};
+
+__device__ __forceinline__ int clamp_tok(int t, int Ttot) { return t < 0 ? 0 : t > Ttot ? Ttot : t; }
+
+// The work item of workgroup blk (maps: the last segment of a sequence has no
+// map and its workgroup has nothing to do).  False: nothing to do.
+__device__ __forceinline__ bool find_item(const Geo& g, int blk, bool maps, Item& it) {
+    if (g.cu == nullptr) {
+        const int per = maps ? g.G - 1 : g.G;
+        const int bh = blk / per;
+        if (bh >= g.BH) return false;
+        it.seg = blk - bh * per;
+        it.G = g.G;
+        it.len = g.T;
+        it.head_tok = static_cast<size_t>(bh) * g.T;
+        it.slot0 = static_cast<size_t>(bh) * g.G;
+        it.state = bh;
+        it.snap0 = 0;
+        it.h = 0;
+    } else {
+        const int h = blk % g.H, gs = blk / g.H;
+        if (gs >= g.seg_base[g.N]) return false;
+        int lo = 0, hi = g.N;  // seg_base[lo] <= gs < seg_base[hi]; every sequence has a segment
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (g.seg_base[mid] <= gs) lo = mid; else hi = mid;
+        }
+        it.seg = gs - g.seg_base[lo];
+        it.G = g.seg_base[lo + 1] - g.seg_base[lo];
+        if (maps && it.seg == it.G - 1) return false;
+        // a table that is not non-decreasing can ask for more segments than
+        // the workspace holds: such sequences are skipped, never overrun
+        if (g.seg_base[lo + 1] > g.Gcap) return false;
+        const int t0 = clamp_tok(g.cu[lo], g.Ttot), t1 = clamp_tok(g.cu[lo + 1], g.Ttot);
+        it.len = t1 > t0 ? t1 - t0 : 0;
+        it.head_tok = static_cast<size_t>(h) * g.Ttot + t0;
+        it.slot0 = static_cast<size_t>(h) * g.Gcap + g.seg_base[lo];
+        it.state = static_cast<size_t>(lo) * g.H + h;
+        it.snap0 = g.snap_base ? g.snap_base[lo] : 0;
+        it.h = h;
+    }
+    it.n0 = it.seg * g.SEGC;
+    it.n1 = min((it.len + C - 1) / C, it.n0 + g.SEGC);
+    return true;
+}
 
 // ============================================================ segment maps
-__global__ __launch_bounds__(kThreads) void gdn_map_kernel(int BH, int T, int NC, int G, int SEGC,
-                                                           const u16* __restrict__ k, const u16* __restrict__ v,
-                                                           const float* __restrict__ alpha,
+__global__ __launch_bounds__(kThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
+                                                           const u16* __restrict__ v, const float* __restrict__ alpha,
                                                            const float* __restrict__ beta, float* __restrict__ ws) {
     __shared__ __attribute__((aligned(16))) ChunkTiles sm;
-    const int bh = blockIdx.x / (G - 1);
-    const int seg = blockIdx.x - bh * (G - 1);
-    if (bh >= BH) return;
+    Item it;
+    if (!find_item(geo, blockIdx.x, true, it)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int n0 = seg * SEGC, n1 = min(NC, n0 + SEGC);
-    const size_t head_tok = static_cast<size_t>(bh) * T;
+    const int n0 = it.n0, n1 = it.n1, T = it.len;
+    const size_t head_tok = it.head_tok;
     // waves 0-3: N columns (value channels 32w..32w+31), start 0;
     // waves 4-7: M columns j = 32(w-4)..+31, start = identity
     const bool npart = w < 4;
@@ -760,9 +834,9 @@ __global__ __launch_bounds__(kThreads) void gdn_map_kernel(int BH, int T, int NC
         if (n + 1 < n1) step1(n + 1);
     }
     if (npart)
-        store_state<2>(P, ws + ws_N(bh, G, seg), col0, lane);
+        store_state<2>(P, ws + ws_N(it.slot0 + it.seg), col0, lane);
     else
-        store_state_rowmajor<2>(P, ws + ws_M(bh, G, seg), col0, lane);
+        store_state_rowmajor<2>(P, ws + ws_M(it.slot0 + it.seg), col0, lane);
 }
 
 // ============================================================ combine
@@ -783,26 +857,41 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
     lo = pack8(l[0], l[1], l[2], l[3], l[4], l[5], l[6], l[7]);
 }
 
-__global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, int G, const float* S0,
+__global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(Geo geo, const float* S0,
                                                                       float* __restrict__ ws) {
     __shared__ __attribute__((aligned(16))) float Ps[2][16][D + 4];  // P_s by parity: [value channel][j]
     // Workgroups are dealt to the 8 XCDs round-robin (each XCD has its own
-    // L2): the 8 column tiles of one head take block indices 8 apart, so all
-    // of them land on one XCD and share that head's maps in its L2.
+    // L2): the 8 column tiles of one (sequence, head) take block indices 8
+    // apart, so all of them land on one XCD and share its maps in that L2.
     const int i = blockIdx.x;
-    const int bh = (i >> 6) * 8 + (i & 7);
+    const int bh = (i >> 6) * 8 + (i & 7);   // (sequence, head) pair
     const int tile = (i >> 3) & 7;
-    if (bh >= BH) return;
+    int G;
+    size_t slot0, state;
+    if (geo.cu == nullptr) {
+        if (bh >= geo.BH) return;
+        G = geo.G;
+        slot0 = static_cast<size_t>(bh) * G;
+        state = bh;
+    } else {
+        if (bh >= geo.N * geo.H) return;
+        const int n = bh / geo.H, h = bh % geo.H;
+        G = geo.seg_base[n + 1] - geo.seg_base[n];
+        if (geo.seg_base[n + 1] > geo.Gcap) return;   // (see find_item)
+        slot0 = static_cast<size_t>(h) * geo.Gcap + geo.seg_base[n];
+        state = bh;
+    }
+    if (G < 2) return;   // a single segment starts from S0 itself
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
     // P_0 = S0 (zeros when absent) for value channels 16 tile .. +15
     for (int e = tid; e < 16 * D / 4; e += kCombineThreads) {
         const int rl = e / (D / 4), d4 = (e % (D / 4)) * 4;
         const size_t off = static_cast<size_t>(16 * tile + rl) * D + d4;
-        const float4 x = S0 ? *reinterpret_cast<const float4*>(S0 + static_cast<size_t>(bh) * kMat + off)
+        const float4 x = S0 ? *reinterpret_cast<const float4*>(S0 + state * kMat + off)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(&Ps[0][rl][d4]) = x;
-        *reinterpret_cast<float4*>(ws + ws_P(bh, G, 0) + off) = x;
+        *reinterpret_cast<float4*>(ws + ws_P(slot0) + off) = x;
     }
     // The maps (M_s, N_s) do not depend on the states: those of step s+1 are
     // loaded while step s runs, and M is split into bf16 pairs ahead of use.
@@ -810,7 +899,7 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, in
     // k-step) and rows d = 32w + 16mt + 4g .. +3 of column v = r of N.
     float4 mraw[2][4][2], nraw[2];
     auto load_maps = [&](int st) {
-        const float* M = ws + ws_M(bh, G, st);
+        const float* M = ws + ws_M(slot0 + st);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -819,7 +908,7 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, in
                 mraw[mt][ks][0] = *reinterpret_cast<const float4*>(mrow);
                 mraw[mt][ks][1] = *reinterpret_cast<const float4*>(mrow + 4);
             }
-            nraw[mt] = *reinterpret_cast<const float4*>(ws + ws_N(bh, G, st) + static_cast<size_t>(16 * tile + r) * D +
+            nraw[mt] = *reinterpret_cast<const float4*>(ws + ws_N(slot0 + st) + static_cast<size_t>(16 * tile + r) * D +
                                                         32 * w + 16 * mt + 4 * g);
         }
     };
@@ -837,10 +926,8 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, in
             nv[mt] = f32x4{nraw[mt].x, nraw[mt].y, nraw[mt].z, nraw[mt].w};
         }
     };
-    if (G > 1) {
-        load_maps(0);
-        split_maps();
-    }
+    load_maps(0);
+    split_maps();
     for (int s = 0; s + 1 < G; ++s) {
         if (s + 2 < G) load_maps(s + 1);
         lds_barrier();
@@ -863,27 +950,35 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(int BH, in
             const int d0 = 32 * w + 16 * mt + 4 * g;
             const float4 x = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
             *reinterpret_cast<float4*>(&Ps[cur ^ 1][r][d0]) = x;
-            *reinterpret_cast<float4*>(ws + ws_P(bh, G, s + 1) + static_cast<size_t>(16 * tile + r) * D + d0) = x;
+            *reinterpret_cast<float4*>(ws + ws_P(slot0 + s + 1) + static_cast<size_t>(16 * tile + r) * D + d0) = x;
         }
         if (s + 2 < G) split_maps();
     }
 }
 
 // ============================================================ outputs
-__global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC, int G, int SEGC,
-                                                           const u16* __restrict__ q, const u16* __restrict__ k,
-                                                           const u16* __restrict__ v, const float* __restrict__ alpha,
+__global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* __restrict__ q,
+                                                           const u16* __restrict__ k, const u16* __restrict__ v,
+                                                           const float* __restrict__ alpha,
                                                            const float* __restrict__ beta, const float* S0,
                                                            const float* __restrict__ ws, u16* __restrict__ o,
                                                            float* S_out) {
     __shared__ __attribute__((aligned(16))) ChunkTiles sm;
-    const int bh = blockIdx.x / G;
-    const int seg = blockIdx.x - bh * G;
-    if (bh >= BH) return;
+    Item it;
+    if (!find_item(geo, blockIdx.x, false, it)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branch below is scalar
-    const int n0 = seg * SEGC, n1 = min(NC, n0 + SEGC);
-    const size_t head_tok = static_cast<size_t>(bh) * T;
+    const int n0 = it.n0, n1 = it.n1, T = it.len;
+    const size_t head_tok = it.head_tok;
+    const float* S0h = S0 ? S0 + it.state * kMat : nullptr;
+    if (n0 >= n1) {   // an empty sequence: its state passes through
+        if (w < 4 && S_out) {
+            f32x4 P[2][8];
+            load_state<2>(P, S0h, 32 * w, lane);
+            store_state<2>(P, S_out + it.state * kMat, 32 * w, lane);
+        }
+        return;
+    }
     // Waves 0-3 carry the state (32 value channels each); waves 4-7 stage the
     // chunks and hold the raw inputs of the next one.  Per chunk n, after
     // barrier A: step 2 (all), B3, step 4 (all), B4, the first half of the scan
@@ -900,8 +995,7 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
         f32x4 P[2][8];
         // entering state: S0 itself when the sequence is one segment, else the
         // combined state (segment 0 included, so S_out may alias S0)
-        load_state<2>(P, G == 1 ? (S0 ? S0 + static_cast<size_t>(bh) * kMat : nullptr) : ws + ws_P(bh, G, seg),
-                      col0, lane);
+        load_state<2>(P, it.G == 1 ? S0h : ws + ws_P(it.slot0 + it.seg), col0, lane);
         lds_barrier();  // chunk n0 staged
         lds_barrier();  // step 1 of chunk n0 done
         for (int n = n0; n < n1; ++n) {
@@ -922,8 +1016,15 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(int BH, int T, int NC
             lds_barrier();  // B5
             scan_out<2>(sm, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0));
             scan_update<2>(sm, gt, P, Ub, lane);
+            // snapshot of the state after chunk n (packed batches)
+            const int end = (n + 1) * C;
+            if (geo.snap > 0 && end <= T && end % geo.snap == 0) {
+                const int j = it.snap0 + end / geo.snap - 1;
+                if (j < geo.snap_cap)
+                    store_state<2>(P, geo.S_snap + (static_cast<size_t>(j) * geo.H + it.h) * kMat, col0, lane);
+            }
         }
-        if (seg == G - 1 && S_out) store_state<2>(P, S_out + static_cast<size_t>(bh) * kMat, col0, lane);
+        if (it.seg == it.G - 1 && S_out) store_state<2>(P, S_out + it.state * kMat, col0, lane);
     } else {
         const int ptid = tid - kThreads / 2;
         const int u = w - 4;
@@ -987,6 +1088,120 @@ Plan make_plan(int BH, int T) {
     return p;
 }
 
+Geo uniform_geo(int BH, int T) {
+    const Plan p = make_plan(BH, T);
+    Geo g{};
+    g.BH = BH;
+    g.T = T;
+    g.G = p.G;
+    g.SEGC = p.SEGC;
+    return g;
+}
+
+// ---- packed batches: plan on the host from N and Ttot only (the sequence
+// lengths stay on the device).  A sequence of NC chunks gets ceil(NC/SEGC)
+// segments (one when empty); SEGC is chosen so that about kTargetBlocks
+// (segment, head) items exist, and Gcap bounds the total segment count:
+// sum ceil(NC_n / SEGC) <= (Ttot / C + N) / SEGC + N.
+struct VarPlan {
+    int SEGC, Gcap;
+    size_t table_bytes;   // seg_base and snap_base, [N+1] each, rounded to 256 bytes
+};
+
+VarPlan make_var_plan(int N, int H, int Ttot) {
+    VarPlan p;
+    const long long chunks = static_cast<long long>(Ttot) / C + N;   // >= sum of per-sequence chunk counts
+    long long segc = (chunks * H + kTargetBlocks - 1) / kTargetBlocks;
+    if (segc < 1) segc = 1;
+    p.SEGC = static_cast<int>(segc);
+    p.Gcap = static_cast<int>(chunks / segc + N + 1);
+    p.table_bytes = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    return p;
+}
+
+// seg_base and snap_base by a block-wide exclusive scan over the sequences.
+constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, int Ttot, int SEGC, int snap,
+                                                                       const int* __restrict__ cu, int* seg_base,
+                                                                       int* snap_base) {
+    __shared__ int part[2][kPlanThreads];
+    const int tid = threadIdx.x;
+    const int per = (N + kPlanThreads - 1) / kPlanThreads;
+    const int a = min(N, tid * per), b = min(N, a + per);
+    auto counts = [&](int n, int& segs, int& snaps) {
+        const int t0 = clamp_tok(cu[n], Ttot), t1 = clamp_tok(cu[n + 1], Ttot);
+        const int len = t1 > t0 ? t1 - t0 : 0;
+        const int nc = (len + C - 1) / C;
+        segs = nc > 0 ? (nc + SEGC - 1) / SEGC : 1;
+        snaps = snap > 0 ? len / snap : 0;
+    };
+    int ss = 0, sn = 0;
+    for (int n = a; n < b; ++n) {
+        int g, z;
+        counts(n, g, z);
+        ss += g;
+        sn += z;
+    }
+    part[0][tid] = ss;
+    part[1][tid] = sn;
+    __syncthreads();
+    // inclusive scan of the per-thread sums (Hillis-Steele)
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int x0 = tid >= off ? part[0][tid - off] : 0;
+        const int x1 = tid >= off ? part[1][tid - off] : 0;
+        __syncthreads();
+        part[0][tid] += x0;
+        part[1][tid] += x1;
+        __syncthreads();
+    }
+    int gb = part[0][tid] - ss, zb = part[1][tid] - sn;   // exclusive
+    for (int n = a; n < b; ++n) {
+        seg_base[n] = gb;
+        snap_base[n] = zb;
+        int g, z;
+        counts(n, g, z);
+        gb += g;
+        zb += z;
+    }
+    if (tid == kPlanThreads - 1) {
+        seg_base[N] = part[0][tid];
+        snap_base[N] = part[1][tid];
+    }
+}
+
+hipError_t launch_all(const Geo& g, int map_blocks, int combine_items, int out_blocks, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
+                      float* ws, bool prep, bool scan, hipStream_t stream) {
+    if (prep && map_blocks > 0) {
+        hipLaunchKernelGGL(gdn_map_kernel, dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream, g,
+                           static_cast<const u16*>(k), static_cast<const u16*>(v), alpha, beta, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!scan) return hipSuccess;
+    if (combine_items > 0) {
+        hipLaunchKernelGGL(gdn_combine_kernel, dim3(static_cast<unsigned>((combine_items + 7) / 8) * 64),
+                           dim3(kCombineThreads), 0, stream, g, S0, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(gdn_out_kernel, dim3(static_cast<unsigned>(out_blocks)), dim3(kThreads), 0, stream, g,
+                       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), alpha, beta,
+                       S0, ws, static_cast<u16*>(o), S_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_uniform(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
+                          const float* beta, const float* S0, void* o, float* S_out, void* workspace, bool prep,
+                          bool scan, hipStream_t stream) {
+    const int BH = B * H;
+    if (BH <= 0 || T <= 0) return hipSuccess;
+    const Geo g = uniform_geo(BH, T);
+    const bool multi = g.G > 1;
+    return launch_all(g, multi ? BH * (g.G - 1) : 0, multi ? BH : 0, BH * g.G, q, k, v, alpha, beta, S0, o, S_out,
+                      static_cast<float*>(workspace), prep, scan, stream);
+}
+
 }  // namespace
 
 bool gdn_mfma_supported(int dtype, int dk, int dv, int chunk) {
@@ -1001,44 +1216,59 @@ size_t gdn_mfma_workspace_bytes(int B, int H, int T, int, int, int) {
     return static_cast<size_t>(BH) * p.G * 3 * kMat * sizeof(float);
 }
 
-hipError_t launch_gdn_mfma_prep(int B, int H, int T, const void*, const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_mfma_prep(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
                                 const float* beta, void* workspace, hipStream_t stream) {
-    const int BH = B * H;
-    if (BH <= 0 || T <= 0) return hipSuccess;
-    const Plan p = make_plan(BH, T);
-    if (p.G == 1) return hipSuccess;
-    hipLaunchKernelGGL(gdn_map_kernel, dim3(static_cast<unsigned>(BH) * (p.G - 1)), dim3(kThreads), 0, stream, BH,
-                       T, p.NC, p.G, p.SEGC, static_cast<const u16*>(k), static_cast<const u16*>(v), alpha, beta,
-                       static_cast<float*>(workspace));
-    return hipGetLastError();
+    return launch_uniform(B, H, T, q, k, v, alpha, beta, nullptr, nullptr, nullptr, workspace, true, false, stream);
 }
 
 hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
                                 const float* beta, const float* S0, void* o, float* S_out, void* workspace,
                                 hipStream_t stream) {
-    const int BH = B * H;
-    if (BH <= 0 || T <= 0) return hipSuccess;
-    const Plan p = make_plan(BH, T);
-    float* ws = static_cast<float*>(workspace);
-    if (p.G > 1) {
-        hipLaunchKernelGGL(gdn_combine_kernel, dim3(static_cast<unsigned>((BH + 7) / 8) * 64), dim3(kCombineThreads), 0,
-                           stream, BH,
-                           p.G, S0, ws);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(gdn_out_kernel, dim3(static_cast<unsigned>(BH) * p.G), dim3(kThreads), 0, stream, BH, T,
-                       p.NC, p.G, p.SEGC, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                       static_cast<const u16*>(v), alpha, beta, S0, ws, static_cast<u16*>(o), S_out);
-    return hipGetLastError();
+    return launch_uniform(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, false, true, stream);
 }
 
 hipError_t launch_gdn_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S0, void* o, float* S_out, void* workspace,
                            hipStream_t stream) {
-    const hipError_t e = launch_gdn_mfma_prep(B, H, T, q, k, v, alpha, beta, workspace, stream);
+    return launch_uniform(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, true, true, stream);
+}
+
+hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream) {
+    if (N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gdn_varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, N, Ttot, segc < 1 ? 1 : segc,
+                       snap, cu, tab, tab + (N + 1));
+    return hipGetLastError();
+}
+
+size_t gdn_mfma_varlen_workspace_bytes(int N, int H, int Ttot) {
+    if (N <= 0 || H <= 0) return 0;
+    const VarPlan p = make_var_plan(N, H, Ttot);
+    return p.table_bytes + static_cast<size_t>(H) * p.Gcap * 3 * kMat * sizeof(float);
+}
+
+hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
+                                  int snap, int snap_cap, float* S_snap, void* workspace, hipStream_t stream) {
+    if (N <= 0 || H <= 0) return hipSuccess;
+    const VarPlan p = make_var_plan(N, H, Ttot);
+    int* tab = static_cast<int*>(workspace);
+    Geo g{};
+    g.SEGC = p.SEGC;
+    g.cu = cu;
+    g.seg_base = tab;
+    g.snap_base = tab + (N + 1);
+    g.N = N;
+    g.H = H;
+    g.Ttot = Ttot;
+    g.Gcap = p.Gcap;
+    g.snap = S_snap ? snap : 0;
+    g.snap_cap = snap_cap;
+    g.S_snap = S_snap;
+    const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream);
     if (e != hipSuccess) return e;
-    return launch_gdn_mfma_scan(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, stream);
+    float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.table_bytes);
+    const int blocks = p.Gcap * H;   // (segment, head) items, a bound; the extra workgroups exit
+    return launch_all(g, blocks, N * H, blocks, q, k, v, alpha, beta, S0, o, S_out, ws, true, true, stream);
 }
 
 }  // namespace la

@@ -17,11 +17,24 @@ enum Dtype { kF32 = 0, kBF16 = 1 };
 // v,o [heads,T,dv]; alpha [heads,T] (gated kinds; [heads,T,dk] per channel
 // for KDA), beta [heads,T] (gated delta and KDA); S0/S_out
 // [heads,dv,dk] (may alias); z0/z_out [heads,dk] (normalized only, may alias).
+// Packed batch (cu != nullptr): heads = N*H; head i = n*H + h runs tokens
+// cu[n]..cu[n+1] of row block h of [H][Ttot][d] (gates [H][Ttot]) with state
+// i, T is ignored, and after every `snap` tokens (0: never) the state goes to
+// S_snap[snap_base[n] + j][h] for the first snap_cap slots.
+struct Packed {
+    const int* cu = nullptr;
+    const int* snap_base = nullptr;
+    int H = 0, Ttot = 0, snap = 0, snap_cap = 0;
+    float* S_snap = nullptr;
+};
 hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int dv,
                             const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta,
                             const float* S0, float* S_out, const float* z0, float* z_out,
-                            void* o, hipStream_t stream);
+                            void* o, hipStream_t stream, const Packed& pk = Packed{});
+// The packed-batch table of seg_base / snap_base ([N+1] ints each, at tab and
+// tab + N + 1) on the device, from cu (1 workgroup).
+hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream);
 
 // ---- normalised linear attention, masked parallel form (la_parallel.hip) -
 hipError_t launch_la_parallel(int dtype, int heads, int T, int dk, int dv,
@@ -57,6 +70,16 @@ hipError_t launch_gdn_mfma_prep(int B, int H, int T, const void* q, const void* 
 hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const void* k, const void* v,
                                 const float* alpha, const float* beta, const float* S0, void* o,
                                 float* S_out, void* workspace, hipStream_t stream);
+
+// Packed batch of N sequences (rows [H][Ttot][d], gates [H][Ttot], states
+// [N][H][d][d], sequence n = tokens cu[n]..cu[n+1] on the device), with state
+// snapshots after every `snap` tokens (a multiple of the chunk; 0 for none)
+// into S_snap [snap_cap][H][d][d].  The workspace (gdn_mfma_varlen_workspace_
+// bytes) holds the device-built segment table and the segment maps.
+size_t gdn_mfma_varlen_workspace_bytes(int N, int H, int Ttot);
+hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
+                                  int snap, int snap_cap, float* S_snap, void* workspace, hipStream_t stream);
 
 // Normalised linear attention, chunked, bf16 in/out (la_mfma.hip).
 bool la_mfma_supported(int dtype, int dk, int dv, int chunk);

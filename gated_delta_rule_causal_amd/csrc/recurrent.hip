@@ -80,11 +80,23 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     int T, int DV, const typename IO::T* __restrict__ q, const typename IO::T* __restrict__ k,
     const typename IO::T* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* S0, float* S_out, const float* z0, float* z_out,
-    typename IO::T* __restrict__ o) {
+    typename IO::T* __restrict__ o, Packed pk) {
     constexpr int LPR = RowSlice<DK>::LPR;
     constexpr int RG = RowSlice<DK>::RG;
     static_assert(KIND != kNormalized || SPLIT == 1, "z is shared by all rows of a head");
-    const int head = blockIdx.x / SPLIT;
+    const int head = blockIdx.x / SPLIT;   // state index (packed: sequence * H + head)
+    // token rows of this head: [head][T] (uniform) or tokens cu[n].. of row
+    // block h of [H][Ttot] (packed batch)
+    size_t tok0 = static_cast<size_t>(head) * T;
+    int Tn = T, hh = 0, snap0 = 0;
+    if (pk.cu != nullptr) {
+        const int n = head / pk.H;
+        hh = head - n * pk.H;
+        const int t0 = min(max(pk.cu[n], 0), pk.Ttot), t1 = min(max(pk.cu[n + 1], 0), pk.Ttot);
+        Tn = t1 > t0 ? t1 - t0 : 0;
+        tok0 = static_cast<size_t>(hh) * pk.Ttot + t0;
+        snap0 = pk.snap_base ? pk.snap_base[n] : 0;
+    }
     const int li = threadIdx.x % LPR;
     const int rg = threadIdx.x / LPR + (blockIdx.x % SPLIT) * RG * R;  // first row of this lane group
     const int c0 = 4 * li;
@@ -119,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     // ---- token inputs, prefetched one token ahead
     float kn[8], qn[8], vn[R], an = 1.f, bn = 0.f, avn[8];
     auto fetch = [&](int t) {
-        const size_t tk = (static_cast<size_t>(head) * T + t) * DK;
-        const size_t tv = (static_cast<size_t>(head) * T + t) * DV;
+        const size_t tk = (tok0 + t) * DK;
+        const size_t tv = (tok0 + t) * DV;
         load_slice<IO>(k, tk, c0, c1, kn);
         load_slice<IO>(q, tk, c0, c1, qn);
         if constexpr (KIND == kKda) load_slice<IoF32>(alpha, tk, c0, c1, avn);
@@ -129,12 +141,12 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
             const int r = rg + RG * j;
             vn[j] = r < DV ? IO::load(v, tv + r) : 0.f;
         }
-        if constexpr (KIND == kGated || KIND == kGatedDelta) an = alpha[static_cast<size_t>(head) * T + t];
-        if constexpr (KIND == kGatedDelta || KIND == kKda) bn = beta[static_cast<size_t>(head) * T + t];
+        if constexpr (KIND == kGated || KIND == kGatedDelta) an = alpha[tok0 + t];
+        if constexpr (KIND == kGatedDelta || KIND == kKda) bn = beta[tok0 + t];
     };
-    fetch(0);
+    if (Tn > 0) fetch(0);
 
-    const int steps = ONE ? 1 : T;  // ONE: the decode step (T = 1), no prefetch path
+    const int steps = ONE ? min(1, Tn) : Tn;  // ONE: the decode step (T = 1), no prefetch path
     for (int t = 0; t < steps; ++t) {
         float kc[8], qc[8], vc[R], ac[8];
 #pragma unroll
@@ -146,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 #pragma unroll
         for (int j = 0; j < R; ++j) vc[j] = vn[j];
         const float a = an, b = bn;
-        if (!ONE && t + 1 < T) fetch(t + 1);
-        const size_t to = (static_cast<size_t>(head) * T + t) * DV;
+        if (!ONE && t + 1 < Tn) fetch(t + 1);
+        const size_t to = (tok0 + t) * DV;
 
         if constexpr (KIND == kGated) {
             (void)b;
@@ -235,6 +247,18 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
                 if (li == 0 && r < DV) IO::store(o, to + r, num * rden);
             }
         }
+        // packed batches: the state after every pk.snap tokens
+        if (!ONE && pk.snap > 0 && (t + 1) % pk.snap == 0) {
+            const int js = snap0 + (t + 1) / pk.snap - 1;
+            if (js < pk.snap_cap) {
+                float* dst = pk.S_snap + (static_cast<size_t>(js) * pk.H + hh) * DV * DK;
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int r = rg + RG * j;
+                    if (r < DV) store_state8(dst + static_cast<size_t>(r) * DK, c0, c1, s[j]);
+                }
+            }
+        }
     }
 
     // ---- write back the state (same lanes that read it: in-place safe)
@@ -260,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 template <int KIND, class IO, int DK, bool ONE>
 hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, const void* v,
                      const float* alpha, const float* beta, const float* S0, float* S_out,
-                     const float* z0, float* z_out, void* o, hipStream_t stream) {
+                     const float* z0, float* z_out, void* o, const Packed& pk, hipStream_t stream) {
     using E = typename IO::T;
     constexpr int RG = RowSlice<DK>::RG;
     // gated delta: two blocks per head when each still gets a whole row group
@@ -270,7 +294,7 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, T, dv, static_cast<const E*>(q),
                            static_cast<const E*>(k), static_cast<const E*>(v), alpha, beta, S0,
-                           S_out, z0, z_out, static_cast<E*>(o));
+                           S_out, z0, z_out, static_cast<E*>(o), pk);
         return hipGetLastError();
     };
     if (split == 2) {
@@ -296,21 +320,21 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
 template <int KIND, class IO, int DK>
 hipError_t launch_dk(int heads, int T, int dv, const void* q, const void* k, const void* v,
                      const float* alpha, const float* beta, const float* S0, float* S_out,
-                     const float* z0, float* z_out, void* o, hipStream_t stream) {
-    if (T == 1)
-        return launch_rows<KIND, IO, DK, true>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
-    return launch_rows<KIND, IO, DK, false>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
+                     const float* z0, float* z_out, void* o, const Packed& pk, hipStream_t stream) {
+    if (T == 1 && pk.cu == nullptr)
+        return launch_rows<KIND, IO, DK, true>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, pk, stream);
+    return launch_rows<KIND, IO, DK, false>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, pk, stream);
 }
 
 template <int KIND, class IO>
 hipError_t launch_io(int heads, int T, int dk, int dv, const void* q, const void* k, const void* v,
                      const float* alpha, const float* beta, const float* S0, float* S_out,
-                     const float* z0, float* z_out, void* o, hipStream_t stream) {
+                     const float* z0, float* z_out, void* o, const Packed& pk, hipStream_t stream) {
     switch (dk) {
-        case 16: return launch_dk<KIND, IO, 16>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
-        case 32: return launch_dk<KIND, IO, 32>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
-        case 64: return launch_dk<KIND, IO, 64>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
-        case 128: return launch_dk<KIND, IO, 128>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, stream);
+        case 16: return launch_dk<KIND, IO, 16>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, pk, stream);
+        case 32: return launch_dk<KIND, IO, 32>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, pk, stream);
+        case 64: return launch_dk<KIND, IO, 64>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, pk, stream);
+        case 128: return launch_dk<KIND, IO, 128>(heads, T, dv, q, k, v, alpha, beta, S0, S_out, z0, z_out, o, pk, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -320,26 +344,31 @@ hipError_t launch_io(int heads, int T, int dk, int dv, const void* q, const void
 hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int dv, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
                             const float* S0, float* S_out, const float* z0, float* z_out, void* o,
-                            hipStream_t stream) {
-    if (heads <= 0 || T <= 0) return hipSuccess;
-    if (kind == kGated) {
-        return dtype == kBF16
-                   ? launch_io<kGated, IoBF16>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr, nullptr, o, stream)
-                   : launch_io<kGated, IoF32>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr, nullptr, o, stream);
+                            hipStream_t stream, const Packed& pk) {
+    if (heads <= 0 || (T <= 0 && pk.cu == nullptr)) return hipSuccess;
+    const bool bf = dtype == kBF16;
+    switch (kind) {
+        case kGated:
+            return bf ? launch_io<kGated, IoBF16>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr,
+                                                  nullptr, o, pk, stream)
+                      : launch_io<kGated, IoF32>(heads, T, dk, dv, q, k, v, alpha, nullptr, S0, S_out, nullptr,
+                                                 nullptr, o, pk, stream);
+        case kKda:
+            return bf ? launch_io<kKda, IoBF16>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr,
+                                                o, pk, stream)
+                      : launch_io<kKda, IoF32>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o,
+                                               pk, stream);
+        case kGatedDelta:
+            return bf ? launch_io<kGatedDelta, IoBF16>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr,
+                                                       nullptr, o, pk, stream)
+                      : launch_io<kGatedDelta, IoF32>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr,
+                                                      nullptr, o, pk, stream);
+        default:
+            return bf ? launch_io<kNormalized, IoBF16>(heads, T, dk, dv, q, k, v, nullptr, nullptr, S0, S_out, z0,
+                                                       z_out, o, pk, stream)
+                      : launch_io<kNormalized, IoF32>(heads, T, dk, dv, q, k, v, nullptr, nullptr, S0, S_out, z0,
+                                                      z_out, o, pk, stream);
     }
-    if (kind == kKda) {
-        return dtype == kBF16
-                   ? launch_io<kKda, IoBF16>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream)
-                   : launch_io<kKda, IoF32>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream);
-    }
-    if (kind == kGatedDelta) {
-        return dtype == kBF16
-                   ? launch_io<kGatedDelta, IoBF16>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream)
-                   : launch_io<kGatedDelta, IoF32>(heads, T, dk, dv, q, k, v, alpha, beta, S0, S_out, nullptr, nullptr, o, stream);
-    }
-    return dtype == kBF16
-               ? launch_io<kNormalized, IoBF16>(heads, T, dk, dv, q, k, v, nullptr, nullptr, S0, S_out, z0, z_out, o, stream)
-               : launch_io<kNormalized, IoF32>(heads, T, dk, dv, q, k, v, nullptr, nullptr, S0, S_out, z0, z_out, o, stream);
 }
 
 }  // namespace la

@@ -65,7 +65,8 @@ enum {
     LA_FN_GDN_PREFILL = 1,
     LA_FN_DECODE_STEP = 2,
     LA_FN_GLA_PREFILL = 3,
-    LA_FN_KDA_PREFILL = 4
+    LA_FN_KDA_PREFILL = 4,
+    LA_FN_GDN_VARLEN = 5   /* B = number of sequences, T = total tokens */
 };
 
 /*
@@ -203,6 +204,47 @@ la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv
                                const void* q, const void* k, const void* v,
                                const float* alpha, const float* beta,
                                float* S, float* z, void* o, void* stream);
+
+/*
+ * gdn_prefill_varlen - the gated delta rule over a packed batch of N
+ * sequences of different lengths, with state snapshots for prefix reuse.
+ *
+ * Every sequence is the recurrence of gdn_prefill (section "Delta rule and
+ * Gated DeltaNet", Gated DeltaNet equation) on its own tokens, from its own
+ * state.  Section "Honest talk: why MiniMax went back to full attention"
+ * names prefix caching (reusing the work done for a shared beginning of
+ * different requests) as missing from many implementations; for this layer
+ * the reusable part of a prefix is its state, which this call can save at
+ * regular positions.
+ * Layout (device pointers, 16-byte aligned unless stated):
+ *   cu_seqlens [N+1] int32, 4-byte aligned: sequence n is tokens
+ *     cu_seqlens[n] .. cu_seqlens[n+1] (non-decreasing from 0 to T_total;
+ *     values outside [0, T_total] are clamped, so a bad table gives wrong
+ *     results but no access outside the buffers);
+ *   q, k [H, T_total, dk]; v, o [H, T_total, dv] (every head holds all the
+ *     sequences back to back); alpha, beta [H, T_total] float32;
+ *   S0, S_out [N, H, dv, dk] float32 (S0 NULL = zeros; S_out may be S0);
+ *   snapshots: when snap_interval > 0 and S_snap is not NULL, the state of
+ *     sequence n after p tokens, for every positive multiple p of
+ *     snap_interval up to its length, is written to
+ *     S_snap[base_n + p / snap_interval - 1] ([snap_count, H, dv, dk]
+ *     float32), base_n = sum over m < n of len_m / snap_interval; slots at or
+ *     past snap_count are not written.
+ * form: LA_FORM_CHUNKED (bf16, dk = dv = 128, chunk 64; snap_interval a
+ * multiple of the chunk) or LA_FORM_RECURRENT (any supported dtype and size).
+ * workspace/ws_bytes: at least la_workspace_bytes(LA_FN_GDN_VARLEN, dtype, N,
+ * H, T_total, dk, dv, form, chunk) bytes (the segment table is built on the
+ * device, so the host never reads cu_seqlens); it must not overlap any
+ * other argument.  Errors as for gdn_prefill.
+ */
+la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int dv,
+                             const int* cu_seqlens,
+                             const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* S0,
+                             void* o, float* S_out,
+                             int snap_interval, int snap_count, float* S_snap,
+                             int form, int chunk,
+                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * kda_prefill - Kimi Delta Attention over T tokens: the gated delta rule with

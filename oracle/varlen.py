@@ -19,17 +19,26 @@ Readings where the page is silent:
   positive multiple of the snapshot interval and at most the sequence's
   length, numbered sequence by sequence in order of p.
 Every sequence is the Gated DeltaNet recurrence of the same section
-(gdn_recurrent), run on its own slice.
+(gdn_recurrent), run on its own slice; form="chunked" evaluates each piece
+with the chunk form gdn_chunked (chunk 64) instead, which is faster for large
+head sizes and agrees with the recurrence up to rounding.
 """
 
 import numpy as np
 
-from .gated_delta import gdn_recurrent
+from .gated_delta import gdn_recurrent, gdn_chunked
 
 
-def gdn_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, snap_interval=0):
+def gdn_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, snap_interval=0, form="recurrent"):
     """Returns (o [H, T_total, d_v], S_final [N, H, d_v, d_k], snaps
     [n_snaps, H, d_v, d_k])."""
+    if form == "recurrent":
+        run = gdn_recurrent
+    elif form == "chunked":
+        def run(Q, K, V, A, B, S):
+            return gdn_chunked(Q, K, V, A, B, 64, S)
+    else:
+        raise ValueError(form)
     q, k, v, alpha, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, beta))
     H, Ttot, dk = q.shape
     dv = v.shape[-1]
@@ -50,8 +59,8 @@ def gdn_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, snap_interval=0):
             ends = cuts + ([b] if not cuts or cuts[-1] != b else [])
             for cut in ends:
                 if cut > start:
-                    o[h, start:cut], S = gdn_recurrent(q[h, start:cut], k[h, start:cut], v[h, start:cut],
-                                                       alpha[h, start:cut], beta[h, start:cut], S)
+                    o[h, start:cut], S = run(q[h, start:cut], k[h, start:cut], v[h, start:cut],
+                                             alpha[h, start:cut], beta[h, start:cut], S)
                 elif S is None:
                     S = np.zeros((dv, dk))
                 if cut in cuts:

@@ -23,6 +23,11 @@ without drawing the rest):
 * KDA: q, k, v, beta as for the gated delta rule; the per-channel decay
   alpha[t, c] = sigmoid(N(mu_c, 1)) with mu_c spread evenly over [1, 5] across
   the d_k key channels (fast- and slow-forgetting channels side by side).
+* packed batches: sequence lengths from one generator (stream 11),
+  lognormal(0, 1) weights scaled to the total token count (every length at
+  least 1, the rounding remainder on the last sequence); the tokens of
+  sequence n, head h are gdn_head(seed, n, h, ...) laid out back to back per
+  head, [H, T_total, d].
 * decode: the carried state S0 ~ N(0, 0.02^2) float32 per head; the per-step
   token inputs come from a pool of ``pool`` draws (step s uses pool entry
   s mod pool), generated with ``default_rng([seed, stream, 1000 + entry])``.
@@ -31,7 +36,7 @@ without drawing the rest):
 import numpy as np
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_ALPHA, STREAM_BETA, STREAM_S0, STREAM_Z0 = range(7)
-STREAM_X, STREAM_CONV_W, STREAM_LOGITS, STREAM_CONV_STATE = range(7, 11)
+STREAM_X, STREAM_CONV_W, STREAM_LOGITS, STREAM_CONV_STATE, STREAM_LENGTHS = range(7, 12)
 
 # The five named workloads.  ``seed`` is the per-workload base seed.
 WORKLOADS = {
@@ -54,6 +59,10 @@ WORKLOADS = {
     "kda_bf16_2x16x8192": dict(seed=1008, kind="kda", B=2, H=16, T=8192, dk=128, dv=128, dtype="bf16"),
     "kda_decode_256x32": dict(seed=1009, kind="kda_decode", N=256, H=32, dk=128, dv=128, dtype="bf16",
                               steps=1000, state_std=0.02),
+    # packed batch: 16 sequences of mixed lengths, 16384 tokens in all (the
+    # head-token count of the 2 x 16 x 8192 prefill), snapshots every 1024
+    "gdn_varlen_bf16_16seq_16k": dict(seed=1010, kind="gdn_varlen", N=16, H=16, T_total=16384, dk=128, dv=128,
+                                      dtype="bf16", chunk=64, snap=1024),
     # pre-operations of a Gated DeltaNet layer in front of the 2 x 16 x 8192
     # prefill: x [2, 8192, 16 * (128 + 128 + 128)]
     "preops_bf16_2x16x8192": dict(seed=1007, kind="preops", B=2, H=16, T=8192, dk=128, dv=128,
@@ -226,3 +235,32 @@ def kda_decode_token_inputs(seed, N, H, dk, dv, dtype, entry):
     q, k, v, _, beta = decode_token_inputs(seed, N, H, dk, dv, dtype, entry)
     alpha = _channel_decay(_normal(seed, STREAM_ALPHA, (3000 + entry,), (N, H, dk)), dk)
     return q, k, v, alpha, beta
+
+
+def varlen_lengths(seed, N, total):
+    """N sequence lengths summing to total (each >= 1 when total >= N)."""
+    w = _rng(seed, STREAM_LENGTHS).lognormal(0.0, 1.0, size=N)
+    lens = np.maximum(1, np.floor(w / w.sum() * total).astype(np.int64)) if total >= N else np.zeros(N, np.int64)
+    lens[-1] += total - lens.sum()
+    if lens[-1] < 0:
+        raise ValueError("lengths do not fit")
+    return lens
+
+
+def varlen_batch(seed, lens, H, dk, dv, dtype):
+    """q, k, v [H, T_total, d], alpha, beta [H, T_total] and cu_seqlens [N+1]
+    (int32) of a packed batch with the given sequence lengths."""
+    lens = [int(x) for x in lens]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = np.empty((H, T, dk), np.float32)
+    k = np.empty((H, T, dk), np.float32)
+    v = np.empty((H, T, dv), np.float32)
+    a = np.empty((H, T), np.float32)
+    b = np.empty((H, T), np.float32)
+    for n, L in enumerate(lens):
+        s0 = int(cu[n])
+        for h in range(H):
+            q[h, s0:s0 + L], k[h, s0:s0 + L], v[h, s0:s0 + L], a[h, s0:s0 + L], b[h, s0:s0 + L] = \
+                gdn_head(seed, n, h, L, dk, dv, dtype)
+    return q, k, v, a, b, cu

@@ -48,7 +48,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gla_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
-                            "gdn_preprocess", "kda_prefill", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
+                            "gdn_preprocess", "kda_prefill", "gdn_prefill_varlen", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -292,3 +292,32 @@ def test_kda_validation(lib):
     # alpha spans N*H*dk floats: an output placed inside it is an overlap
     assert lib.lin_attn_decode_step(3, BF16, 4, 2, 128, 128, P(1), P(2), P(3), P(5), P(6), P(7), None,
                                     ctypes.c_void_p(BASE + 5 * GiB + 2048), None) == LA_ERR_ARG
+
+
+def test_varlen_validation(lib):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    VARLEN = 5
+
+    def vl(dtype=BF16, N=3, H=2, T=500, dk=128, dv=128, cu=10, q=1, k=2, v=3, a=5, b=6, S0=None, o=4, S_out=None,
+           snap=0, nsnap=0, S_snap=None, form=CHUNKED, chunk=64, ws=9, ws_bytes=1 << 40):
+        return lib.gdn_prefill_varlen(dtype, N, H, T, dk, dv, f(cu), f(q), f(k), f(v), f(a), f(b), f(S0), f(o),
+                                      f(S_out), snap, nsnap, f(S_snap), form, chunk, f(ws), ws_bytes, None)
+
+    assert vl(dtype=7) == LA_ERR_DTYPE
+    assert vl(form=PARALLEL) == LA_ERR_ARG
+    assert vl(dtype=F32) == LA_ERR_UNSUPPORTED             # chunked: bf16, d = 128, chunk 64 only
+    assert vl(snap=100, nsnap=4, S_snap=11) == LA_ERR_SHAPE  # chunked snapshots at whole chunks
+    assert vl(snap=-1) == LA_ERR_SHAPE
+    assert vl(cu=None) == LA_ERR_NULL
+    assert vl(a=None) == LA_ERR_NULL
+    assert vl(snap=128, nsnap=4, S_snap=None) == LA_ERR_NULL
+    assert vl(cu=ctypes.c_void_p(BASE + 10 * GiB + 2)) == LA_ERR_ALIGN
+    assert vl(ws=None) == LA_ERR_WORKSPACE
+    assert vl(ws=5) == LA_ERR_ARG                          # workspace on top of alpha
+    assert vl(o=10) == LA_ERR_ARG                          # output on top of cu_seqlens
+    assert vl(snap=128, nsnap=4, S_snap=4) == LA_ERR_ARG   # snapshots on top of o
+    need = lib.la_workspace_bytes(VARLEN, BF16, 3, 2, 500, 128, 128, CHUNKED, 64)
+    assert need > 0 and vl(ws_bytes=need - 1) == LA_ERR_WORKSPACE
+    rec = lib.la_workspace_bytes(VARLEN, F32, 3, 2, 500, 64, 64, RECURRENT, 0)
+    assert 0 < rec < need
+    assert vl(N=0) == LA_OK

@@ -713,6 +713,9 @@ def pin_varlen(ns):
                 assert np.abs(o_t - o[h, s + p:e]).max(initial=0) < 1e-12
                 assert np.abs(S_t - S[n, h]).max() < 1e-12
             j += 1
+    # the chunk-form evaluation agrees
+    o_c, S_c, snaps_c = ns.gdn_varlen(q, k, v, a, b, cu, S0, snap_interval=iv, form="chunked")
+    assert np.abs(o_c - o).max() < 1e-12 and np.abs(S_c - S).max() < 1e-12 and np.abs(snaps_c - snaps).max() < 1e-12
     # without an initial state every sequence starts from zero; without snapshots none are returned
     o0, S0z, sn0 = ns.gdn_varlen(q, k, v, a, b, cu)
     assert sn0.shape[0] == 0 and np.all(S0z[1] == 0)
