@@ -5,10 +5,13 @@
 One timed step is one chunked gated-delta prefill (state-independent pass +
 sequential scan) over the 2 x 16 x 8192 workload (B=2, H=16, T=8192,
 d_k = d_v = 128, bf16 activations, fp32 state, chunk 64), inputs resident in
-HBM.  `value` is prefill tokens/s (B*T tokens per step).  In the same run the
-decode workload (256 sequences x 32 heads, d = 128, fp32 state, 1000 steps)
-is timed and reported as state HBM GB/s, plus the fp64 CPU oracle on a
-bounded sample of the prefill workload.  Prints one JSON line.
+HBM.  `value` is prefill tokens/s (B*T tokens per step).  In the same run,
+each reported beside the headline: the decode workload (256 sequences x 32
+heads, d = 128, fp32 state, 1000 steps) as state HBM GB/s; the normalised and
+the scalar-gated linear-attention prefills; the fused pre-operations of a
+Gated DeltaNet layer; the KDA decode and recurrent prefill; a packed batch of
+16 sequences of mixed lengths with state snapshots; and the fp64 CPU oracle on
+a bounded sample of the prefill workload.  Prints one JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 are launched on (torch's current stream, which the binding passes to the C
@@ -33,6 +36,9 @@ DECODE = "gdn_decode_256x32"
 LA_PREFILL = "la_bf16_4x16x4096"
 GLA_PREFILL = "gla_bf16_2x16x8192"
 PREOPS = "preops_bf16_2x16x8192"
+KDA_DECODE = "kda_decode_256x32"
+KDA_PREFILL = "kda_bf16_2x16x8192"
+VARLEN = "gdn_varlen_bf16_16seq_16k"
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
 # d = d_k = d_v: bytes = q, k, v, o in bf16 + alpha, beta in fp32; flops as
@@ -271,6 +277,85 @@ def main():
     dec_state_gbps = state_bytes / (dec_ms * 1e-3) / 1e9
     dec_total_gbps = (state_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
 
+    # ---------------------------------------------- KDA decode (per-channel decay)
+    wk = synth.WORKLOADS[KDA_DECODE]
+    Nk, Hk, dkk = wk["N"], wk["H"], wk["dk"]
+    Sk = torch.from_numpy(synth.decode_state_fast(wk["seed"], Nk, Hk, dkk, dkk, wk["state_std"])).to(dev)
+    kpool = []
+    for e in range(8):
+        tq, tk, tv, ta, tb = synth.kda_decode_token_inputs(wk["seed"], Nk, Hk, dkk, dkk, "bf16", e)
+        kpool.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (tq, tk, tv)) +
+                     tuple(torch.from_numpy(x).to(dev) for x in (ta, tb)))
+    ok_dec = torch.empty((Nk, Hk, dkk), dtype=torch.bfloat16, device=dev)
+    for i in range(5):
+        tq, tk, tv, ta, tb = kpool[i % 8]
+        gd.lin_attn_decode_step("kda", tq, tk, tv, Sk, alpha=ta, beta=tb, out=ok_dec)
+    torch.cuda.synchronize()
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    kev[0].record()
+    for i in range(steps):
+        tq, tk, tv, ta, tb = kpool[i % 8]
+        gd.lin_attn_decode_step("kda", tq, tk, tv, Sk, alpha=ta, beta=tb, out=ok_dec)
+        kev[i + 1].record()
+    torch.cuda.synchronize()
+    kda_dec_ms = float(np.mean([kev[i].elapsed_time(kev[i + 1]) for i in range(steps)]))
+    # state read + write, q k v o in bf16, alpha per channel and beta in fp32
+    kda_dec_bytes = 2 * Nk * Hk * dkk * dkk * 4 + Nk * Hk * (4 * dkk * 2 + dkk * 4 + 4)
+    kda_dec_gbps = kda_dec_bytes / (kda_dec_ms * 1e-3) / 1e9
+    del Sk, kpool
+
+    # -------------------------------------------- KDA prefill (recurrent form)
+    wkp = synth.WORKLOADS[KDA_PREFILL]
+    Bk, Hkp, Tk, dkp = wkp["B"], wkp["H"], wkp["T"], wkp["dk"]
+    kq, kk, kv, ka, kb = synth.kda_batch(wkp["seed"], Bk, Hkp, Tk, dkp, dkp, "bf16")
+    kda_in = tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (kq, kk, kv)) + \
+        tuple(torch.from_numpy(x).to(dev) for x in (ka, kb))
+    del kq, kk, kv, ka, kb
+    gd.kda_prefill(*kda_in)
+    torch.cuda.synchronize()
+    kpe = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    kpe[0].record()
+    for i in range(2):
+        gd.kda_prefill(*kda_in)
+        kpe[i + 1].record()
+    torch.cuda.synchronize()
+    kda_pre_ms = float(np.mean([kpe[i].elapsed_time(kpe[i + 1]) for i in range(2)]))
+    del kda_in
+
+    # ------------------------------- packed variable-length batch + snapshots
+    wv = synth.WORKLOADS[VARLEN]
+    Hv, dvv, snapv = wv["H"], wv["dk"], wv["snap"]
+    lens = synth.varlen_lengths(wv["seed"], wv["N"], wv["T_total"])
+    vq, vk, vv, va, vb, vcu = synth.varlen_batch(wv["seed"], lens, Hv, dvv, dvv, "bf16")
+    vsets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (vq, vk, vv)) +
+             tuple(torch.from_numpy(x).to(dev) for x in (va, vb)) for _ in range(3)]
+    vcu_t = torch.from_numpy(vcu).to(dev)
+    del vq, vk, vv, va, vb
+    nsnap = int(sum(int(L) // snapv for L in lens))
+    v_out = torch.empty((Hv, wv["T_total"], dvv), dtype=torch.bfloat16, device=dev)
+    v_S = torch.empty((wv["N"], Hv, dvv, dvv), dtype=torch.float32, device=dev)
+    v_snap = torch.empty((nsnap, Hv, dvv, dvv), dtype=torch.float32, device=dev)
+    v_ws = torch.empty(gd.la_workspace_bytes("gdn_prefill_varlen", "bf16", wv["N"], Hv, wv["T_total"], dvv, dvv),
+                       dtype=torch.uint8, device=dev)
+
+    def vcall(i):
+        gd.gdn_prefill_varlen(*vsets[i % 3], vcu_t, snap_interval=snapv, snap_count=nsnap, out=v_out, S_out=v_S,
+                              S_snap=v_snap, workspace=v_ws)
+
+    for i in range(2):
+        vcall(i)
+    torch.cuda.synchronize()
+    vev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    vev[0].record()
+    for i in range(args.la_steps):
+        vcall(i)
+        vev[i + 1].record()
+    torch.cuda.synchronize()
+    var_ms = float(np.mean([vev[i].elapsed_time(vev[i + 1]) for i in range(args.la_steps)]))
+    var_bytes = Hv * wv["T_total"] * path_bytes_per_head_token(dvv) + (nsnap + wv["N"]) * Hv * dvv * dvv * 4
+    var_gbps = var_bytes / (var_ms * 1e-3) / 1e9
+    del vsets, v_out, v_S, v_snap, v_ws
+
     # ----------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu:
@@ -330,6 +415,24 @@ def main():
                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pre_gbps / HBM_PEAK_GBPS,
                                     "traffic": measured_traffic(["gdn_preprocess_kernel"]),
                                     "bytes_per_launch": pre_bytes, "avg_launch_ms": pre_ms}},
+        "kda_decode": {"workload": "KDA decode 256 seq x 32 heads, d=128, per-channel decay, fp32 state, bf16 "
+                                   "token I/O", "steps": steps, "ms_per_step": kda_dec_ms,
+                       "steps_per_s": 1e3 / kda_dec_ms,
+                       "roofline": {"kernel": "recurrent_kernel (KDA decode)", "bound": "hbm",
+                                    "achieved": kda_dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                    "frac": kda_dec_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kda_dec_bytes,
+                                    "avg_launch_ms": kda_dec_ms}},
+        "kda_prefill": {"workload": "KDA prefill B=2 H=16 T=8192 d=128, recurrent form (token by token), bf16 I/O",
+                        "calls": 2, "ms_per_call": kda_pre_ms, "tokens_per_s": Bk * Tk / (kda_pre_ms * 1e-3)},
+        "varlen_prefill": {"workload": f"gated delta prefill, packed batch of {wv['N']} sequences ({wv['T_total']} "
+                                       f"tokens, lengths {int(min(lens))}..{int(max(lens))}), H=16 d=128 chunk=64, "
+                                       f"snapshots every {snapv} tokens ({nsnap})",
+                           "calls": args.la_steps, "ms_per_call": var_ms,
+                           "tokens_per_s": wv["T_total"] / (var_ms * 1e-3),
+                           "roofline": {"kernel": "gdn_prefill_varlen (plan + map + combine + out)", "bound": "hbm",
+                                        "achieved": var_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                        "frac": var_gbps / HBM_PEAK_GBPS, "bytes_per_launch": var_bytes,
+                                        "avg_launch_ms": var_ms}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     // block h of [H][Ttot] (packed batch)
     size_t tok0 = static_cast<size_t>(head) * T;
     int Tn = T, hh = 0, snap0 = 0;
-    if (pk.cu != nullptr) {
+    if (!ONE && pk.cu != nullptr) {   // (the decode step never runs a packed batch)
         const int n = head / pk.H;
         hh = head - n * pk.H;
         const int t0 = min(max(pk.cu[n], 0), pk.Ttot), t1 = min(max(pk.cu[n + 1], 0), pk.Ttot);
@@ -144,9 +144,9 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
         if constexpr (KIND == kGated || KIND == kGatedDelta) an = alpha[tok0 + t];
         if constexpr (KIND == kGatedDelta || KIND == kKda) bn = beta[tok0 + t];
     };
-    if (Tn > 0) fetch(0);
+    if (ONE || Tn > 0) fetch(0);
 
-    const int steps = ONE ? min(1, Tn) : Tn;  // ONE: the decode step (T = 1), no prefetch path
+    const int steps = ONE ? 1 : Tn;  // ONE: the decode step (T = 1), no prefetch path
     for (int t = 0; t < steps; ++t) {
         float kc[8], qc[8], vc[R], ac[8];
 #pragma unroll
