@@ -287,8 +287,12 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
                      const float* z0, float* z_out, void* o, const Packed& pk, hipStream_t stream) {
     using E = typename IO::T;
     constexpr int RG = RowSlice<DK>::RG;
-    // gated delta: two blocks per head when each still gets a whole row group
-    const int split = (KIND != kNormalized && dv >= 2 * RG) ? 2 : 1;
+    // Kinds without a shared normaliser split a head's rows over 2 blocks;
+    // a token-serial prefill over few heads splits further (up to 8 blocks
+    // of at least one row group each) so that about 512 blocks run.
+    int split = (KIND != kNormalized && dv >= 2 * RG) ? 2 : 1;
+    if (!ONE && split == 2)
+        while (split < 8 && dv >= 2 * split * RG && static_cast<long long>(heads) * split < 512) split *= 2;
     const int R = (dv / split + RG - 1) / RG;
     dim3 grid(static_cast<unsigned>(heads) * split), block(kThreads);
     auto args = [&](auto kern) {
@@ -297,8 +301,8 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
                            S_out, z0, z_out, static_cast<E*>(o), pk);
         return hipGetLastError();
     };
-    if (split == 2) {
-        if constexpr (KIND != kNormalized) {
+    if constexpr (KIND != kNormalized) {
+        if (split == 2) {
             switch (R) {
                 case 1: return args(recurrent_kernel<KIND, IO, DK, 1, 2, ONE>);
                 case 2: return args(recurrent_kernel<KIND, IO, DK, 2, 2, ONE>);
@@ -306,7 +310,19 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
                 default: return hipErrorInvalidValue;
             }
         }
-        return hipErrorInvalidValue;
+        if constexpr (!ONE) {
+            if (split == 4) {
+                switch (R) {
+                    case 1: return args(recurrent_kernel<KIND, IO, DK, 1, 4, ONE>);
+                    case 2: return args(recurrent_kernel<KIND, IO, DK, 2, 4, ONE>);
+                    default: return hipErrorInvalidValue;
+                }
+            }
+            if (split == 8) {
+                if (R == 1) return args(recurrent_kernel<KIND, IO, DK, 1, 8, ONE>);
+                return hipErrorInvalidValue;
+            }
+        }
     }
     switch (R) {
         case 1: return args(recurrent_kernel<KIND, IO, DK, 1, 1, ONE>);
