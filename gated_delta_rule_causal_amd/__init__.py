@@ -300,7 +300,7 @@ def gdn_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, form="chunked"
 
 
 def kda_prefill(q, k, v, alpha, beta, S0=None, form="recurrent", chunk=64, out=None, S_out=None, want_state=True,
-                stream=None):
+                workspace=None, stream=None):
     """Kimi Delta Attention (per-channel decay alpha [B,H,T,dk]) over T tokens;
     returns (o, S_out)."""
     torch = _torch()
@@ -319,8 +319,10 @@ def kda_prefill(q, k, v, alpha, beta, S0=None, form="recurrent", chunk=64, out=N
     if want_state and S_out is None:
         S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
     _check(S_out, "S_out", torch.float32, (B, H, dv, dk))
+    ws, ws_bytes = _workspace("kda_prefill", dt, B, H, T, dk, dv, form, chunk, workspace, q.device)
     st = _load().kda_prefill(dt, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
-                             _ptr(out), _ptr(S_out), FORMS[form], chunk, None, 0, _stream_ptr(stream, q.device))
+                             _ptr(out), _ptr(S_out), FORMS[form], chunk, _ptr(ws), ws_bytes,
+                             _stream_ptr(stream, q.device))
     if st != 0:
         raise LinAttnError(st, "kda_prefill")
     return out, S_out

@@ -26,6 +26,7 @@ SOURCES = [
     "gdn_mfma.hip",
     "la_mfma.hip",
     "preops.hip",
+    "kda_chunk.hip",
 ]
 
 ARCH = "gfx950"

@@ -124,8 +124,9 @@ size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv
             if (form == LA_FORM_CHUNKED && !la::la_mfma_supported(dtype, dk, dv, chunk)) return bad;
             return form == LA_FORM_CHUNKED ? la::la_mfma_workspace_bytes(B, H, T, dk, dv, chunk) : 0;
         case LA_FN_KDA_PREFILL:
-            if (form != LA_FORM_RECURRENT) return bad;
-            return 0;
+            if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
+            if (form == LA_FORM_CHUNKED && !la::kda_mfma_supported(dtype, dk, dv, chunk)) return bad;
+            return form == LA_FORM_CHUNKED ? la::kda_mfma_workspace_bytes(B, H, T) : 0;
         case LA_FN_GDN_VARLEN:   // B = number of sequences, T = total tokens
             if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
             if (form == LA_FORM_CHUNKED && !la::gdn_mfma_supported(dtype, dk, dv, chunk)) return bad;
@@ -406,13 +407,10 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
 la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k, const void* v,
                       const float* alpha, const float* beta, const float* S0, void* o, float* S_out, int form,
                       int chunk, void* workspace, size_t ws_bytes, void* stream) {
-    (void)chunk;
-    (void)workspace;
-    (void)ws_bytes;
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
     if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return LA_ERR_ARG;
     if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
-    if (form == LA_FORM_CHUNKED) return LA_ERR_UNSUPPORTED;
+    if (form == LA_FORM_CHUNKED && !valid_chunk(chunk)) return LA_ERR_SHAPE;
     const size_t heads = static_cast<size_t>(B) * H;
     if (heads == 0) return LA_OK;
     const size_t es = io_size(dtype);
@@ -424,7 +422,7 @@ la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
         return LA_ERR_NULL;
     for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(alpha),
                           static_cast<const void*>(beta), static_cast<const void*>(S0),
-                          static_cast<const void*>(S_out)})
+                          static_cast<const void*>(S_out), static_cast<const void*>(workspace)})
         if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
     const Span in[] = {{q, nqk}, {k, nqk}, {v, nv}, {alpha, na}, {beta, nb}, {S0, nS}};
     const Span outs[] = {{o, T > 0 ? nv : 0}, {S_out, nS}};
@@ -434,8 +432,20 @@ la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
             if (overlaps(a, b)) return LA_ERR_ARG;
         }
     if (overlaps(outs[0], outs[1])) return LA_ERR_ARG;
+    if (form == LA_FORM_CHUNKED && !la::kda_mfma_supported(dtype, dk, dv, chunk)) return LA_ERR_UNSUPPORTED;
+    const size_t need = form == LA_FORM_CHUNKED ? la::kda_mfma_workspace_bytes(B, H, T) : 0;
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
+    if (need > 0) {
+        const Span w{workspace, need};
+        for (const Span& b : in)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+        for (const Span& b : outs)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) return copy_state(S0, S_out, heads * dv * dk, s);
+    if (form == LA_FORM_CHUNKED)
+        return from_hip(la::launch_kda_mfma(B, H, T, false, q, k, v, alpha, beta, S0, o, S_out, workspace, s));
     return from_hip(la::launch_recurrent(la::kKda, dtype, static_cast<int>(heads), T, dk, dv, q, k, v, alpha, beta,
                                          S0, S_out, nullptr, nullptr, o, s));
 }

@@ -260,10 +260,14 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
  * Gated DeltaNet equation); beta [B,H,T] float32.  S_0 = S0 (zeros when NULL).
  * form:
  *   LA_FORM_RECURRENT - token by token, any supported dtype and sizes;
- *   LA_FORM_CHUNKED   - LA_ERR_UNSUPPORTED (no block form of KDA here).
+ *   LA_FORM_CHUNKED   - block form on the matrix cores, bf16 with
+ *                       dk = dv = 128 and chunk 64 (other shapes:
+ *                       LA_ERR_UNSUPPORTED).  alpha must lie in (0, 1].
  * Outputs o [B,H,T,dv] and, when not NULL, S_out [B,H,dv,dk] (may be the
- * same pointer as S0; any other overlap is LA_ERR_ARG).  workspace/ws_bytes
- * are unused (la_workspace_bytes(LA_FN_KDA_PREFILL, ...) is 0).
+ * same pointer as S0; any other overlap is LA_ERR_ARG).  workspace/ws_bytes:
+ * at least la_workspace_bytes(LA_FN_KDA_PREFILL, ...) bytes (0 for the
+ * recurrent form; 74 240 bytes per head and chunk of 64 tokens for the block
+ * form), not overlapping any tensor argument.
  */
 la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv,
                       const void* q, const void* k, const void* v,

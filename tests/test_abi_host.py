@@ -276,13 +276,15 @@ def test_kda_validation(lib):
     assert kda(a=None) == LA_ERR_NULL
     assert kda(b=None) == LA_ERR_NULL
     assert kda(form=PARALLEL) == LA_ERR_ARG
-    assert kda(form=CHUNKED) == LA_ERR_UNSUPPORTED
+    assert kda(form=CHUNKED, dtype=F32) == LA_ERR_UNSUPPORTED      # block form: bf16, d = 128, chunk 64
+    assert kda(form=CHUNKED) == LA_ERR_WORKSPACE                   # ... with its workspace
     assert kda(dk=48) == LA_ERR_SHAPE
     assert kda(o=5) == LA_ERR_ARG                          # output on top of alpha
     assert kda(S0=7, S_out=ctypes.c_void_p(BASE + 7 * GiB + 32)) == LA_ERR_ARG
     assert kda(q=ctypes.c_void_p(BASE + GiB + 4)) == LA_ERR_ALIGN
     assert lib.la_workspace_bytes(KDA, BF16, 1, 2, 100, 128, 128, RECURRENT, 0) == 0
-    assert lib.la_workspace_bytes(KDA, BF16, 1, 2, 100, 128, 128, CHUNKED, 64) == ctypes.c_size_t(-1).value
+    assert lib.la_workspace_bytes(KDA, BF16, 1, 2, 100, 128, 128, CHUNKED, 64) == 2 * 2 * 74240
+    assert lib.la_workspace_bytes(KDA, F32, 1, 2, 100, 128, 128, CHUNKED, 64) == ctypes.c_size_t(-1).value
     # decode: KDA needs alpha (per channel) and beta, no z
     dec = lambda a=5, b=6, z=None: lib.lin_attn_decode_step(3, BF16, 4, 2, 128, 128, P(1), P(2), P(3), f(a), f(b),
                                                             P(7), f(z), P(4), None)

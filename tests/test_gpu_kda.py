@@ -113,3 +113,74 @@ def test_kda_decode_workload_256x32(gd):
                                      b.reshape(n), S0.reshape(n, d, d))
     report("kda decode 256x32 o", slice_err(to_host(o).reshape(n, 1, d), o_ref.reshape(n, 1, d), lead=1), TOL["bf16"])
     report("  S", slice_err(to_host(S).reshape(n, d, d), S_ref, lead=1), TOL["bf16"])
+
+
+# ------------------------------------------------------------ block (chunked) form
+def run_chunked(gd, q, k, v, a, b, S0=None, inplace=False):
+    tS = None if S0 is None else to_dev(S0, "f32")
+    o, S = gd.kda_prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(a, "f32"),
+                          to_dev(b, "f32"), tS, form="chunked", chunk=64, S_out=tS if inplace else None)
+    return to_host(o), to_host(S)
+
+
+@pytest.mark.parametrize("B,H,T,with_state", [(1, 2, 300, True), (2, 1, 64, False), (1, 3, 65, True),
+                                               (1, 1, 1, True), (2, 2, 777, True), (1, 2, 2000, False),
+                                               (4, 16, 130, True)])
+def test_kda_chunked(gd, B, H, T, with_state):
+    d = 128
+    q, k, v, a, b = synth.kda_batch(79, B, H, T, d, d, "bf16")
+    S0 = synth.state_batch(80, B, H, d, d, 0.05) if with_state else None
+    o_ref, S_ref = ob.kda(q, k, v, a, b, S0, form="chunked")
+    o, S = run_chunked(gd, q, k, v, a, b, S0, inplace=with_state)
+    report(f"kda chunked B={B} H={H} T={T} o", slice_err(o, o_ref), TOL["bf16"])
+    report("  S", slice_err(S, S_ref), TOL["bf16"])
+
+
+def test_kda_chunked_strong_decay(gd):
+    """Chunks whose decay span exceeds the factored range take the exact path;
+    channels without decay and with near-total decay side by side."""
+    B, H, T, d = 1, 2, 400, 128
+    q, k, v, a, b = synth.kda_batch(81, B, H, T, d, d, "bf16")
+    a[..., ::2] = np.maximum(a[..., ::2] ** 40, np.float32(1e-30))   # decay values stay positive
+    a[..., 1::4] = 1.0
+    a[..., 200:, :] = np.maximum(a[..., 200:, :], 0.9)   # later chunks back on the factored path
+    o_ref, S_ref = ob.kda(q, k, v, a, b, form="chunked")
+    o, S = run_chunked(gd, q, k, v, a, b)
+    report("kda chunked strong decay o", slice_err(o, o_ref), TOL["bf16"])
+    report("  S", slice_err(S, S_ref), TOL["bf16"])
+
+
+def test_kda_chunked_uniform_is_gated_delta(gd):
+    B, H, T, d = 1, 2, 500, 128
+    q, k, v, a, b = synth.kda_batch(82, B, H, T, d, d, "bf16")
+    a[:] = a[..., :1]
+    o_ref, S_ref = ob.gdn(q, k, v, a[..., 0], b, form="chunked")
+    o, S = run_chunked(gd, q, k, v, a, b)
+    report("kda chunked, equal decays vs gated delta o", slice_err(o, o_ref), TOL["bf16"])
+    report("  S", slice_err(S, S_ref), TOL["bf16"])
+
+
+def test_kda_chunked_matches_recurrent_kernel(gd):
+    """The block form against the token-serial kernel on the same inputs."""
+    B, H, T, d = 2, 4, 1000, 128
+    q, k, v, a, b = synth.kda_batch(83, B, H, T, d, d, "bf16")
+    S0 = synth.state_batch(84, B, H, d, d, 0.05)
+    o_c, S_c = run_chunked(gd, q, k, v, a, b, S0)
+    o_r, S_r = run(gd, q, k, v, a, b, "bf16", S0)
+    report("kda chunked vs recurrent kernel o", slice_err(o_c, o_r), TOL["bf16"])
+    report("  S", slice_err(S_c, S_r), TOL["bf16"])
+
+
+def test_kda_chunked_workload_2x16x8192(gd):
+    """The bench workload on every head; the oracle on four heads."""
+    w = synth.WORKLOADS["kda_bf16_2x16x8192"]
+    B, H, T, d = w["B"], w["H"], w["T"], w["dk"]
+    q, k, v, a, b = synth.kda_batch(w["seed"], B, H, T, d, d, "bf16")
+    o, S = run_chunked(gd, q, k, v, a, b)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    heads = [(0, 0), (0, 7), (1, 3), (1, 15)]
+    o_ref, S_ref = ob.kda(q, k, v, a, b, form="chunked", heads=heads)
+    for bb, hh in heads:
+        report(f"kda workload head ({bb},{hh}) o", slice_err(o[bb:bb + 1, hh:hh + 1], o_ref[bb:bb + 1, hh:hh + 1]),
+               TOL["bf16"])
+        report("  S", slice_err(S[bb:bb + 1, hh:hh + 1], S_ref[bb:bb + 1, hh:hh + 1]), TOL["bf16"])
