@@ -102,35 +102,58 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
     unsigned char* rec = ws + (static_cast<size_t>(bh) * NC + n) * kRecord;
 
     if (tid == 0) sm.span = 0;
-    // ---- g (threads 0..127, one channel each) | raw tiles (threads 128..255)
-    if (tid < D) {
-        const int c = tid;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int t = 0; t < C; ++t) {
-            float a = 1.f;
-            if (t < len) a = scalar_gate ? alpha[row0 + t] : alpha[(row0 + t) * D + c];
-            acc += __logf(a);
-            sm.g[t][c] = acc;
-        }
-    } else {
-        const int u = tid - D;                   // 128 threads, 16 bytes each: 8 rows of 256 B per pass
-        const int c8 = (u & 15) * 8;
+    // ---- every input load of the chunk first (coalesced 16-byte pieces): log
+    // alpha into g, raw k, v, q tiles; then the running sums of g
+    {
+        float4 al[8];
+        uint4 kk[4], vv[4], qq[4];
 #pragma unroll
-        for (int it = 0; it < C / 8; ++it) {
-            const int t = it * 8 + (u >> 4);
-            uint4 kk = make_uint4(0, 0, 0, 0), vv = kk, qq = kk;
+        for (int it = 0; it < 8; ++it) {           // alpha: 64 x 128 fp32 = 2048 float4
+            const int e = it * kTileThreads + tid, t = e >> 5, c4 = (e & 31) * 4;
+            al[it] = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (t < len) {
+                if (scalar_gate) {
+                    const float a = alpha[row0 + t];
+                    al[it] = make_float4(a, a, a, a);
+                } else {
+                    al[it] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c4);
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {           // k, v, q: 64 x 128 bf16 = 1024 pieces each
+            const int e = it * kTileThreads + tid, t = e >> 4, c8 = (e & 15) * 8;
+            kk[it] = vv[it] = qq[it] = make_uint4(0, 0, 0, 0);
             if (t < len) {
                 const size_t gi = (row0 + t) * D + c8;
-                kk = *reinterpret_cast<const uint4*>(k + gi);
-                vv = *reinterpret_cast<const uint4*>(v + gi);
-                qq = *reinterpret_cast<const uint4*>(q + gi);
+                kk[it] = *reinterpret_cast<const uint4*>(k + gi);
+                vv[it] = *reinterpret_cast<const uint4*>(v + gi);
+                qq[it] = *reinterpret_cast<const uint4*>(q + gi);
             }
-            *reinterpret_cast<uint4*>(&sm.K[t][c8]) = kk;
-            *reinterpret_cast<uint4*>(&sm.V[t][c8]) = vv;
-            *reinterpret_cast<uint4*>(&sm.Qp[t][c8]) = qq;
         }
-        if (u < C) sm.beta[u] = u < len ? beta[row0 + u] : 0.f;
+        if (tid < C) sm.beta[tid] = tid < len ? beta[row0 + tid] : 0.f;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int e = it * kTileThreads + tid, t = e >> 5, c4 = (e & 31) * 4;
+            *reinterpret_cast<float4*>(&sm.g[t][c4]) =
+                make_float4(__logf(al[it].x), __logf(al[it].y), __logf(al[it].z), __logf(al[it].w));
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int e = it * kTileThreads + tid, t = e >> 4, c8 = (e & 15) * 8;
+            *reinterpret_cast<uint4*>(&sm.K[t][c8]) = kk[it];
+            *reinterpret_cast<uint4*>(&sm.V[t][c8]) = vv[it];
+            *reinterpret_cast<uint4*>(&sm.Qp[t][c8]) = qq[it];
+        }
+    }
+    __syncthreads();
+    if (tid < D) {   // running sum over the chunk's tokens, one channel per thread
+        float acc = 0.f;
+#pragma unroll 16
+        for (int t = 0; t < C; ++t) {
+            acc += sm.g[t][tid];
+            sm.g[t][tid] = acc;
+        }
     }
     __syncthreads();
     if (tid < D) {
@@ -245,12 +268,26 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             x[r] = col < D ? sm.beta[r] * bf(sm.K[r][col]) * __expf(sm.g[r][col]) : sm.beta[r] * bf(sm.V[r][col - D]);
         // (right-hand sides first, then the sweep: one fused loop made the
         // compiler keep every right-hand side live and spill)
+        // row r + 1 of L is read while row r is used (software pipelined:
+        // otherwise every row waits for its own LDS reads)
+        float4 cur[C / 4], nxt[C / 4];
+        cur[0] = *reinterpret_cast<const float4*>(&sm.L[1][0]);
 #pragma unroll
         for (int r = 1; r < C; ++r) {
-            float acc = x[r];
+            if (r + 1 < C) {
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc = fmaf(-sm.L[r][j], x[j], acc);
-            x[r] = acc;
+                for (int j4 = 0; j4 < (r + 4) / 4; ++j4) nxt[j4] = *reinterpret_cast<const float4*>(&sm.L[r + 1][4 * j4]);
+            }
+            float acc[4] = {x[r], 0.f, 0.f, 0.f};   // four chains: the sums are not one long dependency
+#pragma unroll
+            for (int j = 0; j < r; ++j) {
+                const float4 l = cur[j >> 2];
+                const float lj = (j & 3) == 0 ? l.x : (j & 3) == 1 ? l.y : (j & 3) == 2 ? l.z : l.w;
+                acc[j & 3] = fmaf(-lj, x[j], acc[j & 3]);
+            }
+            x[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+            for (int j4 = 0; j4 < C / 4; ++j4) cur[j4] = nxt[j4];
         }
         if (col < D) {
             u16* W = reinterpret_cast<u16*>(rec + oW);
@@ -375,15 +412,26 @@ __global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(int BH, int T, i
     __syncthreads();
     const unsigned char* rec0 = ws + static_cast<size_t>(bh) * NC * kRecord;
     const size_t orow = static_cast<size_t>(bh) * T;
-    ChunkOps a, b;
-    load_ops(a, rec0, w, cb, r, gg);
-    for (int n = 0; n < NC; n += 2) {
-        load_ops(b, rec0 + static_cast<size_t>(min(n + 1, NC - 1)) * kRecord, w, cb, r, gg);
-        scan_chunk(sm, a, P, w, r, gg, o, orow + static_cast<size_t>(n) * C, min(C, T - n * C), cb);
-        load_ops(a, rec0 + static_cast<size_t>(min(n + 2, NC - 1)) * kRecord, w, cb, r, gg);
-        if (n + 1 < NC)
-            scan_chunk(sm, b, P, w, r, gg, o, orow + static_cast<size_t>(n + 1) * C, min(C, T - (n + 1) * C), cb);
+    // tiles of chunks n+1 and n+2 are in flight while chunk n runs (three
+    // register sets in rotation; indices past the end reload the last chunk)
+    ChunkOps a, b, c;
+    auto rec = [&](int m) { return rec0 + static_cast<size_t>(min(m, NC - 1)) * kRecord; };
+    auto run = [&](const ChunkOps& op, int m) {
+        scan_chunk(sm, op, P, w, r, gg, o, orow + static_cast<size_t>(m) * C, min(C, T - m * C), cb);
+    };
+    load_ops(a, rec(0), w, cb, r, gg);
+    load_ops(b, rec(1), w, cb, r, gg);
+    int n = 0;
+    for (; n + 3 <= NC; n += 3) {   // no branches around the chunks: the wait counts stay exact
+        load_ops(c, rec(n + 2), w, cb, r, gg);
+        run(a, n);
+        load_ops(a, rec(n + 3), w, cb, r, gg);
+        run(b, n + 1);
+        load_ops(b, rec(n + 4), w, cb, r, gg);
+        run(c, n + 2);
     }
+    if (n < NC) run(a, n);
+    if (n + 1 < NC) run(b, n + 1);
     if (S_out) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
