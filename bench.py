@@ -9,7 +9,7 @@ HBM.  `value` is prefill tokens/s (B*T tokens per step).  In the same run,
 each reported beside the headline: the decode workload (256 sequences x 32
 heads, d = 128, fp32 state, 1000 steps) as state HBM GB/s; the normalised and
 the scalar-gated linear-attention prefills; the fused pre-operations of a
-Gated DeltaNet layer; the KDA decode and recurrent prefill; a packed batch of
+Gated DeltaNet layer; the KDA decode and prefill (block and recurrent forms); a packed batch of
 16 sequences of mixed lengths with state snapshots; and the fp64 CPU oracle on
 a bounded sample of the prefill workload.  Prints one JSON line.
 
@@ -304,23 +304,41 @@ def main():
     kda_dec_gbps = kda_dec_bytes / (kda_dec_ms * 1e-3) / 1e9
     del Sk, kpool
 
-    # -------------------------------------------- KDA prefill (recurrent form)
+    # ------------------------- KDA prefill: block form (and the recurrent form)
     wkp = synth.WORKLOADS[KDA_PREFILL]
     Bk, Hkp, Tk, dkp = wkp["B"], wkp["H"], wkp["T"], wkp["dk"]
     kq, kk, kv, ka, kb = synth.kda_batch(wkp["seed"], Bk, Hkp, Tk, dkp, dkp, "bf16")
-    kda_in = tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (kq, kk, kv)) + \
-        tuple(torch.from_numpy(x).to(dev) for x in (ka, kb))
+    kda_sets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (kq, kk, kv)) +
+                tuple(torch.from_numpy(x).to(dev) for x in (ka, kb)) for _ in range(2)]
     del kq, kk, kv, ka, kb
-    gd.kda_prefill(*kda_in)
-    torch.cuda.synchronize()
-    kpe = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    kpe[0].record()
+    kda_ws = torch.empty(gd.la_workspace_bytes("kda_prefill", "bf16", Bk, Hkp, Tk, dkp, dkp, "chunked", 64),
+                         dtype=torch.uint8, device=dev)
+    kda_out = torch.empty((Bk, Hkp, Tk, dkp), dtype=torch.bfloat16, device=dev)
+    kda_S = torch.empty((Bk, Hkp, dkp, dkp), dtype=torch.float32, device=dev)
+
+    def kcall(i, form="chunked"):
+        gd.kda_prefill(*kda_sets[i % 2], form=form, out=kda_out, S_out=kda_S, workspace=kda_ws)
+
     for i in range(2):
-        gd.kda_prefill(*kda_in)
+        kcall(i)
+    torch.cuda.synchronize()
+    kpe = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    kpe[0].record()
+    for i in range(args.la_steps):
+        kcall(i)
         kpe[i + 1].record()
     torch.cuda.synchronize()
-    kda_pre_ms = float(np.mean([kpe[i].elapsed_time(kpe[i + 1]) for i in range(2)]))
-    del kda_in
+    kda_pre_ms = float(np.mean([kpe[i].elapsed_time(kpe[i + 1]) for i in range(args.la_steps)]))
+    # q, k, v, o in bf16, per-channel alpha and beta in fp32
+    kda_pre_bytes = Bk * Hkp * Tk * (4 * dkp * 2 + dkp * 4 + 4)
+    kda_pre_gbps = kda_pre_bytes / (kda_pre_ms * 1e-3) / 1e9
+    kre = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    kre[0].record()
+    kcall(0, "recurrent")
+    kre[1].record()
+    torch.cuda.synchronize()
+    kda_rec_ms = kre[0].elapsed_time(kre[1])
+    del kda_sets, kda_ws, kda_out, kda_S
 
     # ------------------------------- packed variable-length batch + snapshots
     wv = synth.WORKLOADS[VARLEN]
@@ -422,8 +440,14 @@ def main():
                                     "achieved": kda_dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                     "frac": kda_dec_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kda_dec_bytes,
                                     "avg_launch_ms": kda_dec_ms}},
-        "kda_prefill": {"workload": "KDA prefill B=2 H=16 T=8192 d=128, recurrent form (token by token), bf16 I/O",
-                        "calls": 2, "ms_per_call": kda_pre_ms, "tokens_per_s": Bk * Tk / (kda_pre_ms * 1e-3)},
+        "kda_prefill": {"workload": "KDA prefill B=2 H=16 T=8192 d=128 chunk=64 (block form: tile pass + "
+                                    "column-parallel scan), bf16 I/O, fp32 state", "calls": args.la_steps,
+                        "ms_per_call": kda_pre_ms, "tokens_per_s": Bk * Tk / (kda_pre_ms * 1e-3),
+                        "recurrent_form_ms": kda_rec_ms,
+                        "roofline": {"kernel": "kda_tile_kernel + kda_scan_kernel", "bound": "hbm",
+                                     "achieved": kda_pre_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": kda_pre_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kda_pre_bytes,
+                                     "avg_launch_ms": kda_pre_ms}},
         "varlen_prefill": {"workload": f"gated delta prefill, packed batch of {wv['N']} sequences ({wv['T_total']} "
                                        f"tokens, lengths {int(min(lens))}..{int(max(lens))}), H=16 d=128 chunk=64, "
                                        f"snapshots every {snapv} tokens ({nsnap})",
