@@ -25,6 +25,7 @@ __all__ = [
     "gdn_prefill_prep",
     "gdn_prefill_scan",
     "gdn_preprocess",
+    "gdn_preprocess_varlen",
     "lin_attn_decode_step",
     "la_workspace_bytes",
     "la_status_str",
@@ -80,6 +81,8 @@ def _load():
     lib.gdn_prefill_varlen.restype = I
     lib.gdn_preprocess.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdn_preprocess.restype = I
+    lib.gdn_preprocess_varlen.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gdn_preprocess_varlen.restype = I
     lib.gdn_prefill_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P, Z, P]
     lib.gdn_prefill_prep.restype = I
     lib.gdn_prefill_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, Z, P]
@@ -297,6 +300,43 @@ def gdn_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, form="chunked"
     if st != 0:
         raise LinAttnError(st, "gdn_prefill_varlen")
     return out, S_out, (S_snap[:snap_count] if S_snap is not None else None)
+
+
+def gdn_preprocess_varlen(x, conv_w, a_logit, b_logit, H, dk, dv, cu_seqlens, conv_state=None, want_state=True,
+                          stream=None):
+    """Fused pre-operations over a packed batch; returns (q, k, v, alpha, beta,
+    conv_state_out).
+
+    x [T_total, H*(2dk+dv)]; a_logit, b_logit [T_total, H] float32;
+    cu_seqlens [N+1] int32 on the device; conv_state [N, 3, C] or None.
+    Outputs q, k [H, T_total, dk], v [H, T_total, dv], alpha, beta
+    [H, T_total] (the layout of gdn_prefill_varlen) and the next states.
+    """
+    torch = _torch()
+    T, C = x.shape
+    N = cu_seqlens.numel() - 1
+    if C != H * (2 * dk + dv):
+        raise ValueError(f"x has {C} channels, expected H*(2dk+dv) = {H * (2 * dk + dv)}")
+    dt = _dtype_code(x.dtype)
+    _check(x, "x", x.dtype)
+    _check(conv_w, "conv_w", torch.float32, (C, 4))
+    _check(a_logit, "a_logit", torch.float32, (T, H))
+    _check(b_logit, "b_logit", torch.float32, (T, H))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    _check(conv_state, "conv_state", x.dtype, (N, 3, C))
+    dev = x.device
+    q = torch.empty((H, T, dk), dtype=x.dtype, device=dev)
+    k = torch.empty((H, T, dk), dtype=x.dtype, device=dev)
+    v = torch.empty((H, T, dv), dtype=x.dtype, device=dev)
+    alpha = torch.empty((H, T), dtype=torch.float32, device=dev)
+    beta = torch.empty((H, T), dtype=torch.float32, device=dev)
+    st_out = torch.empty((N, 3, C), dtype=x.dtype, device=dev) if want_state else None
+    st = _load().gdn_preprocess_varlen(dt, N, T, H, dk, dv, _ptr(cu_seqlens), _ptr(x), _ptr(conv_w), _ptr(a_logit),
+                                       _ptr(b_logit), _ptr(conv_state), _ptr(st_out), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _stream_ptr(stream, dev))
+    if st != 0:
+        raise LinAttnError(st, "gdn_preprocess_varlen")
+    return q, k, v, alpha, beta, st_out
 
 
 def kda_prefill(q, k, v, alpha, beta, S0=None, form="recurrent", chunk=64, out=None, S_out=None, want_state=True,

@@ -336,6 +336,45 @@ la_status gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const v
                                               static_cast<hipStream_t>(stream)));
 }
 
+la_status gdn_preprocess_varlen(int dtype, int N, int T_total, int H, int dk, int dv, const int* cu_seqlens,
+                                const void* x, const float* conv_w, const float* a_logit, const float* b_logit,
+                                const void* conv_state, void* conv_state_out, void* q, void* k, void* v, float* alpha,
+                                float* beta, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (!sizes_ok(N, H, T_total) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (static_cast<long long>(H) * (2 * dk + dv) > 0x7fffffffLL) return LA_ERR_SHAPE;
+    if (static_cast<long long>(H) * ((T_total + 127) / 128 > 0 ? (T_total + 127) / 128 : 1) > 0x7fffffffLL)
+        return LA_ERR_SHAPE;
+    if (N == 0 || H == 0) return LA_OK;
+    if (cu_seqlens == nullptr || conv_w == nullptr) return LA_ERR_NULL;
+    if (T_total > 0 && (x == nullptr || a_logit == nullptr || b_logit == nullptr || q == nullptr || k == nullptr ||
+                        v == nullptr || alpha == nullptr || beta == nullptr))
+        return LA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return LA_ERR_ALIGN;
+    for (const void* p : {x, static_cast<const void*>(conv_w), static_cast<const void*>(a_logit),
+                          static_cast<const void*>(b_logit), conv_state, static_cast<const void*>(conv_state_out),
+                          static_cast<const void*>(q), static_cast<const void*>(k), static_cast<const void*>(v),
+                          static_cast<const void*>(alpha), static_cast<const void*>(beta)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const size_t es = io_size(dtype);
+    const size_t C = static_cast<size_t>(H) * (2 * dk + dv);
+    const size_t rows = static_cast<size_t>(T_total);
+    const size_t nx = rows * C * es, nl = rows * H * sizeof(float), nst = static_cast<size_t>(N) * 3 * C * es;
+    const size_t nqk = rows * H * dk * es, nv = rows * H * dv * es;
+    const Span in[] = {{x, nx}, {conv_w, C * 4 * sizeof(float)}, {a_logit, nl}, {b_logit, nl}, {conv_state, nst},
+                       {cu_seqlens, (static_cast<size_t>(N) + 1) * sizeof(int)}};
+    const Span outs[] = {{conv_state_out, nst}, {q, nqk}, {k, nqk}, {v, nv}, {alpha, nl}, {beta, nl}};
+    for (const Span& a : outs) {
+        for (const Span& b : in)
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        for (const Span& b : outs)
+            if (&a != &b && overlaps(a, b)) return LA_ERR_ARG;
+    }
+    return from_hip(la::launch_gdn_preprocess_varlen(dtype, N, T_total, H, dk, dv, cu_seqlens, x, conv_w, a_logit,
+                                                     b_logit, conv_state, conv_state_out, q, k, v, alpha, beta,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int dv, const int* cu_seqlens,
                              const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                              const float* S0, void* o, float* S_out, int snap_interval, int snap_count,

@@ -109,5 +109,11 @@ hipError_t launch_gla_mfma(int B, int H, int T, const void* q, const void* k, co
 hipError_t launch_gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv, const void* x, const float* w,
                                  const float* a_logit, const float* b_logit, const void* st_in, void* st_out,
                                  void* q, void* k, void* v, float* alpha, float* beta, hipStream_t stream);
+// Packed batch: N sequences on one token axis of T tokens (cu [N+1] on the
+// device), states [N,3,C]; outputs [H,T,d] and [H,T].
+hipError_t launch_gdn_preprocess_varlen(int dtype, int N, int T, int H, int dk, int dv, const int* cu, const void* x,
+                                        const float* w, const float* a_logit, const float* b_logit,
+                                        const void* st_in, void* st_out, void* q, void* k, void* v, float* alpha,
+                                        float* beta, hipStream_t stream);
 
 }  // namespace la

@@ -91,9 +91,21 @@ __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-
 // output row is divided by its Euclidean norm (a zero row stays zero).
 // Called by every thread of the workgroup with len > 0 (the xor reductions
 // need whole waves).
+// Packed batch: sequence n is tokens cu[n] .. cu[n+1] of the projections
+// (one sequence axis, B = 1); a tap before its sequence's first token reads
+// row 3 + (tap - start) of that sequence's carried state st[n] ([3][C]), or
+// zero when there is none.  cu == nullptr: the uniform layout.
+template <class E>
+struct Seqs {
+    const int* cu;
+    int N;
+    const E* st;
+};
+
 template <int D, bool NORM, class E>
 __device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st, const float* __restrict__ w, int C,
-                                          int cbase, int t0, int len, int T, E* __restrict__ dst, int tid) {
+                                          int cbase, int t0, int len, int T, E* __restrict__ dst, int tid,
+                                          const Seqs<E>& sq) {
     constexpr int L = D / 8;                                          // lanes per token row
     constexpr int TPL = kTile * L / kThreads >= 1 ? kTile * L / kThreads : 1;   // tokens per lane
     constexpr int NL = kTile / TPL * L;                               // lanes in use
@@ -133,15 +145,51 @@ __device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st,
 #pragma unroll
         for (int e = 0; e < 8; ++e) xr[r][e] = live ? xr[r][e] : 0.f;
     }
+    // packed batch: the sequence of this lane's first token (binary search)
+    int n = 0;
+    if (sq.cu != nullptr) {
+        const int tf = t0 + jb;
+        int lo = 0, hi = sq.N;   // the last n with cu[n] <= tf
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sq.cu[mid] <= tf) lo = mid; else hi = mid;
+        }
+        n = lo;
+    }
 #pragma unroll
     for (int s = 0; s < TPL; ++s) {
+        float tap[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tap[i][e] = xr[s + i][e];
+        if (sq.cu != nullptr) {
+            const int t = t0 + jb + s;
+            while (n + 1 < sq.N && sq.cu[n + 1] <= t) ++n;
+            const int d = max(0, t - min(max(sq.cu[n], 0), T));   // position inside its sequence
+            if (d < 3) {   // taps before the sequence start: its carried state (or zero)
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    if (i < 3 - d) {
+                        if (sq.st != nullptr) {
+                            Raw<E> rs;
+                            rs.load(sq.st + (static_cast<size_t>(n) * 3 + d + i) * C + c0);
+                            rs.get(tap[i]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) tap[i][e] = 0.f;
+                        }
+                    }
+                }
+            }
+        }
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float acc = wv[e][0] * xr[s][e];
-            acc = fmaf(wv[e][1], xr[s + 1][e], acc);
-            acc = fmaf(wv[e][2], xr[s + 2][e], acc);
-            y[e] = fmaf(wv[e][3], xr[s + 3][e], acc);
+            float acc = wv[e][0] * tap[0][e];
+            acc = fmaf(wv[e][1], tap[1][e], acc);
+            acc = fmaf(wv[e][2], tap[2][e], acc);
+            y[e] = fmaf(wv[e][3], tap[3][e], acc);
         }
         if constexpr (NORM) {
             float ss = 0.f;
@@ -159,7 +207,7 @@ __device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st,
 
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
-    int T, int H, int tiles, const typename IO::T* __restrict__ x, const float* __restrict__ w,
+    int T, int H, int tiles, const int* cu, int N, const typename IO::T* __restrict__ x, const float* __restrict__ w,
     const float* __restrict__ a_logit, const float* __restrict__ b_logit, const typename IO::T* st_in,
     typename IO::T* st_out, typename IO::T* __restrict__ q, typename IO::T* __restrict__ k,
     typename IO::T* __restrict__ v, float* __restrict__ alpha, float* __restrict__ beta) {
@@ -171,14 +219,16 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     const int t0 = tile * kTile;
     const int len = max(0, min(kTile, T - t0));
     const E* xb = x + static_cast<size_t>(b) * T * C;
-    const E* st = st_in ? st_in + static_cast<size_t>(b) * 3 * C : nullptr;
+    // packed batch: one sequence axis; states are per sequence and handled in conv_part
+    const Seqs<E> sq{cu, N, cu ? st_in : nullptr};
+    const E* st = (st_in && !cu) ? st_in + static_cast<size_t>(b) * 3 * C : nullptr;
     const size_t row0 = (static_cast<size_t>(b) * H + h) * T;   // row (b, h, t = 0) of the outputs
     const int tid = threadIdx.x;
 
     if (len > 0) {   // (T == 0: only the state below)
-        conv_part<DK, true>(xb, st, w, C, h * DK, t0, len, T, q + row0 * DK, tid);
-        conv_part<DK, true>(xb, st, w, C, H * DK + h * DK, t0, len, T, k + row0 * DK, tid);
-        conv_part<DV, false>(xb, st, w, C, 2 * H * DK + h * DV, t0, len, T, v + row0 * DV, tid);
+        conv_part<DK, true>(xb, st, w, C, h * DK, t0, len, T, q + row0 * DK, tid, sq);
+        conv_part<DK, true>(xb, st, w, C, H * DK + h * DK, t0, len, T, k + row0 * DK, tid, sq);
+        conv_part<DV, false>(xb, st, w, C, 2 * H * DK + h * DV, t0, len, T, v + row0 * DV, tid, sq);
         for (int j = tid; j < len; j += kThreads) {
             const size_t li = (static_cast<size_t>(b) * T + t0 + j) * H + h;
             alpha[row0 + t0 + j] = sigmoid(a_logit[li]);
@@ -186,7 +236,8 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
         }
     }
     // carried state: the last three tokens of [state; x], this head's channels
-    if (st_out != nullptr && tile == tiles - 1) {
+    // (packed batches: written per sequence by gdn_state_out_kernel)
+    if (st_out != nullptr && cu == nullptr && tile == tiles - 1) {
         constexpr int nch = 2 * DK + DV;
         for (int e = tid; e < 3 * nch; e += kThreads) {
             const int r = e / nch, cc = e % nch;
@@ -204,15 +255,38 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     }
 }
 
+// Packed batch: the next conv state of every sequence, the last three
+// tokens of [state; its tokens].
+template <class IO>
+__global__ __launch_bounds__(256) void gdn_state_out_kernel(int N, int T, int C, const int* cu,
+                                                            const typename IO::T* __restrict__ x,
+                                                            const typename IO::T* st_in, typename IO::T* st_out) {
+    const size_t total = static_cast<size_t>(N) * 3 * C;
+    for (size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; e < total;
+         e += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const int c = static_cast<int>(e % C);
+        const int j = static_cast<int>((e / C) % 3);
+        const int n = static_cast<int>(e / (static_cast<size_t>(3) * C));
+        const int s0 = min(max(cu[n], 0), T), e1 = max(min(max(cu[n + 1], 0), T), s0);
+        const int src = e1 - 3 + j;
+        float val = 0.f;
+        if (src >= s0)
+            val = IO::load(x, static_cast<size_t>(src) * C + c);
+        else if (st_in != nullptr)
+            val = IO::load(st_in, (static_cast<size_t>(n) * 3 + 3 + (src - s0)) * C + c);
+        IO::store(st_out, e, val);
+    }
+}
+
 template <class IO, int DK>
-hipError_t launch_dv(int B, int T, int H, int dv, const void* x, const float* w, const float* al, const float* bl,
-                     const void* st_in, void* st_out, void* q, void* k, void* v, float* alpha, float* beta,
-                     hipStream_t stream) {
+hipError_t launch_dv(int B, int T, int H, int dv, const int* cu, int N, const void* x, const float* w,
+                     const float* al, const float* bl, const void* st_in, void* st_out, void* q, void* k, void* v,
+                     float* alpha, float* beta, hipStream_t stream) {
     using E = typename IO::T;
     const int tiles = T > 0 ? (T + kTile - 1) / kTile : 1;   // T == 0: one workgroup per head writes the state
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * H * tiles)), block(kThreads);
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, block, 0, stream, T, H, tiles, static_cast<const E*>(x), w, al, bl,
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, T, H, tiles, cu, N, static_cast<const E*>(x), w, al, bl,
                            static_cast<const E*>(st_in), static_cast<E*>(st_out), static_cast<E*>(q),
                            static_cast<E*>(k), static_cast<E*>(v), alpha, beta);
         return hipGetLastError();
@@ -227,16 +301,25 @@ hipError_t launch_dv(int B, int T, int H, int dv, const void* x, const float* w,
 }
 
 template <class IO>
-hipError_t launch_io(int B, int T, int H, int dk, int dv, const void* x, const float* w, const float* al,
-                     const float* bl, const void* st_in, void* st_out, void* q, void* k, void* v, float* alpha,
-                     float* beta, hipStream_t stream) {
+hipError_t launch_io(int B, int T, int H, int dk, int dv, const int* cu, int N, const void* x, const float* w,
+                     const float* al, const float* bl, const void* st_in, void* st_out, void* q, void* k, void* v,
+                     float* alpha, float* beta, hipStream_t stream) {
+    hipError_t e;
     switch (dk) {
-        case 16: return launch_dv<IO, 16>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
-        case 32: return launch_dv<IO, 32>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
-        case 64: return launch_dv<IO, 64>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
-        case 128: return launch_dv<IO, 128>(B, T, H, dv, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream);
+        case 16: e = launch_dv<IO, 16>(B, T, H, dv, cu, N, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream); break;
+        case 32: e = launch_dv<IO, 32>(B, T, H, dv, cu, N, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream); break;
+        case 64: e = launch_dv<IO, 64>(B, T, H, dv, cu, N, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream); break;
+        case 128: e = launch_dv<IO, 128>(B, T, H, dv, cu, N, x, w, al, bl, st_in, st_out, q, k, v, alpha, beta, stream); break;
         default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess || cu == nullptr || st_out == nullptr) return e;
+    using E = typename IO::T;
+    const int C = H * (2 * dk + dv);
+    const size_t total = static_cast<size_t>(N) * 3 * C;
+    const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    hipLaunchKernelGGL(gdn_state_out_kernel<IO>, dim3(blocks), dim3(256), 0, stream, N, T, C, cu,
+                       static_cast<const E*>(x), static_cast<const E*>(st_in), static_cast<E*>(st_out));
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -245,10 +328,23 @@ hipError_t launch_gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv,
                                  const float* a_logit, const float* b_logit, const void* st_in, void* st_out,
                                  void* q, void* k, void* v, float* alpha, float* beta, hipStream_t stream) {
     if (B <= 0 || H <= 0) return hipSuccess;
-    return dtype == kBF16 ? launch_io<IoBF16>(B, T, H, dk, dv, x, w, a_logit, b_logit, st_in, st_out, q, k, v, alpha,
-                                              beta, stream)
-                          : launch_io<IoF32>(B, T, H, dk, dv, x, w, a_logit, b_logit, st_in, st_out, q, k, v, alpha,
-                                             beta, stream);
+    return dtype == kBF16 ? launch_io<IoBF16>(B, T, H, dk, dv, nullptr, 0, x, w, a_logit, b_logit, st_in, st_out, q,
+                                              k, v, alpha, beta, stream)
+                          : launch_io<IoF32>(B, T, H, dk, dv, nullptr, 0, x, w, a_logit, b_logit, st_in, st_out, q,
+                                             k, v, alpha, beta, stream);
+}
+
+hipError_t launch_gdn_preprocess_varlen(int dtype, int N, int T, int H, int dk, int dv, const int* cu, const void* x,
+                                        const float* w, const float* a_logit, const float* b_logit,
+                                        const void* st_in, void* st_out, void* q, void* k, void* v, float* alpha,
+                                        float* beta, hipStream_t stream) {
+    if (N <= 0 || H <= 0) return hipSuccess;
+    if (T == 0 && st_out == nullptr) return hipSuccess;
+    // (T == 0: one workgroup per head runs with nothing to convolve; the states pass through)
+    return dtype == kBF16 ? launch_io<IoBF16>(1, T, H, dk, dv, cu, N, x, w, a_logit, b_logit, st_in, st_out, q, k, v,
+                                              alpha, beta, stream)
+                          : launch_io<IoF32>(1, T, H, dk, dv, cu, N, x, w, a_logit, b_logit, st_in, st_out, q, k, v,
+                                             alpha, beta, stream);
 }
 
 }  // namespace la

@@ -315,6 +315,32 @@ la_status gdn_preprocess(int dtype, int B, int T, int H, int dk, int dv,
                          void* stream);
 
 /*
+ * gdn_preprocess_varlen - gdn_preprocess over a packed batch of N sequences
+ * of different lengths, producing the layout gdn_prefill_varlen reads.
+ *
+ * Same operations and sources as gdn_preprocess, per sequence: the
+ * convolution of sequence n never reaches into another sequence; its three
+ * tokens before the first come from conv_state[n] (zeros when conv_state is
+ * NULL), and conv_state_out[n] receives the last three tokens of
+ * [conv_state[n]; its tokens].  Layout (device pointers):
+ *   cu_seqlens [N+1] int32 (4-byte aligned): sequence n is tokens
+ *     cu_seqlens[n] .. cu_seqlens[n+1] (non-decreasing from 0 to T_total;
+ *     out-of-range values are clamped, never read past a buffer);
+ *   x [T_total, C], a_logit, b_logit [T_total, H] float32, conv_w [C, 4]
+ *   float32, conv_state / conv_state_out [N, 3, C] (dtype; NULL allowed, not
+ *   the same memory);
+ *   q, k [H, T_total, dk], v [H, T_total, dv], alpha, beta [H, T_total]
+ *   float32.
+ * Errors as for gdn_preprocess; nothing is launched on error.
+ */
+la_status gdn_preprocess_varlen(int dtype, int N, int T_total, int H, int dk, int dv,
+                                const int* cu_seqlens, const void* x, const float* conv_w,
+                                const float* a_logit, const float* b_logit,
+                                const void* conv_state, void* conv_state_out,
+                                void* q, void* k, void* v, float* alpha, float* beta,
+                                void* stream);
+
+/*
  * la_workspace_bytes - device workspace needed by one call of `fn` with the
  * given arguments (0 when none is needed).  Returns (size_t)-1 when the
  * arguments are invalid or the combination is not supported.

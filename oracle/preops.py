@@ -65,3 +65,28 @@ def gdn_preprocess(x, w, a_logit, b_logit, H, dk, dv, state=None):
     alpha = sigmoid(np.asarray(a_logit).T)
     beta = sigmoid(np.asarray(b_logit).T)
     return l2_normalize(q), l2_normalize(k), v, alpha, beta, new_state
+
+
+def gdn_preprocess_varlen(x, w, a_logit, b_logit, H, dk, dv, cu_seqlens, state=None):
+    """A packed batch: sequence n is rows cu[n] .. cu[n+1] of x [T_total, C]
+    (a_logit, b_logit [T_total, H]); each runs gdn_preprocess on its own rows
+    from its own state (state [N, 3, C], zeros when None).  Returns q, k
+    [H, T_total, dk], v [H, T_total, dv], alpha, beta [H, T_total] and the
+    new states [N, 3, C]."""
+    x = np.asarray(x, dtype=np.float64)
+    T, C = x.shape
+    cu = [int(c) for c in cu_seqlens]
+    N = len(cu) - 1
+    q = np.zeros((H, T, dk))
+    k = np.zeros((H, T, dk))
+    v = np.zeros((H, T, dv))
+    al = np.zeros((H, T))
+    be = np.zeros((H, T))
+    new = np.zeros((N, 3, C))
+    for n in range(N):
+        s, e = cu[n], cu[n + 1]
+        st = None if state is None else state[n]
+        qn, kn, vn, an, bn, new[n] = gdn_preprocess(x[s:e], w, np.asarray(a_logit)[s:e], np.asarray(b_logit)[s:e],
+                                                    H, dk, dv, st)
+        q[:, s:e], k[:, s:e], v[:, s:e], al[:, s:e], be[:, s:e] = qn, kn, vn, an, bn
+    return q, k, v, al, be, new

@@ -48,7 +48,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gla_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
-                            "gdn_preprocess", "kda_prefill", "gdn_prefill_varlen", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
+                            "gdn_preprocess", "gdn_preprocess_varlen", "kda_prefill", "gdn_prefill_varlen", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -323,3 +323,21 @@ def test_varlen_validation(lib):
     rec = lib.la_workspace_bytes(VARLEN, F32, 3, 2, 500, 64, 64, RECURRENT, 0)
     assert 0 < rec < need
     assert vl(N=0) == LA_OK
+
+
+def test_preprocess_varlen_validation(lib):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+
+    def pre(dtype=BF16, N=3, T=100, H=4, dk=128, dv=128, cu=10, x=1, w=2, a=3, b=4, st=None, st_out=None, q=5, k=6,
+            v=7, al=8, be=9):
+        return lib.gdn_preprocess_varlen(dtype, N, T, H, dk, dv, f(cu), f(x), f(w), f(a), f(b), f(st), f(st_out),
+                                         f(q), f(k), f(v), f(al), f(be), None)
+
+    assert pre(dtype=3) == LA_ERR_DTYPE
+    assert pre(dk=48) == LA_ERR_SHAPE
+    assert pre(cu=None) == LA_ERR_NULL
+    assert pre(x=None) == LA_ERR_NULL
+    assert pre(cu=ctypes.c_void_p(BASE + 10 * GiB + 2)) == LA_ERR_ALIGN
+    assert pre(q=10) == LA_ERR_ARG                         # output on top of cu_seqlens
+    assert pre(st=11, st_out=11) == LA_ERR_ARG
+    assert pre(N=0) == LA_OK

@@ -176,3 +176,55 @@ def test_preops_feed_the_gated_delta_prefill(gd):
     o_ref, S_ref = ob.gdn(hq, hk, hv, to_host(al), to_host(be), form="recurrent")
     report("preops -> gdn_prefill o", slice_err(to_host(o), o_ref), TOL["bf16"])
     report("  S", slice_err(to_host(S), S_ref), TOL["bf16"])
+
+
+# ------------------------------------------------------------- packed batches
+def run_varlen(gd, x, w, a, bl, H, dk, dv, cu, dtype, st=None):
+    import torch
+    tst = None if st is None else to_dev(st, dtype)
+    tcu = torch.from_numpy(np.asarray(cu, np.int32)).to("cuda:0")
+    res = gd.gdn_preprocess_varlen(to_dev(x, dtype), to_dev(w, "f32"), to_dev(a, "f32"), to_dev(bl, "f32"), H, dk, dv,
+                                   tcu, conv_state=tst)
+    return [to_host(t) for t in res]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lens,H,dk,dv,with_state", [
+    ([5, 0, 2, 130, 1, 300], 2, 128, 128, True), ([64, 64, 129], 3, 64, 32, False),
+    ([1, 1, 1, 3, 200], 2, 16, 64, True), ([1000], 2, 128, 128, True)])
+def test_preprocess_varlen_matches_oracle(gd, dtype, lens, H, dk, dv, with_state):
+    C = H * (2 * dk + dv)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    x, w, a, bl = synth.preops_batch(67, 1, T, H, dk, dv, dtype)
+    x, a, bl = x[0], a[0], bl[0]
+    st = synth.conv_state_batch(68, len(lens), H, dk, dv, dtype) if with_state else None
+    ref = op.gdn_preprocess_varlen(x, w, a, bl, H, dk, dv, cu, st)
+    got = run_varlen(gd, x, w, a, bl, H, dk, dv, cu, dtype, st)
+    # outputs [H, T, d] (rows per head), gates [H, T], states bit-exact
+    compare(f"preops varlen {dtype} lens={lens} H={H} dk={dk} dv={dv}", [g[None] for g in got[:5]] + [got[5]],
+            [r[None] for r in ref[:5]] + [ref[5]], dtype)
+    assert C == x.shape[1]
+
+
+def test_preprocess_varlen_feeds_the_packed_prefill(gd):
+    """Packed pre-operations then the packed chunked prefill, against the
+    oracle's pre-operations then its packed recurrence."""
+    import torch
+    from oracle import varlen as ov
+    H, d = 2, 128
+    lens = [300, 70, 0, 500]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    x, w, a, bl = synth.preops_batch(69, 1, T, H, d, d, "bf16")
+    tcu = torch.from_numpy(cu).to("cuda:0")
+    q, k, v, al, be, _ = gd.gdn_preprocess_varlen(to_dev(x[0], "bf16"), to_dev(w, "f32"), to_dev(a[0], "f32"),
+                                                  to_dev(bl[0], "f32"), H, d, d, tcu, want_state=False)
+    o, S, _ = gd.gdn_prefill_varlen(q, k, v, al, be, tcu, form="chunked")
+    hq, hk, hv, ha, hb = to_host(q), to_host(k), to_host(v), to_host(al), to_host(be)
+    rq, rk, rv, ra, rb, _ = op.gdn_preprocess_varlen(x[0], w, a[0], bl[0], H, d, d, cu)
+    for name, g, r in (("q", hq, rq), ("k", hk, rk), ("v", hv, rv)):
+        check(f"packed chain {name}", g[None], r[None], RTOL["bf16"])
+    o_ref, S_ref, _ = ov.gdn_varlen(hq, hk, hv, ha, hb, cu, form="chunked")
+    report("packed preops -> gdn_prefill_varlen o", slice_err(to_host(o), o_ref, lead=1), TOL["bf16"])
+    report("  S", slice_err(to_host(S), S_ref), TOL["bf16"])

@@ -497,6 +497,38 @@ def pin_preops(ns):
         assert np.abs(be[h] - 1 / (1 + np.exp(-b[:, h]))).max() < 1e-15
 
 
+def pin_preops_varlen(ns):
+    """A packed batch = each sequence alone (the pinned one-sequence
+    function), with history never crossing a sequence boundary: a sequence
+    run after another gives the outputs of the same sequence run alone."""
+    rng = np.random.default_rng(33)
+    H, dk, dv = 2, 3, 2
+    C = H * (2 * dk + dv)
+    lens = [5, 0, 2, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    x = rng.normal(size=(T, C))
+    w = rng.normal(size=(C, 4))
+    a, b = rng.normal(size=(T, H)), rng.normal(size=(T, H))
+    st = rng.normal(size=(len(lens), 3, C))
+    q, k, v, al, be, new = ns.gdn_preprocess_varlen(x, w, a, b, H, dk, dv, cu, st)
+    for n, L in enumerate(lens):
+        s, e = cu[n], cu[n + 1]
+        ref = ns.gdn_preprocess(x[s:e], w, a[s:e], b[s:e], H, dk, dv, st[n])
+        for got, want in zip((q[:, s:e], k[:, s:e], v[:, s:e], al[:, s:e], be[:, s:e], new[n]), ref):
+            assert np.abs(got - want).max(initial=0) < 1e-12
+    # an empty sequence passes its state through; a 2-token one keeps one state row
+    assert np.array_equal(new[1], st[1])
+    assert np.array_equal(new[2][0], st[2][2]) and np.array_equal(new[2][1:], x[cu[2]:cu[3]])
+    # the last sequence alone, from zeros, differs from the packed one only through its state
+    _, _, v0, _, _, _ = ns.gdn_preprocess(x[cu[3]:], w, a[cu[3]:], b[cu[3]:], H, dk, dv)
+    assert np.abs(v0[:, 3:] - v[:, cu[3] + 3:]).max() < 1e-12
+
+
+def test_preops_varlen_pin():
+    pin_preops_varlen(pre_mod)
+
+
 PRE_MUTATIONS = [
     ("y[t] += w[:, i] * xx[t + i]", "y[t] += w[:, 3 - i] * xx[t + i]"),
     ("xx = np.concatenate([prev, x], axis=0)", "xx = np.concatenate([np.zeros_like(prev), x], axis=0)"),
@@ -516,6 +548,19 @@ def test_preops_pins():
 def test_planted_preops_mistake_is_caught(old, new):
     ns = types.SimpleNamespace(**_mutant(pre_mod, old, new))
     assert _fails_some_pin(ns, [pin_preops])
+
+
+PRE_VARLEN_MUTATIONS = [
+    ("st = None if state is None else state[n]", "st = None"),
+    ("q[:, s:e], k[:, s:e], v[:, s:e], al[:, s:e], be[:, s:e] = qn, kn, vn, an, bn",
+     "q[:, s:e], k[:, s:e], v[:, s:e], al[:, s:e], be[:, s:e] = qn, kn, vn, bn, an"),
+]
+
+
+@pytest.mark.parametrize("old,new", PRE_VARLEN_MUTATIONS, ids=[m[1][:40] for m in PRE_VARLEN_MUTATIONS])
+def test_planted_preops_varlen_mistake_is_caught(old, new):
+    ns = types.SimpleNamespace(**_mutant(pre_mod, old, new))
+    assert _fails_some_pin(ns, [pin_preops_varlen])
 
 
 # ------------------------------------------------------------------ KDA
