@@ -8,7 +8,8 @@ d_k = d_v = 128, bf16 activations, fp32 state, chunk 64), inputs resident in
 HBM.  `value` is prefill tokens/s (B*T tokens per step).  In the same run,
 each reported beside the headline: the decode workload (256 sequences x 32
 heads, d = 128, fp32 state, 1000 steps) as state HBM GB/s; the normalised and
-the scalar-gated linear-attention prefills; the fused pre-operations of a
+the scalar-gated linear-attention prefills; the 1 x 16 x 262144 long-context
+prefill; the fused pre-operations of a
 Gated DeltaNet layer; the KDA decode and prefill (block and recurrent forms); a packed batch of
 16 sequences of mixed lengths with state snapshots; and the fp64 CPU oracle on
 a bounded sample of the prefill workload.  Prints one JSON line.
@@ -39,6 +40,7 @@ PREOPS = "preops_bf16_2x16x8192"
 KDA_DECODE = "kda_decode_256x32"
 KDA_PREFILL = "kda_bf16_2x16x8192"
 VARLEN = "gdn_varlen_bf16_16seq_16k"
+LONG = "gdn_bf16_1x16x262144"
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
 # d = d_k = d_v: bytes = q, k, v, o in bf16 + alpha, beta in fp32; flops as
@@ -85,6 +87,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--la-steps", type=int, default=10, help="timed calls of the linear-attention prefill")
+    ap.add_argument("--long-calls", type=int, default=2,
+                    help="timed calls of the 1 x 16 x 262144 prefill (0 skips that leg, e.g. under a profiler)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -277,6 +281,38 @@ def main():
     dec_state_gbps = state_bytes / (dec_ms * 1e-3) / 1e9
     dec_total_gbps = (state_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
 
+    # ------------------------------------ long-context prefill (1 x 16 x 262144)
+    # Inputs drawn on the device (torch's seeded generator, the distributions
+    # of the synthetic recipe): 3 GiB of bf16 activations would take minutes to
+    # draw on the host.  Values do not change the work; the parity tests check
+    # this shape against the oracle on the host-drawn inputs.
+    long_ms = long_gbps = None
+    wl5 = synth.WORKLOADS[LONG]
+    B5, H5, T5, d5 = wl5["B"], wl5["H"], wl5["T"], wl5["dk"]
+    if args.long_calls > 0:
+        g5 = torch.Generator(device=dev)
+        g5.manual_seed(wl5["seed"])
+        norm = torch.nn.functional.normalize
+        l_q = norm(torch.randn(B5, H5, T5, d5, device=dev, generator=g5), dim=-1).to(torch.bfloat16)
+        l_k = norm(torch.randn(B5, H5, T5, d5, device=dev, generator=g5), dim=-1).to(torch.bfloat16)
+        l_v = torch.randn(B5, H5, T5, d5, device=dev, generator=g5).to(torch.bfloat16)
+        l_a = torch.sigmoid(torch.randn(B5, H5, T5, device=dev, generator=g5) + 3.0)
+        l_b = torch.sigmoid(torch.randn(B5, H5, T5, device=dev, generator=g5))
+        l_ws = gd.gdn_workspace(l_q, l_v, 64)
+        l_out = torch.empty_like(l_v)
+        l_S = torch.empty((B5, H5, d5, d5), dtype=torch.float32, device=dev)
+        gd.gdn_prefill(l_q, l_k, l_v, l_a, l_b, form="chunked", chunk=64, out=l_out, S_out=l_S, workspace=l_ws)
+        torch.cuda.synchronize()
+        lev = [torch.cuda.Event(enable_timing=True) for _ in range(args.long_calls + 1)]
+        lev[0].record()
+        for i in range(args.long_calls):
+            gd.gdn_prefill(l_q, l_k, l_v, l_a, l_b, form="chunked", chunk=64, out=l_out, S_out=l_S, workspace=l_ws)
+            lev[i + 1].record()
+        torch.cuda.synchronize()
+        long_ms = float(np.mean([lev[i].elapsed_time(lev[i + 1]) for i in range(args.long_calls)]))
+        long_gbps = B5 * H5 * T5 * path_bytes_per_head_token(d5) / (long_ms * 1e-3) / 1e9
+        del l_q, l_k, l_v, l_a, l_b, l_ws, l_out, l_S
+
     # ---------------------------------------------- KDA decode (per-channel decay)
     wk = synth.WORKLOADS[KDA_DECODE]
     Nk, Hk, dkk = wk["N"], wk["H"], wk["dk"]
@@ -433,6 +469,13 @@ def main():
                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pre_gbps / HBM_PEAK_GBPS,
                                     "traffic": measured_traffic(["gdn_preprocess_kernel"]),
                                     "bytes_per_launch": pre_bytes, "avg_launch_ms": pre_ms}},
+        "long_context_prefill": None if long_ms is None else {
+            "workload": "gated delta prefill B=1 H=16 T=262144 d=128 chunk=64, bf16 I/O, fp32 state (inputs drawn "
+                        "on the device)", "calls": args.long_calls, "ms_per_call": long_ms,
+            "tokens_per_s": B5 * T5 / (long_ms * 1e-3),
+            "roofline": {"kernel": "gdn_prefill (map + combine + out)", "bound": "hbm", "achieved": long_gbps,
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": long_gbps / HBM_PEAK_GBPS,
+                         "bytes_per_launch": B5 * H5 * T5 * path_bytes_per_head_token(d5), "avg_launch_ms": long_ms}},
         "kda_decode": {"workload": "KDA decode 256 seq x 32 heads, d=128, per-channel decay, fp32 state, bf16 "
                                    "token I/O", "steps": steps, "ms_per_step": kda_dec_ms,
                        "steps_per_s": 1e3 / kda_dec_ms,
