@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
     __shared__ __attribute__((aligned(16))) u16 fKt[D][LDT];
     __shared__ __attribute__((aligned(16))) u16 Vt[D][LDT];
     __shared__ __attribute__((aligned(16))) u16 As[C][LDT];
-    __shared__ float zs[D], dens[C], rsum[C];
+    __shared__ float zs[D], dens[C];
     __shared__ float gs[C], egs[C];   // GATED: chunk-local g and e^g
 
     const int nseg = OUT ? G : G - 1;
@@ -255,32 +255,38 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 }
             }
             if (!GATED) {
+                // den = rowsum(A) + phi(Q) z (z of the previous blocks) for this
+                // wave's rows: the 16 lanes of a row group split the channels
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * w + 4 * g + i;
                     const float t = group_sum<16>(rs[i]);
-                    if (r == 0) rsum[16 * w + 4 * g + i] = t;
+                    const uint4 u = *reinterpret_cast<const uint4*>(&fQ[row][8 * r]);
+                    const float4 za = *reinterpret_cast<const float4*>(&zs[8 * r]);
+                    const float4 zb = *reinterpret_cast<const float4*>(&zs[8 * r + 4]);
+                    float d0 = __uint_as_float(u.x << 16) * za.x, d1 = __uint_as_float(u.x & 0xffff0000u) * za.y;
+                    d0 = fmaf(__uint_as_float(u.y << 16), za.z, d0);
+                    d1 = fmaf(__uint_as_float(u.y & 0xffff0000u), za.w, d1);
+                    d0 = fmaf(__uint_as_float(u.z << 16), zb.x, d0);
+                    d1 = fmaf(__uint_as_float(u.z & 0xffff0000u), zb.y, d1);
+                    d0 = fmaf(__uint_as_float(u.w << 16), zb.z, d0);
+                    d1 = fmaf(__uint_as_float(u.w & 0xffff0000u), zb.w, d1);
+                    const float dot = group_sum<16>(d0 + d1);
+                    if (r == 0) dens[row] = t + dot;
                 }
             }
         }
-        if constexpr (OUT && GATED) lds_barrier();   // A complete
-        if constexpr (OUT && !GATED) {
-        lds_barrier();
-        // ---- den = rowsum(A) + phi(Q) z   (z of the previous blocks)
-        {
-            const int row = tid >> 2, qd = (tid & 3) * 32;
-            float acc = 0.f;
-#pragma unroll
-            for (int d = 0; d < 32; ++d) acc = fmaf(bf16_bits_to_f32(fQ[row][qd + d]), zs[qd + d], acc);
-            acc = group_sum<4>(acc);
-            if ((tid & 3) == 0) dens[row] = acc + rsum[row];
-        }
-        lds_barrier();
-        }
+        if constexpr (OUT) lds_barrier();   // A and den complete
         // ---- z += colsum phi(K)  (read again only after the next loop-top barrier)
         if (!GATED && tid < D) {
-            float acc = zs[tid];
-            for (int c = 0; c < C; ++c) acc += bf16_bits_to_f32(fK[c][tid]);
-            zs[tid] = acc;
+            // two independent sums: the loads do not wait on one chain
+            float a0 = zs[tid], a1 = 0.f;
+#pragma unroll 16
+            for (int c = 0; c < C; c += 2) {
+                a0 += bf16_bits_to_f32(fK[c][tid]);
+                a1 += bf16_bits_to_f32(fK[c + 1][tid]);
+            }
+            zs[tid] = a0 + a1;
         }
 
         // ---- this wave's 32 value channels: outputs, then the state update
