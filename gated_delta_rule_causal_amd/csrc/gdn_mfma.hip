@@ -575,7 +575,7 @@ __device__ __forceinline__ void scan_qp(const ChunkTiles& sm, const f32x4 (&P)[N
 template <int NT>
 __device__ __forceinline__ void scan_out(const ChunkTiles& sm, const Gates& gt, f32x4 (&O)[NT][4],
                                          const bf16x8 (&Ub)[NT][2], int col0, int lane, u16* __restrict__ o,
-                                         size_t o_row0, int len) {
+                                         size_t o_row0, int len, u16 (*Os)[LDQ]) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -597,17 +597,25 @@ __device__ __forceinline__ void scan_out(const ChunkTiles& sm, const Gates& gt, 
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, Ub[nt][s2], O[nt][m]);
         }
+    // Outputs go through LDS (Os: this wave's 16 NT columns of a free 64-row
+    // tile) so that every global store is 16 contiguous bytes.
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = perm_row(m, 4 * g + i);
-            if (row < len) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    o[(o_row0 + row) * D + col0 + 16 * nt + r] = f32_to_bf16_bits(O[nt][m][i]);
-            }
+            for (int nt = 0; nt < NT; ++nt) Os[row][col0 + 16 * nt + r] = f32_to_bf16_bits(O[nt][m][i]);
         }
+    wave_fence();   // this wave's LDS writes before its reads of other lanes' values
+    constexpr int P8 = 2 * NT;   // 16-byte pieces per row of this wave's columns
+#pragma unroll
+    for (int pass = 0; pass < C * P8 / kWave; ++pass) {
+        const int e = pass * kWave + lane, row = e / P8, c8 = 8 * (e % P8);
+        if (row < len)
+            *reinterpret_cast<uint4*>(o + (o_row0 + row) * D + col0 + c8) =
+                *reinterpret_cast<const uint4*>(&Os[row][col0 + c8]);
+    }
 }
 
 // P <- e^{g_c} P + K~^T U, K~^T read transposed in the permuted row order.
@@ -1014,7 +1022,8 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
             scan_qp<2>(sm, P, lane, O);
             scan_u<2>(sm, P, col0, true, lane, Ub);
             lds_barrier();  // B5
-            scan_out<2>(sm, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0));
+            // (W of this chunk was last read before barrier B5: its tile stages the outputs)
+            scan_out<2>(sm, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Ws);
             scan_update<2>(sm, gt, P, Ub, lane);
             // snapshot of the state after chunk n (packed batches)
             const int end = (n + 1) * C;
