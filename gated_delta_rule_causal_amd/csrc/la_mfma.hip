@@ -321,15 +321,27 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 acc[0] = mfma16x16x32(a, Vb[0][s2], acc[0]);
                 acc[1] = mfma16x16x32(a, Vb[1][s2], acc[1]);
             }
+            // staged in this wave's own rows of V^T (read into Vb above, by
+            // this wave only): a [64][32] tile of its 32 value channels
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * m + 4 * g + i;
-                if (row < len) {
-                    const float rden = GATED ? 1.f : 1.f / dens[row];
-                    const size_t oi = head + static_cast<size_t>(t0 + row) * D + 32 * w + r;
-                    o[oi] = f32_to_bf16_bits(acc[0][i] * rden);
-                    o[oi + 16] = f32_to_bf16_bits(acc[1][i] * rden);
-                }
+                const float rden = GATED ? 1.f : 1.f / dens[row];
+                u16* Os = &Vt[32 * w][0];
+                Os[row * 32 + r] = f32_to_bf16_bits(acc[0][i] * rden);
+                Os[row * 32 + 16 + r] = f32_to_bf16_bits(acc[1][i] * rden);
+            }
+        }
+        if constexpr (OUT) {
+            // 16-byte global stores: 64 rows x 4 pieces of this wave's 32 channels
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            const u16* Os = &Vt[32 * w][0];
+#pragma unroll
+            for (int pass = 0; pass < C * 4 / kWave; ++pass) {
+                const int e = pass * kWave + lane, row = e >> 2, c8 = 8 * (e & 3);
+                if (row < len)
+                    *reinterpret_cast<uint4*>(o + head + static_cast<size_t>(t0 + row) * D + 32 * w + c8) =
+                        *reinterpret_cast<const uint4*>(Os + row * 32 + c8);
             }
         }
         if (GATED) {
