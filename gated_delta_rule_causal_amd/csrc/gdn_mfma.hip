@@ -98,24 +98,6 @@ struct Gates {
     float g[C], b[C], eg[C], sw[C], ek[C];  // g, beta, e^g, beta e^g, e^{g_c - g}
 };
 
-// Every 64 x 128 tile is row-major (row = token of the chunk).  Products
-// that contract over the token index read their operands with the
-// transposing LDS load, so no transposed copy is ever stored.  The gates come
-// in two copies selected by chunk parity: the scan of chunk n still reads
-// its copy while the next chunk's is written.
-struct ChunkTiles {
-    u16 Qs[C][LDQ];       // q (output kernel only)
-    u16 Ks[C][LDQ];       // k
-    u16 Kx[C][LDQ];       // K~ = diag(e^{g_c - g}) K (state update)
-    u16 Vs[C][LDQ];       // v
-    u16 Ws[C][LDQ];       // W
-    u16 Ut[D][LDA];       // Ut^T: [value channel][c]
-    u16 Lb[C][LDA];       // -L (bf16)
-    u16 Tm[C][LDA];       // (I + L)^{-1}, lower triangular
-    u16 As[C][LDA];       // decay-masked Q K^T (output kernel only)
-    Gates gt[2];
-};
-
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4v* lds_short4_ptr;
 
@@ -159,8 +141,12 @@ struct RawChunk {
     static __device__ __forceinline__ int col(int tid) { return (tid & 15) * 8; }
 };
 
-// WITH_Q / WITH_KV select the tensors loaded (the gates come with k and v).
-template <bool WITH_Q, bool WITH_KV, int NTHR, bool WR>
+// WITH_Q / WITH_K / WITH_V select the tensors loaded (the gates come with k).
+// Every load is issued, rows past the end of the sequence (len >= 1 tokens
+// from t0) reading its last row: they are zeroed when staged.  With no
+// branches around the loads, the wait before a staging step covers only the
+// loads it consumes, and the others stay in flight.
+template <bool WITH_Q, bool WITH_K, bool WITH_V, int NTHR, bool WR>
 __device__ __forceinline__ void fetch_chunk(RawChunk<NTHR, WR>& rc, const u16* __restrict__ q, const u16* __restrict__ k,
                                             const u16* __restrict__ v, const float* __restrict__ alpha,
                                             const float* __restrict__ beta, size_t head_tok, int t0, int len,
@@ -168,31 +154,28 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<NTHR, WR>& rc, const u16* _
     using RC = RawChunk<NTHR, WR>;
 #pragma unroll
     for (int it = 0; it < RC::NI; ++it) {
-        const int row = RC::row(tid, it), c8 = RC::col(tid);
-        if (WITH_Q) rc.q[it] = make_uint4(0, 0, 0, 0);
-        if (WITH_KV) rc.k[it] = rc.v[it] = make_uint4(0, 0, 0, 0);
-        if (row < len) {
-            const size_t gi = (head_tok + t0 + row) * D + c8;
-            if (WITH_Q) rc.q[it] = *reinterpret_cast<const uint4*>(q + gi);
-            if (WITH_KV) {
-                rc.k[it] = *reinterpret_cast<const uint4*>(k + gi);
-                rc.v[it] = *reinterpret_cast<const uint4*>(v + gi);
-            }
-        }
+        const int row = min(RC::row(tid, it), len - 1), c8 = RC::col(tid);
+        const size_t gi = (head_tok + t0 + row) * D + c8;
+        if (WITH_Q) rc.q[it] = *reinterpret_cast<const uint4*>(q + gi);
+        if (WITH_K) rc.k[it] = *reinterpret_cast<const uint4*>(k + gi);
+        if (WITH_V) rc.v[it] = *reinterpret_cast<const uint4*>(v + gi);
     }
-    if (WITH_KV) {
-        // padded tokens: alpha = 1 (log 0), beta = 0, zero rows: they change nothing
-        const int t = tid & 63;
-        rc.a = t < len ? alpha[head_tok + t0 + t] : 1.f;
-        rc.b = t < len ? beta[head_tok + t0 + t] : 0.f;
+    if (WITH_K) {
+        const int t = min(tid & 63, len - 1);
+        rc.a = alpha[head_tok + t0 + t];
+        rc.b = beta[head_tok + t0 + t];
     }
 }
 
-template <int NTHR, bool WR>
-__device__ __forceinline__ void stage_q(ChunkTiles& sm, const RawChunk<NTHR, WR>& rc, int tid) {
-    using RC = RawChunk<NTHR, WR>;
+// One tensor's raw rows (rc.q, rc.k or rc.v) into a row-major LDS tile, rows
+// len.. (past the end of the sequence) as zeros.
+template <class RC, int NI>
+__device__ __forceinline__ void stage_rows(u16 (*X)[LDQ], const uint4 (&raw)[NI], int tid, int len) {
 #pragma unroll
-    for (int it = 0; it < RC::NI; ++it) *reinterpret_cast<uint4*>(&sm.Qs[RC::row(tid, it)][RC::col(tid)]) = rc.q[it];
+    for (int it = 0; it < NI; ++it) {
+        const int row = RC::row(tid, it);
+        *reinterpret_cast<uint4*>(&X[row][RC::col(tid)]) = row < len ? raw[it] : make_uint4(0, 0, 0, 0);
+    }
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
@@ -223,10 +206,14 @@ __device__ __forceinline__ float dpp_add(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xf, true));
 }
 
-__device__ __forceinline__ GateRegs chunk_gates(float a, float b) {
+// Tokens past the end of the sequence (lane >= len) take alpha = 1 (log 0)
+// and beta = 0: with their zero rows they change nothing.
+__device__ __forceinline__ GateRegs chunk_gates(float a, float b, int len) {
+    const bool in = static_cast<int>(threadIdx.x & 63) < len;
+    b = in ? b : 0.f;
     // inclusive scan without LDS: shifts by 1, 2, 4, 8 inside each 16-lane
     // row, then lane 15 added into rows 1 and 3 and lane 31 into rows 2 and 3
-    float x = __logf(a);
+    float x = in ? __logf(a) : 0.f;
     x = dpp_add<0x111, 0xf>(x);   // row_shr:1
     x = dpp_add<0x112, 0xf>(x);   // row_shr:2
     x = dpp_add<0x114, 0xf>(x);   // row_shr:4
@@ -237,31 +224,20 @@ __device__ __forceinline__ GateRegs chunk_gates(float a, float b) {
     return GateRegs{x, b, __expf(x), __expf(gl - x)};
 }
 
-// k, v and the gate vectors of copy `buf` (the first wave writes the gates).
-template <int NTHR, bool WR>
-__device__ __forceinline__ void stage_kv(ChunkTiles& sm, const RawChunk<NTHR, WR>& rc, const GateRegs& gr, int tid,
-                                         int buf) {
-    using RC = RawChunk<NTHR, WR>;
-#pragma unroll
-    for (int it = 0; it < RC::NI; ++it) {
-        *reinterpret_cast<uint4*>(&sm.Ks[RC::row(tid, it)][RC::col(tid)]) = rc.k[it];
-        *reinterpret_cast<uint4*>(&sm.Vs[RC::row(tid, it)][RC::col(tid)]) = rc.v[it];
-    }
-    if (tid < C) {
-        Gates& gt = sm.gt[buf];
-        gt.g[tid] = gr.g;
-        gt.b[tid] = gr.b;
-        gt.eg[tid] = gr.eg;
-        gt.sw[tid] = gr.b * gr.eg;
-        gt.ek[tid] = gr.ek;
-    }
+// Gate vectors of token t (one lane each).
+__device__ __forceinline__ void write_gates(Gates& gt, const GateRegs& gr, int t) {
+    gt.g[t] = gr.g;
+    gt.b[t] = gr.b;
+    gt.eg[t] = gr.eg;
+    gt.sw[t] = gr.b * gr.eg;
+    gt.ek[t] = gr.ek;
 }
 
 // B operand (K = 16) of a diagonal block of Tm: lane (r, g) holds T[4g+i][r].
-__device__ __forceinline__ short4v tdiag_b(const ChunkTiles& sm, int blk, int r, int g) {
+__device__ __forceinline__ short4v tdiag_b(const u16 (*Tm)[LDA], int blk, int r, int g) {
     short4v x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = static_cast<short>(sm.Tm[16 * blk + 4 * g + i][16 * blk + r]);
+    for (int i = 0; i < 4; ++i) x[i] = static_cast<short>(Tm[16 * blk + 4 * g + i][16 * blk + r]);
     return x;
 }
 
@@ -313,25 +289,39 @@ __device__ __forceinline__ f32x4 unit_lower_inverse(f32x4 N, f32x4 Nt, int r, in
     return mfma16x16x16(to_bf16x4(P8t), to_bf16x4(R), R);   // R (I + N^8)
 }
 
-// 16x16 tile (rt, ct) of X Y^T for two row-major 64 x 128 LDS operands.
-__device__ __forceinline__ f32x4 rows_dot(const u16 (*X)[LDQ], const u16 (*Y)[LDQ], int rt, int ct, int r, int g) {
+// Everything one 16x16 tile (rt, ct) of X Y^T (two row-major 64 x 128 LDS
+// operands) and its epilogue read from LDS: four K = 32 slices of row
+// 16 rt + r of X and of row 16 ct + r of Y, g and beta of rows 16 rt + 4 g ..
+// +3 and of column 16 ct + r.  Loading it all before the products keeps the
+// reads in flight together instead of one round trip per product.
+struct TileOps {
+    bf16x8 x[4], y[4];
+    float4 gr, br;
+    float gc, bc;
+};
+
+__device__ __forceinline__ void load_tile(TileOps& o, const u16 (*X)[LDQ], const u16 (*Y)[LDQ], const Gates& gt,
+                                          int rt, int ct, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        o.x[s] = lds_bf16x8(&X[16 * rt + r][32 * s + 8 * g]);
+        o.y[s] = lds_bf16x8(&Y[16 * ct + r][32 * s + 8 * g]);
+    }
+    o.gr = *reinterpret_cast<const float4*>(&gt.g[16 * rt + 4 * g]);
+    o.br = *reinterpret_cast<const float4*>(&gt.b[16 * rt + 4 * g]);
+    o.gc = gt.g[16 * ct + r];
+    o.bc = gt.b[16 * ct + r];
+}
+
+__device__ __forceinline__ f32x4 dot_tile(const TileOps& o) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        acc = mfma16x16x32(lds_bf16x8(&X[16 * rt + r][32 * s + 8 * g]), lds_bf16x8(&Y[16 * ct + r][32 * s + 8 * g]), acc);
+    for (int s = 0; s < 4; ++s) acc = mfma16x16x32(o.x[s], o.y[s], acc);
     return acc;
 }
 
-// Two such tiles formed together (interleaved products for latency hiding).
-__device__ __forceinline__ void rows_dot2(const u16 (*X)[LDQ], const u16 (*Y)[LDQ], int rta, int cta, int rtb, int ctb,
-                                          int r, int g, f32x4& acc_a, f32x4& acc_b) {
-    acc_a = acc_b = zero4();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        acc_a = mfma16x16x32(lds_bf16x8(&X[16 * rta + r][32 * s + 8 * g]), lds_bf16x8(&Y[16 * cta + r][32 * s + 8 * g]), acc_a);
-        acc_b = mfma16x16x32(lds_bf16x8(&X[16 * rtb + r][32 * s + 8 * g]), lds_bf16x8(&Y[16 * ctb + r][32 * s + 8 * g]), acc_b);
-    }
-}
+__device__ __forceinline__ float f4get(const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // 16x16 block coordinates.  Blocks below the diagonal, 0..5:
 // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); blocks on or below it, 0..9, in row order.
@@ -346,63 +336,67 @@ __device__ __forceinline__ int lower_col(int t) { const int rt = lower_row(t); r
 // Diagonal block b: K K^T is symmetric there, so one accumulator tile yields
 // both L_bb and its transpose; the inverse is formed in registers and stored
 // in bf16 into Tm.
-__device__ __forceinline__ void step1_diag(ChunkTiles& sm, const Gates& gt, int b, int lane) {
+__device__ __forceinline__ void step1_diag(const u16 (*Ks)[LDQ], u16 (*Tm)[LDA], const Gates& gt, int b, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    const f32x4 acc = rows_dot(sm.Ks, sm.Ks, b, b, r, g);
-    const int kap = 16 * b + r;
-    const float gk = gt.g[kap], bk = gt.b[kap];
+    TileOps o;
+    load_tile(o, Ks, Ks, gt, b, b, lane);
+    const f32x4 acc = dot_tile(o);
     f32x4 N, Nt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int rho = 16 * b + 4 * g + i;
-        const float gr = gt.g[rho], br = gt.b[rho];
-        N[i] = r < 4 * g + i ? -br * __expf(fminf(gr - gk, 0.f)) * acc[i] : 0.f;
-        Nt[i] = 4 * g + i < r ? -bk * __expf(fminf(gk - gr, 0.f)) * acc[i] : 0.f;
+        const float gr = f4get(o.gr, i), br = f4get(o.br, i);
+        N[i] = r < 4 * g + i ? -br * __expf(fminf(gr - o.gc, 0.f)) * acc[i] : 0.f;
+        Nt[i] = 4 * g + i < r ? -o.bc * __expf(fminf(o.gc - gr, 0.f)) * acc[i] : 0.f;
     }
     const f32x4 Tb = unit_lower_inverse(N, Nt, r, g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.Tm[16 * b + 4 * g + i][16 * b + r] = f32_to_bf16_bits(Tb[i]);
+    for (int i = 0; i < 4; ++i) Tm[16 * b + 4 * g + i][16 * b + r] = f32_to_bf16_bits(Tb[i]);
 }
 
 // Below-diagonal blocks ta and tb (numbering above): -L in bf16 into Lb.  With
 // two = false, tb is formed and dropped, which keeps the code free of
 // branches around the matrix-core instructions.
-__device__ __forceinline__ void step1_below(ChunkTiles& sm, const Gates& gt, int ta, int tb, bool two, int lane) {
+__device__ __forceinline__ void step1_below(const u16 (*Ks)[LDQ], u16 (*Lb)[LDA], const Gates& gt, int ta, int tb,
+                                            bool two, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    f32x4 acc[2];
-    rows_dot2(sm.Ks, sm.Ks, below_row(ta), below_col(ta), below_row(tb), below_col(tb), r, g, acc[0], acc[1]);
+    TileOps o[2];
+    load_tile(o[0], Ks, Ks, gt, below_row(ta), below_col(ta), lane);
+    load_tile(o[1], Ks, Ks, gt, below_row(tb), below_col(tb), lane);
+    const f32x4 acc[2] = {dot_tile(o[0]), dot_tile(o[1])};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         if (j == 1 && !two) break;
         const int t = j ? tb : ta;
         const int rt = below_row(t), ct = below_col(t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
-            sm.Lb[row][col] = f32_to_bf16_bits(-gt.b[row] * __expf(fminf(gt.g[row] - gt.g[col], 0.f)) * acc[j][i]);
-        }
+        for (int i = 0; i < 4; ++i)
+            Lb[16 * rt + 4 * g + i][16 * ct + r] =
+                f32_to_bf16_bits(-f4get(o[j].br, i) * __expf(fminf(f4get(o[j].gr, i) - o[j].gc, 0.f)) * acc[j][i]);
     }
 }
 
 // ---- step 2 (one wave): (I + L)^{-1} below the diagonal, by diagonal distance,
 //     T_ij = T_ii * sum_{j<=k<i} (-L_ik) T_kj.
-__device__ __forceinline__ void step2_inverse_below(ChunkTiles& sm, int lane) {
+// Every LDS operand is read first; the products then form a chain of depth 6.
+__device__ __forceinline__ void step2_inverse_below(u16 (*Tm)[LDA], const u16 (*Lb)[LDA], int lane) {
     const int r = lane & 15, g = lane >> 4;
-    const short4v t00 = tdiag_b(sm, 0, r, g), t11 = tdiag_b(sm, 1, r, g), t22 = tdiag_b(sm, 2, r, g);
-    auto nl = [&](int i, int j) { return lds_short4(&sm.Lb[16 * i + r][16 * j + 4 * g]); };
-    auto ta = [&](int i) { return lds_short4(&sm.Tm[16 * i + r][16 * i + 4 * g]); };
-    const short4v t10 = to_bf16x4(mfma16x16x16(ta(1), to_bf16x4(mfma16x16x16(nl(1, 0), t00, zero4())), zero4()));
-    const short4v t21 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(mfma16x16x16(nl(2, 1), t11, zero4())), zero4()));
-    const short4v t32 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(mfma16x16x16(nl(3, 2), t22, zero4())), zero4()));
-    f32x4 y = mfma16x16x16(nl(2, 1), t10, mfma16x16x16(nl(2, 0), t00, zero4()));
-    const short4v t20 = to_bf16x4(mfma16x16x16(ta(2), to_bf16x4(y), zero4()));
-    y = mfma16x16x16(nl(3, 2), t21, mfma16x16x16(nl(3, 1), t11, zero4()));
-    const short4v t31 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
-    y = mfma16x16x16(nl(3, 2), t20, mfma16x16x16(nl(3, 1), t10, mfma16x16x16(nl(3, 0), t00, zero4())));
-    const short4v t30 = to_bf16x4(mfma16x16x16(ta(3), to_bf16x4(y), zero4()));
+    const short4v t00 = tdiag_b(Tm, 0, r, g), t11 = tdiag_b(Tm, 1, r, g), t22 = tdiag_b(Tm, 2, r, g);
+    auto nl = [&](int i, int j) { return lds_short4(&Lb[16 * i + r][16 * j + 4 * g]); };
+    auto ta = [&](int i) { return lds_short4(&Tm[16 * i + r][16 * i + 4 * g]); };
+    const short4v l10 = nl(1, 0), l21 = nl(2, 1), l32 = nl(3, 2), l20 = nl(2, 0), l31 = nl(3, 1), l30 = nl(3, 0);
+    const short4v a1 = ta(1), a2 = ta(2), a3 = ta(3);
+    const short4v t10 = to_bf16x4(mfma16x16x16(a1, to_bf16x4(mfma16x16x16(l10, t00, zero4())), zero4()));
+    const short4v t21 = to_bf16x4(mfma16x16x16(a2, to_bf16x4(mfma16x16x16(l21, t11, zero4())), zero4()));
+    const short4v t32 = to_bf16x4(mfma16x16x16(a3, to_bf16x4(mfma16x16x16(l32, t22, zero4())), zero4()));
+    f32x4 y = mfma16x16x16(l21, t10, mfma16x16x16(l20, t00, zero4()));
+    const short4v t20 = to_bf16x4(mfma16x16x16(a2, to_bf16x4(y), zero4()));
+    y = mfma16x16x16(l32, t21, mfma16x16x16(l31, t11, zero4()));
+    const short4v t31 = to_bf16x4(mfma16x16x16(a3, to_bf16x4(y), zero4()));
+    y = mfma16x16x16(l32, t20, mfma16x16x16(l31, t10, mfma16x16x16(l30, t00, zero4())));
+    const short4v t30 = to_bf16x4(mfma16x16x16(a3, to_bf16x4(y), zero4()));
     auto put = [&](int i, int j, short4v t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Tm[16 * i + 4 * g + e][16 * j + r] = static_cast<u16>(t[e]);
+        for (int e = 0; e < 4; ++e) Tm[16 * i + 4 * g + e][16 * j + r] = static_cast<u16>(t[e]);
     };
     put(1, 0, t10);
     put(2, 1, t21);
@@ -412,33 +406,26 @@ __device__ __forceinline__ void step2_inverse_below(ChunkTiles& sm, int lane) {
     put(3, 0, t30);
 }
 
-// K~ = diag(e^{g_c - g}) K, rows of 16-byte pieces shared by threads t = 0..nthr-1.
-__device__ __forceinline__ void step2_ktilde(ChunkTiles& sm, const Gates& gt, int t, int nthr) {
-    for (int e = t; e < C * (D / 8); e += nthr) {
-        const int row = e >> 4, c0 = (e & 15) * 8;
-        float x[8];
-        unpack8(*reinterpret_cast<const uint4*>(&sm.Ks[row][c0]), x);
-        const float f = gt.ek[row];
-        *reinterpret_cast<bf16x8*>(&sm.Kx[row][c0]) =
-            pack8(x[0] * f, x[1] * f, x[2] * f, x[3] * f, x[4] * f, x[5] * f, x[6] * f, x[7] * f);
-    }
-}
-
-// A = (Q K^T) * Gamma on and below the diagonal: blocks ta and tb of the
-// 0..9 numbering (tb formed and dropped when two = false).
-__device__ __forceinline__ void step2_qk(ChunkTiles& sm, const Gates& gt, int ta, int tb, bool two, int lane) {
+// A = (Q K^T) * Gamma on and below the diagonal: blocks t0 .. t0+NB-1 of the
+// 0..9 numbering, the operands of block j+1 read while block j is formed.
+template <int NB>
+__device__ __forceinline__ void step2_qk(const u16 (*Qs)[LDQ], const u16 (*Ks)[LDQ], u16 (*As)[LDA], const Gates& gt,
+                                         int t0, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    f32x4 acc[2];
-    rows_dot2(sm.Qs, sm.Ks, lower_row(ta), lower_col(ta), lower_row(tb), lower_col(tb), r, g, acc[0], acc[1]);
+    TileOps o[2];
+    load_tile(o[0], Qs, Ks, gt, lower_row(t0), lower_col(t0), lane);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        if (j == 1 && !two) break;
-        const int t = j ? tb : ta;
+    for (int j = 0; j < NB; ++j) {
+        const int t = t0 + j;
+        if (j + 1 < NB) load_tile(o[(j + 1) & 1], Qs, Ks, gt, lower_row(t + 1), lower_col(t + 1), lane);
+        const TileOps& c = o[j & 1];
+        const f32x4 acc = dot_tile(c);
         const int rt = lower_row(t), ct = lower_col(t);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rt + 4 * g + i, col = 16 * ct + r;
-            sm.As[row][col] = f32_to_bf16_bits(col <= row ? __expf(fminf(gt.g[row] - gt.g[col], 0.f)) * acc[j][i] : 0.f);
+            const float e = __expf(fminf(f4get(c.gr, i) - c.gc, 0.f)) * acc[i];
+            As[row][col] = f32_to_bf16_bits(col <= row ? e : 0.f);
         }
     }
 }
@@ -450,113 +437,20 @@ __device__ __forceinline__ void zero_above(u16 (*X)[LDA], int z, int lane) {
     for (int i = 0; i < 4; ++i) X[16 * below_col(z) + 4 * g + i][16 * below_row(z) + r] = 0;
 }
 
-// ---- step 4: W = (I + L)^{-1} diag(beta e^g) K and Ut = (I + L)^{-1} diag(beta) V
-// as plain products; the row scalings fold into the (I + L)^{-1} operand and
-// K, V are read transposed.
-// waves 0-3: W^T = K^T (Tm diag(beta e^g))^T for d rows 32w..32w+31, so each
-//            lane ends up holding 4 consecutive d of one W row (8-byte stores);
-// waves 4-7: Ut = (Tm diag(beta)) V for value channels 32(w-4)..+31.
-__device__ __forceinline__ void step4_w_ut(ChunkTiles& sm, const Gates& gt, int w, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    const bool isW = w < 4;
-    const int w4 = w & 3;
-    f32x4 acc[2][4];
-#pragma unroll
-    for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[a2][ct] = zero4();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        bf16x8 xf[2];
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2) {
-            const int n0 = 32 * w4 + 16 * a2;  // d (W) or value channel (Ut)
-            xf[a2] = tr_operand(isW ? sm.Ks : sm.Vs, 32 * s, [&](int aa) { return n0 + 4 * aa; }, lane);
-        }
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            if (s == 1 && ct < 2) continue;  // (I + L)^{-1} is lower triangular
-            float t[8];
-            unpack8(*reinterpret_cast<const uint4*>(&sm.Tm[16 * ct + r][32 * s + 8 * g]), t);
-            const float* sc = isW ? gt.sw : gt.b;
-            const bf16x8 tf = pack8(t[0] * sc[32 * s + 8 * g], t[1] * sc[32 * s + 8 * g + 1],
-                                    t[2] * sc[32 * s + 8 * g + 2], t[3] * sc[32 * s + 8 * g + 3],
-                                    t[4] * sc[32 * s + 8 * g + 4], t[5] * sc[32 * s + 8 * g + 5],
-                                    t[6] * sc[32 * s + 8 * g + 6], t[7] * sc[32 * s + 8 * g + 7]);
-#pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2) {
-                // W^T tile (d x c):  A = K^T, B = scaled Tm rows
-                // Ut tile (c x v):   A = scaled Tm rows, B = V
-                acc[a2][ct] = isW ? mfma16x16x32(xf[a2], tf, acc[a2][ct]) : mfma16x16x32(tf, xf[a2], acc[a2][ct]);
-            }
-        }
-    }
-#pragma unroll
-    for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const short4v h = to_bf16x4(acc[a2][ct]);
-            if (isW)  // lane holds W^T[d = 32w+16a2+4g+i][c = 16ct+r]
-                *reinterpret_cast<short4v*>(&sm.Ws[16 * ct + r][32 * w4 + 16 * a2 + 4 * g]) = h;
-            else      // lane holds Ut[c = 16ct+4g+i][v = 32(w-4)+16a2+r]
-                *reinterpret_cast<short4v*>(&sm.Ut[32 * w4 + 16 * a2 + r][16 * ct + 4 * g]) = h;
-        }
-}
-
 // ---- scan of one chunk for the NT 16-wide state tiles a wave owns (columns
 // col0 + 16 nt + r of P).
 //
-// U = Ut - W P (use_ut) or -W P (the map part), in the B-operand layout.  W
-// rows are taken in the permuted order so X = W P lands in U's layout; the
-// bf16 copy of the state is packed on the fly to save registers.
-template <int NT>
-__device__ __forceinline__ void scan_u(const ChunkTiles& sm, const f32x4 (&P)[NT][8], int col0, bool use_ut, int lane,
-                                       bf16x8 (&Ub)[NT][2]) {
-    const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        f32x4 Xa[NT], Xb[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) Xa[nt] = Xb[nt] = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bf16x8 a0 = lds_bf16x8(&sm.Ws[perm_row(2 * s2, r)][32 * s + 8 * g]);
-            const bf16x8 a1 = lds_bf16x8(&sm.Ws[perm_row(2 * s2 + 1, r)][32 * s + 8 * g]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bf16x8 pb = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
-                Xa[nt] = mfma16x16x32(a0, pb, Xa[nt]);
-                Xb[nt] = mfma16x16x32(a1, pb, Xb[nt]);
-            }
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            float ut[8];
-            if (use_ut) {
-                unpack8(*reinterpret_cast<const uint4*>(&sm.Ut[col0 + 16 * nt + r][32 * s2 + 8 * g]), ut);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ut[j] = 0.f;
-            }
-            f32x4 lo, hi;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lo[i] = ut[i] - Xa[nt][i];
-                hi[i] = ut[4 + i] - Xb[nt][i];
-            }
-            Ub[nt][s2] = pack_acc_pair(lo, hi);
-        }
-    }
-}
-
-// O = Q P (the inter-chunk part of the outputs, before the e^g row scaling).
-template <int NT>
-__device__ __forceinline__ void scan_qp(const ChunkTiles& sm, const f32x4 (&P)[NT][8], int lane, f32x4 (&O)[NT][4]) {
+// O = Q P (the inter-chunk part of the outputs, before the e^g row scaling;
+// WITH_Q only) and X = K P, rows in the permuted order, in one pass over the
+// packed state.
+template <int NT, bool WITH_Q>
+__device__ __forceinline__ void scan_qk(const u16 (*Qs)[LDQ], const u16 (*Ks)[LDQ], const f32x4 (&P)[NT][8], int lane,
+                                        f32x4 (&O)[NT][4], f32x4 (&X)[NT][4]) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) O[nt][m] = zero4();
+        for (int m = 0; m < 4; ++m) O[nt][m] = X[nt][m] = zero4();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         bf16x8 pb[NT];
@@ -564,16 +458,89 @@ __device__ __forceinline__ void scan_qp(const ChunkTiles& sm, const f32x4 (&P)[N
         for (int nt = 0; nt < NT; ++nt) pb[nt] = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const bf16x8 a = lds_bf16x8(&sm.Qs[perm_row(m, r)][32 * s + 8 * g]);
+            const bf16x8 ak = lds_bf16x8(&Ks[perm_row(m, r)][32 * s + 8 * g]);
+            if constexpr (WITH_Q) {
+                const bf16x8 aq = lds_bf16x8(&Qs[perm_row(m, r)][32 * s + 8 * g]);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, pb[nt], O[nt][m]);
+                for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(aq, pb[nt], O[nt][m]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) X[nt][m] = mfma16x16x32(ak, pb[nt], X[nt][m]);
+        }
+    }
+}
+
+// Right-hand side of the chunk's triangular system, diag(beta) (V - diag(e^g) K P)
+// (without the V term when WITH_V is false: the M part of a segment map),
+// packed as the B operands of two K = 32 slices: lane (r, g) of slice s2 holds
+// tokens 32 s2 + 8 g .. +7 of value column col0 + 16 nt + r.  V is read
+// transposed from its row-major tile.
+template <int NT, bool WITH_V>
+__device__ __forceinline__ void scan_rhs(const u16 (*Vs)[LDQ], const Gates& gt, const f32x4 (&X)[NT][4], int col0,
+                                         int lane, bf16x8 (&Xb)[NT][2]) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int t0 = 32 * s2 + 8 * g;
+        const float4 b0 = *reinterpret_cast<const float4*>(&gt.b[t0]), b1 = *reinterpret_cast<const float4*>(&gt.b[t0 + 4]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&gt.sw[t0]), w1 = *reinterpret_cast<const float4*>(&gt.sw[t0 + 4]);
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = -ww[i] * X[nt][2 * s2][i];
+                x[4 + i] = -ww[4 + i] * X[nt][2 * s2 + 1][i];
+            }
+            if constexpr (WITH_V) {
+                const bf16x8 vv = tr_operand(Vs, 32 * s2, [&](int aa) { return col0 + 16 * nt + 4 * aa; }, lane);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] += bb[j] * static_cast<float>(vv[j]);
+            }
+            Xb[nt][s2] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+        }
+    }
+}
+
+// U = (I + L)^{-1} times that right-hand side (rows permuted), returned packed
+// with the rows scaled by e^{g_c - g} (for the state update, which then reads
+// K itself) and, WITH_UB, as is (for A U).
+template <int NT, bool WITH_UB>
+__device__ __forceinline__ void scan_solve(const u16 (*Tm)[LDA], const Gates& gt, const bf16x8 (&Xb)[NT][2], int lane,
+                                           bf16x8 (&Ub)[NT][2], bf16x8 (&Ue)[NT][2]) {
+    const int r = lane & 15, g = lane >> 4;
+    f32x4 U[NT][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) U[nt][m] = zero4();
+        // row tile m (chunk rows 32(m/2)..+31) needs column slices s2 <= m/2
+#pragma unroll
+        for (int s2 = 0; s2 <= (m >> 1); ++s2) {
+            const bf16x8 a = lds_bf16x8(&Tm[perm_row(m, r)][32 * s2 + 8 * g]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) U[nt][m] = mfma16x16x32(a, Xb[nt][s2], U[nt][m]);
+        }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int t0 = 32 * s2 + 8 * g;
+        const float4 e0 = *reinterpret_cast<const float4*>(&gt.ek[t0]), e1 = *reinterpret_cast<const float4*>(&gt.ek[t0 + 4]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const f32x4 lo = U[nt][2 * s2], hi = U[nt][2 * s2 + 1];
+            if constexpr (WITH_UB) Ub[nt][s2] = pack_acc_pair(lo, hi);
+            Ue[nt][s2] = pack8(lo[0] * e0.x, lo[1] * e0.y, lo[2] * e0.z, lo[3] * e0.w, hi[0] * e1.x, hi[1] * e1.y,
+                               hi[2] * e1.z, hi[3] * e1.w);
         }
     }
 }
 
 // O <- diag(e^g) O + A U, stored for the rows that exist.
 template <int NT>
-__device__ __forceinline__ void scan_out(const ChunkTiles& sm, const Gates& gt, f32x4 (&O)[NT][4],
+__device__ __forceinline__ void scan_out(const u16 (*As)[LDA], const Gates& gt, f32x4 (&O)[NT][4],
                                          const bf16x8 (&Ub)[NT][2], int col0, int lane, u16* __restrict__ o,
                                          size_t o_row0, int len, u16 (*Os)[LDQ]) {
     const int r = lane & 15, g = lane >> 4;
@@ -593,7 +560,7 @@ __device__ __forceinline__ void scan_out(const ChunkTiles& sm, const Gates& gt, 
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int s2 = 0; s2 <= (m >> 1); ++s2) {
-            const bf16x8 a = lds_bf16x8(&sm.As[perm_row(m, r)][32 * s2 + 8 * g]);
+            const bf16x8 a = lds_bf16x8(&As[perm_row(m, r)][32 * s2 + 8 * g]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, Ub[nt][s2], O[nt][m]);
         }
@@ -618,9 +585,10 @@ __device__ __forceinline__ void scan_out(const ChunkTiles& sm, const Gates& gt, 
     }
 }
 
-// P <- e^{g_c} P + K~^T U, K~^T read transposed in the permuted row order.
+// P <- e^{g_c} P + Kx^T U, Kx^T read transposed in the permuted row order
+// (Kx = K~ with U as is, or Kx = K with U's rows scaled by e^{g_c - g}).
 template <int NT>
-__device__ __forceinline__ void scan_update(const ChunkTiles& sm, const Gates& gt, f32x4 (&P)[NT][8],
+__device__ __forceinline__ void scan_update(const u16 (*Kx)[LDQ], const Gates& gt, f32x4 (&P)[NT][8],
                                             const bf16x8 (&Ub)[NT][2], int lane) {
     const float egc = gt.eg[C - 1];
 #pragma unroll
@@ -629,7 +597,7 @@ __device__ __forceinline__ void scan_update(const ChunkTiles& sm, const Gates& g
         for (int nt = 0; nt < NT; ++nt) P[nt][t] *= egc;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 a = tr_operand(sm.Kx, 32 * s2, [&](int aa) { return 32 * (t >> 1) + 8 * aa + 4 * (t & 1); }, lane);
+            const bf16x8 a = tr_operand(Kx, 32 * s2, [&](int aa) { return 32 * (t >> 1) + 8 * aa + 4 * (t & 1); }, lane);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) P[nt][t] = mfma16x16x32(a, Ub[nt][s2], P[nt][t]);
         }
@@ -773,78 +741,109 @@ __device__ __forceinline__ bool find_item(const Geo& g, int blk, bool maps, Item
 }
 
 // ============================================================ segment maps
-__global__ __launch_bounds__(kThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
-                                                           const u16* __restrict__ v, const float* __restrict__ alpha,
-                                                           const float* __restrict__ beta, float* __restrict__ ws) {
-    __shared__ __attribute__((aligned(16))) ChunkTiles sm;
+// LDS of the map kernel: k, (I + L)^{-1} and gates in two copies by chunk
+// parity, v in one (rewritten after the carriers' last read of it).
+struct MapTiles {
+    u16 Ks[2][C][LDQ];
+    u16 Vs[C][LDQ];
+    u16 Tm[2][C][LDA];
+    u16 Lb[C][LDA];
+    Gates gt[2];
+};
+
+constexpr int kMapThreads = 768;   // 8 state carriers + 4 stagers
+
+// Waves 0-7 carry the augmented state [N | M] (d_k x 256, starting from
+// [0 | I]): waves 0-3 the N columns (value channels 32w..32w+31, with V),
+// waves 4-7 the M columns (no V term).  Per chunk, like the output kernel
+// without Q, A and the outputs:
+//     carriers:  K P | B1 | right-hand side (reads v), solve | B2 | update | B0
+//     stagers:   k + gates, diagonal inverse blocks | B1 | L below the diagonal | B2 |
+//                inverse below the diagonal, v | B0
+__global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
+                                                              const u16* __restrict__ v,
+                                                              const float* __restrict__ alpha,
+                                                              const float* __restrict__ beta, float* __restrict__ ws) {
+    __shared__ __attribute__((aligned(16))) MapTiles sm;
     Item it;
     if (!find_item(geo, blockIdx.x, true, it)) return;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branches below are scalar
     const int n0 = it.n0, n1 = it.n1, T = it.len;
     const size_t head_tok = it.head_tok;
-    // waves 0-3: N columns (value channels 32w..32w+31), start 0;
-    // waves 4-7: M columns j = 32(w-4)..+31, start = identity
-    const bool npart = w < 4;
-    const int col0 = 32 * (w & 3);
-    f32x4 P[2][8];
+    if (w < 8) {
+        const int r = lane & 15, g = lane >> 4;
+        const bool npart = w < 4;
+        const int col0 = 32 * (w & 3);
+        f32x4 P[2][8];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                P[nt][t][i] = (!npart && perm_row(t, 4 * g + i) == col0 + 16 * nt + r) ? 1.f : 0.f;
-
-    // The blocks (0,1) and (2,3) above the diagonal of Tm and A are read by
-    // 32-wide operand slices and must be zero; nothing else writes them.
-    if (w >= 4) zero_above(w < 6 ? sm.Tm : sm.As, (w & 1) ? 5 : 0, lane);
-    // Per chunk n: barrier A, step 2, B3, step 4, B4, then k, v and the gates of
-    // chunk n+1 are staged (their LDS tiles are no longer read), B5, and the
-    // scan of chunk n runs together with step 1 of chunk n+1 (the scan reads
-    // neither L nor the inverse blocks).
-    RawChunk<kThreads> rc;
-    auto fetch = [&](int n) {
-        fetch_chunk<false, true>(rc, nullptr, k, v, alpha, beta, head_tok, n * C, min(C, T - n * C), tid);
-    };
-    auto step1 = [&](int n) {
-        if (w < 4) {
-            step1_diag(sm, sm.gt[n & 1], w, lane);
-        } else {
-            const int u = w - 4;
-            step1_below(sm, sm.gt[n & 1], u, u < 2 ? u + 4 : u, u < 2, lane);
+                for (int i = 0; i < 4; ++i)
+                    P[nt][t][i] = (!npart && perm_row(t, 4 * g + i) == col0 + 16 * nt + r) ? 1.f : 0.f;
+        lds_barrier();  // B1, B2, B0 of chunk n0's staging
+        lds_barrier();
+        lds_barrier();
+        for (int n = n0; n < n1; ++n) {
+            const int cb = n & 1;
+            const Gates& gt = sm.gt[cb];
+            f32x4 O[2][4], X[2][4];
+            bf16x8 Xb[2][2], Ub[2][2], Ue[2][2];
+            scan_qk<2, false>(nullptr, sm.Ks[cb], P, lane, O, X);
+            lds_barrier();  // B1
+            if (npart)
+                scan_rhs<2, true>(sm.Vs, gt, X, col0, lane, Xb);
+            else
+                scan_rhs<2, false>(sm.Vs, gt, X, col0, lane, Xb);
+            scan_solve<2, false>(sm.Tm[cb], gt, Xb, lane, Ub, Ue);
+            lds_barrier();  // B2
+            scan_update<2>(sm.Ks[cb], gt, P, Ue, lane);
+            lds_barrier();  // B0
         }
-    };
-    fetch(n0);
-    stage_kv(sm, rc, chunk_gates(rc.a, rc.b), tid, n0 & 1);
-    if (n0 + 1 < n1) fetch(n0 + 1);
-    lds_barrier();
-    step1(n0);
-    for (int n = n0; n < n1; ++n) {
-        const Gates& gt = sm.gt[n & 1];
-        lds_barrier();  // A
-        if (w == 0)
-            step2_inverse_below(sm, lane);
+        if (npart)
+            store_state<2>(P, ws + ws_N(it.slot0 + it.seg), col0, lane);
         else
-            step2_ktilde(sm, gt, tid - 64, kThreads - 64);
-        lds_barrier();  // B3
-        step4_w_ut(sm, gt, w, lane);
-        lds_barrier();  // B4
-        if (n + 1 < n1) {
-            stage_kv(sm, rc, chunk_gates(rc.a, rc.b), tid, (n + 1) & 1);
-            if (n + 2 < n1) fetch(n + 2);
+            store_state_rowmajor<2>(P, ws + ws_M(it.slot0 + it.seg), col0, lane);
+    } else {
+        const int ptid = tid - 512;
+        const int u = w - 8;
+        // The blocks (0,1) and (2,3) above the diagonal of Tm are read by
+        // 32-wide operand slices and must be zero; nothing else writes them.
+        zero_above(sm.Tm[u & 1], (u & 2) ? 5 : 0, lane);
+        using RC = RawChunk<256, true>;
+        RC rc;
+        using yes = std::true_type;
+        using no = std::false_type;
+        auto fetch = [&](int m, auto with_k, auto with_v) {
+            fetch_chunk<false, decltype(with_k)::value, decltype(with_v)::value>(
+                rc, nullptr, k, v, alpha, beta, head_tok, m * C, min(C, T - m * C), ptid);
+        };
+        // the same issue order as inside the loop (k and gates, then v)
+        fetch(n0, yes{}, no{});
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(n0, no{}, yes{});
+        __builtin_amdgcn_sched_barrier(0);
+        for (int m = n0; m < n1; ++m) {
+            const int cb = m & 1, len = min(C, T - m * C), mn = min(m + 1, n1 - 1);
+            write_gates(sm.gt[cb], chunk_gates(rc.a, rc.b, len), lane);
+            stage_rows<RC>(sm.Ks[cb], rc.k, ptid, len);
+            fetch(mn, yes{}, no{});
+            wave_fence();
+            step1_diag(sm.Ks[cb], sm.Tm[cb], sm.gt[cb], u, lane);
+            lds_barrier();  // B1
+            step1_below(sm.Ks[cb], sm.Lb, sm.gt[cb], u, u < 2 ? u + 4 : u, u < 2, lane);
+            lds_barrier();  // B2
+            if (u == 0) step2_inverse_below(sm.Tm[cb], sm.Lb, lane);
+            stage_rows<RC>(sm.Vs, rc.v, ptid, len);
+            fetch(mn, no{}, yes{});
+            lds_barrier();  // B0
         }
-        lds_barrier();  // B5
-        bf16x8 Ub[2][2];
-        scan_u<2>(sm, P, col0, npart, lane, Ub);
-        scan_update<2>(sm, gt, P, Ub, lane);
-        if (n + 1 < n1) step1(n + 1);
+        lds_barrier();  // B1, B2, B0 of the carriers' last chunk
+        lds_barrier();
+        lds_barrier();
     }
-    if (npart)
-        store_state<2>(P, ws + ws_N(it.slot0 + it.seg), col0, lane);
-    else
-        store_state_rowmajor<2>(P, ws + ws_M(it.slot0 + it.seg), col0, lane);
 }
 
 // ============================================================ combine
@@ -965,17 +964,44 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(Geo geo, c
 }
 
 // ============================================================ outputs
+// LDS of the output kernel.  Chunk m's k, (I + L)^{-1}, A and gates sit in
+// copy m & 1: the stagers fill copy m+1 while the state carriers read copy m.
+// q and v have one copy each; each is rewritten only after the carriers' last
+// read of the previous chunk's.
+struct OutTiles {
+    u16 Ks[2][C][LDQ];
+    u16 Qs[C][LDQ];
+    u16 Vs[C][LDQ];
+    u16 Os[C][LDQ];      // output staging (state carriers)
+    u16 Tm[2][C][LDA];   // (I + L)^{-1}
+    u16 As[2][C][LDA];   // decay-masked Q K^T
+    u16 Lb[C][LDA];      // -L (stagers only)
+    Gates gt[2];
+};
+
+// Waves 0-3 carry the state (32 value channels each) and compute, per chunk,
+//     O = diag(e^g) Q P + A U,   U = (I + L)^{-1} diag(beta) (V - diag(e^g) K P),
+//     P <- e^{g_c} P + K^T diag(e^{g_c - g}) U
+// (the chunk form above with W and Ut folded: W P = (I + L)^{-1} diag(beta e^g) K P,
+// so no chunk-sized W or Ut tile is formed).  Waves 4-7 stage chunk m+1 and
+// form its state-independent tiles (L, (I + L)^{-1}, A) while the carriers run
+// chunk m.  Every chunk has three barriers, met by both roles:
+//     carriers:  Q P and K P | B1 | right-hand side (reads v), solve | B2 | outputs, update | B0
+//     stagers:   k + gates, diagonal inverse blocks | B1 | L below the diagonal, q | B2 |
+//                inverse below the diagonal, A, v | B0
+// The stagers run one chunk ahead: they stage chunk n0 while the carriers
+// wait, and wait through the carriers' last chunk.
 __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* __restrict__ q,
                                                            const u16* __restrict__ k, const u16* __restrict__ v,
                                                            const float* __restrict__ alpha,
                                                            const float* __restrict__ beta, const float* S0,
                                                            const float* __restrict__ ws, u16* __restrict__ o,
                                                            float* S_out) {
-    __shared__ __attribute__((aligned(16))) ChunkTiles sm;
+    __shared__ __attribute__((aligned(16))) OutTiles sm;
     Item it;
     if (!find_item(geo, blockIdx.x, false, it)) return;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branch below is scalar
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branches below are scalar
     const int n0 = it.n0, n1 = it.n1, T = it.len;
     const size_t head_tok = it.head_tok;
     const float* S0h = S0 ? S0 + it.state * kMat : nullptr;
@@ -987,44 +1013,28 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
         }
         return;
     }
-    // Waves 0-3 carry the state (32 value channels each); waves 4-7 stage the
-    // chunks and hold the raw inputs of the next one.  Per chunk n, after
-    // barrier A: step 2 (all), B3, step 4 (all), B4, the first half of the scan
-    // (Q P and U, state carriers) while the stagers write k, v and the gates of
-    // chunk n+1, B5, then the second half (outputs, state update) while the
-    // stagers write q and run step 1 of chunk n+1 (L and the diagonal inverse
-    // blocks, whose LDS tiles the scan no longer reads).  Both roles meet the
-    // same barriers; neither keeps the other's registers live.
-    // The blocks (0,1) and (2,3) above the diagonal of Tm and A are read by
-    // 32-wide operand slices and must be zero; nothing else writes them.
-    if (w >= 4) zero_above(w < 6 ? sm.Tm : sm.As, (w & 1) ? 5 : 0, lane);
     if (w < 4) {
         const int col0 = 32 * w;
         f32x4 P[2][8];
         // entering state: S0 itself when the sequence is one segment, else the
         // combined state (segment 0 included, so S_out may alias S0)
         load_state<2>(P, it.G == 1 ? S0h : ws + ws_P(it.slot0 + it.seg), col0, lane);
-        lds_barrier();  // chunk n0 staged
-        lds_barrier();  // step 1 of chunk n0 done
+        lds_barrier();  // B1, B2, B0 of chunk n0's staging
+        lds_barrier();
+        lds_barrier();
         for (int n = n0; n < n1; ++n) {
+            const int cb = n & 1;
+            const Gates& gt = sm.gt[cb];
+            f32x4 O[2][4], X[2][4];
+            bf16x8 Xb[2][2], Ub[2][2], Ue[2][2];
+            scan_qk<2, true>(sm.Qs, sm.Ks[cb], P, lane, O, X);
+            lds_barrier();  // B1
+            scan_rhs<2, true>(sm.Vs, gt, X, col0, lane, Xb);
+            scan_solve<2, true>(sm.Tm[cb], gt, Xb, lane, Ub, Ue);
+            lds_barrier();  // B2
             const int t0 = n * C;
-            const Gates& gt = sm.gt[n & 1];
-            lds_barrier();  // A
-            if (w == 0)
-                step2_inverse_below(sm, lane);
-            else
-                step2_qk(sm, gt, w - 1, w + 2, true, lane);
-            lds_barrier();  // B3
-            step4_w_ut(sm, gt, w, lane);
-            lds_barrier();  // B4
-            f32x4 O[2][4];
-            bf16x8 Ub[2][2];
-            scan_qp<2>(sm, P, lane, O);
-            scan_u<2>(sm, P, col0, true, lane, Ub);
-            lds_barrier();  // B5
-            // (W of this chunk was last read before barrier B5: its tile stages the outputs)
-            scan_out<2>(sm, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Ws);
-            scan_update<2>(sm, gt, P, Ub, lane);
+            scan_out<2>(sm.As[cb], gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Os);
+            scan_update<2>(sm.Ks[cb], gt, P, Ue, lane);
             // snapshot of the state after chunk n (packed batches)
             const int end = (n + 1) * C;
             if (geo.snap > 0 && end <= T && end % geo.snap == 0) {
@@ -1032,52 +1042,64 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
                 if (j < geo.snap_cap)
                     store_state<2>(P, geo.S_snap + (static_cast<size_t>(j) * geo.H + it.h) * kMat, col0, lane);
             }
+            lds_barrier();  // B0
         }
         if (it.seg == it.G - 1 && S_out) store_state<2>(P, S_out + it.state * kMat, col0, lane);
     } else {
         const int ptid = tid - kThreads / 2;
         const int u = w - 4;
+        // The blocks (0,1) and (2,3) above the diagonal of Tm and A are read by
+        // 32-wide operand slices and must be zero; nothing else writes them.
+        zero_above((u & 2) ? sm.As[u & 1] : sm.Tm[u & 1], 0, lane);
+        zero_above((u & 2) ? sm.As[u & 1] : sm.Tm[u & 1], 5, lane);
         // Wave u owns rows 16u..16u+15 of every staged tile, so right after
-        // writing its k rows it can form diagonal block u of step 1.  Loads of
-        // k and v for chunk n+2 are issued once those of n+1 are staged, loads
-        // of q once its q is staged.
-        RawChunk<kThreads / 2, true> rc;
-        auto fetch = [&](int n, auto with_q, auto with_kv) {
-            fetch_chunk<decltype(with_q)::value, decltype(with_kv)::value>(rc, q, k, v, alpha, beta, head_tok, n * C,
-                                                                           min(C, T - n * C), ptid);
-        };
+        // writing its k rows (and all the gates) it forms diagonal block u.
+        // Each tensor of chunk m+1 is fetched right after the same tensor of
+        // chunk m is staged (the last chunk fetches itself again).
+        using RC = RawChunk<kThreads / 2, true>;
+        RC rc;
         using yes = std::true_type;
         using no = std::false_type;
-        auto step1 = [&](int n) {
-            step1_diag(sm, sm.gt[n & 1], u, lane);
-            step1_below(sm, sm.gt[n & 1], u, u < 2 ? u + 4 : u, u < 2, lane);
+        auto fetch = [&](int m, auto with_q, auto with_k, auto with_v) {
+            fetch_chunk<decltype(with_q)::value, decltype(with_k)::value, decltype(with_v)::value>(
+                rc, q, k, v, alpha, beta, head_tok, m * C, min(C, T - m * C), ptid);
         };
-        fetch(n0, yes{}, yes{});
-        stage_kv(sm, rc, chunk_gates(rc.a, rc.b), ptid, n0 & 1);
-        stage_q(sm, rc, ptid);
-        lds_barrier();  // chunk n0 staged
-        step1(n0);
-        if (n0 + 1 < n1) fetch(n0 + 1, yes{}, yes{});
-        lds_barrier();  // step 1 of chunk n0 done
-        for (int n = n0; n < n1; ++n) {
-            const Gates& gt = sm.gt[n & 1];
-            lds_barrier();  // A
-            step2_ktilde(sm, gt, ptid, kThreads / 2);
-            step2_qk(sm, gt, w + 2, w + 2, false, lane);
-            lds_barrier();  // B3
-            step4_w_ut(sm, gt, w, lane);
-            lds_barrier();  // B4
-            if (n + 1 < n1) {
-                stage_kv(sm, rc, chunk_gates(rc.a, rc.b), ptid, (n + 1) & 1);
-                if (n + 2 < n1) fetch(n + 2, no{}, yes{});
+        // the same issue order as inside the loop (k and gates, q, v), so the
+        // wait before each staging step is as short there as on every later chunk
+        fetch(n0, no{}, yes{}, no{});
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(n0, yes{}, no{}, no{});
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(n0, no{}, no{}, yes{});
+        __builtin_amdgcn_sched_barrier(0);
+        for (int m = n0; m < n1; ++m) {
+            const int cb = m & 1, len = min(C, T - m * C), mn = min(m + 1, n1 - 1);
+            write_gates(sm.gt[cb], chunk_gates(rc.a, rc.b, len), lane);
+            stage_rows<RC>(sm.Ks[cb], rc.k, ptid, len);
+            fetch(mn, no{}, yes{}, no{});
+            wave_fence();
+            step1_diag(sm.Ks[cb], sm.Tm[cb], sm.gt[cb], u, lane);
+            lds_barrier();  // B1
+            step1_below(sm.Ks[cb], sm.Lb, sm.gt[cb], u, u < 2 ? u + 4 : u, u < 2, lane);
+            stage_rows<RC>(sm.Qs, rc.q, ptid, len);
+            fetch(mn, yes{}, no{}, no{});
+            lds_barrier();  // B2
+            if (u == 0) {
+                step2_inverse_below(sm.Tm[cb], sm.Lb, lane);
+            } else {
+                // blocks 0..9 of A: waves 1 and 2 four each, wave 3 two
+                if (u < 3)
+                    step2_qk<4>(sm.Qs, sm.Ks[cb], sm.As[cb], sm.gt[cb], 4 * (u - 1), lane);
+                else
+                    step2_qk<2>(sm.Qs, sm.Ks[cb], sm.As[cb], sm.gt[cb], 8, lane);
             }
-            lds_barrier();  // B5
-            if (n + 1 < n1) {
-                stage_q(sm, rc, ptid);
-                if (n + 2 < n1) fetch(n + 2, yes{}, no{});
-                step1(n + 1);
-            }
+            stage_rows<RC>(sm.Vs, rc.v, ptid, len);
+            fetch(mn, no{}, no{}, yes{});
+            lds_barrier();  // B0
         }
+        lds_barrier();  // B1, B2, B0 of the last chunk's scan
+        lds_barrier();
+        lds_barrier();
     }
 }
 
@@ -1182,7 +1204,7 @@ hipError_t launch_all(const Geo& g, int map_blocks, int combine_items, int out_b
                       const void* v, const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                       float* ws, bool prep, bool scan, hipStream_t stream) {
     if (prep && map_blocks > 0) {
-        hipLaunchKernelGGL(gdn_map_kernel, dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream, g,
+        hipLaunchKernelGGL(gdn_map_kernel, dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream, g,
                            static_cast<const u16*>(k), static_cast<const u16*>(v), alpha, beta, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
