@@ -375,35 +375,45 @@ __device__ __forceinline__ void step1_below(const u16 (*Ks)[LDQ], u16 (*Lb)[LDA]
     }
 }
 
-// ---- step 2 (one wave): (I + L)^{-1} below the diagonal, by diagonal distance,
-//     T_ij = T_ii * sum_{j<=k<i} (-L_ik) T_kj.
-// Every LDS operand is read first; the products then form a chain of depth 6.
+// ---- step 2: (I + L)^{-1} below the diagonal,
+//     T_ij = T_ii * sum_{j<=k<i} (-L_ik) T_kj,
+// as three independent chains, one per wave: part 0 forms T_10, T_20, T_30;
+// part 1 T_21, T_31; part 2 T_32.  Every LDS operand is read first.  The
+// part is a template argument: each wave runs straight-line code of its own.
+template <int PART>
 __device__ __forceinline__ void step2_inverse_below(u16 (*Tm)[LDA], const u16 (*Lb)[LDA], int lane) {
     const int r = lane & 15, g = lane >> 4;
-    const short4v t00 = tdiag_b(Tm, 0, r, g), t11 = tdiag_b(Tm, 1, r, g), t22 = tdiag_b(Tm, 2, r, g);
     auto nl = [&](int i, int j) { return lds_short4(&Lb[16 * i + r][16 * j + 4 * g]); };
     auto ta = [&](int i) { return lds_short4(&Tm[16 * i + r][16 * i + 4 * g]); };
-    const short4v l10 = nl(1, 0), l21 = nl(2, 1), l32 = nl(3, 2), l20 = nl(2, 0), l31 = nl(3, 1), l30 = nl(3, 0);
-    const short4v a1 = ta(1), a2 = ta(2), a3 = ta(3);
-    const short4v t10 = to_bf16x4(mfma16x16x16(a1, to_bf16x4(mfma16x16x16(l10, t00, zero4())), zero4()));
-    const short4v t21 = to_bf16x4(mfma16x16x16(a2, to_bf16x4(mfma16x16x16(l21, t11, zero4())), zero4()));
-    const short4v t32 = to_bf16x4(mfma16x16x16(a3, to_bf16x4(mfma16x16x16(l32, t22, zero4())), zero4()));
-    f32x4 y = mfma16x16x16(l21, t10, mfma16x16x16(l20, t00, zero4()));
-    const short4v t20 = to_bf16x4(mfma16x16x16(a2, to_bf16x4(y), zero4()));
-    y = mfma16x16x16(l32, t21, mfma16x16x16(l31, t11, zero4()));
-    const short4v t31 = to_bf16x4(mfma16x16x16(a3, to_bf16x4(y), zero4()));
-    y = mfma16x16x16(l32, t20, mfma16x16x16(l31, t10, mfma16x16x16(l30, t00, zero4())));
-    const short4v t30 = to_bf16x4(mfma16x16x16(a3, to_bf16x4(y), zero4()));
     auto put = [&](int i, int j, short4v t) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) Tm[16 * i + 4 * g + e][16 * j + r] = static_cast<u16>(t[e]);
     };
-    put(1, 0, t10);
-    put(2, 1, t21);
-    put(3, 2, t32);
-    put(2, 0, t20);
-    put(3, 1, t31);
-    put(3, 0, t30);
+    auto solve = [&](short4v a, f32x4 y) { return to_bf16x4(mfma16x16x16(a, to_bf16x4(y), zero4())); };
+    if constexpr (PART == 0) {
+        const short4v t00 = tdiag_b(Tm, 0, r, g);
+        const short4v l10 = nl(1, 0), l20 = nl(2, 0), l21 = nl(2, 1), l30 = nl(3, 0), l31 = nl(3, 1), l32 = nl(3, 2);
+        const short4v a1 = ta(1), a2 = ta(2), a3 = ta(3);
+        const short4v t10 = solve(a1, mfma16x16x16(l10, t00, zero4()));
+        const short4v t20 = solve(a2, mfma16x16x16(l21, t10, mfma16x16x16(l20, t00, zero4())));
+        const short4v t30 =
+            solve(a3, mfma16x16x16(l32, t20, mfma16x16x16(l31, t10, mfma16x16x16(l30, t00, zero4()))));
+        put(1, 0, t10);
+        put(2, 0, t20);
+        put(3, 0, t30);
+    } else if constexpr (PART == 1) {
+        const short4v t11 = tdiag_b(Tm, 1, r, g);
+        const short4v l21 = nl(2, 1), l31 = nl(3, 1), l32 = nl(3, 2);
+        const short4v a2 = ta(2), a3 = ta(3);
+        const short4v t21 = solve(a2, mfma16x16x16(l21, t11, zero4()));
+        const short4v t31 = solve(a3, mfma16x16x16(l32, t21, mfma16x16x16(l31, t11, zero4())));
+        put(2, 1, t21);
+        put(3, 1, t31);
+    } else {
+        const short4v t22 = tdiag_b(Tm, 2, r, g);
+        const short4v l32 = nl(3, 2), a3 = ta(3);
+        put(3, 2, solve(a3, mfma16x16x16(l32, t22, zero4())));
+    }
 }
 
 // A = (Q K^T) * Gamma on and below the diagonal: blocks t0 .. t0+NB-1 of the
@@ -758,8 +768,8 @@ constexpr int kMapThreads = 768;   // 8 state carriers + 4 stagers
 // waves 4-7 the M columns (no V term).  Per chunk, like the output kernel
 // without Q, A and the outputs:
 //     carriers:  K P | B1 | right-hand side (reads v), solve | B2 | update | B0
-//     stagers:   k + gates, diagonal inverse blocks | B1 | L below the diagonal | B2 |
-//                inverse below the diagonal, v | B0
+//     stagers:   k + gates, diagonal inverse blocks of chunk n+1 | B1 |
+//                L below the diagonal | B2 | inverse below the diagonal (three waves), v | B0
 __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
                                                               const u16* __restrict__ v,
                                                               const float* __restrict__ alpha,
@@ -830,12 +840,18 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
             write_gates(sm.gt[cb], chunk_gates(rc.a, rc.b, len), lane);
             stage_rows<RC>(sm.Ks[cb], rc.k, ptid, len);
             fetch(mn, yes{}, no{});
+            // wave u staged rows 16u..16u+15 (and all the gates): diagonal block u
             wave_fence();
             step1_diag(sm.Ks[cb], sm.Tm[cb], sm.gt[cb], u, lane);
             lds_barrier();  // B1
             step1_below(sm.Ks[cb], sm.Lb, sm.gt[cb], u, u < 2 ? u + 4 : u, u < 2, lane);
             lds_barrier();  // B2
-            if (u == 0) step2_inverse_below(sm.Tm[cb], sm.Lb, lane);
+            if (u == 0)
+                step2_inverse_below<0>(sm.Tm[cb], sm.Lb, lane);
+            else if (u == 1)
+                step2_inverse_below<1>(sm.Tm[cb], sm.Lb, lane);
+            else if (u == 2)
+                step2_inverse_below<2>(sm.Tm[cb], sm.Lb, lane);
             stage_rows<RC>(sm.Vs, rc.v, ptid, len);
             fetch(mn, no{}, yes{});
             lds_barrier();  // B0
@@ -986,9 +1002,10 @@ struct OutTiles {
 // so no chunk-sized W or Ut tile is formed).  Waves 4-7 stage chunk m+1 and
 // form its state-independent tiles (L, (I + L)^{-1}, A) while the carriers run
 // chunk m.  Every chunk has three barriers, met by both roles:
-//     carriers:  Q P and K P | B1 | right-hand side (reads v), solve | B2 | outputs, update | B0
-//     stagers:   k + gates, diagonal inverse blocks | B1 | L below the diagonal, q | B2 |
-//                inverse below the diagonal, A, v | B0
+//     carriers:  Q P and K P | B1 | right-hand side (reads v), solve, diagonal inverse
+//                blocks of chunk n+1 | B2 | outputs, update | B0
+//     stagers:   k + gates of chunk n+1 | B1 | L below the diagonal, q | B2 |
+//                inverse below the diagonal (three waves), A, v | B0
 // The stagers run one chunk ahead: they stage chunk n0 while the carriers
 // wait, and wait through the carriers' last chunk.
 __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* __restrict__ q,
@@ -1019,7 +1036,10 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
         // entering state: S0 itself when the sequence is one segment, else the
         // combined state (segment 0 included, so S_out may alias S0)
         load_state<2>(P, it.G == 1 ? S0h : ws + ws_P(it.slot0 + it.seg), col0, lane);
+        // diagonal block w of (I + L)^{-1} of chunk m (staged before the last B1)
+        auto diag = [&](int m) { step1_diag(sm.Ks[m & 1], sm.Tm[m & 1], sm.gt[m & 1], w, lane); };
         lds_barrier();  // B1, B2, B0 of chunk n0's staging
+        diag(n0);
         lds_barrier();
         lds_barrier();
         for (int n = n0; n < n1; ++n) {
@@ -1031,6 +1051,7 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
             lds_barrier();  // B1
             scan_rhs<2, true>(sm.Vs, gt, X, col0, lane, Xb);
             scan_solve<2, true>(sm.Tm[cb], gt, Xb, lane, Ub, Ue);
+            if (n + 1 < n1) diag(n + 1);
             lds_barrier();  // B2
             const int t0 = n * C;
             scan_out<2>(sm.As[cb], gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Os);
@@ -1052,8 +1073,6 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
         // 32-wide operand slices and must be zero; nothing else writes them.
         zero_above((u & 2) ? sm.As[u & 1] : sm.Tm[u & 1], 0, lane);
         zero_above((u & 2) ? sm.As[u & 1] : sm.Tm[u & 1], 5, lane);
-        // Wave u owns rows 16u..16u+15 of every staged tile, so right after
-        // writing its k rows (and all the gates) it forms diagonal block u.
         // Each tensor of chunk m+1 is fetched right after the same tensor of
         // chunk m is staged (the last chunk fetches itself again).
         using RC = RawChunk<kThreads / 2, true>;
@@ -1077,22 +1096,23 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
             write_gates(sm.gt[cb], chunk_gates(rc.a, rc.b, len), lane);
             stage_rows<RC>(sm.Ks[cb], rc.k, ptid, len);
             fetch(mn, no{}, yes{}, no{});
-            wave_fence();
-            step1_diag(sm.Ks[cb], sm.Tm[cb], sm.gt[cb], u, lane);
             lds_barrier();  // B1
             step1_below(sm.Ks[cb], sm.Lb, sm.gt[cb], u, u < 2 ? u + 4 : u, u < 2, lane);
             stage_rows<RC>(sm.Qs, rc.q, ptid, len);
             fetch(mn, yes{}, no{}, no{});
             lds_barrier();  // B2
-            if (u == 0) {
-                step2_inverse_below(sm.Tm[cb], sm.Lb, lane);
-            } else {
-                // blocks 0..9 of A: waves 1 and 2 four each, wave 3 two
-                if (u < 3)
-                    step2_qk<4>(sm.Qs, sm.Ks[cb], sm.As[cb], sm.gt[cb], 4 * (u - 1), lane);
-                else
-                    step2_qk<2>(sm.Qs, sm.Ks[cb], sm.As[cb], sm.gt[cb], 8, lane);
-            }
+            // the inverse in three parts (waves 0-2) and blocks 0..9 of A:
+            // waves 0 and 1 two each, waves 2 and 3 three each
+            if (u == 0)
+                step2_inverse_below<0>(sm.Tm[cb], sm.Lb, lane);
+            else if (u == 1)
+                step2_inverse_below<1>(sm.Tm[cb], sm.Lb, lane);
+            else if (u == 2)
+                step2_inverse_below<2>(sm.Tm[cb], sm.Lb, lane);
+            if (u < 2)
+                step2_qk<2>(sm.Qs, sm.Ks[cb], sm.As[cb], sm.gt[cb], 2 * u, lane);
+            else
+                step2_qk<3>(sm.Qs, sm.Ks[cb], sm.As[cb], sm.gt[cb], 3 * u - 2, lane);
             stage_rows<RC>(sm.Vs, rc.v, ptid, len);
             fetch(mn, no{}, no{}, yes{});
             lds_barrier();  // B0
