@@ -16,8 +16,10 @@ a bounded sample of the prefill workload.  Prints one JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 are launched on (torch's current stream, which the binding passes to the C
-ABI).  Input sets rotate over three copies so the 256 MB last-level cache
-cannot serve one step's inputs from the previous step.
+ABI): around the two launches of every fourth timed prefill step, and around
+each other leg's run of back-to-back calls (an event record costs a few
+microseconds of GPU time).  Input sets rotate over three copies so the 256 MB
+last-level cache cannot serve one step's inputs from the previous step.
 """
 
 import argparse
@@ -134,15 +136,20 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Per-kernel durations come from events recorded around the two launches of
+    # every fourth step of the timed run (an event record costs a few
+    # microseconds of GPU time, so recording them on every step would inflate
+    # the step time that `value` reports).
+    sampled = set(range(min(1, args.steps - 1), args.steps, 4))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs.values()]))
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = B * T * args.steps / elapsed
     head_tokens = B * H * T
@@ -189,13 +196,14 @@ def main():
     for i in range(2):
         gd.lin_attn_prefill(*la_sets[i % 3], form="chunked", chunk=Cl, out=la_out, S_out=la_S, z_out=la_z)
     torch.cuda.synchronize()
-    la_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    # the calls of each leg below run back to back between two events
+    la_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     la_ev[0].record()
     for i in range(args.la_steps):
         gd.lin_attn_prefill(*la_sets[i % 3], form="chunked", chunk=Cl, out=la_out, S_out=la_S, z_out=la_z)
-        la_ev[i + 1].record()
+    la_ev[1].record()
     torch.cuda.synchronize()
-    la_ms = float(np.mean([la_ev[i].elapsed_time(la_ev[i + 1]) for i in range(args.la_steps)]))
+    la_ms = la_ev[0].elapsed_time(la_ev[1]) / args.la_steps
     la_head_tokens = Bl * Hl * Tl
     la_bytes = la_head_tokens * 4 * dl * 2           # q, k, v, o in bf16
     la_flops = la_head_tokens * (2 * Cl * dl + 4 * dl * dl)
@@ -213,13 +221,13 @@ def main():
     for i in range(2):
         gd.gla_prefill(*gla_sets[i % 3], form="chunked", chunk=wg["chunk"], out=gla_out, S_out=gla_S)
     torch.cuda.synchronize()
-    g_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    g_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     g_ev[0].record()
     for i in range(args.la_steps):
         gd.gla_prefill(*gla_sets[i % 3], form="chunked", chunk=wg["chunk"], out=gla_out, S_out=gla_S)
-        g_ev[i + 1].record()
+    g_ev[1].record()
     torch.cuda.synchronize()
-    gla_ms = float(np.mean([g_ev[i].elapsed_time(g_ev[i + 1]) for i in range(args.la_steps)]))
+    gla_ms = g_ev[0].elapsed_time(g_ev[1]) / args.la_steps
     gla_bytes = wg["B"] * wg["H"] * wg["T"] * (4 * wg["dk"] * 2 + 4)   # q, k, v, o bf16 + alpha fp32
     gla_gbps = gla_bytes / (gla_ms * 1e-3) / 1e9
     del gla_sets
@@ -240,13 +248,13 @@ def main():
     for i in range(2):
         gd.gdn_preprocess(*pre_sets[i % 3], Hp, dkp, dvp, want_state=False, **pre_out)
     torch.cuda.synchronize()
-    p_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    p_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     p_ev[0].record()
     for i in range(args.la_steps):
         gd.gdn_preprocess(*pre_sets[i % 3], Hp, dkp, dvp, want_state=False, **pre_out)
-        p_ev[i + 1].record()
+    p_ev[1].record()
     torch.cuda.synchronize()
-    pre_ms = float(np.mean([p_ev[i].elapsed_time(p_ev[i + 1]) for i in range(args.la_steps)]))
+    pre_ms = p_ev[0].elapsed_time(p_ev[1]) / args.la_steps
     # x read + gate logits read, q, k, v written + alpha, beta written
     pre_bytes = Bp * Hp * Tp * (2 * ((2 * dkp + dvp) * 2 + 8))
     pre_gbps = pre_bytes / (pre_ms * 1e-3) / 1e9
@@ -266,16 +274,16 @@ def main():
         tq, tk, tv, ta, tb = pool[i % 8]
         gd.lin_attn_decode_step("gated_delta", tq, tk, tv, S, alpha=ta, beta=tb, out=o_dec)
     torch.cuda.synchronize()
-    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
     dev_ev[0].record()
     for i in range(steps):
         tq, tk, tv, ta, tb = pool[i % 8]
         gd.lin_attn_decode_step("gated_delta", tq, tk, tv, S, alpha=ta, beta=tb, out=o_dec)
-        dev_ev[i + 1].record()
+    dev_ev[1].record()
     torch.cuda.synchronize()
     dec_elapsed = time.perf_counter() - t0
-    dec_ms = float(np.mean([dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(steps)]))
+    dec_ms = dev_ev[0].elapsed_time(dev_ev[1]) / steps
     state_bytes = 2 * N * Hd * dd * dd * 4
     io_bytes = N * Hd * (3 * dd * 2 + dd * 2 + 8)
     dec_state_gbps = state_bytes / (dec_ms * 1e-3) / 1e9
@@ -303,13 +311,13 @@ def main():
         l_S = torch.empty((B5, H5, d5, d5), dtype=torch.float32, device=dev)
         gd.gdn_prefill(l_q, l_k, l_v, l_a, l_b, form="chunked", chunk=64, out=l_out, S_out=l_S, workspace=l_ws)
         torch.cuda.synchronize()
-        lev = [torch.cuda.Event(enable_timing=True) for _ in range(args.long_calls + 1)]
+        lev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         lev[0].record()
         for i in range(args.long_calls):
             gd.gdn_prefill(l_q, l_k, l_v, l_a, l_b, form="chunked", chunk=64, out=l_out, S_out=l_S, workspace=l_ws)
-            lev[i + 1].record()
+        lev[1].record()
         torch.cuda.synchronize()
-        long_ms = float(np.mean([lev[i].elapsed_time(lev[i + 1]) for i in range(args.long_calls)]))
+        long_ms = lev[0].elapsed_time(lev[1]) / args.long_calls
         long_gbps = B5 * H5 * T5 * path_bytes_per_head_token(d5) / (long_ms * 1e-3) / 1e9
         del l_q, l_k, l_v, l_a, l_b, l_ws, l_out, l_S
 
@@ -327,14 +335,14 @@ def main():
         tq, tk, tv, ta, tb = kpool[i % 8]
         gd.lin_attn_decode_step("kda", tq, tk, tv, Sk, alpha=ta, beta=tb, out=ok_dec)
     torch.cuda.synchronize()
-    kev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     kev[0].record()
     for i in range(steps):
         tq, tk, tv, ta, tb = kpool[i % 8]
         gd.lin_attn_decode_step("kda", tq, tk, tv, Sk, alpha=ta, beta=tb, out=ok_dec)
-        kev[i + 1].record()
+    kev[1].record()
     torch.cuda.synchronize()
-    kda_dec_ms = float(np.mean([kev[i].elapsed_time(kev[i + 1]) for i in range(steps)]))
+    kda_dec_ms = kev[0].elapsed_time(kev[1]) / steps
     # state read + write, q k v o in bf16, alpha per channel and beta in fp32
     kda_dec_bytes = 2 * Nk * Hk * dkk * dkk * 4 + Nk * Hk * (4 * dkk * 2 + dkk * 4 + 4)
     kda_dec_gbps = kda_dec_bytes / (kda_dec_ms * 1e-3) / 1e9
@@ -358,13 +366,13 @@ def main():
     for i in range(2):
         kcall(i)
     torch.cuda.synchronize()
-    kpe = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    kpe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     kpe[0].record()
     for i in range(args.la_steps):
         kcall(i)
-        kpe[i + 1].record()
+    kpe[1].record()
     torch.cuda.synchronize()
-    kda_pre_ms = float(np.mean([kpe[i].elapsed_time(kpe[i + 1]) for i in range(args.la_steps)]))
+    kda_pre_ms = kpe[0].elapsed_time(kpe[1]) / args.la_steps
     # q, k, v, o in bf16, per-channel alpha and beta in fp32
     kda_pre_bytes = Bk * Hkp * Tk * (4 * dkp * 2 + dkp * 4 + 4)
     kda_pre_gbps = kda_pre_bytes / (kda_pre_ms * 1e-3) / 1e9
@@ -399,13 +407,13 @@ def main():
     for i in range(2):
         vcall(i)
     torch.cuda.synchronize()
-    vev = [torch.cuda.Event(enable_timing=True) for _ in range(args.la_steps + 1)]
+    vev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     vev[0].record()
     for i in range(args.la_steps):
         vcall(i)
-        vev[i + 1].record()
+    vev[1].record()
     torch.cuda.synchronize()
-    var_ms = float(np.mean([vev[i].elapsed_time(vev[i + 1]) for i in range(args.la_steps)]))
+    var_ms = vev[0].elapsed_time(vev[1]) / args.la_steps
     var_bytes = Hv * wv["T_total"] * path_bytes_per_head_token(dvv) + (nsnap + wv["N"]) * Hv * dvv * dvv * 4
     var_gbps = var_bytes / (var_ms * 1e-3) / 1e9
     del vsets, v_out, v_S, v_snap, v_ws
