@@ -95,4 +95,44 @@ __device__ __forceinline__ bf16x8 pack_acc_pair(f32x4 lo, f32x4 hi) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ------------------------------------------------------------ LDS helpers
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v* lds_short4_ptr;
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
+// for this wave's global loads to land (its fence covers global memory); no
+// kernel here communicates through global memory inside a launch, so loads
+// issued ahead of time stay in flight across these barriers.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data (a wave executes LDS operations in order; this keeps the compiler from
+// moving them across).
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// i reads 4 consecutive 16-bit values E[i][0..3] at its own address, and lane
+// j = 4a + b receives E[a][b], E[a+4][b], E[a+8][b], E[a+12][b].
+__device__ __forceinline__ short4v ds_read_tr(const u16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(p));
+}
+
+// MFMA operand (8 values along the contraction index k) from a tile stored
+// k-major, X[k][n] with row stride LD: lane (r = 4a + b, g) receives
+// X[k0 + 8g + j][col(a) + b], j = 0..7, where col(a) (a multiple of 4) is the
+// first of the four columns that lanes 4a..4a+3 of every group take.
+template <int LD, class ColFn>
+__device__ __forceinline__ bf16x8 tr_operand(const u16 (*X)[LD], int k0, ColFn col, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int c = col(i & 3);
+    const short4v lo = ds_read_tr(&X[k0 + 8 * g + (i >> 2)][c]);
+    const short4v hi = ds_read_tr(&X[k0 + 8 * g + 4 + (i >> 2)][c]);
+    return __builtin_bit_cast(bf16x8, short8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+}
+
 }  // namespace la

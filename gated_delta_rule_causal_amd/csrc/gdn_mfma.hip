@@ -55,8 +55,6 @@ constexpr int LDA = C + 8;   // bf16 row stride of 64-wide LDS tiles (144 B)
 constexpr int kThreads = 512;                 // 8 waves per workgroup
 constexpr int kTargetBlocks = 256;            // workgroups that fill the chip (one per CU)
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ f32x4 mfma16x16x16(short4v a, short4v b, f32x4 c) {
     // v_mfma_f32_16x16x16_bf16: lane (r = l%16, g = l/16) holds A[r][4g..4g+3],
     // B[4g..4g+3][r]; the accumulator holds D[4g..4g+3][r].  K = 16 equals the
@@ -97,29 +95,6 @@ __device__ __forceinline__ void unpack8(uint4 raw, float* x) {
 struct Gates {
     float g[C], b[C], eg[C], sw[C], ek[C];  // g, beta, e^g, beta e^g, e^{g_c - g}
 };
-
-typedef short short8v __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) short4v* lds_short4_ptr;
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
-// i reads 4 consecutive 16-bit values E[i][0..3] at its own address, and lane
-// j = 4a + b receives E[a][b], E[a+4][b], E[a+8][b], E[a+12][b].
-__device__ __forceinline__ short4v ds_read_tr(const u16* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(p));
-}
-
-// MFMA operand (8 values along the contraction index k) from a tile stored
-// k-major, X[k][n]: lane (r = 4a + b, g) receives X[k0 + 8g + j][col(a) + b],
-// j = 0..7, where col(a) (a multiple of 4) is the first of the four columns
-// that lanes 4a..4a+3 of every group take.
-template <class ColFn>
-__device__ __forceinline__ bf16x8 tr_operand(const u16 (*X)[LDQ], int k0, ColFn col, int lane) {
-    const int g = lane >> 4, i = lane & 15;
-    const int c = col(i & 3);
-    const short4v lo = ds_read_tr(&X[k0 + 8 * g + (i >> 2)][c]);
-    const short4v hi = ds_read_tr(&X[k0 + 8 * g + 4 + (i >> 2)][c]);
-    return __builtin_bit_cast(bf16x8, short8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
-}
 
 // Raw chunk inputs held in registers between chunks.  Each 16-byte piece is
 // one of the sixteen in a 256-byte row, so the global loads are contiguous
@@ -177,21 +152,6 @@ __device__ __forceinline__ void stage_rows(u16 (*X)[LDQ], const uint4 (&raw)[NI]
         *reinterpret_cast<uint4*>(&X[row][RC::col(tid)]) = row < len ? raw[it] : make_uint4(0, 0, 0, 0);
     }
 }
-
-// Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
-// for this wave's global loads to land (its fence covers global memory); no
-// kernel here communicates through global memory inside a launch, so loads
-// issued ahead of time stay in flight across these barriers.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Orders this wave's LDS writes before its later LDS reads of other lanes'
-// data (a wave executes LDS operations in order; this keeps the compiler from
-// moving them across).
-__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
 // Gates of the chunk, one token per lane: g = inclusive scan of log alpha
 // over the wave.

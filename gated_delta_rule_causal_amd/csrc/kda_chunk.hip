@@ -64,15 +64,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Workgroup barrier ordering LDS accesses only: __syncthreads would also wait
-// for this wave's outstanding global loads, which here are the next chunk's
-// tiles loaded ahead on purpose.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ======================================================== tile pass
 struct TileSmem {
     u16 K[C][LDB];        // raw k

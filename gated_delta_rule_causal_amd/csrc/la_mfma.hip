@@ -67,16 +67,6 @@ __device__ __forceinline__ int perm_row(int t, int rr) {
 
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// Workgroup barrier that orders LDS accesses only: __syncthreads also waits
-// for this wave's outstanding global loads, which would stall on the next
-// block's prefetch.  Nothing here communicates through global memory inside
-// a launch.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // x + (x of the lane the DPP control selects, 0 where there is none).
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ float dpp_add(float x) {
