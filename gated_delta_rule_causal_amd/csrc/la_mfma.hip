@@ -22,9 +22,10 @@
 // accumulator registers; the state update is a plain accumulation
 // P += phi(K_b)^T V_b on MFMA and, as in the gated-delta scan, accumulator
 // tiles feed the next product as B operands through a permuted contraction
-// index.  Per block the tiles phi(Q), phi(K) (row-major), phi(K)^T and V^T
-// are staged in LDS with phi applied on the way in; the next block's raw
-// q/k/v are prefetched into registers while the current block computes.
+// index.  Per block the tiles phi(Q), phi(K) and V are staged row-major in
+// LDS with phi applied on the way in (the products that contract over tokens
+// read them with the transposing LDS load); the next block's raw q/k/v are
+// prefetched into registers while the current block computes.
 // z lives in LDS and is only written back by this workgroup, so an in-place
 // update of z is race-free.
 //
@@ -47,7 +48,7 @@ namespace {
 constexpr int C = 64;
 constexpr int D = 128;
 constexpr int LDR = D + 8;   // row-major [C][LDR] bf16 tiles (272-B rows)
-constexpr int LDT = C + 8;   // transposed [D][LDT] bf16 tiles (144-B rows)
+constexpr int LDT = C + 8;   // 64-wide [C][LDT] bf16 tiles (144-B rows)
 constexpr int kThreads = 256;
 constexpr int kItems = C * D / 8 / kThreads;  // 16-byte loads per thread per tile
 constexpr int kTargetBlocks = 256;           // workgroups that fill the chip (one per CU)
@@ -93,11 +94,10 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
     u16* __restrict__ o, float* S_out, float* z_out) {
     __shared__ __attribute__((aligned(16))) u16 fQ[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 fK[C][LDR];
-    __shared__ __attribute__((aligned(16))) u16 fKt[D][LDT];
-    __shared__ __attribute__((aligned(16))) u16 Vt[D][LDT];
+    __shared__ __attribute__((aligned(16))) u16 Vs[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 As[C][LDT];
     __shared__ float zs[D], dens[C];
-    __shared__ float gs[C], egs[C];   // GATED: chunk-local g and e^g
+    __shared__ float gs[C], egs[C], eks[C];   // GATED: chunk-local g, e^g, e^{g_c - g}
 
     const int nseg = OUT ? G : G - 1;
     const int bh = blockIdx.x / nseg;
@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             if (w == 0) {
                 gs[lane] = gx;
                 egs[lane] = __expf(gx);
+                eks[lane] = ek;
             }
         }
         // ---- stage phi(Q), phi(K), phi(K)^T, V^T (padded rows stay zero: phi is
@@ -191,7 +192,6 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             const bool real = row < len;
             const uint32_t wq[4] = {rq[it].x, rq[it].y, rq[it].z, rq[it].w};
             const uint32_t wk[4] = {rk[it].x, rk[it].y, rk[it].z, rk[it].w};
-            const uint32_t wv[4] = {rv[it].x, rv[it].y, rv[it].z, rv[it].w};
             float xq[8], xk[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -209,13 +209,7 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
             const bf16x8 pk = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
             if (OUT) *reinterpret_cast<bf16x8*>(&fQ[row][c8]) = pq;
             *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // bits from the fp32 value, not from an element of the packed
-                // __bf16 vector (extracting those for a bit cast miscompiles)
-                fKt[c8 + j][row] = f32_to_bf16_bits(GATED ? xk[j] * ek : xk[j]);
-                Vt[c8 + j][row] = static_cast<u16>((j & 1) ? (wv[j >> 1] >> 16) : (wv[j >> 1] & 0xffffu));
-            }
+            *reinterpret_cast<uint4*>(&Vs[row][c8]) = rv[it];
         }
         if (n + 1 < n1) fetch(n + 1);
         lds_barrier();
@@ -280,13 +274,29 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
         }
 
         // ---- this wave's 32 value channels: outputs, then the state update
-        bf16x8 Pb[2][4], Vb[2][2];
+        // V as B operands (tokens 32 s2 + 8 g .. +7 of value channel 32 w + 16 nb + r),
+        // read transposed from its row-major tile; GATED: Ve has the rows
+        // scaled by e^{g_c - g} for the state update
+        bf16x8 Pb[2][4], Vb[2][2], Ve[2][2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) Pb[nb][s] = pack_acc_pair(P[nb][2 * s], P[nb][2 * s + 1]);
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) Vb[nb][s2] = lds8(&Vt[32 * w + 16 * nb + r][32 * s2 + 8 * g]);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                Vb[nb][s2] = tr_operand(Vs, 32 * s2, [&](int aa) { return 32 * w + 16 * nb + 4 * aa; }, lane);
+                if constexpr (GATED) {
+                    const float4 e0 = *reinterpret_cast<const float4*>(&eks[32 * s2 + 8 * g]);
+                    const float4 e1 = *reinterpret_cast<const float4*>(&eks[32 * s2 + 8 * g + 4]);
+                    const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                    float x[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[j] = static_cast<float>(Vb[nb][s2][j]) * ee[j];
+                    Ve[nb][s2] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+                } else {
+                    Ve[nb][s2] = Vb[nb][s2];
+                }
+            }
         }
 #pragma unroll
         for (int m = 0; m < (OUT ? 4 : 0); ++m) {
@@ -311,27 +321,25 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
                 acc[0] = mfma16x16x32(a, Vb[0][s2], acc[0]);
                 acc[1] = mfma16x16x32(a, Vb[1][s2], acc[1]);
             }
-            // staged in this wave's own rows of V^T (read into Vb above, by
-            // this wave only): a [64][32] tile of its 32 value channels
+            // staged in this wave's own 32 columns of V (read into Vb above,
+            // by this wave only)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * m + 4 * g + i;
                 const float rden = GATED ? 1.f : 1.f / dens[row];
-                u16* Os = &Vt[32 * w][0];
-                Os[row * 32 + r] = f32_to_bf16_bits(acc[0][i] * rden);
-                Os[row * 32 + 16 + r] = f32_to_bf16_bits(acc[1][i] * rden);
+                Vs[row][32 * w + r] = f32_to_bf16_bits(acc[0][i] * rden);
+                Vs[row][32 * w + 16 + r] = f32_to_bf16_bits(acc[1][i] * rden);
             }
         }
         if constexpr (OUT) {
             // 16-byte global stores: 64 rows x 4 pieces of this wave's 32 channels
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            const u16* Os = &Vt[32 * w][0];
+            wave_fence();
 #pragma unroll
             for (int pass = 0; pass < C * 4 / kWave; ++pass) {
                 const int e = pass * kWave + lane, row = e >> 2, c8 = 8 * (e & 3);
                 if (row < len)
                     *reinterpret_cast<uint4*>(o + head + static_cast<size_t>(t0 + row) * D + 32 * w + c8) =
-                        *reinterpret_cast<const uint4*>(Os + row * 32 + c8);
+                        *reinterpret_cast<const uint4*>(&Vs[row][32 * w + c8]);
             }
         }
         if (GATED) {
@@ -346,9 +354,11 @@ __global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
         for (int t = 0; t < 8; ++t) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const bf16x8 a = lds8(&fKt[perm_row(t, r)][32 * s2 + 8 * g]);
-                P[0][t] = mfma16x16x32(a, Vb[0][s2], P[0][t]);
-                P[1][t] = mfma16x16x32(a, Vb[1][s2], P[1][t]);
+                // (phi(K) or K)^T rows in the permuted order, read transposed
+                const bf16x8 a =
+                    tr_operand(fK, 32 * s2, [&](int aa) { return 32 * (t >> 1) + 8 * aa + 4 * (t & 1); }, lane);
+                P[0][t] = mfma16x16x32(a, Ve[0][s2], P[0][t]);
+                P[1][t] = mfma16x16x32(a, Ve[1][s2], P[1][t]);
             }
         }
     }
