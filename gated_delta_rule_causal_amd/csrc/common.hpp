@@ -13,6 +13,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v* lds_short4_ptr;
 
 constexpr int kWave = 64;
 
@@ -95,10 +98,84 @@ __device__ __forceinline__ bf16x8 pack_acc_pair(f32x4 lo, f32x4 hi) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ------------------------------------------------- small MFMA building blocks
+__device__ __forceinline__ f32x4 mfma16x16x16(short4v a, short4v b, f32x4 c) {
+    // v_mfma_f32_16x16x16_bf16: lane (r = l%16, g = l/16) holds A[r][4g..4g+3],
+    // B[4g..4g+3][r]; the accumulator holds D[4g..4g+3][r].  K = 16 equals the
+    // accumulator's row span, so an accumulator tile is directly a B operand.
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ short4v to_bf16x4(f32x4 x) {
+    short4v r;
+    r[0] = static_cast<short>(f32_to_bf16_bits(x[0]));
+    r[1] = static_cast<short>(f32_to_bf16_bits(x[1]));
+    r[2] = static_cast<short>(f32_to_bf16_bits(x[2]));
+    r[3] = static_cast<short>(f32_to_bf16_bits(x[3]));
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_bf16x8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ short4v lds_short4(const u16* p) { return *reinterpret_cast<const short4v*>(p); }
+
+// Decode 8 packed bf16 (one uint4) to fp32.
+__device__ __forceinline__ void unpack8(uint4 raw, float* x) {
+    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        x[j] = __uint_as_float((j & 1) ? (wds[j >> 1] & 0xffff0000u) : (wds[j >> 1] << 16));
+}
+
+// fp32 value as a bf16 pair (high part, rounded remainder).
+struct Split4 {
+    short4v h, l;
+};
+
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+    Split4 s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const u16 hb = f32_to_bf16_bits(x[e]);
+        s.h[e] = static_cast<short>(hb);
+        s.l[e] = static_cast<short>(f32_to_bf16_bits(x[e] - bf16_bits_to_f32(hb)));
+    }
+    return s;
+}
+
+// c + a b for 16x16 fp32 matrices given as bf16 pairs (hi*hi + hi*lo + lo*hi:
+// about 16 significant bits).  a in operand layout, b in accumulator layout.
+__device__ __forceinline__ f32x4 mm3(const Split4& a, const Split4& b, f32x4 c) {
+    c = mfma16x16x16(a.l, b.h, c);
+    c = mfma16x16x16(a.h, b.l, c);
+    return mfma16x16x16(a.h, b.h, c);
+}
+
+// (I - N)^{-1} for a strictly lower triangular 16x16 N = -L given in the
+// accumulator layout together with its transpose Nt (the operand layout of N
+// is the accumulator layout of N^T).  N is nilpotent (N^16 = 0), so
+//     (I - N)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8),
+// built by three squarings, each folded into the running product; the
+// factors are powers of one matrix and commute.  The first (largest)
+// correction is formed from split bf16 pairs, the higher powers in bf16.
+__device__ __forceinline__ f32x4 unit_lower_inverse(f32x4 N, f32x4 Nt, int r, int g) {
+    f32x4 R = N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * g + i == r) R[i] += 1.f;
+    const Split4 P = split4(N), Pt = split4(Nt);
+    const f32x4 P2 = mm3(Pt, P, zero4());    // N N
+    const f32x4 P2t = mm3(P, Pt, zero4());   // (N N)^T = N^T N^T
+    R = mm3(split4(P2t), split4(R), R);      // R (I + N^2)
+    const short4v q2 = to_bf16x4(P2), q2t = to_bf16x4(P2t);
+    const f32x4 P4 = mfma16x16x16(q2t, q2, zero4());
+    const f32x4 P4t = mfma16x16x16(q2, q2t, zero4());
+    R = mfma16x16x16(to_bf16x4(P4t), to_bf16x4(R), R);   // R (I + N^4)
+    const f32x4 P8t = mfma16x16x16(to_bf16x4(P4), to_bf16x4(P4t), zero4());
+    return mfma16x16x16(to_bf16x4(P8t), to_bf16x4(R), R);   // R (I + N^8)
+}
+
+
 // ------------------------------------------------------------ LDS helpers
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef short short8v __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) short4v* lds_short4_ptr;
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
 // for this wave's global loads to land (its fence covers global memory); no

@@ -24,8 +24,10 @@
 // K * e^{g - g_m}, K * e^{g_m - g}, Q * e^{g - g_m} (g_m: the chunk's middle
 // token, so every factor lies within e^{+-80} whenever the chunk's decay span
 // is at most 80 in every channel; chunks with a larger span take an exact
-// path with one exponential per term); then [W | Ut] by forward substitution
-// in fp32, one column per thread.  Per chunk it writes W, Q * e^g (64 x 128),
+// path with one exponential per term); then T = (I + L)^{-1} on the matrix
+// cores (the four diagonal 16x16 blocks by the nilpotent product form in
+// registers, the blocks below them as three independent MFMA chains) and W,
+// Ut as plain products with T.  Per chunk it writes W, Q * e^g (64 x 128),
 // A (64 x 64), (K * e^{g_c - g})^T and Ut^T (128 x 64) in bf16 and e^{g_c}
 // (128 fp32): 74 240 bytes.
 //
@@ -45,6 +47,7 @@ namespace {
 constexpr int C = 64;           // tokens per chunk
 constexpr int D = 128;          // d_k = d_v
 constexpr int LDB = D + 8;      // bf16 row stride of the tile pass's LDS tiles
+constexpr int LDT = C + 8;      // bf16 row stride of the 64-wide T tile
 constexpr int kTileThreads = 256;
 constexpr int kScanThreads = 256;
 constexpr float kMaxSpan = 80.f;   // largest decay span of the factored fast path
@@ -147,53 +150,44 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
         }
     }
     __syncthreads();
-    if (tid < D) {
-        const float s = fmaxf(sm.g[0][tid] - sm.g[31][tid], sm.g[31][tid] - sm.g[C - 1][tid]);
-        atomicMax(&sm.span, __float_as_int(fmaxf(s, 0.f)));
+    if (tid < D) {   // largest span of the two half-chunks over the channels: one atomic per wave
+        float s = fmaxf(fmaxf(sm.g[0][tid] - sm.g[31][tid], sm.g[31][tid] - sm.g[C - 1][tid]), 0.f);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s = fmaxf(s, __shfl_xor(s, off, kWave));
+        if ((tid & 63) == 0) atomicMax(&sm.span, __float_as_int(s));
     }
     __syncthreads();
     const bool fast = __int_as_float(sm.span) <= kMaxSpan;
 
-    // ---- elementwise: scaled copies, Q e^g, Kt^T, e^{g_c}
+    // ---- elementwise: scaled copies, Q e^g (16-byte LDS reads of 8 channels)
     for (int e = tid; e < C * D / 8; e += kTileThreads) {
         const int t = e / (D / 8), c0 = (e % (D / 8)) * 8;
-        uint32_t wq[4], wp[4], wm[4], wqp[4];
+        const float4 g0 = *reinterpret_cast<const float4*>(&sm.g[t][c0]);
+        const float4 g1 = *reinterpret_cast<const float4*>(&sm.g[t][c0 + 4]);
+        const float4 m0 = *reinterpret_cast<const float4*>(&sm.g[31][c0]);
+        const float4 m1 = *reinterpret_cast<const float4*>(&sm.g[31][c0 + 4]);
+        const float gr[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float gm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float kv[8], qv[8];
+        unpack8(*reinterpret_cast<const uint4*>(&sm.K[t][c0]), kv);
+        unpack8(*reinterpret_cast<const uint4*>(&sm.Qp[t][c0]), qv);
+        float kp[8], km[8], qp[8], qe[8];
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            float kp[2], km[2], qp[2], qe[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int c = c0 + i + h;
-                const float gr = sm.g[t][c], gm = sm.g[31][c];
-                const float kv = bf(sm.K[t][c]), qv = bf(sm.Qp[t][c]);
-                const float up = __expf(gr - gm);
-                kp[h] = kv * up;
-                km[h] = kv * __expf(gm - gr);
-                qp[h] = qv * up;
-                qe[h] = qv * __expf(gr);
-            }
-            wp[i / 2] = pack2(kp[0], kp[1]);
-            wm[i / 2] = pack2(km[0], km[1]);
-            wqp[i / 2] = pack2(qp[0], qp[1]);
-            wq[i / 2] = pack2(qe[0], qe[1]);
+        for (int j = 0; j < 8; ++j) {
+            const float up = __expf(gr[j] - gm[j]);
+            kp[j] = kv[j] * up;
+            km[j] = kv[j] * __expf(gm[j] - gr[j]);
+            qp[j] = qv[j] * up;
+            qe[j] = qv[j] * __expf(gr[j]);
         }
-        *reinterpret_cast<uint4*>(rec + oQ + (static_cast<size_t>(t) * D + c0) * 2) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+        *reinterpret_cast<bf16x8*>(rec + oQ + (static_cast<size_t>(t) * D + c0) * 2) =
+            pack8(qe[0], qe[1], qe[2], qe[3], qe[4], qe[5], qe[6], qe[7]);
         if (fast) {
-            *reinterpret_cast<uint4*>(&sm.Kp[t][c0]) = make_uint4(wp[0], wp[1], wp[2], wp[3]);
-            *reinterpret_cast<uint4*>(&sm.Km[t][c0]) = make_uint4(wm[0], wm[1], wm[2], wm[3]);
+            *reinterpret_cast<bf16x8*>(&sm.Kp[t][c0]) = pack8(kp[0], kp[1], kp[2], kp[3], kp[4], kp[5], kp[6], kp[7]);
+            *reinterpret_cast<bf16x8*>(&sm.Km[t][c0]) = pack8(km[0], km[1], km[2], km[3], km[4], km[5], km[6], km[7]);
+            // q e^{g - g_m} replaces raw q only on the fast path (the exact path reads raw q)
+            *reinterpret_cast<bf16x8*>(&sm.Qp[t][c0]) = pack8(qp[0], qp[1], qp[2], qp[3], qp[4], qp[5], qp[6], qp[7]);
         }
-        // q e^{g - g_m} replaces raw q only on the fast path (the exact path reads raw q)
-        if (fast) *reinterpret_cast<uint4*>(&sm.Qp[t][c0]) = make_uint4(wqp[0], wqp[1], wqp[2], wqp[3]);
-    }
-    for (int e = tid; e < D * (C / 8); e += kTileThreads) {
-        const int c = e / (C / 8), tb = (e % (C / 8)) * 8;
-        const float gc = sm.g[C - 1][c];
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 8; i += 2)
-            w[i / 2] = pack2(bf(sm.K[tb + i][c]) * __expf(gc - sm.g[tb + i][c]),
-                             bf(sm.K[tb + i + 1][c]) * __expf(gc - sm.g[tb + i + 1][c]));
-        *reinterpret_cast<uint4*>(rec + oKt + (static_cast<size_t>(c) * C + tb) * 2) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     if (tid < D) reinterpret_cast<float*>(rec + oDec)[tid] = __expf(sm.g[C - 1][tid]);
     __syncthreads();
@@ -250,47 +244,143 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
     }
     __syncthreads();
 
-    // ---- [W | Ut] = (I + L)^{-1} diag(beta) [K e^g | V]: column tid, forward substitution
+    // ---- T = (I + L)^{-1} on the matrix cores (L fp32 in LDS, beta-scaled,
+    // strictly lower), then W = T diag(beta) (K e^g) and Ut = T diag(beta) V as
+    // plain products.  The tiles of Q e^{g - g_m}, K e^{g - g_m} and
+    // K e^{g_m - g} are no longer read: T and the two right-hand sides take
+    // their place.
+    u16 (*Tm)[LDT] = reinterpret_cast<u16 (*)[LDT]>(&sm.Qp[0][0]);   // T (bf16, lower triangular)
+    u16 (*Xw)[LDB] = sm.Kp;                                          // beta K e^g
+    u16 (*Xv)[LDB] = sm.Km;                                          // beta V
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15, gg = lane >> 4;
     {
-        const int col = tid;
-        float x[C];
+        // diagonal block w: N = -L_ww and its transpose, both in the accumulator layout
+        f32x4 N, Nt;
 #pragma unroll
-        for (int r = 0; r < C; ++r)
-            x[r] = col < D ? sm.beta[r] * bf(sm.K[r][col]) * __expf(sm.g[r][col]) : sm.beta[r] * bf(sm.V[r][col - D]);
-        // (right-hand sides first, then the sweep: one fused loop made the
-        // compiler keep every right-hand side live and spill)
-        // row r + 1 of L is read while row r is used (software pipelined:
-        // otherwise every row waits for its own LDS reads)
-        float4 cur[C / 4], nxt[C / 4];
-        cur[0] = *reinterpret_cast<const float4*>(&sm.L[1][0]);
-#pragma unroll
-        for (int r = 1; r < C; ++r) {
-            if (r + 1 < C) {
-#pragma unroll
-                for (int j4 = 0; j4 < (r + 4) / 4; ++j4) nxt[j4] = *reinterpret_cast<const float4*>(&sm.L[r + 1][4 * j4]);
-            }
-            float acc[4] = {x[r], 0.f, 0.f, 0.f};   // four chains: the sums are not one long dependency
-#pragma unroll
-            for (int j = 0; j < r; ++j) {
-                const float4 l = cur[j >> 2];
-                const float lj = (j & 3) == 0 ? l.x : (j & 3) == 1 ? l.y : (j & 3) == 2 ? l.z : l.w;
-                acc[j & 3] = fmaf(-lj, x[j], acc[j & 3]);
-            }
-            x[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-#pragma unroll
-            for (int j4 = 0; j4 < C / 4; ++j4) cur[j4] = nxt[j4];
+        for (int i = 0; i < 4; ++i) {
+            const int a_ = 16 * w + 4 * gg + i, b_ = 16 * w + r;
+            N[i] = r < 4 * gg + i ? -sm.L[a_][b_] : 0.f;
+            Nt[i] = 4 * gg + i < r ? -sm.L[b_][a_] : 0.f;
         }
-        if (col < D) {
-            u16* W = reinterpret_cast<u16*>(rec + oW);
+        const f32x4 Tb = unit_lower_inverse(N, Nt, r, gg);
 #pragma unroll
-            for (int r = 0; r < C; ++r) W[r * D + col] = f32_to_bf16_bits(x[r]);
-        } else {
-            unsigned char* ut = rec + oUt + static_cast<size_t>(col - D) * C * 2;
+        for (int i = 0; i < 4; ++i) Tm[16 * w + 4 * gg + i][16 * w + r] = f32_to_bf16_bits(Tb[i]);
+        // blocks (0,1) and (2,3) above the diagonal are read by 32-wide slices
+        if (w < 2) {
 #pragma unroll
-            for (int r = 0; r < C; r += 8)
-                *reinterpret_cast<uint4*>(ut + r * 2) =
-                    make_uint4(pack2(x[r], x[r + 1]), pack2(x[r + 2], x[r + 3]), pack2(x[r + 4], x[r + 5]),
-                               pack2(x[r + 6], x[r + 7]));
+            for (int i = 0; i < 4; ++i) Tm[32 * w + 4 * gg + i][32 * w + 16 + r] = 0;
+        }
+    }
+    for (int e = tid; e < C * D / 8; e += kTileThreads) {
+        const int t = e / (D / 8), c0 = (e % (D / 8)) * 8;
+        const uint4 kr = *reinterpret_cast<const uint4*>(&sm.K[t][c0]);
+        const uint4 vr = *reinterpret_cast<const uint4*>(&sm.V[t][c0]);
+        const float4 g0 = *reinterpret_cast<const float4*>(&sm.g[t][c0]);
+        const float4 g1 = *reinterpret_cast<const float4*>(&sm.g[t][c0 + 4]);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float4 c0v = *reinterpret_cast<const float4*>(&sm.g[C - 1][c0]);
+        const float4 c1v = *reinterpret_cast<const float4*>(&sm.g[C - 1][c0 + 4]);
+        const float gcv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
+        const float bt = sm.beta[t];
+        float kx[8], vx[8];
+        unpack8(kr, kx);
+        unpack8(vr, vx);
+        float xw[8], xv[8], xk[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            xw[j] = bt * kx[j] * __expf(gv[j]);
+            xv[j] = bt * vx[j];
+            xk[j] = kx[j] * __expf(gcv[j] - gv[j]);
+        }
+        *reinterpret_cast<bf16x8*>(&Xw[t][c0]) = pack8(xw[0], xw[1], xw[2], xw[3], xw[4], xw[5], xw[6], xw[7]);
+        *reinterpret_cast<bf16x8*>(&Xv[t][c0]) = pack8(xv[0], xv[1], xv[2], xv[3], xv[4], xv[5], xv[6], xv[7]);
+        // K e^{g_c - g} over raw v (this thread's piece, already read)
+        *reinterpret_cast<bf16x8*>(&sm.V[t][c0]) = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
+    }
+    __syncthreads();
+    // (K e^{g_c - g})^T: a transposed read gives lane (r, g) 8 consecutive
+    // tokens of one channel, one 16-byte piece of the record's [128][64] tile
+    {
+        u16* Kt = reinterpret_cast<u16*>(rec + oKt);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int item = 4 * w + j, dt = item >> 1, s = item & 1;   // 16 channels x 32 tokens
+            const bf16x8 x = tr_operand(sm.V, 32 * s, [&](int aa) { return 16 * dt + 4 * aa; }, lane);
+            *reinterpret_cast<bf16x8*>(Kt + (16 * dt + r) * C + 32 * s + 8 * gg) = x;
+        }
+    }
+    // below-diagonal blocks of T, T_ij = T_ii sum_{j<=k<i} (-L_ik) T_kj, as
+    // three independent chains on waves 0-2 (T_10, T_20, T_30; T_21, T_31; T_32)
+    {
+        auto nl = [&](int i, int j) {   // A operand of -L_ij (bf16)
+            const float4 x = *reinterpret_cast<const float4*>(&sm.L[16 * i + r][16 * j + 4 * gg]);
+            return to_bf16x4(f32x4{-x.x, -x.y, -x.z, -x.w});
+        };
+        auto ta = [&](int i) { return lds_short4(&Tm[16 * i + r][16 * i + 4 * gg]); };
+        auto tb = [&](int i) {          // B operand of T_ii
+            short4v x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = static_cast<short>(Tm[16 * i + 4 * gg + e][16 * i + r]);
+            return x;
+        };
+        auto put = [&](int i, int j, short4v t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Tm[16 * i + 4 * gg + e][16 * j + r] = static_cast<u16>(t[e]);
+        };
+        auto solve = [&](short4v a, f32x4 y) { return to_bf16x4(mfma16x16x16(a, to_bf16x4(y), zero4())); };
+        if (w == 0) {
+            const short4v t00 = tb(0);
+            const short4v l10 = nl(1, 0), l20 = nl(2, 0), l21 = nl(2, 1), l30 = nl(3, 0), l31 = nl(3, 1), l32 = nl(3, 2);
+            const short4v a1 = ta(1), a2 = ta(2), a3 = ta(3);
+            const short4v t10 = solve(a1, mfma16x16x16(l10, t00, zero4()));
+            const short4v t20 = solve(a2, mfma16x16x16(l21, t10, mfma16x16x16(l20, t00, zero4())));
+            const short4v t30 =
+                solve(a3, mfma16x16x16(l32, t20, mfma16x16x16(l31, t10, mfma16x16x16(l30, t00, zero4()))));
+            put(1, 0, t10);
+            put(2, 0, t20);
+            put(3, 0, t30);
+        } else if (w == 1) {
+            const short4v t11 = tb(1);
+            const short4v l21 = nl(2, 1), l31 = nl(3, 1), l32 = nl(3, 2);
+            const short4v a2 = ta(2), a3 = ta(3);
+            const short4v t21 = solve(a2, mfma16x16x16(l21, t11, zero4()));
+            const short4v t31 = solve(a3, mfma16x16x16(l32, t21, mfma16x16x16(l31, t11, zero4())));
+            put(2, 1, t21);
+            put(3, 1, t31);
+        } else if (w == 2) {
+            const short4v t22 = tb(2);
+            const short4v l32 = nl(3, 2), a3 = ta(3);
+            put(3, 2, solve(a3, mfma16x16x16(l32, t22, zero4())));
+        }
+    }
+    __syncthreads();
+    // W^T = Xw^T T^T and Ut = T Xv on the matrix cores; wave w takes the
+    // 16-token column tile w of W^T and the 16-token row tile w of Ut.
+    // T is lower triangular: slices s > w/2 of its rows are zero.
+    {
+        const int tt = w;
+        u16* Wrec = reinterpret_cast<u16*>(rec + oW);
+        u16* Urec = reinterpret_cast<u16*>(rec + oUt);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            f32x4 accw = zero4(), accu = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (s > (tt >> 1)) break;
+                const bf16x8 trow = lds_bf16x8(&Tm[16 * tt + r][32 * s + 8 * gg]);
+                // W^T[d][tok] = sum_j Xw[j][d] T[tok][j]: A = Xw^T (transposed read), B = T rows
+                const bf16x8 xw = tr_operand(Xw, 32 * s, [&](int aa) { return 16 * dt + 4 * aa; }, lane);
+                accw = mfma16x16x32(xw, trow, accw);
+                // Ut[tok][v] = sum_j T[tok][j] Xv[j][v]: A = T rows, B = Xv (transposed read)
+                const bf16x8 xv = tr_operand(Xv, 32 * s, [&](int aa) { return 16 * dt + 4 * aa; }, lane);
+                accu = mfma16x16x32(trow, xv, accu);
+            }
+            // accw: lane holds W[tok = 16 tt + r][d = 16 dt + 4 gg .. +3];
+            // accu: lane holds Ut[tok = 16 tt + 4 gg .. +3][v = 16 dt + r] = Ut^T[v][tok ..]
+            *reinterpret_cast<uint2*>(Wrec + (16 * tt + r) * D + 16 * dt + 4 * gg) =
+                make_uint2(pack2(accw[0], accw[1]), pack2(accw[2], accw[3]));
+            *reinterpret_cast<uint2*>(Urec + (16 * dt + r) * C + 16 * tt + 4 * gg) =
+                make_uint2(pack2(accu[0], accu[1]), pack2(accu[2], accu[3]));
         }
     }
 }
