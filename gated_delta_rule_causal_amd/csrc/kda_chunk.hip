@@ -197,26 +197,34 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
     if (fast) {
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15, gg = lane >> 4;
         // 10 lower tile pairs (I >= J) x {L, A}: wave w takes items w, w+4, ...
+        // A is formed transposed (K e^{g_m - g} times Q e^{g - g_m}) so each lane
+        // holds 4 consecutive columns of one row: 8-byte stores into the record.
         for (int item = w; item < 20; item += 4) {
             const int p = item >> 1;
             const bool isA = item & 1;
             int I = 0;
             while ((I + 1) * (I + 2) / 2 <= p) ++I;
             const int J = p - I * (I + 1) / 2;
-            f32x4 acc = zero4();
-            const u16 (*X)[LDB] = isA ? sm.Qp : sm.Kp;
+            bf16x8 xa[4], xb[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&X[16 * I + r][32 * s + 8 * gg]));
-                const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Km[16 * J + r][32 * s + 8 * gg]));
-                acc = mfma16x16x32(a, b, acc);
+                xa[s] = lds_bf16x8(isA ? &sm.Km[16 * J + r][32 * s + 8 * gg] : &sm.Kp[16 * I + r][32 * s + 8 * gg]);
+                xb[s] = lds_bf16x8(isA ? &sm.Qp[16 * I + r][32 * s + 8 * gg] : &sm.Km[16 * J + r][32 * s + 8 * gg]);
             }
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * I + 4 * gg + i, col = 16 * J + r;
-                if (isA) {
-                    Arec[row * C + col] = f32_to_bf16_bits(col <= row ? acc[i] : 0.f);
-                } else {
+            for (int s = 0; s < 4; ++s) acc = mfma16x16x32(xa[s], xb[s], acc);
+            if (isA) {
+                // lane holds A[row = 16 I + r][cols 16 J + 4 gg .. +3]
+                const int row = 16 * I + r, col = 16 * J + 4 * gg;
+                float a4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a4[i] = col + i <= row ? acc[i] : 0.f;
+                *reinterpret_cast<uint2*>(Arec + row * C + col) = make_uint2(pack2(a4[0], a4[1]), pack2(a4[2], a4[3]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * I + 4 * gg + i, col = 16 * J + r;
                     sm.L[row][col] = col < row ? sm.beta[row] * acc[i] : 0.f;
                 }
             }
@@ -237,10 +245,13 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             Arec[row * C + col] = f32_to_bf16_bits(col <= row ? sa : 0.f);
         }
     }
-    // tiles above the diagonal block row of A are zero
-    for (int e = tid; e < C * C; e += kTileThreads) {
-        const int row = e / C, col = e % C;
-        if (col / 16 > row / 16) Arec[row * C + col] = 0;
+    // the six 16x16 tiles above the diagonal tiles of A are zero (8-byte stores)
+    {
+        const int lane = tid & 63, wv = tid >> 6;
+        for (int blk = wv; blk < 6; blk += 4) {
+            const int I = blk < 3 ? 0 : blk < 5 ? 1 : 2, J = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+            *reinterpret_cast<uint2*>(Arec + (16 * I + (lane & 15)) * C + 16 * J + 4 * (lane >> 4)) = make_uint2(0, 0);
+        }
     }
     __syncthreads();
 
