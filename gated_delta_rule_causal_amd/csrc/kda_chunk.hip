@@ -34,7 +34,8 @@
 // Scan (one workgroup per (head, 16 value channels), 4 waves).  Wave w owns
 // token rows 16w.. of X = W P, U and O and key rows 32w.. of P (fp32 in its
 // accumulators); P^T and U^T (bf16) are shared through LDS, two barriers per
-// chunk.  The tiles of chunk n+1 are loaded while chunk n runs.  The eight
+// chunk.  The tiles of chunks n+1 and n+2 are loaded while chunk n runs, each
+// wave-wide load one contiguous run of the record.  The eight
 // workgroups of a head take block indices eight apart, so they run on one XCD
 // and read each chunk's tiles from that XCD's L2.
 #include "common.hpp"
@@ -53,13 +54,29 @@ constexpr int kScanThreads = 256;
 constexpr float kMaxSpan = 80.f;   // largest decay span of the factored fast path
 
 // per-chunk record (bytes)
-constexpr size_t oW = 0;              // W       [64][128] bf16
-constexpr size_t oQ = 16384;          // Q e^g   [64][128] bf16
-constexpr size_t oA = 32768;          // A       [64][64]  bf16 (zero above the diagonal)
-constexpr size_t oKt = 40960;         // Kt^T    [128][64] bf16
-constexpr size_t oUt = 57344;         // Ut^T    [128][64] bf16
+constexpr size_t oW = 0;              // W       [64][128] bf16, fragment order (frag8)
+constexpr size_t oQ = 16384;          // Q e^g   [64][128] bf16, frag8
+constexpr size_t oA = 32768;          // A       [64][64]  bf16 (zero above the diagonal), frag8
+constexpr size_t oKt = 40960;         // Kt^T    [128][64] bf16, frag8
+constexpr size_t oUt = 57344;         // Ut^T    [128][64] bf16, frag4
 constexpr size_t oDec = 73728;        // e^{g_c} [128] fp32
 constexpr size_t kRecord = 74240;
+
+// The bf16 tiles of the record are stored in the order the scan's MFMA
+// operands read them, so each wave-wide load is one contiguous run (1 KiB for
+// a 16-byte piece per lane) instead of 16 half cache lines.
+//   frag8: 16 x 32 blocks (row-block major), inside a block lane (r, g) =
+//          16 g + r holds row r, columns 8g .. 8g+7 (16 bytes);
+//   frag4: 16 x 16 blocks, lane 16 g + r holds row r, columns 4g .. 4g+3.
+// Element offsets for a tile with `ncols` columns:
+__host__ __device__ constexpr int frag8(int row, int col, int ncols) {
+    return ((((row >> 4) * (ncols >> 5) + (col >> 5)) * 64 + ((col >> 3) & 3) * 16 + (row & 15)) << 3) + (col & 7);
+}
+__host__ __device__ constexpr int frag4(int row, int col, int ncols) {
+    return ((((row >> 4) * (ncols >> 4) + (col >> 4)) * 64 + ((col >> 2) & 3) * 16 + (row & 15)) << 2) + (col & 3);
+}
+static_assert(frag8(17, 40, 128) == ((4 + 1) * 64 + 16 + 1) * 8, "frag8 block order");
+static_assert(frag4(17, 21, 64) == ((4 + 1) * 64 + 16 + 1) * 4 + 1, "frag4 block order");
 
 __device__ __forceinline__ float bf(u16 b) { return bf16_bits_to_f32(b); }
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -180,7 +197,7 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             qp[j] = qv[j] * up;
             qe[j] = qv[j] * __expf(gr[j]);
         }
-        *reinterpret_cast<bf16x8*>(rec + oQ + (static_cast<size_t>(t) * D + c0) * 2) =
+        *reinterpret_cast<bf16x8*>(rec + oQ + static_cast<size_t>(frag8(t, c0, D)) * 2) =
             pack8(qe[0], qe[1], qe[2], qe[3], qe[4], qe[5], qe[6], qe[7]);
         if (fast) {
             *reinterpret_cast<bf16x8*>(&sm.Kp[t][c0]) = pack8(kp[0], kp[1], kp[2], kp[3], kp[4], kp[5], kp[6], kp[7]);
@@ -220,7 +237,7 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
                 float a4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) a4[i] = col + i <= row ? acc[i] : 0.f;
-                *reinterpret_cast<uint2*>(Arec + row * C + col) = make_uint2(pack2(a4[0], a4[1]), pack2(a4[2], a4[3]));
+                *reinterpret_cast<uint2*>(Arec + frag8(row, col, C)) = make_uint2(pack2(a4[0], a4[1]), pack2(a4[2], a4[3]));
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
                 }
             }
             sm.L[row][col] = col < row ? sm.beta[row] * sl : 0.f;
-            Arec[row * C + col] = f32_to_bf16_bits(col <= row ? sa : 0.f);
+            Arec[frag8(row, col, C)] = f32_to_bf16_bits(col <= row ? sa : 0.f);
         }
     }
     // the six 16x16 tiles above the diagonal tiles of A are zero (8-byte stores)
@@ -250,7 +267,7 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
         const int lane = tid & 63, wv = tid >> 6;
         for (int blk = wv; blk < 6; blk += 4) {
             const int I = blk < 3 ? 0 : blk < 5 ? 1 : 2, J = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-            *reinterpret_cast<uint2*>(Arec + (16 * I + (lane & 15)) * C + 16 * J + 4 * (lane >> 4)) = make_uint2(0, 0);
+            *reinterpret_cast<uint2*>(Arec + frag8(16 * I + (lane & 15), 16 * J + 4 * (lane >> 4), C)) = make_uint2(0, 0);
         }
     }
     __syncthreads();
@@ -317,7 +334,7 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
         for (int j = 0; j < 4; ++j) {
             const int item = 4 * w + j, dt = item >> 1, s = item & 1;   // 16 channels x 32 tokens
             const bf16x8 x = tr_operand(sm.V, 32 * s, [&](int aa) { return 16 * dt + 4 * aa; }, lane);
-            *reinterpret_cast<bf16x8*>(Kt + (16 * dt + r) * C + 32 * s + 8 * gg) = x;
+            *reinterpret_cast<bf16x8*>(Kt + frag8(16 * dt + r, 32 * s + 8 * gg, C)) = x;
         }
     }
     // below-diagonal blocks of T, T_ij = T_ii sum_{j<=k<i} (-L_ik) T_kj, as
@@ -388,9 +405,9 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             }
             // accw: lane holds W[tok = 16 tt + r][d = 16 dt + 4 gg .. +3];
             // accu: lane holds Ut[tok = 16 tt + 4 gg .. +3][v = 16 dt + r] = Ut^T[v][tok ..]
-            *reinterpret_cast<uint2*>(Wrec + (16 * tt + r) * D + 16 * dt + 4 * gg) =
+            *reinterpret_cast<uint2*>(Wrec + frag8(16 * tt + r, 16 * dt + 4 * gg, D)) =
                 make_uint2(pack2(accw[0], accw[1]), pack2(accw[2], accw[3]));
-            *reinterpret_cast<uint2*>(Urec + (16 * dt + r) * C + 16 * tt + 4 * gg) =
+            *reinterpret_cast<uint2*>(Urec + frag4(16 * dt + r, 16 * tt + 4 * gg, C)) =
                 make_uint2(pack2(accu[0], accu[1]), pack2(accu[2], accu[3]));
         }
     }
@@ -400,6 +417,7 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
 struct ScanSmem {
     u16 PT[16][D + 8];    // P^T (bf16): [value column][key channel]
     u16 UT[16][C + 8];    // U^T (bf16): [value column][token]
+    u16 Os[4][16][20];    // each wave's 16 x 16 output tile, turned into row pieces
 };
 
 struct ChunkOps {
@@ -417,17 +435,17 @@ __device__ __forceinline__ void load_ops(ChunkOps& op, const unsigned char* rec,
     const float* d = reinterpret_cast<const float*>(rec + oDec);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        op.W[s] = *reinterpret_cast<const uint4*>(W + (16 * w + r) * D + 32 * s + 8 * gg);
-        op.Q[s] = *reinterpret_cast<const uint4*>(Q + (16 * w + r) * D + 32 * s + 8 * gg);
+        op.W[s] = *reinterpret_cast<const uint4*>(W + frag8(16 * w + r, 32 * s + 8 * gg, D));
+        op.Q[s] = *reinterpret_cast<const uint4*>(Q + frag8(16 * w + r, 32 * s + 8 * gg, D));
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        op.A[s] = *reinterpret_cast<const uint4*>(A + (16 * w + r) * C + 32 * s + 8 * gg);
+        op.A[s] = *reinterpret_cast<const uint4*>(A + frag8(16 * w + r, 32 * s + 8 * gg, C));
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-            op.K[mt][s] = *reinterpret_cast<const uint4*>(K + (32 * w + 16 * mt + r) * C + 32 * s + 8 * gg);
+            op.K[mt][s] = *reinterpret_cast<const uint4*>(K + frag8(32 * w + 16 * mt + r, 32 * s + 8 * gg, C));
     }
-    op.U = *reinterpret_cast<const uint2*>(U + (16 * cb + r) * C + 16 * w + 4 * gg);
+    op.U = *reinterpret_cast<const uint2*>(U + frag4(16 * cb + r, 16 * w + 4 * gg, C));
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) op.d[mt] = *reinterpret_cast<const float4*>(d + 32 * w + 16 * mt + 4 * gg);
 }
@@ -453,15 +471,8 @@ __device__ __forceinline__ void scan_chunk(ScanSmem& sm, const ChunkOps& op, f32
     bf16x8 ub[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) ub[s] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.UT[r][32 * s + 8 * gg]));
-    // O += A U; store rows inside the sequence
-#pragma unroll
-    for (int s = 0; s < 2; ++s) O = mfma16x16x32(as_bf16x8(op.A[s]), ub[s], O);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 16 * w + 4 * gg + i;
-        if (t < len) o[(orow + t) * D + 16 * cb + r] = f32_to_bf16_bits(O[i]);
-    }
-    // P <- Diag(e^{g_c}) P + Kt^T U (key rows 32w + 16mt + 4gg + i)
+    // P <- Diag(e^{g_c}) P + Kt^T U (key rows 32w + 16mt + 4gg + i): first,
+    // since the next chunk waits for P^T
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
         const float dd[4] = {op.d[mt].x, op.d[mt].y, op.d[mt].z, op.d[mt].w};
@@ -474,7 +485,18 @@ __device__ __forceinline__ void scan_chunk(ScanSmem& sm, const ChunkOps& op, f32
         *reinterpret_cast<uint2*>(&sm.PT[r][32 * w + 16 * mt + 4 * gg]) =
             make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
     }
+    // O += A U.  The lane holds O[16w + 4gg + i][r]; the wave's tile goes
+    // through its own LDS block so each lane stores 4 columns of one row.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) O = mfma16x16x32(as_bf16x8(op.A[s]), ub[s], O);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.Os[w][4 * gg + i][r] = f32_to_bf16_bits(O[i]);
+    wave_fence();
+    const int lane = 16 * gg + r, orw = lane >> 2, ocl = 4 * (lane & 3);
+    const uint2 orow_bits = *reinterpret_cast<const uint2*>(&sm.Os[w][orw][ocl]);
     lds_barrier();
+    if (16 * w + orw < len)
+        *reinterpret_cast<uint2*>(o + (orow + 16 * w + orw) * D + 16 * cb + ocl) = orow_bits;
 }
 
 __global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(int BH, int T, int NC,
