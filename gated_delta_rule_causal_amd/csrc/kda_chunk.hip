@@ -19,8 +19,8 @@
 // of P) evolves on its own: P <- Diag(e^{g_c}) P + Kt^T (Ut - W P), which is
 // what lets the scan split a head over workgroups.
 //
-// Tile pass (one workgroup per chunk, 256 threads).  g by a per-channel
-// running sum; the decayed products L and A as MFMA products of scaled copies
+// Tile pass (one workgroup per chunk, 256 threads, two workgroups per CU).
+// g by sums over 4-token blocks plus their exclusive prefix; the decayed products L and A as MFMA products of scaled copies
 // K * e^{g - g_m}, K * e^{g_m - g}, Q * e^{g - g_m} (g_m: the chunk's middle
 // token, so every factor lies within e^{+-80} whenever the chunk's decay span
 // is at most 80 in every channel; chunks with a larger span take an exact
@@ -85,17 +85,36 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // ======================================================== tile pass
+// LDS of the tile pass, about 79 KiB so that two workgroups share a CU (one
+// loads its chunk while the other computes).  The raw k, v, q pieces and the
+// decay sums stay in the registers of the thread that loaded them; the three
+// scaled copies, then the exact path's g and k, then the right-hand sides of
+// W and Ut take turns in one region.
 struct TileSmem {
-    u16 K[C][LDB];        // raw k
-    u16 V[C][LDB];        // raw v
-    u16 Qp[C][LDB];       // raw q, then q e^{g - g_m} (fast path)
-    u16 Kp[C][LDB];       // k e^{g - g_m}
-    u16 Km[C][LDB];       // k e^{g_m - g}
-    float g[C][D];        // chunk-local cumulative log decay
+    union {
+        struct {
+            u16 Kp[C][LDB];     // k e^{g - g_m}
+            u16 Km[C][LDB];     // k e^{g_m - g}
+            u16 Qp[C][LDB];     // q e^{g - g_m}
+        } f;                    // fast path, L and A
+        struct {
+            float g[C][D];      // chunk-local cumulative log decay
+            u16 K[C][LDB];      // raw k
+        } x;                    // exact path, L and A
+        struct {
+            u16 Xw[C][LDB];     // beta k e^g
+            u16 Xv[C][LDB];     // beta v
+            u16 Kc[C][LDB];     // k e^{g_c - g}
+        } r;                    // right-hand sides and (K e^{g_c - g})^T
+        float part[16][D];      // log-decay sums of 4-token blocks, then their exclusive prefix
+    };
+    u16 Tm[C][LDT];       // T = (I + L)^{-1} (bf16, lower triangular)
     float L[C][C + 4];    // beta_r L_rj (strictly lower)
     float beta[C];
+    float g0[D], gm[D], gc[D];   // g at tokens 0, C/2 - 1 and C - 1
     int span;             // max decay span over channels (float bits, >= 0)
 };
+static_assert(sizeof(TileSmem) <= 80 * 1024, "two tile workgroups per CU");
 
 __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, int NC, bool scalar_gate,
                                                                 const u16* __restrict__ q, const u16* __restrict__ k,
@@ -112,101 +131,127 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
     const size_t row0 = static_cast<size_t>(bh) * T + t0;   // first token row of the chunk
     unsigned char* rec = ws + (static_cast<size_t>(bh) * NC + n) * kRecord;
 
+    // Thread (tb, cg) owns tokens 4 tb .. 4 tb + 3 and channels 8 cg .. 8 cg + 7
+    // of every per-token tile: 16 threads cover one 256-byte row of k, v, q.
+    const int tb = tid >> 4, c0 = (tid & 15) * 8;
+    uint4 kr[4], vr[4], qr[4];
+    float g[4][8];   // running log decay of the owned tokens (local sums first)
     if (tid == 0) sm.span = 0;
-    // ---- every input load of the chunk first (coalesced 16-byte pieces): log
-    // alpha into g, raw k, v, q tiles; then the running sums of g
     {
-        float4 al[8];
-        uint4 kk[4], vv[4], qq[4];
+        float4 al[4][2];
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {           // alpha: 64 x 128 fp32 = 2048 float4
-            const int e = it * kTileThreads + tid, t = e >> 5, c4 = (e & 31) * 4;
-            al[it] = make_float4(1.f, 1.f, 1.f, 1.f);
+        for (int j = 0; j < 4; ++j) {   // rows past the sequence: alpha = 1, k = v = q = 0
+            const int t = 4 * tb + j;
+            al[j][0] = al[j][1] = make_float4(1.f, 1.f, 1.f, 1.f);
+            kr[j] = vr[j] = qr[j] = make_uint4(0, 0, 0, 0);
             if (t < len) {
                 if (scalar_gate) {
                     const float a = alpha[row0 + t];
-                    al[it] = make_float4(a, a, a, a);
+                    al[j][0] = al[j][1] = make_float4(a, a, a, a);
                 } else {
-                    al[it] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c4);
+                    al[j][0] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c0);
+                    al[j][1] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c0 + 4);
                 }
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {           // k, v, q: 64 x 128 bf16 = 1024 pieces each
-            const int e = it * kTileThreads + tid, t = e >> 4, c8 = (e & 15) * 8;
-            kk[it] = vv[it] = qq[it] = make_uint4(0, 0, 0, 0);
-            if (t < len) {
-                const size_t gi = (row0 + t) * D + c8;
-                kk[it] = *reinterpret_cast<const uint4*>(k + gi);
-                vv[it] = *reinterpret_cast<const uint4*>(v + gi);
-                qq[it] = *reinterpret_cast<const uint4*>(q + gi);
+                const size_t gi = (row0 + t) * D + c0;
+                kr[j] = *reinterpret_cast<const uint4*>(k + gi);
+                vr[j] = *reinterpret_cast<const uint4*>(v + gi);
+                qr[j] = *reinterpret_cast<const uint4*>(q + gi);
             }
         }
         if (tid < C) sm.beta[tid] = tid < len ? beta[row0 + tid] : 0.f;
+        float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int e = it * kTileThreads + tid, t = e >> 5, c4 = (e & 31) * 4;
-            *reinterpret_cast<float4*>(&sm.g[t][c4]) =
-                make_float4(__logf(al[it].x), __logf(al[it].y), __logf(al[it].z), __logf(al[it].w));
-        }
+        for (int j = 0; j < 4; ++j) {
+            const float la[8] = {__logf(al[j][0].x), __logf(al[j][0].y), __logf(al[j][0].z), __logf(al[j][0].w),
+                                 __logf(al[j][1].x), __logf(al[j][1].y), __logf(al[j][1].z), __logf(al[j][1].w)};
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int e = it * kTileThreads + tid, t = e >> 4, c8 = (e & 15) * 8;
-            *reinterpret_cast<uint4*>(&sm.K[t][c8]) = kk[it];
-            *reinterpret_cast<uint4*>(&sm.V[t][c8]) = vv[it];
-            *reinterpret_cast<uint4*>(&sm.Qp[t][c8]) = qq[it];
+            for (int i = 0; i < 8; ++i) {
+                run[i] += la[i];
+                g[j][i] = run[i];
+            }
+            if (tb == 0 && j == 0) {
+                *reinterpret_cast<float4*>(&sm.g0[c0]) = make_float4(la[0], la[1], la[2], la[3]);
+                *reinterpret_cast<float4*>(&sm.g0[c0 + 4]) = make_float4(la[4], la[5], la[6], la[7]);
+            }
         }
+        *reinterpret_cast<float4*>(&sm.part[tb][c0]) = make_float4(run[0], run[1], run[2], run[3]);
+        *reinterpret_cast<float4*>(&sm.part[tb][c0 + 4]) = make_float4(run[4], run[5], run[6], run[7]);
     }
     __syncthreads();
-    if (tid < D) {   // running sum over the chunk's tokens, one channel per thread
-        float acc = 0.f;
-#pragma unroll 16
-        for (int t = 0; t < C; ++t) {
-            acc += sm.g[t][tid];
-            sm.g[t][tid] = acc;
-        }
-    }
-    __syncthreads();
-    if (tid < D) {   // largest span of the two half-chunks over the channels: one atomic per wave
-        float s = fmaxf(fmaxf(sm.g[0][tid] - sm.g[31][tid], sm.g[31][tid] - sm.g[C - 1][tid]), 0.f);
+    if (tid < D) {   // exclusive prefix of the 16 block sums, one channel per thread; g_m, g_c, e^{g_c}, span
+        float acc = 0.f, gmid = 0.f;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s = fmaxf(s, __shfl_xor(s, off, kWave));
-        if ((tid & 63) == 0) atomicMax(&sm.span, __float_as_int(s));
+        for (int b = 0; b < 16; ++b) {
+            if (b == C / 2 / 4) gmid = acc;   // blocks of tokens 0 .. C/2 - 1
+            const float x = sm.part[b][tid];
+            sm.part[b][tid] = acc;
+            acc += x;
+        }
+        sm.gm[tid] = gmid;
+        sm.gc[tid] = acc;
+        reinterpret_cast<float*>(rec + oDec)[tid] = __expf(acc);
+        // largest span of the two half-chunks over the channels: one atomic per wave
+        float sp = fmaxf(fmaxf(sm.g0[tid] - gmid, gmid - acc), 0.f);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, kWave));
+        if ((tid & 63) == 0) atomicMax(&sm.span, __float_as_int(sp));
     }
     __syncthreads();
     const bool fast = __int_as_float(sm.span) <= kMaxSpan;
-
-    // ---- elementwise: scaled copies, Q e^g (16-byte LDS reads of 8 channels)
-    for (int e = tid; e < C * D / 8; e += kTileThreads) {
-        const int t = e / (D / 8), c0 = (e % (D / 8)) * 8;
-        const float4 g0 = *reinterpret_cast<const float4*>(&sm.g[t][c0]);
-        const float4 g1 = *reinterpret_cast<const float4*>(&sm.g[t][c0 + 4]);
-        const float4 m0 = *reinterpret_cast<const float4*>(&sm.g[31][c0]);
-        const float4 m1 = *reinterpret_cast<const float4*>(&sm.g[31][c0 + 4]);
-        const float gr[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const float gm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        float kv[8], qv[8];
-        unpack8(*reinterpret_cast<const uint4*>(&sm.K[t][c0]), kv);
-        unpack8(*reinterpret_cast<const uint4*>(&sm.Qp[t][c0]), qv);
-        float kp[8], km[8], qp[8], qe[8];
+    float gmv[8], gcv[8];
+    {
+        const float4 p0 = *reinterpret_cast<const float4*>(&sm.part[tb][c0]);
+        const float4 p1 = *reinterpret_cast<const float4*>(&sm.part[tb][c0 + 4]);
+        const float pre[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float up = __expf(gr[j] - gm[j]);
-            kp[j] = kv[j] * up;
-            km[j] = kv[j] * __expf(gm[j] - gr[j]);
-            qp[j] = qv[j] * up;
-            qe[j] = qv[j] * __expf(gr[j]);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[j][i] += pre[i];
+        const float4 m0 = *reinterpret_cast<const float4*>(&sm.gm[c0]);
+        const float4 m1 = *reinterpret_cast<const float4*>(&sm.gm[c0 + 4]);
+        const float4 e0 = *reinterpret_cast<const float4*>(&sm.gc[c0]);
+        const float4 e1 = *reinterpret_cast<const float4*>(&sm.gc[c0 + 4]);
+        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        const float cv[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            gmv[i] = mv[i];
+            gcv[i] = cv[i];
         }
+    }
+    __syncthreads();   // every thread has read its block prefix: the region now takes the tiles
+
+    // ---- elementwise: Q e^g to the record; the scaled copies (fast path) or
+    // g and raw k (exact path) into LDS
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * tb + j;
+        float kv[8], qv[8];
+        unpack8(kr[j], kv);
+        unpack8(qr[j], qv);
+        float qe[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qe[i] = qv[i] * __expf(g[j][i]);
         *reinterpret_cast<bf16x8*>(rec + oQ + static_cast<size_t>(frag8(t, c0, D)) * 2) =
             pack8(qe[0], qe[1], qe[2], qe[3], qe[4], qe[5], qe[6], qe[7]);
         if (fast) {
-            *reinterpret_cast<bf16x8*>(&sm.Kp[t][c0]) = pack8(kp[0], kp[1], kp[2], kp[3], kp[4], kp[5], kp[6], kp[7]);
-            *reinterpret_cast<bf16x8*>(&sm.Km[t][c0]) = pack8(km[0], km[1], km[2], km[3], km[4], km[5], km[6], km[7]);
-            // q e^{g - g_m} replaces raw q only on the fast path (the exact path reads raw q)
-            *reinterpret_cast<bf16x8*>(&sm.Qp[t][c0]) = pack8(qp[0], qp[1], qp[2], qp[3], qp[4], qp[5], qp[6], qp[7]);
+            float kp[8], km[8], qp[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float up = __expf(g[j][i] - gmv[i]);
+                kp[i] = kv[i] * up;
+                km[i] = kv[i] * __expf(gmv[i] - g[j][i]);
+                qp[i] = qv[i] * up;
+            }
+            *reinterpret_cast<bf16x8*>(&sm.f.Kp[t][c0]) = pack8(kp[0], kp[1], kp[2], kp[3], kp[4], kp[5], kp[6], kp[7]);
+            *reinterpret_cast<bf16x8*>(&sm.f.Km[t][c0]) = pack8(km[0], km[1], km[2], km[3], km[4], km[5], km[6], km[7]);
+            *reinterpret_cast<bf16x8*>(&sm.f.Qp[t][c0]) = pack8(qp[0], qp[1], qp[2], qp[3], qp[4], qp[5], qp[6], qp[7]);
+        } else {
+            *reinterpret_cast<float4*>(&sm.x.g[t][c0]) = make_float4(g[j][0], g[j][1], g[j][2], g[j][3]);
+            *reinterpret_cast<float4*>(&sm.x.g[t][c0 + 4]) = make_float4(g[j][4], g[j][5], g[j][6], g[j][7]);
+            *reinterpret_cast<uint4*>(&sm.x.K[t][c0]) = kr[j];
         }
     }
-    if (tid < D) reinterpret_cast<float*>(rec + oDec)[tid] = __expf(sm.g[C - 1][tid]);
     __syncthreads();
 
     // ---- L (beta-scaled, strictly lower) into LDS, A (lower incl. diagonal) to the record
@@ -225,8 +270,8 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             bf16x8 xa[4], xb[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                xa[s] = lds_bf16x8(isA ? &sm.Km[16 * J + r][32 * s + 8 * gg] : &sm.Kp[16 * I + r][32 * s + 8 * gg]);
-                xb[s] = lds_bf16x8(isA ? &sm.Qp[16 * I + r][32 * s + 8 * gg] : &sm.Km[16 * J + r][32 * s + 8 * gg]);
+                xa[s] = lds_bf16x8(isA ? &sm.f.Km[16 * J + r][32 * s + 8 * gg] : &sm.f.Kp[16 * I + r][32 * s + 8 * gg]);
+                xb[s] = lds_bf16x8(isA ? &sm.f.Qp[16 * I + r][32 * s + 8 * gg] : &sm.f.Km[16 * J + r][32 * s + 8 * gg]);
             }
             f32x4 acc = zero4();
 #pragma unroll
@@ -247,15 +292,18 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             }
         }
     } else {
-        // exact path: one exponential per term
+        // exact path: one exponential per term (raw q read from memory: rows
+        // past the sequence are zero)
         for (int e = tid; e < C * C; e += kTileThreads) {
             const int row = e / C, col = e % C;
             float sl = 0.f, sa = 0.f;
             if (col <= row) {
+                const u16* qrow = q + (row0 + min(row, len - 1)) * D;
+                const float qs = row < len ? 1.f : 0.f;
                 for (int c = 0; c < D; ++c) {
-                    const float f = __expf(sm.g[row][c] - sm.g[col][c]) * bf(sm.K[col][c]);
-                    sl = fmaf(bf(sm.K[row][c]), f, sl);
-                    sa = fmaf(bf(sm.Qp[row][c]), f, sa);
+                    const float f = __expf(sm.x.g[row][c] - sm.x.g[col][c]) * bf(sm.x.K[col][c]);
+                    sl = fmaf(bf(sm.x.K[row][c]), f, sl);
+                    sa = fmaf(qs * bf(qrow[c]), f, sa);
                 }
             }
             sm.L[row][col] = col < row ? sm.beta[row] * sl : 0.f;
@@ -274,12 +322,11 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
 
     // ---- T = (I + L)^{-1} on the matrix cores (L fp32 in LDS, beta-scaled,
     // strictly lower), then W = T diag(beta) (K e^g) and Ut = T diag(beta) V as
-    // plain products.  The tiles of Q e^{g - g_m}, K e^{g - g_m} and
-    // K e^{g_m - g} are no longer read: T and the two right-hand sides take
-    // their place.
-    u16 (*Tm)[LDT] = reinterpret_cast<u16 (*)[LDT]>(&sm.Qp[0][0]);   // T (bf16, lower triangular)
-    u16 (*Xw)[LDB] = sm.Kp;                                          // beta K e^g
-    u16 (*Xv)[LDB] = sm.Km;                                          // beta V
+    // plain products.  The scaled copies are no longer read: the two
+    // right-hand sides and K e^{g_c - g} take their place.
+    u16 (*Tm)[LDT] = sm.Tm;
+    u16 (*Xw)[LDB] = sm.r.Xw;
+    u16 (*Xv)[LDB] = sm.r.Xv;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15, gg = lane >> 4;
     {
         // diagonal block w: N = -L_ww and its transpose, both in the accumulator layout
@@ -299,31 +346,23 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             for (int i = 0; i < 4; ++i) Tm[32 * w + 4 * gg + i][32 * w + 16 + r] = 0;
         }
     }
-    for (int e = tid; e < C * D / 8; e += kTileThreads) {
-        const int t = e / (D / 8), c0 = (e % (D / 8)) * 8;
-        const uint4 kr = *reinterpret_cast<const uint4*>(&sm.K[t][c0]);
-        const uint4 vr = *reinterpret_cast<const uint4*>(&sm.V[t][c0]);
-        const float4 g0 = *reinterpret_cast<const float4*>(&sm.g[t][c0]);
-        const float4 g1 = *reinterpret_cast<const float4*>(&sm.g[t][c0 + 4]);
-        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const float4 c0v = *reinterpret_cast<const float4*>(&sm.g[C - 1][c0]);
-        const float4 c1v = *reinterpret_cast<const float4*>(&sm.g[C - 1][c0 + 4]);
-        const float gcv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {   // from the pieces this thread loaded
+        const int t = 4 * tb + j;
         const float bt = sm.beta[t];
         float kx[8], vx[8];
-        unpack8(kr, kx);
-        unpack8(vr, vx);
+        unpack8(kr[j], kx);
+        unpack8(vr[j], vx);
         float xw[8], xv[8], xk[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            xw[j] = bt * kx[j] * __expf(gv[j]);
-            xv[j] = bt * vx[j];
-            xk[j] = kx[j] * __expf(gcv[j] - gv[j]);
+        for (int i = 0; i < 8; ++i) {
+            xw[i] = bt * kx[i] * __expf(g[j][i]);
+            xv[i] = bt * vx[i];
+            xk[i] = kx[i] * __expf(gcv[i] - g[j][i]);
         }
         *reinterpret_cast<bf16x8*>(&Xw[t][c0]) = pack8(xw[0], xw[1], xw[2], xw[3], xw[4], xw[5], xw[6], xw[7]);
         *reinterpret_cast<bf16x8*>(&Xv[t][c0]) = pack8(xv[0], xv[1], xv[2], xv[3], xv[4], xv[5], xv[6], xv[7]);
-        // K e^{g_c - g} over raw v (this thread's piece, already read)
-        *reinterpret_cast<bf16x8*>(&sm.V[t][c0]) = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
+        *reinterpret_cast<bf16x8*>(&sm.r.Kc[t][c0]) = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
     }
     __syncthreads();
     // (K e^{g_c - g})^T: a transposed read gives lane (r, g) 8 consecutive
@@ -333,7 +372,7 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int item = 4 * w + j, dt = item >> 1, s = item & 1;   // 16 channels x 32 tokens
-            const bf16x8 x = tr_operand(sm.V, 32 * s, [&](int aa) { return 16 * dt + 4 * aa; }, lane);
+            const bf16x8 x = tr_operand(sm.r.Kc, 32 * s, [&](int aa) { return 16 * dt + 4 * aa; }, lane);
             *reinterpret_cast<bf16x8*>(Kt + frag8(16 * dt + r, 32 * s + 8 * gg, C)) = x;
         }
     }
