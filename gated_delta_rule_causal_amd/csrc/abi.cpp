@@ -484,7 +484,7 @@ la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) return copy_state(S0, S_out, heads * dv * dk, s);
     if (form == LA_FORM_CHUNKED)
-        return from_hip(la::launch_kda_mfma(B, H, T, false, q, k, v, alpha, beta, S0, o, S_out, workspace, s));
+        return from_hip(la::launch_kda_mfma(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, s));
     return from_hip(la::launch_recurrent(la::kKda, dtype, static_cast<int>(heads), T, dk, dv, q, k, v, alpha, beta,
                                          S0, S_out, nullptr, nullptr, o, s));
 }

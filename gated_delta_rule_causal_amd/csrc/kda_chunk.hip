@@ -116,7 +116,7 @@ struct TileSmem {
 };
 static_assert(sizeof(TileSmem) <= 80 * 1024, "two tile workgroups per CU");
 
-__global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, int NC, bool scalar_gate,
+__global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, int NC,
                                                                 const u16* __restrict__ q, const u16* __restrict__ k,
                                                                 const u16* __restrict__ v,
                                                                 const float* __restrict__ alpha,
@@ -145,13 +145,8 @@ __global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, i
             al[j][0] = al[j][1] = make_float4(1.f, 1.f, 1.f, 1.f);
             kr[j] = vr[j] = qr[j] = make_uint4(0, 0, 0, 0);
             if (t < len) {
-                if (scalar_gate) {
-                    const float a = alpha[row0 + t];
-                    al[j][0] = al[j][1] = make_float4(a, a, a, a);
-                } else {
-                    al[j][0] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c0);
-                    al[j][1] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c0 + 4);
-                }
+                al[j][0] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c0);
+                al[j][1] = *reinterpret_cast<const float4*>(alpha + (row0 + t) * D + c0 + 4);
                 const size_t gi = (row0 + t) * D + c0;
                 kr[j] = *reinterpret_cast<const uint4*>(k + gi);
                 vr[j] = *reinterpret_cast<const uint4*>(v + gi);
@@ -604,7 +599,7 @@ size_t kda_mfma_workspace_bytes(int B, int H, int T) {
     return static_cast<size_t>(B) * H * ((T + C - 1) / C) * kRecord;
 }
 
-hipError_t launch_kda_mfma(int B, int H, int T, bool scalar_gate, const void* q, const void* k, const void* v,
+hipError_t launch_kda_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                            void* workspace, hipStream_t stream) {
     const int BH = B * H;
@@ -612,7 +607,7 @@ hipError_t launch_kda_mfma(int B, int H, int T, bool scalar_gate, const void* q,
     const int NC = (T + C - 1) / C;
     auto* ws = static_cast<unsigned char*>(workspace);
     hipLaunchKernelGGL(kda_tile_kernel, dim3(static_cast<unsigned>(BH) * NC), dim3(kTileThreads), 0, stream, BH, T, NC,
-                       scalar_gate, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                       static_cast<const u16*>(q), static_cast<const u16*>(k),
                        static_cast<const u16*>(v), alpha, beta, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -82,11 +82,10 @@ hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
                                   int snap, int snap_cap, float* S_snap, void* workspace, hipStream_t stream);
 
 // Chunked KDA (kda_chunk.hip): a per-chunk tile pass into the workspace, then
-// a column-parallel scan.  alpha [B,H,T,128] per channel, or [B,H,T] when
-// scalar_gate (the Gated DeltaNet equation through the same kernels).
+// a column-parallel scan.  alpha [B,H,T,128] per channel.
 bool kda_mfma_supported(int dtype, int dk, int dv, int chunk);
 size_t kda_mfma_workspace_bytes(int B, int H, int T);
-hipError_t launch_kda_mfma(int B, int H, int T, bool scalar_gate, const void* q, const void* k, const void* v,
+hipError_t launch_kda_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                            void* workspace, hipStream_t stream);
 
