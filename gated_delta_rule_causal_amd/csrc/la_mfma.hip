@@ -17,7 +17,9 @@
 //  * la_combine_kernel: entering states by prefix sums, S0 + dS_0 + ... ;
 //  * la_chunked_mfma_kernel<true> (every segment): outputs from the entering
 //    state, and the final state in the last segment.
-// One workgroup (4 waves) walks the blocks of its segment in order.  Each wave
+// One workgroup (4 waves) walks the blocks of its segment in order; the
+// kernels are held to 256 registers per lane so that two workgroups share a
+// CU (about 512 segments in flight, one hiding the other's latencies).  Each wave
 // owns 32 value channels of the state, P = S_rows^T (d_k x 32, fp32) in
 // accumulator registers; the state update is a plain accumulation
 // P += phi(K_b)^T V_b on MFMA and, as in the gated-delta scan, accumulator
@@ -51,7 +53,7 @@ constexpr int LDR = D + 8;   // row-major [C][LDR] bf16 tiles (272-B rows)
 constexpr int LDT = C + 8;   // 64-wide [C][LDT] bf16 tiles (144-B rows)
 constexpr int kThreads = 256;
 constexpr int kItems = C * D / 8 / kThreads;  // 16-byte loads per thread per tile
-constexpr int kTargetBlocks = 256;           // workgroups that fill the chip (one per CU)
+constexpr int kTargetBlocks = 512;           // workgroups that fill the chip (two per CU)
 constexpr size_t kMat = static_cast<size_t>(D) * D;
 
 // Workspace record per (head, segment): entering state P (state layout
@@ -88,7 +90,7 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // OUT = false: segment contributions only (no q, no outputs), from a zero state.
 // GATED: the scalar-gated variant (alpha used, z0/z_out unused).
 template <bool GATED, bool OUT>
-__global__ __launch_bounds__(kThreads) void la_chunked_mfma_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void la_chunked_mfma_kernel(
     int BH, int T, int NC, int G, int SEGC, const u16* __restrict__ q, const u16* __restrict__ k,
     const u16* __restrict__ v, const float* __restrict__ alpha, const float* S0, const float* z0, float* ws,
     u16* __restrict__ o, float* S_out, float* z_out) {
