@@ -150,6 +150,20 @@ def test_kda_chunked_strong_decay(gd):
     report("  S", slice_err(S, S_ref), TOL["bf16"])
 
 
+@pytest.mark.parametrize("T", [100, 37])
+def test_kda_chunked_strong_decay_ragged(gd, T):
+    """Every chunk on the exact path, the last one shorter than a chunk (its
+    padded rows must add nothing), with an entering state."""
+    B, H, d = 2, 2, 128
+    q, k, v, a, b = synth.kda_batch(85, B, H, T, d, d, "bf16")
+    a[..., ::2] = np.maximum(a[..., ::2] ** 60, np.float32(1e-30))
+    S0 = synth.state_batch(86, B, H, d, d, 0.05)
+    o_ref, S_ref = ob.kda(q, k, v, a, b, S0, form="chunked")
+    o, S = run_chunked(gd, q, k, v, a, b, S0)
+    report(f"kda chunked strong decay, ragged T={T} o", slice_err(o, o_ref), TOL["bf16"])
+    report("  S", slice_err(S, S_ref), TOL["bf16"])
+
+
 def test_kda_chunked_uniform_is_gated_delta(gd):
     B, H, T, d = 1, 2, 500, 128
     q, k, v, a, b = synth.kda_batch(82, B, H, T, d, d, "bf16")
