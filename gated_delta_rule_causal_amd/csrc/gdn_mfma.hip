@@ -639,11 +639,11 @@ __device__ __forceinline__ bool find_item(const Geo& g, int blk, bool maps, Item
 // LDS of the map kernel: k, (I + L)^{-1} and gates in two copies by chunk
 // parity, v in one (rewritten after the carriers' last read of it).
 struct MapTiles {
-    u16 Ks[2][C][LDQ];
+    u16 Ks[3][C][LDQ];    // chunk m in copy m % 3
     u16 Vs[C][LDQ];
-    u16 Tm[2][C][LDA];
+    u16 Tm[2][C][LDA];    // chunk m in copy m & 1
     u16 Lb[C][LDA];
-    Gates gt[2];
+    Gates gt[3];          // chunk m in copy m % 3
 };
 
 constexpr int kMapThreads = 768;   // 8 state carriers + 4 stagers
@@ -652,9 +652,15 @@ constexpr int kMapThreads = 768;   // 8 state carriers + 4 stagers
 // [0 | I]): waves 0-3 the N columns (value channels 32w..32w+31, with V),
 // waves 4-7 the M columns (no V term).  Per chunk, like the output kernel
 // without Q, A and the outputs:
-//     carriers:  K P | B1 | right-hand side (reads v), solve | B2 | update | B0
-//     stagers:   k + gates, diagonal inverse blocks of chunk n+1 | B1 |
-//                L below the diagonal | B2 | inverse below the diagonal (three waves), v | B0
+//     carriers:  K P | B1 | right-hand side (reads v), solve | B2 | update,
+//                staging | B0
+//     stagers:   diagonal inverse blocks of chunk n+1 | B1 |
+//                L below the diagonal | B2 | inverse below the diagonal (three waves) | B0
+// The stagers' three steps are the longest path of a chunk, so the carriers
+// also stage the inputs, in their last phase: waves 0-3 (whose update is the
+// shorter) k and the gates of chunk n+2, waves 4-7 v of chunk n+1 (k has
+// three LDS copies: chunk n for the carriers, n+1 for the stagers, n+2 being
+// written).
 __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
                                                               const u16* __restrict__ v,
                                                               const float* __restrict__ alpha,
@@ -666,6 +672,7 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branches below are scalar
     const int n0 = it.n0, n1 = it.n1, T = it.len;
     const size_t head_tok = it.head_tok;
+    using RC = RawChunk<256, true>;
     if (w < 8) {
         const int r = lane & 15, g = lane >> 4;
         const bool npart = w < 4;
@@ -678,15 +685,46 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     P[nt][t][i] = (!npart && perm_row(t, 4 * g + i) == col0 + 16 * nt + r) ? 1.f : 0.f;
-        lds_barrier();  // B1, B2, B0 of chunk n0's staging
+        // inputs: waves 0-3 load k and the gates, waves 4-7 v into rc.k (the
+        // gates that come with it are not used); chunk n + ahead is staged in
+        // the last phase of chunk n, every index past the segment clamped to
+        // its last chunk (no branch around the loads)
+        const bool kpart = npart;
+        const int ptid = tid & 255, ahead = kpart ? 2 : 1;
+        const u16* src = kpart ? k : v;
+        RC rc;
+        auto fetch = [&](int m) {
+            m = min(m, n1 - 1);
+            fetch_chunk<false, true, false>(rc, nullptr, src, nullptr, alpha, beta, head_tok, m * C, min(C, T - m * C),
+                                            ptid);
+        };
+        auto stage = [&](int m) {
+            m = min(m, n1 - 1);
+            const int len = min(C, T - m * C);
+            if (kpart) {
+                write_gates(sm.gt[m % 3], chunk_gates(rc.a, rc.b, len), lane);
+                stage_rows<RC>(sm.Ks[m % 3], rc.k, ptid, len);
+            } else {
+                stage_rows<RC>(sm.Vs, rc.k, ptid, len);
+            }
+        };
+        fetch(n0);
+        stage(n0);
+        fetch(n0 + 1);
+        lds_barrier();  // k, gates and v of chunk n0 staged
+        lds_barrier();  // B1, B2, B0 of the stagers' chunk n0
         lds_barrier();
+        if (kpart) {   // k of chunk n0 + 1 before the stagers start on it
+            stage(n0 + 1);
+            fetch(n0 + 2);
+        }
         lds_barrier();
         for (int n = n0; n < n1; ++n) {
-            const int cb = n & 1;
-            const Gates& gt = sm.gt[cb];
+            const int c3 = n % 3, cb = n & 1;
+            const Gates& gt = sm.gt[c3];
             f32x4 O[2][4], X[2][4];
             bf16x8 Xb[2][2], Ub[2][2], Ue[2][2];
-            scan_qk<2, false>(nullptr, sm.Ks[cb], P, lane, O, X);
+            scan_qk<2, false>(nullptr, sm.Ks[c3], P, lane, O, X);
             lds_barrier();  // B1
             if (npart)
                 scan_rhs<2, true>(sm.Vs, gt, X, col0, lane, Xb);
@@ -694,7 +732,9 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
                 scan_rhs<2, false>(sm.Vs, gt, X, col0, lane, Xb);
             scan_solve<2, false>(sm.Tm[cb], gt, Xb, lane, Ub, Ue);
             lds_barrier();  // B2
-            scan_update<2>(sm.Ks[cb], gt, P, Ue, lane);
+            scan_update<2>(sm.Ks[c3], gt, P, Ue, lane);
+            stage(n + ahead);
+            fetch(n + ahead + 1);
             lds_barrier();  // B0
         }
         if (npart)
@@ -702,34 +742,16 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
         else
             store_state_rowmajor<2>(P, ws + ws_M(it.slot0 + it.seg), col0, lane);
     } else {
-        const int ptid = tid - 512;
         const int u = w - 8;
         // The blocks (0,1) and (2,3) above the diagonal of Tm are read by
         // 32-wide operand slices and must be zero; nothing else writes them.
         zero_above(sm.Tm[u & 1], (u & 2) ? 5 : 0, lane);
-        using RC = RawChunk<256, true>;
-        RC rc;
-        using yes = std::true_type;
-        using no = std::false_type;
-        auto fetch = [&](int m, auto with_k, auto with_v) {
-            fetch_chunk<false, decltype(with_k)::value, decltype(with_v)::value>(
-                rc, nullptr, k, v, alpha, beta, head_tok, m * C, min(C, T - m * C), ptid);
-        };
-        // the same issue order as inside the loop (k and gates, then v)
-        fetch(n0, yes{}, no{});
-        __builtin_amdgcn_sched_barrier(0);
-        fetch(n0, no{}, yes{});
-        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();  // the carriers staged chunk n0
         for (int m = n0; m < n1; ++m) {
-            const int cb = m & 1, len = min(C, T - m * C), mn = min(m + 1, n1 - 1);
-            write_gates(sm.gt[cb], chunk_gates(rc.a, rc.b, len), lane);
-            stage_rows<RC>(sm.Ks[cb], rc.k, ptid, len);
-            fetch(mn, yes{}, no{});
-            // wave u staged rows 16u..16u+15 (and all the gates): diagonal block u
-            wave_fence();
-            step1_diag(sm.Ks[cb], sm.Tm[cb], sm.gt[cb], u, lane);
+            const int c3 = m % 3, cb = m & 1;
+            step1_diag(sm.Ks[c3], sm.Tm[cb], sm.gt[c3], u, lane);
             lds_barrier();  // B1
-            step1_below(sm.Ks[cb], sm.Lb, sm.gt[cb], u, u < 2 ? u + 4 : u, u < 2, lane);
+            step1_below(sm.Ks[c3], sm.Lb, sm.gt[c3], u, u < 2 ? u + 4 : u, u < 2, lane);
             lds_barrier();  // B2
             if (u == 0)
                 step2_inverse_below<0>(sm.Tm[cb], sm.Lb, lane);
@@ -737,8 +759,6 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
                 step2_inverse_below<1>(sm.Tm[cb], sm.Lb, lane);
             else if (u == 2)
                 step2_inverse_below<2>(sm.Tm[cb], sm.Lb, lane);
-            stage_rows<RC>(sm.Vs, rc.v, ptid, len);
-            fetch(mn, no{}, yes{});
             lds_barrier();  // B0
         }
         lds_barrier();  // B1, B2, B0 of the carriers' last chunk
