@@ -142,37 +142,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     if (tid < D) zs[tid] = zin ? zin[tid] : 0.f;
 
-    // ---- raw chunk prefetch: item e = tid + kThreads * it -> row = e % C, c8 = 8 (e / C).
-    // The output pass keeps the next chunk in flight (its registers go to the
-    // state and the output tiles); the state pass keeps the next two, in two
-    // register sets used in turn (the loop is unrolled by two so that each set
-    // keeps a fixed name; loads past the segment reload its last chunk).
-    struct Raw {
-        uint4 q[kItems], k[kItems], v[kItems];
-        float a;   // GATED: alpha of token `lane` of the chunk (1 past the end)
-    };
+    // ---- raw chunk prefetch: item e = tid + kThreads * it -> row = e % C, c8 = 8 (e / C)
+    uint4 rq[kItems], rk[kItems], rv[kItems];
+    float ra = 1.f;   // GATED: alpha of token `lane` of the chunk (1 past the end)
     float decay = 1.f;  // GATED: product of the gates seen so far in this segment
     const size_t head = static_cast<size_t>(bh) * T * D;
-    auto fetch = [&](Raw& R, int n) {
+    auto fetch = [&](int n) {
         const int t0 = n * C;
         const int len = min(C, T - t0);
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int e = tid + kThreads * it;
             const int row = e % C, c8 = 8 * (e / C);
-            R.q[it] = R.k[it] = R.v[it] = make_uint4(0, 0, 0, 0);
+            rq[it] = rk[it] = rv[it] = make_uint4(0, 0, 0, 0);
             if (row < len) {
                 const size_t gi = head + static_cast<size_t>(t0 + row) * D + c8;
-                if (OUT) R.q[it] = *reinterpret_cast<const uint4*>(q + gi);
-                R.k[it] = *reinterpret_cast<const uint4*>(k + gi);
-                R.v[it] = *reinterpret_cast<const uint4*>(v + gi);
+                if (OUT) rq[it] = *reinterpret_cast<const uint4*>(q + gi);
+                rk[it] = *reinterpret_cast<const uint4*>(k + gi);
+                rv[it] = *reinterpret_cast<const uint4*>(v + gi);
             }
         }
-        R.a = 1.f;
-        if (GATED) R.a = lane < len ? alpha[static_cast<size_t>(bh) * T + t0 + lane] : 1.f;
+        if (GATED) ra = lane < len ? alpha[static_cast<size_t>(bh) * T + t0 + lane] : 1.f;
     };
+    fetch(n0);
 
-    auto body = [&](Raw& R, int n) {
+    for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
         const int len = min(C, T - t0);
         lds_barrier();  // the previous block's LDS tiles are no longer read
@@ -180,7 +174,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // e^{g_c - g} scales K^T for the state update
         float ek = 1.f, egc = 1.f;
         if constexpr (GATED) {
-            const float gx = wave_prefix_sum(__logf(R.a));
+            const float gx = wave_prefix_sum(__logf(ra));
             const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gx), C - 1));
             ek = __expf(gl - gx);
             egc = __expf(gl);
@@ -198,8 +192,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const int e = tid + kThreads * it;
             const int row = e % C, c8 = 8 * (e / C);
             const bool real = row < len;
-            const uint32_t wq[4] = {R.q[it].x, R.q[it].y, R.q[it].z, R.q[it].w};
-            const uint32_t wk[4] = {R.k[it].x, R.k[it].y, R.k[it].z, R.k[it].w};
+            const uint32_t wq[4] = {rq[it].x, rq[it].y, rq[it].z, rq[it].w};
+            const uint32_t wk[4] = {rk[it].x, rk[it].y, rk[it].z, rk[it].w};
             float xq[8], xk[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -217,13 +211,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const bf16x8 pk = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
             if (OUT) *reinterpret_cast<bf16x8*>(&fQ[row][c8]) = pq;
             *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
-            *reinterpret_cast<uint4*>(&Vs[row][c8]) = R.v[it];
+            *reinterpret_cast<uint4*>(&Vs[row][c8]) = rv[it];
         }
-        if (OUT) {
-            if (n + 1 < n1) fetch(R, n + 1);
-        } else {
-            fetch(R, min(n + 2, n1 - 1));
-        }
+        if (n + 1 < n1) fetch(n + 1);
         lds_barrier();
 
         // ---- A = tril(phi(Q) phi(K)^T), row tile w, and its row sums (fp32)
@@ -373,20 +363,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 P[1][t] = mfma16x16x32(a, Ve[1][s2], P[1][t]);
             }
         }
-    };
-    Raw A;
-    fetch(A, n0);
-    if constexpr (OUT) {
-        for (int n = n0; n < n1; ++n) body(A, n);
-    } else {
-        Raw B;
-        fetch(B, min(n0 + 1, n1 - 1));
-        int n = n0;
-        for (; n + 2 <= n1; n += 2) {
-            body(A, n);
-            body(B, n + 1);
-        }
-        if (n < n1) body(A, n);
     }
 
     // OUT: final state of the last segment; otherwise the segment's contributions
