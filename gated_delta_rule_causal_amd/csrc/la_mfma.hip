@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     if (tid < D) zs[tid] = zin ? zin[tid] : 0.f;
 
-    // ---- raw chunk prefetch: item e = tid + kThreads * it -> row = e % C, c8 = 8 (e / C)
+    // ---- raw chunk prefetch: item e = tid + kThreads * it -> row = e / 16, c8 = 8 (e % 16):
+    //      16 lanes read one 256-byte row, so a wave-wide load is 1 KiB contiguous
     uint4 rq[kItems], rk[kItems], rv[kItems];
     float ra = 1.f;   // GATED: alpha of token `lane` of the chunk (1 past the end)
     float decay = 1.f;  // GATED: product of the gates seen so far in this segment
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int e = tid + kThreads * it;
-            const int row = e % C, c8 = 8 * (e / C);
+            const int row = e >> 4, c8 = 8 * (e & 15);
             rq[it] = rk[it] = rv[it] = make_uint4(0, 0, 0, 0);
             if (row < len) {
                 const size_t gi = head + static_cast<size_t>(t0 + row) * D + c8;
@@ -170,8 +171,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int t0 = n * C;
         const int len = min(C, T - t0);
         lds_barrier();  // the previous block's LDS tiles are no longer read
-        // GATED: g for token `lane` (every item of this thread has row = lane),
-        // e^{g_c - g} scales K^T for the state update
+        // GATED: g for token `lane` (alpha of token `lane` is in ra); e^{g_c - g}
+        // scales the rows of V for the state update
         float ek = 1.f, egc = 1.f;
         if constexpr (GATED) {
             const float gx = wave_prefix_sum(__logf(ra));
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int e = tid + kThreads * it;
-            const int row = e % C, c8 = 8 * (e / C);
+            const int row = e >> 4, c8 = 8 * (e & 15);
             const bool real = row < len;
             const uint32_t wq[4] = {rq[it].x, rq[it].y, rq[it].z, rq[it].w};
             const uint32_t wk[4] = {rk[it].x, rk[it].y, rk[it].z, rk[it].w};
