@@ -31,6 +31,11 @@ __device__ __forceinline__ u16 f32_to_bf16_bits(float x) {
     return __builtin_bit_cast(u16, h);
 }
 
+// Two floats as packed bf16 (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
 // Activation element type tags.
 struct IoF32 {
     using T = float;

@@ -219,48 +219,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
         // ---- A = tril(phi(Q) phi(K)^T), row tile w, and its row sums (fp32)
         if constexpr (OUT) {
-            float rs[4] = {0.f, 0.f, 0.f, 0.f};
+            // A is formed transposed (phi(K) tile times phi(Q) tile) so that the
+            // lane holds 4 consecutive columns of one row: A[16w + r][16ct + 4g ..]
+            // (one 8-byte LDS write per tile, row sums over the 4 g lanes)
+            const int row = 16 * w + r;
+            float rs = 0.f;
             for (int ct = 0; ct < 4; ++ct) {
+                uint2 bits = make_uint2(0, 0);
                 if (ct <= w) {
                     f32x4 acc = zero4();
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        acc = mfma16x16x32(lds8(&fQ[16 * w + r][32 * s + 8 * g]),
-                                           lds8(&fK[16 * ct + r][32 * s + 8 * g]), acc);
+                        acc = mfma16x16x32(lds8(&fK[16 * ct + r][32 * s + 8 * g]),
+                                           lds8(&fQ[16 * w + r][32 * s + 8 * g]), acc);
+                    float a4[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * w + 4 * g + i, col = 16 * ct + r;
-                        const float a = col > row ? 0.f
-                                        : GATED ? acc[i] * __expf(fminf(gs[row] - gs[col], 0.f))
-                                                : acc[i];
-                        As[row][col] = f32_to_bf16_bits(a);
-                        rs[i] += a;
+                        const int col = 16 * ct + 4 * g + i;
+                        a4[i] = col > row ? 0.f
+                                : GATED ? acc[i] * __expf(fminf(gs[row] - gs[col], 0.f))
+                                        : acc[i];
+                        rs += a4[i];
                     }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) As[16 * w + 4 * g + i][16 * ct + r] = 0;
+                    bits = make_uint2(pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3]));
                 }
+                *reinterpret_cast<uint2*>(&As[row][16 * ct + 4 * g]) = bits;
             }
             if (!GATED) {
-                // den = rowsum(A) + phi(Q) z (z of the previous blocks) for this
-                // wave's rows: the 16 lanes of a row group split the channels
+                // den = rowsum(A) + phi(Q) z (z of the previous blocks): the 4
+                // lanes of a row split its columns and the 128 channels
+                rs += __shfl_xor(rs, 16, kWave);
+                rs += __shfl_xor(rs, 32, kWave);
+                float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * w + 4 * g + i;
-                    const float t = group_sum<16>(rs[i]);
-                    const uint4 u = *reinterpret_cast<const uint4*>(&fQ[row][8 * r]);
-                    const float4 za = *reinterpret_cast<const float4*>(&zs[8 * r]);
-                    const float4 zb = *reinterpret_cast<const float4*>(&zs[8 * r + 4]);
-                    float d0 = __uint_as_float(u.x << 16) * za.x, d1 = __uint_as_float(u.x & 0xffff0000u) * za.y;
+                for (int j = 0; j < 4; ++j) {
+                    const int c0 = 32 * g + 8 * j;
+                    const uint4 u = *reinterpret_cast<const uint4*>(&fQ[row][c0]);
+                    const float4 za = *reinterpret_cast<const float4*>(&zs[c0]);
+                    const float4 zb = *reinterpret_cast<const float4*>(&zs[c0 + 4]);
+                    d0 = fmaf(__uint_as_float(u.x << 16), za.x, d0);
+                    d1 = fmaf(__uint_as_float(u.x & 0xffff0000u), za.y, d1);
                     d0 = fmaf(__uint_as_float(u.y << 16), za.z, d0);
                     d1 = fmaf(__uint_as_float(u.y & 0xffff0000u), za.w, d1);
                     d0 = fmaf(__uint_as_float(u.z << 16), zb.x, d0);
                     d1 = fmaf(__uint_as_float(u.z & 0xffff0000u), zb.y, d1);
                     d0 = fmaf(__uint_as_float(u.w << 16), zb.z, d0);
                     d1 = fmaf(__uint_as_float(u.w & 0xffff0000u), zb.w, d1);
-                    const float dot = group_sum<16>(d0 + d1);
-                    if (r == 0) dens[row] = t + dot;
                 }
+                float dot = d0 + d1;
+                dot += __shfl_xor(dot, 16, kWave);
+                dot += __shfl_xor(dot, 32, kWave);
+                if (g == 0) dens[row] = rs + dot;
             }
         }
         if constexpr (OUT) lds_barrier();   // A and den complete
