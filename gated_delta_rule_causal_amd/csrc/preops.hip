@@ -102,44 +102,67 @@ struct Seqs {
     const E* st;
 };
 
-template <int D, bool NORM, class E>
-__device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st, const float* __restrict__ w, int C,
-                                          int cbase, int t0, int len, int T, E* __restrict__ dst, int tid,
-                                          const Seqs<E>& sq) {
-    constexpr int L = D / 8;                                          // lanes per token row
-    constexpr int TPL = kTile * L / kThreads >= 1 ? kTile * L / kThreads : 1;   // tokens per lane
-    constexpr int NL = kTile / TPL * L;                               // lanes in use
+// The window of one part: this lane's channels of the TPL + 3 rows its outputs
+// need, and the kernel weights of those channels.  conv_load issues every load
+// (a row the outputs do not need reads row t0, which exists, so no load sits
+// in a branch); conv_store convolves, normalises and stores.
+template <int D, class E>
+struct Window {
+    static constexpr int L = D / 8;                                          // lanes per token row
+    static constexpr int TPL = kTile * L / kThreads >= 1 ? kTile * L / kThreads : 1;   // tokens per lane
+    static constexpr int NL = kTile / TPL * L;                               // lanes in use
     static_assert(NL <= kThreads && NL % kWave == 0, "lane layout");
-    if (tid >= NL) return;                                            // whole waves
-    const int m = tid % L;
-    const int jb = (tid / L) * TPL;                                   // first token of this lane in the tile
-    const int c0 = cbase + 8 * m;
-    float wv[8][4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float4 a = *reinterpret_cast<const float4*>(w + static_cast<size_t>(c0 + e) * 4);
-        wv[e][0] = a.x; wv[e][1] = a.y; wv[e][2] = a.z; wv[e][3] = a.w;
-    }
-    // Window rows r = 0 .. TPL + 2 hold token t0 + jb - 3 + r.  Every load is
-    // unconditional (a row the outputs do not need reads row t0, which
-    // exists), so that no load waits in a branch of its own.
     Raw<E> raw[TPL + 3];
+    float4 w[8];
+};
+
+template <int D, class E>
+__device__ __forceinline__ void conv_load(Window<D, E>& win, const E* __restrict__ xb, const E* st,
+                                          const float* __restrict__ w, int C, int cbase, int t0, int len, int tid) {
+    using W = Window<D, E>;
+    if (tid >= W::NL) return;                                         // whole waves
+    const int m = tid % W::L;
+    const int jb = (tid / W::L) * W::TPL;                             // first token of this lane in the tile
+    const int c0 = cbase + 8 * m;
 #pragma unroll
-    for (int r = 0; r < TPL + 3; ++r) {
+    for (int e = 0; e < 8; ++e) win.w[e] = *reinterpret_cast<const float4*>(w + static_cast<size_t>(c0 + e) * 4);
+    // window rows r = 0 .. TPL + 2 hold token t0 + jb - 3 + r
+#pragma unroll
+    for (int r = 0; r < W::TPL + 3; ++r) {
         const int ts = t0 + jb - 3 + r;                               // >= -3
         const bool in_tile = jb + r - 3 < len;                        // later rows feed no stored output
         const bool from_state = in_tile && ts < 0 && st != nullptr;
         const int row = in_tile && ts >= 0 ? ts : t0;
         const E* src = from_state ? st + static_cast<size_t>(3 + ts) * C : xb + static_cast<size_t>(row) * C;
-        raw[r].load(src + c0);
+        win.raw[r].load(src + c0);
     }
     // keep the scheduler from unpacking the first rows (and so waiting for
     // them) before every load above has been issued
     __builtin_amdgcn_sched_barrier(0);
-    float xr[TPL + 3][8];
+}
+
+// One part of the tile: the head's D channels starting at channel cbase of
+// the projection, written to dst = the head's rows [T, D].  With NORM every
+// output row is divided by its Euclidean norm (a zero row stays zero).
+// Called by every thread of the workgroup with len > 0 (the xor reductions
+// need whole waves).  PACKED: the packed-batch layout of Seqs.
+template <int D, bool NORM, bool PACKED, class E>
+__device__ __forceinline__ void conv_store(const Window<D, E>& win, const E* st, int C, int cbase, int t0, int len,
+                                           int T, E* __restrict__ dst, int tid, const Seqs<E>& sq) {
+    using W = Window<D, E>;
+    if (tid >= W::NL) return;                                         // whole waves
+    const int m = tid % W::L;
+    const int jb = (tid / W::L) * W::TPL;
+    const int c0 = cbase + 8 * m;
+    float wv[8][4];
 #pragma unroll
-    for (int r = 0; r < TPL + 3; ++r) {
-        raw[r].get(xr[r]);
+    for (int e = 0; e < 8; ++e) {
+        wv[e][0] = win.w[e].x; wv[e][1] = win.w[e].y; wv[e][2] = win.w[e].z; wv[e][3] = win.w[e].w;
+    }
+    float xr[W::TPL + 3][8];
+#pragma unroll
+    for (int r = 0; r < W::TPL + 3; ++r) {
+        win.raw[r].get(xr[r]);
         // before the first token, without a carried state: zeros
         const bool live = t0 + jb - 3 + r >= 0 || st != nullptr;
 #pragma unroll
@@ -147,7 +170,7 @@ __device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st,
     }
     // packed batch: the sequence of this lane's first token (binary search)
     int n = 0;
-    if (sq.cu != nullptr) {
+    if constexpr (PACKED) {
         const int tf = t0 + jb;
         int lo = 0, hi = sq.N;   // the last n with cu[n] <= tf
         while (hi - lo > 1) {
@@ -157,13 +180,13 @@ __device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st,
         n = lo;
     }
 #pragma unroll
-    for (int s = 0; s < TPL; ++s) {
+    for (int s = 0; s < W::TPL; ++s) {
         float tap[4][8];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 8; ++e) tap[i][e] = xr[s + i][e];
-        if (sq.cu != nullptr) {
+        if constexpr (PACKED) {
             const int t = t0 + jb + s;
             while (n + 1 < sq.N && sq.cu[n + 1] <= t) ++n;
             const int d = max(0, t - min(max(sq.cu[n], 0), T));   // position inside its sequence
@@ -195,7 +218,7 @@ __device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st,
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-            ss = group_sum<L>(ss);
+            ss = group_sum<W::L>(ss);
             const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] *= inv;
@@ -205,7 +228,7 @@ __device__ __forceinline__ void conv_part(const E* __restrict__ xb, const E* st,
     }
 }
 
-template <class IO, int DK, int DV>
+template <class IO, int DK, int DV, bool PACKED>
 __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     int T, int H, int tiles, const int* cu, int N, const typename IO::T* __restrict__ x, const float* __restrict__ w,
     const float* __restrict__ a_logit, const float* __restrict__ b_logit, const typename IO::T* st_in,
@@ -226,9 +249,17 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     const int tid = threadIdx.x;
 
     if (len > 0) {   // (T == 0: only the state below)
-        conv_part<DK, true>(xb, st, w, C, h * DK, t0, len, T, q + row0 * DK, tid, sq);
-        conv_part<DK, true>(xb, st, w, C, H * DK + h * DK, t0, len, T, k + row0 * DK, tid, sq);
-        conv_part<DV, false>(xb, st, w, C, 2 * H * DK + h * DV, t0, len, T, v + row0 * DV, tid, sq);
+        // one part after another: loading the next part's window before the
+        // current part's stores needs two windows of registers, and the lower
+        // occupancy that costs was measured slower than the wait it removes
+        Window<DK, E> wq, wk;
+        Window<DV, E> wv;
+        conv_load<DK>(wq, xb, st, w, C, h * DK, t0, len, tid);
+        conv_store<DK, true, PACKED>(wq, st, C, h * DK, t0, len, T, q + row0 * DK, tid, sq);
+        conv_load<DK>(wk, xb, st, w, C, H * DK + h * DK, t0, len, tid);
+        conv_store<DK, true, PACKED>(wk, st, C, H * DK + h * DK, t0, len, T, k + row0 * DK, tid, sq);
+        conv_load<DV>(wv, xb, st, w, C, 2 * H * DK + h * DV, t0, len, tid);
+        conv_store<DV, false, PACKED>(wv, st, C, 2 * H * DK + h * DV, t0, len, T, v + row0 * DV, tid, sq);
         for (int j = tid; j < len; j += kThreads) {
             const size_t li = (static_cast<size_t>(b) * T + t0 + j) * H + h;
             alpha[row0 + t0 + j] = sigmoid(a_logit[li]);
@@ -291,11 +322,13 @@ hipError_t launch_dv(int B, int T, int H, int dv, const int* cu, int N, const vo
                            static_cast<E*>(k), static_cast<E*>(v), alpha, beta);
         return hipGetLastError();
     };
+    const bool packed = cu != nullptr;
     switch (dv) {
-        case 16: return go(gdn_preprocess_kernel<IO, DK, 16>);
-        case 32: return go(gdn_preprocess_kernel<IO, DK, 32>);
-        case 64: return go(gdn_preprocess_kernel<IO, DK, 64>);
-        case 128: return go(gdn_preprocess_kernel<IO, DK, 128>);
+        case 16: return packed ? go(gdn_preprocess_kernel<IO, DK, 16, true>) : go(gdn_preprocess_kernel<IO, DK, 16, false>);
+        case 32: return packed ? go(gdn_preprocess_kernel<IO, DK, 32, true>) : go(gdn_preprocess_kernel<IO, DK, 32, false>);
+        case 64: return packed ? go(gdn_preprocess_kernel<IO, DK, 64, true>) : go(gdn_preprocess_kernel<IO, DK, 64, false>);
+        case 128:
+            return packed ? go(gdn_preprocess_kernel<IO, DK, 128, true>) : go(gdn_preprocess_kernel<IO, DK, 128, false>);
         default: return hipErrorInvalidValue;
     }
 }
