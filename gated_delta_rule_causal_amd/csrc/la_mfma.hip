@@ -155,19 +155,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int it = 0; it < kItems; ++it) {
             const int e = tid + kThreads * it;
             const int row = e >> 4, c8 = 8 * (e & 15);
-            rq[it] = rk[it] = rv[it] = make_uint4(0, 0, 0, 0);
-            if (row < len) {
-                const size_t gi = head + static_cast<size_t>(t0 + row) * D + c8;
+            if constexpr (!GATED) {
+                // every load issued (rows past the end read the last row and
+                // are zeroed when staged): see the peeled first chunk below
+                const size_t gi = head + static_cast<size_t>(t0 + min(row, len - 1)) * D + c8;
                 if (OUT) rq[it] = *reinterpret_cast<const uint4*>(q + gi);
                 rk[it] = *reinterpret_cast<const uint4*>(k + gi);
                 rv[it] = *reinterpret_cast<const uint4*>(v + gi);
+            } else {
+                rq[it] = rk[it] = rv[it] = make_uint4(0, 0, 0, 0);
+                if (row < len) {
+                    const size_t gi = head + static_cast<size_t>(t0 + row) * D + c8;
+                    if (OUT) rq[it] = *reinterpret_cast<const uint4*>(q + gi);
+                    rk[it] = *reinterpret_cast<const uint4*>(k + gi);
+                    rv[it] = *reinterpret_cast<const uint4*>(v + gi);
+                }
             }
         }
         if (GATED) ra = lane < len ? alpha[static_cast<size_t>(bh) * T + t0 + lane] : 1.f;
     };
     fetch(n0);
 
-    for (int n = n0; n < n1; ++n) {
+    // One chunk.  Normalised kind: the first chunk is peeled off the loop, so
+    // every path into the loop ends with the same loads and stores and the
+    // wait for a chunk's loads is a count that leaves the previous chunk's
+    // output stores in flight (with both paths merged at the loop head the
+    // compiler waits for everything).  The gated kind measured slower peeled.
+    auto chunk = [&](int n) {
         const int t0 = n * C;
         const int len = min(C, T - t0);
         lds_barrier();  // the previous block's LDS tiles are no longer read
@@ -212,9 +226,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const bf16x8 pk = pack8(xk[0], xk[1], xk[2], xk[3], xk[4], xk[5], xk[6], xk[7]);
             if (OUT) *reinterpret_cast<bf16x8*>(&fQ[row][c8]) = pq;
             *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
-            *reinterpret_cast<uint4*>(&Vs[row][c8]) = rv[it];
+            *reinterpret_cast<uint4*>(&Vs[row][c8]) = real ? rv[it] : make_uint4(0, 0, 0, 0);
         }
-        if (n + 1 < n1) fetch(n + 1);
+        if constexpr (GATED) {
+            if (n + 1 < n1) fetch(n + 1);
+        } else {
+            fetch(min(n + 1, n1 - 1));
+        }
         lds_barrier();
 
         // ---- A = tril(phi(Q) phi(K)^T), row tile w, and its row sums (fp32)
@@ -348,10 +366,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             wave_fence();
 #pragma unroll
             for (int pass = 0; pass < C * 4 / kWave; ++pass) {
-                const int e = pass * kWave + lane, row = e >> 2, c8 = 8 * (e & 3);
-                if (row < len)
+                const int e = pass * kWave + lane, c8 = 8 * (e & 3);
+                if constexpr (!GATED) {   // every store issued: rows past the end write the last row again
+                    const int row = min(e >> 2, len - 1);
                     *reinterpret_cast<uint4*>(o + head + static_cast<size_t>(t0 + row) * D + 32 * w + c8) =
                         *reinterpret_cast<const uint4*>(&Vs[row][32 * w + c8]);
+                } else if ((e >> 2) < len) {
+                    const int row = e >> 2;
+                    *reinterpret_cast<uint4*>(o + head + static_cast<size_t>(t0 + row) * D + 32 * w + c8) =
+                        *reinterpret_cast<const uint4*>(&Vs[row][32 * w + c8]);
+                }
             }
         }
         if (GATED) {
@@ -373,7 +397,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 P[1][t] = mfma16x16x32(a, Ve[1][s2], P[1][t]);
             }
         }
+    };
+    int nstart = n0;
+    if constexpr (!GATED) {
+        chunk(n0);
+        nstart = n0 + 1;
     }
+    for (int n = nstart; n < n1; ++n) chunk(n);
 
     // OUT: final state of the last segment; otherwise the segment's contributions
     float* Sdst = OUT ? (seg == G - 1 && S_out ? S_out + static_cast<size_t>(bh) * kMat : nullptr)
