@@ -539,21 +539,31 @@ __device__ __forceinline__ void store_state(const f32x4 (&P)[NT][8], float* rows
     }
 }
 
-// The same slice written as plain row-major M[d][j] (j = column of P).
+// Element (row d, column j) of a segment map M in the order the combine's
+// MFMA operands read it: 64-lane blocks of 16 bytes, block (w, mt, ks, h)
+// holding, for lane 16 g + r, M[32 w + 16 mt + r][32 ks + 8 g + 4 h .. +3].
+// Every wave-wide load of the combine is then one contiguous 1 KiB run.
+__device__ __forceinline__ int map_frag(int row, int col) {
+    const int blk = (((row >> 5) * 2 + ((row >> 4) & 1)) * 4 + (col >> 5)) * 2 + ((col >> 2) & 1);
+    const int ln = ((col >> 3) & 3) * 16 + (row & 15);
+    return ((blk * 64 + ln) << 2) + (col & 3);
+}
+
+// The slice of M a map carrier holds, written in that order.
 template <int NT>
-__device__ __forceinline__ void store_state_rowmajor(const f32x4 (&P)[NT][8], float* M, int col0, int lane) {
+__device__ __forceinline__ void store_map_frag(const f32x4 (&P)[NT][8], float* M, int col0, int lane) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) M[static_cast<size_t>(perm_row(t, 4 * g + i)) * D + col0 + 16 * nt + r] = P[nt][t][i];
+            for (int i = 0; i < 4; ++i) M[map_frag(perm_row(t, 4 * g + i), col0 + 16 * nt + r)] = P[nt][t][i];
 }
 
 // ---- workspace: per (head, segment) three 128 x 128 fp32 matrices: the
 // entering state P_s and N_s in the state's row layout ([value channel][d]),
-// and M_s row-major ([d][j]).
+// and M_s in the combine's operand order (map_frag).
 constexpr size_t kMat = static_cast<size_t>(D) * D;
 __device__ __forceinline__ size_t ws_P(size_t slot) { return slot * 3 * kMat; }
 __device__ __forceinline__ size_t ws_N(size_t slot) { return ws_P(slot) + kMat; }
@@ -740,7 +750,7 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
         if (npart)
             store_state<2>(P, ws + ws_N(it.slot0 + it.seg), col0, lane);
         else
-            store_state_rowmajor<2>(P, ws + ws_M(it.slot0 + it.seg), col0, lane);
+            store_map_frag<2>(P, ws + ws_M(it.slot0 + it.seg), col0, lane);
     } else {
         const int u = w - 8;
         // The blocks (0,1) and (2,3) above the diagonal of Tm are read by
@@ -832,9 +842,10 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(Geo geo, c
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const float* mrow = M + static_cast<size_t>(32 * w + 16 * mt + r) * D + 32 * ks + 8 * g;
-                mraw[mt][ks][0] = *reinterpret_cast<const float4*>(mrow);
-                mraw[mt][ks][1] = *reinterpret_cast<const float4*>(mrow + 4);
+                // M[32w + 16mt + r][32ks + 8g ..] in the operand order of map_frag
+                const float* mb = M + static_cast<size_t>((((w * 2 + mt) * 4 + ks) * 2) * 64 + lane) * 4;
+                mraw[mt][ks][0] = *reinterpret_cast<const float4*>(mb);
+                mraw[mt][ks][1] = *reinterpret_cast<const float4*>(mb + 64 * 4);
             }
             nraw[mt] = *reinterpret_cast<const float4*>(ws + ws_N(slot0 + st) + static_cast<size_t>(16 * tile + r) * D +
                                                         32 * w + 16 * mt + 4 * g);
