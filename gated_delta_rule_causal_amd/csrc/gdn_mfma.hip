@@ -32,8 +32,10 @@
 //    the chunk tiles, outputs O, and the final state of the last segment.
 // Per chunk, the state-independent tiles (chunk-local prefix sum of log alpha
 // with a wave scan; K K^T and Q K^T on v_mfma_f32_16x16x32_bf16; the four
-// 16x16 diagonal blocks of I + L inverted by substitution in fp32; the rest of
-// the unit lower-triangular solve as blocked v_mfma_f32_16x16x16_bf16
+// 16x16 diagonal blocks of I + L inverted in registers by the product form
+// (I + N)(I + N^2)(I + N^4)(I + N^8), N = -L_bb nilpotent, on
+// v_mfma_f32_16x16x16_bf16 (the first squaring from split bf16 pairs); the
+// rest of the unit lower-triangular solve as blocked v_mfma_f32_16x16x16_bf16
 // products) never leave LDS.  The state slice of each wave stays in MFMA
 // accumulator registers for the whole segment: an accumulator tile is fed
 // back as the B operand of the next product by permuting the contraction

@@ -52,3 +52,47 @@ def slice_err(x, r, lead=2):
 def report(name, err, tol):
     print(f"[parity] {name}: worst slice rel err {err:.3e} (bar {tol:.0e})", flush=True)
     assert err <= tol, f"{name}: {err:.3e} > {tol:.0e}"
+
+
+def long_head_inputs(seed, h, T, d):
+    """Inputs of head h of a 1 x H x T gated-delta workload, as the device
+    wants them: q, k, v as bf16 bit patterns (uint16), alpha and beta float32.
+    Runs in a worker process (no GPU, no torch)."""
+    import synth
+    q, k, v, a, b = synth.gdn_head(seed, 0, h, T, d, d, "bf16")
+    bits = [np.ascontiguousarray(x).view(np.uint32) >> 16 for x in (q, k, v)]
+    return h, [x.astype(np.uint16) for x in bits], a, b
+
+
+def long_head_check(seed, h, T, d, C, o_gpu, S_gpu):
+    """Oracle check of head h of a 1 x H x T gated-delta workload in a worker
+    process: regenerate the head's inputs, run the fp64 chunked oracle over all
+    T tokens, and return the normwise errors of every output position, of the
+    seeded sample of positions, and of the final state."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+    with threadpool_limits(limits=2):
+        q, k, v, a, b = synth.gdn_head(seed, 0, h, T, d, d, "bf16")
+        o_ref, S_ref = oracle.gdn_chunked(q, k, v, a, b, C)
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    err_all = slice_err(o_gpu[None], o_ref[None], 1)
+    pos = long_sample_positions(seed, h, T, C)
+    err_pos = slice_err(o_gpu[pos][None], o_ref[pos][None], 1)
+    err_S = slice_err(np.asarray(S_gpu, dtype=np.float64)[None], S_ref[None], 1)
+    return h, err_all, err_pos, err_S, len(pos)
+
+
+def long_sample_positions(seed, h, T, C, n=4096, boundaries=32):
+    """A seeded sample of output positions of one head: n uniform positions,
+    the whole first and last chunk, and the first and last row of `boundaries`
+    seeded chunk boundaries."""
+    rng = np.random.default_rng([int(seed), 99, int(h)])
+    nc = (T + C - 1) // C
+    pos = set(rng.integers(0, T, size=n).tolist())
+    pos.update(range(0, min(C, T)))
+    pos.update(range((nc - 1) * C, T))
+    for c in rng.integers(1, nc, size=boundaries).tolist():
+        pos.update((c * C - 1, c * C))
+    return np.array(sorted(p for p in pos if 0 <= p < T), dtype=np.int64)

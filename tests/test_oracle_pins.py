@@ -191,27 +191,35 @@ def pin_delta_example(ns):
 
 
 def pin_memory_capacity(ns):
-    g = golden("memory_capacity.json")
+    """The capacity table of section "Memory capacity: what a fixed state
+    loses": n unit keys and random values stored in a d = 32 state, each key
+    then used as the query.  Columns: softmax attention at temperature 1/20,
+    plain linear attention, the delta rule (beta = 1), and the delta rule on
+    the last four pairs only; each is the mean cosine between what is read
+    back and the value stored.  The generator and its draw order (keys, then
+    values, for each n in turn) are the page's, so the printed 3-decimal
+    values must come back exactly."""
+    from scipy.special import softmax
+
+    table = golden("memory_capacity.json")
     d = 32
-    rng = np.random.default_rng(0)
+    draws = np.random.default_rng(0)
 
-    def cos_rows(x, y):
-        return np.sum(x * y, axis=1) / np.linalg.norm(x, axis=1) / np.linalg.norm(y, axis=1)
+    def mean_cosine(read, stored):
+        dots = np.einsum("nd,nd->n", read, stored)
+        return float(np.mean(dots / (np.linalg.norm(read, axis=1) * np.linalg.norm(stored, axis=1))))
 
-    for n, soft_p, lin_p, delta_p, last_p in g["rows"]:
-        K = rng.normal(size=(n, d))
-        K = K / np.linalg.norm(K, axis=1, keepdims=True)
-        V = rng.normal(size=(n, d))
-        logits = 20.0 * K @ K.T
-        w = np.exp(logits - logits.max(axis=1, keepdims=True))
-        soft = (w / w.sum(axis=1, keepdims=True)) @ V
-        _, S_lin = ns.decayed_recurrent(K, K, V, 1.0)
-        _, S_delta = ns.gdn_recurrent(K, K, V, np.ones(n), np.ones(n))
-        c_delta = cos_rows(K @ S_delta.T, V)
-        got = [cos_rows(soft, V).mean(), cos_rows(K @ S_lin.T, V).mean(), c_delta.mean(),
-               c_delta[-4:].mean()]
-        want = [soft_p, lin_p, delta_p, last_p]
-        assert [round(float(x), g["decimals"]) for x in got] == want, (n, got, want)
+    for n, *printed in table["rows"]:
+        keys = draws.normal(size=(n, d))
+        keys /= np.linalg.norm(keys, axis=1)[:, None]
+        values = draws.normal(size=(n, d))
+        read_softmax = softmax(20.0 * (keys @ keys.T), axis=1) @ values
+        S_plain = ns.decayed_recurrent(keys, keys, values, 1.0)[1]
+        S_delta = ns.gdn_recurrent(keys, keys, values, np.ones(n), np.ones(n))[1]
+        read_delta = keys @ S_delta.T
+        got = [mean_cosine(read_softmax, values), mean_cosine(keys @ S_plain.T, values),
+               mean_cosine(read_delta, values), mean_cosine(read_delta[-4:], values[-4:])]
+        assert [round(x, table["decimals"]) for x in got] == printed, (n, got, printed)
 
 
 def pin_gdn_unit_key_recall(ns):
