@@ -19,6 +19,7 @@ import os
 __all__ = [
     "lin_attn_prefill",
     "gdn_prefill",
+    "gdn_prefill_noalloc",
     "gla_prefill",
     "kda_prefill",
     "gdn_prefill_varlen",
@@ -73,6 +74,8 @@ def _load():
     lib.lin_attn_prefill.restype = I
     lib.gdn_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, Z, P]
     lib.gdn_prefill.restype = I
+    lib.gdn_prefill_noalloc.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P]
+    lib.gdn_prefill_noalloc.restype = I
     lib.gla_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, P, Z, P]
     lib.gla_prefill.restype = I
     lib.kda_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, Z, P]
@@ -225,6 +228,35 @@ def gdn_prefill(q, k, v, alpha, beta, S0=None, form="chunked", chunk=64, out=Non
                              _stream_ptr(stream, q.device))
     if st != 0:
         raise LinAttnError(st, "gdn_prefill")
+    return out, S_out
+
+
+def gdn_prefill_noalloc(q, k, v, alpha, beta, S0=None, form="chunked", chunk=64, out=None, S_out=None,
+                        want_state=True, stream=None):
+    """gdn_prefill with the library's own workspace (the C entry point takes
+    no workspace and allocates nothing; pass `out` and `S_out` to keep this
+    call free of allocations too).  Returns (o, S_out)."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(alpha, "alpha", torch.float32, (B, H, T))
+    _check(beta, "beta", torch.float32, (B, H, T))
+    _check(S0, "S0", torch.float32, (B, H, dv, dk))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (B, H, T, dv))
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _check(S_out, "S_out", torch.float32, (B, H, dv, dk))
+    st = _load().gdn_prefill_noalloc(dt, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(S0), _ptr(out), _ptr(S_out), FORMS[form], chunk,
+                                     _stream_ptr(stream, q.device))
+    if st != 0:
+        raise LinAttnError(st, "gdn_prefill_noalloc")
     return out, S_out
 
 

@@ -201,10 +201,16 @@ la_status lin_attn_prefill(int dtype, int B, int H, int T, int dk, int dv, const
     }
 }
 
-la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
-                      const void* v, const float* alpha, const float* beta, const float* S0, void* o,
-                      float* S_out, int form, int chunk, void* workspace, size_t ws_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill with either the caller's workspace or (own_ws) the library's
+// array, taken only after every argument has been validated.
+la_status gdn_prefill_impl(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta, const float* S0, void* o,
+                           float* S_out, int form, int chunk, void* workspace, size_t ws_bytes, bool own_ws,
+                           void* stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
     if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return LA_ERR_ARG;
     if (!sizes_ok(B, H, T) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
@@ -235,6 +241,11 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
         if (path < 0) return LA_ERR_UNSUPPORTED;
     }
     const size_t need = gdn_prefill_ws(dtype, B, H, T, dk, dv, form, chunk);
+    if (own_ws && need > 0) {
+        if (need > la::gdn_scratch_bytes()) return LA_ERR_WORKSPACE;
+        if (la::gdn_scratch(&workspace) != hipSuccess) return LA_ERR_HIP;
+        ws_bytes = need;
+    }
     if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
     if (need > 0 && (overlaps({workspace, need}, outs[0]) || overlaps({workspace, need}, outs[1]) ||
                      overlaps({workspace, need}, Span{S0, nS})))
@@ -252,6 +263,25 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void
         return from_hip(la::launch_gdn_mfma(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, s));
     return from_hip(la::launch_gdn_chunked_generic(dtype, nh, T, dk, dv, chunk, q, k, v, alpha, beta, S0,
                                                    o, S_out, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, const float* S0, void* o,
+                      float* S_out, int form, int chunk, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    return gdn_prefill_impl(dtype, B, H, T, dk, dv, q, k, v, alpha, beta, S0, o, S_out, form, chunk, workspace,
+                            ws_bytes, false, stream);
+}
+
+la_status gdn_prefill_noalloc(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
+                              const void* v, const float* alpha, const float* beta, const float* S0, void* o,
+                              float* S_out, int form, int chunk, void* stream) {
+    return gdn_prefill_impl(dtype, B, H, T, dk, dv, q, k, v, alpha, beta, S0, o, S_out, form, chunk, nullptr, 0,
+                            true, stream);
 }
 
 la_status gla_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,

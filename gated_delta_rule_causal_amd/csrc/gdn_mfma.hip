@@ -41,6 +41,7 @@
 // back as the B operand of the next product by permuting the contraction
 // index (pack_acc_pair), so no state crosses lanes.  The next chunk's raw
 // q/k/v are loaded into registers while the current chunk computes.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1171,7 +1172,40 @@ hipError_t launch_uniform(int B, int H, int T, const void* q, const void* k, con
                       static_cast<float*>(workspace), prep, scan, stream);
 }
 
+// ---- a workspace held by the library, for callers that cannot allocate.
+// The uniform plan never makes more than kTargetBlocks (head, segment) items,
+// so kScratchBytes (48 MiB) covers every uniform call.  The array is part of
+// the code object: each device the library runs on holds its own copy from
+// the first launch until the process ends.  Host code must not use the
+// array's name as an address (on the host it is only a stand-in); the device
+// address comes from hipGetSymbolAddress, looked up once per device with that
+// device current, and is kept per device.
+constexpr size_t kScratchBytes = static_cast<size_t>(kTargetBlocks) * 3 * kMat * sizeof(float);
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex scratch_mutex;
+void* scratch_ptr[kScratchDevices];
+
 }  // namespace
+
+size_t gdn_scratch_bytes() { return kScratchBytes; }
+
+hipError_t gdn_scratch(void** out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool gdn_mfma_supported(int dtype, int dk, int dv, int chunk) {
     return dtype == kBF16 && dk == D && dv == D && chunk == C;

@@ -71,6 +71,12 @@ hipError_t launch_gdn_mfma_scan(int B, int H, int T, const void* q, const void* 
                                 const float* alpha, const float* beta, const float* S0, void* o,
                                 float* S_out, void* workspace, hipStream_t stream);
 
+// The library's own workspace for the chunked gated-delta path (one array per
+// device, in the code object): its size, and its device address on the
+// current device (looked up once per device).
+size_t gdn_scratch_bytes();
+hipError_t gdn_scratch(void** out);
+
 // Packed batch of N sequences (rows [H][Ttot][d], gates [H][Ttot], states
 // [N][H][d][d], sequence n = tokens cu[n]..cu[n+1] on the device), with state
 // snapshots after every `snap` tokens (a multiple of the chunk; 0 for none)

@@ -9,8 +9,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *    library never allocates, frees or keeps device memory, and keeps no
- *    mutable global state; calls on different streams are independent.
+ *    library never allocates or frees device memory, and keeps no mutable
+ *    global state; calls on different streams are independent.  The one
+ *    exception is gdn_prefill_noalloc, which uses a fixed array in the
+ *    library's own device memory (see there).
  *  - Tensors are dense row-major (C order) with the shapes given, and every
  *    pointer must be 16-byte aligned.
  *  - Activations (q, k, v, o) are float32 (LA_F32) or bfloat16 (LA_BF16), as
@@ -148,6 +150,31 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv,
                       const float* S0, void* o, float* S_out,
                       int form, int chunk,
                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gdn_prefill_noalloc - gdn_prefill with no workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Same operation, arguments, layouts and errors as gdn_prefill (workspace and
+ * ws_bytes omitted).  Where gdn_prefill needs a workspace, this call uses one
+ * array in the library's own device memory instead: 48 MiB per device
+ * (la_workspace_bytes(LA_FN_GDN_PREFILL, ...) never exceeds it for the
+ * supported shapes; a call that would need more returns LA_ERR_WORKSPACE),
+ * held by every device the library runs on until the process ends.  The call
+ * itself allocates nothing and frees nothing.  Every call on one device
+ * shares that array and it keeps the last call's contents (nothing in it is
+ * read before the same call writes it): calls that overlap in time on one
+ * device - on different streams, or from different threads - race and give
+ * wrong results; order them on one stream.  The array's address is looked up
+ * on the first call on each device (with that device current); a failure
+ * there returns LA_ERR_HIP.
+ */
+la_status gdn_prefill_noalloc(int dtype, int B, int H, int T, int dk, int dv,
+                              const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta,
+                              const float* S0, void* o, float* S_out,
+                              int form, int chunk, void* stream);
 
 /*
  * gdn_prefill_prep / gdn_prefill_scan - the two halves of gdn_prefill with

@@ -47,8 +47,10 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gla_prefill", "gdn_prefill_prep", "gdn_prefill_scan",
-                            "gdn_preprocess", "gdn_preprocess_varlen", "kda_prefill", "gdn_prefill_varlen", "lin_attn_decode_step", "la_workspace_bytes", "la_status_str", "la_abi_version"])
+    assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gdn_prefill_noalloc", "gla_prefill",
+                            "gdn_prefill_prep", "gdn_prefill_scan", "gdn_preprocess", "gdn_preprocess_varlen",
+                            "kda_prefill", "gdn_prefill_varlen", "lin_attn_decode_step", "la_workspace_bytes",
+                            "la_status_str", "la_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -123,6 +125,32 @@ def test_gdn_validation(lib):
     assert gdn(lib, o=5) == LA_ERR_ARG  # o on top of alpha
     assert gdn(lib, S0=8, S_out=ctypes.c_void_p(BASE + 8 * GiB + 64)) == LA_ERR_ARG
     assert gdn(lib, B=0) == LA_OK
+
+
+def gdn_noalloc(lib, dtype=BF16, B=2, H=16, T=8192, dk=128, dv=128, q=1, k=2, v=3, a=5, b=6, S0=None, o=4,
+                S_out=None, form=CHUNKED, chunk=64):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    return lib.gdn_prefill_noalloc(dtype, B, H, T, dk, dv, f(q), f(k), f(v), f(a), f(b), f(S0), f(o), f(S_out),
+                                   form, chunk, None)
+
+
+def test_gdn_noalloc_validation(lib):
+    """The allocation-free variant reports argument errors exactly as
+    gdn_prefill does, before it looks up the library's device array (which
+    needs a device): these calls never reach HIP."""
+    assert gdn_noalloc(lib, dtype=2) == LA_ERR_DTYPE
+    assert gdn_noalloc(lib, form=PARALLEL) == LA_ERR_ARG
+    assert gdn_noalloc(lib, dk=8) == LA_ERR_SHAPE
+    assert gdn_noalloc(lib, chunk=0) == LA_ERR_SHAPE
+    assert gdn_noalloc(lib, q=None) == LA_ERR_NULL
+    assert gdn_noalloc(lib, a=None) == LA_ERR_NULL
+    assert gdn_noalloc(lib, a=ctypes.c_void_p(BASE + 5 * GiB + 4)) == LA_ERR_ALIGN
+    assert gdn_noalloc(lib, o=5) == LA_ERR_ARG
+    assert gdn_noalloc(lib, S0=8, S_out=ctypes.c_void_p(BASE + 8 * GiB + 64)) == LA_ERR_ARG
+    assert gdn_noalloc(lib, B=0) == LA_OK
+    # the workspace a uniform call needs never exceeds the library's 48 MiB array
+    for B, H, T in ((1, 1, 1 << 20), (2, 16, 8192), (1, 16, 262144), (4, 64, 4096), (1, 257, 100000)):
+        assert gd.la_workspace_bytes("gdn_prefill", "bf16", B, H, T, 128, 128, "chunked", 64) <= 48 << 20
 
 
 def test_decode_validation(lib):
