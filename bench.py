@@ -1,6 +1,6 @@
 """Benchmark of the gated-delta prefill and decode hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--legs a,b,...]
 
 One timed step is one chunked gated-delta prefill (state-independent pass +
 sequential scan) over the 2 x 16 x 8192 workload (B=2, H=16, T=8192,
@@ -9,10 +9,16 @@ HBM.  `value` is prefill tokens/s (B*T tokens per step).  In the same run,
 each reported beside the headline: the decode workload (256 sequences x 32
 heads, d = 128, fp32 state, 1000 steps) as state HBM GB/s; the normalised and
 the scalar-gated linear-attention prefills; the 1 x 16 x 262144 long-context
-prefill; the fused pre-operations of a
-Gated DeltaNet layer; the KDA decode and prefill (block and recurrent forms); a packed batch of
-16 sequences of mixed lengths with state snapshots; and the fp64 CPU oracle on
-a bounded sample of the prefill workload.  Prints one JSON line.
+prefill; the fused pre-operations of a Gated DeltaNet layer; the KDA decode
+and prefill (block and recurrent forms); a packed batch of 16 sequences of
+mixed lengths with state snapshots; and the fp64 CPU oracle on a bounded
+sample of the prefill workload.  Prints one JSON line.
+
+The headline prefill is timed last, after the other legs: by then the GPU has
+been busy for several hundred milliseconds and its clocks have settled, as in
+a serving process (on a cold GPU the first milliseconds of work run at lower
+clocks).  `--legs` runs a subset (e.g. one leg under a profiler); the legs not
+run are null in the JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 are launched on (torch's current stream, which the binding passes to the C
@@ -23,6 +29,7 @@ last-level cache cannot serve one step's inputs from the previous step.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +50,8 @@ KDA_DECODE = "kda_decode_256x32"
 KDA_PREFILL = "kda_bf16_2x16x8192"
 VARLEN = "gdn_varlen_bf16_16seq_16k"
 LONG = "gdn_bf16_1x16x262144"
+LEGS = ["la", "gla", "preops", "decode", "long", "kda_decode", "kda_prefill", "varlen", "prefill", "copy"]
+
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
 # d = d_k = d_v: bytes = q, k, v, o in bf16 + alpha, beta in fp32; flops as
@@ -56,73 +65,300 @@ def path_flops_per_head_token(d, C):
     return 5 * C * d + C * C / 3 + 6 * d * d
 
 
-# HBM bytes per dispatch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# (scaled by the same counters on a plain copy of known size), stored per
-# kernel with the hash of the source file it was built from; numbers taken on
-# another version of that source are not used.
+# Counter figures measured with rocprofv3 (profile_summary.py writes them),
+# stored per kernel with the hash of the source file it was built from;
+# numbers taken on another version of that source are not used.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_counters.json")
+
+
+def _current(rec):
+    src = os.path.join(ROOT, rec["source"])
+    return hashlib.sha256(open(src, "rb").read()).hexdigest() == rec["source_sha256"]
 
 
 def measured_traffic(kernels):
-    """Summed HBM bytes per launch of `kernels`, or None when any of them has
-    no counters for its current source."""
-    import hashlib
+    """Summed HBM bytes per launch of `kernels` (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE scaled by the same counters on a plain copy), or None when any
+    of them has no counters for its current source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))["kernels"]
-        total = 0.0
-        for k in kernels:
-            src = os.path.join(ROOT, rec[k]["source"])
-            if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec[k]["source_sha256"]:
-                return None
-            total += rec[k]["bytes_per_dispatch"]
-        return total
+        if not all(_current(rec[k]) for k in kernels):
+            return None
+        return sum(rec[k]["bytes_per_dispatch"] for k in kernels)
     except (OSError, KeyError, ValueError):
         return None
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    # the GPU's clocks take several milliseconds of work to settle: 100 untimed
-    # steps (about 16 ms) come before the 200 timed ones
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--la-steps", type=int, default=10, help="timed calls of the linear-attention prefill")
-    ap.add_argument("--long-calls", type=int, default=2,
-                    help="timed calls of the 1 x 16 x 262144 prefill (0 skips that leg, e.g. under a profiler)")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
-              "multi-GPU mode: each GPU would run its own share of heads independently.", file=sys.stderr)
-        sys.exit(2)
+def measured_pmc(kernels):
+    """MFMA and LDS counters of `kernels` (rocprofv3 --pmc MfmaUtil, LdsUtil,
+    LdsBankConflict, MfmaFlopsBF16 per dispatch): the MFMA busy fraction over
+    the kernels weighted by their durations in the same run, the summed BF16
+    MFMA flops, and the per-kernel records.  None when any kernel's source has
+    changed since."""
+    try:
+        rec = json.load(open(PMC_FILE))["kernels"]
+        if not all(_current(rec[k]) for k in kernels):
+            return None
+        t = sum(rec[k]["avg_us"] for k in kernels)
+        busy = sum(rec[k]["MfmaUtil"] / 100.0 * rec[k]["avg_us"] for k in kernels) / t
+        return {"busy_frac": busy, "flops": sum(rec[k]["MfmaFlopsBF16"] for k in kernels),
+                "kernels": {k: {m: rec[k][m] for m in ("MfmaUtil", "LdsUtil", "LdsBankConflict", "avg_us")}
+                            for k in kernels}}
+    except (OSError, KeyError, ValueError, ZeroDivisionError):
+        return None
 
-    import numpy as np
-    import torch
 
-    import gated_delta_rule_causal_amd as gd
+def hbm_roofline(kernel, nbytes, ms, traffic_kernels=None):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(traffic_kernels) if traffic_kernels else None,
+            "bytes_per_launch": nbytes, "avg_launch_ms": ms}
+
+
+class Ctx:
+    """What every leg needs: torch, the binding, the device, the arguments."""
+
+    def __init__(self, args):
+        import torch
+
+        import gated_delta_rule_causal_amd as gd
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        self.torch, self.gd, self.args = torch, gd, args
+        self.dev = torch.device("cuda:0")
+        gd._load()
+
+    def up(self, x, bf16=False):
+        t = self.torch.from_numpy(x).to(self.dev)
+        return t.to(self.torch.bfloat16) if bf16 else t
+
+    def timed(self, calls, fn, warm=2):
+        """Mean event time (ms) of `calls` back-to-back calls fn(i), after
+        `warm` untimed ones."""
+        torch = self.torch
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for i in range(calls):
+            fn(i)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / calls
+
+
+# ------------------------------------------------------------------ legs
+def leg_la(c):
     import synth
+    torch, gd, n = c.torch, c.gd, c.args.la_steps
+    w = synth.WORKLOADS[LA_PREFILL]
+    B, H, T, d, C = w["B"], w["H"], w["T"], w["dk"], w["chunk"]
+    q, k, v = synth.la_batch(w["seed"], B, H, T, d, d, "bf16", w["scale"])
+    sets = [tuple(c.up(x, True) for x in (q, k, v)) for _ in range(3)]
+    del q, k, v
+    out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=c.dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
+    z = torch.empty((B, H, d), dtype=torch.float32, device=c.dev)
+    ms = c.timed(n, lambda i: gd.lin_attn_prefill(*sets[i % 3], form="chunked", chunk=C, out=out, S_out=S, z_out=z))
+    ht = B * H * T
+    roof = hbm_roofline("la_chunked_mfma_kernel (state pass + combine + output pass)", ht * 4 * d * 2, ms,
+                        ["la_chunked_mfma_kernel_state", "la_combine_kernel", "la_chunked_mfma_kernel_out"])
+    roof["achieved_TFLOPs"] = ht * (2 * C * d + 4 * d * d) / (ms * 1e-3) / 1e12
+    return {"workload": "normalised linear attention prefill B=4 H=16 T=4096 d=128 chunk=64, bf16 I/O, fp32 state",
+            "calls": n, "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3), "roofline": roof}
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    gd._load()
 
-    # ------------------------------------------------------------ prefill
+def leg_gla(c):
+    import synth
+    torch, gd, n = c.torch, c.gd, c.args.la_steps
+    w = synth.WORKLOADS[GLA_PREFILL]
+    B, H, T, d, C = w["B"], w["H"], w["T"], w["dk"], w["chunk"]
+    q, k, v, a, _ = synth.gdn_batch(w["seed"], B, H, T, d, d, "bf16")
+    sets = [tuple(c.up(x, True) for x in (q, k, v)) + (c.up(a),) for _ in range(3)]
+    del q, k, v, a
+    out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=c.dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
+    ms = c.timed(n, lambda i: gd.gla_prefill(*sets[i % 3], form="chunked", chunk=C, out=out, S_out=S))
+    nbytes = B * H * T * (4 * d * 2 + 4)   # q, k, v, o bf16 + alpha fp32
+    return {"workload": "scalar-gated linear attention prefill B=2 H=16 T=8192 d=128 chunk=64, bf16 I/O, fp32 state",
+            "calls": n, "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "roofline": hbm_roofline("la_chunked_mfma_kernel, gated (state pass + combine + output pass)", nbytes, ms,
+                                     ["gla_chunked_mfma_kernel_state", "gla_combine_kernel",
+                                      "gla_chunked_mfma_kernel_out"])}
+
+
+def leg_preops(c):
+    import synth
+    torch, gd, n = c.torch, c.gd, c.args.la_steps
+    w = synth.WORKLOADS[PREOPS]
+    B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
+    x, cw, al, bl = synth.preops_batch(w["seed"], B, T, H, dk, dv, "bf16")
+    x0 = c.up(x, True)
+    sets = [(x0 if i == 0 else x0.clone(), c.up(cw), c.up(al), c.up(bl)) for i in range(3)]
+    del x, cw, al, bl, x0
+    outs = dict(q=torch.empty((B, H, T, dk), dtype=torch.bfloat16, device=c.dev),
+                k=torch.empty((B, H, T, dk), dtype=torch.bfloat16, device=c.dev),
+                v=torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=c.dev),
+                alpha=torch.empty((B, H, T), dtype=torch.float32, device=c.dev),
+                beta=torch.empty((B, H, T), dtype=torch.float32, device=c.dev))
+    ms = c.timed(n, lambda i: gd.gdn_preprocess(*sets[i % 3], H, dk, dv, want_state=False, **outs))
+    # x read + gate logits read, q, k, v written + alpha, beta written
+    nbytes = B * H * T * (2 * ((2 * dk + dv) * 2 + 8))
+    return {"workload": "Gated DeltaNet pre-operations (conv k=4, q/k L2 norm, sigmoid gates) B=2 H=16 T=8192 d=128, "
+                        "bf16 I/O", "calls": n, "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "roofline": hbm_roofline("gdn_preprocess_kernel", nbytes, ms, ["gdn_preprocess_kernel"])}
+
+
+def _decode(c, kind, wname, inputs, traffic_key):
+    import synth
+    torch, gd = c.torch, c.gd
+    w = synth.WORKLOADS[wname]
+    N, H, d, steps = w["N"], w["H"], w["dk"], c.args.decode_steps
+    S = c.up(synth.decode_state_fast(w["seed"], N, H, d, d, w["state_std"]))
+    pool = []
+    for e in range(8):
+        tq, tk, tv, ta, tb = inputs(w["seed"], N, H, d, d, "bf16", e)
+        pool.append(tuple(c.up(x, True) for x in (tq, tk, tv)) + tuple(c.up(x) for x in (ta, tb)))
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device=c.dev)
+
+    def call(i):
+        tq, tk, tv, ta, tb = pool[i % 8]
+        gd.lin_attn_decode_step(kind, tq, tk, tv, S, alpha=ta, beta=tb, out=o)
+
+    t0 = time.perf_counter()
+    ms = c.timed(steps, call, warm=5)
+    wall = time.perf_counter() - t0
+    state_bytes = 2 * N * H * d * d * 4
+    a_bytes = d * 4 if kind == "kda" else 4
+    io_bytes = N * H * (4 * d * 2 + a_bytes + 4)   # q, k, v, o bf16; alpha, beta fp32
+    rec = {"steps": steps, "ms_per_step": ms, "steps_per_s": 1e3 / ms, "wall_steps_per_s": steps / wall,
+           "state_GBps": state_bytes / (ms * 1e-3) / 1e9, "total_GBps": (state_bytes + io_bytes) / (ms * 1e-3) / 1e9,
+           "roofline": hbm_roofline(f"recurrent_kernel ({kind} decode)", state_bytes + io_bytes, ms, [traffic_key])}
+    del S, pool
+    return rec
+
+
+def leg_decode(c):
+    import synth
+    r = _decode(c, "gated_delta", DECODE, synth.decode_token_inputs, "recurrent_kernel_gated_delta_decode")
+    return dict(workload="gated delta decode 256 seq x 32 heads, d=128, fp32 state, bf16 token I/O", **r)
+
+
+def leg_kda_decode(c):
+    import synth
+    r = _decode(c, "kda", KDA_DECODE, synth.kda_decode_token_inputs, "recurrent_kernel_kda_decode")
+    return dict(workload="KDA decode 256 seq x 32 heads, d=128, per-channel decay, fp32 state, bf16 token I/O", **r)
+
+
+def leg_long(c):
+    # Inputs drawn on the device (torch's seeded generator, the distributions
+    # of the synthetic recipe): 3 GiB of bf16 activations would take minutes
+    # to draw on the host.  Values do not change the work; the parity tests
+    # check this shape against the oracle on the host-drawn inputs.
+    import synth
+    torch, gd, n = c.torch, c.gd, c.args.long_calls
+    w = synth.WORKLOADS[LONG]
+    B, H, T, d = w["B"], w["H"], w["T"], w["dk"]
+    g = torch.Generator(device=c.dev)
+    g.manual_seed(w["seed"])
+    norm = torch.nn.functional.normalize
+    q = norm(torch.randn(B, H, T, d, device=c.dev, generator=g), dim=-1).to(torch.bfloat16)
+    k = norm(torch.randn(B, H, T, d, device=c.dev, generator=g), dim=-1).to(torch.bfloat16)
+    v = torch.randn(B, H, T, d, device=c.dev, generator=g).to(torch.bfloat16)
+    a = torch.sigmoid(torch.randn(B, H, T, device=c.dev, generator=g) + 3.0)
+    b = torch.sigmoid(torch.randn(B, H, T, device=c.dev, generator=g))
+    ws = gd.gdn_workspace(q, v, 64)
+    out = torch.empty_like(v)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
+    ms = c.timed(n, lambda i: gd.gdn_prefill(q, k, v, a, b, form="chunked", chunk=64, out=out, S_out=S, workspace=ws),
+                 warm=1)
+    nbytes = B * H * T * path_bytes_per_head_token(d)
+    return {"workload": "gated delta prefill B=1 H=16 T=262144 d=128 chunk=64, bf16 I/O, fp32 state (inputs drawn "
+                        "on the device)", "calls": n, "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "roofline": hbm_roofline("gdn_prefill (map + combine + out)", nbytes, ms)}
+
+
+def leg_kda_prefill(c):
+    import synth
+    torch, gd, n = c.torch, c.gd, c.args.la_steps
+    w = synth.WORKLOADS[KDA_PREFILL]
+    B, H, T, d = w["B"], w["H"], w["T"], w["dk"]
+    q, k, v, a, b = synth.kda_batch(w["seed"], B, H, T, d, d, "bf16")
+    sets = [tuple(c.up(x, True) for x in (q, k, v)) + tuple(c.up(x) for x in (a, b)) for _ in range(2)]
+    del q, k, v, a, b
+    ws = torch.empty(gd.la_workspace_bytes("kda_prefill", "bf16", B, H, T, d, d, "chunked", 64), dtype=torch.uint8,
+                     device=c.dev)
+    out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=c.dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
+
+    def call(i, form="chunked"):
+        gd.kda_prefill(*sets[i % 2], form=form, out=out, S_out=S, workspace=ws)
+
+    ms = c.timed(n, call)
+    rec_ms = c.timed(1, lambda i: call(i, "recurrent"), warm=0)
+    # q, k, v, o in bf16, per-channel alpha and beta in fp32
+    nbytes = B * H * T * (4 * d * 2 + d * 4 + 4)
+    return {"workload": "KDA prefill B=2 H=16 T=8192 d=128 chunk=64 (block form: tile pass + column-parallel scan), "
+                        "bf16 I/O, fp32 state", "calls": n, "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "recurrent_form_ms": rec_ms,
+            "roofline": hbm_roofline("kda_tile_kernel + kda_scan_kernel", nbytes, ms,
+                                     ["kda_tile_kernel", "kda_scan_kernel"])}
+
+
+def leg_varlen(c):
+    import synth
+    torch, gd, n = c.torch, c.gd, c.args.la_steps
+    w = synth.WORKLOADS[VARLEN]
+    H, d, snap, N, Tt = w["H"], w["dk"], w["snap"], w["N"], w["T_total"]
+    lens = synth.varlen_lengths(w["seed"], N, Tt)
+    q, k, v, a, b, cu = synth.varlen_batch(w["seed"], lens, H, d, d, "bf16")
+    sets = [tuple(c.up(x, True) for x in (q, k, v)) + tuple(c.up(x) for x in (a, b)) for _ in range(3)]
+    cu_t = c.up(cu)
+    del q, k, v, a, b
+    nsnap = int(sum(int(L) // snap for L in lens))
+    out = torch.empty((H, Tt, d), dtype=torch.bfloat16, device=c.dev)
+    S = torch.empty((N, H, d, d), dtype=torch.float32, device=c.dev)
+    S_snap = torch.empty((nsnap, H, d, d), dtype=torch.float32, device=c.dev)
+    ws = torch.empty(gd.la_workspace_bytes("gdn_prefill_varlen", "bf16", N, H, Tt, d, d), dtype=torch.uint8,
+                     device=c.dev)
+    ms = c.timed(n, lambda i: gd.gdn_prefill_varlen(*sets[i % 3], cu_t, snap_interval=snap, snap_count=nsnap, out=out,
+                                                     S_out=S, S_snap=S_snap, workspace=ws))
+    nbytes = H * Tt * path_bytes_per_head_token(d) + (nsnap + N) * H * d * d * 4
+    return {"workload": f"gated delta prefill, packed batch of {N} sequences ({Tt} tokens, lengths "
+                        f"{int(min(lens))}..{int(max(lens))}), H=16 d=128 chunk=64, snapshots every {snap} tokens "
+                        f"({nsnap})", "calls": n, "ms_per_call": ms, "tokens_per_s": Tt / (ms * 1e-3),
+            "roofline": hbm_roofline("gdn_prefill_varlen (plan + map + combine + out)", nbytes, ms)}
+
+
+def leg_copy(c):
+    # a plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
+    # WRITE_SIZE give the factor that turns those counters into bytes
+    torch = c.torch
+    src = torch.empty(64 << 20, dtype=torch.float32, device=c.dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes": src.numel() * 4}
+
+
+def leg_prefill(c):
+    """The headline: W untimed steps, then exactly K timed steps between two
+    synchronisations; events around the two launches of every fourth step."""
+    import numpy as np
+
+    import synth
+    torch, gd, args = c.torch, c.gd, c.args
     w = synth.WORKLOADS[PREFILL]
     B, H, T, d, C = w["B"], w["H"], w["T"], w["dk"], w["chunk"]
     q, k, v, a, b = synth.gdn_batch(w["seed"], B, H, T, d, d, "bf16")
-    sets = []
-    for _ in range(3):
-        sets.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v)) +
-                    tuple(torch.from_numpy(x).to(dev) for x in (a, b)))
+    sets = [tuple(c.up(x, True) for x in (q, k, v)) + tuple(c.up(x) for x in (a, b)) for _ in range(3)]
     del q, k, v, a, b
     ws = gd.gdn_workspace(sets[0][0], sets[0][2], C)
-    out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
-    S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=c.dev)
+    S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
 
     def step(i, ev=None):
         tq, tk, tv, ta, tb = sets[i % 3]
@@ -138,10 +374,8 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # Per-kernel durations come from events recorded around the two launches of
-    # every fourth step of the timed run (an event record costs a few
-    # microseconds of GPU time, so recording them on every step would inflate
-    # the step time that `value` reports).
+    # an event record costs a few microseconds of GPU time, so only every
+    # fourth timed step carries events
     sampled = set(range(min(1, args.steps - 1), args.steps, 4))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
@@ -152,396 +386,152 @@ def main():
     elapsed = time.perf_counter() - t0
     prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
     scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs.values()]))
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = B * T * args.steps / elapsed
     head_tokens = B * H * T
     # segments per head, from the workspace size (3 fp32 d x d matrices per head-segment)
-    mat = d * d * 4
-    G = max(1, ws.numel() // (B * H * 3 * mat)) if ws.numel() > 16 else 1
-    # compulsory bytes of each call in this design (inputs read once, outputs written once):
-    #   prep  = segment maps: k, v, alpha, beta of the first G-1 segments; (M, N) per head-segment
-    #   scan  = combine (maps + entering states) + outputs: q, k, v, alpha, beta, o, entering
-    #           states, final state
-    # roofline of the dominant launch: algorithmic bytes = the path's minimal
-    # I/O per head-token (q, k, v, o in bf16, alpha, beta in fp32) times the
-    # head-tokens one launch processes (all of them, for either launch)
+    G = max(1, ws.numel() // (B * H * 3 * d * d * 4)) if ws is not None and ws.numel() > 16 else 1
+    # Roofline of the whole step (every kernel of the path: gdn_map_kernel,
+    # gdn_combine_kernel, gdn_out_kernel): algorithmic bytes = the path's
+    # minimal I/O per head-token (q, k, v, o in bf16, alpha, beta in fp32)
+    # times the head-tokens of the step, over the summed event time of its two
+    # launches.  The counter figures (HBM bytes, MFMA busy) come from rocprofv3
+    # runs stored under profiles/ and are null once the source has changed.
+    step_kernels = ["gdn_map_kernel", "gdn_combine_kernel", "gdn_out_kernel"]
+    step_ms = prep_ms + scan_ms
     alg_bytes = head_tokens * path_bytes_per_head_token(d)
-    kern = {"gdn_prefill_prep (gdn_map_kernel)": (prep_ms, ["gdn_map_kernel"]),
-            "gdn_prefill_scan (gdn_combine_kernel + gdn_out_kernel)": (scan_ms,
-                                                                       ["gdn_combine_kernel", "gdn_out_kernel"])}
-    dom = max(kern, key=lambda n: kern[n][0])
-    dom_ms, dom_kernels = kern[dom]
-    dom_gbps = alg_bytes / (dom_ms * 1e-3) / 1e9
-    dom_traffic = measured_traffic(dom_kernels)
-    path_gbps = head_tokens * path_bytes_per_head_token(d) / ((prep_ms + scan_ms) * 1e-3) / 1e9
-    path_tflops = head_tokens * path_flops_per_head_token(d, C) / ((prep_ms + scan_ms) * 1e-3) / 1e12
+    alg_flops = head_tokens * path_flops_per_head_token(d, C)
+    tflops = alg_flops / (step_ms * 1e-3) / 1e12
+    pmc = measured_pmc(step_kernels)
+    roof = hbm_roofline("gdn_prefill step (gdn_map_kernel + gdn_combine_kernel + gdn_out_kernel)", alg_bytes,
+                        step_ms, step_kernels)
+    roof["launches_ms"] = {"gdn_prefill_prep": prep_ms, "gdn_prefill_scan": scan_ms}
+    roof["segments_per_head"] = G
+    return {"elapsed": elapsed, "ms_per_step": elapsed * 1e3 / args.steps,
+            "tokens_per_s": B * T * args.steps / elapsed, "roofline": roof,
+            "mfma": {"algorithmic_flops_per_step": alg_flops, "achieved_TFLOPs": tflops,
+                     "peak_TFLOPs": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
+                     "counter_busy_frac": None if pmc is None else pmc["busy_frac"],
+                     "counter_flops_per_step": None if pmc is None else pmc["flops"],
+                     "counter_kernels": None if pmc is None else pmc["kernels"]}}
 
-    if args.copy_probe:
-        # a plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
-        # WRITE_SIZE give the factor that turns those counters into bytes
-        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
-    # ------------------------------------------- linear-attention prefill
-    wl = synth.WORKLOADS[LA_PREFILL]
-    Bl, Hl, Tl, dl, Cl = wl["B"], wl["H"], wl["T"], wl["dk"], wl["chunk"]
-    lq, lk, lv = synth.la_batch(wl["seed"], Bl, Hl, Tl, dl, dl, "bf16", wl["scale"])
-    la_sets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (lq, lk, lv)) for _ in range(3)]
-    del lq, lk, lv
-    la_out = torch.empty((Bl, Hl, Tl, dl), dtype=torch.bfloat16, device=dev)
-    la_S = torch.empty((Bl, Hl, dl, dl), dtype=torch.float32, device=dev)
-    la_z = torch.empty((Bl, Hl, dl), dtype=torch.float32, device=dev)
-    for i in range(2):
-        gd.lin_attn_prefill(*la_sets[i % 3], form="chunked", chunk=Cl, out=la_out, S_out=la_S, z_out=la_z)
-    torch.cuda.synchronize()
-    # the calls of each leg below run back to back between two events
-    la_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    la_ev[0].record()
-    for i in range(args.la_steps):
-        gd.lin_attn_prefill(*la_sets[i % 3], form="chunked", chunk=Cl, out=la_out, S_out=la_S, z_out=la_z)
-    la_ev[1].record()
-    torch.cuda.synchronize()
-    la_ms = la_ev[0].elapsed_time(la_ev[1]) / args.la_steps
-    la_head_tokens = Bl * Hl * Tl
-    la_bytes = la_head_tokens * 4 * dl * 2           # q, k, v, o in bf16
-    la_flops = la_head_tokens * (2 * Cl * dl + 4 * dl * dl)
-    la_gbps = la_bytes / (la_ms * 1e-3) / 1e9
-    del la_sets
+# ------------------------------------------------------ CPU oracle baseline
+def _oracle_worker(job):
+    """One host process of the CPU baseline: the fp64 chunked oracle, BLAS held
+    to one thread, over heads of the prefill workload (cycling from `first`)
+    until `budget` seconds of oracle time have passed.  Input drawing is not
+    timed."""
+    seed, heads, first, T, d, C, budget = job
+    from threadpoolctl import threadpool_limits
 
-    # --------------------------------- scalar-gated linear-attention prefill
-    wg = synth.WORKLOADS[GLA_PREFILL]
-    gq, gk, gv, ga, _ = synth.gdn_batch(wg["seed"], wg["B"], wg["H"], wg["T"], wg["dk"], wg["dv"], "bf16")
-    gla_sets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (gq, gk, gv)) +
-                (torch.from_numpy(ga).to(dev),) for _ in range(3)]
-    del gq, gk, gv, ga
-    gla_out = torch.empty((wg["B"], wg["H"], wg["T"], wg["dv"]), dtype=torch.bfloat16, device=dev)
-    gla_S = torch.empty((wg["B"], wg["H"], wg["dv"], wg["dk"]), dtype=torch.float32, device=dev)
-    for i in range(2):
-        gd.gla_prefill(*gla_sets[i % 3], form="chunked", chunk=wg["chunk"], out=gla_out, S_out=gla_S)
-    torch.cuda.synchronize()
-    g_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    g_ev[0].record()
-    for i in range(args.la_steps):
-        gd.gla_prefill(*gla_sets[i % 3], form="chunked", chunk=wg["chunk"], out=gla_out, S_out=gla_S)
-    g_ev[1].record()
-    torch.cuda.synchronize()
-    gla_ms = g_ev[0].elapsed_time(g_ev[1]) / args.la_steps
-    gla_bytes = wg["B"] * wg["H"] * wg["T"] * (4 * wg["dk"] * 2 + 4)   # q, k, v, o bf16 + alpha fp32
-    gla_gbps = gla_bytes / (gla_ms * 1e-3) / 1e9
-    del gla_sets
+    import oracle
+    import synth
+    done, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        while spent < budget:
+            bb, hh = heads[(first + done) % len(heads)]
+            q, k, v, a, b = synth.gdn_head(seed, bb, hh, T, d, d, "bf16")
+            ts = time.perf_counter()
+            oracle.gdn_chunked(q, k, v, a, b, C)
+            spent += time.perf_counter() - ts
+            done += 1
+    return done, spent
 
-    # --------------------------------------- pre-operations of the layer
-    wp = synth.WORKLOADS[PREOPS]
-    Bp, Tp, Hp, dkp, dvp = wp["B"], wp["T"], wp["H"], wp["dk"], wp["dv"]
-    px, pw, pa, pb = synth.preops_batch(wp["seed"], Bp, Tp, Hp, dkp, dvp, "bf16")
-    x0 = torch.from_numpy(px).to(dev).to(torch.bfloat16)
-    pre_sets = [(x0 if i == 0 else x0.clone(), torch.from_numpy(pw).to(dev), torch.from_numpy(pa).to(dev),
-                 torch.from_numpy(pb).to(dev)) for i in range(3)]
-    del px, pw, pa, pb, x0
-    pre_out = dict(q=torch.empty((Bp, Hp, Tp, dkp), dtype=torch.bfloat16, device=dev),
-                   k=torch.empty((Bp, Hp, Tp, dkp), dtype=torch.bfloat16, device=dev),
-                   v=torch.empty((Bp, Hp, Tp, dvp), dtype=torch.bfloat16, device=dev),
-                   alpha=torch.empty((Bp, Hp, Tp), dtype=torch.float32, device=dev),
-                   beta=torch.empty((Bp, Hp, Tp), dtype=torch.float32, device=dev))
-    for i in range(2):
-        gd.gdn_preprocess(*pre_sets[i % 3], Hp, dkp, dvp, want_state=False, **pre_out)
-    torch.cuda.synchronize()
-    p_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    p_ev[0].record()
-    for i in range(args.la_steps):
-        gd.gdn_preprocess(*pre_sets[i % 3], Hp, dkp, dvp, want_state=False, **pre_out)
-    p_ev[1].record()
-    torch.cuda.synchronize()
-    pre_ms = p_ev[0].elapsed_time(p_ev[1]) / args.la_steps
-    # x read + gate logits read, q, k, v written + alpha, beta written
-    pre_bytes = Bp * Hp * Tp * (2 * ((2 * dkp + dvp) * 2 + 8))
-    pre_gbps = pre_bytes / (pre_ms * 1e-3) / 1e9
-    del pre_sets, pre_out
 
-    # ------------------------------------------------------------- decode
-    wd = synth.WORKLOADS[DECODE]
-    N, Hd, dd, steps = wd["N"], wd["H"], wd["dk"], args.decode_steps
-    S = torch.from_numpy(synth.decode_state_fast(wd["seed"], N, Hd, dd, dd, wd["state_std"])).to(dev)
-    pool = []
-    for e in range(8):
-        tq, tk, tv, ta, tb = synth.decode_token_inputs(wd["seed"], N, Hd, dd, dd, "bf16", e)
-        pool.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (tq, tk, tv)) +
-                    tuple(torch.from_numpy(x).to(dev) for x in (ta, tb)))
-    o_dec = torch.empty((N, Hd, dd), dtype=torch.bfloat16, device=dev)
-    for i in range(5):
-        tq, tk, tv, ta, tb = pool[i % 8]
-        gd.lin_attn_decode_step("gated_delta", tq, tk, tv, S, alpha=ta, beta=tb, out=o_dec)
-    torch.cuda.synchronize()
-    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    t0 = time.perf_counter()
-    dev_ev[0].record()
-    for i in range(steps):
-        tq, tk, tv, ta, tb = pool[i % 8]
-        gd.lin_attn_decode_step("gated_delta", tq, tk, tv, S, alpha=ta, beta=tb, out=o_dec)
-    dev_ev[1].record()
-    torch.cuda.synchronize()
-    dec_elapsed = time.perf_counter() - t0
-    dec_ms = dev_ev[0].elapsed_time(dev_ev[1]) / steps
-    state_bytes = 2 * N * Hd * dd * dd * 4
-    io_bytes = N * Hd * (3 * dd * 2 + dd * 2 + 8)
-    dec_state_gbps = state_bytes / (dec_ms * 1e-3) / 1e9
-    dec_total_gbps = (state_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
+def cpu_baseline(w, seconds):
+    """The fp64 oracle (chunked form) on the host's cores: one process per core
+    (at most 16, the CPU share of one GPU), each with single-threaded BLAS and
+    its own heads of the prefill workload, together spending about `seconds`
+    of oracle time.  The rate is the sum of the processes' rates while all of
+    them run."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
 
-    # ------------------------------------ long-context prefill (1 x 16 x 262144)
-    # Inputs drawn on the device (torch's seeded generator, the distributions
-    # of the synthetic recipe): 3 GiB of bf16 activations would take minutes to
-    # draw on the host.  Values do not change the work; the parity tests check
-    # this shape against the oracle on the host-drawn inputs.
-    long_ms = long_gbps = None
-    wl5 = synth.WORKLOADS[LONG]
-    B5, H5, T5, d5 = wl5["B"], wl5["H"], wl5["T"], wl5["dk"]
-    if args.long_calls > 0:
-        g5 = torch.Generator(device=dev)
-        g5.manual_seed(wl5["seed"])
-        norm = torch.nn.functional.normalize
-        l_q = norm(torch.randn(B5, H5, T5, d5, device=dev, generator=g5), dim=-1).to(torch.bfloat16)
-        l_k = norm(torch.randn(B5, H5, T5, d5, device=dev, generator=g5), dim=-1).to(torch.bfloat16)
-        l_v = torch.randn(B5, H5, T5, d5, device=dev, generator=g5).to(torch.bfloat16)
-        l_a = torch.sigmoid(torch.randn(B5, H5, T5, device=dev, generator=g5) + 3.0)
-        l_b = torch.sigmoid(torch.randn(B5, H5, T5, device=dev, generator=g5))
-        l_ws = gd.gdn_workspace(l_q, l_v, 64)
-        l_out = torch.empty_like(l_v)
-        l_S = torch.empty((B5, H5, d5, d5), dtype=torch.float32, device=dev)
-        gd.gdn_prefill(l_q, l_k, l_v, l_a, l_b, form="chunked", chunk=64, out=l_out, S_out=l_S, workspace=l_ws)
-        torch.cuda.synchronize()
-        lev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        lev[0].record()
-        for i in range(args.long_calls):
-            gd.gdn_prefill(l_q, l_k, l_v, l_a, l_b, form="chunked", chunk=64, out=l_out, S_out=l_S, workspace=l_ws)
-        lev[1].record()
-        torch.cuda.synchronize()
-        long_ms = lev[0].elapsed_time(lev[1]) / args.long_calls
-        long_gbps = B5 * H5 * T5 * path_bytes_per_head_token(d5) / (long_ms * 1e-3) / 1e9
-        del l_q, l_k, l_v, l_a, l_b, l_ws, l_out, l_S
+    B, H, T, d, C = w["B"], w["H"], w["T"], w["dk"], w["chunk"]
+    host_cpus = len(os.sched_getaffinity(0))
+    n = max(1, min(host_cpus, 16))
+    heads = [(bb, hh) for bb in range(B) for hh in range(H)]
+    jobs = [(w["seed"], heads, j, T, d, C, seconds / n) for j in range(n)]
+    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_worker, jobs))
+    done = sum(r[0] for r in res)
+    spent = sum(r[1] for r in res)
+    head_tokens_per_s = sum(r[0] * T / r[1] for r in res)
+    # one token of the workload carries H heads
+    return {"value": head_tokens_per_s / H, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{done} head passes over the {B * H} heads of the prefill workload ({done * T} head-tokens), "
+                      f"fp64 chunked form, {n} processes x 1 BLAS thread, {spent:.1f} s of oracle time in all",
+            "host_cpus": host_cpus, "blas_threads_per_process": 1, "seconds": spent}
 
-    # ---------------------------------------------- KDA decode (per-channel decay)
-    wk = synth.WORKLOADS[KDA_DECODE]
-    Nk, Hk, dkk = wk["N"], wk["H"], wk["dk"]
-    Sk = torch.from_numpy(synth.decode_state_fast(wk["seed"], Nk, Hk, dkk, dkk, wk["state_std"])).to(dev)
-    kpool = []
-    for e in range(8):
-        tq, tk, tv, ta, tb = synth.kda_decode_token_inputs(wk["seed"], Nk, Hk, dkk, dkk, "bf16", e)
-        kpool.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (tq, tk, tv)) +
-                     tuple(torch.from_numpy(x).to(dev) for x in (ta, tb)))
-    ok_dec = torch.empty((Nk, Hk, dkk), dtype=torch.bfloat16, device=dev)
-    for i in range(5):
-        tq, tk, tv, ta, tb = kpool[i % 8]
-        gd.lin_attn_decode_step("kda", tq, tk, tv, Sk, alpha=ta, beta=tb, out=ok_dec)
-    torch.cuda.synchronize()
-    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    kev[0].record()
-    for i in range(steps):
-        tq, tk, tv, ta, tb = kpool[i % 8]
-        gd.lin_attn_decode_step("kda", tq, tk, tv, Sk, alpha=ta, beta=tb, out=ok_dec)
-    kev[1].record()
-    torch.cuda.synchronize()
-    kda_dec_ms = kev[0].elapsed_time(kev[1]) / steps
-    # state read + write, q k v o in bf16, alpha per channel and beta in fp32
-    kda_dec_bytes = 2 * Nk * Hk * dkk * dkk * 4 + Nk * Hk * (4 * dkk * 2 + dkk * 4 + 4)
-    kda_dec_gbps = kda_dec_bytes / (kda_dec_ms * 1e-3) / 1e9
-    del Sk, kpool
 
-    # ------------------------- KDA prefill: block form (and the recurrent form)
-    wkp = synth.WORKLOADS[KDA_PREFILL]
-    Bk, Hkp, Tk, dkp = wkp["B"], wkp["H"], wkp["T"], wkp["dk"]
-    kq, kk, kv, ka, kb = synth.kda_batch(wkp["seed"], Bk, Hkp, Tk, dkp, dkp, "bf16")
-    kda_sets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (kq, kk, kv)) +
-                tuple(torch.from_numpy(x).to(dev) for x in (ka, kb)) for _ in range(2)]
-    del kq, kk, kv, ka, kb
-    kda_ws = torch.empty(gd.la_workspace_bytes("kda_prefill", "bf16", Bk, Hkp, Tk, dkp, dkp, "chunked", 64),
-                         dtype=torch.uint8, device=dev)
-    kda_out = torch.empty((Bk, Hkp, Tk, dkp), dtype=torch.bfloat16, device=dev)
-    kda_S = torch.empty((Bk, Hkp, dkp, dkp), dtype=torch.float32, device=dev)
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=24.0,
+                    help="oracle time of the CPU baseline, summed over its processes")
+    ap.add_argument("--la-steps", type=int, default=10, help="timed calls of each secondary prefill leg")
+    ap.add_argument("--long-calls", type=int, default=2, help="timed calls of the 1 x 16 x 262144 prefill")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated legs to run (" + ",".join(LEGS) + "; 'copy' is a 256 MiB device copy "
+                    "for counter scaling, off unless named); default all but copy")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
+              "multi-GPU mode: each GPU would run its own share of heads independently.", file=sys.stderr)
+        sys.exit(2)
+    legs = [l for l in LEGS if l != "copy"] if args.legs == "all" else args.legs.split(",")
+    bad = [l for l in legs if l not in LEGS]
+    if bad:
+        ap.error(f"unknown legs {bad}")
+    if args.long_calls <= 0 and "long" in legs:
+        legs.remove("long")
 
-    def kcall(i, form="chunked"):
-        gd.kda_prefill(*kda_sets[i % 2], form=form, out=kda_out, S_out=kda_S, workspace=kda_ws)
+    c = Ctx(args)
+    fns = {"la": leg_la, "gla": leg_gla, "preops": leg_preops, "decode": leg_decode, "long": leg_long,
+           "kda_decode": leg_kda_decode, "kda_prefill": leg_kda_prefill, "varlen": leg_varlen,
+           "prefill": leg_prefill, "copy": leg_copy}
+    res = {}
+    for name in LEGS:   # fixed order: the headline prefill after every other leg
+        if name in legs:
+            res[name] = fns[name](c)
+            c.torch.cuda.empty_cache()
 
-    for i in range(2):
-        kcall(i)
-    torch.cuda.synchronize()
-    kpe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    kpe[0].record()
-    for i in range(args.la_steps):
-        kcall(i)
-    kpe[1].record()
-    torch.cuda.synchronize()
-    kda_pre_ms = kpe[0].elapsed_time(kpe[1]) / args.la_steps
-    # q, k, v, o in bf16, per-channel alpha and beta in fp32
-    kda_pre_bytes = Bk * Hkp * Tk * (4 * dkp * 2 + dkp * 4 + 4)
-    kda_pre_gbps = kda_pre_bytes / (kda_pre_ms * 1e-3) / 1e9
-    kre = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    kre[0].record()
-    kcall(0, "recurrent")
-    kre[1].record()
-    torch.cuda.synchronize()
-    kda_rec_ms = kre[0].elapsed_time(kre[1])
-    del kda_sets, kda_ws, kda_out, kda_S
-
-    # ------------------------------- packed variable-length batch + snapshots
-    wv = synth.WORKLOADS[VARLEN]
-    Hv, dvv, snapv = wv["H"], wv["dk"], wv["snap"]
-    lens = synth.varlen_lengths(wv["seed"], wv["N"], wv["T_total"])
-    vq, vk, vv, va, vb, vcu = synth.varlen_batch(wv["seed"], lens, Hv, dvv, dvv, "bf16")
-    vsets = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (vq, vk, vv)) +
-             tuple(torch.from_numpy(x).to(dev) for x in (va, vb)) for _ in range(3)]
-    vcu_t = torch.from_numpy(vcu).to(dev)
-    del vq, vk, vv, va, vb
-    nsnap = int(sum(int(L) // snapv for L in lens))
-    v_out = torch.empty((Hv, wv["T_total"], dvv), dtype=torch.bfloat16, device=dev)
-    v_S = torch.empty((wv["N"], Hv, dvv, dvv), dtype=torch.float32, device=dev)
-    v_snap = torch.empty((nsnap, Hv, dvv, dvv), dtype=torch.float32, device=dev)
-    v_ws = torch.empty(gd.la_workspace_bytes("gdn_prefill_varlen", "bf16", wv["N"], Hv, wv["T_total"], dvv, dvv),
-                       dtype=torch.uint8, device=dev)
-
-    def vcall(i):
-        gd.gdn_prefill_varlen(*vsets[i % 3], vcu_t, snap_interval=snapv, snap_count=nsnap, out=v_out, S_out=v_S,
-                              S_snap=v_snap, workspace=v_ws)
-
-    for i in range(2):
-        vcall(i)
-    torch.cuda.synchronize()
-    vev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    vev[0].record()
-    for i in range(args.la_steps):
-        vcall(i)
-    vev[1].record()
-    torch.cuda.synchronize()
-    var_ms = vev[0].elapsed_time(vev[1]) / args.la_steps
-    var_bytes = Hv * wv["T_total"] * path_bytes_per_head_token(dvv) + (nsnap + wv["N"]) * Hv * dvv * dvv * 4
-    var_gbps = var_bytes / (var_ms * 1e-3) / 1e9
-    del vsets, v_out, v_S, v_snap, v_ws
-
-    # ----------------------------------------------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(w, args.cpu_seconds)
-
+    import synth
+    cpu = None if args.no_cpu else cpu_baseline(synth.WORKLOADS[PREFILL], args.cpu_seconds)
+    p = res.get("prefill")
     rec = {
         "metric": "prefill tokens/s (gated delta, H=16,d=128) + decode state HBM GB/s at 1 GPU",
-        "value": tokens_per_s,
+        "value": p["tokens_per_s"] if p else None,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": p["ms_per_step"] if p else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k unit rows, v~N(0,1), alpha=sigmoid(N(3,1)), beta=sigmoid(N(0,1)))",
         "config": {"workload": "gated delta prefill B=2 H=16 T=8192 d_k=d_v=128 chunk=64, bf16 I/O, fp32 state",
-                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "chunk": C,
+                   "global_batch": 2, "seq_len": 8192, "heads": 16, "head_dim": 128, "chunk": 64,
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": dom_traffic,
-                     "bytes_per_launch": alg_bytes, "avg_launch_ms": dom_ms},
-        "kernels_ms": {"gdn_prefill_prep": prep_ms, "gdn_prefill_scan": scan_ms, "segments_per_head": G},
-        "path_roofline": {"bytes_per_head_token": path_bytes_per_head_token(d),
-                          "flops_per_head_token": path_flops_per_head_token(d, C),
-                          "achieved_GBps": path_gbps, "hbm_frac": path_gbps / HBM_PEAK_GBPS,
-                          "achieved_TFLOPs": path_tflops, "mfma_frac": path_tflops / BF16_PEAK_TFLOPS},
-        "decode": {"workload": "gated delta decode 256 seq x 32 heads, d=128, fp32 state, bf16 token I/O",
-                   "steps": steps, "ms_per_step": dec_ms, "steps_per_s": 1e3 / dec_ms,
-                   "wall_steps_per_s": steps / dec_elapsed,
-                   "state_GBps": dec_state_gbps, "total_GBps": dec_total_gbps,
-                   "roofline": {"kernel": "recurrent_kernel (decode)", "bound": "hbm",
-                                "achieved": dec_total_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                "frac": dec_total_gbps / HBM_PEAK_GBPS,
-                                "traffic": measured_traffic(["recurrent_kernel_gated_delta_decode"]),
-                                "bytes_per_launch": state_bytes + io_bytes, "avg_launch_ms": dec_ms}},
-        "la_prefill": {"workload": "normalised linear attention prefill B=4 H=16 T=4096 d=128 chunk=64, bf16 I/O, "
-                                   "fp32 state", "calls": args.la_steps, "ms_per_call": la_ms,
-                       "tokens_per_s": Bl * Tl / (la_ms * 1e-3),
-                       "roofline": {"kernel": "la_chunked_mfma_kernel", "bound": "hbm", "achieved": la_gbps,
-                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": la_gbps / HBM_PEAK_GBPS,
-                                    "bytes_per_launch": la_bytes, "avg_launch_ms": la_ms,
-                                    "achieved_TFLOPs": la_flops / (la_ms * 1e-3) / 1e12}},
-        "gla_prefill": {"workload": "scalar-gated linear attention prefill B=2 H=16 T=8192 d=128 chunk=64, bf16 "
-                                    "I/O, fp32 state", "calls": args.la_steps, "ms_per_call": gla_ms,
-                        "tokens_per_s": wg["B"] * wg["T"] / (gla_ms * 1e-3),
-                        "roofline": {"kernel": "la_chunked_mfma_kernel (gated)", "bound": "hbm",
-                                     "achieved": gla_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                     "frac": gla_gbps / HBM_PEAK_GBPS, "bytes_per_launch": gla_bytes,
-                                     "avg_launch_ms": gla_ms}},
-        "preprocess": {"workload": "Gated DeltaNet pre-operations (conv k=4, q/k L2 norm, sigmoid gates) B=2 "
-                                   "H=16 T=8192 d=128, bf16 I/O", "calls": args.la_steps, "ms_per_call": pre_ms,
-                       "tokens_per_s": Bp * Tp / (pre_ms * 1e-3),
-                       "roofline": {"kernel": "gdn_preprocess_kernel", "bound": "hbm", "achieved": pre_gbps,
-                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pre_gbps / HBM_PEAK_GBPS,
-                                    "traffic": measured_traffic(["gdn_preprocess_kernel"]),
-                                    "bytes_per_launch": pre_bytes, "avg_launch_ms": pre_ms}},
-        "long_context_prefill": None if long_ms is None else {
-            "workload": "gated delta prefill B=1 H=16 T=262144 d=128 chunk=64, bf16 I/O, fp32 state (inputs drawn "
-                        "on the device)", "calls": args.long_calls, "ms_per_call": long_ms,
-            "tokens_per_s": B5 * T5 / (long_ms * 1e-3),
-            "roofline": {"kernel": "gdn_prefill (map + combine + out)", "bound": "hbm", "achieved": long_gbps,
-                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": long_gbps / HBM_PEAK_GBPS,
-                         "bytes_per_launch": B5 * H5 * T5 * path_bytes_per_head_token(d5), "avg_launch_ms": long_ms}},
-        "kda_decode": {"workload": "KDA decode 256 seq x 32 heads, d=128, per-channel decay, fp32 state, bf16 "
-                                   "token I/O", "steps": steps, "ms_per_step": kda_dec_ms,
-                       "steps_per_s": 1e3 / kda_dec_ms,
-                       "roofline": {"kernel": "recurrent_kernel (KDA decode)", "bound": "hbm",
-                                    "achieved": kda_dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                    "frac": kda_dec_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kda_dec_bytes,
-                                    "avg_launch_ms": kda_dec_ms}},
-        "kda_prefill": {"workload": "KDA prefill B=2 H=16 T=8192 d=128 chunk=64 (block form: tile pass + "
-                                    "column-parallel scan), bf16 I/O, fp32 state", "calls": args.la_steps,
-                        "ms_per_call": kda_pre_ms, "tokens_per_s": Bk * Tk / (kda_pre_ms * 1e-3),
-                        "recurrent_form_ms": kda_rec_ms,
-                        "roofline": {"kernel": "kda_tile_kernel + kda_scan_kernel", "bound": "hbm",
-                                     "achieved": kda_pre_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                     "frac": kda_pre_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kda_pre_bytes,
-                                     "avg_launch_ms": kda_pre_ms}},
-        "varlen_prefill": {"workload": f"gated delta prefill, packed batch of {wv['N']} sequences ({wv['T_total']} "
-                                       f"tokens, lengths {int(min(lens))}..{int(max(lens))}), H=16 d=128 chunk=64, "
-                                       f"snapshots every {snapv} tokens ({nsnap})",
-                           "calls": args.la_steps, "ms_per_call": var_ms,
-                           "tokens_per_s": wv["T_total"] / (var_ms * 1e-3),
-                           "roofline": {"kernel": "gdn_prefill_varlen (plan + map + combine + out)", "bound": "hbm",
-                                        "achieved": var_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                        "frac": var_gbps / HBM_PEAK_GBPS, "bytes_per_launch": var_bytes,
-                                        "avg_launch_ms": var_ms}},
+        "roofline": p["roofline"] if p else None,
+        "mfma": p["mfma"] if p else None,
+        "decode": res.get("decode"),
+        "la_prefill": res.get("la"),
+        "gla_prefill": res.get("gla"),
+        "preprocess": res.get("preops"),
+        "long_context_prefill": res.get("long"),
+        "kda_decode": res.get("kda_decode"),
+        "kda_prefill": res.get("kda_prefill"),
+        "varlen_prefill": res.get("varlen"),
+        "legs_run": legs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
-
-
-def cpu_baseline(w, seconds):
-    """The fp64 oracle (chunked form), single-threaded BLAS, on the first heads
-    of the prefill workload until `seconds` have passed."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle
-    import synth
-
-    B, H, T, d, C = w["B"], w["H"], w["T"], w["dk"], w["chunk"]
-    done = 0
-    spent = 0.0
-    heads = [(bb, hh) for bb in range(B) for hh in range(H)]
-    with threadpool_limits(limits=1):
-        while spent < seconds:
-            bb, hh = heads[done % len(heads)]
-            q, k, v, a, b = synth.gdn_head(w["seed"], bb, hh, T, d, d, "bf16")
-            ts = time.perf_counter()
-            oracle.gdn_chunked(q, k, v, a, b, C)
-            spent += time.perf_counter() - ts
-            done += 1
-    elapsed = spent
-    # one token of the workload carries H heads
-    return {"value": done * T / H / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} head passes over the {B * H} heads of the prefill workload, cycling "
-                      f"({done * T} head-tokens), fp64 chunked form, {elapsed:.1f} s of oracle time",
-            "seconds": elapsed}
 
 
 if __name__ == "__main__":
