@@ -122,6 +122,12 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<NTHR, WR>& rc, const u16* _
 // len.. (past the end of the sequence) as zeros.
 template <class RC, int NI>
 __device__ __forceinline__ void stage_rows(u16 (*X)[LDQ], const uint4 (&raw)[NI], int tid, int len) {
+    if (len >= C) {   // a whole chunk (len is uniform): no rows to clear
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+            *reinterpret_cast<uint4*>(&X[RC::row(tid, it)][RC::col(tid)]) = raw[it];
+        return;
+    }
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
         const int row = RC::row(tid, it);
@@ -340,31 +346,43 @@ __device__ __forceinline__ void zero_above(u16 (*X)[LDA], int z, int lane) {
 //
 // O = Q P (the inter-chunk part of the outputs, before the e^g row scaling;
 // WITH_Q only) and X = K P, rows in the permuted order, in one pass over the
-// packed state.
+// packed state.  Sixteen steps (K-slice s, row tile m); the LDS operands of
+// step i + AHEAD are read before the products of step i, so each wait for a
+// read is covered by AHEAD steps of matrix-core work (a read issued right
+// before its products left the whole LDS latency exposed).
 template <int NT, bool WITH_Q>
 __device__ __forceinline__ void scan_qk(const u16 (*Qs)[LDQ], const u16 (*Ks)[LDQ], const f32x4 (&P)[NT][8], int lane,
                                         f32x4 (&O)[NT][4], f32x4 (&X)[NT][4]) {
     const int r = lane & 15, g = lane >> 4;
+    constexpr int AHEAD = WITH_Q ? 2 : 4, NBUF = AHEAD + 1;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int m = 0; m < 4; ++m) O[nt][m] = X[nt][m] = zero4();
+    bf16x8 ak[NBUF], aq[NBUF];
+    auto load = [&](int i) {
+        const int s = i >> 2, m = i & 3;
+        ak[i % NBUF] = lds_bf16x8(&Ks[perm_row(m, r)][32 * s + 8 * g]);
+        if constexpr (WITH_Q) aq[i % NBUF] = lds_bf16x8(&Qs[perm_row(m, r)][32 * s + 8 * g]);
+    };
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        bf16x8 pb[NT];
+    for (int i = 0; i < AHEAD; ++i) load(i);
+    bf16x8 pb[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pb[nt] = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
+    for (int i = 0; i < 16; ++i) {
+        const int s = i >> 2, m = i & 3;
+        if (i + AHEAD < 16) load(i + AHEAD);
+        if (m == 0) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const bf16x8 ak = lds_bf16x8(&Ks[perm_row(m, r)][32 * s + 8 * g]);
-            if constexpr (WITH_Q) {
-                const bf16x8 aq = lds_bf16x8(&Qs[perm_row(m, r)][32 * s + 8 * g]);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(aq, pb[nt], O[nt][m]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) X[nt][m] = mfma16x16x32(ak, pb[nt], X[nt][m]);
+            for (int nt = 0; nt < NT; ++nt) pb[nt] = pack_acc_pair(P[nt][2 * s], P[nt][2 * s + 1]);
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of these products
+        if constexpr (WITH_Q) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(aq[i % NBUF], pb[nt], O[nt][m]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) X[nt][m] = mfma16x16x32(ak[i % NBUF], pb[nt], X[nt][m]);
     }
 }
 
@@ -402,25 +420,40 @@ __device__ __forceinline__ void scan_rhs(const u16 (*Vs)[LDQ], const Gates& gt, 
     }
 }
 
+// The A operands a lower-triangular 64 x 64 tile (Tm or A) contributes to a
+// product with a 64-row right-hand side: row tile m (chunk rows
+// 32(m/2)..+31, permuted) needs K-slices s2 <= m/2, six pieces in all, read
+// in one go so that their LDS latency overlaps (and, issued early, the work
+// before their products).
+struct TriOps {
+    bf16x8 a[6];
+};
+__device__ __forceinline__ constexpr int tri_idx(int m, int s2) { return m < 2 ? m : 2 + 2 * (m - 2) + s2; }
+
+__device__ __forceinline__ void load_tri(TriOps& t, const u16 (*X)[LDA], int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int s2 = 0; s2 <= (m >> 1); ++s2) t.a[tri_idx(m, s2)] = lds_bf16x8(&X[perm_row(m, r)][32 * s2 + 8 * g]);
+}
+
 // U = (I + L)^{-1} times that right-hand side (rows permuted), returned packed
 // with the rows scaled by e^{g_c - g} (for the state update, which then reads
 // K itself) and, WITH_UB, as is (for A U).
 template <int NT, bool WITH_UB>
-__device__ __forceinline__ void scan_solve(const u16 (*Tm)[LDA], const Gates& gt, const bf16x8 (&Xb)[NT][2], int lane,
+__device__ __forceinline__ void scan_solve(const TriOps& tm, const Gates& gt, const bf16x8 (&Xb)[NT][2], int lane,
                                            bf16x8 (&Ub)[NT][2], bf16x8 (&Ue)[NT][2]) {
-    const int r = lane & 15, g = lane >> 4;
+    const int g = lane >> 4;
     f32x4 U[NT][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) U[nt][m] = zero4();
-        // row tile m (chunk rows 32(m/2)..+31) needs column slices s2 <= m/2
 #pragma unroll
-        for (int s2 = 0; s2 <= (m >> 1); ++s2) {
-            const bf16x8 a = lds_bf16x8(&Tm[perm_row(m, r)][32 * s2 + 8 * g]);
+        for (int s2 = 0; s2 <= (m >> 1); ++s2)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) U[nt][m] = mfma16x16x32(a, Xb[nt][s2], U[nt][m]);
-        }
+            for (int nt = 0; nt < NT; ++nt) U[nt][m] = mfma16x16x32(tm.a[tri_idx(m, s2)], Xb[nt][s2], U[nt][m]);
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -438,7 +471,7 @@ __device__ __forceinline__ void scan_solve(const u16 (*Tm)[LDA], const Gates& gt
 
 // O <- diag(e^g) O + A U, stored for the rows that exist.
 template <int NT>
-__device__ __forceinline__ void scan_out(const u16 (*As)[LDA], const Gates& gt, f32x4 (&O)[NT][4],
+__device__ __forceinline__ void scan_out(const TriOps& am, const Gates& gt, f32x4 (&O)[NT][4],
                                          const bf16x8 (&Ub)[NT][2], int col0, int lane, u16* __restrict__ o,
                                          size_t o_row0, int len, u16 (*Os)[LDQ]) {
     const int r = lane & 15, g = lane >> 4;
@@ -457,11 +490,9 @@ __device__ __forceinline__ void scan_out(const u16 (*As)[LDA], const Gates& gt, 
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int s2 = 0; s2 <= (m >> 1); ++s2) {
-            const bf16x8 a = lds_bf16x8(&As[perm_row(m, r)][32 * s2 + 8 * g]);
+        for (int s2 = 0; s2 <= (m >> 1); ++s2)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(a, Ub[nt][s2], O[nt][m]);
-        }
+            for (int nt = 0; nt < NT; ++nt) O[nt][m] = mfma16x16x32(am.a[tri_idx(m, s2)], Ub[nt][s2], O[nt][m]);
     // Outputs go through LDS (Os: this wave's 16 NT columns of a free 64-row
     // tile) so that every global store is 16 contiguous bytes.
 #pragma unroll
@@ -649,11 +680,12 @@ __device__ __forceinline__ bool find_item(const Geo& g, int blk, bool maps, Item
 }
 
 // ============================================================ segment maps
-// LDS of the map kernel: k, (I + L)^{-1} and gates in two copies by chunk
-// parity, v in one (rewritten after the carriers' last read of it).
+// LDS of the map kernel: k and the gates in three copies (chunk n for the
+// carriers, n+1 for the stagers, n+2 being written), v and (I + L)^{-1} in two
+// by chunk parity.
 struct MapTiles {
     u16 Ks[3][C][LDQ];    // chunk m in copy m % 3
-    u16 Vs[C][LDQ];
+    u16 Vs[2][C][LDQ];    // chunk m in copy m & 1
     u16 Tm[2][C][LDA];    // chunk m in copy m & 1
     u16 Lb[C][LDA];
     Gates gt[3];          // chunk m in copy m % 3
@@ -665,15 +697,13 @@ constexpr int kMapThreads = 768;   // 8 state carriers + 4 stagers
 // [0 | I]): waves 0-3 the N columns (value channels 32w..32w+31, with V),
 // waves 4-7 the M columns (no V term).  Per chunk, like the output kernel
 // without Q, A and the outputs:
-//     carriers:  K P | B1 | right-hand side (reads v), solve | B2 | update,
-//                staging | B0
+//     carriers:  K P, staging | B1 | right-hand side (reads v), solve | B2 |
+//                update | B0
 //     stagers:   diagonal inverse blocks of chunk n+1 | B1 |
 //                L below the diagonal | B2 | inverse below the diagonal (three waves) | B0
-// The stagers' three steps are the longest path of a chunk, so the carriers
-// also stage the inputs, in their last phase: waves 0-3 (whose update is the
-// shorter) k and the gates of chunk n+2, waves 4-7 v of chunk n+1 (k has
-// three LDS copies: chunk n for the carriers, n+1 for the stagers, n+2 being
-// written).
+// The carriers also stage the inputs, in the first phase, which the stagers'
+// diagonal blocks bound: waves 0-3 k and the gates of chunk n+2, waves 4-7 v
+// of chunk n+1.
 __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
                                                               const u16* __restrict__ v,
                                                               const float* __restrict__ alpha,
@@ -700,8 +730,10 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
                     P[nt][t][i] = (!npart && perm_row(t, 4 * g + i) == col0 + 16 * nt + r) ? 1.f : 0.f;
         // inputs: waves 0-3 load k and the gates, waves 4-7 v into rc.k (the
         // gates that come with it are not used); chunk n + ahead is staged in
-        // the last phase of chunk n, every index past the segment clamped to
-        // its last chunk (no branch around the loads)
+        // the first phase of chunk n, where the carriers' products are shorter
+        // than the stagers' diagonal inverse blocks, every index past the
+        // segment clamped to its last chunk (no branch around the loads; a
+        // clamped copy rewrites a tile with the values it already holds)
         const bool kpart = npart;
         const int ptid = tid & 255, ahead = kpart ? 2 : 1;
         const u16* src = kpart ? k : v;
@@ -718,7 +750,7 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
                 write_gates(sm.gt[m % 3], chunk_gates(rc.a, rc.b, len), lane);
                 stage_rows<RC>(sm.Ks[m % 3], rc.k, ptid, len);
             } else {
-                stage_rows<RC>(sm.Vs, rc.k, ptid, len);
+                stage_rows<RC>(sm.Vs[m & 1], rc.k, ptid, len);
             }
         };
         fetch(n0);
@@ -738,16 +770,18 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
             f32x4 O[2][4], X[2][4];
             bf16x8 Xb[2][2], Ub[2][2], Ue[2][2];
             scan_qk<2, false>(nullptr, sm.Ks[c3], P, lane, O, X);
-            lds_barrier();  // B1
-            if (npart)
-                scan_rhs<2, true>(sm.Vs, gt, X, col0, lane, Xb);
-            else
-                scan_rhs<2, false>(sm.Vs, gt, X, col0, lane, Xb);
-            scan_solve<2, false>(sm.Tm[cb], gt, Xb, lane, Ub, Ue);
-            lds_barrier();  // B2
-            scan_update<2>(sm.Ks[c3], gt, P, Ue, lane);
             stage(n + ahead);
             fetch(n + ahead + 1);
+            lds_barrier();  // B1
+            if (npart)
+                scan_rhs<2, true>(sm.Vs[cb], gt, X, col0, lane, Xb);
+            else
+                scan_rhs<2, false>(sm.Vs[cb], gt, X, col0, lane, Xb);
+            TriOps tm;
+            load_tri(tm, sm.Tm[cb], lane);
+            scan_solve<2, false>(tm, gt, Xb, lane, Ub, Ue);
+            lds_barrier();  // B2
+            scan_update<2>(sm.Ks[c3], gt, P, Ue, lane);
             lds_barrier();  // B0
         }
         if (npart)
@@ -968,12 +1002,15 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
             bf16x8 Xb[2][2], Ub[2][2], Ue[2][2];
             scan_qk<2, true>(sm.Qs, sm.Ks[cb], P, lane, O, X);
             lds_barrier();  // B1
+            TriOps tm, am;
+            load_tri(tm, sm.Tm[cb], lane);
             scan_rhs<2, true>(sm.Vs, gt, X, col0, lane, Xb);
-            scan_solve<2, true>(sm.Tm[cb], gt, Xb, lane, Ub, Ue);
+            scan_solve<2, true>(tm, gt, Xb, lane, Ub, Ue);
+            load_tri(am, sm.As[cb], lane);   // A of chunk n was formed during chunk n - 1
             if (n + 1 < n1) diag(n + 1);
             lds_barrier();  // B2
             const int t0 = n * C;
-            scan_out<2>(sm.As[cb], gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Os);
+            scan_out<2>(am, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Os);
             scan_update<2>(sm.Ks[cb], gt, P, Ue, lane);
             // snapshot of the state after chunk n (packed batches)
             const int end = (n + 1) * C;
