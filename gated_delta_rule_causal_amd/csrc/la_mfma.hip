@@ -435,7 +435,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 // Entering states of every segment: P_0 = S0 (or 0), P_{s+1} = P_s + dS_s, and
 // the same for z; GATED: P_{s+1} = m_s P_s + dS_s with the segment decay m_s.
-// 16 workgroups per head, 4 consecutive floats per thread.
+// 16 workgroups per head, 4 consecutive floats per thread.  The contributions
+// of up to kBatch segments are loaded before any of them is added, so the
+// chain of additions waits for one memory latency per batch instead of one
+// per segment.
+constexpr int kBatch = 8;
+
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) void la_combine_kernel(int BH, int G, const float* S0, const float* z0,
                                                               float* ws) {
@@ -445,20 +450,41 @@ __global__ __launch_bounds__(kThreads) void la_combine_kernel(int BH, int G, con
     const size_t e = (static_cast<size_t>(part) * kThreads + threadIdx.x) * 4;   // < kMat
     float4 run = S0 ? *reinterpret_cast<const float4*>(S0 + static_cast<size_t>(bh) * kMat + e)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < G; ++s) {
-        *reinterpret_cast<float4*>(ws + ws_P(bh, G, s) + e) = run;
-        if (s + 1 < G) {
-            const float4 d = *reinterpret_cast<const float4*>(ws + ws_dS(bh, G, s) + e);
-            const float m = GATED ? ws[ws_dz(bh, G, s)] : 1.f;
-            run.x = fmaf(m, run.x, d.x); run.y = fmaf(m, run.y, d.y);
-            run.z = fmaf(m, run.z, d.z); run.w = fmaf(m, run.w, d.w);
+    for (int s0 = 0; s0 < G; s0 += kBatch) {
+        float4 d[kBatch];
+        float m[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int s = min(s0 + j, G - 2);   // (G >= 2) clamped: loads past the last map are unused
+            d[j] = *reinterpret_cast<const float4*>(ws + ws_dS(bh, G, s) + e);
+            m[j] = GATED ? ws[ws_dz(bh, G, s)] : 1.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int s = s0 + j;
+            if (s < G) {
+                *reinterpret_cast<float4*>(ws + ws_P(bh, G, s) + e) = run;
+                if (s + 1 < G) {
+                    run.x = fmaf(m[j], run.x, d[j].x); run.y = fmaf(m[j], run.y, d[j].y);
+                    run.z = fmaf(m[j], run.z, d[j].z); run.w = fmaf(m[j], run.w, d[j].w);
+                }
+            }
         }
     }
     if (!GATED && part == 0 && threadIdx.x < D) {
         float zr = z0 ? z0[static_cast<size_t>(bh) * D + threadIdx.x] : 0.f;
-        for (int s = 0; s < G; ++s) {
-            ws[ws_zP(bh, G, s) + threadIdx.x] = zr;
-            if (s + 1 < G) zr += ws[ws_dz(bh, G, s) + threadIdx.x];
+        for (int s0 = 0; s0 < G; s0 += kBatch) {
+            float dz[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) dz[j] = ws[ws_dz(bh, G, min(s0 + j, G - 2)) + threadIdx.x];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int s = s0 + j;
+                if (s < G) {
+                    ws[ws_zP(bh, G, s) + threadIdx.x] = zr;
+                    if (s + 1 < G) zr += dz[j];
+                }
+            }
         }
     }
 }
