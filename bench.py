@@ -14,11 +14,12 @@ and prefill (block and recurrent forms); a packed batch of 16 sequences of
 mixed lengths with state snapshots; and the fp64 CPU oracle on a bounded
 sample of the prefill workload.  Prints one JSON line.
 
-The headline prefill is timed last, after the other legs: by then the GPU has
-been busy for several hundred milliseconds and its clocks have settled, as in
-a serving process (on a cold GPU the first milliseconds of work run at lower
-clocks).  `--legs` runs a subset (e.g. one leg under a profiler); the legs not
-run are null in the JSON line.
+Every leg's inputs are drawn and uploaded first; then the GPU runs about 0.3 s
+of untimed work and the timed parts of the legs follow back to back, the
+headline prefill last: every figure is taken at settled clocks, as in a
+serving process (an idle GPU lowers its clocks, and the first milliseconds of
+work after an idle gap run slower).  `--legs` runs a subset (e.g. one
+leg under a profiler); the legs not run are null in the JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 are launched on (torch's current stream, which the binding passes to the C
@@ -161,6 +162,7 @@ def leg_la(c):
     out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=c.dev)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
     z = torch.empty((B, H, d), dtype=torch.float32, device=c.dev)
+    yield   # inputs prepared; the timed part runs when every leg is prepared
     ms = c.timed(n, lambda i: gd.lin_attn_prefill(*sets[i % 3], form="chunked", chunk=C, out=out, S_out=S, z_out=z))
     ht = B * H * T
     roof = hbm_roofline("la_chunked_mfma_kernel (state pass + combine + output pass)", ht * 4 * d * 2, ms,
@@ -180,6 +182,7 @@ def leg_gla(c):
     del q, k, v, a
     out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=c.dev)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
+    yield
     ms = c.timed(n, lambda i: gd.gla_prefill(*sets[i % 3], form="chunked", chunk=C, out=out, S_out=S))
     nbytes = B * H * T * (4 * d * 2 + 4)   # q, k, v, o bf16 + alpha fp32
     return {"workload": "scalar-gated linear attention prefill B=2 H=16 T=8192 d=128 chunk=64, bf16 I/O, fp32 state",
@@ -203,6 +206,7 @@ def leg_preops(c):
                 v=torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=c.dev),
                 alpha=torch.empty((B, H, T), dtype=torch.float32, device=c.dev),
                 beta=torch.empty((B, H, T), dtype=torch.float32, device=c.dev))
+    yield
     ms = c.timed(n, lambda i: gd.gdn_preprocess(*sets[i % 3], H, dk, dv, want_state=False, **outs))
     # x read + gate logits read, q, k, v written + alpha, beta written
     nbytes = B * H * T * (2 * ((2 * dk + dv) * 2 + 8))
@@ -227,6 +231,7 @@ def _decode(c, kind, wname, inputs, traffic_key):
         tq, tk, tv, ta, tb = pool[i % 8]
         gd.lin_attn_decode_step(kind, tq, tk, tv, S, alpha=ta, beta=tb, out=o)
 
+    yield
     t0 = time.perf_counter()
     ms = c.timed(steps, call, warm=5)
     wall = time.perf_counter() - t0
@@ -242,13 +247,13 @@ def _decode(c, kind, wname, inputs, traffic_key):
 
 def leg_decode(c):
     import synth
-    r = _decode(c, "gated_delta", DECODE, synth.decode_token_inputs, "recurrent_kernel_gated_delta_decode")
+    r = yield from _decode(c, "gated_delta", DECODE, synth.decode_token_inputs, "recurrent_kernel_gated_delta_decode")
     return dict(workload="gated delta decode 256 seq x 32 heads, d=128, fp32 state, bf16 token I/O", **r)
 
 
 def leg_kda_decode(c):
     import synth
-    r = _decode(c, "kda", KDA_DECODE, synth.kda_decode_token_inputs, "recurrent_kernel_kda_decode")
+    r = yield from _decode(c, "kda", KDA_DECODE, synth.kda_decode_token_inputs, "recurrent_kernel_kda_decode")
     return dict(workload="KDA decode 256 seq x 32 heads, d=128, per-channel decay, fp32 state, bf16 token I/O", **r)
 
 
@@ -272,6 +277,7 @@ def leg_long(c):
     ws = gd.gdn_workspace(q, v, 64)
     out = torch.empty_like(v)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
+    yield
     ms = c.timed(n, lambda i: gd.gdn_prefill(q, k, v, a, b, form="chunked", chunk=64, out=out, S_out=S, workspace=ws),
                  warm=1)
     nbytes = B * H * T * path_bytes_per_head_token(d)
@@ -296,6 +302,7 @@ def leg_kda_prefill(c):
     def call(i, form="chunked"):
         gd.kda_prefill(*sets[i % 2], form=form, out=out, S_out=S, workspace=ws)
 
+    yield
     ms = c.timed(n, call)
     rec_ms = c.timed(1, lambda i: call(i, "recurrent"), warm=0)
     # q, k, v, o in bf16, per-channel alpha and beta in fp32
@@ -323,6 +330,7 @@ def leg_varlen(c):
     S_snap = torch.empty((nsnap, H, d, d), dtype=torch.float32, device=c.dev)
     ws = torch.empty(gd.la_workspace_bytes("gdn_prefill_varlen", "bf16", N, H, Tt, d, d), dtype=torch.uint8,
                      device=c.dev)
+    yield
     ms = c.timed(n, lambda i: gd.gdn_prefill_varlen(*sets[i % 3], cu_t, snap_interval=snap, snap_count=nsnap, out=out,
                                                      S_out=S, S_snap=S_snap, workspace=ws))
     nbytes = H * Tt * path_bytes_per_head_token(d) + (nsnap + N) * H * d * d * 4
@@ -335,6 +343,7 @@ def leg_varlen(c):
 def leg_copy(c):
     # a plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
     # WRITE_SIZE give the factor that turns those counters into bytes
+    yield
     torch = c.torch
     src = torch.empty(64 << 20, dtype=torch.float32, device=c.dev).fill_(1.0)
     dst = torch.empty_like(src)
@@ -371,6 +380,7 @@ def leg_prefill(c):
         if ev is not None:
             ev[2].record()
 
+    yield
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -412,6 +422,26 @@ def leg_prefill(c):
                      "counter_busy_frac": None if pmc is None else pmc["busy_frac"],
                      "counter_flops_per_step": None if pmc is None else pmc["flops"],
                      "counter_kernels": None if pmc is None else pmc["kernels"]}}
+
+
+def settle(c, ms):
+    """About `ms` milliseconds of untimed GPU work (repeated decode steps of a
+    small batch) before anything is measured: the GPU raises its clocks only
+    after several milliseconds of sustained work, and without this the first
+    leg would be timed on a cold GPU."""
+    torch, gd = c.torch, c.gd
+    if ms <= 0:
+        return
+    N, H, d = 64, 32, 128
+    S = torch.zeros((N, H, d, d), dtype=torch.float32, device=c.dev)
+    x = torch.zeros((N, H, d), dtype=torch.bfloat16, device=c.dev)
+    o = torch.empty_like(x)
+    a = torch.ones((N, H), dtype=torch.float32, device=c.dev)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(50):
+            gd.lin_attn_decode_step("gated_delta", x, x, x, S, alpha=a, beta=a, out=o)
+        torch.cuda.synchronize()
 
 
 # ------------------------------------------------------ CPU oracle baseline
@@ -474,6 +504,8 @@ def main():
                     help="oracle time of the CPU baseline, summed over its processes")
     ap.add_argument("--la-steps", type=int, default=10, help="timed calls of each secondary prefill leg")
     ap.add_argument("--long-calls", type=int, default=2, help="timed calls of the 1 x 16 x 262144 prefill")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed GPU work before the first leg, so that every leg runs at settled clocks")
     ap.add_argument("--legs", default="all",
                     help="comma-separated legs to run (" + ",".join(LEGS) + "; 'copy' is a 256 MiB device copy "
                     "for counter scaling, off unless named); default all but copy")
@@ -493,11 +525,24 @@ def main():
     fns = {"la": leg_la, "gla": leg_gla, "preops": leg_preops, "decode": leg_decode, "long": leg_long,
            "kda_decode": leg_kda_decode, "kda_prefill": leg_kda_prefill, "varlen": leg_varlen,
            "prefill": leg_prefill, "copy": leg_copy}
+    # Every leg first draws and uploads its inputs (seconds of host work, the
+    # GPU idle); then the timed parts run back to back, in a fixed order with
+    # the headline prefill last, so that no leg is timed right after an idle
+    # gap (the GPU lowers its clocks when idle).
+    order = [name for name in LEGS if name in legs]
+    gens = {}
+    for name in order:
+        gens[name] = fns[name](c)
+        next(gens[name])
+    torch_sync = c.torch.cuda.synchronize
+    torch_sync()
+    settle(c, args.settle_ms)
     res = {}
-    for name in LEGS:   # fixed order: the headline prefill after every other leg
-        if name in legs:
-            res[name] = fns[name](c)
-            c.torch.cuda.empty_cache()
+    for name in order:
+        try:
+            next(gens[name])
+        except StopIteration as stop:
+            res[name] = stop.value
 
     import synth
     cpu = None if args.no_cpu else cpu_baseline(synth.WORKLOADS[PREFILL], args.cpu_seconds)
