@@ -23,6 +23,7 @@ __all__ = [
     "gla_prefill",
     "kda_prefill",
     "gdn_prefill_varlen",
+    "lin_attn_prefill_varlen",
     "gdn_prefill_prep",
     "gdn_prefill_scan",
     "gdn_preprocess",
@@ -45,7 +46,7 @@ LA_F32, LA_BF16 = 0, 1
 FORMS = {"chunked": 0, "recurrent": 1, "parallel": 2}
 KINDS = {"normalized": 0, "gated_delta": 1, "gated": 2, "kda": 3}
 FNS = {"lin_attn_prefill": 0, "gdn_prefill": 1, "decode_step": 2, "gla_prefill": 3, "kda_prefill": 4,
-       "gdn_prefill_varlen": 5}
+       "gdn_prefill_varlen": 5, "prefill_varlen": 6}
 
 _lib = None
 
@@ -82,6 +83,9 @@ def _load():
     lib.kda_prefill.restype = I
     lib.gdn_prefill_varlen.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, I, P, I, I, P, Z, P]
     lib.gdn_prefill_varlen.restype = I
+    lib.lin_attn_prefill_varlen.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, I, I,
+                                            P, Z, P]
+    lib.lin_attn_prefill_varlen.restype = I
     lib.gdn_preprocess.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdn_preprocess.restype = I
     lib.gdn_preprocess_varlen.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]
@@ -332,6 +336,68 @@ def gdn_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, form="chunked"
     if st != 0:
         raise LinAttnError(st, "gdn_prefill_varlen")
     return out, S_out, (S_snap[:snap_count] if S_snap is not None else None)
+
+
+def lin_attn_prefill_varlen(kind, q, k, v, cu_seqlens, alpha=None, beta=None, S0=None, z0=None, form="recurrent",
+                            chunk=64, snap_interval=0, snap_count=None, out=None, S_out=None, z_out=None, S_snap=None,
+                            z_snap=None, want_state=True, workspace=None, stream=None):
+    """Any kind of recurrence over a packed batch; returns (o, S_out, z_out,
+    S_snap, z_snap), the z entries None except for the normalised kind.
+
+    kind: "normalized", "gated", "kda" or "gated_delta".  q, k [H,T_total,dk];
+    v [H,T_total,dv]; alpha [H,T_total] float32 ("gated", "gated_delta") or
+    [H,T_total,dk] ("kda"); beta [H,T_total] float32 ("kda", "gated_delta");
+    cu_seqlens [N+1] int32 on the device; S0 [N,H,dv,dk], z0 [N,H,dk]
+    ("normalized") or None.  With snap_interval > 0 the states after every
+    snap_interval tokens of each sequence are returned in S_snap
+    [snap_count,H,dv,dk] (and z_snap [snap_count,H,dk]); when snap_count is
+    None it is counted from a host copy of cu_seqlens (a synchronisation).
+    """
+    torch = _torch()
+    kind_i = KINDS[kind]
+    has_z = kind == "normalized"
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt = _dtype_code(q.dtype)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (H, T, dk))
+    _check(v, "v", q.dtype, (H, T, dv))
+    _check(alpha, "alpha", torch.float32, (H, T, dk) if kind == "kda" else (H, T))
+    _check(beta, "beta", torch.float32, (H, T))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    _check(S0, "S0", torch.float32, (N, H, dv, dk))
+    _check(z0, "z0", torch.float32, (N, H, dk))
+    if out is None:
+        out = torch.empty((H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (H, T, dv))
+    if want_state and S_out is None:
+        S_out = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    if want_state and has_z and z_out is None:
+        z_out = torch.empty((N, H, dk), dtype=torch.float32, device=q.device)
+    _check(S_out, "S_out", torch.float32, (N, H, dv, dk))
+    _check(z_out, "z_out", torch.float32, (N, H, dk))
+    if snap_interval > 0:
+        if snap_count is None:
+            lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
+            snap_count = int((lens // snap_interval).sum()) if N > 0 else 0
+        if S_snap is None:
+            S_snap = torch.empty((max(snap_count, 1), H, dv, dk), dtype=torch.float32, device=q.device)
+        if has_z and z_snap is None:
+            z_snap = torch.empty((max(snap_count, 1), H, dk), dtype=torch.float32, device=q.device)
+        _check(S_snap, "S_snap", torch.float32)
+        _check(z_snap, "z_snap", torch.float32)
+    else:
+        snap_count, S_snap, z_snap = 0, None, None
+    ws, ws_bytes = _workspace("prefill_varlen", dt, N, H, T, dk, dv, form, chunk, workspace, q.device)
+    st = _load().lin_attn_prefill_varlen(kind_i, dt, N, H, T, dk, dv, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_out),
+                                         _ptr(z_out), snap_interval, snap_count, _ptr(S_snap), _ptr(z_snap),
+                                         FORMS[form], chunk, _ptr(ws), ws_bytes, _stream_ptr(stream, q.device))
+    if st != 0:
+        raise LinAttnError(st, "lin_attn_prefill_varlen")
+    cut = (lambda t: t[:snap_count] if t is not None else None)
+    return out, S_out, z_out, cut(S_snap), cut(z_snap)
 
 
 def gdn_preprocess_varlen(x, conv_w, a_logit, b_logit, H, dk, dv, cu_seqlens, conv_state=None, want_state=True,

@@ -128,6 +128,7 @@ size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv
             if (form == LA_FORM_CHUNKED && !la::kda_mfma_supported(dtype, dk, dv, chunk)) return bad;
             return form == LA_FORM_CHUNKED ? la::kda_mfma_workspace_bytes(B, H, T) : 0;
         case LA_FN_GDN_VARLEN:   // B = number of sequences, T = total tokens
+        case LA_FN_PREFILL_VARLEN:
             if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
             if (form == LA_FORM_CHUNKED && !la::gdn_mfma_supported(dtype, dk, dv, chunk)) return bad;
             return form == LA_FORM_CHUNKED ? la::gdn_mfma_varlen_workspace_bytes(B, H, T) : varlen_table_bytes(B);
@@ -471,6 +472,90 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
     if (e != hipSuccess) return LA_ERR_HIP;
     return from_hip(la::launch_recurrent(la::kGatedDelta, dtype, N * H, T_total, dk, dv, q, k, v, alpha, beta, S0,
                                          S_out, nullptr, nullptr, o, s, pk));
+}
+
+la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total, int dk, int dv,
+                                  const int* cu_seqlens, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, const float* S0, const float* z0, void* o,
+                                  float* S_out, float* z_out, int snap_interval, int snap_count, float* S_snap,
+                                  float* z_snap, int form, int chunk, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+    if (kind != LA_KIND_NORMALIZED && kind != LA_KIND_GATED_DELTA && kind != LA_KIND_GATED && kind != LA_KIND_KDA)
+        return LA_ERR_ARG;
+    const bool has_z = kind == LA_KIND_NORMALIZED;
+    if (!has_z && (z0 != nullptr || z_out != nullptr || z_snap != nullptr)) return LA_ERR_ARG;
+    if (kind == LA_KIND_GATED_DELTA)
+        return gdn_prefill_varlen(dtype, N, H, T_total, dk, dv, cu_seqlens, q, k, v, alpha, beta, S0, o, S_out,
+                                  snap_interval, snap_count, S_snap, form, chunk, workspace, ws_bytes, stream);
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return LA_ERR_ARG;
+    if (kind == LA_KIND_NORMALIZED && (alpha != nullptr || beta != nullptr)) return LA_ERR_ARG;
+    if (kind == LA_KIND_GATED && beta != nullptr) return LA_ERR_ARG;
+    if (!sizes_ok(N, H, T_total) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
+    if (static_cast<long long>(T_total) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
+    if (snap_interval < 0 || snap_count < 0) return LA_ERR_SHAPE;
+    if (form == LA_FORM_CHUNKED) return valid_chunk(chunk) ? LA_ERR_UNSUPPORTED : LA_ERR_SHAPE;
+    if (N == 0 || H == 0) return LA_OK;
+    if (cu_seqlens == nullptr) return LA_ERR_NULL;
+    if (T_total > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr)) return LA_ERR_NULL;
+    if (T_total > 0 && kind != LA_KIND_NORMALIZED && alpha == nullptr) return LA_ERR_NULL;
+    if (T_total > 0 && kind == LA_KIND_KDA && beta == nullptr) return LA_ERR_NULL;
+    const bool snaps = snap_interval > 0 && snap_count > 0 && S_snap != nullptr;
+    if (snap_interval > 0 && snap_count > 0 && S_snap == nullptr) return LA_ERR_NULL;
+    if (snaps && has_z && z_snap == nullptr) return LA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return LA_ERR_ALIGN;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(alpha),
+                          static_cast<const void*>(beta), static_cast<const void*>(S0), static_cast<const void*>(z0),
+                          static_cast<const void*>(S_out), static_cast<const void*>(z_out),
+                          static_cast<const void*>(S_snap), static_cast<const void*>(z_snap),
+                          static_cast<const void*>(workspace)})
+        if (p != nullptr && !aligned16(p)) return LA_ERR_ALIGN;
+    const size_t es = io_size(dtype);
+    const size_t rows = static_cast<size_t>(H) * T_total;
+    const size_t nS = static_cast<size_t>(N) * H * dv * dk * sizeof(float);
+    const size_t nz = static_cast<size_t>(N) * H * dk * sizeof(float);
+    const size_t nsnap = snaps ? static_cast<size_t>(snap_count) * H * dv * dk * sizeof(float) : 0;
+    const size_t nzsnap = snaps && has_z ? static_cast<size_t>(snap_count) * H * dk * sizeof(float) : 0;
+    const size_t na = rows * (kind == LA_KIND_KDA ? dk : 1) * sizeof(float);
+    const Span in[] = {{q, rows * dk * es}, {k, rows * dk * es}, {v, rows * dv * es}, {alpha, na},
+                       {beta, rows * sizeof(float)}, {S0, nS}, {z0, nz},
+                       {cu_seqlens, (static_cast<size_t>(N) + 1) * sizeof(int)}};
+    const Span outs[] = {{o, rows * dv * es}, {S_out, nS}, {z_out, has_z ? nz : 0}, {S_snap, nsnap},
+                         {z_snap, nzsnap}};
+    for (const Span& a : outs) {
+        for (const Span& b : in) {
+            if (a.p == S_out && b.p == S0 && S_out == S0) continue;   // in-place state update
+            if (a.p == z_out && b.p == z0 && z_out == z0) continue;
+            if (overlaps(a, b)) return LA_ERR_ARG;
+        }
+        for (const Span& b : outs)
+            if (&a != &b && overlaps(a, b)) return LA_ERR_ARG;
+    }
+    const size_t need = varlen_table_bytes(N);
+    if (workspace == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
+    {
+        const Span w{workspace, need};
+        for (const Span& b : in)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+        for (const Span& b : outs)
+            if (overlaps(w, b)) return LA_ERR_ARG;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int* tab = static_cast<int*>(workspace);
+    la::Packed pk;
+    pk.cu = cu_seqlens;
+    pk.snap_base = tab + (N + 1);
+    pk.H = H;
+    pk.Ttot = T_total;
+    pk.snap = snaps ? snap_interval : 0;
+    pk.snap_cap = snap_count;
+    pk.S_snap = snaps ? S_snap : nullptr;
+    pk.z_snap = snaps && has_z ? z_snap : nullptr;
+    const hipError_t e = la::launch_varlen_table(N, T_total, 1, pk.snap, cu_seqlens, tab, s);
+    if (e != hipSuccess) return LA_ERR_HIP;
+    const int k_kind = kind == LA_KIND_GATED ? la::kGated : kind == LA_KIND_KDA ? la::kKda : la::kNormalized;
+    return from_hip(la::launch_recurrent(k_kind, dtype, N * H, T_total, dk, dv, q, k, v, alpha, beta, S0, S_out,
+                                         has_z ? z0 : nullptr, has_z ? z_out : nullptr, o, s, pk));
 }
 
 la_status kda_prefill(int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k, const void* v,

@@ -26,6 +26,7 @@ struct Packed {
     const int* snap_base = nullptr;
     int H = 0, Ttot = 0, snap = 0, snap_cap = 0;
     float* S_snap = nullptr;
+    float* z_snap = nullptr;   // normalised kind: z at the same positions as S_snap
 };
 hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int dv,
                             const void* q, const void* k, const void* v,

@@ -257,6 +257,13 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
                     const int r = rg + RG * j;
                     if (r < DV) store_state8(dst + static_cast<size_t>(r) * DK, c0, c1, s[j]);
                 }
+                if constexpr (KIND == kNormalized) {
+                    if (rg == 0 && pk.z_snap != nullptr) {   // every lane group holds the same z
+                        float* zp = pk.z_snap + (static_cast<size_t>(js) * pk.H + hh) * DK;
+                        *reinterpret_cast<float4*>(zp + c0) = make_float4(z[0], z[1], z[2], z[3]);
+                        *reinterpret_cast<float4*>(zp + c1) = make_float4(z[4], z[5], z[6], z[7]);
+                    }
+                }
             }
         }
     }

@@ -68,7 +68,8 @@ enum {
     LA_FN_DECODE_STEP = 2,
     LA_FN_GLA_PREFILL = 3,
     LA_FN_KDA_PREFILL = 4,
-    LA_FN_GDN_VARLEN = 5   /* B = number of sequences, T = total tokens */
+    LA_FN_GDN_VARLEN = 5,  /* B = number of sequences, T = total tokens */
+    LA_FN_PREFILL_VARLEN = 6  /* lin_attn_prefill_varlen; sizes as for 5 */
 };
 
 /*
@@ -272,6 +273,69 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
                              int snap_interval, int snap_count, float* S_snap,
                              int form, int chunk,
                              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * lin_attn_prefill_varlen - a packed batch of N sequences of different
+ * lengths, with state snapshots for prefix reuse, for every kind of
+ * recurrence in this library.
+ *
+ * kind picks the recurrence each sequence runs on its own tokens from its own
+ * state, the same equations as the uniform entry points:
+ *   LA_KIND_NORMALIZED  - lin_attn_prefill (section "Three forms of one
+ *                         computation"); state (S, z); alpha, beta NULL;
+ *   LA_KIND_GATED       - gla_prefill (section "Memory must forget: decay and
+ *                         gates"); alpha [H, T_total] float32; beta NULL;
+ *   LA_KIND_KDA         - kda_prefill (section "Delta rule and Gated
+ *                         DeltaNet", KDA); alpha [H, T_total, dk] and beta
+ *                         [H, T_total] float32;
+ *   LA_KIND_GATED_DELTA - forwards to gdn_prefill_varlen (same arguments;
+ *                         z0, z_out and z_snap must be NULL).
+ * Section "Honest talk: why MiniMax went back to full attention" names prefix
+ * caching (reusing the work done for a shared beginning of different
+ * requests) as missing from many implementations; for these layers the
+ * reusable part of a prefix is the state (S, and z for the normalised kind),
+ * which this call can save at regular positions.
+ * Layout (device pointers, 16-byte aligned unless stated):
+ *   cu_seqlens [N+1] int32, 4-byte aligned: sequence n is tokens
+ *     cu_seqlens[n] .. cu_seqlens[n+1] (non-decreasing from 0 to T_total;
+ *     values outside [0, T_total] are clamped, so a bad table gives wrong
+ *     results but no access outside the buffers);
+ *   q, k [H, T_total, dk]; v, o [H, T_total, dv] (every head holds all the
+ *     sequences back to back);
+ *   S0, S_out [N, H, dv, dk] and (normalised kind) z0, z_out [N, H, dk]
+ *     float32; S0/z0 NULL = zeros; S_out may be S0 and z_out may be z0;
+ *     other kinds: z0, z_out, z_snap must be NULL (LA_ERR_ARG);
+ *   snapshots: when snap_interval > 0 and S_snap is not NULL, the state of
+ *     sequence n after p tokens, for every positive multiple p of
+ *     snap_interval up to its length, is written to
+ *     S_snap[base_n + p / snap_interval - 1] ([snap_count, H, dv, dk]
+ *     float32) and, for the normalised kind, z_snap[same slot]
+ *     ([snap_count, H, dk] float32, then required), with base_n = sum over
+ *     m < n of len_m / snap_interval; slots at or past snap_count are not
+ *     written.
+ * form: LA_FORM_RECURRENT (token by token, state in registers; any supported
+ * dtype and size).  LA_FORM_CHUNKED is implemented for LA_KIND_GATED_DELTA
+ * only (see gdn_prefill_varlen); for the other kinds it returns
+ * LA_ERR_UNSUPPORTED.  The recurrent form costs one pass over the tokens per
+ * sequence and head, token-serial in each: it suits the short and mid-length
+ * sequences of a serving batch, not single sequences of many thousands of
+ * tokens (use the uniform chunked entry points there).
+ * workspace/ws_bytes: at least la_workspace_bytes(LA_FN_PREFILL_VARLEN,
+ * dtype, N, H, T_total, dk, dv, form, chunk) bytes (the snapshot table is
+ * built on the device, so the host never reads cu_seqlens); it must not
+ * overlap any other argument.  Any overlap between outputs, or between an
+ * output and an input other than the in-place state pairs, is LA_ERR_ARG.
+ */
+la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total, int dk, int dv,
+                                  const int* cu_seqlens,
+                                  const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta,
+                                  const float* S0, const float* z0,
+                                  void* o, float* S_out, float* z_out,
+                                  int snap_interval, int snap_count,
+                                  float* S_snap, float* z_snap,
+                                  int form, int chunk,
+                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * kda_prefill - Kimi Delta Attention over T tokens: the gated delta rule with

@@ -264,3 +264,37 @@ def varlen_batch(seed, lens, H, dk, dv, dtype):
             q[h, s0:s0 + L], k[h, s0:s0 + L], v[h, s0:s0 + L], a[h, s0:s0 + L], b[h, s0:s0 + L] = \
                 gdn_head(seed, n, h, L, dk, dv, dtype)
     return q, k, v, a, b, cu
+
+
+def varlen_kind_batch(seed, kind, lens, H, dk, dv, dtype, scale=1.0):
+    """A packed batch for one kind of recurrence: q, k, v [H, T_total, d];
+    alpha ([H, T_total] for "gated", [H, T_total, dk] for "kda", else None);
+    beta ([H, T_total] for "kda", else None); cu_seqlens [N+1] int32.
+    Sequence n, head h holds the inputs the uniform generators draw for batch
+    index n, head h (la_head for "normalized", gdn_head for "gated",
+    kda_head for "kda")."""
+    lens = [int(x) for x in lens]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = np.empty((H, T, dk), np.float32)
+    k = np.empty((H, T, dk), np.float32)
+    v = np.empty((H, T, dv), np.float32)
+    a = None if kind == "normalized" else np.empty((H, T, dk) if kind == "kda" else (H, T), np.float32)
+    b = np.empty((H, T), np.float32) if kind == "kda" else None
+    for n, L in enumerate(lens):
+        s = slice(int(cu[n]), int(cu[n]) + L)
+        for h in range(H):
+            if kind == "normalized":
+                q[h, s], k[h, s], v[h, s] = la_head(seed, n, h, L, dk, dv, dtype, scale)
+            elif kind == "gated":
+                q[h, s], k[h, s], v[h, s], a[h, s], _ = gdn_head(seed, n, h, L, dk, dv, dtype)
+            elif kind == "kda":
+                q[h, s], k[h, s], v[h, s], a[h, s], b[h, s] = kda_head(seed, n, h, L, dk, dv, dtype)
+            else:
+                raise ValueError(kind)
+    return q, k, v, a, b, cu
+
+
+def norm_batch(seed, B, H, dk, scale=1.0):
+    """Carried normalisers z0 [B, H, dk] (norm_head per head)."""
+    return np.stack([[norm_head(seed, b, h, dk, scale) for h in range(H)] for b in range(B)]).astype(np.float32)

@@ -118,6 +118,19 @@ int main() {
     CHECK(gdn_prefill_varlen(LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)), P(1), P(2), P(3), F(5),
                              F(6), nullptr, P(4), nullptr, 100, 4, F(11), 0, 64, P(9), 1 << 30, nullptr),
           LA_ERR_SHAPE);
+    // packed batches of the other kinds: z arguments only for the normalised kind, z snapshots required with S ones
+    CHECK(lin_attn_prefill_varlen(LA_KIND_KDA, LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)), P(1),
+                                  P(2), P(3), F(5), F(6), nullptr, F(12), P(4), nullptr, nullptr, 0, 0, nullptr,
+                                  nullptr, LA_FORM_RECURRENT, 0, P(9), 1 << 30, nullptr), LA_ERR_ARG);
+    CHECK(lin_attn_prefill_varlen(LA_KIND_NORMALIZED, LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)),
+                                  P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, P(4), nullptr, nullptr, 128, 4,
+                                  F(11), nullptr, LA_FORM_RECURRENT, 0, P(9), 1 << 30, nullptr), LA_ERR_NULL);
+    CHECK(lin_attn_prefill_varlen(LA_KIND_GATED, LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)), P(1),
+                                  P(2), P(3), F(5), nullptr, nullptr, nullptr, P(4), nullptr, nullptr, 0, 0, nullptr,
+                                  nullptr, LA_FORM_CHUNKED, 64, P(9), 1 << 30, nullptr), LA_ERR_UNSUPPORTED);
+    CHECK(lin_attn_prefill_varlen(LA_KIND_GATED, LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)), P(1),
+                                  P(2), P(3), F(5), nullptr, nullptr, nullptr, P(4), nullptr, nullptr, 0, 0, nullptr,
+                                  nullptr, LA_FORM_RECURRENT, 0, P(9), 15, nullptr), LA_ERR_WORKSPACE);
     CHECK(gdn_preprocess(LA_BF16, 2, 100, 4, 128, 128, P(1), F(2), F(3), F(4), nullptr, nullptr, P(1), P(6), P(7),
                          F(8), F(9), nullptr), LA_ERR_ARG);
     CHECK(gdn_preprocess_varlen(LA_BF16, 3, 100, 4, 128, 128, nullptr, P(1), F(2), F(3), F(4), nullptr, nullptr, P(5),
@@ -138,6 +151,10 @@ int main() {
                                    nullptr, P(4), nullptr), LA_ERR_HIP);
         CHECK(lin_attn_prefill(LA_BF16, 1, 2, 1000, 128, 128, P(1), P(2), P(3), nullptr, nullptr, P(4), nullptr,
                                nullptr, 0, 64, P(9), 1 << 30, nullptr), LA_ERR_HIP);
+        CHECK(lin_attn_prefill_varlen(LA_KIND_NORMALIZED, LA_BF16, 3, 2, 500, 128, 128,
+                                      static_cast<const int*>(P(10)), P(1), P(2), P(3), nullptr, nullptr, nullptr,
+                                      nullptr, P(4), nullptr, nullptr, 128, 4, F(11), F(12), LA_FORM_RECURRENT, 0,
+                                      P(9), 1 << 30, nullptr), LA_ERR_HIP);
     }
     printf("%d checks, %d failed%s\n", checks, failures, no_device ? " (no device: launches checked)" : "");
     return failures == 0 ? 0 : 1;

@@ -49,7 +49,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["lin_attn_prefill", "gdn_prefill", "gdn_prefill_noalloc", "gla_prefill",
                             "gdn_prefill_prep", "gdn_prefill_scan", "gdn_preprocess", "gdn_preprocess_varlen",
-                            "kda_prefill", "gdn_prefill_varlen", "lin_attn_decode_step", "la_workspace_bytes",
+                            "kda_prefill", "gdn_prefill_varlen", "lin_attn_prefill_varlen",
+                            "lin_attn_decode_step", "la_workspace_bytes",
                             "la_status_str", "la_abi_version"])
 
 
@@ -351,6 +352,62 @@ def test_varlen_validation(lib):
     rec = lib.la_workspace_bytes(VARLEN, F32, 3, 2, 500, 64, 64, RECURRENT, 0)
     assert 0 < rec < need
     assert vl(N=0) == LA_OK
+
+
+def test_varlen_kinds_validation(lib):
+    f = lambda x: None if x is None else (x if isinstance(x, ctypes.c_void_p) else P(x))
+    K_NORM, K_GDN, K_GATED, K_KDA = 0, 1, 2, 3
+    PREFILL_VARLEN = 6
+
+    def vl(kind=K_KDA, dtype=BF16, N=3, H=2, T=500, dk=128, dv=128, cu=10, q=1, k=2, v=3, a=5, b=6, S0=None,
+           z0=None, o=4, S_out=None, z_out=None, snap=0, nsnap=0, S_snap=None, z_snap=None, form=RECURRENT,
+           chunk=64, ws=9, ws_bytes=1 << 40):
+        return lib.lin_attn_prefill_varlen(kind, dtype, N, H, T, dk, dv, f(cu), f(q), f(k), f(v), f(a), f(b), f(S0),
+                                           f(z0), f(o), f(S_out), f(z_out), snap, nsnap, f(S_snap), f(z_snap), form,
+                                           chunk, f(ws), ws_bytes, None)
+
+    assert vl(kind=9) == LA_ERR_ARG
+    assert vl(dtype=7) == LA_ERR_DTYPE
+    assert vl(form=PARALLEL) == LA_ERR_ARG
+    assert vl(form=CHUNKED) == LA_ERR_UNSUPPORTED          # block form: gated delta only
+    assert vl(form=CHUNKED, chunk=48) == LA_ERR_SHAPE
+    assert vl(dk=48) == LA_ERR_SHAPE
+    assert vl(snap=-1) == LA_ERR_SHAPE
+    assert vl(z0=12) == LA_ERR_ARG                         # no normaliser outside the normalised kind
+    assert vl(kind=K_GATED, z_out=12) == LA_ERR_ARG
+    assert vl(kind=K_GDN, z_snap=12) == LA_ERR_ARG
+    assert vl(kind=K_NORM) == LA_ERR_ARG                   # the normalised kind takes no gates
+    assert vl(kind=K_NORM, a=None) == LA_ERR_ARG
+    assert vl(kind=K_GATED) == LA_ERR_ARG                  # ... and the scalar-gated kind no beta
+    assert vl(cu=None) == LA_ERR_NULL
+    assert vl(a=None) == LA_ERR_NULL
+    assert vl(b=None) == LA_ERR_NULL
+    assert vl(kind=K_GATED, b=None, a=None) == LA_ERR_NULL
+    assert vl(o=None) == LA_ERR_NULL
+    assert vl(snap=128, nsnap=4, S_snap=None) == LA_ERR_NULL
+    assert vl(kind=K_NORM, a=None, b=None, snap=128, nsnap=4, S_snap=11) == LA_ERR_NULL   # z snapshots needed
+    assert vl(cu=ctypes.c_void_p(BASE + 10 * GiB + 2)) == LA_ERR_ALIGN
+    assert vl(z_snap=ctypes.c_void_p(BASE + 12 * GiB + 4), kind=K_NORM, a=None, b=None) == LA_ERR_ALIGN
+    assert vl(ws=None) == LA_ERR_WORKSPACE
+    need = lib.la_workspace_bytes(PREFILL_VARLEN, BF16, 3, 2, 500, 128, 128, RECURRENT, 0)
+    assert need == lib.la_workspace_bytes(5, BF16, 3, 2, 500, 128, 128, RECURRENT, 0) > 0
+    assert vl(ws_bytes=need - 1) == LA_ERR_WORKSPACE
+    assert vl(ws=5) == LA_ERR_ARG                          # workspace on top of alpha
+    assert vl(o=10) == LA_ERR_ARG                          # output on top of cu_seqlens
+    assert vl(snap=128, nsnap=4, S_snap=4) == LA_ERR_ARG   # snapshots on top of o
+    # KDA's alpha holds H*T*dk floats (512 000 bytes here), the scalar gate H*T
+    # (4 000 bytes): an output state 300 000 bytes past alpha overlaps only the first
+    inside = ctypes.c_void_p(BASE + 5 * GiB + 300000)
+    assert vl(S_out=inside) == LA_ERR_ARG
+    assert vl(kind=K_GATED, b=None, S_out=inside, ws=None) == LA_ERR_WORKSPACE
+    # in-place state update is allowed (stopped here by the missing workspace, checked last)
+    assert vl(kind=K_NORM, a=None, b=None, S0=11, S_out=11, z0=12, z_out=12, ws=None) == LA_ERR_WORKSPACE
+    assert vl(kind=K_NORM, a=None, b=None, S_out=12, z_out=12) == LA_ERR_ARG
+    assert vl(kind=K_NORM, a=None, b=None, snap=128, nsnap=4, S_snap=11, z_snap=11) == LA_ERR_ARG
+    # the gated-delta kind forwards to gdn_prefill_varlen (chunked: bf16, d = 128, chunk 64)
+    assert vl(kind=K_GDN, dtype=F32, form=CHUNKED) == LA_ERR_UNSUPPORTED
+    assert vl(N=0) == LA_OK
+    assert vl(H=0) == LA_OK
 
 
 def test_preprocess_varlen_validation(lib):

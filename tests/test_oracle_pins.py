@@ -786,7 +786,7 @@ VARLEN_MUTATIONS = [
     ("S = None if S0 is None else np.asarray(S0[n, h], dtype=np.float64)", "S = None"),
     ("return sum((cu[n + 1] - cu[n]) // snap_interval for n in range(len(cu) - 1))",
      "return (cu[-1] - cu[0]) // snap_interval"),
-    ("states.append(S.copy())", "states.append(np.zeros_like(S))"),
+    ("else S.copy(),", "else np.zeros_like(S),"),
 ]
 
 
@@ -794,3 +794,115 @@ VARLEN_MUTATIONS = [
 def test_planted_varlen_mistake_is_caught(old, new):
     ns = types.SimpleNamespace(**_mutant(vl_mod, old, new))
     assert _fails_some_pin(ns, [pin_varlen])
+
+
+def _kind_inputs(rng, kind, H, Tt, dk, dv, N):
+    q, k = rng.normal(size=(H, Tt, dk)), rng.normal(size=(H, Tt, dk))
+    if kind == "kda":
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(size=(H, Tt, dv))
+    a = b = z0 = None
+    if kind == "gated":
+        a = 1 / (1 + np.exp(-rng.normal(2, 1, (H, Tt))))
+    elif kind == "kda":
+        a = 1 / (1 + np.exp(-rng.normal(2, 1, (H, Tt, dk))))
+        b = 1 / (1 + np.exp(-rng.normal(size=(H, Tt))))
+    S0 = rng.normal(size=(N, H, dv, dk))
+    if kind == "normalized":
+        S0 = np.abs(S0)
+        z0 = rng.uniform(0.5, 2.0, size=(N, H, dk))
+    return q, k, v, a, b, S0, z0
+
+
+def _kind_reference(kind, q, k, v, a, b, S, z):
+    """The kind's pinned single-sequence recurrence on one slice: (O, S, z)."""
+    if kind == "normalized":
+        return oracle.la_recurrent(q, k, v, S, z)
+    if kind == "gated":
+        return oracle.gated_recurrent(q, k, v, a, S) + (None,)
+    return oracle.kda_recurrent(q, k, v, a, b, S) + (None,)
+
+
+def pin_varlen_kinds(ns):
+    """For the normalised, scalar-gated and KDA kinds: packed sequences are
+    independent runs of the kind's own (separately pinned) recurrence on their
+    slices from their own state (S, and z for the normalised kind); a snapshot
+    is the state after that prefix, and resuming from it reproduces the rest
+    of the sequence and its final state."""
+    H, dk, dv, iv = 2, 4, 3, 4
+    lens = [9, 0, 4, 13, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    Tt = int(cu[-1])
+    for seed, kind in enumerate(("normalized", "gated", "kda")):
+        rng = np.random.default_rng(60 + seed)
+        q, k, v, a, b, S0, z0 = _kind_inputs(rng, kind, H, Tt, dk, dv, len(lens))
+        o, S, z, snaps, zsnaps = ns.packed_varlen(kind, q, k, v, cu, a, b, S0, z0, snap_interval=iv)
+        assert snaps.shape[0] == ns.snapshot_count(cu, iv) == sum(L // iv for L in lens)
+        assert (z is None) == (kind != "normalized") and (zsnaps is None) == (kind != "normalized")
+        sl = lambda x, h, s, e: None if x is None else x[h, s:e]
+        j = 0
+        for n, L in enumerate(lens):
+            s, e = cu[n], cu[n + 1]
+            for h in range(H):
+                zi = None if z0 is None else z0[n, h]
+                o_ref, S_ref, z_ref = _kind_reference(kind, q[h, s:e], k[h, s:e], v[h, s:e], sl(a, h, s, e),
+                                                      sl(b, h, s, e), S0[n, h], zi)
+                assert np.abs(o[h, s:e] - o_ref).max(initial=0) < 1e-12
+                assert np.abs(S[n, h] - S_ref).max() < 1e-12
+                if kind == "normalized":
+                    assert np.abs(z[n, h] - z_ref).max() < 1e-12
+            for p in range(iv, L + 1, iv):
+                for h in range(H):
+                    zi = None if z0 is None else z0[n, h]
+                    _, S_p, z_p = _kind_reference(kind, q[h, s:s + p], k[h, s:s + p], v[h, s:s + p],
+                                                  sl(a, h, s, s + p), sl(b, h, s, s + p), S0[n, h], zi)
+                    assert np.abs(snaps[j, h] - S_p).max() < 1e-12
+                    zs = None
+                    if kind == "normalized":
+                        assert np.abs(zsnaps[j, h] - z_p).max() < 1e-12
+                        zs = zsnaps[j, h]
+                    # prefix caching: the tail from the snapshot gives the same outputs and end state
+                    o_t, S_t, z_t = _kind_reference(kind, q[h, s + p:e], k[h, s + p:e], v[h, s + p:e],
+                                                    sl(a, h, s + p, e), sl(b, h, s + p, e), snaps[j, h], zs)
+                    assert np.abs(o_t - o[h, s + p:e]).max(initial=0) < 1e-12
+                    assert np.abs(S_t - S[n, h]).max() < 1e-12
+                    if kind == "normalized":
+                        assert np.abs(z_t - z[n, h]).max() < 1e-12
+                j += 1
+        if kind != "gated":
+            # the chunk-form evaluation agrees (the scalar-gated kind has none here)
+            o_c, S_c, z_c, sn_c, zs_c = ns.packed_varlen(kind, q, k, v, cu, a, b, S0, z0, iv, form="chunked")
+            assert np.abs(o_c - o).max() < 1e-9 and np.abs(S_c - S).max() < 1e-9 and np.abs(sn_c - snaps).max() < 1e-9
+            if kind == "normalized":
+                assert np.abs(z_c - z).max() < 1e-12 and np.abs(zs_c - zsnaps).max() < 1e-12
+        # without an initial state every sequence starts from zero
+        o0, S0z, z0z, sn0, _ = ns.packed_varlen(kind, q, k, v, cu, a, b)
+        assert sn0.shape[0] == 0 and np.all(S0z[1] == 0)
+        if kind == "normalized":
+            assert np.all(z0z[1] == 0)
+        o_ref, _, _ = _kind_reference(kind, q[1, 13:26], k[1, 13:26], v[1, 13:26], sl(a, 1, 13, 26),
+                                      sl(b, 1, 13, 26), None, None)
+        assert np.abs(o0[1, 13:26] - o_ref).max() < 1e-12
+
+
+def test_varlen_kinds_pin():
+    pin_varlen_kinds(vl_mod)
+
+
+VARLEN_KIND_MUTATIONS = [
+    ("z = None if (not has_z or z0 is None) else np.asarray(z0[n, h], dtype=np.float64)", "z = None"),
+    ("else z.copy())))", "else np.zeros_like(z))))"),
+    ("A = None if gate is None else gate[h, start:cut]", "A = None if gate is None else gate[h, a:a + cut - start]"),
+    ("B = None if wgt is None else wgt[h, start:cut]", "B = None if wgt is None else wgt[h, a:a + cut - start]"),
+    ("z_fin[n, h] = np.zeros(dk) if z is None else z", "z_fin[n, h] = np.zeros(dk)"),
+    ("kda_recurrent(Q, K, V, A, B, S) + (None,)", "kda_recurrent(Q, K, V, A, B, None) + (None,)"),
+    ("gated_recurrent(Q, K, V, A, S) + (None,)", "gated_recurrent(Q, K, V, A, None) + (None,)"),
+    ("la_recurrent(Q, K, V, S, z)", "la_recurrent(Q, K, V, S, None)"),
+    ("o[h, start:cut], S, z = run(", "o[h, a:a + cut - start], S, z = run("),
+]
+
+
+@pytest.mark.parametrize("old,new", VARLEN_KIND_MUTATIONS, ids=[m[1][:40] for m in VARLEN_KIND_MUTATIONS])
+def test_planted_varlen_kind_mistake_is_caught(old, new):
+    ns = types.SimpleNamespace(**_mutant(vl_mod, old, new))
+    assert _fails_some_pin(ns, [pin_varlen_kinds])
