@@ -41,6 +41,7 @@ SOURCES = {
     "gdn_preprocess": CSRC + "preops.hip",
 }
 COPY_BYTES = 256 << 20
+SETTLE_WORKGROUPS = 64 * 32 * 2   # bench.py settle(): 64 x 32 heads, two workgroups per head
 
 
 def short_name(name):
@@ -49,7 +50,10 @@ def short_name(name):
     return name.split("(")[0].strip()
 
 
-def kernel_key(name, tag):
+def kernel_key(name, tag, wg=None):
+    """Name of a dispatch in the summaries; None for kernels not summarised,
+    among them the bench's clock-settling decode steps (64 sequences x 32
+    heads, 4096 workgroups: `wg`), which are not a measured leg."""
     s = short_name(name)
     base = s.split("<")[0]
     targs = [a.strip() for a in s[len(base) + 1:-1].split(",")] if "<" in s else []
@@ -62,7 +66,9 @@ def kernel_key(name, tag):
         return "gla_combine_kernel" if targs[0] == "true" else "la_combine_kernel"
     if base == "recurrent_kernel" and len(targs) == 6:
         kind = {"0": "normalized", "1": "gated_delta", "2": "gated", "3": "kda"}.get(targs[0], targs[0])
-        return f"recurrent_kernel_{kind}_" + ("decode" if targs[5] == "true" else "recurrent_prefill")
+        if targs[5] != "true":
+            return f"recurrent_kernel_{kind}_recurrent_prefill"
+        return None if wg == SETTLE_WORKGROUPS else f"recurrent_kernel_{kind}_decode"
     if base == "gdn_preprocess_kernel":
         return base + ("_varlen" if targs and targs[-1] == "true" else "")
     if base in ("kda_tile_kernel", "kda_scan_kernel"):
@@ -122,7 +128,7 @@ def trace_durations(d, tag):
         us = (int(col(r, "End_Timestamp")) - int(col(r, "Start_Timestamp"))) / 1e3
         name = col(r, "Kernel_Name")
         by_name.setdefault(short_name(name), []).append((workgroups(r), us))
-        k = kernel_key(name, tag)
+        k = kernel_key(name, tag, workgroups(r))
         if k:
             by_key.setdefault(k, []).append(us)
     return by_key, by_name
@@ -132,7 +138,7 @@ def counters(d, tag):
     """{key: {counter: [value per dispatch, ...]}} from counter_collection.csv."""
     per = {}
     for r in read_csvs(d, "counter_collection.csv"):
-        k = kernel_key(col(r, "Kernel_Name"), tag)
+        k = kernel_key(col(r, "Kernel_Name"), tag, workgroups(r))
         if not k:
             continue
         disp = col(r, "Dispatch_Id", "Correlation_Id")
@@ -156,9 +162,9 @@ def do_times(a):
         _, by_name = trace_durations(d, tag)
         rows = []
         for name, xs in by_name.items():
-            if kernel_key(name, tag) in (None, "copy"):
-                continue   # torch's own kernels (uploads, input draws) and copies are not part of the path
             for wg in sorted({w for w, _ in xs}):
+                if kernel_key(name, tag, wg) in (None, "copy"):
+                    continue   # torch's own kernels (uploads, input draws), copies, clock settling: not the path
                 us = [u for w, u in xs if w == wg]
                 rows.append((sum(us), name, wg, us))
         for _, name, wg, us in sorted(rows, reverse=True):
