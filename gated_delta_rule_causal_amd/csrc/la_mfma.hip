@@ -40,6 +40,8 @@
 //     O = diag(e^g) Q S^T + A V,   S <- e^{g_c} S + V^T diag(e^{g_c - g}) K
 // and a segment's contribution is (decay m = e^{sum of log alpha}, dS), with
 // entering states P_{s+1} = m_s P_s + dS_s.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -202,11 +204,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // ---- stage phi(Q), phi(K), phi(K)^T, V^T (padded rows stay zero: phi is
         //      applied only to real tokens, so they add nothing to A, S or z);
         //      GATED: Q, K, (e^{g_c - g} K)^T, V^T
+        // (a whole chunk, the usual case, takes a copy of the loop without the
+        // row masks: len is uniform over the workgroup)
+        auto stage = [&](auto whole) {
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int e = tid + kThreads * it;
             const int row = e >> 4, c8 = 8 * (e & 15);
-            const bool real = row < len;
+            const bool real = decltype(whole)::value || row < len;
             const uint32_t wq[4] = {rq[it].x, rq[it].y, rq[it].z, rq[it].w};
             const uint32_t wk[4] = {rk[it].x, rk[it].y, rk[it].z, rk[it].w};
             float xq[8], xk[8];
@@ -228,6 +233,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
             *reinterpret_cast<uint4*>(&Vs[row][c8]) = real ? rv[it] : make_uint4(0, 0, 0, 0);
         }
+        };
+        if (len == C)
+            stage(std::true_type{});
+        else
+            stage(std::false_type{});
         if constexpr (GATED) {
             if (n + 1 < n1) fetch(n + 1);
         } else {
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * m + 4 * g + i;
-                const float rden = GATED ? 1.f : 1.f / dens[row];
+                const float rden = GATED ? 1.f : __builtin_amdgcn_rcpf(dens[row]);
                 Vs[row][32 * w + r] = f32_to_bf16_bits(acc[0][i] * rden);
                 Vs[row][32 * w + 16 + r] = f32_to_bf16_bits(acc[1][i] * rden);
             }
