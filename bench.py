@@ -16,10 +16,12 @@ sample of the prefill workload.  Prints one JSON line.
 
 Every leg's inputs are drawn and uploaded first; then the GPU runs about 0.3 s
 of untimed work and the timed parts of the legs follow back to back, the
-headline prefill last: every figure is taken at settled clocks, as in a
-serving process (an idle GPU lowers its clocks, and the first milliseconds of
-work after an idle gap run slower).  `--legs` runs a subset (e.g. one
-leg under a profiler); the legs not run are null in the JSON line.
+headline prefill last (the memory-bound decode legs first, the long-context
+prefill right before the headline, and that leg after three untimed calls):
+every figure is taken at settled clocks, as in a serving process (an idle GPU
+lowers its clocks, and the first milliseconds of work after an idle gap run
+slower).  `--legs` runs a subset (e.g. one leg under a profiler); the legs not
+run are null in the JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 are launched on (torch's current stream, which the binding passes to the C
@@ -51,7 +53,7 @@ KDA_DECODE = "kda_decode_256x32"
 KDA_PREFILL = "kda_bf16_2x16x8192"
 VARLEN = "gdn_varlen_bf16_16seq_16k"
 LONG = "gdn_bf16_1x16x262144"
-LEGS = ["la", "gla", "preops", "decode", "long", "kda_decode", "kda_prefill", "varlen", "prefill", "copy"]
+LEGS = ["decode", "kda_decode", "la", "gla", "preops", "kda_prefill", "varlen", "long", "prefill", "copy"]
 
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
@@ -279,7 +281,7 @@ def leg_long(c):
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=c.dev)
     yield
     ms = c.timed(n, lambda i: gd.gdn_prefill(q, k, v, a, b, form="chunked", chunk=64, out=out, S_out=S, workspace=ws),
-                 warm=1)
+                 warm=3)
     nbytes = B * H * T * path_bytes_per_head_token(d)
     return {"workload": "gated delta prefill B=1 H=16 T=262144 d=128 chunk=64, bf16 I/O, fp32 state (inputs drawn "
                         "on the device)", "calls": n, "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
@@ -503,7 +505,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=24.0,
                     help="oracle time of the CPU baseline, summed over its processes")
     ap.add_argument("--la-steps", type=int, default=10, help="timed calls of each secondary prefill leg")
-    ap.add_argument("--long-calls", type=int, default=2, help="timed calls of the 1 x 16 x 262144 prefill")
+    ap.add_argument("--long-calls", type=int, default=4, help="timed calls of the 1 x 16 x 262144 prefill")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed GPU work before the first leg, so that every leg runs at settled clocks")
     ap.add_argument("--legs", default="all",
