@@ -53,7 +53,12 @@ namespace {
 
 constexpr int C = 64;        // chunk length
 constexpr int D = 128;       // d_k = d_v
-constexpr int LDQ = D + 8;   // bf16 row stride of 128-wide LDS tiles (272 B)
+// bf16 row stride of 128-wide LDS tiles (304 B).  Measured on gfx950 LDS: any
+// stride of 136 u16 or more (16-byte multiple, not a power of two) serves the
+// 16-row x 16-byte operand reads at full rate; 152 also halves the bank
+// conflicts of the transposing reads of K in the state update (the four
+// column groups of a lane quad are 16 bytes apart there).
+constexpr int LDQ = D + 24;
 constexpr int LDA = C + 8;   // bf16 row stride of 64-wide LDS tiles (144 B)
 constexpr int kThreads = 512;                 // 8 waves per workgroup
 constexpr int kTargetBlocks = 256;            // workgroups that fill the chip (one per CU)
