@@ -418,7 +418,7 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
     if (form == LA_FORM_CHUNKED) {
         if (!valid_chunk(chunk)) return LA_ERR_SHAPE;
         if (!la::gdn_mfma_supported(dtype, dk, dv, chunk)) return LA_ERR_UNSUPPORTED;
-        if (snap_interval % chunk != 0) return LA_ERR_SHAPE;
+        if (snap_interval % la::kMfmaChunk != 0) return LA_ERR_SHAPE;
     }
     if (N == 0 || H == 0) return LA_OK;
     if (cu_seqlens == nullptr) return LA_ERR_NULL;

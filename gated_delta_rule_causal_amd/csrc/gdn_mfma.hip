@@ -1250,7 +1250,8 @@ hipError_t gdn_scratch(void** out) {
 }
 
 bool gdn_mfma_supported(int dtype, int dk, int dv, int chunk) {
-    return dtype == kBF16 && dk == D && dv == D && chunk == C;
+    static_assert(C == kMfmaChunk, "the matrix-core kernels share one block length");
+    return dtype == kBF16 && dk == D && dv == D && mfma_chunk_ok(chunk);
 }
 
 size_t gdn_mfma_workspace_bytes(int B, int H, int T, int, int, int) {

@@ -591,7 +591,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(int BH, int T, i
 }  // namespace
 
 bool kda_mfma_supported(int dtype, int dk, int dv, int chunk) {
-    return dtype == kBF16 && dk == D && dv == D && chunk == C;
+    static_assert(C == kMfmaChunk, "the matrix-core kernels share one block length");
+    return dtype == kBF16 && dk == D && dv == D && mfma_chunk_ok(chunk);
 }
 
 size_t kda_mfma_workspace_bytes(int B, int H, int T) {

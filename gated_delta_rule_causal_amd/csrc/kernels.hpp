@@ -11,6 +11,14 @@ namespace la {
 
 enum Kind { kNormalized = 0, kGatedDelta = 1, kGated = 2, kKda = 3 };
 enum Dtype { kF32 = 0, kBF16 = 1 };
+// Block length of every matrix-core chunk kernel (bf16, d_k = d_v = 128).
+// They serve any requested chunk length: the chunk form's result does not
+// depend on the block length beyond rounding, and smaller blocks would only
+// leave the matrix cores idler.
+constexpr int kMfmaChunk = 64;
+__host__ __device__ inline bool mfma_chunk_ok(int chunk) {
+    return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128;
+}
 
 // ---- token-by-token recurrence, one block per head (recurrent.hip) --------
 // heads = B*H (or N*H for a decode step); T >= 1.  q,k [heads,T,dk];

@@ -51,7 +51,7 @@ namespace {
 
 constexpr int C = 64;
 constexpr int D = 128;
-constexpr int LDR = D + 8;   // row-major [C][LDR] bf16 tiles (272-B rows)
+constexpr int LDR = D + 24;  // row-major [C][LDR] bf16 tiles (304-B rows: see the gated-delta kernels)
 constexpr int LDT = C + 8;   // 64-wide [C][LDT] bf16 tiles (144-B rows)
 constexpr int kThreads = 256;
 constexpr int kItems = C * D / 8 / kThreads;  // 16-byte loads per thread per tile
@@ -518,7 +518,8 @@ Plan make_plan(int BH, int T) {
 }  // namespace
 
 bool la_mfma_supported(int dtype, int dk, int dv, int chunk) {
-    return dtype == kBF16 && dk == D && dv == D && chunk == C;
+    static_assert(C == kMfmaChunk, "the matrix-core kernels share one block length");
+    return dtype == kBF16 && dk == D && dv == D && mfma_chunk_ok(chunk);
 }
 
 size_t la_mfma_workspace_bytes(int B, int H, int T, int, int, int) {

@@ -33,6 +33,16 @@
  *    B, H, N >= 0 and T >= 0 (a zero-sized call copies the carried state to
  *    the output state and returns LA_OK).  Combinations that are valid but
  *    not implemented return LA_ERR_UNSUPPORTED.
+ *  - Chunk length.  The chunked form gives the same result for every block
+ *    length up to rounding, so `chunk` is a performance choice.  bf16 with
+ *    dk = dv = 128 runs on the matrix-core kernels, which always use 64-token
+ *    blocks, whatever valid chunk is asked for.  Every other shape runs on
+ *    fp32 kernels with the requested block length and ONE workgroup per head;
+ *    they suit small heads and few tokens, and are slow at large head sizes:
+ *    measured on MI355X for B=2, H=16, T=8192, dk = dv = 128, those kernels
+ *    (fp32 activations, chunk 32) take about 180 ms for
+ *    gdn_prefill and 97 ms for lin_attn_prefill, against 0.19 ms and 0.13 ms
+ *    on the matrix cores and 7 ms for the gated delta rule's recurrent form.
  */
 #ifndef LINATTN_H
 #define LINATTN_H
@@ -112,8 +122,9 @@ la_status lin_attn_prefill(int dtype, int B, int H, int T, int dk, int dv,
  * alpha [B,H,T] float32 holds gate values (a constant alpha is the decay
  * equation itself).  S_0 = S0 (zeros when NULL).  form:
  *   LA_FORM_RECURRENT - token by token, any supported dtype and sizes;
- *   LA_FORM_CHUNKED   - block form, bf16 with dk = dv = 128 and chunk 64
- *                       (other shapes: LA_ERR_UNSUPPORTED).
+ *   LA_FORM_CHUNKED   - block form, bf16 with dk = dv = 128 (64-token
+ *                       blocks for any valid chunk; other shapes:
+ *                       LA_ERR_UNSUPPORTED).
  * Outputs o [B,H,T,dv] and, when not NULL, S_out [B,H,dv,dk] (may be the
  * same pointer as S0).  workspace/ws_bytes: at least
  * la_workspace_bytes(LA_FN_GLA_PREFILL, ...) bytes, not overlapping any
@@ -180,7 +191,8 @@ la_status gdn_prefill_noalloc(int dtype, int B, int H, int T, int dk, int dv,
 /*
  * gdn_prefill_prep / gdn_prefill_scan - the two halves of gdn_prefill with
  * LA_FORM_CHUNKED on the matrix-core path (dtype LA_BF16, dk = dv = 128,
- * chunk = 64; other shapes return LA_ERR_UNSUPPORTED).  Same equation and
+ * any valid chunk (64-token blocks); other shapes return
+ * LA_ERR_UNSUPPORTED).  Same equation and
  * section as gdn_prefill.  The library cuts each head's sequence into
  * segments of whole chunks (so that the chip is filled even with few heads);
  * over a segment the recurrence is an affine map of the entering state.
@@ -258,8 +270,9 @@ la_status lin_attn_decode_step(int kind, int dtype, int N, int H, int dk, int dv
  *     S_snap[base_n + p / snap_interval - 1] ([snap_count, H, dv, dk]
  *     float32), base_n = sum over m < n of len_m / snap_interval; slots at or
  *     past snap_count are not written.
- * form: LA_FORM_CHUNKED (bf16, dk = dv = 128, chunk 64; snap_interval a
- * multiple of the chunk) or LA_FORM_RECURRENT (any supported dtype and size).
+ * form: LA_FORM_CHUNKED (bf16, dk = dv = 128, any valid chunk: 64-token
+ * blocks; snap_interval a multiple of 64) or LA_FORM_RECURRENT (any
+ * supported dtype and size, snapshots at any interval).
  * workspace/ws_bytes: at least la_workspace_bytes(LA_FN_GDN_VARLEN, dtype, N,
  * H, T_total, dk, dv, form, chunk) bytes (the segment table is built on the
  * device, so the host never reads cu_seqlens); it must not overlap any
@@ -352,8 +365,9 @@ la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total
  * form:
  *   LA_FORM_RECURRENT - token by token, any supported dtype and sizes;
  *   LA_FORM_CHUNKED   - block form on the matrix cores, bf16 with
- *                       dk = dv = 128 and chunk 64 (other shapes:
- *                       LA_ERR_UNSUPPORTED).  alpha must lie in (0, 1].
+ *                       dk = dv = 128 (64-token blocks for any valid
+ *                       chunk; other shapes: LA_ERR_UNSUPPORTED).  alpha
+ *                       must lie in (0, 1].
  * Outputs o [B,H,T,dv] and, when not NULL, S_out [B,H,dv,dk] (may be the
  * same pointer as S0; any other overlap is LA_ERR_ARG).  workspace/ws_bytes:
  * at least la_workspace_bytes(LA_FN_KDA_PREFILL, ...) bytes (0 for the

@@ -204,7 +204,7 @@ def test_split_gdn_validation(lib):
 
     assert prep(dtype=F32) == LA_ERR_UNSUPPORTED
     assert prep(dk=64, dv=64) == LA_ERR_UNSUPPORTED
-    assert prep(chunk=32) == LA_ERR_UNSUPPORTED
+    assert prep(chunk=32, ws=None) == LA_ERR_WORKSPACE   # any valid chunk: the kernels' 64-token blocks
     assert prep(chunk=33) == LA_ERR_SHAPE
     assert prep(ws=None) == LA_ERR_WORKSPACE
     assert prep(ws_bytes=1000) == LA_ERR_WORKSPACE

@@ -51,7 +51,7 @@ def test_la_fp32_small_workload(gd, form):
 
 @pytest.mark.parametrize("dtype,dk,dv,T,C", [
     ("f32", 64, 64, 1000, 64), ("f32", 32, 128, 77, 16), ("bf16", 128, 64, 300, 32),
-    ("f32", 128, 128, 130, 32), ("bf16", 16, 16, 1, 16)])
+    ("f32", 128, 128, 130, 32), ("bf16", 16, 16, 1, 16), ("f32", 32, 32, 300, 128), ("bf16", 16, 64, 257, 128)])
 def test_la_chunked_generic_with_state(gd, dtype, dk, dv, T, C):
     q, k, v = la_inputs(7, 2, 3, T, dk, dv, dtype, scale=0.5)
     S0 = synth.state_batch(8, 2, 3, dk, dv, 0.3) ** 2
@@ -107,7 +107,8 @@ def test_gdn_recurrent_with_state(gd, dtype, dk, dv, T):
 
 @pytest.mark.parametrize("dtype,dk,dv,T,C,amean", [
     ("f32", 64, 64, 1000, 64, 3.0), ("f32", 32, 32, 333, 16, 6.0), ("f32", 16, 128, 129, 64, 1.0),
-    ("bf16", 64, 64, 500, 32, 3.0), ("f32", 128, 128, 200, 32, 6.0)])
+    ("bf16", 64, 64, 500, 32, 3.0), ("f32", 128, 128, 200, 32, 6.0), ("f32", 32, 32, 300, 128, 3.0),
+    ("bf16", 16, 16, 257, 128, 1.0)])
 def test_gdn_chunked_generic(gd, dtype, dk, dv, T, C, amean):
     q, k, v, a, b = gdn_inputs(14, 1, 3, T, dk, dv, dtype, alpha_mean=amean)
     S0 = synth.state_batch(15, 1, 3, dk, dv, 0.2)
@@ -246,3 +247,27 @@ def test_determinism_and_edge_cases(gd):
                           S0=to_host(S0))
     report("T=1 o", slice_err(to_host(o), o_ref), TOL["f32"])
     report("T=1 S", slice_err(to_host(S), S_ref), TOL["f32"])
+
+
+# ------------------------------------ matrix-core path at any chunk length
+@pytest.mark.parametrize("C", [16, 32, 128])
+def test_matrix_core_path_serves_every_chunk_length(gd, C):
+    """bf16 with d = 128 runs on the matrix-core kernels (64-token blocks)
+    whatever valid chunk is asked for; the chunk form is exact for any block
+    length, so the oracle's chunk form at the requested C is the reference
+    (states at the bf16 bar: the matrix-core state products take bf16
+    operands)."""
+    T = 200
+    q, k, v = la_inputs(16, 1, 2, T, 128, 128, "bf16", scale=0.1)
+    o_ref, S_ref, z_ref = ob.lin_attn(q, k, v, form="chunked", chunk=C)
+    o, S, z = gd.lin_attn_prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), form="chunked", chunk=C)
+    report(f"la matrix-core C={C} o", slice_err(to_host(o), o_ref), TOL["bf16"])
+    report("  S", slice_err(to_host(S), S_ref), TOL["bf16"])
+    report("  z", slice_err(to_host(z), z_ref), TOL["bf16"])
+    q, k, v, a, b = gdn_inputs(17, 1, 2, T, 128, 128, "bf16", alpha_mean=3.0)
+    S0 = synth.state_batch(18, 1, 2, 128, 128, 0.2)
+    o_ref, S_ref = ob.gdn(q, k, v, a, b, form="chunked", chunk=C, S0=S0)
+    o, S = gd.gdn_prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(a, "f32"), to_dev(b, "f32"),
+                          to_dev(S0, "f32"), form="chunked", chunk=C)
+    report(f"gdn matrix-core C={C} o", slice_err(to_host(o), o_ref), TOL["bf16"])
+    report("  S", slice_err(to_host(S), S_ref), TOL["bf16"])
