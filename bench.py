@@ -505,7 +505,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=24.0,
                     help="oracle time of the CPU baseline, summed over its processes")
     ap.add_argument("--la-steps", type=int, default=10, help="timed calls of each secondary prefill leg")
-    ap.add_argument("--long-calls", type=int, default=4, help="timed calls of the 1 x 16 x 262144 prefill")
+    ap.add_argument("--long-calls", type=int, default=8, help="timed calls of the 1 x 16 x 262144 prefill")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed GPU work before the first leg, so that every leg runs at settled clocks")
     ap.add_argument("--legs", default="all",
