@@ -96,3 +96,18 @@ def long_sample_positions(seed, h, T, C, n=4096, boundaries=32):
     for c in rng.integers(1, nc, size=boundaries).tolist():
         pos.update((c * C - 1, c * C))
     return np.array(sorted(p for p in pos if 0 <= p < T), dtype=np.int64)
+
+
+def decode_step_inputs(seed, N, H, dk, dv, step):
+    """Token inputs of one decode step (synth.decode_token_inputs, entry =
+    step) as the device wants them: q, k, v as bf16 bit patterns (uint16),
+    alpha and beta float32.  Runs in a worker process (no GPU, no torch)."""
+    import synth
+    q, k, v, a, b = synth.decode_token_inputs(seed, N, H, dk, dv, "bf16", step)
+    bits = [(np.ascontiguousarray(x).view(np.uint32) >> 16).astype(np.uint16) for x in (q, k, v)]
+    return step, bits, a, b
+
+
+def bf16_bits_to_f32(bits):
+    """uint16 bf16 bit patterns -> float32 values."""
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)

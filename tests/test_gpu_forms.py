@@ -155,41 +155,56 @@ def test_decode_normalized_small(gd, dtype, dk, dv):
     report("  z", slice_err(to_host(tz).reshape(N * H, dk), z_ref, 1), TOL["f32"])
 
 
+@pytest.mark.timeout(600)
 def test_decode_workload_full_size(gd):
-    """256 sequences x 32 heads, d = 128, bf16 token inputs, fp32 state N(0, 0.02^2):
-    every head checked after step 1; a seeded sample of 256 heads checked on
-    every one of 1000 steps (outputs) and at the end (state)."""
+    """256 sequences x 32 heads, d = 128, bf16 token inputs, fp32 state N(0, 0.02^2),
+    1000 steps with fresh token inputs every step (drawn on the host by worker
+    processes, in step order): every head checked after step 1; a seeded
+    sample of 256 heads checked on every step (outputs) and at the end
+    (state)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
     import torch
+    from gpu_helpers import bf16_bits_to_f32, decode_step_inputs
+
     w = synth.WORKLOADS["gdn_decode_256x32"]
-    N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], w["steps"]
-    pool = 16
-    S0 = synth.decode_state_fast(w["seed"], N, H, dk, dv, w["state_std"])
+    N, H, dk, dv, steps, seed = w["N"], w["H"], w["dk"], w["dv"], w["steps"], w["seed"]
+    S0 = synth.decode_state_fast(seed, N, H, dk, dv, w["state_std"])
     tS = to_dev(S0, "f32")
-    toks = [synth.decode_token_inputs(w["seed"], N, H, dk, dv, "bf16", e) for e in range(pool)]
-    dev_toks = [tuple(to_dev(x, "bf16") for x in t[:3]) + tuple(to_dev(x, "f32") for x in t[3:]) for t in toks]
     rng = np.random.default_rng(4242)
     sample = np.sort(rng.choice(N * H, size=256, replace=False))
     idx = torch.from_numpy(sample).to(tS.device)
     S_s = S0.reshape(N * H, dv, dk)[sample].astype(np.float64)
     out = torch.empty((N, H, dv), dtype=torch.bfloat16, device=tS.device)
+    up_bits = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(tS.device)
     worst = 0.0
-    for s in range(steps):
-        q, k, v, a, b = dev_toks[s % pool]
-        gd.lin_attn_decode_step("gated_delta", q, k, v, tS, alpha=a, beta=b, out=out)
-        hq, hk, hv, ha, hb = (x.reshape(N * H, -1) if x.ndim == 3 else x.reshape(N * H) for x in toks[s % pool])
-        if s == 0:
-            o_all, S1 = ob.gdn_step_heads(hq, hk, hv, ha, hb, S0.reshape(N * H, dv, dk))
-            report("decode full step 1: all heads o", slice_err(to_host(out).reshape(N * H, dv), o_all, 1),
-                   TOL["bf16"])
-            report("decode full step 1: all heads S", slice_err(to_host(tS).reshape(N * H, dv, dk), S1, 1),
-                   TOL["f32"])
-            del S1
-        o_s, S_s = ob.gdn_step_heads(hq[sample], hk[sample], hv[sample], ha[sample], hb[sample], S_s)
-        got = to_host(out.reshape(N * H, dv).index_select(0, idx))
-        worst = max(worst, slice_err(got, o_s, 1))
-    report("decode full: sampled heads o, worst over 1000 steps", worst, TOL["bf16"])
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=8, mp_context=ctx) as ex:
+        draws = ex.map(decode_step_inputs, [seed] * steps, [N] * steps, [H] * steps, [dk] * steps, [dv] * steps,
+                       range(steps), chunksize=4)
+        for s, (step, (bq, bk, bv), ha, hb) in enumerate(draws):
+            assert step == s
+            gd.lin_attn_decode_step("gated_delta", up_bits(bq), up_bits(bk), up_bits(bv), tS,
+                                    alpha=torch.from_numpy(ha).to(tS.device), beta=torch.from_numpy(hb).to(tS.device),
+                                    out=out)
+            hq, hk, hv = (bf16_bits_to_f32(x).reshape(N * H, -1) for x in (bq, bk, bv))
+            ha, hb = ha.reshape(N * H), hb.reshape(N * H)
+            if s == 0:
+                o_all, S1 = ob.gdn_step_heads(hq, hk, hv, ha, hb, S0.reshape(N * H, dv, dk))
+                report("decode full step 1: all heads o", slice_err(to_host(out).reshape(N * H, dv), o_all, 1),
+                       TOL["bf16"])
+                report("decode full step 1: all heads S", slice_err(to_host(tS).reshape(N * H, dv, dk), S1, 1),
+                       TOL["f32"])
+                del S1
+            o_s, S_s = ob.gdn_step_heads(hq[sample], hk[sample], hv[sample], ha[sample], hb[sample], S_s)
+            got = to_host(out.reshape(N * H, dv).index_select(0, idx))
+            worst = max(worst, slice_err(got, o_s, 1))
+            if s % 250 == 249:
+                print(f"[parity] decode full: step {s + 1} of {steps}", flush=True)
+    report(f"decode full: sampled heads o, worst over {steps} steps", worst, TOL["bf16"])
     got_S = to_host(tS.reshape(N * H, dv, dk).index_select(0, idx))
-    report("decode full: sampled heads S after 1000 steps", slice_err(got_S, S_s, 1), TOL["f32"])
+    report(f"decode full: sampled heads S after {steps} steps", slice_err(got_S, S_s, 1), TOL["f32"])
 
 
 # --------------------------------------------------------- cross-form checks
