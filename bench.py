@@ -438,6 +438,12 @@ def leg_prefill(c):
                         step_ms, step_kernels)
     roof["launches_ms"] = {"gdn_prefill_prep": prep_ms, "gdn_prefill_scan": scan_ms}
     roof["segments_per_head"] = G
+    # The HBM roofline is the one that bounds this path (its intensity, 136
+    # flop/B, is below the chip's ridge); what holds the step below it is the
+    # serial chain of 64-token chunks inside each segment: per chunk, the
+    # state carriers' matrix-core groups, operand conversions and barriers.
+    roof["limiter"] = ("latency of the per-chunk chain in each segment (MFMA busy "
+                       + (f"{pmc['busy_frac']:.0%}" if pmc else "n/a") + " by counters)")
     return {"elapsed": elapsed, "ms_per_step": elapsed * 1e3 / args.steps,
             "tokens_per_s": B * T * args.steps / elapsed, "roofline": roof,
             "mfma": {"algorithmic_flops_per_step": alg_flops, "achieved_TFLOPs": tflops,
