@@ -54,7 +54,7 @@ def slice_err(x, r, lead=2):
     diff = np.abs(xs - rs)
     num = diff.max(axis=1)
     den = np.abs(rs).max(axis=1)
-    big = np.abs(rs) >= 1e-3 * den[:, None]
+    big = (np.abs(rs) >= 1e-3 * den[:, None]) & (np.abs(rs) > 0)
     _median["value"] = float(np.median(diff[big] / np.abs(rs[big]))) if big.any() else 0.0
     den = np.where(den == 0, 1.0, den)
     return float((num / den).max())
