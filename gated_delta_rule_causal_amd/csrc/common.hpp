@@ -66,12 +66,28 @@ struct IoBF16 {
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // --------------------------------------------------------- wave reductions
+// x plus the x of another lane of its 16-lane row chosen by a DPP control.
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
 // Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
-// every lane of the group receives the group sum.
+// every lane of the group receives the group sum, bitwise the same in every
+// lane.  Up to 16 lanes (one DPP row) the partial sums move by DPP, which
+// stays in the VALU: lane pairs (quad_perm 1,0,3,2), then quad halves
+// (2,3,0,1), then the mirrored quad of each 8-lane half and the mirrored half
+// of the row; each step adds two equal-sized partial sums, so every lane ends
+// with the same value (addition commutes).  Wider groups continue with
+// cross-row shuffles.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
+    if constexpr (G >= 2) x = dpp_sum<0xb1>(x);    // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) x = dpp_sum<0x4e>(x);    // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) x = dpp_sum<0x141>(x);   // row_half_mirror
+    if constexpr (G >= 16) x = dpp_sum<0x140>(x);  // row_mirror
 #pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    for (int off = 16; off < G; off <<= 1) x += __shfl_xor(x, off, kWave);
     return x;
 }
 

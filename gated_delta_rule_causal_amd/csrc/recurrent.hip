@@ -75,6 +75,97 @@ __device__ __forceinline__ void load_slice(const typename IO::T* p, size_t base,
     IO::load4(p, base + c1, out + 4);
 }
 
+// A block of TB tokens of one head's inputs in LDS: k, q [TB][DK], v [TB][DV]
+// (DV <= 128), the gates (alpha [TB] or, per key channel, [TB][DK]; beta
+// [TB]).  The workgroup copies a block cooperatively in 16-byte pieces: load()
+// issues the global loads of block tokens t0 .. t0+TB-1 into registers, and
+// store() writes them to LDS; rows past the sequence's end (Tn tokens) are
+// neither read nor written.  Every token row of k, q, v and of a per-channel
+// alpha is a whole number of 16-byte pieces (DK, DV >= 16), contiguous in
+// global memory and in LDS.
+template <int KIND, class IO, int DK>
+struct Stage {
+    static constexpr int TB = 16;
+    using E = typename IO::T;
+    static constexpr int KA = KIND == kKda ? DK : 1;
+    struct Tiles {
+        E k[TB * DK], q[TB * DK], v[TB * 128];
+        float a[TB * KA], b[TB];
+    };
+    static constexpr int KROW = DK * static_cast<int>(sizeof(E)) / 16;    // pieces per row of k, q
+    static constexpr int KPT = (TB * KROW + kThreads - 1) / kThreads;       // pieces per thread
+    static constexpr int VPT = (TB * 128 * static_cast<int>(sizeof(E)) / 16 + kThreads - 1) / kThreads;
+    static constexpr int AROW = KA * 4 / 16;                                 // per-channel alpha only
+    static constexpr int APT = KIND == kKda ? (TB * AROW + kThreads - 1) / kThreads : 0;
+    struct Regs {
+        uint4 k[KPT], q[KPT], v[VPT], a[APT > 0 ? APT : 1];
+        float as, bs;
+    };
+    static __device__ __forceinline__ void load(Regs& r, const E* q, const E* k, const E* v, const float* alpha,
+                                                const float* beta, size_t tok0, int t0, int Tn, int DV) {
+        const int tid = threadIdx.x, nt = min(TB, Tn - t0), vrow = DV * static_cast<int>(sizeof(E)) / 16;
+        const char* kb = reinterpret_cast<const char*>(k + (tok0 + t0) * DK);
+        const char* qb = reinterpret_cast<const char*>(q + (tok0 + t0) * DK);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int p = tid + i * kThreads;
+            if (p < nt * KROW) {
+                r.k[i] = *reinterpret_cast<const uint4*>(kb + 16 * static_cast<size_t>(p));
+                r.q[i] = *reinterpret_cast<const uint4*>(qb + 16 * static_cast<size_t>(p));
+            }
+        }
+        const char* vb = reinterpret_cast<const char*>(v + (tok0 + t0) * DV);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int p = tid + i * kThreads;
+            if (p < nt * vrow) r.v[i] = *reinterpret_cast<const uint4*>(vb + 16 * static_cast<size_t>(p));
+        }
+        if constexpr (KIND == kKda) {
+            const char* ab = reinterpret_cast<const char*>(alpha + (tok0 + t0) * DK);
+#pragma unroll
+            for (int i = 0; i < APT; ++i) {
+                const int p = tid + i * kThreads;
+                if (p < nt * AROW) r.a[i] = *reinterpret_cast<const uint4*>(ab + 16 * static_cast<size_t>(p));
+            }
+        }
+        if constexpr (KIND == kGated || KIND == kGatedDelta) {
+            if (tid < nt) r.as = alpha[tok0 + t0 + tid];
+        }
+        if constexpr (KIND == kGatedDelta || KIND == kKda) {
+            if (tid < nt) r.bs = beta[tok0 + t0 + tid];
+        }
+    }
+    static __device__ __forceinline__ void store(const Regs& r, Tiles& s, int t0, int Tn, int DV) {
+        const int tid = threadIdx.x, nt = min(TB, Tn - t0), vrow = DV * static_cast<int>(sizeof(E)) / 16;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int p = tid + i * kThreads;
+            if (p < nt * KROW) {
+                reinterpret_cast<uint4*>(s.k)[p] = r.k[i];
+                reinterpret_cast<uint4*>(s.q)[p] = r.q[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int p = tid + i * kThreads;
+            if (p < nt * vrow) reinterpret_cast<uint4*>(s.v)[p] = r.v[i];
+        }
+        if constexpr (KIND == kKda) {
+#pragma unroll
+            for (int i = 0; i < APT; ++i) {
+                const int p = tid + i * kThreads;
+                if (p < nt * AROW) reinterpret_cast<uint4*>(s.a)[p] = r.a[i];
+            }
+        }
+        if constexpr (KIND == kGated || KIND == kGatedDelta) {
+            if (tid < nt) s.a[tid] = r.as;
+        }
+        if constexpr (KIND == kGatedDelta || KIND == kKda) {
+            if (tid < nt) s.b[tid] = r.bs;
+        }
+    }
+};
+
 template <int KIND, class IO, int DK, int R, int SPLIT, bool ONE>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     int T, int DV, const typename IO::T* __restrict__ q, const typename IO::T* __restrict__ k,
@@ -128,22 +219,52 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
         }
     }
 
-    // ---- token inputs, prefetched one token ahead
+    // ---- token inputs, prefetched one token ahead.  The decode step reads
+    // them from global memory; the prefill stages blocks of TB tokens through
+    // LDS (Stage below), so the wait for HBM is paid once per block, not once
+    // per token of the serial chain.
     float kn[8], qn[8], vn[R], an = 1.f, bn = 0.f, avn[8];
+    using St = Stage<KIND, IO, DK>;
+    __shared__ __attribute__((aligned(16))) typename St::Tiles st[ONE ? 1 : 2];
+    typename St::Regs sr;
     auto fetch = [&](int t) {
-        const size_t tk = (tok0 + t) * DK;
-        const size_t tv = (tok0 + t) * DV;
-        load_slice<IO>(k, tk, c0, c1, kn);
-        load_slice<IO>(q, tk, c0, c1, qn);
-        if constexpr (KIND == kKda) load_slice<IoF32>(alpha, tk, c0, c1, avn);
+        if constexpr (ONE) {
+            const size_t tk = (tok0 + t) * DK;
+            const size_t tv = (tok0 + t) * DV;
+            load_slice<IO>(k, tk, c0, c1, kn);
+            load_slice<IO>(q, tk, c0, c1, qn);
+            if constexpr (KIND == kKda) load_slice<IoF32>(alpha, tk, c0, c1, avn);
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const int r = rg + RG * j;
-            vn[j] = r < DV ? IO::load(v, tv + r) : 0.f;
+            for (int j = 0; j < R; ++j) {
+                const int r = rg + RG * j;
+                vn[j] = r < DV ? IO::load(v, tv + r) : 0.f;
+            }
+            if constexpr (KIND == kGated || KIND == kGatedDelta) an = alpha[tok0 + t];
+            if constexpr (KIND == kGatedDelta || KIND == kKda) bn = beta[tok0 + t];
+        } else {
+            const typename St::Tiles& b = st[(t / St::TB) & 1];
+            const int tl = t % St::TB;
+            load_slice<IO>(b.k, static_cast<size_t>(tl) * DK, c0, c1, kn);
+            load_slice<IO>(b.q, static_cast<size_t>(tl) * DK, c0, c1, qn);
+            if constexpr (KIND == kKda) load_slice<IoF32>(b.a, static_cast<size_t>(tl) * DK, c0, c1, avn);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int r = rg + RG * j;
+                vn[j] = r < DV ? IO::load(b.v, static_cast<size_t>(tl) * DV + r) : 0.f;
+            }
+            if constexpr (KIND == kGated || KIND == kGatedDelta) an = b.a[tl];
+            if constexpr (KIND == kGatedDelta || KIND == kKda) bn = b.b[tl];
         }
-        if constexpr (KIND == kGated || KIND == kGatedDelta) an = alpha[tok0 + t];
-        if constexpr (KIND == kGatedDelta || KIND == kKda) bn = beta[tok0 + t];
     };
+    if constexpr (!ONE) {
+        // block 0 into LDS, block 1 in flight in registers
+        if (Tn > 0) {
+            St::load(sr, q, k, v, alpha, beta, tok0, 0, Tn, DV);
+            St::store(sr, st[0], 0, Tn, DV);
+            __syncthreads();
+            if (Tn > St::TB) St::load(sr, q, k, v, alpha, beta, tok0, St::TB, Tn, DV);
+        }
+    }
     if (ONE || Tn > 0) fetch(0);
 
     const int steps = ONE ? 1 : Tn;  // ONE: the decode step (T = 1), no prefetch path
@@ -158,7 +279,19 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 #pragma unroll
         for (int j = 0; j < R; ++j) vc[j] = vn[j];
         const float a = an, b = bn;
-        if (!ONE && t + 1 < Tn) fetch(t + 1);
+        if constexpr (!ONE) {
+            if (t + 1 < Tn) {
+                if ((t + 1) % St::TB == 0) {
+                    // next block: registers -> LDS (the copy it replaces was last
+                    // read before the previous block's barrier), then the block
+                    // after it into registers
+                    St::store(sr, st[((t + 1) / St::TB) & 1], t + 1, Tn, DV);
+                    __syncthreads();
+                    if (t + 1 + St::TB < Tn) St::load(sr, q, k, v, alpha, beta, tok0, t + 1 + St::TB, Tn, DV);
+                }
+                fetch(t + 1);
+            }
+        }
         const size_t to = (tok0 + t) * DV;
 
         if constexpr (KIND == kGated) {
@@ -296,10 +429,15 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
     constexpr int RG = RowSlice<DK>::RG;
     // Kinds without a shared normaliser split a head's rows over 2 blocks;
     // a token-serial prefill over few heads splits further (up to 8 blocks
-    // of at least one row group each) so that about 512 blocks run.
+    // of at least one row group each) so that about 512 blocks run, and a
+    // packed batch always splits as far as it can: its longest sequence runs
+    // on after the others have finished, and fewer rows per wave shorten
+    // that sequence's per-token chain.
     int split = (KIND != kNormalized && dv >= 2 * RG) ? 2 : 1;
     if (!ONE && split == 2)
-        while (split < 8 && dv >= 2 * split * RG && static_cast<long long>(heads) * split < 512) split *= 2;
+        while (split < 8 && dv >= 2 * split * RG &&
+               (pk.cu != nullptr || static_cast<long long>(heads) * split < 512))
+            split *= 2;
     const int R = (dv / split + RG - 1) / RG;
     dim3 grid(static_cast<unsigned>(heads) * split), block(kThreads);
     auto args = [&](auto kern) {
