@@ -27,10 +27,13 @@
 // them over lane groups: LPR = dk/8 lanes per row, 8 fp32 state elements per
 // lane held as two float4 (columns [4l, 4l+4) and [dk/2 + 4l, dk/2 + 4l + 4)
 // for lane l of the group, so one load instruction covers 256 contiguous
-// bytes of a row).  Dot products reduce over the LPR lanes with xor-shuffles.
-// The gated-delta kind cuts each head's rows in two blocks (twice the blocks,
-// half the registers); the normalised kind keeps one block per head because
-// every row needs the shared normaliser z, which is updated in place.
+// bytes of a row).  Dot products reduce over the LPR lanes by DPP.  The
+// kinds without a normaliser cut each head's rows over two or more blocks
+// (more blocks, fewer registers); the normalised kind does so only when z is
+// not updated in place: every block then keeps its own copy of z (it depends
+// on k alone) and the block holding row 0 writes it, while an in-place z
+// (always so in the decode step) needs one block per head, so that no block
+// can overwrite z before another has read it.
 // The state is touched exactly once per call, so its loads and stores carry
 // the nontemporal hint: the decode step streams the whole state through HBM
 // and nothing it moves is reused by the next kernel.
@@ -174,7 +177,6 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     typename IO::T* __restrict__ o, Packed pk) {
     constexpr int LPR = RowSlice<DK>::LPR;
     constexpr int RG = RowSlice<DK>::RG;
-    static_assert(KIND != kNormalized || SPLIT == 1, "z is shared by all rows of a head");
     const int head = blockIdx.x / SPLIT;   // state index (packed: sequence * H + head)
     // token rows of this head: [head][T] (uniform) or tokens cu[n].. of row
     // block h of [H][Ttot] (packed batch)
@@ -427,13 +429,14 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
                      const float* z0, float* z_out, void* o, const Packed& pk, hipStream_t stream) {
     using E = typename IO::T;
     constexpr int RG = RowSlice<DK>::RG;
-    // Kinds without a shared normaliser split a head's rows over 2 blocks;
-    // a token-serial prefill over few heads splits further (up to 8 blocks
+    // A head's rows go to 2 blocks (the normalised kind: only when z is not
+    // updated in place); a token-serial prefill over few heads splits further (up to 8 blocks
     // of at least one row group each) so that about 512 blocks run, and a
     // packed batch always splits as far as it can: its longest sequence runs
     // on after the others have finished, and fewer rows per wave shorten
     // that sequence's per-token chain.
-    int split = (KIND != kNormalized && dv >= 2 * RG) ? 2 : 1;
+    const bool z_in_place = KIND == kNormalized && (ONE || (z0 != nullptr && z0 == z_out));
+    int split = (!z_in_place && dv >= 2 * RG) ? 2 : 1;
     if (!ONE && split == 2)
         while (split < 8 && dv >= 2 * split * RG &&
                (pk.cu != nullptr || static_cast<long long>(heads) * split < 512))
@@ -446,7 +449,7 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
                            S_out, z0, z_out, static_cast<E*>(o), pk);
         return hipGetLastError();
     };
-    if constexpr (KIND != kNormalized) {
+    {
         if (split == 2) {
             switch (R) {
                 case 1: return args(recurrent_kernel<KIND, IO, DK, 1, 2, ONE>);
