@@ -84,6 +84,36 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// ======================================================== geometry
+// Where the chunks of a call live: a uniform batch (BH heads of T tokens, NC
+// chunks each, record of chunk n of head bh at bh * NC + n) or a packed batch
+// (cu != nullptr: N sequences back to back in every one of H heads of Ttot
+// tokens; chunk_base[n] = chunks of the sequences before n, built on the
+// device; the record of chunk j of sequence n in head h at
+// h * cap + chunk_base[n] + j, cap bounding the total chunk count).
+struct KGeo {
+    int BH, T, NC;
+    const int* cu;
+    const int* chunk_base;
+    const int* snap_base;
+    int N, H, Ttot, cap;
+    int snap, snap_cap;   // snapshots of P after every `snap` tokens (a multiple of C), slots below snap_cap
+    float* S_snap;
+};
+
+__device__ __forceinline__ int kclamp(int t, int Ttot) { return t < 0 ? 0 : t > Ttot ? Ttot : t; }
+
+// Sequence of global chunk gc of a packed batch (chunk_base non-decreasing,
+// chunk_base[0] = 0 <= gc < chunk_base[N]).
+__device__ __forceinline__ int chunk_seq(const KGeo& g, int gc) {
+    int lo = 0, hi = g.N;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.chunk_base[mid] <= gc) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 // ======================================================== tile pass
 // LDS of the tile pass, about 79 KiB so that two workgroups share a CU (one
 // loads its chunk while the other computes).  The raw k, v, q pieces and the
@@ -116,20 +146,33 @@ struct TileSmem {
 };
 static_assert(sizeof(TileSmem) <= 80 * 1024, "two tile workgroups per CU");
 
-__global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(int BH, int T, int NC,
-                                                                const u16* __restrict__ q, const u16* __restrict__ k,
+__global__ __launch_bounds__(kTileThreads) void kda_tile_kernel(KGeo geo, const u16* __restrict__ q,
+                                                                const u16* __restrict__ k,
                                                                 const u16* __restrict__ v,
                                                                 const float* __restrict__ alpha,
                                                                 const float* __restrict__ beta,
                                                                 unsigned char* __restrict__ ws) {
     __shared__ __attribute__((aligned(16))) TileSmem sm;
-    const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
-    if (bh >= BH) return;
+    int len;
+    size_t row0;   // first token row of the chunk
+    unsigned char* rec;
+    if (geo.cu == nullptr) {
+        const int bh = blockIdx.x / geo.NC, n = blockIdx.x % geo.NC;
+        if (bh >= geo.BH) return;
+        len = min(C, geo.T - n * C);
+        row0 = static_cast<size_t>(bh) * geo.T + n * C;
+        rec = ws + (static_cast<size_t>(bh) * geo.NC + n) * kRecord;
+    } else {
+        const int h = blockIdx.x % geo.H, gc = blockIdx.x / geo.H;
+        if (gc >= geo.chunk_base[geo.N] || gc >= geo.cap) return;
+        const int sq = chunk_seq(geo, gc), j = gc - geo.chunk_base[sq];
+        const int t0 = kclamp(geo.cu[sq], geo.Ttot), t1 = kclamp(geo.cu[sq + 1], geo.Ttot);
+        len = min(C, (t1 > t0 ? t1 - t0 : 0) - j * C);
+        if (len <= 0) return;   // an empty sequence counts one chunk in the table and has none
+        row0 = static_cast<size_t>(h) * geo.Ttot + t0 + static_cast<size_t>(j) * C;
+        rec = ws + (static_cast<size_t>(h) * geo.cap + gc) * kRecord;
+    }
     const int tid = threadIdx.x;
-    const int t0 = n * C;
-    const int len = min(C, T - t0);
-    const size_t row0 = static_cast<size_t>(bh) * T + t0;   // first token row of the chunk
-    unsigned char* rec = ws + (static_cast<size_t>(bh) * NC + n) * kRecord;
 
     // Thread (tb, cg) owns tokens 4 tb .. 4 tb + 3 and channels 8 cg .. 8 cg + 7
     // of every per-token tile: 16 threads cover one 256-byte row of k, v, q.
@@ -533,15 +576,37 @@ __device__ __forceinline__ void scan_chunk(ScanSmem& sm, const ChunkOps& op, f32
         *reinterpret_cast<uint2*>(o + (orow + 16 * w + orw) * D + 16 * cb + ocl) = orow_bits;
 }
 
-__global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(int BH, int T, int NC,
-                                                                const unsigned char* __restrict__ ws,
+__global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(KGeo geo, const unsigned char* __restrict__ ws,
                                                                 const float* S0, u16* __restrict__ o, float* S_out) {
     __shared__ __attribute__((aligned(16))) ScanSmem sm;
     // the 8 column blocks of a head take block indices 8 apart (one XCD)
     const int i = blockIdx.x;
-    const int bh = (i >> 6) * 8 + (i & 7);
+    const int bh = (i >> 6) * 8 + (i & 7);   // head (uniform) or sequence * H + head (packed)
     const int cb = (i >> 3) & 7;
-    if (bh >= BH) return;
+    int T, NC, hh = 0, snap0 = 0;
+    const unsigned char* rec0;
+    size_t orow;
+    if (geo.cu == nullptr) {
+        if (bh >= geo.BH) return;
+        T = geo.T;
+        NC = geo.NC;
+        rec0 = ws + static_cast<size_t>(bh) * NC * kRecord;
+        orow = static_cast<size_t>(bh) * T;
+    } else {
+        if (bh >= geo.N * geo.H) return;
+        const int sq = bh / geo.H;
+        hh = bh - sq * geo.H;
+        const int t0 = kclamp(geo.cu[sq], geo.Ttot), t1 = kclamp(geo.cu[sq + 1], geo.Ttot);
+        T = t1 > t0 ? t1 - t0 : 0;
+        // a table that is not non-decreasing can promise more chunks than the
+        // workspace holds: those are never read
+        const int base = geo.chunk_base[sq];
+        NC = min((T + C - 1) / C, min(geo.chunk_base[sq + 1], geo.cap) - base);
+        if (NC < 0) NC = 0;
+        rec0 = ws + (static_cast<size_t>(hh) * geo.cap + base) * kRecord;
+        orow = static_cast<size_t>(hh) * geo.Ttot + t0;
+        snap0 = geo.snap_base ? geo.snap_base[sq] : 0;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, gg = lane >> 4;
@@ -558,17 +623,29 @@ __global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(int BH, int T, i
             make_uint2(pack2(x.x, x.y), pack2(x.z, x.w));
     }
     __syncthreads();
-    const unsigned char* rec0 = ws + static_cast<size_t>(bh) * NC * kRecord;
-    const size_t orow = static_cast<size_t>(bh) * T;
     // tiles of chunks n+1 and n+2 are in flight while chunk n runs (three
     // register sets in rotation; indices past the end reload the last chunk)
     ChunkOps a, b, c;
     auto rec = [&](int m) { return rec0 + static_cast<size_t>(min(m, NC - 1)) * kRecord; };
     auto run = [&](const ChunkOps& op, int m) {
         scan_chunk(sm, op, P, w, r, gg, o, orow + static_cast<size_t>(m) * C, min(C, T - m * C), cb);
+        // packed batches: the state after every geo.snap tokens
+        const int end = (m + 1) * C;
+        if (geo.snap > 0 && end <= T && end % geo.snap == 0) {
+            const int js = snap0 + end / geo.snap - 1;
+            if (js < geo.snap_cap) {
+                float* dst = geo.S_snap + (static_cast<size_t>(js) * geo.H + hh) * D * D;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    *reinterpret_cast<float4*>(dst + static_cast<size_t>(16 * cb + r) * D + 32 * w + 16 * mt +
+                                               4 * gg) = make_float4(P[mt][0], P[mt][1], P[mt][2], P[mt][3]);
+            }
+        }
     };
-    load_ops(a, rec(0), w, cb, r, gg);
-    load_ops(b, rec(1), w, cb, r, gg);
+    if (NC > 0) {
+        load_ops(a, rec(0), w, cb, r, gg);
+        load_ops(b, rec(1), w, cb, r, gg);
+    }
     int n = 0;
     for (; n + 3 <= NC; n += 3) {   // no branches around the chunks: the wait counts stay exact
         load_ops(c, rec(n + 2), w, cb, r, gg);
@@ -600,21 +677,63 @@ size_t kda_mfma_workspace_bytes(int B, int H, int T) {
     return static_cast<size_t>(B) * H * ((T + C - 1) / C) * kRecord;
 }
 
+hipError_t kda_launch(const KGeo& g, int tile_blocks, int scan_items, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
+                      unsigned char* ws, hipStream_t stream) {
+    hipLaunchKernelGGL(kda_tile_kernel, dim3(static_cast<unsigned>(tile_blocks)), dim3(kTileThreads), 0, stream, g,
+                       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), alpha, beta,
+                       ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_scan_kernel, dim3(static_cast<unsigned>((scan_items + 7) / 8) * 64), dim3(kScanThreads), 0,
+                       stream, g, ws, S0, static_cast<u16*>(o), S_out);
+    return hipGetLastError();
+}
+
 hipError_t launch_kda_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                            void* workspace, hipStream_t stream) {
     const int BH = B * H;
     if (BH <= 0 || T <= 0) return hipSuccess;
-    const int NC = (T + C - 1) / C;
-    auto* ws = static_cast<unsigned char*>(workspace);
-    hipLaunchKernelGGL(kda_tile_kernel, dim3(static_cast<unsigned>(BH) * NC), dim3(kTileThreads), 0, stream, BH, T, NC,
-                       static_cast<const u16*>(q), static_cast<const u16*>(k),
-                       static_cast<const u16*>(v), alpha, beta, ws);
-    hipError_t e = hipGetLastError();
+    KGeo g{};
+    g.BH = BH;
+    g.T = T;
+    g.NC = (T + C - 1) / C;
+    return kda_launch(g, BH * g.NC, BH, q, k, v, alpha, beta, S0, o, S_out, static_cast<unsigned char*>(workspace),
+                      stream);
+}
+
+// Packed batches: a device-built table (chunk_base, snap_base: [N+1] each)
+// ahead of the records; at most Ttot / C + N chunks per head.
+size_t kda_mfma_varlen_workspace_bytes(int N, int H, int Ttot) {
+    if (N <= 0 || H <= 0) return 0;
+    const size_t table = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    const size_t cap = static_cast<size_t>(Ttot) / C + N;
+    return table + static_cast<size_t>(H) * cap * kRecord;
+}
+
+hipError_t launch_kda_mfma_varlen(int N, int H, int Ttot, const int* cu, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
+                                  int snap, int snap_cap, float* S_snap, void* workspace, hipStream_t stream) {
+    if (N <= 0 || H <= 0) return hipSuccess;
+    const size_t table = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    int* tab = static_cast<int*>(workspace);
+    KGeo g{};
+    g.cu = cu;
+    g.chunk_base = tab;
+    g.snap_base = tab + (N + 1);
+    g.N = N;
+    g.H = H;
+    g.Ttot = Ttot;
+    g.cap = Ttot / C + N;
+    g.snap = S_snap ? snap : 0;
+    g.snap_cap = snap_cap;
+    g.S_snap = S_snap;
+    // chunk_base: one "segment" per chunk (an empty sequence counts one)
+    const hipError_t e = launch_varlen_table(N, Ttot, 1, g.snap, cu, tab, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_scan_kernel, dim3(static_cast<unsigned>((BH + 7) / 8) * 64), dim3(kScanThreads), 0, stream,
-                       BH, T, NC, ws, S0, static_cast<u16*>(o), S_out);
-    return hipGetLastError();
+    return kda_launch(g, g.cap * H, N * H, q, k, v, alpha, beta, S0, o, S_out,
+                      static_cast<unsigned char*>(workspace) + table, stream);
 }
 
 }  // namespace la

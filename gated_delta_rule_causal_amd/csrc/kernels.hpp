@@ -100,6 +100,10 @@ hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
 // a column-parallel scan.  alpha [B,H,T,128] per channel.
 bool kda_mfma_supported(int dtype, int dk, int dv, int chunk);
 size_t kda_mfma_workspace_bytes(int B, int H, int T);
+size_t kda_mfma_varlen_workspace_bytes(int N, int H, int Ttot);
+hipError_t launch_kda_mfma_varlen(int N, int H, int Ttot, const int* cu, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
+                                  int snap, int snap_cap, float* S_snap, void* workspace, hipStream_t stream);
 hipError_t launch_kda_mfma(int B, int H, int T, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                            void* workspace, hipStream_t stream);

@@ -327,16 +327,18 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
  *     m < n of len_m / snap_interval; slots at or past snap_count are not
  *     written.
  * form: LA_FORM_RECURRENT (token by token, state in registers; any supported
- * dtype and size).  LA_FORM_CHUNKED is implemented for LA_KIND_GATED_DELTA
- * only (see gdn_prefill_varlen); for the other kinds it returns
- * LA_ERR_UNSUPPORTED.  The recurrent form costs one pass over the tokens per
- * sequence and head, token-serial in each: it suits the short and mid-length
- * sequences of a serving batch, not single sequences of many thousands of
- * tokens (use the uniform chunked entry points there).
+ * dtype and size; snapshots at any interval) or LA_FORM_CHUNKED, the block
+ * form on the matrix cores for LA_KIND_KDA and LA_KIND_GATED_DELTA (bf16,
+ * dk = dv = 128, any valid chunk: 64-token blocks; snap_interval a multiple
+ * of 64); the chunked form of the normalised and scalar-gated kinds returns
+ * LA_ERR_UNSUPPORTED.  The recurrent form is token-serial within each
+ * sequence: on 16 sequences of mixed lengths (16 384 tokens, the longest
+ * 3551, H = 16, d = 128) it takes 2.4-3.9 ms, against 0.40 ms (KDA) and
+ * 0.19 ms (gated delta) for the block form.
  * workspace/ws_bytes: at least la_workspace_bytes(LA_FN_PREFILL_VARLEN,
- * dtype, N, H, T_total, dk, dv, form, chunk) bytes (the snapshot table is
- * built on the device, so the host never reads cu_seqlens); it must not
- * overlap any other argument.  Any overlap between outputs, or between an
+ * dtype, N, H, T_total, dk, dv, form, chunk) bytes (one size for every kind;
+ * the sequence and snapshot tables are built on the device, so the host
+ * never reads cu_seqlens); it must not overlap any other argument.  Any overlap between outputs, or between an
  * output and an input other than the in-place state pairs, is LA_ERR_ARG.
  */
 la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total, int dk, int dv,
