@@ -137,7 +137,8 @@ size_t la_workspace_bytes(int fn, int dtype, int B, int H, int T, int dk, int dv
             if (form != LA_FORM_CHUNKED && form != LA_FORM_RECURRENT) return bad;
             if (form == LA_FORM_CHUNKED && !la::gdn_mfma_supported(dtype, dk, dv, chunk)) return bad;
             if (form == LA_FORM_RECURRENT) return varlen_table_bytes(B);
-            return std::max(la::gdn_mfma_varlen_workspace_bytes(B, H, T), la::kda_mfma_varlen_workspace_bytes(B, H, T));
+            return std::max({la::gdn_mfma_varlen_workspace_bytes(B, H, T), la::kda_mfma_varlen_workspace_bytes(B, H, T),
+                             la::la_mfma_varlen_workspace_bytes(B, H, T)});
         default:
             return bad;
     }
@@ -500,9 +501,11 @@ la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total
     if (!sizes_ok(N, H, T_total) || !valid_dim(dk) || !valid_dim(dv)) return LA_ERR_SHAPE;
     if (static_cast<long long>(T_total) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
     if (snap_interval < 0 || snap_count < 0) return LA_ERR_SHAPE;
-    if (form == LA_FORM_CHUNKED) {   // the block form: KDA on the matrix cores
+    if (form == LA_FORM_CHUNKED) {   // the block forms, on the matrix cores
         if (!valid_chunk(chunk)) return LA_ERR_SHAPE;
-        if (kind != LA_KIND_KDA || !la::kda_mfma_supported(dtype, dk, dv, chunk)) return LA_ERR_UNSUPPORTED;
+        const bool ok = kind == LA_KIND_KDA ? la::kda_mfma_supported(dtype, dk, dv, chunk)
+                                            : la::la_mfma_supported(dtype, dk, dv, chunk);
+        if (!ok) return LA_ERR_UNSUPPORTED;
         if (snap_interval % la::kMfmaChunk != 0) return LA_ERR_SHAPE;
     }
     if (N == 0 || H == 0) return LA_OK;
@@ -541,8 +544,9 @@ la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total
         for (const Span& b : outs)
             if (&a != &b && overlaps(a, b)) return LA_ERR_ARG;
     }
-    const size_t need = form == LA_FORM_CHUNKED ? la::kda_mfma_varlen_workspace_bytes(N, H, T_total)
-                                                : varlen_table_bytes(N);
+    const size_t need = form != LA_FORM_CHUNKED ? varlen_table_bytes(N)
+                        : kind == LA_KIND_KDA  ? la::kda_mfma_varlen_workspace_bytes(N, H, T_total)
+                                               : la::la_mfma_varlen_workspace_bytes(N, H, T_total);
     if (workspace == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
     {
         const Span w{workspace, need};
@@ -552,10 +556,15 @@ la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total
             if (overlaps(w, b)) return LA_ERR_ARG;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (form == LA_FORM_CHUNKED)
+    if (form == LA_FORM_CHUNKED && kind == LA_KIND_KDA)
         return from_hip(la::launch_kda_mfma_varlen(N, H, T_total, cu_seqlens, q, k, v, alpha, beta, S0, o, S_out,
                                                    snaps ? snap_interval : 0, snap_count, snaps ? S_snap : nullptr,
                                                    workspace, s));
+    if (form == LA_FORM_CHUNKED)
+        return from_hip(la::launch_la_mfma_varlen(kind == LA_KIND_GATED, N, H, T_total, cu_seqlens, q, k, v, alpha,
+                                                  S0, z0, o, S_out, z_out, snaps ? snap_interval : 0, snap_count,
+                                                  snaps ? S_snap : nullptr, snaps && has_z ? z_snap : nullptr,
+                                                  workspace, s));
     int* tab = static_cast<int*>(workspace);
     la::Packed pk;
     pk.cu = cu_seqlens;

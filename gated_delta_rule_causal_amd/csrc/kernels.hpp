@@ -101,6 +101,11 @@ hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
 bool kda_mfma_supported(int dtype, int dk, int dv, int chunk);
 size_t kda_mfma_workspace_bytes(int B, int H, int T);
 size_t kda_mfma_varlen_workspace_bytes(int N, int H, int Ttot);
+size_t la_mfma_varlen_workspace_bytes(int N, int H, int Ttot);
+hipError_t launch_la_mfma_varlen(bool gated, int N, int H, int Ttot, const int* cu, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* S0, const float* z0, void* o,
+                                 float* S_out, float* z_out, int snap, int snap_cap, float* S_snap, float* z_snap,
+                                 void* workspace, hipStream_t stream);
 hipError_t launch_kda_mfma_varlen(int N, int H, int Ttot, const int* cu, const void* q, const void* k, const void* v,
                                   const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                                   int snap, int snap_cap, float* S_snap, void* workspace, hipStream_t stream);

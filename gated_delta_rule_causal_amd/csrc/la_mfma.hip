@@ -17,6 +17,11 @@
 //  * la_combine_kernel: entering states by prefix sums, S0 + dS_0 + ... ;
 //  * la_chunked_mfma_kernel<true> (every segment): outputs from the entering
 //    state, and the final state in the last segment.
+// A packed batch of sequences of different lengths runs the same three
+// kernels with each sequence cut into its own segments: a table built on the
+// device maps a workgroup to (sequence, head, segment), and the output pass
+// also writes state snapshots at whole blocks (S, and z for the normalised
+// kind), since it holds the running state after every block.
 // One workgroup (4 waves) walks the blocks of its segment in order; the
 // kernels are held to 256 registers per lane so that two workgroups share a
 // CU (about 512 segments in flight, one hiding the other's latencies).  Each wave
@@ -58,13 +63,81 @@ constexpr int kItems = C * D / 8 / kThreads;  // 16-byte loads per thread per ti
 constexpr int kTargetBlocks = 512;           // workgroups that fill the chip (two per CU)
 constexpr size_t kMat = static_cast<size_t>(D) * D;
 
-// Workspace record per (head, segment): entering state P (state layout
+// Workspace record per (head, segment) slot: entering state P (state layout
 // [d_v][d_k]) and normaliser zP, then the segment's contributions dS, dz.
 constexpr size_t kRec = 2 * kMat + 2 * D;
-__device__ __forceinline__ size_t ws_P(int bh, int G, int s) { return (static_cast<size_t>(bh) * G + s) * kRec; }
-__device__ __forceinline__ size_t ws_zP(int bh, int G, int s) { return ws_P(bh, G, s) + kMat; }
-__device__ __forceinline__ size_t ws_dS(int bh, int G, int s) { return ws_P(bh, G, s) + kMat + D; }
-__device__ __forceinline__ size_t ws_dz(int bh, int G, int s) { return ws_P(bh, G, s) + 2 * kMat + D; }
+__device__ __forceinline__ size_t ws_P(size_t slot) { return slot * kRec; }
+__device__ __forceinline__ size_t ws_zP(size_t slot) { return ws_P(slot) + kMat; }
+__device__ __forceinline__ size_t ws_dS(size_t slot) { return ws_P(slot) + kMat + D; }
+__device__ __forceinline__ size_t ws_dz(size_t slot) { return ws_P(slot) + 2 * kMat + D; }
+
+// Where the segments of a call live: a uniform batch (BH heads of T tokens,
+// G segments of SEGC chunks each, slot of segment s of head bh at bh G + s),
+// or a packed batch (cu != nullptr: N sequences back to back in each of H
+// heads of Ttot tokens; seg_base[n] = segments of the sequences before n,
+// built on the device; slot of segment s of sequence n in head h at
+// h Gcap + seg_base[n] + s).
+struct LGeo {
+    int BH, T, NC, G, SEGC;
+    const int* cu;
+    const int* seg_base;
+    const int* snap_base;
+    int N, H, Ttot, Gcap;
+    int snap, snap_cap;   // packed: snapshots of (S, z) after every `snap` tokens (a multiple of C)
+    float* S_snap;
+    float* z_snap;
+};
+
+// One (sequence, head, segment) work item.
+struct LItem {
+    size_t head_tok;   // token row of the sequence's first token (this head)
+    size_t slot0;      // slot of the sequence's segment 0
+    size_t state;      // index of the sequence's state in S0 / S_out (and z)
+    int T, G, seg, n0, n1, snap0, h;
+};
+
+__device__ __forceinline__ int lclamp(int t, int Ttot) { return t < 0 ? 0 : t > Ttot ? Ttot : t; }
+
+// The item of workgroup blk: OUT, every segment; else segments 0..G-2 (the
+// last segment's contribution is never needed).  False: nothing to do.
+template <bool PACKED>
+__device__ __forceinline__ bool la_item(const LGeo& g, int blk, bool out, LItem& it) {
+    if constexpr (!PACKED) {
+        const int per = out ? g.G : g.G - 1;
+        const int bh = blk / per;
+        if (bh >= g.BH) return false;
+        it.seg = blk - bh * per;
+        it.G = g.G;
+        it.T = g.T;
+        it.head_tok = static_cast<size_t>(bh) * g.T;
+        it.slot0 = static_cast<size_t>(bh) * g.G;
+        it.state = bh;
+        it.snap0 = 0;
+        it.h = 0;
+    } else {
+        const int h = blk % g.H, gs = blk / g.H;
+        if (gs >= g.seg_base[g.N]) return false;
+        int lo = 0, hi = g.N;   // seg_base[lo] <= gs < seg_base[hi]; every sequence has a segment
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (g.seg_base[mid] <= gs) lo = mid; else hi = mid;
+        }
+        it.seg = gs - g.seg_base[lo];
+        it.G = g.seg_base[lo + 1] - g.seg_base[lo];
+        if (!out && it.seg == it.G - 1) return false;
+        if (g.seg_base[lo + 1] > g.Gcap) return false;   // a bad table never overruns the workspace
+        const int t0 = lclamp(g.cu[lo], g.Ttot), t1 = lclamp(g.cu[lo + 1], g.Ttot);
+        it.T = t1 > t0 ? t1 - t0 : 0;
+        it.head_tok = static_cast<size_t>(h) * g.Ttot + t0;
+        it.slot0 = static_cast<size_t>(h) * g.Gcap + g.seg_base[lo];
+        it.state = static_cast<size_t>(lo) * g.H + h;
+        it.snap0 = g.snap_base ? g.snap_base[lo] : 0;
+        it.h = h;
+    }
+    it.n0 = it.seg * g.SEGC;
+    it.n1 = min((it.T + C - 1) / C, it.n0 + g.SEGC);
+    return true;
+}
 
 __device__ __forceinline__ int perm_row(int t, int rr) {
     return 32 * (t >> 1) + 8 * (rr >> 2) + 4 * (t & 1) + (rr & 3);
@@ -91,11 +164,13 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 
 // OUT = false: segment contributions only (no q, no outputs), from a zero state.
 // GATED: the scalar-gated variant (alpha used, z0/z_out unused).
-template <bool GATED, bool OUT>
+// PACKED: a packed batch (geo.cu set; a copy of the kernel so that the
+// uniform batch carries none of its table lookups).
+template <bool GATED, bool OUT, bool PACKED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void la_chunked_mfma_kernel(
-    int BH, int T, int NC, int G, int SEGC, const u16* __restrict__ q, const u16* __restrict__ k,
-    const u16* __restrict__ v, const float* __restrict__ alpha, const float* S0, const float* z0, float* ws,
-    u16* __restrict__ o, float* S_out, float* z_out) {
+    LGeo geo, const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const float* __restrict__ alpha, const float* S0, const float* z0, float* ws, u16* __restrict__ o, float* S_out,
+    float* z_out) {
     __shared__ __attribute__((aligned(16))) u16 fQ[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 fK[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 Vs[C][LDR];
@@ -103,19 +178,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ float zs[D], dens[C];
     __shared__ float gs[C], egs[C], eks[C];   // GATED: chunk-local g, e^g, e^{g_c - g}
 
-    const int nseg = OUT ? G : G - 1;
-    const int bh = blockIdx.x / nseg;
-    const int seg = blockIdx.x - bh * nseg;
-    if (bh >= BH) return;
-    const int n0 = seg * SEGC, n1 = min(NC, n0 + SEGC);
+    LItem it;
+    if (!la_item<PACKED>(geo, blockIdx.x, OUT, it)) return;
+    const int G = it.G, seg = it.seg, n0 = it.n0, n1 = it.n1, T = it.T;
+    const size_t slot = it.slot0 + seg;
     // entering state: S0 itself when the sequence is one segment, else the
     // prefix sum from the workspace (segment 0 included, so S_out may alias S0)
     const float* Sin = !OUT ? nullptr
-                       : G == 1 ? (S0 ? S0 + static_cast<size_t>(bh) * kMat : nullptr)
-                                : ws + ws_P(bh, G, seg);
+                       : G == 1 ? (S0 ? S0 + it.state * kMat : nullptr)
+                                : ws + ws_P(slot);
     const float* zin = (!OUT || GATED) ? nullptr
-                       : G == 1 ? (z0 ? z0 + static_cast<size_t>(bh) * D : nullptr)
-                                : ws + ws_zP(bh, G, seg);
+                       : G == 1 ? (z0 ? z0 + it.state * D : nullptr)
+                                : ws + ws_zP(slot);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: MFMAs sit in branches on it
     const int lane = tid & 63;
@@ -149,7 +223,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     uint4 rq[kItems], rk[kItems], rv[kItems];
     float ra = 1.f;   // GATED: alpha of token `lane` of the chunk (1 past the end)
     float decay = 1.f;  // GATED: product of the gates seen so far in this segment
-    const size_t head = static_cast<size_t>(bh) * T * D;
+    const size_t head = it.head_tok * D;
     auto fetch = [&](int n) {
         const int t0 = n * C;
         const int len = min(C, T - t0);
@@ -174,9 +248,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             }
         }
-        if (GATED) ra = lane < len ? alpha[static_cast<size_t>(bh) * T + t0 + lane] : 1.f;
+        if (GATED) ra = lane < len ? alpha[it.head_tok + t0 + lane] : 1.f;
     };
-    fetch(n0);
+    if (n1 > n0) fetch(n0);   // (an empty sequence has no chunk to load)
+    // this wave's rows of the state (value channels 32w + 16nb + r) into a [d_v][d_k] fp32 matrix
+    auto store_P = [&](float* dst) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            float* srow = dst + static_cast<size_t>(32 * w + 16 * nb + r) * D;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int d0 = 32 * s + 8 * g;
+                *reinterpret_cast<float4*>(srow + d0) =
+                    make_float4(P[nb][2 * s][0], P[nb][2 * s][1], P[nb][2 * s][2], P[nb][2 * s][3]);
+                *reinterpret_cast<float4*>(srow + d0 + 4) =
+                    make_float4(P[nb][2 * s + 1][0], P[nb][2 * s + 1][1], P[nb][2 * s + 1][2], P[nb][2 * s + 1][3]);
+            }
+        }
+    };
+    // packed batches: slot of the snapshot taken after chunk n, or -1
+    auto snap_slot = [&](int n) {
+        const int end = (n + 1) * C;
+        if (!OUT || !PACKED || geo.snap <= 0 || end > T || end % geo.snap != 0) return -1;
+        const int js = it.snap0 + end / geo.snap - 1;
+        return js < geo.snap_cap ? js : -1;
+    };
 
     // One chunk.  Normalised kind: the first chunk is peeled off the loop, so
     // every path into the loop ends with the same loads and stores and the
@@ -311,6 +407,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 a1 += bf16_bits_to_f32(fK[c + 1][tid]);
             }
             zs[tid] = a0 + a1;
+            const int js = snap_slot(n);
+            if (js >= 0) geo.z_snap[(static_cast<size_t>(js) * geo.H + it.h) * D + tid] = a0 + a1;
         }
 
         // ---- this wave's 32 value channels: outputs, then the state update
@@ -407,33 +505,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 P[1][t] = mfma16x16x32(a, Ve[1][s2], P[1][t]);
             }
         }
+        const int js = snap_slot(n);
+        if (js >= 0) store_P(geo.S_snap + (static_cast<size_t>(js) * geo.H + it.h) * kMat);
     };
-    int nstart = n0;
-    if constexpr (!GATED) {
-        chunk(n0);
-        nstart = n0 + 1;
+    if (n1 > n0) {
+        int nstart = n0;
+        if constexpr (!GATED) {
+            chunk(n0);
+            nstart = n0 + 1;
+        }
+        for (int n = nstart; n < n1; ++n) chunk(n);
     }
-    for (int n = nstart; n < n1; ++n) chunk(n);
 
     // OUT: final state of the last segment; otherwise the segment's contributions
-    float* Sdst = OUT ? (seg == G - 1 && S_out ? S_out + static_cast<size_t>(bh) * kMat : nullptr)
-                      : ws + ws_dS(bh, G, seg);
-    float* zdst = OUT ? (seg == G - 1 && z_out ? z_out + static_cast<size_t>(bh) * D : nullptr)
-                      : ws + ws_dz(bh, G, seg);
-    if (Sdst) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            float* srow = Sdst + static_cast<size_t>(32 * w + 16 * nb + r) * D;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int d0 = 32 * s + 8 * g;
-                *reinterpret_cast<float4*>(srow + d0) =
-                    make_float4(P[nb][2 * s][0], P[nb][2 * s][1], P[nb][2 * s][2], P[nb][2 * s][3]);
-                *reinterpret_cast<float4*>(srow + d0 + 4) =
-                    make_float4(P[nb][2 * s + 1][0], P[nb][2 * s + 1][1], P[nb][2 * s + 1][2], P[nb][2 * s + 1][3]);
-            }
-        }
-    }
+    float* Sdst = OUT ? (seg == G - 1 && S_out ? S_out + it.state * kMat : nullptr) : ws + ws_dS(slot);
+    float* zdst = OUT ? (seg == G - 1 && z_out ? z_out + it.state * D : nullptr) : ws + ws_dz(slot);
+    if (Sdst) store_P(Sdst);
     lds_barrier();
     if (GATED) {
         // the segment's total decay in slot 0 of the dz record (z is unused)
@@ -452,28 +539,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 constexpr int kBatch = 8;
 
 template <bool GATED>
-__global__ __launch_bounds__(kThreads) void la_combine_kernel(int BH, int G, const float* S0, const float* z0,
-                                                              float* ws) {
-    const int bh = blockIdx.x >> 4;
-    if (bh >= BH) return;
+__global__ __launch_bounds__(kThreads) void la_combine_kernel(LGeo geo, const float* S0, const float* z0, float* ws) {
+    // item: a head (uniform) or a (sequence, head) pair (packed)
+    const int item = blockIdx.x >> 4;
+    int G;
+    size_t slot0, state;
+    if (geo.cu == nullptr) {
+        if (item >= geo.BH) return;
+        G = geo.G;
+        slot0 = static_cast<size_t>(item) * G;
+        state = item;
+    } else {
+        if (item >= geo.N * geo.H) return;
+        const int sq = item / geo.H, h = item - sq * geo.H;
+        G = geo.seg_base[sq + 1] - geo.seg_base[sq];
+        if (G < 2 || geo.seg_base[sq + 1] > geo.Gcap) return;   // one segment: the output pass reads S0 itself
+        slot0 = static_cast<size_t>(h) * geo.Gcap + geo.seg_base[sq];
+        state = item;
+    }
     const int part = blockIdx.x & 15;
     const size_t e = (static_cast<size_t>(part) * kThreads + threadIdx.x) * 4;   // < kMat
-    float4 run = S0 ? *reinterpret_cast<const float4*>(S0 + static_cast<size_t>(bh) * kMat + e)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 run = S0 ? *reinterpret_cast<const float4*>(S0 + state * kMat + e) : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < G; s0 += kBatch) {
         float4 d[kBatch];
         float m[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int s = min(s0 + j, G - 2);   // (G >= 2) clamped: loads past the last map are unused
-            d[j] = *reinterpret_cast<const float4*>(ws + ws_dS(bh, G, s) + e);
-            m[j] = GATED ? ws[ws_dz(bh, G, s)] : 1.f;
+            d[j] = *reinterpret_cast<const float4*>(ws + ws_dS(slot0 + s) + e);
+            m[j] = GATED ? ws[ws_dz(slot0 + s)] : 1.f;
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int s = s0 + j;
             if (s < G) {
-                *reinterpret_cast<float4*>(ws + ws_P(bh, G, s) + e) = run;
+                *reinterpret_cast<float4*>(ws + ws_P(slot0 + s) + e) = run;
                 if (s + 1 < G) {
                     run.x = fmaf(m[j], run.x, d[j].x); run.y = fmaf(m[j], run.y, d[j].y);
                     run.z = fmaf(m[j], run.z, d[j].z); run.w = fmaf(m[j], run.w, d[j].w);
@@ -482,16 +582,16 @@ __global__ __launch_bounds__(kThreads) void la_combine_kernel(int BH, int G, con
         }
     }
     if (!GATED && part == 0 && threadIdx.x < D) {
-        float zr = z0 ? z0[static_cast<size_t>(bh) * D + threadIdx.x] : 0.f;
+        float zr = z0 ? z0[state * D + threadIdx.x] : 0.f;
         for (int s0 = 0; s0 < G; s0 += kBatch) {
             float dz[kBatch];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) dz[j] = ws[ws_dz(bh, G, min(s0 + j, G - 2)) + threadIdx.x];
+            for (int j = 0; j < kBatch; ++j) dz[j] = ws[ws_dz(slot0 + min(s0 + j, G - 2)) + threadIdx.x];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 const int s = s0 + j;
                 if (s < G) {
-                    ws[ws_zP(bh, G, s) + threadIdx.x] = zr;
+                    ws[ws_zP(slot0 + s) + threadIdx.x] = zr;
                     if (s + 1 < G) zr += dz[j];
                 }
             }
@@ -531,6 +631,27 @@ size_t la_mfma_workspace_bytes(int B, int H, int T, int, int, int) {
 
 namespace {
 
+template <bool GATED, bool PACKED>
+hipError_t launch_geo(const LGeo& g, int state_blocks, int combine_items, int out_blocks, const void* q,
+                      const void* k, const void* v, const float* alpha, const float* S0, const float* z0, void* o,
+                      float* S_out, float* z_out, float* ws, hipStream_t stream) {
+    const u16 *q16 = static_cast<const u16*>(q), *k16 = static_cast<const u16*>(k), *v16 = static_cast<const u16*>(v);
+    if (state_blocks > 0) {
+        hipLaunchKernelGGL((la_chunked_mfma_kernel<GATED, false, PACKED>), dim3(static_cast<unsigned>(state_blocks)),
+                           dim3(kThreads), 0, stream, g, q16, k16, v16, alpha, S0, z0, ws, nullptr, nullptr, nullptr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(la_combine_kernel<GATED>, dim3(static_cast<unsigned>(combine_items) * 16), dim3(kThreads),
+                           0, stream, g, S0, z0, ws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((la_chunked_mfma_kernel<GATED, true, PACKED>), dim3(static_cast<unsigned>(out_blocks)),
+                       dim3(kThreads), 0, stream, g, q16, k16, v16, alpha, S0, z0, ws, static_cast<u16*>(o), S_out,
+                       z_out);
+    return hipGetLastError();
+}
+
 template <bool GATED>
 hipError_t launch_segmented(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
                             const float* S0, const float* z0, void* o, float* S_out, float* z_out, void* workspace,
@@ -538,23 +659,61 @@ hipError_t launch_segmented(int B, int H, int T, const void* q, const void* k, c
     const int BH = B * H;
     if (BH <= 0 || T <= 0) return hipSuccess;
     const Plan p = make_plan(BH, T);
-    float* ws = static_cast<float*>(workspace);
-    const u16 *q16 = static_cast<const u16*>(q), *k16 = static_cast<const u16*>(k), *v16 = static_cast<const u16*>(v);
-    if (p.G > 1) {
-        hipLaunchKernelGGL((la_chunked_mfma_kernel<GATED, false>), dim3(static_cast<unsigned>(BH) * (p.G - 1)),
-                           dim3(kThreads), 0, stream, BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, alpha, S0, z0, ws,
-                           nullptr, nullptr, nullptr);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(la_combine_kernel<GATED>, dim3(static_cast<unsigned>(BH) * 16), dim3(kThreads), 0, stream,
-                           BH, p.G, S0, z0, ws);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((la_chunked_mfma_kernel<GATED, true>), dim3(static_cast<unsigned>(BH) * p.G), dim3(kThreads),
-                       0, stream, BH, T, p.NC, p.G, p.SEGC, q16, k16, v16, alpha, S0, z0, ws, static_cast<u16*>(o),
-                       S_out, z_out);
-    return hipGetLastError();
+    LGeo g{};
+    g.BH = BH;
+    g.T = T;
+    g.NC = p.NC;
+    g.G = p.G;
+    g.SEGC = p.SEGC;
+    return launch_geo<GATED, false>(g, p.G > 1 ? BH * (p.G - 1) : 0, BH, BH * p.G, q, k, v, alpha, S0, z0, o, S_out,
+                                    z_out, static_cast<float*>(workspace), stream);
+}
+
+// ---- packed batches: plan on the host from N and Ttot only (the sequence
+// lengths stay on the device).  SEGC is chosen so that about kTargetBlocks
+// (segment, head) items exist; Gcap bounds the total segment count,
+// sum ceil(NC_n / SEGC) <= (Ttot / C + N) / SEGC + N.
+struct LVarPlan {
+    int SEGC, Gcap;
+    size_t table_bytes;
+};
+
+LVarPlan make_lvar_plan(int N, int H, int Ttot) {
+    LVarPlan p;
+    const long long chunks = static_cast<long long>(Ttot) / C + N;
+    long long segc = (chunks * H + kTargetBlocks - 1) / kTargetBlocks;
+    if (segc < 1) segc = 1;
+    p.SEGC = static_cast<int>(segc);
+    p.Gcap = static_cast<int>(chunks / segc + N + 1);
+    p.table_bytes = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    return p;
+}
+
+template <bool GATED>
+hipError_t launch_packed(int N, int H, int Ttot, const int* cu, const void* q, const void* k, const void* v,
+                         const float* alpha, const float* S0, const float* z0, void* o, float* S_out, float* z_out,
+                         int snap, int snap_cap, float* S_snap, float* z_snap, void* workspace, hipStream_t stream) {
+    if (N <= 0 || H <= 0) return hipSuccess;
+    const LVarPlan p = make_lvar_plan(N, H, Ttot);
+    int* tab = static_cast<int*>(workspace);
+    LGeo g{};
+    g.SEGC = p.SEGC;
+    g.cu = cu;
+    g.seg_base = tab;
+    g.snap_base = tab + (N + 1);
+    g.N = N;
+    g.H = H;
+    g.Ttot = Ttot;
+    g.Gcap = p.Gcap;
+    g.snap = S_snap ? snap : 0;
+    g.snap_cap = snap_cap;
+    g.S_snap = S_snap;
+    g.z_snap = z_snap;
+    const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream);
+    if (e != hipSuccess) return e;
+    float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.table_bytes);
+    const int blocks = p.Gcap * H;   // (segment, head) items, a bound; the extra workgroups exit
+    return launch_geo<GATED, true>(g, blocks, N * H, blocks, q, k, v, alpha, S0, z0, o, S_out, z_out, ws, stream);
 }
 
 }  // namespace
@@ -567,6 +726,22 @@ hipError_t launch_la_mfma(int B, int H, int T, const void* q, const void* k, con
 hipError_t launch_gla_mfma(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
                            const float* S0, void* o, float* S_out, void* workspace, hipStream_t stream) {
     return launch_segmented<true>(B, H, T, q, k, v, alpha, S0, nullptr, o, S_out, nullptr, workspace, stream);
+}
+
+size_t la_mfma_varlen_workspace_bytes(int N, int H, int Ttot) {
+    if (N <= 0 || H <= 0) return 0;
+    const LVarPlan p = make_lvar_plan(N, H, Ttot);
+    return p.table_bytes + static_cast<size_t>(H) * p.Gcap * kRec * sizeof(float);
+}
+
+hipError_t launch_la_mfma_varlen(bool gated, int N, int H, int Ttot, const int* cu, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* S0, const float* z0, void* o,
+                                 float* S_out, float* z_out, int snap, int snap_cap, float* S_snap, float* z_snap,
+                                 void* workspace, hipStream_t stream) {
+    return gated ? launch_packed<true>(N, H, Ttot, cu, q, k, v, alpha, S0, nullptr, o, S_out, nullptr, snap, snap_cap,
+                                       S_snap, nullptr, workspace, stream)
+                 : launch_packed<false>(N, H, Ttot, cu, q, k, v, nullptr, S0, z0, o, S_out, z_out, snap, snap_cap,
+                                        S_snap, z_snap, workspace, stream);
 }
 
 }  // namespace la

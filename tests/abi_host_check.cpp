@@ -125,7 +125,7 @@ int main() {
     CHECK(lin_attn_prefill_varlen(LA_KIND_NORMALIZED, LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)),
                                   P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, P(4), nullptr, nullptr, 128, 4,
                                   F(11), nullptr, LA_FORM_RECURRENT, 0, P(9), 1 << 30, nullptr), LA_ERR_NULL);
-    CHECK(lin_attn_prefill_varlen(LA_KIND_GATED, LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)), P(1),
+    CHECK(lin_attn_prefill_varlen(LA_KIND_GATED, LA_F32, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)), P(1),
                                   P(2), P(3), F(5), nullptr, nullptr, nullptr, P(4), nullptr, nullptr, 0, 0, nullptr,
                                   nullptr, LA_FORM_CHUNKED, 64, P(9), 1 << 30, nullptr), LA_ERR_UNSUPPORTED);
     CHECK(lin_attn_prefill_varlen(LA_KIND_GATED, LA_BF16, 3, 2, 500, 128, 128, static_cast<const int*>(P(10)), P(1),

@@ -369,16 +369,21 @@ def test_varlen_kinds_validation(lib):
     assert vl(kind=9) == LA_ERR_ARG
     assert vl(dtype=7) == LA_ERR_DTYPE
     assert vl(form=PARALLEL) == LA_ERR_ARG
-    # block form: KDA (and the gated delta rule, forwarded) on the matrix cores: bf16, d = 128
+    # block form of every kind on the matrix cores: bf16, d = 128
     assert vl(form=CHUNKED, ws=None) == LA_ERR_WORKSPACE
     assert vl(form=CHUNKED, dtype=F32) == LA_ERR_UNSUPPORTED
     assert vl(form=CHUNKED, dk=64, dv=64) == LA_ERR_UNSUPPORTED
-    assert vl(form=CHUNKED, kind=K_GATED, b=None) == LA_ERR_UNSUPPORTED
-    assert vl(form=CHUNKED, kind=K_NORM, a=None, b=None) == LA_ERR_UNSUPPORTED
+    assert vl(form=CHUNKED, kind=K_GATED, b=None, ws=None) == LA_ERR_WORKSPACE
+    assert vl(form=CHUNKED, kind=K_NORM, a=None, b=None, ws=None) == LA_ERR_WORKSPACE
+    assert vl(form=CHUNKED, kind=K_GATED, b=None, dtype=F32) == LA_ERR_UNSUPPORTED
+    assert vl(form=CHUNKED, kind=K_NORM, a=None, b=None, dk=64, dv=64) == LA_ERR_UNSUPPORTED
     assert vl(form=CHUNKED, snap=100, nsnap=4, S_snap=11) == LA_ERR_SHAPE   # snapshots at whole 64-token blocks
+    assert vl(form=CHUNKED, kind=K_NORM, a=None, b=None, snap=100, nsnap=4, S_snap=11, z_snap=12) == LA_ERR_SHAPE
     kneed = lib.la_workspace_bytes(PREFILL_VARLEN, BF16, 3, 2, 500, 128, 128, CHUNKED, 64)
     assert kneed >= lib.la_workspace_bytes(5, BF16, 3, 2, 500, 128, 128, CHUNKED, 64)
     assert vl(form=CHUNKED, ws_bytes=1000) == LA_ERR_WORKSPACE
+    assert vl(form=CHUNKED, kind=K_GATED, b=None, ws_bytes=1000) == LA_ERR_WORKSPACE
+    assert vl(form=CHUNKED, kind=K_NORM, a=None, b=None, ws_bytes=1000) == LA_ERR_WORKSPACE
     assert vl(form=CHUNKED, chunk=48) == LA_ERR_SHAPE
     assert vl(dk=48) == LA_ERR_SHAPE
     assert vl(snap=-1) == LA_ERR_SHAPE

@@ -6,8 +6,9 @@ intervals (z snapshots for the normalised kind), carried and in-place states,
 empty and one-token sequences, a truncated snapshot buffer, an empty batch,
 resuming a sequence from one of its snapshots with the uniform entry points
 (prefix reuse), and a 16-sequence, 16-head, 16 384-token batch checked on
-sampled heads; and the same cases for the KDA block form on the matrix cores
-(form="chunked", bf16, d = 128, snapshots at whole 64-token blocks).
+sampled heads; and the same cases for the block forms of every kind on the
+matrix cores (form="chunked", bf16, d = 128, snapshots at whole 64-token
+blocks), with sequences long enough to be cut into several segments.
 """
 
 import numpy as np
@@ -169,62 +170,98 @@ def test_varlen_kind_16_sequences(gd, kind):
 
 
 # ------------------------------------------------ KDA block form, packed batches
-def run_kda_chunked(gd, q, k, v, a, b, cu, S0=None, snap=0, snap_count=None, inplace=False):
+def run_chunked(gd, kind, q, k, v, a, b, cu, S0=None, z0=None, snap=0, snap_count=None, inplace=False):
     import torch
     tS = None if S0 is None else to_dev(S0, "f32")
+    tz = None if z0 is None else to_dev(z0, "f32")
     tcu = torch.from_numpy(np.asarray(cu, np.int32)).to("cuda:0")
-    print(f"[case] kda chunked H={q.shape[0]} T={q.shape[1]} N={len(cu) - 1} snap={snap}", flush=True)
-    o, S, _, sn, _ = gd.lin_attn_prefill_varlen("kda", to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), tcu,
-                                                to_dev(a, "f32"), to_dev(b, "f32"), tS, form="chunked",
-                                                snap_interval=snap, snap_count=snap_count,
-                                                S_out=tS if inplace else None)
-    return to_host(o), to_host(S), None, (None if sn is None else to_host(sn)), None
+    opt = lambda x: None if x is None else to_dev(x, "f32")
+    print(f"[case] {kind} chunked H={q.shape[0]} T={q.shape[1]} N={len(cu) - 1} snap={snap} inplace={inplace}",
+          flush=True)
+    o, S, z, sn, zsn = gd.lin_attn_prefill_varlen(kind, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), tcu,
+                                                  opt(a), opt(b), tS, tz, form="chunked", snap_interval=snap,
+                                                  snap_count=snap_count, S_out=tS if inplace else None,
+                                                  z_out=tz if inplace else None)
+    h = lambda t: None if t is None else to_host(t)
+    return h(o), h(S), h(z), h(sn), h(zsn)
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("snap,inplace", [(0, False), (64, True), (128, False)])
-def test_varlen_kda_chunked(gd, snap, inplace):
-    """The KDA block form (tile pass + column scan on the matrix cores) over a
-    packed batch: empty, one-token and chunk-edge lengths, carried states,
-    snapshots at whole 64-token blocks."""
+def test_varlen_chunked(gd, kind, snap, inplace):
+    """The block forms on the matrix cores over a packed batch (normalised and
+    scalar-gated: segment pass, combine, output pass; KDA: tile pass and
+    column scan): empty, one-token and chunk-edge lengths, carried states,
+    snapshots at whole 64-token blocks (z snapshots for the normalised kind)."""
     H, d = 2, 128
-    q, k, v, a, b, cu, S0, _ = inputs("kda", 101, LENS, H, d, "bf16")
-    ref = ov.packed_varlen("kda", q, k, v, cu, a, b, S0, snap_interval=snap)
-    got = run_kda_chunked(gd, q, k, v, a, b, cu, S0, snap=snap, inplace=inplace)
-    check(f"varlen kda chunked snap={snap}", got, ref, cu, "bf16")
+    q, k, v, a, b, cu, S0, z0 = inputs(kind, 101, LENS, H, d, "bf16")
+    ref = ov.packed_varlen(kind, q, k, v, cu, a, b, S0, z0, snap_interval=snap)
+    got = run_chunked(gd, kind, q, k, v, a, b, cu, S0, z0, snap=snap, inplace=inplace)
+    check(f"varlen {kind} chunked snap={snap}", got, ref, cu, "bf16")
 
 
-def test_varlen_kda_chunked_truncated_snapshots_and_resume(gd):
+@pytest.mark.parametrize("kind", ("normalized", "gated"))
+def test_varlen_chunked_many_segments(gd, kind):
+    """Few heads and long sequences: each sequence is cut into several
+    segments whose states are combined (one 8192-token sequence among short
+    ones), snapshots every 512 tokens."""
+    H, d = 1, 128
+    lens = [8192, 5, 700, 0, 2049]
+    q, k, v, a, b, cu, S0, z0 = inputs(kind, 111, lens, H, d, "bf16")
+    ref = ov.packed_varlen(kind, q, k, v, cu, a, b, S0, z0, snap_interval=512)
+    got = run_chunked(gd, kind, q, k, v, a, b, cu, S0, z0, snap=512, inplace=True)
+    check(f"varlen {kind} chunked long sequences", got, ref, cu, "bf16")
+
+
+def _resume(gd, kind, q, k, v, a, b, Sj, zj):
+    """The uniform block-form entry point of the kind, one sequence."""
+    if kind == "normalized":
+        o, S, _ = gd.lin_attn_prefill(q, k, v, Sj, zj, form="chunked")
+    elif kind == "gated":
+        o, S = gd.gla_prefill(q, k, v, a, Sj, form="chunked")
+    else:
+        o, S = gd.kda_prefill(q, k, v, a, b, Sj, form="chunked")
+    return o, S
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_varlen_chunked_truncated_snapshots_and_resume(gd, kind):
     """Only the first 5 snapshots fit the buffer; a sequence resumed from one
-    of its snapshots with kda_prefill (block form) gives the packed call's
-    outputs and final state."""
+    of its snapshots with the kind's uniform entry point (block form) gives
+    the packed call's outputs and final state."""
     import torch
     H, d = 2, 128
     lens = [700, 1100]
-    q, k, v, a, b, cu, _, _ = inputs("kda", 103, lens, H, d, "bf16", states=False)
-    _, _, _, sn_r, _ = ov.packed_varlen("kda", q, k, v, cu, a, b, snap_interval=256)
-    _, _, _, sn5, _ = run_kda_chunked(gd, q, k, v, a, b, cu, snap=256, snap_count=5)
+    q, k, v, a, b, cu, _, _ = inputs(kind, 103, lens, H, d, "bf16", states=False)
+    _, _, _, sn_r, zsn_r = ov.packed_varlen(kind, q, k, v, cu, a, b, snap_interval=256)
+    _, _, _, sn5, zsn5 = run_chunked(gd, kind, q, k, v, a, b, cu, snap=256, snap_count=5)
     assert sn5.shape[0] == 5
-    report("varlen kda chunked first 5 snapshots", slice_err(sn5, sn_r[:5]), TOL["bf16"])
-    o, S, _, sn, _ = run_kda_chunked(gd, q, k, v, a, b, cu, snap=256)
+    report(f"varlen {kind} chunked first 5 snapshots", slice_err(sn5, sn_r[:5]), TOL["bf16"])
+    if zsn_r is not None:
+        report(f"varlen {kind} chunked first 5 z snapshots", slice_err(zsn5, zsn_r[:5]), TOL["bf16"])
+    o, S, _, sn, zsn = run_chunked(gd, kind, q, k, v, a, b, cu, snap=256)
     p, j = 1024, 2 + 3
     s0, e = int(cu[1]) + p, int(cu[2])
-    up = lambda x, dt: to_dev(np.ascontiguousarray(x[:, s0:e][None]), dt)
-    Sj = torch.from_numpy(np.ascontiguousarray(sn[j][None], np.float32)).to("cuda:0")
-    o_t, S_t = gd.kda_prefill(up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), up(a, "f32"), up(b, "f32"), Sj,
-                              form="chunked")
-    report("resume kda chunked o vs packed", slice_err(to_host(o_t)[0], o[:, s0:e], lead=1), TOL["bf16"])
-    report("resume kda chunked S vs packed", slice_err(to_host(S_t)[0], S[1]), TOL["bf16"])
+    up = lambda x, dt: None if x is None else to_dev(np.ascontiguousarray(x[:, s0:e][None]), dt)
+    st = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x[j][None], np.float32)).to("cuda:0")
+    o_t, S_t = _resume(gd, kind, up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), up(a, "f32"), up(b, "f32"), st(sn),
+                       st(zsn))
+    report(f"resume {kind} chunked o vs packed", slice_err(to_host(o_t)[0], o[:, s0:e], lead=1), TOL["bf16"])
+    report(f"resume {kind} chunked S vs packed", slice_err(to_host(S_t)[0], S[1]), TOL["bf16"])
 
 
 @pytest.mark.timeout(600)
-def test_varlen_kda_chunked_16_sequences(gd):
+@pytest.mark.parametrize("kind", KINDS)
+def test_varlen_chunked_16_sequences(gd, kind):
     """16 sequences of mixed lengths, 16 heads, 16 384 tokens, snapshots every
     1024 tokens; heads 0, 7 and 15 checked against the oracle."""
     H, d, snap = 16, 128, 1024
     lens = synth.varlen_lengths(98, 16, 16384)
-    q, k, v, a, b, cu, S0, _ = inputs("kda", 105, lens, H, d, "bf16")
-    o, S, _, sn, _ = run_kda_chunked(gd, q, k, v, a, b, cu, S0, snap=snap)
+    q, k, v, a, b, cu, S0, z0 = inputs(kind, 105, lens, H, d, "bf16")
+    o, S, z, sn, zsn = run_chunked(gd, kind, q, k, v, a, b, cu, S0, z0, snap=snap)
     hs = [0, 7, 15]
-    ref = ov.packed_varlen("kda", q[hs], k[hs], v[hs], cu, a[hs], b[hs], S0[:, hs], snap_interval=snap)
-    check("varlen kda chunked 16 seq x 16 heads (heads 0, 7, 15)", (o[hs], S[:, hs], None, sn[:, hs], None), ref,
-          cu, "bf16")
+    pick = lambda x: None if x is None else x[hs]
+    pick2 = lambda x: None if x is None else x[:, hs]
+    ref = ov.packed_varlen(kind, q[hs], k[hs], v[hs], cu, pick(a), pick(b), S0[:, hs], pick2(z0), snap_interval=snap)
+    check(f"varlen {kind} chunked 16 seq x 16 heads (heads 0, 7, 15)",
+          (o[hs], S[:, hs], pick2(z), pick2(sn), pick2(zsn)), ref, cu, "bf16")
