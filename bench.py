@@ -11,7 +11,8 @@ heads, d = 128, fp32 state, 1000 steps) as state HBM GB/s; the normalised and
 the scalar-gated linear-attention prefills; the 1 x 16 x 262144 long-context
 prefill; the fused pre-operations of a Gated DeltaNet layer; the KDA decode
 and prefill (block and recurrent forms); a packed batch of 16 sequences of
-mixed lengths with state snapshots; and the fp64 CPU oracle on a bounded
+mixed lengths with state snapshots (gated delta, and the same batch for the
+normalised, scalar-gated and KDA kinds); and the fp64 CPU oracle on a bounded
 sample of the prefill workload.  Prints one JSON line.
 
 Every leg's inputs are drawn and uploaded first; then the GPU runs about 0.3 s
@@ -53,7 +54,8 @@ KDA_DECODE = "kda_decode_256x32"
 KDA_PREFILL = "kda_bf16_2x16x8192"
 VARLEN = "gdn_varlen_bf16_16seq_16k"
 LONG = "gdn_bf16_1x16x262144"
-LEGS = ["decode", "kda_decode", "la", "gla", "preops", "kda_prefill", "varlen", "long", "prefill", "copy"]
+LEGS = ["decode", "kda_decode", "la", "gla", "preops", "kda_prefill", "varlen", "varlen_kinds", "long", "prefill",
+        "copy"]
 
 
 # Algorithmic work per head-token of the chunked gated-delta path, chunk C,
@@ -363,6 +365,49 @@ def leg_varlen(c):
             "roofline": hbm_roofline("gdn_prefill_varlen (plan + map + combine + out)", nbytes, ms)}
 
 
+def leg_varlen_kinds(c):
+    """The packed batch of the varlen leg (same lengths, snapshots every 1024
+    tokens) for the other kinds through lin_attn_prefill_varlen: block form
+    on the matrix cores, and one call of the recurrent form for reference."""
+    import numpy as np
+
+    import synth
+    torch, gd, n = c.torch, c.gd, c.args.la_steps
+    w = synth.WORKLOADS[VARLEN]
+    H, d, snap, N, Tt = w["H"], w["dk"], w["snap"], w["N"], w["T_total"]
+    lens = synth.varlen_lengths(w["seed"], N, Tt)
+    nsnap = int(sum(int(L) // snap for L in lens))
+    ws = torch.empty(gd.la_workspace_bytes("prefill_varlen", "bf16", N, H, Tt, d, d, "chunked", 64), dtype=torch.uint8,
+                     device=c.dev)
+    out = torch.empty((H, Tt, d), dtype=torch.bfloat16, device=c.dev)
+    S = torch.empty((N, H, d, d), dtype=torch.float32, device=c.dev)
+    z = torch.empty((N, H, d), dtype=torch.float32, device=c.dev)
+    S_snap = torch.empty((nsnap, H, d, d), dtype=torch.float32, device=c.dev)
+    z_snap = torch.empty((nsnap, H, d), dtype=torch.float32, device=c.dev)
+    inputs = {}
+    for kind in ("normalized", "gated", "kda"):
+        q, k, v, a, b, cu = synth.varlen_kind_batch(w["seed"], kind, lens, H, d, d, "bf16",
+                                                    1 / np.sqrt(d) if kind == "normalized" else 1.0)
+        inputs[kind] = tuple(c.up(x, True) for x in (q, k, v)) + tuple(None if x is None else c.up(x) for x in (a, b))
+        cu_t = c.up(cu)
+    del q, k, v, a, b
+
+    def call(kind, form):
+        has_z = kind == "normalized"
+        gd.lin_attn_prefill_varlen(kind, *inputs[kind][:3], cu_t, *inputs[kind][3:], form=form, snap_interval=snap,
+                                   snap_count=nsnap, out=out, S_out=S, z_out=z if has_z else None, S_snap=S_snap,
+                                   z_snap=z_snap if has_z else None, workspace=ws)
+
+    yield
+    res = {"workload": f"packed batch of {N} sequences ({Tt} tokens, lengths {int(min(lens))}..{int(max(lens))}), "
+                       f"H=16 d=128, bf16 I/O, fp32 state, snapshots every {snap} tokens ({nsnap}); kinds through "
+                       "lin_attn_prefill_varlen", "calls": n, "block_form_ms": {}, "recurrent_form_ms": {}}
+    for kind in inputs:
+        res["block_form_ms"][kind] = c.timed(n, lambda i: call(kind, "chunked"))
+        res["recurrent_form_ms"][kind] = c.timed(1, lambda i: call(kind, "recurrent"), warm=0)
+    return res
+
+
 def leg_copy(c):
     # a plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
     # WRITE_SIZE give the factor that turns those counters into bytes
@@ -552,7 +597,7 @@ def main():
 
     c = Ctx(args)
     fns = {"la": leg_la, "gla": leg_gla, "preops": leg_preops, "decode": leg_decode, "long": leg_long,
-           "kda_decode": leg_kda_decode, "kda_prefill": leg_kda_prefill, "varlen": leg_varlen,
+           "kda_decode": leg_kda_decode, "kda_prefill": leg_kda_prefill, "varlen": leg_varlen, "varlen_kinds": leg_varlen_kinds,
            "prefill": leg_prefill, "copy": leg_copy}
     # Every leg first draws and uploads its inputs (seconds of host work, the
     # GPU idle); then the timed parts run back to back, in a fixed order with
@@ -602,6 +647,7 @@ def main():
         "kda_decode": res.get("kda_decode"),
         "kda_prefill": res.get("kda_prefill"),
         "varlen_prefill": res.get("varlen"),
+        "varlen_prefill_other_kinds": res.get("varlen_kinds"),
         "legs_run": legs,
         "cpu_baseline": cpu,
     }

@@ -59,9 +59,9 @@ def kernel_key(name, tag, wg=None):
     targs = [a.strip() for a in s[len(base) + 1:-1].split(",")] if "<" in s else []
     if base in ("gdn_map_kernel", "gdn_combine_kernel", "gdn_out_kernel", "gdn_varlen_plan_kernel"):
         return base + ("_varlen_16seq" if tag == "legs" else "")
-    if base == "la_chunked_mfma_kernel" and len(targs) == 2:
-        return ("gla" if targs[0] == "true" else "la") + "_chunked_mfma_kernel_" + ("out" if targs[1] == "true"
-                                                                                else "state")
+    if base == "la_chunked_mfma_kernel" and len(targs) == 3:   # <GATED, OUT, PACKED>
+        return (("gla" if targs[0] == "true" else "la") + "_chunked_mfma_kernel_" +
+                ("out" if targs[1] == "true" else "state") + ("_varlen" if targs[2] == "true" else ""))
     if base == "la_combine_kernel" and targs:
         return "gla_combine_kernel" if targs[0] == "true" else "la_combine_kernel"
     if base == "recurrent_kernel" and len(targs) == 6:
