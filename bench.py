@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--legs a,b,...]
 
-One timed step is one chunked gated-delta prefill (state-independent pass +
-sequential scan) over the 2 x 16 x 8192 workload (B=2, H=16, T=8192,
+One timed step is one chunked gated-delta prefill (one gdn_prefill call: the
+map pass, the combine and the output pass) over the 2 x 16 x 8192 workload (B=2, H=16, T=8192,
 d_k = d_v = 128, bf16 activations, fp32 state, chunk 64), inputs resident in
 HBM.  `value` is prefill tokens/s (B*T tokens per step).  In the same run,
 each reported beside the headline: the decode workload (256 sequences x 32
@@ -26,7 +26,7 @@ run are null in the JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 are launched on (torch's current stream, which the binding passes to the C
-ABI): around the two launches of every fourth timed prefill step, and around
+ABI): around the call of every fourth timed prefill step, and around
 each other leg's run of back-to-back calls (an event record costs a few
 microseconds of GPU time).  Input sets rotate over three copies so the 256 MB
 last-level cache cannot serve one step's inputs from the previous step.
@@ -423,7 +423,7 @@ def leg_copy(c):
 
 def leg_prefill(c):
     """The headline: W untimed steps, then exactly K timed steps between two
-    synchronisations; events around the two launches of every fourth step."""
+    synchronisations; events around the call of every fourth step."""
     import numpy as np
 
     import synth
@@ -441,12 +441,9 @@ def leg_prefill(c):
         tq, tk, tv, ta, tb = sets[i % 3]
         if ev is not None:
             ev[0].record()
-        gd.gdn_prefill_prep(tq, tk, tv, ta, tb, ws, chunk=C)
+        gd.gdn_prefill(tq, tk, tv, ta, tb, None, form="chunked", chunk=C, out=out, S_out=S_out, workspace=ws)
         if ev is not None:
             ev[1].record()
-        gd.gdn_prefill_scan(tq, tk, tv, ta, tb, ws, None, out=out, S_out=S_out, chunk=C)
-        if ev is not None:
-            ev[2].record()
 
     yield
     for i in range(args.warmup):
@@ -455,34 +452,34 @@ def leg_prefill(c):
     # an event record costs a few microseconds of GPU time, so only every
     # fourth timed step carries events
     sampled = set(range(min(1, args.steps - 1), args.steps, 4))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, evs.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs.values()]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
     head_tokens = B * H * T
-    # segments per head, from the workspace size (3 fp32 d x d matrices per head-segment)
+    # segments per head, from the workspace size (3 fp32 d x d matrices per
+    # head-segment); more than 256 / (B*H) means the plan with a lead segment
+    # (segment 0 runs beside the maps in gdn_lead_map_kernel)
     G = max(1, ws.numel() // (B * H * 3 * d * d * 4)) if ws is not None and ws.numel() > 16 else 1
-    # Roofline of the whole step (every kernel of the path: gdn_map_kernel,
-    # gdn_combine_kernel, gdn_out_kernel): algorithmic bytes = the path's
-    # minimal I/O per head-token (q, k, v, o in bf16, alpha, beta in fp32)
-    # times the head-tokens of the step, over the summed event time of its two
-    # launches.  The counter figures (HBM bytes, MFMA busy) come from rocprofv3
+    lead = G * B * H > 256
+    # Roofline of the whole step (every kernel of the call: gdn_lead_map_kernel
+    # or gdn_map_kernel, gdn_combine_kernel, gdn_out_kernel): algorithmic
+    # bytes = the path's minimal I/O per head-token (q, k, v, o in bf16, alpha,
+    # beta in fp32) times the head-tokens of the step, over the event time of
+    # the call.  The counter figures (HBM bytes, MFMA busy) come from rocprofv3
     # runs stored under profiles/ and are null once the source has changed.
-    step_kernels = ["gdn_map_kernel", "gdn_combine_kernel", "gdn_out_kernel"]
-    step_ms = prep_ms + scan_ms
+    step_kernels = ["gdn_lead_map_kernel" if lead else "gdn_map_kernel", "gdn_combine_kernel", "gdn_out_kernel"]
     alg_bytes = head_tokens * path_bytes_per_head_token(d)
     alg_flops = head_tokens * path_flops_per_head_token(d, C)
     tflops = alg_flops / (step_ms * 1e-3) / 1e12
     pmc = measured_pmc(step_kernels)
-    roof = hbm_roofline("gdn_prefill step (gdn_map_kernel + gdn_combine_kernel + gdn_out_kernel)", alg_bytes,
-                        step_ms, step_kernels)
-    roof["launches_ms"] = {"gdn_prefill_prep": prep_ms, "gdn_prefill_scan": scan_ms}
+    roof = hbm_roofline("gdn_prefill step (" + " + ".join(step_kernels) + ")", alg_bytes, step_ms, step_kernels)
     roof["segments_per_head"] = G
+    roof["lead_segment"] = lead
     # The HBM roofline is the one that bounds this path (its intensity, 136
     # flop/B, is below the chip's ridge); what holds the step below it is the
     # serial chain of 64-token chunks inside each segment: per chunk, the

@@ -27,9 +27,14 @@
 //    (d_k x 256, starting from [0 | I]) through the chunk map; emits the
 //    segment's (M, N).
 //  * gdn_combine_kernel - per head, the entering state of every segment:
-//    P_0 = S0, P_{s+1} = M_s P_s + N_s (fp32).
+//    P_0 = S0, P_{s+1} = M_s P_s + N_s (split bf16 products, fp32 sums).
 //  * gdn_out_kernel     - every segment from its entering state: recompute
 //    the chunk tiles, outputs O, and the final state of the last segment.
+// The map pass needs one workgroup fewer per head than the output pass; a
+// whole gdn_prefill call can instead give segment 0 (whose entering state is
+// S0) to gdn_lead_map_kernel, which runs it beside the maps of segments
+// 1..G-2 and writes P_1; the combine then starts from P_1 and the output pass
+// runs segments 1..G-1, so both passes fill the chip with one more segment.
 // Per chunk, the state-independent tiles (chunk-local prefix sum of log alpha
 // with a wave scan; K K^T and Q K^T on v_mfma_f32_16x16x32_bf16; the four
 // 16x16 diagonal blocks of I + L inverted in registers by the product form
@@ -622,6 +627,8 @@ __device__ __forceinline__ size_t ws_M(size_t slot) { return ws_P(slot) + 2 * kM
 //   is written to S_snap[snap_base[n] + j][h] for the first snap_cap slots.
 struct Geo {
     int BH, T, G, SEGC;
+    int L0;     // chunks of segment 0 (SEGC unless lead)
+    int lead;   // uniform only: segment 0 runs in the map pass (1) or with the others (0)
     const int* cu;
     const int* seg_base;
     const int* snap_base;
@@ -646,10 +653,11 @@ __device__ __forceinline__ int clamp_tok(int t, int Ttot) { return t < 0 ? 0 : t
 // map and its workgroup has nothing to do).  False: nothing to do.
 __device__ __forceinline__ bool find_item(const Geo& g, int blk, bool maps, Item& it) {
     if (g.cu == nullptr) {
-        const int per = maps ? g.G - 1 : g.G;
+        // with a lead segment, segment 0 is neither mapped nor run here
+        const int per = (maps ? g.G - 1 : g.G) - g.lead;
         const int bh = blk / per;
         if (bh >= g.BH) return false;
-        it.seg = blk - bh * per;
+        it.seg = g.lead + blk - bh * per;
         it.G = g.G;
         it.len = g.T;
         it.head_tok = static_cast<size_t>(bh) * g.T;
@@ -679,9 +687,23 @@ __device__ __forceinline__ bool find_item(const Geo& g, int blk, bool maps, Item
         it.snap0 = g.snap_base ? g.snap_base[lo] : 0;
         it.h = h;
     }
-    it.n0 = it.seg * g.SEGC;
-    it.n1 = min((it.len + C - 1) / C, it.n0 + g.SEGC);
+    it.n0 = it.seg == 0 ? 0 : g.L0 + (it.seg - 1) * g.SEGC;
+    it.n1 = min((it.len + C - 1) / C, it.n0 + (it.seg == 0 ? g.L0 : g.SEGC));
     return true;
+}
+
+// Segment 0 of head bh of a uniform batch (the lead segment).
+__device__ __forceinline__ void lead_item(const Geo& g, int bh, Item& it) {
+    it.seg = 0;
+    it.G = g.G;
+    it.len = g.T;
+    it.head_tok = static_cast<size_t>(bh) * g.T;
+    it.slot0 = static_cast<size_t>(bh) * g.G;
+    it.state = bh;
+    it.snap0 = 0;
+    it.h = 0;
+    it.n0 = 0;
+    it.n1 = min((g.T + C - 1) / C, g.L0);
 }
 
 // ============================================================ segment maps
@@ -709,13 +731,9 @@ constexpr int kMapThreads = 768;   // 8 state carriers + 4 stagers
 // The carriers also stage the inputs, in the first phase, which the stagers'
 // diagonal blocks bound: waves 0-3 k and the gates of chunk n+2, waves 4-7 v
 // of chunk n+1.
-__global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
-                                                              const u16* __restrict__ v,
-                                                              const float* __restrict__ alpha,
-                                                              const float* __restrict__ beta, float* __restrict__ ws) {
-    __shared__ __attribute__((aligned(16))) MapTiles sm;
-    Item it;
-    if (!find_item(geo, blockIdx.x, true, it)) return;
+__device__ __forceinline__ void map_body(MapTiles& sm, const Item& it, const u16* __restrict__ k,
+                                        const u16* __restrict__ v, const float* __restrict__ alpha,
+                                        const float* __restrict__ beta, float* __restrict__ ws) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branches below are scalar
     const int n0 = it.n0, n1 = it.n1, T = it.len;
@@ -819,6 +837,17 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
     }
 }
 
+
+__global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16* __restrict__ k,
+                                                              const u16* __restrict__ v,
+                                                              const float* __restrict__ alpha,
+                                                              const float* __restrict__ beta, float* __restrict__ ws) {
+    __shared__ __attribute__((aligned(16))) MapTiles sm;
+    Item it;
+    if (!find_item(geo, blockIdx.x, true, it)) return;
+    map_body(sm, it, k, v, alpha, beta, ws);
+}
+
 // ============================================================ combine
 // One workgroup (4 waves) per (head, 16 value channels): P_0 = S0,
 // P_{s+1} = M_s P_s + N_s, writing every P_s.  The products run on MFMA with
@@ -861,17 +890,20 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(Geo geo, c
         slot0 = static_cast<size_t>(h) * geo.Gcap + geo.seg_base[n];
         state = bh;
     }
-    if (G < 2) return;   // a single segment starts from S0 itself
+    // with a lead segment the chain starts from P_1, which pass 1 wrote
+    const int s0 = geo.cu == nullptr ? geo.lead : 0;
+    if (G < 2 + s0) return;   // a single segment starts from S0 itself (or P_1 is the last state needed)
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
-    // P_0 = S0 (zeros when absent) for value channels 16 tile .. +15
+    // P_0 = S0 (zeros when absent), or P_1, for value channels 16 tile .. +15
     for (int e = tid; e < 16 * D / 4; e += kCombineThreads) {
         const int rl = e / (D / 4), d4 = (e % (D / 4)) * 4;
         const size_t off = static_cast<size_t>(16 * tile + rl) * D + d4;
-        const float4 x = S0 ? *reinterpret_cast<const float4*>(S0 + state * kMat + off)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 x = s0 ? *reinterpret_cast<const float4*>(ws + ws_P(slot0 + 1) + off)
+                         : S0 ? *reinterpret_cast<const float4*>(S0 + state * kMat + off)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(&Ps[0][rl][d4]) = x;
-        *reinterpret_cast<float4*>(ws + ws_P(slot0) + off) = x;
+        if (!s0) *reinterpret_cast<float4*>(ws + ws_P(slot0) + off) = x;
     }
     // The maps (M_s, N_s) do not depend on the states: those of step s+1 are
     // loaded while step s runs, and M is split into bf16 pairs ahead of use.
@@ -907,12 +939,12 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(Geo geo, c
             nv[mt] = f32x4{nraw[mt].x, nraw[mt].y, nraw[mt].z, nraw[mt].w};
         }
     };
-    load_maps(0);
+    load_maps(s0);
     split_maps();
-    for (int s = 0; s + 1 < G; ++s) {
+    for (int s = s0; s + 1 < G; ++s) {
         if (s + 2 < G) load_maps(s + 1);
         lds_barrier();
-        const int cur = s & 1;
+        const int cur = (s - s0) & 1;
         f32x4 acc[2] = {nv[0], nv[1]};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -966,36 +998,24 @@ struct OutTiles {
 //                inverse below the diagonal (three waves), A, v | B0
 // The stagers run one chunk ahead: they stage chunk n0 while the carriers
 // wait, and wait through the carriers' last chunk.
-__global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* __restrict__ q,
-                                                           const u16* __restrict__ k, const u16* __restrict__ v,
-                                                           const float* __restrict__ alpha,
-                                                           const float* __restrict__ beta, const float* S0,
-                                                           const float* __restrict__ ws, u16* __restrict__ o,
-                                                           float* S_out) {
-    __shared__ __attribute__((aligned(16))) OutTiles sm;
-    Item it;
-    if (!find_item(geo, blockIdx.x, false, it)) return;
+template <int NCAR>
+__device__ __forceinline__ void out_body(OutTiles& sm, const Geo& geo, const Item& it, const u16* __restrict__ q,
+                                        const u16* __restrict__ k, const u16* __restrict__ v,
+                                        const float* __restrict__ alpha, const float* __restrict__ beta,
+                                        const float* Sin, float* Send, u16* __restrict__ o) {
+    constexpr int NT = 128 / 16 / NCAR;   // 16-column tiles per carrier
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the branches below are scalar
     const int n0 = it.n0, n1 = it.n1, T = it.len;
     const size_t head_tok = it.head_tok;
-    const float* S0h = S0 ? S0 + it.state * kMat : nullptr;
-    if (n0 >= n1) {   // an empty sequence: its state passes through
-        if (w < 4 && S_out) {
-            f32x4 P[2][8];
-            load_state<2>(P, S0h, 32 * w, lane);
-            store_state<2>(P, S_out + it.state * kMat, 32 * w, lane);
-        }
-        return;
-    }
-    if (w < 4) {
-        const int col0 = 32 * w;
-        f32x4 P[2][8];
-        // entering state: S0 itself when the sequence is one segment, else the
-        // combined state (segment 0 included, so S_out may alias S0)
-        load_state<2>(P, it.G == 1 ? S0h : ws + ws_P(it.slot0 + it.seg), col0, lane);
-        // diagonal block w of (I + L)^{-1} of chunk m (staged before the last B1)
-        auto diag = [&](int m) { step1_diag(sm.Ks[m & 1], sm.Tm[m & 1], sm.gt[m & 1], w, lane); };
+    if (w < NCAR) {
+        const int col0 = 16 * NT * w;
+        f32x4 P[NT][8];
+        load_state<NT>(P, Sin, col0, lane);
+        // diagonal block w of (I + L)^{-1} of chunk m (staged before the last B1), waves 0-3
+        auto diag = [&](int m) {
+            if (NCAR == 4 || w < 4) step1_diag(sm.Ks[m & 1], sm.Tm[m & 1], sm.gt[m & 1], w, lane);
+        };
         lds_barrier();  // B1, B2, B0 of chunk n0's staging
         diag(n0);
         lds_barrier();
@@ -1003,40 +1023,40 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
         for (int n = n0; n < n1; ++n) {
             const int cb = n & 1;
             const Gates& gt = sm.gt[cb];
-            f32x4 O[2][4], X[2][4];
-            bf16x8 Xb[2][2], Ub[2][2], Ue[2][2];
-            scan_qk<2, true>(sm.Qs, sm.Ks[cb], P, lane, O, X);
+            f32x4 O[NT][4], X[NT][4];
+            bf16x8 Xb[NT][2], Ub[NT][2], Ue[NT][2];
+            scan_qk<NT, true>(sm.Qs, sm.Ks[cb], P, lane, O, X);
             lds_barrier();  // B1
             TriOps tm, am;
             load_tri(tm, sm.Tm[cb], lane);
-            scan_rhs<2, true>(sm.Vs, gt, X, col0, lane, Xb);
-            scan_solve<2, true>(tm, gt, Xb, lane, Ub, Ue);
+            scan_rhs<NT, true>(sm.Vs, gt, X, col0, lane, Xb);
+            scan_solve<NT, true>(tm, gt, Xb, lane, Ub, Ue);
             load_tri(am, sm.As[cb], lane);   // A of chunk n was formed during chunk n - 1
             if (n + 1 < n1) diag(n + 1);
             lds_barrier();  // B2
             const int t0 = n * C;
-            scan_out<2>(am, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Os);
-            scan_update<2>(sm.Ks[cb], gt, P, Ue, lane);
+            scan_out<NT>(am, gt, O, Ub, col0, lane, o, head_tok + t0, min(C, T - t0), sm.Os);
+            scan_update<NT>(sm.Ks[cb], gt, P, Ue, lane);
             // snapshot of the state after chunk n (packed batches)
             const int end = (n + 1) * C;
             if (geo.snap > 0 && end <= T && end % geo.snap == 0) {
                 const int j = it.snap0 + end / geo.snap - 1;
                 if (j < geo.snap_cap)
-                    store_state<2>(P, geo.S_snap + (static_cast<size_t>(j) * geo.H + it.h) * kMat, col0, lane);
+                    store_state<NT>(P, geo.S_snap + (static_cast<size_t>(j) * geo.H + it.h) * kMat, col0, lane);
             }
             lds_barrier();  // B0
         }
-        if (it.seg == it.G - 1 && S_out) store_state<2>(P, S_out + it.state * kMat, col0, lane);
+        if (Send) store_state<NT>(P, Send, col0, lane);
     } else {
-        const int ptid = tid - kThreads / 2;
-        const int u = w - 4;
+        const int ptid = tid - 64 * NCAR;
+        const int u = w - NCAR;
         // The blocks (0,1) and (2,3) above the diagonal of Tm and A are read by
         // 32-wide operand slices and must be zero; nothing else writes them.
         zero_above((u & 2) ? sm.As[u & 1] : sm.Tm[u & 1], 0, lane);
         zero_above((u & 2) ? sm.As[u & 1] : sm.Tm[u & 1], 5, lane);
         // Each tensor of chunk m+1 is fetched right after the same tensor of
         // chunk m is staged (the last chunk fetches itself again).
-        using RC = RawChunk<kThreads / 2, true>;
+        using RC = RawChunk<256, true>;
         RC rc;
         using yes = std::true_type;
         using no = std::false_type;
@@ -1084,8 +1104,66 @@ __global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* _
     }
 }
 
+__global__ __launch_bounds__(kThreads) void gdn_out_kernel(Geo geo, const u16* __restrict__ q,
+                                                           const u16* __restrict__ k, const u16* __restrict__ v,
+                                                           const float* __restrict__ alpha,
+                                                           const float* __restrict__ beta, const float* S0,
+                                                           const float* __restrict__ ws, u16* __restrict__ o,
+                                                           float* S_out) {
+    __shared__ __attribute__((aligned(16))) OutTiles sm;
+    Item it;
+    if (!find_item(geo, blockIdx.x, false, it)) return;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float* S0h = S0 ? S0 + it.state * kMat : nullptr;
+    float* Send = it.seg == it.G - 1 && S_out ? S_out + it.state * kMat : nullptr;
+    if (it.n0 >= it.n1) {   // an empty sequence: its state passes through
+        if (w < 4 && S_out) {
+            f32x4 P[2][8];
+            load_state<2>(P, S0h, 32 * w, threadIdx.x & 63);
+            store_state<2>(P, S_out + it.state * kMat, 32 * w, threadIdx.x & 63);
+        }
+        return;
+    }
+    // entering state: S0 itself when the sequence is one segment, else the
+    // combined state (segment 0 included, so S_out may alias S0)
+    out_body<4>(sm, geo, it, q, k, v, alpha, beta, it.G == 1 ? S0h : ws + ws_P(it.slot0 + it.seg), Send, o);
+}
+
+// ---- pass 1 with a lead segment (uniform batches).  The map pass has one
+// workgroup fewer per head than the output pass (the last segment needs no
+// map), so it leaves CUs idle; with a lead segment, workgroups 0..BH-1 run
+// segment 0 of their head from S0 instead (its outputs, and its final state
+// P_1 into the workspace), while the others compute the maps of segments
+// 1..G-2.  The output pass then runs segments 1..G-1.  Both roles use the
+// map kernel's 768 threads: the lead role runs the output kernel's work with
+// eight carriers of 16 value channels (and the four stagers).
+union PassOneTiles {
+    MapTiles m;
+    OutTiles o;
+};
+
+__global__ __launch_bounds__(kMapThreads) void gdn_lead_map_kernel(Geo geo, const u16* __restrict__ q,
+                                                                   const u16* __restrict__ k,
+                                                                   const u16* __restrict__ v,
+                                                                   const float* __restrict__ alpha,
+                                                                   const float* __restrict__ beta, const float* S0,
+                                                                   float* __restrict__ ws, u16* __restrict__ o) {
+    __shared__ __attribute__((aligned(16))) PassOneTiles sm;
+    Item it;
+    const int blk = blockIdx.x;
+    if (blk < geo.BH) {
+        lead_item(geo, blk, it);
+        out_body<8>(sm.o, geo, it, q, k, v, alpha, beta, S0 ? S0 + it.state * kMat : nullptr,
+                    ws + ws_P(it.slot0 + 1), o);
+        return;
+    }
+    if (!find_item(geo, blk - geo.BH, true, it)) return;
+    map_body(sm.m, it, k, v, alpha, beta, ws);
+}
+
 struct Plan {
     int NC, G, SEGC;
+    int L0, lead;   // chunks of segment 0; whether it runs in the map pass
 };
 
 // Segments per head so that B*H*G workgroups roughly fill the chip.
@@ -1097,16 +1175,60 @@ Plan make_plan(int BH, int T) {
     if (G > p.NC) G = p.NC;
     p.SEGC = (p.NC + G - 1) / G;
     p.G = (p.NC + p.SEGC - 1) / p.SEGC;  // every segment non-empty
+    p.L0 = p.SEGC;
+    p.lead = 0;
     return p;
 }
 
-Geo uniform_geo(int BH, int T) {
-    const Plan p = make_plan(BH, T);
+// Expected time of a plan, in output-pass chunk times: the longest map-pass
+// workgroup, the combine chain and the longest output-pass workgroup.  Per
+// chunk, measured against an output-pass chunk: a map chunk 0.94-1.045 (taken
+// as 1), a lead chunk (eight 16-channel carriers) 1.25 (taken as 1.3, so that
+// the lead segment does not set the pace), a combine step 0.45.
+double plan_cost(const Plan& p) {
+    if (p.G < 2) return p.NC;
+    if (!p.lead) return p.SEGC + 0.45 * (p.G - 1) + p.SEGC;
+    const double pass1 = std::max(1.3 * p.L0, p.G > 2 ? 1.0 * p.SEGC : 0.0);
+    return pass1 + 0.45 * (p.G - 2) + p.SEGC;
+}
+
+// The plan of a whole prefill call: with a lead segment (segment 0 in the map
+// pass, G = slots + 1 segments, segments 1..G-1 of SEGC chunks and segment 0
+// of the rest) when that is expected to be at least 3% faster, else the plain
+// plan.  gdn_prefill_prep / gdn_prefill_scan always use the plain plan (the
+// lead segment needs S0 and writes o, which prep does not take).
+Plan make_step_plan(int BH, int T) {
+    Plan best = make_plan(BH, T);
+    if (best.G < 2 || BH <= 0) return best;
+    const int slots = kTargetBlocks / BH;
+    if (slots < 2) return best;
+    const double plain = plan_cost(best);
+    double best_cost = 0.97 * plain;
+    for (int S = (best.NC + slots) / (slots + 1); S >= 1 && slots * S < best.NC; ++S) {
+        Plan q;
+        q.NC = best.NC;
+        q.G = slots + 1;
+        q.SEGC = S;
+        q.L0 = best.NC - slots * S;
+        q.lead = 1;
+        if (q.L0 < 1) continue;
+        const double c = plan_cost(q);
+        if (c < best_cost) {
+            best_cost = c;
+            best = q;
+        }
+    }
+    return best;
+}
+
+Geo uniform_geo(const Plan& p, int BH, int T) {
     Geo g{};
     g.BH = BH;
     g.T = T;
     g.G = p.G;
     g.SEGC = p.SEGC;
+    g.L0 = p.L0;
+    g.lead = p.lead;
     return g;
 }
 
@@ -1208,21 +1330,32 @@ hipError_t launch_uniform(int B, int H, int T, const void* q, const void* k, con
                           bool scan, hipStream_t stream) {
     const int BH = B * H;
     if (BH <= 0 || T <= 0) return hipSuccess;
-    const Geo g = uniform_geo(BH, T);
+    const Geo g = uniform_geo(prep && scan ? make_step_plan(BH, T) : make_plan(BH, T), BH, T);
+    float* ws = static_cast<float*>(workspace);
+    if (g.lead) {   // (G >= 3 by construction: slots >= 2)
+        hipLaunchKernelGGL(gdn_lead_map_kernel, dim3(static_cast<unsigned>(BH * (g.G - 1))), dim3(kMapThreads), 0,
+                           stream, g, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                           static_cast<const u16*>(v), alpha, beta, S0, ws, static_cast<u16*>(o));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_all(g, 0, BH, BH * (g.G - 1), q, k, v, alpha, beta, S0, o, S_out, ws, false, true, stream);
+    }
     const bool multi = g.G > 1;
     return launch_all(g, multi ? BH * (g.G - 1) : 0, multi ? BH : 0, BH * g.G, q, k, v, alpha, beta, S0, o, S_out,
-                      static_cast<float*>(workspace), prep, scan, stream);
+                      ws, prep, scan, stream);
 }
 
 // ---- a workspace held by the library, for callers that cannot allocate.
-// The uniform plan never makes more than kTargetBlocks (head, segment) items,
-// so kScratchBytes (48 MiB) covers every uniform call.  The array is part of
+// The plain uniform plan makes at most kTargetBlocks (head, segment) items and
+// the lead plan BH (slots + 1) with slots = kTargetBlocks / BH >= 2, so at
+// most kTargetBlocks + kTargetBlocks / 2: kScratchBytes (72 MiB) covers every
+// uniform call.  The array is part of
 // the code object: each device the library runs on holds its own copy from
 // the first launch until the process ends.  Host code must not use the
 // array's name as an address (on the host it is only a stand-in); the device
 // address comes from hipGetSymbolAddress, looked up once per device with that
 // device current, and is kept per device.
-constexpr size_t kScratchBytes = static_cast<size_t>(kTargetBlocks) * 3 * kMat * sizeof(float);
+constexpr size_t kScratchBytes = static_cast<size_t>(kTargetBlocks + kTargetBlocks / 2) * 3 * kMat * sizeof(float);
 constexpr int kScratchDevices = 64;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 std::mutex scratch_mutex;
@@ -1257,9 +1390,11 @@ bool gdn_mfma_supported(int dtype, int dk, int dv, int chunk) {
 size_t gdn_mfma_workspace_bytes(int B, int H, int T, int, int, int) {
     const int BH = B * H;
     if (BH <= 0 || T <= 0) return 0;
-    const Plan p = make_plan(BH, T);
-    if (p.G == 1) return 0;
-    return static_cast<size_t>(BH) * p.G * 3 * kMat * sizeof(float);
+    // one size for gdn_prefill (plain or lead plan) and prep / scan (plain)
+    const Plan p = make_plan(BH, T), s = make_step_plan(BH, T);
+    const int G = std::max(p.G, s.G);
+    if (G == 1) return 0;
+    return static_cast<size_t>(BH) * G * 3 * kMat * sizeof(float);
 }
 
 hipError_t launch_gdn_mfma_prep(int B, int H, int T, const void* q, const void* k, const void* v, const float* alpha,
@@ -1300,6 +1435,7 @@ hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
     int* tab = static_cast<int*>(workspace);
     Geo g{};
     g.SEGC = p.SEGC;
+    g.L0 = p.SEGC;
     g.cu = cu;
     g.seg_base = tab;
     g.snap_base = tab + (N + 1);

@@ -170,7 +170,7 @@ la_status gdn_prefill(int dtype, int B, int H, int T, int dk, int dv,
  *
  * Same operation, arguments, layouts and errors as gdn_prefill (workspace and
  * ws_bytes omitted).  Where gdn_prefill needs a workspace, this call uses one
- * array in the library's own device memory instead: 48 MiB per device
+ * array in the library's own device memory instead: 72 MiB per device
  * (la_workspace_bytes(LA_FN_GDN_PREFILL, ...) never exceeds it for the
  * supported shapes; a call that would need more returns LA_ERR_WORKSPACE),
  * held by every device the library runs on until the process ends.  The call
@@ -202,9 +202,12 @@ la_status gdn_prefill_noalloc(int dtype, int B, int H, int T, int dk, int dv,
  *   scan: composes the maps with S0 into each segment's entering state, then
  *     computes o and S_out for all segments in parallel; reads q, k, v,
  *     alpha, beta and the workspace written by prep for the same B, H, T.
- * gdn_prefill(..., LA_FORM_CHUNKED, 64, ...) is exactly prep followed by scan
- * on one stream.  Callers that split them must order scan after prep (e.g.
- * with an event) and must not reuse the workspace before scan has finished.
+ * gdn_prefill(..., LA_FORM_CHUNKED, 64, ...) computes the same result; it may
+ * cut the sequence differently (its first segment runs beside the maps, which
+ * needs S0 and o, so only the one-call form can do it), so the two agree to
+ * rounding, not bit for bit.  Callers that split them must order scan after
+ * prep (e.g. with an event) and must not reuse the workspace before scan has
+ * finished.
  * The workspace layout is private to the library; when a single segment
  * covers the sequence the workspace size is 0 and prep does nothing.
  */

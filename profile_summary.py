@@ -57,7 +57,8 @@ def kernel_key(name, tag, wg=None):
     s = short_name(name)
     base = s.split("<")[0]
     targs = [a.strip() for a in s[len(base) + 1:-1].split(",")] if "<" in s else []
-    if base in ("gdn_map_kernel", "gdn_combine_kernel", "gdn_out_kernel", "gdn_varlen_plan_kernel"):
+    if base in ("gdn_map_kernel", "gdn_lead_map_kernel", "gdn_combine_kernel", "gdn_out_kernel",
+                "gdn_varlen_plan_kernel"):
         return base + ("_varlen_16seq" if tag == "legs" else "")
     if base == "la_chunked_mfma_kernel" and len(targs) == 3:   # <GATED, OUT, PACKED>
         return (("gla" if targs[0] == "true" else "la") + "_chunked_mfma_kernel_" +

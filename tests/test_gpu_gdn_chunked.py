@@ -48,6 +48,36 @@ def test_gdn_mfma_small(gd, B, H, T, amean, with_state):
     report("  S", slice_err(S, S_ref), TOL["bf16"])
 
 
+@pytest.mark.parametrize("alpha_one", [True, False])
+def test_gdn_mfma_lead_segment_and_split_calls(gd, alpha_one):
+    """64 heads of 640 tokens: one gdn_prefill call cuts each head as a lead
+    segment of 2 chunks (run beside the maps) and four of 2, the split calls
+    gdn_prefill_prep + gdn_prefill_scan as four segments of 3, 3, 3, 1 chunks.
+    Both against the oracle on every head, with a carried state, and with no
+    decay (alpha = 1, the entering states of later segments depend on every
+    earlier token) as well as with decay; and against each other."""
+    import torch
+    B, H, T = 1, 64, 640
+    q, k, v, a, b = synth.gdn_batch(35, B, H, T, D, D, "bf16")
+    if alpha_one:
+        a = np.ones_like(a)
+    S0 = synth.state_batch(36, B, H, D, D, 0.05)
+    o_ref, S_ref = ob.gdn(q, k, v, a, b, form="chunked", chunk=C, S0=S0)
+    o1, S1 = run_gpu(gd, q, k, v, a, b, S0)
+    tag = "alpha=1" if alpha_one else "alpha~sig(N(3,1))"
+    report(f"gdn mfma one call (lead segment), {tag} o", slice_err(o1, o_ref), TOL["bf16"])
+    report("  S", slice_err(S1, S_ref), TOL["bf16"])
+    x = [to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(a, "f32"), to_dev(b, "f32")]
+    ws = gd.gdn_workspace(x[0], x[2], C)
+    gd.gdn_prefill_prep(*x, ws, chunk=C)
+    o2, S2 = gd.gdn_prefill_scan(*x, ws, to_dev(S0, "f32"), chunk=C)
+    torch.cuda.synchronize()
+    o2, S2 = to_host(o2), to_host(S2)
+    report(f"gdn mfma prep + scan, {tag} o", slice_err(o2, o_ref), TOL["bf16"])
+    report("  S", slice_err(S2, S_ref), TOL["bf16"])
+    report("  one call vs prep + scan, o", slice_err(o1, o2), TOL["bf16"])
+
+
 def test_gdn_mfma_plain_delta_rule(gd):
     """alpha = 1 (no decay): the state is carried across every chunk unchanged
     except by the delta-rule writes."""

@@ -34,7 +34,7 @@ def _case(gd, seed, B, H, T, with_state, heads):
     args = [to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(a, "f32"), to_dev(b, "f32")]
     tS = None if S0 is None else to_dev(S0, "f32")
     ws_need = gd.la_workspace_bytes("gdn_prefill", "bf16", B, H, T, D, D, "chunked", C)
-    assert 0 < ws_need <= 48 << 20, ws_need
+    assert 0 < ws_need <= 72 << 20, ws_need
     o_ref_dev, S_ref_dev = gd.gdn_prefill(*args, tS, form="chunked", chunk=C)
     out = torch.empty_like(args[2])
     S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=out.device)
@@ -57,7 +57,7 @@ def _case(gd, seed, B, H, T, with_state, heads):
 
 
 def test_noalloc_two_calls_second_smaller(gd):
-    # first call: the 2 x 16 x 8192 workload fills the whole array (256
+    # first call: the 2 x 16 x 8192 workload (288 of the array's 384
     # head-segments); second call: fewer heads, a ragged length and a carried
     # state, so it reads only the part of the array it writes itself
     _case(gd, 71, 2, 16, 8192, False, [(0, 0), (1, 15)])
