@@ -632,6 +632,7 @@ struct Geo {
     const int* cu;
     const int* seg_base;
     const int* snap_base;
+    const int* order;   // packed: segments longest first (workgroup i takes order[i])
     int N, H, Ttot, Gcap;
     int snap, snap_cap;
     float* S_snap;
@@ -666,8 +667,9 @@ __device__ __forceinline__ bool find_item(const Geo& g, int blk, bool maps, Item
         it.snap0 = 0;
         it.h = 0;
     } else {
-        const int h = blk % g.H, gs = blk / g.H;
-        if (gs >= g.seg_base[g.N]) return false;
+        const int h = blk % g.H, i = blk / g.H;
+        if (i >= min(g.seg_base[g.N], g.Gcap)) return false;
+        const int gs = g.order ? g.order[i] : i;
         int lo = 0, hi = g.N;  // seg_base[lo] <= gs < seg_base[hi]; every sequence has a segment
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -1249,30 +1251,34 @@ VarPlan make_var_plan(int N, int H, int Ttot) {
     if (segc < 1) segc = 1;
     p.SEGC = static_cast<int>(segc);
     p.Gcap = static_cast<int>(chunks / segc + N + 1);
-    p.table_bytes = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    // seg_base, snap_base ([N+1] each), order ([Gcap])
+    p.table_bytes = ((2 * (static_cast<size_t>(N) + 1) + p.Gcap) * sizeof(int) + 255) / 256 * 256;
     return p;
 }
 
-// seg_base and snap_base by a block-wide exclusive scan over the sequences.
+// seg_base and snap_base by a block-wide exclusive scan over the sequences;
+// with `order`, then a counting sort of the segments by descending chunk count
+// (bins in LDS, positions taken with LDS atomics: the order within a bin is
+// arbitrary, and every workgroup computes the same thing whatever its place).
 constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, int Ttot, int SEGC, int snap,
                                                                        const int* __restrict__ cu, int* seg_base,
-                                                                       int* snap_base) {
+                                                                       int* snap_base, int* order, int cap) {
     __shared__ int part[2][kPlanThreads];
     const int tid = threadIdx.x;
     const int per = (N + kPlanThreads - 1) / kPlanThreads;
     const int a = min(N, tid * per), b = min(N, a + per);
-    auto counts = [&](int n, int& segs, int& snaps) {
+    auto counts = [&](int n, int& segs, int& snaps, int& nc) {
         const int t0 = clamp_tok(cu[n], Ttot), t1 = clamp_tok(cu[n + 1], Ttot);
         const int len = t1 > t0 ? t1 - t0 : 0;
-        const int nc = (len + C - 1) / C;
+        nc = (len + C - 1) / C;
         segs = nc > 0 ? (nc + SEGC - 1) / SEGC : 1;
         snaps = snap > 0 ? len / snap : 0;
     };
     int ss = 0, sn = 0;
     for (int n = a; n < b; ++n) {
-        int g, z;
-        counts(n, g, z);
+        int g, z, nc;
+        counts(n, g, z, nc);
         ss += g;
         sn += z;
     }
@@ -1288,12 +1294,13 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
         part[1][tid] += x1;
         __syncthreads();
     }
-    int gb = part[0][tid] - ss, zb = part[1][tid] - sn;   // exclusive
+    const int gb0 = part[0][tid] - ss;   // exclusive
+    int gb = gb0, zb = part[1][tid] - sn;
     for (int n = a; n < b; ++n) {
         seg_base[n] = gb;
         snap_base[n] = zb;
-        int g, z;
-        counts(n, g, z);
+        int g, z, nc;
+        counts(n, g, z, nc);
         gb += g;
         zb += z;
     }
@@ -1301,6 +1308,37 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
         seg_base[N] = part[0][tid];
         snap_base[N] = part[1][tid];
     }
+    if (order == nullptr) return;
+    // ---- segments longest first: bin kPlanThreads - 1 - chunks (chunk counts
+    // past the last bin share it), histogram, exclusive scan, scatter
+    int* hist = part[0];
+    __syncthreads();   // the scan's last reads of part are done
+    hist[tid] = 0;
+    __syncthreads();
+    auto each_segment = [&](auto&& fn) {
+        int base = gb0;
+        for (int n = a; n < b; ++n) {
+            int g, z, nc;
+            counts(n, g, z, nc);
+            for (int s = 0; s < g && base + s < cap; ++s) {
+                const int ch = min(SEGC, nc - s * SEGC);   // 0 for an empty sequence
+                fn(base + s, kPlanThreads - 1 - min(max(ch, 0), kPlanThreads - 1));
+            }
+            base += g;
+        }
+    };
+    each_segment([&](int, int bin) { atomicAdd(&hist[bin], 1); });
+    __syncthreads();
+    const int own = hist[tid];
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int x = tid >= off ? hist[tid - off] : 0;
+        __syncthreads();
+        hist[tid] += x;
+        __syncthreads();
+    }
+    hist[tid] -= own;   // exclusive: the first position of bin tid
+    __syncthreads();
+    each_segment([&](int gs, int bin) { order[atomicAdd(&hist[bin], 1)] = gs; });
 }
 
 hipError_t launch_all(const Geo& g, int map_blocks, int combine_items, int out_blocks, const void* q, const void* k,
@@ -1414,10 +1452,11 @@ hipError_t launch_gdn_mfma(int B, int H, int T, const void* q, const void* k, co
     return launch_uniform(B, H, T, q, k, v, alpha, beta, S0, o, S_out, workspace, true, true, stream);
 }
 
-hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream) {
+hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream,
+                               int* order, int cap) {
     if (N <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, N, Ttot, segc < 1 ? 1 : segc,
-                       snap, cu, tab, tab + (N + 1));
+                       snap, cu, tab, tab + (N + 1), order, order ? cap : 0);
     return hipGetLastError();
 }
 
@@ -1439,6 +1478,7 @@ hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
     g.cu = cu;
     g.seg_base = tab;
     g.snap_base = tab + (N + 1);
+    g.order = tab + 2 * (N + 1);
     g.N = N;
     g.H = H;
     g.Ttot = Ttot;
@@ -1446,7 +1486,7 @@ hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
     g.snap = S_snap ? snap : 0;
     g.snap_cap = snap_cap;
     g.S_snap = S_snap;
-    const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream);
+    const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream, tab + 2 * (N + 1), p.Gcap);
     if (e != hipSuccess) return e;
     float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.table_bytes);
     const int blocks = p.Gcap * H;   // (segment, head) items, a bound; the extra workgroups exit

@@ -42,8 +42,12 @@ hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int d
                             const float* S0, float* S_out, const float* z0, float* z_out,
                             void* o, hipStream_t stream, const Packed& pk = Packed{});
 // The packed-batch table of seg_base / snap_base ([N+1] ints each, at tab and
-// tab + N + 1) on the device, from cu (1 workgroup).
-hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream);
+// tab + N + 1) on the device, from cu (1 workgroup).  With order != nullptr
+// (room for cap ints) it also lists the first min(segments, cap) segments,
+// numbered as seg_base numbers them, longest first: a workgroup per segment
+// taken in that order starts the long chains first.
+hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream,
+                               int* order = nullptr, int cap = 0);
 
 // ---- normalised linear attention, masked parallel form (la_parallel.hip) -
 hipError_t launch_la_parallel(int dtype, int heads, int T, int dk, int dv,

@@ -82,6 +82,7 @@ struct LGeo {
     const int* cu;
     const int* seg_base;
     const int* snap_base;
+    const int* order;   // packed: segments longest first (workgroup i takes order[i])
     int N, H, Ttot, Gcap;
     int snap, snap_cap;   // packed: snapshots of (S, z) after every `snap` tokens (a multiple of C)
     float* S_snap;
@@ -115,8 +116,9 @@ __device__ __forceinline__ bool la_item(const LGeo& g, int blk, bool out, LItem&
         it.snap0 = 0;
         it.h = 0;
     } else {
-        const int h = blk % g.H, gs = blk / g.H;
-        if (gs >= g.seg_base[g.N]) return false;
+        const int h = blk % g.H, i = blk / g.H;
+        if (i >= min(g.seg_base[g.N], g.Gcap)) return false;
+        const int gs = g.order ? g.order[i] : i;
         int lo = 0, hi = g.N;   // seg_base[lo] <= gs < seg_base[hi]; every sequence has a segment
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -685,7 +687,8 @@ LVarPlan make_lvar_plan(int N, int H, int Ttot) {
     if (segc < 1) segc = 1;
     p.SEGC = static_cast<int>(segc);
     p.Gcap = static_cast<int>(chunks / segc + N + 1);
-    p.table_bytes = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    // seg_base, snap_base ([N+1] each), order ([Gcap])
+    p.table_bytes = ((2 * (static_cast<size_t>(N) + 1) + p.Gcap) * sizeof(int) + 255) / 256 * 256;
     return p;
 }
 
@@ -701,6 +704,7 @@ hipError_t launch_packed(int N, int H, int Ttot, const int* cu, const void* q, c
     g.cu = cu;
     g.seg_base = tab;
     g.snap_base = tab + (N + 1);
+    g.order = tab + 2 * (N + 1);
     g.N = N;
     g.H = H;
     g.Ttot = Ttot;
@@ -709,7 +713,7 @@ hipError_t launch_packed(int N, int H, int Ttot, const int* cu, const void* q, c
     g.snap_cap = snap_cap;
     g.S_snap = S_snap;
     g.z_snap = z_snap;
-    const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream);
+    const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream, tab + 2 * (N + 1), p.Gcap);
     if (e != hipSuccess) return e;
     float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.table_bytes);
     const int blocks = p.Gcap * H;   // (segment, head) items, a bound; the extra workgroups exit
