@@ -1263,7 +1263,8 @@ VarPlan make_var_plan(int N, int H, int Ttot) {
 constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, int Ttot, int SEGC, int snap,
                                                                        const int* __restrict__ cu, int* seg_base,
-                                                                       int* snap_base, int* order, int cap) {
+                                                                       int* snap_base, int* order, int cap,
+                                                                       int* seq_order) {
     __shared__ int part[2][kPlanThreads];
     const int tid = threadIdx.x;
     const int per = (N + kPlanThreads - 1) / kPlanThreads;
@@ -1308,13 +1309,40 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
         seg_base[N] = part[0][tid];
         snap_base[N] = part[1][tid];
     }
-    if (order == nullptr) return;
-    // ---- segments longest first: bin kPlanThreads - 1 - chunks (chunk counts
-    // past the last bin share it), histogram, exclusive scan, scatter
+    if (order == nullptr && seq_order == nullptr) return;
+    // ---- longest first: bin kPlanThreads - 1 - chunks (chunk counts past the
+    // last bin share it), histogram, exclusive scan, scatter
     int* hist = part[0];
-    __syncthreads();   // the scan's last reads of part are done
-    hist[tid] = 0;
-    __syncthreads();
+    auto sort_by_chunks = [&](auto&& each) {
+        __syncthreads();   // earlier reads of part are done
+        hist[tid] = 0;
+        __syncthreads();
+        each([&](int, int bin) { atomicAdd(&hist[bin], 1); });
+        __syncthreads();
+        const int own = hist[tid];
+        for (int off = 1; off < kPlanThreads; off <<= 1) {
+            const int x = tid >= off ? hist[tid - off] : 0;
+            __syncthreads();
+            hist[tid] += x;
+            __syncthreads();
+        }
+        hist[tid] -= own;   // exclusive: the first position of bin tid
+        __syncthreads();
+    };
+    auto bin_of = [&](int chunks) { return kPlanThreads - 1 - min(max(chunks, 0), kPlanThreads - 1); };
+    // sequences (seq_order: every sequence, by its chunk count)
+    auto each_sequence = [&](auto&& fn) {
+        for (int n = a; n < b; ++n) {
+            int g, z, nc;
+            counts(n, g, z, nc);
+            fn(n, bin_of(nc));
+        }
+    };
+    if (seq_order) {
+        sort_by_chunks(each_sequence);
+        each_sequence([&](int n, int bin) { seq_order[atomicAdd(&hist[bin], 1)] = n; });
+    }
+    if (order == nullptr) return;
     auto each_segment = [&](auto&& fn) {
         int base = gb0;
         for (int n = a; n < b; ++n) {
@@ -1322,22 +1350,12 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
             counts(n, g, z, nc);
             for (int s = 0; s < g && base + s < cap; ++s) {
                 const int ch = min(SEGC, nc - s * SEGC);   // 0 for an empty sequence
-                fn(base + s, kPlanThreads - 1 - min(max(ch, 0), kPlanThreads - 1));
+                fn(base + s, bin_of(ch));
             }
             base += g;
         }
     };
-    each_segment([&](int, int bin) { atomicAdd(&hist[bin], 1); });
-    __syncthreads();
-    const int own = hist[tid];
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int x = tid >= off ? hist[tid - off] : 0;
-        __syncthreads();
-        hist[tid] += x;
-        __syncthreads();
-    }
-    hist[tid] -= own;   // exclusive: the first position of bin tid
-    __syncthreads();
+    sort_by_chunks(each_segment);
     each_segment([&](int gs, int bin) { order[atomicAdd(&hist[bin], 1)] = gs; });
 }
 
@@ -1453,10 +1471,10 @@ hipError_t launch_gdn_mfma(int B, int H, int T, const void* q, const void* k, co
 }
 
 hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream,
-                               int* order, int cap) {
+                               int* order, int cap, int* seq_order) {
     if (N <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, N, Ttot, segc < 1 ? 1 : segc,
-                       snap, cu, tab, tab + (N + 1), order, order ? cap : 0);
+                       snap, cu, tab, tab + (N + 1), order, order ? cap : 0, seq_order);
     return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ struct KGeo {
     const int* cu;
     const int* chunk_base;
     const int* snap_base;
+    const int* seq_order;   // packed: sequences longest first (the scan takes them in that order)
     int N, H, Ttot, cap;
     int snap, snap_cap;   // snapshots of P after every `snap` tokens (a multiple of C), slots below snap_cap
     float* S_snap;
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(KGeo geo, const 
     const int cb = (i >> 3) & 7;
     int T, NC, hh = 0, snap0 = 0;
     const unsigned char* rec0;
-    size_t orow;
+    size_t orow, state = bh;   // index of the (sequence, head) state in S0 / S_out
     if (geo.cu == nullptr) {
         if (bh >= geo.BH) return;
         T = geo.T;
@@ -594,8 +595,10 @@ __global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(KGeo geo, const 
         orow = static_cast<size_t>(bh) * T;
     } else {
         if (bh >= geo.N * geo.H) return;
-        const int sq = bh / geo.H;
-        hh = bh - sq * geo.H;
+        const int si = bh / geo.H;
+        hh = bh - si * geo.H;
+        const int sq = geo.seq_order ? geo.seq_order[si] : si;
+        state = static_cast<size_t>(sq) * geo.H + hh;
         const int t0 = kclamp(geo.cu[sq], geo.Ttot), t1 = kclamp(geo.cu[sq + 1], geo.Ttot);
         T = t1 > t0 ? t1 - t0 : 0;
         // a table that is not non-decreasing can promise more chunks than the
@@ -610,7 +613,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_scan_kernel(KGeo geo, const 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, gg = lane >> 4;
-    const size_t sbase = static_cast<size_t>(bh) * D * D;
+    const size_t sbase = state * D * D;
     // P[key c][value col] = S0[col][c]: this lane holds c = 32w + 16mt + 4gg + i, col = 16cb + r
     f32x4 P[2];
 #pragma unroll
@@ -703,11 +706,14 @@ hipError_t launch_kda_mfma(int B, int H, int T, const void* q, const void* k, co
                       stream);
 }
 
-// Packed batches: a device-built table (chunk_base, snap_base: [N+1] each)
-// ahead of the records; at most Ttot / C + N chunks per head.
+// Packed batches: a device-built table (chunk_base, snap_base: [N+1] each;
+// the sequences longest first: [N]) ahead of the records; at most Ttot / C + N
+// chunks per head.
+static size_t kda_table_bytes(int N) { return ((3 * static_cast<size_t>(N) + 2) * sizeof(int) + 255) / 256 * 256; }
+
 size_t kda_mfma_varlen_workspace_bytes(int N, int H, int Ttot) {
     if (N <= 0 || H <= 0) return 0;
-    const size_t table = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    const size_t table = kda_table_bytes(N);
     const size_t cap = static_cast<size_t>(Ttot) / C + N;
     return table + static_cast<size_t>(H) * cap * kRecord;
 }
@@ -716,12 +722,13 @@ hipError_t launch_kda_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
                                   const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                                   int snap, int snap_cap, float* S_snap, void* workspace, hipStream_t stream) {
     if (N <= 0 || H <= 0) return hipSuccess;
-    const size_t table = (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256;
+    const size_t table = kda_table_bytes(N);
     int* tab = static_cast<int*>(workspace);
     KGeo g{};
     g.cu = cu;
     g.chunk_base = tab;
     g.snap_base = tab + (N + 1);
+    g.seq_order = tab + 2 * (N + 1);
     g.N = N;
     g.H = H;
     g.Ttot = Ttot;
@@ -730,7 +737,7 @@ hipError_t launch_kda_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
     g.snap_cap = snap_cap;
     g.S_snap = S_snap;
     // chunk_base: one "segment" per chunk (an empty sequence counts one)
-    const hipError_t e = launch_varlen_table(N, Ttot, 1, g.snap, cu, tab, stream);
+    const hipError_t e = launch_varlen_table(N, Ttot, 1, g.snap, cu, tab, stream, nullptr, 0, tab + 2 * (N + 1));
     if (e != hipSuccess) return e;
     return kda_launch(g, g.cap * H, N * H, q, k, v, alpha, beta, S0, o, S_out,
                       static_cast<unsigned char*>(workspace) + table, stream);

@@ -45,9 +45,10 @@ hipError_t launch_recurrent(int kind, int dtype, int heads, int T, int dk, int d
 // tab + N + 1) on the device, from cu (1 workgroup).  With order != nullptr
 // (room for cap ints) it also lists the first min(segments, cap) segments,
 // numbered as seg_base numbers them, longest first: a workgroup per segment
-// taken in that order starts the long chains first.
+// taken in that order starts the long chains first.  With seq_order != nullptr
+// (room for N ints) it lists the sequences longest first.
 hipError_t launch_varlen_table(int N, int Ttot, int segc, int snap, const int* cu, int* tab, hipStream_t stream,
-                               int* order = nullptr, int cap = 0);
+                               int* order = nullptr, int cap = 0, int* seq_order = nullptr);
 
 // ---- normalised linear attention, masked parallel form (la_parallel.hip) -
 hipError_t launch_la_parallel(int dtype, int heads, int T, int dk, int dv,
