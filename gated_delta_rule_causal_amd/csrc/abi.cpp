@@ -59,7 +59,8 @@ la_status copy_state(const float* src, float* dst, size_t n, hipStream_t s) {
 }
 
 // seg_base and snap_base of a packed batch, [N+1] ints each, rounded to 256 bytes
-size_t varlen_table_bytes(int N) { return N > 0 ? (2 * (static_cast<size_t>(N) + 1) * sizeof(int) + 255) / 256 * 256 : 0; }
+// seg_base, snap_base ([N+1] each) and the sequences longest first ([N])
+size_t varlen_table_bytes(int N) { return N > 0 ? ((3 * static_cast<size_t>(N) + 2) * sizeof(int) + 255) / 256 * 256 : 0; }
 
 size_t la_prefill_ws(int dtype, int B, int H, int T, int dk, int dv, int form, int chunk) {
     if (form == LA_FORM_CHUNKED && la::la_mfma_supported(dtype, dk, dv, chunk))
@@ -475,7 +476,9 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
     pk.snap = S_snap ? snap_interval : 0;
     pk.snap_cap = snap_count;
     pk.S_snap = S_snap;
-    const hipError_t e = la::launch_varlen_table(N, T_total, 1, pk.snap, cu_seqlens, tab, s);
+    pk.seq_order = tab + 2 * (N + 1);
+    const hipError_t e = la::launch_varlen_table(N, T_total, 1, pk.snap, cu_seqlens, tab, s, nullptr, 0,
+                                                 tab + 2 * (N + 1));
     if (e != hipSuccess) return LA_ERR_HIP;
     return from_hip(la::launch_recurrent(la::kGatedDelta, dtype, N * H, T_total, dk, dv, q, k, v, alpha, beta, S0,
                                          S_out, nullptr, nullptr, o, s, pk));
@@ -575,7 +578,9 @@ la_status lin_attn_prefill_varlen(int kind, int dtype, int N, int H, int T_total
     pk.snap_cap = snap_count;
     pk.S_snap = snaps ? S_snap : nullptr;
     pk.z_snap = snaps && has_z ? z_snap : nullptr;
-    const hipError_t e = la::launch_varlen_table(N, T_total, 1, pk.snap, cu_seqlens, tab, s);
+    pk.seq_order = tab + 2 * (N + 1);
+    const hipError_t e = la::launch_varlen_table(N, T_total, 1, pk.snap, cu_seqlens, tab, s, nullptr, 0,
+                                                 tab + 2 * (N + 1));
     if (e != hipSuccess) return LA_ERR_HIP;
     const int k_kind = kind == LA_KIND_GATED ? la::kGated : kind == LA_KIND_KDA ? la::kKda : la::kNormalized;
     return from_hip(la::launch_recurrent(k_kind, dtype, N * H, T_total, dk, dv, q, k, v, alpha, beta, S0, S_out,

@@ -28,10 +28,12 @@ __host__ __device__ inline bool mfma_chunk_ok(int chunk) {
 // Packed batch (cu != nullptr): heads = N*H; head i = n*H + h runs tokens
 // cu[n]..cu[n+1] of row block h of [H][Ttot][d] (gates [H][Ttot]) with state
 // i, T is ignored, and after every `snap` tokens (0: never) the state goes to
-// S_snap[snap_base[n] + j][h] for the first snap_cap slots.
+// S_snap[snap_base[n] + j][h] for the first snap_cap slots.  With seq_order,
+// block group i takes sequence seq_order[i / H] (longest first).
 struct Packed {
     const int* cu = nullptr;
     const int* snap_base = nullptr;
+    const int* seq_order = nullptr;
     int H = 0, Ttot = 0, snap = 0, snap_cap = 0;
     float* S_snap = nullptr;
     float* z_snap = nullptr;   // normalised kind: z at the same positions as S_snap

@@ -177,14 +177,16 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     typename IO::T* __restrict__ o, Packed pk) {
     constexpr int LPR = RowSlice<DK>::LPR;
     constexpr int RG = RowSlice<DK>::RG;
-    const int head = blockIdx.x / SPLIT;   // state index (packed: sequence * H + head)
+    int head = blockIdx.x / SPLIT;   // state index (packed: sequence * H + head)
     // token rows of this head: [head][T] (uniform) or tokens cu[n].. of row
     // block h of [H][Ttot] (packed batch)
     size_t tok0 = static_cast<size_t>(head) * T;
     int Tn = T, hh = 0, snap0 = 0;
     if (!ONE && pk.cu != nullptr) {   // (the decode step never runs a packed batch)
-        const int n = head / pk.H;
-        hh = head - n * pk.H;
+        const int ni = head / pk.H;
+        hh = head - ni * pk.H;
+        const int n = pk.seq_order ? pk.seq_order[ni] : ni;
+        head = n * pk.H + hh;
         const int t0 = min(max(pk.cu[n], 0), pk.Ttot), t1 = min(max(pk.cu[n + 1], 0), pk.Ttot);
         Tn = t1 > t0 ? t1 - t0 : 0;
         tok0 = static_cast<size_t>(hh) * pk.Ttot + t0;
