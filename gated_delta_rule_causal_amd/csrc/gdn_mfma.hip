@@ -1261,11 +1261,39 @@ VarPlan make_var_plan(int N, int H, int Ttot) {
 // (bins in LDS, positions taken with LDS atomics: the order within a bin is
 // arbitrary, and every workgroup computes the same thing whatever its place).
 constexpr int kPlanThreads = 1024;
+
+// Inclusive prefix sum over the plan kernel's threads: a shuffle scan in each
+// wave, then one over the wave totals (tot: kPlanThreads / 64 ints of LDS,
+// not shared with another scan in flight).
+__device__ __forceinline__ int plan_scan(int x, int* tot) {
+    constexpr int kWaves = kPlanThreads / 64;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) tot[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+        int t = lane < kWaves ? tot[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kWaves; d <<= 1) {
+            const int y = __shfl_up(t, d, 64);
+            if (lane >= d) t += y;
+        }
+        if (lane < kWaves) tot[lane] = t;
+    }
+    __syncthreads();
+    return wv > 0 ? x + tot[wv - 1] : x;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, int Ttot, int SEGC, int snap,
                                                                        const int* __restrict__ cu, int* seg_base,
                                                                        int* snap_base, int* order, int cap,
                                                                        int* seq_order) {
-    __shared__ int part[2][kPlanThreads];
+    __shared__ int hist[kPlanThreads];
+    __shared__ int tot[4][kPlanThreads / 64];
     const int tid = threadIdx.x;
     const int per = (N + kPlanThreads - 1) / kPlanThreads;
     const int a = min(N, tid * per), b = min(N, a + per);
@@ -1283,20 +1311,10 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
         ss += g;
         sn += z;
     }
-    part[0][tid] = ss;
-    part[1][tid] = sn;
-    __syncthreads();
-    // inclusive scan of the per-thread sums (Hillis-Steele)
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int x0 = tid >= off ? part[0][tid - off] : 0;
-        const int x1 = tid >= off ? part[1][tid - off] : 0;
-        __syncthreads();
-        part[0][tid] += x0;
-        part[1][tid] += x1;
-        __syncthreads();
-    }
-    const int gb0 = part[0][tid] - ss;   // exclusive
-    int gb = gb0, zb = part[1][tid] - sn;
+    const int ss_incl = plan_scan(ss, tot[0]);
+    const int sn_incl = plan_scan(sn, tot[1]);
+    const int gb0 = ss_incl - ss;   // exclusive
+    int gb = gb0, zb = sn_incl - sn;
     for (int n = a; n < b; ++n) {
         seg_base[n] = gb;
         snap_base[n] = zb;
@@ -1306,27 +1324,21 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
         zb += z;
     }
     if (tid == kPlanThreads - 1) {
-        seg_base[N] = part[0][tid];
-        snap_base[N] = part[1][tid];
+        seg_base[N] = ss_incl;
+        snap_base[N] = sn_incl;
     }
     if (order == nullptr && seq_order == nullptr) return;
     // ---- longest first: bin kPlanThreads - 1 - chunks (chunk counts past the
     // last bin share it), histogram, exclusive scan, scatter
-    int* hist = part[0];
-    auto sort_by_chunks = [&](auto&& each) {
-        __syncthreads();   // earlier reads of part are done
+    auto sort_by_chunks = [&](auto&& each, int* t) {
+        __syncthreads();   // the previous scatter's atomics are done
         hist[tid] = 0;
         __syncthreads();
         each([&](int, int bin) { atomicAdd(&hist[bin], 1); });
         __syncthreads();
         const int own = hist[tid];
-        for (int off = 1; off < kPlanThreads; off <<= 1) {
-            const int x = tid >= off ? hist[tid - off] : 0;
-            __syncthreads();
-            hist[tid] += x;
-            __syncthreads();
-        }
-        hist[tid] -= own;   // exclusive: the first position of bin tid
+        const int incl = plan_scan(own, t);
+        hist[tid] = incl - own;   // exclusive: the first position of bin tid
         __syncthreads();
     };
     auto bin_of = [&](int chunks) { return kPlanThreads - 1 - min(max(chunks, 0), kPlanThreads - 1); };
@@ -1339,7 +1351,7 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
         }
     };
     if (seq_order) {
-        sort_by_chunks(each_sequence);
+        sort_by_chunks(each_sequence, tot[2]);
         each_sequence([&](int n, int bin) { seq_order[atomicAdd(&hist[bin], 1)] = n; });
     }
     if (order == nullptr) return;
@@ -1355,7 +1367,7 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
             base += g;
         }
     };
-    sort_by_chunks(each_segment);
+    sort_by_chunks(each_segment, tot[3]);
     each_segment([&](int gs, int bin) { order[atomicAdd(&hist[bin], 1)] = gs; });
 }
 
@@ -1405,9 +1417,9 @@ hipError_t launch_uniform(int B, int H, int T, const void* q, const void* k, con
 // The plain uniform plan makes at most kTargetBlocks (head, segment) items and
 // the lead plan BH (slots + 1) with slots = kTargetBlocks / BH >= 2, so at
 // most kTargetBlocks + kTargetBlocks / 2: kScratchBytes (72 MiB) covers every
-// uniform call.  The array is part of
-// the code object: each device the library runs on holds its own copy from
-// the first launch until the process ends.  Host code must not use the
+// uniform call.  The array is part of the code object: each device the
+// library runs on holds its own copy from the first launch until the process
+// ends.  Host code must not use the
 // array's name as an address (on the host it is only a stand-in); the device
 // address comes from hipGetSymbolAddress, looked up once per device with that
 // device current, and is kept per device.
