@@ -583,31 +583,42 @@ __device__ __forceinline__ void store_state(const f32x4 (&P)[NT][8], float* rows
     }
 }
 
-// Element (row d, column j) of a segment map M in the order the combine's
-// MFMA operands read it: 64-lane blocks of 16 bytes, block (w, mt, ks, h)
-// holding, for lane 16 g + r, M[32 w + 16 mt + r][32 ks + 8 g + 4 h .. +3].
-// Every wave-wide load of the combine is then one contiguous 1 KiB run.
+// A segment map M is stored split, M = hi + lo with hi = bf16(M) and
+// lo = bf16(M - hi), the two bf16 operands the combine multiplies with, in
+// the order its MFMA operands read them: 64-lane blocks of 16 bytes, block
+// (w, mt, ks) holding, for lane 16 g + r, M[32 w + 16 mt + r][32 ks + 8 g .. +7];
+// hi in the first half of the matrix's space, lo in the second.  Every
+// wave-wide load of the combine is then one contiguous 1 KiB run, and the
+// combine does no splitting of its own.
+constexpr int kMapHalf = D * D;   // bf16 elements of each half
 __device__ __forceinline__ int map_frag(int row, int col) {
-    const int blk = (((row >> 5) * 2 + ((row >> 4) & 1)) * 4 + (col >> 5)) * 2 + ((col >> 2) & 1);
+    const int blk = ((row >> 5) * 2 + ((row >> 4) & 1)) * 4 + (col >> 5);
     const int ln = ((col >> 3) & 3) * 16 + (row & 15);
-    return ((blk * 64 + ln) << 2) + (col & 3);
+    return ((blk * 64 + ln) << 3) + (col & 7);
 }
 
 // The slice of M a map carrier holds, written in that order.
 template <int NT>
-__device__ __forceinline__ void store_map_frag(const f32x4 (&P)[NT][8], float* M, int col0, int lane) {
+__device__ __forceinline__ void store_map_frag(const f32x4 (&P)[NT][8], u16* M, int col0, int lane) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) M[map_frag(perm_row(t, 4 * g + i), col0 + 16 * nt + r)] = P[nt][t][i];
+            for (int i = 0; i < 4; ++i) {
+                const int at = map_frag(perm_row(t, 4 * g + i), col0 + 16 * nt + r);
+                const float x = P[nt][t][i];
+                const u16 hi = f32_to_bf16_bits(x);
+                M[at] = hi;
+                M[kMapHalf + at] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+            }
 }
 
-// ---- workspace: per (head, segment) three 128 x 128 fp32 matrices: the
-// entering state P_s and N_s in the state's row layout ([value channel][d]),
-// and M_s in the combine's operand order (map_frag).
+// ---- workspace: per (head, segment) three 128 x 128 fp32 matrices' room:
+// the entering state P_s and N_s in the state's row layout ([value
+// channel][d]), and M_s as two bf16 halves in the combine's operand order
+// (map_frag).
 constexpr size_t kMat = static_cast<size_t>(D) * D;
 __device__ __forceinline__ size_t ws_P(size_t slot) { return slot * 3 * kMat; }
 __device__ __forceinline__ size_t ws_N(size_t slot) { return ws_P(slot) + kMat; }
@@ -812,7 +823,7 @@ __device__ __forceinline__ void map_body(MapTiles& sm, const Item& it, const u16
         if (npart)
             store_state<2>(P, ws + ws_N(it.slot0 + it.seg), col0, lane);
         else
-            store_map_frag<2>(P, ws + ws_M(it.slot0 + it.seg), col0, lane);
+            store_map_frag<2>(P, reinterpret_cast<u16*>(ws + ws_M(it.slot0 + it.seg)), col0, lane);
     } else {
         const int u = w - 8;
         // The blocks (0,1) and (2,3) above the diagonal of Tm are read by
@@ -907,56 +918,45 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(Geo geo, c
         *reinterpret_cast<float4*>(&Ps[0][rl][d4]) = x;
         if (!s0) *reinterpret_cast<float4*>(ws + ws_P(slot0) + off) = x;
     }
-    // The maps (M_s, N_s) do not depend on the states: those of step s+1 are
-    // loaded while step s runs, and M is split into bf16 pairs ahead of use.
-    // Lane (r, g) of wave w uses rows d = 32w + 16mt + r of M (8 columns per
-    // k-step) and rows d = 32w + 16mt + 4g .. +3 of column v = r of N.
-    float4 mraw[2][4][2], nraw[2];
-    auto load_maps = [&](int st) {
-        const float* M = ws + ws_M(slot0 + st);
+    // The maps (M_s, N_s) do not depend on the states: they are loaded two
+    // steps ahead into a ring of two register sets (M already split into its
+    // bf16 halves by the map kernel).  Lane (r, g) of wave w uses rows
+    // d = 32w + 16mt + r of M (8 columns per k-step) and rows
+    // d = 32w + 16mt + 4g .. +3 of column v = r of N.
+    bf16x8 mh[2][2][4], ml[2][2][4];
+    f32x4 nv[2][2];
+    auto load_maps = [&](int st, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        const u16* Mh = reinterpret_cast<const u16*>(ws + ws_M(slot0 + st));
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                // M[32w + 16mt + r][32ks + 8g ..] in the operand order of map_frag
-                const float* mb = M + static_cast<size_t>((((w * 2 + mt) * 4 + ks) * 2) * 64 + lane) * 4;
-                mraw[mt][ks][0] = *reinterpret_cast<const float4*>(mb);
-                mraw[mt][ks][1] = *reinterpret_cast<const float4*>(mb + 64 * 4);
+                // M[32w + 16mt + r][32ks + 8g .. +7] in the operand order of map_frag
+                const size_t at = static_cast<size_t>(((w * 2 + mt) * 4 + ks) * 64 + lane) * 8;
+                mh[B][mt][ks] = *reinterpret_cast<const bf16x8*>(Mh + at);
+                ml[B][mt][ks] = *reinterpret_cast<const bf16x8*>(Mh + kMapHalf + at);
             }
-            nraw[mt] = *reinterpret_cast<const float4*>(ws + ws_N(slot0 + st) + static_cast<size_t>(16 * tile + r) * D +
-                                                        32 * w + 16 * mt + 4 * g);
+            const float4 x = *reinterpret_cast<const float4*>(ws + ws_N(slot0 + st) +
+                                                              static_cast<size_t>(16 * tile + r) * D + 32 * w +
+                                                              16 * mt + 4 * g);
+            nv[B][mt] = f32x4{x.x, x.y, x.z, x.w};
         }
     };
-    bf16x8 mh[2][4], ml[2][4];
-    f32x4 nv[2];
-    auto split_maps = [&]() {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const float mv[8] = {mraw[mt][ks][0].x, mraw[mt][ks][0].y, mraw[mt][ks][0].z, mraw[mt][ks][0].w,
-                                     mraw[mt][ks][1].x, mraw[mt][ks][1].y, mraw[mt][ks][1].z, mraw[mt][ks][1].w};
-                split8(mv, mh[mt][ks], ml[mt][ks]);
-            }
-            nv[mt] = f32x4{nraw[mt].x, nraw[mt].y, nraw[mt].z, nraw[mt].w};
-        }
-    };
-    load_maps(s0);
-    split_maps();
-    for (int s = s0; s + 1 < G; ++s) {
-        if (s + 2 < G) load_maps(s + 1);
+    // step s: P_{s+1} = M_s P_s + N_s with the maps in ring slot B = (s - s0) & 1
+    auto step = [&](int s, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
         lds_barrier();
-        const int cur = (s - s0) & 1;
-        f32x4 acc[2] = {nv[0], nv[1]};
+        f32x4 acc[2] = {nv[B][0], nv[B][1]};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             bf16x8 ph, pl;
-            split8(&Ps[cur][r][32 * ks + 8 * g], ph, pl);
+            split8(&Ps[B][r][32 * ks + 8 * g], ph, pl);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                acc[mt] = mfma16x16x32(mh[mt][ks], ph, acc[mt]);
-                acc[mt] = mfma16x16x32(mh[mt][ks], pl, acc[mt]);
-                acc[mt] = mfma16x16x32(ml[mt][ks], ph, acc[mt]);
+                acc[mt] = mfma16x16x32(mh[B][mt][ks], ph, acc[mt]);
+                acc[mt] = mfma16x16x32(mh[B][mt][ks], pl, acc[mt]);
+                acc[mt] = mfma16x16x32(ml[B][mt][ks], ph, acc[mt]);
             }
         }
 #pragma unroll
@@ -964,10 +964,18 @@ __global__ __launch_bounds__(kCombineThreads) void gdn_combine_kernel(Geo geo, c
             // lane holds P_{s+1}[d = 32w+16mt+4g+i][v = r]
             const int d0 = 32 * w + 16 * mt + 4 * g;
             const float4 x = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-            *reinterpret_cast<float4*>(&Ps[cur ^ 1][r][d0]) = x;
+            *reinterpret_cast<float4*>(&Ps[B ^ 1][r][d0]) = x;
             *reinterpret_cast<float4*>(ws + ws_P(slot0 + s + 1) + static_cast<size_t>(16 * tile + r) * D + d0) = x;
         }
-        if (s + 2 < G) split_maps();
+        if (s + 2 <= G - 2) load_maps(s + 2, bufc);   // the maps two steps on, into the slot just used
+    };
+    using b0 = std::integral_constant<int, 0>;
+    using b1 = std::integral_constant<int, 1>;
+    load_maps(s0, b0{});
+    if (s0 + 1 <= G - 2) load_maps(s0 + 1, b1{});
+    for (int s = s0; s + 1 < G; s += 2) {
+        step(s, b0{});
+        if (s + 2 < G) step(s + 1, b1{});
     }
 }
 
