@@ -41,8 +41,8 @@
  *    they suit small heads and few tokens, and are slow at large head sizes:
  *    measured on MI355X for B=2, H=16, T=8192, dk = dv = 128, those kernels
  *    (fp32 activations, chunk 32) take about 180 ms for
- *    gdn_prefill and 97 ms for lin_attn_prefill, against 0.19 ms and 0.13 ms
- *    on the matrix cores and 7 ms for the gated delta rule's recurrent form.
+ *    gdn_prefill and 97 ms for lin_attn_prefill, against 0.15 ms and 0.12 ms
+ *    on the matrix cores and 5 ms for the gated delta rule's recurrent form.
  */
 #ifndef LINATTN_H
 #define LINATTN_H
@@ -335,9 +335,9 @@ la_status gdn_prefill_varlen(int dtype, int N, int H, int T_total, int dk, int d
  * chunk: 64-token blocks; snap_interval a multiple of 64; other dtypes and
  * sizes return LA_ERR_UNSUPPORTED).  The recurrent form is token-serial
  * within each sequence: on 16 sequences of mixed lengths (16 384 tokens, the
- * longest 3551, H = 16, d = 128) it takes 1.9-2.6 ms, against 0.12 ms
- * (normalised and scalar-gated), 0.36 ms (KDA) and 0.17 ms (gated delta) for
- * the block form.
+ * longest 3551, H = 16, d = 128) it takes 1.9-2.8 ms, against 0.13 ms
+ * (normalised), 0.12 ms (scalar-gated), 0.36 ms (KDA) and 0.18 ms (gated
+ * delta) for the block form.
  * workspace/ws_bytes: at least la_workspace_bytes(LA_FN_PREFILL_VARLEN,
  * dtype, N, H, T_total, dk, dv, form, chunk) bytes (one size for every kind;
  * the sequence and snapshot tables are built on the device, so the host
