@@ -42,7 +42,7 @@
  *    measured on MI355X for B=2, H=16, T=8192, dk = dv = 128, those kernels
  *    (fp32 activations, chunk 32) take about 180 ms for
  *    gdn_prefill and 97 ms for lin_attn_prefill, against 0.15 ms and 0.12 ms
- *    on the matrix cores and 5 ms for the gated delta rule's recurrent form.
+ *    on the matrix cores and 4 ms for the gated delta rule's recurrent form.
  */
 #ifndef LINATTN_H
 #define LINATTN_H
