@@ -4,8 +4,9 @@ different lengths, with state snapshots, against the fp64 oracle
 d = 128, chunk 64) and the recurrent path (fp32 and bf16, any head size,
 snapshots at any interval); empty sequences, one-token sequences, lengths
 around chunk edges, carried and in-place states, a truncated snapshot
-buffer, many sequences, an empty batch, resuming a sequence from one of its
-snapshots with gdn_prefill (prefix reuse), and the 16-sequence workload.
+buffer, many sequences (up to 2500, more than the plan kernel's threads), an
+empty batch, resuming a sequence from one of its snapshots with gdn_prefill
+(prefix reuse), and the 16-sequence workload.
 """
 
 import numpy as np
@@ -85,6 +86,32 @@ def test_varlen_many_sequences(gd):
     ref = ov.gdn_varlen(q, k, v, a, b, cu, None, snap_interval=256, form="chunked")
     got = run(gd, q, k, v, a, b, cu, "bf16", None, snap=256)
     check("varlen 64 sequences", got, ref, cu, "bf16")
+
+
+def _many_short_lengths(seed, N, total):
+    """N lengths summing to total, every 97th sequence empty (its tokens moved
+    to the last one)."""
+    lens = synth.varlen_lengths(seed, N, total)
+    moved = int(lens[::97].sum())
+    lens[::97] = 0
+    lens[-1] += moved
+    return lens
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("form", ["chunked", "recurrent"])
+def test_varlen_thousands_of_sequences(gd, form):
+    """2500 sequences (more than one per plan-kernel thread), most a few
+    chunks long, some empty: the device-built tables, the longest-first
+    order of segments and sequences, and every sequence's output and state
+    against the oracle."""
+    H, d = 2, 128
+    lens = _many_short_lengths(87, 2500, 60000)
+    q, k, v, a, b, cu = synth.varlen_batch(88, lens, H, d, d, "bf16")
+    S0 = synth.state_batch(89, len(lens), H, d, d, 0.05)
+    ref = ov.gdn_varlen(q, k, v, a, b, cu, S0, snap_interval=128, form="chunked")
+    got = run(gd, q, k, v, a, b, cu, "bf16", S0, snap=128, form=form)
+    check(f"varlen 2500 sequences ({form})", got, ref, cu, "bf16")
 
 
 def test_varlen_truncated_snapshot_buffer(gd):

@@ -251,6 +251,26 @@ def test_varlen_chunked_truncated_snapshots_and_resume(gd, kind):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("kind,form", [("normalized", "chunked"), ("kda", "chunked"), ("gated", "recurrent")])
+def test_varlen_kind_thousands_of_sequences(gd, kind, form):
+    """2500 sequences, most a few chunks long, every 97th empty: the
+    longest-first order of segments (block form of the normalised kind),
+    of sequences (KDA's column scan, the recurrent form), against the oracle."""
+    H, d = 2, 128
+    lens = synth.varlen_lengths(91, 2500, 30000)
+    moved = int(lens[::97].sum())
+    lens[::97] = 0
+    lens[-1] += moved
+    q, k, v, a, b, cu, S0, z0 = inputs(kind, 93, lens, H, d, "bf16")
+    ref = ov.packed_varlen(kind, q, k, v, cu, a, b, S0, z0, snap_interval=128)
+    if form == "chunked":
+        got = run_chunked(gd, kind, q, k, v, a, b, cu, S0, z0, snap=128)
+    else:
+        got = run(gd, kind, q, k, v, a, b, cu, "bf16", S0, z0, snap=128)
+    check(f"varlen {kind} {form} 2500 sequences", got, ref, cu, "bf16")
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("kind", KINDS)
 def test_varlen_chunked_16_sequences(gd, kind):
     """16 sequences of mixed lengths, 16 heads, 16 384 tokens, snapshots every
