@@ -236,9 +236,13 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     typename IO::T* __restrict__ v, float* __restrict__ alpha, float* __restrict__ beta) {
     using E = typename IO::T;
     const int C = H * (2 * DK + DV);
-    const int h = blockIdx.x % H;
-    const int tile = (blockIdx.x / H) % tiles;
-    const int b = blockIdx.x / (H * tiles);
+    // the three parts (q, k, v) of a (tile, head) are neighbouring workgroups,
+    // and the heads of a tile follow each other
+    const int part = blockIdx.x % 3;
+    const int rest = blockIdx.x / 3;
+    const int h = rest % H;
+    const int tile = (rest / H) % tiles;
+    const int b = rest / (H * tiles);
     const int t0 = tile * kTile;
     const int len = max(0, min(kTile, T - t0));
     const E* xb = x + static_cast<size_t>(b) * T * C;
@@ -249,32 +253,36 @@ __global__ __launch_bounds__(kThreads) void gdn_preprocess_kernel(
     const int tid = threadIdx.x;
 
     if (len > 0) {   // (T == 0: only the state below)
-        // one part after another: loading the next part's window before the
-        // current part's stores needs two windows of registers, and the lower
-        // occupancy that costs was measured slower than the wait it removes
-        Window<DK, E> wq, wk;
-        Window<DV, E> wv;
-        conv_load<DK>(wq, xb, st, w, C, h * DK, t0, len, tid);
-        conv_store<DK, true, PACKED>(wq, st, C, h * DK, t0, len, T, q + row0 * DK, tid, sq);
-        conv_load<DK>(wk, xb, st, w, C, H * DK + h * DK, t0, len, tid);
-        conv_store<DK, true, PACKED>(wk, st, C, H * DK + h * DK, t0, len, T, k + row0 * DK, tid, sq);
-        conv_load<DV>(wv, xb, st, w, C, 2 * H * DK + h * DV, t0, len, tid);
-        conv_store<DV, false, PACKED>(wv, st, C, 2 * H * DK + h * DV, t0, len, T, v + row0 * DV, tid, sq);
-        for (int j = tid; j < len; j += kThreads) {
-            const size_t li = (static_cast<size_t>(b) * T + t0 + j) * H + h;
-            alpha[row0 + t0 + j] = sigmoid(a_logit[li]);
-            beta[row0 + t0 + j] = sigmoid(b_logit[li]);
+        // one part per workgroup: a workgroup's window loads never wait
+        // behind its own stores of another part (loads and stores share one
+        // counter), and the parts of neighbouring workgroups overlap
+        if (part == 0) {
+            Window<DK, E> wq;
+            conv_load<DK>(wq, xb, st, w, C, h * DK, t0, len, tid);
+            conv_store<DK, true, PACKED>(wq, st, C, h * DK, t0, len, T, q + row0 * DK, tid, sq);
+            for (int j = tid; j < len; j += kThreads) {
+                const size_t li = (static_cast<size_t>(b) * T + t0 + j) * H + h;
+                alpha[row0 + t0 + j] = sigmoid(a_logit[li]);
+                beta[row0 + t0 + j] = sigmoid(b_logit[li]);
+            }
+        } else if (part == 1) {
+            Window<DK, E> wk;
+            conv_load<DK>(wk, xb, st, w, C, H * DK + h * DK, t0, len, tid);
+            conv_store<DK, true, PACKED>(wk, st, C, H * DK + h * DK, t0, len, T, k + row0 * DK, tid, sq);
+        } else {
+            Window<DV, E> wv;
+            conv_load<DV>(wv, xb, st, w, C, 2 * H * DK + h * DV, t0, len, tid);
+            conv_store<DV, false, PACKED>(wv, st, C, 2 * H * DK + h * DV, t0, len, T, v + row0 * DV, tid, sq);
         }
     }
     // carried state: the last three tokens of [state; x], this head's channels
     // (packed batches: written per sequence by gdn_state_out_kernel)
     if (st_out != nullptr && cu == nullptr && tile == tiles - 1) {
-        constexpr int nch = 2 * DK + DV;
+        // this part's channels
+        const int nch = part == 2 ? DV : DK;
+        const int cb = part == 0 ? h * DK : part == 1 ? H * DK + h * DK : 2 * H * DK + h * DV;
         for (int e = tid; e < 3 * nch; e += kThreads) {
-            const int r = e / nch, cc = e % nch;
-            const int c = cc < DK       ? h * DK + cc
-                          : cc < 2 * DK ? H * DK + h * DK + (cc - DK)
-                                        : 2 * H * DK + h * DV + (cc - 2 * DK);
+            const int r = e / nch, c = cb + e % nch;
             const int ts = T - 3 + r;
             float val = 0.f;
             if (ts >= 0)
@@ -315,7 +323,7 @@ hipError_t launch_dv(int B, int T, int H, int dv, const int* cu, int N, const vo
                      float* alpha, float* beta, hipStream_t stream) {
     using E = typename IO::T;
     const int tiles = T > 0 ? (T + kTile - 1) / kTile : 1;   // T == 0: one workgroup per head writes the state
-    const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * H * tiles)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * H * tiles * 3)), block(kThreads);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, T, H, tiles, cu, N, static_cast<const E*>(x), w, al, bl,
                            static_cast<const E*>(st_in), static_cast<E*>(st_out), static_cast<E*>(q),
