@@ -178,6 +178,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ __attribute__((aligned(16))) u16 Vs[C][LDR];
     __shared__ __attribute__((aligned(16))) u16 As[C][LDT];
     __shared__ float zs[D], dens[C];
+    // normalised kind: per 16-row group of a chunk, the column sums of phi(K)
+    // that the staging threads formed (padded rows: fewer bank conflicts)
+    __shared__ float zpart[GATED ? 1 : D][17];
     __shared__ float gs[C], egs[C], eks[C];   // GATED: chunk-local g, e^g, e^{g_c - g}
 
     LItem it;
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // (a whole chunk, the usual case, takes a copy of the loop without the
         // row masks: len is uniform over the workgroup)
         auto stage = [&](auto whole) {
+        float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // this thread's rows of its 8 channels
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int e = tid + kThreads * it;
@@ -330,6 +334,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if (OUT) *reinterpret_cast<bf16x8*>(&fQ[row][c8]) = pq;
             *reinterpret_cast<bf16x8*>(&fK[row][c8]) = pk;
             *reinterpret_cast<uint4*>(&Vs[row][c8]) = real ? rv[it] : make_uint4(0, 0, 0, 0);
+            if (!GATED) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) zp[j] += xk[j];
+            }
+        }
+        if (!GATED) {   // rows (tid >> 4) + 16 it of channels 8 (tid & 15) .. +7
+#pragma unroll
+            for (int j = 0; j < 8; ++j) zpart[8 * (tid & 15) + j][tid >> 4] = zp[j];
         }
         };
         if (len == C)
@@ -399,18 +411,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         if constexpr (OUT) lds_barrier();   // A and den complete
-        // ---- z += colsum phi(K)  (read again only after the next loop-top barrier)
+        // ---- z += colsum phi(K) from the 16 row-group sums of the staging
+        //      (read again only after the next loop-top barrier)
         if (!GATED && tid < D) {
-            // two independent sums: the loads do not wait on one chain
-            float a0 = zs[tid], a1 = 0.f;
-#pragma unroll 16
-            for (int c = 0; c < C; c += 2) {
-                a0 += bf16_bits_to_f32(fK[c][tid]);
-                a1 += bf16_bits_to_f32(fK[c + 1][tid]);
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                a0 += zpart[tid][i];
+                a1 += zpart[tid][i + 1];
             }
-            zs[tid] = a0 + a1;
+            const float zn = zs[tid] + (a0 + a1);
+            zs[tid] = zn;
             const int js = snap_slot(n);
-            if (js >= 0) geo.z_snap[(static_cast<size_t>(js) * geo.H + it.h) * D + tid] = a0 + a1;
+            if (js >= 0) geo.z_snap[(static_cast<size_t>(js) * geo.H + it.h) * D + tid] = zn;
         }
 
         // ---- this wave's 32 value channels: outputs, then the state update
