@@ -20,8 +20,9 @@
 // and a run of chunks composes to one such map.
 //
 // The sequence of every head is cut into G segments of whole chunks so that
-// B*H*G workgroups fill the chip.  Three kernels, one workgroup (4 waves) per
-// (head, segment) in the two big ones:
+// B*H*G workgroups fill the chip.  Three kernels, one workgroup per (head,
+// segment) in the two big ones (the map kernel 12 waves: 8 carry state
+// columns, 4 stage tiles; the output kernel 8 waves: 4 and 4):
 //  * gdn_map_kernel     - segments 0..G-2: for each chunk, recompute its
 //    state-independent tiles in LDS and push the augmented state [N | M]
 //    (d_k x 256, starting from [0 | I]) through the chunk map; emits the
@@ -863,7 +864,8 @@ __global__ __launch_bounds__(kMapThreads) void gdn_map_kernel(Geo geo, const u16
 
 // ============================================================ combine
 // One workgroup (4 waves) per (head, 16 value channels): P_0 = S0,
-// P_{s+1} = M_s P_s + N_s, writing every P_s.  The products run on MFMA with
+// P_{s+1} = M_s P_s + N_s, writing every P_s that the output pass reads (from
+// P_1 on when the lead kernel has run segment 0 and written P_1).  The products run on MFMA with
 // both operands split into bf16 high and low parts (hi*hi + hi*lo + lo*hi),
 // which keeps about 16 significant bits.  Wave w owns d rows 32w..32w+31.
 constexpr int kCombineThreads = 256;
