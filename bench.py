@@ -306,9 +306,13 @@ def leg_long(c):
     ms = c.timed(n, lambda i: gd.gdn_prefill(q, k, v, a, b, form="chunked", chunk=64, out=out, S_out=S, workspace=ws),
                  warm=3)
     nbytes = B * H * T * path_bytes_per_head_token(d)
+    # the plan with a lead segment when the workspace holds more than 256 / (B*H) segments per head
+    lead = ws.numel() // (B * H * 3 * d * d * 4) * B * H > 256
+    kernels = ["gdn_lead_map_kernel" if lead else "gdn_map_kernel", "gdn_combine_kernel", "gdn_out_kernel"]
     return {"workload": "gated delta prefill B=1 H=16 T=262144 d=128 chunk=64, bf16 I/O, fp32 state (inputs drawn "
                         "on the device)", "calls": n, "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
-            "roofline": hbm_roofline("gdn_prefill (map + combine + out)", nbytes, ms)}
+            "roofline": hbm_roofline("gdn_prefill (" + " + ".join(kernels) + ")", nbytes, ms,
+                                     [x + "_long" for x in kernels])}
 
 
 def leg_kda_prefill(c):
@@ -362,7 +366,9 @@ def leg_varlen(c):
     return {"workload": f"gated delta prefill, packed batch of {N} sequences ({Tt} tokens, lengths "
                         f"{int(min(lens))}..{int(max(lens))}), H=16 d=128 chunk=64, snapshots every {snap} tokens "
                         f"({nsnap})", "calls": n, "ms_per_call": ms, "tokens_per_s": Tt / (ms * 1e-3),
-            "roofline": hbm_roofline("gdn_prefill_varlen (plan + map + combine + out)", nbytes, ms)}
+            "roofline": hbm_roofline("gdn_prefill_varlen (plan + map + combine + out)", nbytes, ms,
+                                     [x + "_varlen_16seq" for x in ("gdn_varlen_plan_kernel", "gdn_map_kernel",
+                                                                    "gdn_combine_kernel", "gdn_out_kernel")])}
 
 
 def leg_varlen_kinds(c):

@@ -5,11 +5,12 @@
     python profile_summary.py pmc     --run TAG:DIR ... --cmd CMD --json OUT.json --md OUT.md
 
 Each DIR is a rocprofv3 output directory (``-d DIR --output-format csv``);
-TAG says which bench legs the run held: ``headline`` (``--legs prefill,copy``)
-or ``legs`` (the other legs, ``copy`` included).  Kernels are named by what
-they compute for a workload (``gdn_out_kernel`` is the 2 x 16 x 8192
-prefill's; in a ``legs`` run the gated-delta kernels belong to the packed
-batch and get the suffix ``_varlen_16seq``).
+TAG says which bench legs the run held: ``headline`` (``--legs prefill,copy``),
+``long`` (``--legs long,copy``) or ``legs`` (the other legs, ``copy``
+included).  Kernels are named by what they compute for a workload
+(``gdn_out_kernel`` is the 2 x 16 x 8192 prefill's; the gated-delta kernels
+of a ``long`` run, the 1 x 16 x 262144 prefill, get the suffix ``_long``, and
+those of a ``legs`` run belong to the packed batch and get ``_varlen_16seq``).
 
 * times: per-kernel call counts and durations from the kernel trace.
 * traffic: HBM bytes per dispatch = FETCH_SIZE x f + WRITE_SIZE x w (KiB),
@@ -59,7 +60,7 @@ def kernel_key(name, tag, wg=None):
     targs = [a.strip() for a in s[len(base) + 1:-1].split(",")] if "<" in s else []
     if base in ("gdn_map_kernel", "gdn_lead_map_kernel", "gdn_combine_kernel", "gdn_out_kernel",
                 "gdn_varlen_plan_kernel"):
-        return base + ("_varlen_16seq" if tag == "legs" else "")
+        return base + {"legs": "_varlen_16seq", "long": "_long"}.get(tag, "")
     if base == "la_chunked_mfma_kernel" and len(targs) == 3:   # <GATED, OUT, PACKED>
         return (("gla" if targs[0] == "true" else "la") + "_chunked_mfma_kernel_" +
                 ("out" if targs[1] == "true" else "state") + ("_varlen" if targs[2] == "true" else ""))
@@ -93,8 +94,8 @@ def sha256(path):
 def runs(specs):
     for spec in specs:
         tag, _, d = spec.partition(":")
-        if tag not in ("headline", "legs") or not d:
-            sys.exit(f"bad run spec {spec!r}: expected headline:DIR or legs:DIR")
+        if tag not in ("headline", "long", "legs") or not d:
+            sys.exit(f"bad run spec {spec!r}: expected headline:DIR, long:DIR or legs:DIR")
         yield tag, d
 
 
