@@ -42,7 +42,12 @@ bool sizes_ok(long long B, long long H, long long T) {
 
 size_t io_size(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
 
-la_status from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+// hipErrorInvalidConfiguration is what the launchers return for a grid of
+// 2^32 or more work-items (sizes that pass the bounds above but are more than
+// one launch can hold): a shape the library cannot run.
+la_status from_hip(hipError_t e) {
+    return e == hipSuccess ? LA_OK : e == hipErrorInvalidConfiguration ? LA_ERR_SHAPE : LA_ERR_HIP;
+}
 
 // Copy S0 -> S_out (zero-fill when S0 is NULL) for empty sequences.
 __global__ void state_copy_kernel(const float* src, float* dst, size_t n) {

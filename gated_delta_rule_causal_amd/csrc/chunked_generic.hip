@@ -222,6 +222,7 @@ hipError_t launch_la_chunked_generic(int dtype, int heads, int T, int dk, int dv
                                      const float* z0, void* o, float* S_out, float* z_out,
                                      hipStream_t stream) {
     if (heads <= 0) return hipSuccess;
+    if (!grid_fits(heads, kThreads)) return hipErrorInvalidConfiguration;
     const size_t lds = la_chunked_generic_lds_bytes(dk, dv, chunk);
     if (dtype == kBF16) {
         auto kern = la_chunked_generic_kernel<IoBF16>;
@@ -248,6 +249,7 @@ hipError_t launch_gdn_chunked_generic(int dtype, int heads, int T, int dk, int d
                                       const float* alpha, const float* beta, const float* S0,
                                       void* o, float* S_out, hipStream_t stream) {
     if (heads <= 0) return hipSuccess;
+    if (!grid_fits(heads, kThreads)) return hipErrorInvalidConfiguration;
     const size_t lds = gdn_chunked_generic_lds_bytes(dk, dv, chunk);
     if (dtype == kBF16) {
         auto kern = gdn_chunked_generic_kernel<IoBF16>;

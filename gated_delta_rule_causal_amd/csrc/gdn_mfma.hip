@@ -1381,9 +1381,13 @@ __global__ __launch_bounds__(kPlanThreads) void gdn_varlen_plan_kernel(int N, in
     each_segment([&](int gs, int bin) { order[atomicAdd(&hist[bin], 1)] = gs; });
 }
 
-hipError_t launch_all(const Geo& g, int map_blocks, int combine_items, int out_blocks, const void* q, const void* k,
-                      const void* v, const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
-                      float* ws, bool prep, bool scan, hipStream_t stream) {
+hipError_t launch_all(const Geo& g, long long map_blocks, long long combine_items, long long out_blocks,
+                      const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                      const float* S0, void* o, float* S_out, float* ws, bool prep, bool scan, hipStream_t stream) {
+    if (!grid_fits(prep ? map_blocks : 0, kMapThreads) ||
+        !grid_fits(scan ? (combine_items + 7) / 8 * 64 : 0, kCombineThreads) ||
+        !grid_fits(scan ? out_blocks : 0, kThreads))
+        return hipErrorInvalidConfiguration;
     if (prep && map_blocks > 0) {
         hipLaunchKernelGGL(gdn_map_kernel, dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream, g,
                            static_cast<const u16*>(k), static_cast<const u16*>(v), alpha, beta, ws);
@@ -1411,15 +1415,20 @@ hipError_t launch_uniform(int B, int H, int T, const void* q, const void* k, con
     const Geo g = uniform_geo(prep && scan ? make_step_plan(BH, T) : make_plan(BH, T), BH, T);
     float* ws = static_cast<float*>(workspace);
     if (g.lead) {   // (G >= 3 by construction: slots >= 2)
-        hipLaunchKernelGGL(gdn_lead_map_kernel, dim3(static_cast<unsigned>(BH * (g.G - 1))), dim3(kMapThreads), 0,
+        const long long blocks = static_cast<long long>(BH) * (g.G - 1);
+        if (!grid_fits(blocks, kMapThreads) || !grid_fits((BH + 7LL) / 8 * 64, kCombineThreads) ||
+            !grid_fits(blocks, kThreads))
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(gdn_lead_map_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kMapThreads), 0,
                            stream, g, static_cast<const u16*>(q), static_cast<const u16*>(k),
                            static_cast<const u16*>(v), alpha, beta, S0, ws, static_cast<u16*>(o));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        return launch_all(g, 0, BH, BH * (g.G - 1), q, k, v, alpha, beta, S0, o, S_out, ws, false, true, stream);
+        return launch_all(g, 0, BH, blocks, q, k, v, alpha, beta, S0, o, S_out, ws, false, true, stream);
     }
     const bool multi = g.G > 1;
-    return launch_all(g, multi ? BH * (g.G - 1) : 0, multi ? BH : 0, BH * g.G, q, k, v, alpha, beta, S0, o, S_out,
+    const long long bh = BH;
+    return launch_all(g, multi ? bh * (g.G - 1) : 0, multi ? bh : 0, bh * g.G, q, k, v, alpha, beta, S0, o, S_out,
                       ws, prep, scan, stream);
 }
 
@@ -1526,11 +1535,16 @@ hipError_t launch_gdn_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
     g.snap = S_snap ? snap : 0;
     g.snap_cap = snap_cap;
     g.S_snap = S_snap;
+    // (segment, head) items, a bound; the extra workgroups exit.  Every grid
+    // is checked before the table kernel runs.
+    const long long blocks = static_cast<long long>(p.Gcap) * H, items = static_cast<long long>(N) * H;
+    if (!grid_fits(blocks, kMapThreads) || !grid_fits(blocks, kThreads) ||
+        !grid_fits((items + 7) / 8 * 64, kCombineThreads))
+        return hipErrorInvalidConfiguration;
     const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream, tab + 2 * (N + 1), p.Gcap);
     if (e != hipSuccess) return e;
     float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.table_bytes);
-    const int blocks = p.Gcap * H;   // (segment, head) items, a bound; the extra workgroups exit
-    return launch_all(g, blocks, N * H, blocks, q, k, v, alpha, beta, S0, o, S_out, ws, true, true, stream);
+    return launch_all(g, blocks, items, blocks, q, k, v, alpha, beta, S0, o, S_out, ws, true, true, stream);
 }
 
 }  // namespace la

@@ -680,9 +680,11 @@ size_t kda_mfma_workspace_bytes(int B, int H, int T) {
     return static_cast<size_t>(B) * H * ((T + C - 1) / C) * kRecord;
 }
 
-hipError_t kda_launch(const KGeo& g, int tile_blocks, int scan_items, const void* q, const void* k, const void* v,
-                      const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
+hipError_t kda_launch(const KGeo& g, long long tile_blocks, long long scan_items, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, const float* S0, void* o, float* S_out,
                       unsigned char* ws, hipStream_t stream) {
+    if (!grid_fits(tile_blocks, kTileThreads) || !grid_fits((scan_items + 7) / 8 * 64, kScanThreads))
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kda_tile_kernel, dim3(static_cast<unsigned>(tile_blocks)), dim3(kTileThreads), 0, stream, g,
                        static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), alpha, beta,
                        ws);
@@ -702,8 +704,8 @@ hipError_t launch_kda_mfma(int B, int H, int T, const void* q, const void* k, co
     g.BH = BH;
     g.T = T;
     g.NC = (T + C - 1) / C;
-    return kda_launch(g, BH * g.NC, BH, q, k, v, alpha, beta, S0, o, S_out, static_cast<unsigned char*>(workspace),
-                      stream);
+    return kda_launch(g, static_cast<long long>(BH) * g.NC, BH, q, k, v, alpha, beta, S0, o, S_out,
+                      static_cast<unsigned char*>(workspace), stream);
 }
 
 // Packed batches: a device-built table (chunk_base, snap_base: [N+1] each;
@@ -736,11 +738,15 @@ hipError_t launch_kda_mfma_varlen(int N, int H, int Ttot, const int* cu, const v
     g.snap = S_snap ? snap : 0;
     g.snap_cap = snap_cap;
     g.S_snap = S_snap;
+    // every grid checked before the table kernel runs
+    const long long tiles = static_cast<long long>(g.cap) * H, items = static_cast<long long>(N) * H;
+    if (!grid_fits(tiles, kTileThreads) || !grid_fits((items + 7) / 8 * 64, kScanThreads))
+        return hipErrorInvalidConfiguration;
     // chunk_base: one "segment" per chunk (an empty sequence counts one)
     const hipError_t e = launch_varlen_table(N, Ttot, 1, g.snap, cu, tab, stream, nullptr, 0, tab + 2 * (N + 1));
     if (e != hipSuccess) return e;
-    return kda_launch(g, g.cap * H, N * H, q, k, v, alpha, beta, S0, o, S_out,
-                      static_cast<unsigned char*>(workspace) + table, stream);
+    return kda_launch(g, tiles, items, q, k, v, alpha, beta, S0, o, S_out, static_cast<unsigned char*>(workspace) + table,
+                      stream);
 }
 
 }  // namespace la

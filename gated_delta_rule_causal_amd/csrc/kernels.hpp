@@ -1,7 +1,9 @@
 // Internal launcher interface between the C ABI (abi.cpp) and the kernel
 // translation units.  Not part of the public ABI.  Every launcher enqueues on
-// `stream`, checks nothing (abi.cpp validated the arguments) and returns the
-// hipError_t of the launch.
+// `stream`, relies on abi.cpp's validation of the arguments, and returns the
+// hipError_t of the launch; the one check of its own is the size of each grid
+// (grid_fits), for which it returns hipErrorInvalidConfiguration before
+// launching anything more.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +20,13 @@ enum Dtype { kF32 = 0, kBF16 = 1 };
 constexpr int kMfmaChunk = 64;
 __host__ __device__ inline bool mfma_chunk_ok(int chunk) {
     return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128;
+}
+
+// A one-dimensional launch holds fewer than 2^32 work-items: blocks of
+// `threads` each, counted in 64 bits (the block counts of very many heads or
+// chunks would wrap in 32).
+inline bool grid_fits(long long blocks, long long threads) {
+    return blocks >= 0 && threads > 0 && blocks <= 0xffffffffLL / threads;
 }
 
 // ---- token-by-token recurrence, one block per head (recurrent.hip) --------

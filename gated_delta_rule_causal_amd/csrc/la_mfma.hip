@@ -647,9 +647,12 @@ size_t la_mfma_workspace_bytes(int B, int H, int T, int, int, int) {
 namespace {
 
 template <bool GATED, bool PACKED>
-hipError_t launch_geo(const LGeo& g, int state_blocks, int combine_items, int out_blocks, const void* q,
-                      const void* k, const void* v, const float* alpha, const float* S0, const float* z0, void* o,
-                      float* S_out, float* z_out, float* ws, hipStream_t stream) {
+hipError_t launch_geo(const LGeo& g, long long state_blocks, long long combine_items, long long out_blocks,
+                      const void* q, const void* k, const void* v, const float* alpha, const float* S0,
+                      const float* z0, void* o, float* S_out, float* z_out, float* ws, hipStream_t stream) {
+    if (!grid_fits(state_blocks, kThreads) || !grid_fits(state_blocks > 0 ? combine_items * 16 : 0, kThreads) ||
+        !grid_fits(out_blocks, kThreads))
+        return hipErrorInvalidConfiguration;
     const u16 *q16 = static_cast<const u16*>(q), *k16 = static_cast<const u16*>(k), *v16 = static_cast<const u16*>(v);
     if (state_blocks > 0) {
         hipLaunchKernelGGL((la_chunked_mfma_kernel<GATED, false, PACKED>), dim3(static_cast<unsigned>(state_blocks)),
@@ -680,7 +683,8 @@ hipError_t launch_segmented(int B, int H, int T, const void* q, const void* k, c
     g.NC = p.NC;
     g.G = p.G;
     g.SEGC = p.SEGC;
-    return launch_geo<GATED, false>(g, p.G > 1 ? BH * (p.G - 1) : 0, BH, BH * p.G, q, k, v, alpha, S0, z0, o, S_out,
+    const long long bh = BH;
+    return launch_geo<GATED, false>(g, p.G > 1 ? bh * (p.G - 1) : 0, bh, bh * p.G, q, k, v, alpha, S0, z0, o, S_out,
                                     z_out, static_cast<float*>(workspace), stream);
 }
 
@@ -726,11 +730,14 @@ hipError_t launch_packed(int N, int H, int Ttot, const int* cu, const void* q, c
     g.snap_cap = snap_cap;
     g.S_snap = S_snap;
     g.z_snap = z_snap;
+    // (segment, head) items, a bound; the extra workgroups exit.  Every grid
+    // is checked before the table kernel runs.
+    const long long blocks = static_cast<long long>(p.Gcap) * H, items = static_cast<long long>(N) * H;
+    if (!grid_fits(blocks, kThreads) || !grid_fits(items * 16, kThreads)) return hipErrorInvalidConfiguration;
     const hipError_t e = launch_varlen_table(N, Ttot, p.SEGC, g.snap, cu, tab, stream, tab + 2 * (N + 1), p.Gcap);
     if (e != hipSuccess) return e;
     float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.table_bytes);
-    const int blocks = p.Gcap * H;   // (segment, head) items, a bound; the extra workgroups exit
-    return launch_geo<GATED, true>(g, blocks, N * H, blocks, q, k, v, alpha, S0, z0, o, S_out, z_out, ws, stream);
+    return launch_geo<GATED, true>(g, blocks, items, blocks, q, k, v, alpha, S0, z0, o, S_out, z_out, ws, stream);
 }
 
 }  // namespace

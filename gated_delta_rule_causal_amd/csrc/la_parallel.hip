@@ -121,6 +121,7 @@ hipError_t launch_dv(int heads, int T, int dv, const void* q, const void* k, con
 template <class IO>
 hipError_t launch_io(int heads, int T, int dk, int dv, const void* q, const void* k, const void* v,
                      void* o, float* S_out, float* z_out, hipStream_t stream) {
+    if (!grid_fits(heads, 256)) return hipErrorInvalidConfiguration;   // both kernels: x = heads
     hipError_t e;
     switch (dk) {
         case 16: e = launch_dv<IO, 16>(heads, T, dv, q, k, v, o, stream); break;

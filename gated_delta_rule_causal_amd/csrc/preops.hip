@@ -323,7 +323,9 @@ hipError_t launch_dv(int B, int T, int H, int dv, const int* cu, int N, const vo
                      float* alpha, float* beta, hipStream_t stream) {
     using E = typename IO::T;
     const int tiles = T > 0 ? (T + kTile - 1) / kTile : 1;   // T == 0: one workgroup per head writes the state
-    const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * H * tiles * 3)), block(kThreads);
+    const long long blocks = static_cast<long long>(B) * H * tiles * 3;
+    if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, T, H, tiles, cu, N, static_cast<const E*>(x), w, al, bl,
                            static_cast<const E*>(st_in), static_cast<E*>(st_out), static_cast<E*>(q),

@@ -444,6 +444,7 @@ hipError_t launch_rows(int heads, int T, int dv, const void* q, const void* k, c
                (pk.cu != nullptr || static_cast<long long>(heads) * split < 512))
             split *= 2;
     const int R = (dv / split + RG - 1) / RG;
+    if (!grid_fits(static_cast<long long>(heads) * split, kThreads)) return hipErrorInvalidConfiguration;
     dim3 grid(static_cast<unsigned>(heads) * split), block(kThreads);
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, T, dv, static_cast<const E*>(q),

@@ -60,7 +60,10 @@ typedef int la_status;
 enum {
     LA_OK = 0,
     LA_ERR_NULL = 1,        /* a required pointer is NULL                         */
-    LA_ERR_SHAPE = 2,       /* a size is negative, out of range or too large      */
+    LA_ERR_SHAPE = 2,       /* a size is negative, out of range or too large
+                               (also: a grid of 2^32 or more work-items, which
+                               one launch cannot hold, e.g. a decode step over
+                               2^24 heads of d = 16)                             */
     LA_ERR_DTYPE = 3,       /* dtype is not LA_F32 / LA_BF16                      */
     LA_ERR_UNSUPPORTED = 4, /* valid arguments, combination not implemented       */
     LA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                   */

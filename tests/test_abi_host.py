@@ -168,6 +168,19 @@ def test_decode_validation(lib):
     assert decode(lib, N=0) == LA_OK
 
 
+def test_grid_beyond_one_launch_is_a_shape_error(lib):
+    """Sizes within every bound whose launch would hold 2^32 or more
+    work-items are refused before anything is launched (so no device is
+    needed to see it, and no call here launches anything): a decode step
+    over 2^24 heads of d = 16 (1 KiB of state each, 16 GiB in all) and the
+    fp32 chunked kernels, one workgroup per head, over as many heads."""
+    W = lambda i: ctypes.c_void_p(BASE + i * 32 * GiB)
+    many = dict(N=1 << 19, H=32)
+    assert decode(lib, q=W(1), k=W(2), v=W(3), a=W(5), b=W(6), S=W(7), o=W(4), **many) == LA_ERR_SHAPE
+    assert prefill(lib, B=1 << 19, H=32, T=1, q=W(1), k=W(2), v=W(3), o=W(4)) == LA_ERR_SHAPE
+    assert gdn(lib, B=1 << 19, H=32, T=1, q=W(1), k=W(2), v=W(3), a=W(5), b=W(6), o=W(4)) == LA_ERR_SHAPE
+
+
 def test_workspace_query(lib):
     big = ctypes.c_size_t(-1).value
     assert lib.la_workspace_bytes(9, F32, 1, 1, 8, 16, 16, CHUNKED, 16) == big
