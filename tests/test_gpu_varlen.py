@@ -6,7 +6,7 @@ snapshots at any interval); empty sequences, one-token sequences, lengths
 around chunk edges, carried and in-place states, a truncated snapshot
 buffer, many sequences (up to 2500, more than the plan kernel's threads), an
 empty batch, resuming a sequence from one of its snapshots with gdn_prefill
-(prefix reuse), and the 16-sequence workload.
+(prefix reuse), and the 16-sequence workload on every sequence and head.
 """
 
 import numpy as np
@@ -155,19 +155,14 @@ def test_resume_from_snapshot(gd):
 
 
 def test_varlen_workload_16seq(gd):
+    """The 16-sequence workload (16 384 tokens, 16 heads, snapshots every
+    1024 tokens) in the launch the bench times: every sequence's outputs,
+    final state and snapshots, on every head, against the oracle."""
     w = synth.WORKLOADS["gdn_varlen_bf16_16seq_16k"]
     H, d = w["H"], w["dk"]
     lens = synth.varlen_lengths(w["seed"], w["N"], w["T_total"])
     q, k, v, a, b, cu = synth.varlen_batch(w["seed"], lens, H, d, d, "bf16")
     got = run(gd, q, k, v, a, b, cu, "bf16", None, snap=w["snap"])
-    # every head of the four longest sequences (and all snapshots of those)
-    order = np.argsort(lens)[::-1][:4]
-    for n in order:
-        s, e = int(cu[n]), int(cu[n + 1])
-        sub_cu = np.array([0, e - s])
-        ref = ov.gdn_varlen(q[:, s:e], k[:, s:e], v[:, s:e], a[:, s:e], b[:, s:e], sub_cu, None,
-                            snap_interval=w["snap"], form="chunked")
-        base = int(sum(int(L) // w["snap"] for L in lens[:n]))
-        nsn = int(lens[n]) // w["snap"]
-        sub = (got[0][:, s:e], got[1][n:n + 1], got[2][base:base + nsn])
-        check(f"varlen workload sequence {n} (len {e - s})", sub, ref, sub_cu, "bf16")
+    ref = ov.gdn_varlen(q, k, v, a, b, cu, None, snap_interval=w["snap"], form="chunked")
+    assert got[2].shape == ref[2].shape
+    check("varlen workload, 16 sequences x 16 heads", got, ref, cu, "bf16")
