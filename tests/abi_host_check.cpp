@@ -140,6 +140,12 @@ int main() {
     CHECK(lin_attn_decode_step(9, LA_BF16, 4, 2, 128, 128, P(1), P(2), P(3), F(5), F(6), F(7), nullptr, P(4),
                                nullptr), LA_ERR_ARG);
 
+    // ---- a grid of 2^32 or more work-items (sizes within every other bound):
+    //      refused before anything is launched, with or without a device
+    CHECK(lin_attn_decode_step(LA_KIND_GATED_DELTA, LA_BF16, 1 << 19, 32, 16, 16, P(1), P(2), P(3), F(5), F(6),
+                               F(7), nullptr, P(4), nullptr), LA_ERR_SHAPE);
+    CHECK(gdn(LA_F32, 1 << 19, 32, 1, 16, 16, LA_FORM_CHUNKED, 16, nullptr, 0), LA_ERR_SHAPE);
+
     // ---- valid calls with no device: the launch fails and is reported
     if (no_device) {
         CHECK(gdn(LA_BF16, 1, 2, 100, 128, 128, 0, 64, P(9), 1 << 30), LA_ERR_HIP);
