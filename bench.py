@@ -18,10 +18,12 @@ sample of the prefill workload.  Prints one JSON line.
 Every leg's inputs are drawn and uploaded first; then the GPU runs about 0.3 s
 of untimed work and the timed parts of the legs follow back to back, the
 headline prefill last (the memory-bound decode legs first, the long-context
-prefill right before the headline, and that leg after three untimed calls):
-every figure is taken at settled clocks, as in a serving process (an idle GPU
-lowers its clocks, and the first milliseconds of work after an idle gap run
-slower).  `--legs` runs a subset (e.g. one leg under a profiler); the legs not
+prefill right before the headline, and that leg after three untimed calls),
+as in a serving process that is already busy (an idle GPU lowers its clocks,
+and the first milliseconds of work after an idle gap run slower).  The
+untimed decode steps settle the memory-bound legs; compute-bound work still
+speeds up over its own first tens of milliseconds, so a short timed run of
+the headline (20 steps after 5) stays slower than a long one (200 after 100).  `--legs` runs a subset (e.g. one leg under a profiler); the legs not
 run are null in the JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
@@ -505,7 +507,8 @@ def settle(c, ms):
     """About `ms` milliseconds of untimed GPU work (repeated decode steps of a
     small batch) before anything is measured: the GPU raises its clocks only
     after several milliseconds of sustained work, and without this the first
-    leg would be timed on a cold GPU."""
+    leg would be timed on a cold GPU (this memory-bound load does not bring
+    the compute-bound legs to their settled speed)."""
     torch, gd = c.torch, c.gd
     if ms <= 0:
         return
@@ -582,7 +585,7 @@ def main():
     ap.add_argument("--la-steps", type=int, default=10, help="timed calls of each secondary prefill leg")
     ap.add_argument("--long-calls", type=int, default=8, help="timed calls of the 1 x 16 x 262144 prefill")
     ap.add_argument("--settle-ms", type=float, default=300.0,
-                    help="untimed GPU work before the first leg, so that every leg runs at settled clocks")
+                    help="untimed decode steps before the first leg, so that no leg starts on an idle GPU")
     ap.add_argument("--legs", default="all",
                     help="comma-separated legs to run (" + ",".join(LEGS) + "; 'copy' is a 256 MiB device copy "
                     "for counter scaling, off unless named); default all but copy")
